@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for one MatRIS-MoE interaction block.
+
+This module only draws random numbers and lays them out in the shapes the
+block takes.  It holds none of the method's arithmetic, so both the GPU path
+and the CPU oracle can be fed from it.
+
+Workloads follow the model widths of Table II in the paper review
+"Breaking the Training Barrier of Billion-Parameter Universal Machine Learning
+Interatomic Potentials" (xllm-io, section 3.1): S = node 2560 / edge 384 /
+hidden 2560 / 72 experts / top-4; M = 1536 / 1536 / 1536 / 40 / top-8;
+L = 1920 / 1920 / 1920 / 72 / top-16.  Structures are periodic cubic cells of
+uniformly random atoms; the cell edge is chosen so that the expected number of
+neighbours inside the cutoff hits a target degree.  The pages train on public
+datasets that are not available here; these synthetic cells stand in for
+them (about 128 atoms and 50 neighbours per atom, the same order of edges per
+configuration as the pages' training corpus).
+
+Draw order for a config with seed s (numpy PCG64 ``default_rng(s)``):
+  1. positions, one structure after another: ``rng.random((n, 3)) * L``
+     rounded to float32 (a value that rounds up to L is wrapped to 0);
+  2. element types z: uniform integers, or a Zipf(s) law over T types;
+  3. node features h ~ N(0, 1), float32 [N, Dn];
+  4. the routing logit table ~ N(0, 1), float32 [T, X];
+  5. weights ~ N(0, 1/fan_in), float32: W_e [K, De], W_d [Dn, De],
+     W_u [De, Dn], W1 [X, Dn, H], W2 [X, H, Dn], w_r [Dn].
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Union
+
+import numpy as np
+
+IntOrList = Union[int, Sequence[int]]
+FloatOrList = Union[float, Sequence[float]]
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockConfig:
+    """Shape of one synthetic interaction-block workload."""
+
+    name: str
+    atoms_per_struct: IntOrList      # int (same for all) or one entry per structure
+    n_structs: int
+    cutoff: float                    # r_c in Angstrom
+    n_types: int                     # T
+    n_rbf: int                       # K
+    d_edge: int                      # De
+    d_node: int                      # Dn
+    d_hidden: int                    # H
+    n_experts: int                   # X
+    top_k: int                       # k
+    seed: int
+    box: Optional[FloatOrList] = None        # cubic cell edge; None -> from target_degree
+    target_degree: Optional[float] = None
+    zipf: Optional[float] = None             # None -> uniform element types
+    description: str = ""
+
+    def atoms_list(self) -> List[int]:
+        if isinstance(self.atoms_per_struct, int):
+            return [self.atoms_per_struct] * self.n_structs
+        out = [int(v) for v in self.atoms_per_struct]
+        assert len(out) == self.n_structs
+        return out
+
+    def boxes(self) -> List[float]:
+        n = self.atoms_list()
+        if self.box is None:
+            assert self.target_degree is not None
+            # expected neighbours = n * (4/3) pi r_c^3 / L^3  ->  solve for L
+            vol_sphere = 4.0 / 3.0 * math.pi * self.cutoff ** 3
+            return [(max(m, 1) * vol_sphere / self.target_degree) ** (1.0 / 3.0) for m in n]
+        if isinstance(self.box, (int, float)):
+            return [float(self.box)] * self.n_structs
+        out = [float(v) for v in self.box]
+        assert len(out) == self.n_structs
+        return out
+
+    @property
+    def n_atoms(self) -> int:
+        return int(sum(self.atoms_list()))
+
+    @property
+    def n_tokens(self) -> int:
+        return self.n_atoms * self.top_k
+
+
+CONFIGS: Dict[str, BlockConfig] = {}
+
+
+def _reg(c: BlockConfig) -> BlockConfig:
+    CONFIGS[c.name] = c
+    return c
+
+
+# The five workloads of the block: a tiny reference case, the S/M/L widths of
+# Table II, and one GPU's graph-partition share at S widths.
+TINY = _reg(BlockConfig(
+    "tiny", 64, 1, 5.0, 4, 16, 32, 64, 128, 8, 2, seed=0, box=8.0,
+    description="1 cubic cell of edge 8 A, 64 atoms, 4 uniform types, r_c 5 A, "
+                "De 32, Dn 64, 8 experts top-2, MLP 64->128->64"))
+S = _reg(BlockConfig(
+    "S", 128, 32, 6.0, 16, 16, 384, 2560, 2560, 72, 4, seed=1, target_degree=50.0,
+    description="32 cells x 128 atoms, ~50 nbrs at 6 A, 16 uniform types, De 384, "
+                "Dn 2560, 72 experts top-4, MLP 2560->2560->2560"))
+M = _reg(BlockConfig(
+    "M", 128, 128, 6.0, 32, 16, 1536, 1536, 1536, 40, 8, seed=2, target_degree=50.0,
+    zipf=1.1,
+    description="128 cells x 128 atoms, 32 Zipf(1.1) types, De=Dn=H=1536, 40 experts top-8"))
+L = _reg(BlockConfig(
+    "L", 128, 64, 6.0, 64, 16, 1920, 1920, 1920, 72, 16, seed=3, target_degree=50.0,
+    zipf=1.1,
+    description="64 cells x 128 atoms, 64 Zipf(1.1) types, De=Dn=H=1920, 72 experts top-16"))
+SHARE = _reg(BlockConfig(
+    "share", 262144, 1, 6.0, 89, 16, 384, 2560, 2560, 72, 4, seed=4, target_degree=60.0,
+    zipf=1.3,
+    description="one periodic supercell of 262144 atoms, ~60 nbrs at 6 A, 89 Zipf(1.3) "
+                "types, S widths"))
+
+# Parity cases sized so the oracle finishes in seconds while the kernels still
+# see several tiles, ragged tails and uneven structures.
+RAGGED = _reg(BlockConfig(
+    "ragged", [97, 130, 61, 1, 0, 200], 6, 5.5, 5, 16, 100, 132, 196, 7, 3, seed=11,
+    box=[10.5, 11.0, 9.25, 12.0, 7.0, 14.5],
+    description="6 uneven cells (incl. a 1-atom and an empty one), dims not tile multiples"))
+CELLLIST = _reg(BlockConfig(
+    "celllist", 3000, 1, 5.0, 6, 16, 64, 96, 160, 9, 2, seed=12, target_degree=45.0,
+    zipf=1.2,
+    description="one 3000-atom cell large enough for a >=3 bins/axis cell list"))
+S_SLICE = _reg(BlockConfig(
+    "S_slice", 128, 2, 6.0, 16, 16, 384, 2560, 2560, 72, 4, seed=13, target_degree=50.0,
+    description="two cells at the full S widths (production tiles at oracle-friendly size)"))
+SPARSE = _reg(BlockConfig(
+    "sparse", [5, 3, 9], 3, 3.0, 3, 16, 36, 40, 44, 3, 3, seed=14, box=[30.0, 25.0, 28.0],
+    description="dilute cells with isolated atoms (degree 0 rows), k = X"))
+TOP1 = _reg(BlockConfig(
+    "top1", [40, 33], 2, 4.0, 2, 16, 48, 68, 72, 5, 1, seed=15, box=[7.0, 6.5],
+    description="top-1 routing (gate exactly 1), images because r_c > L/2"))
+
+
+def make_positions(cfg: BlockConfig, rng: np.random.Generator):
+    """Positions [N,3] f32 (wrapped into [0,L)), cells [B,3,3] f32, struct_ptr [B+1] i32."""
+    counts = cfg.atoms_list()
+    boxes = cfg.boxes()
+    pos_parts = []
+    cells = np.zeros((cfg.n_structs, 3, 3), dtype=np.float32)
+    for b, (n, L_b) in enumerate(zip(counts, boxes)):
+        Lf = np.float32(L_b)
+        cells[b] = np.diag([Lf, Lf, Lf])
+        p = (rng.random((n, 3)) * L_b).astype(np.float32)
+        p[p >= Lf] = np.float32(0.0)
+        pos_parts.append(p)
+    pos = np.concatenate(pos_parts, axis=0) if pos_parts else np.zeros((0, 3), np.float32)
+    struct_ptr = np.zeros(cfg.n_structs + 1, dtype=np.int32)
+    struct_ptr[1:] = np.cumsum(counts)
+    return pos, cells, struct_ptr
+
+
+def make_types(cfg: BlockConfig, rng: np.random.Generator) -> np.ndarray:
+    N, T = cfg.n_atoms, cfg.n_types
+    if cfg.zipf is None:
+        return rng.integers(0, T, N).astype(np.int32)
+    p = (np.arange(T, dtype=np.float64) + 1.0) ** (-cfg.zipf)
+    p /= p.sum()
+    return rng.choice(T, N, p=p).astype(np.int32)
+
+
+def _normal(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return x
+
+
+def make_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """All host-side inputs of one block, in the fixed draw order of the module doc."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    pos, cells, struct_ptr = make_positions(cfg, rng)
+    z = make_types(cfg, rng)
+    N, T, X = cfg.n_atoms, cfg.n_types, cfg.n_experts
+    K, De, Dn, H = cfg.n_rbf, cfg.d_edge, cfg.d_node, cfg.d_hidden
+    out = dict(pos=pos, cell=cells, struct_ptr=struct_ptr, z=z)
+    out["h"] = _normal(rng, (N, Dn), 1.0)
+    out["logits"] = _normal(rng, (T, X), 1.0)
+    out["W_e"] = _normal(rng, (K, De), 1.0 / math.sqrt(K))
+    out["W_d"] = _normal(rng, (Dn, De), 1.0 / math.sqrt(Dn))
+    out["W_u"] = _normal(rng, (De, Dn), 1.0 / math.sqrt(De))
+    out["W1"] = _normal(rng, (X, Dn, H), 1.0 / math.sqrt(Dn))
+    out["W2"] = _normal(rng, (X, H, Dn), 1.0 / math.sqrt(H))
+    out["w_r"] = _normal(rng, (Dn,), 1.0 / math.sqrt(Dn))
+    out["cutoff"] = np.float32(cfg.cutoff)
+    out["top_k"] = int(cfg.top_k)
+    return out
+
+
+def upstream_grad(cfg: BlockConfig, inputs: Dict[str, np.ndarray], kind: str = "energy",
+                  seed: int = 99) -> np.ndarray:
+    """Upstream gradient dL/dh' [N, Dn] f32 for the block's VJP.
+
+    ``energy``: every row is the readout vector w_r, so the VJP returns dE/d(inputs)
+    of a one-block model.  ``random``: N(0,1) rows, the general upstream a later
+    block would send.
+    """
+    N, Dn = cfg.n_atoms, cfg.d_node
+    if kind == "energy":
+        return np.broadcast_to(inputs["w_r"], (N, Dn)).astype(np.float32, copy=True)
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((N, Dn), dtype=np.float32)

@@ -1,0 +1,42 @@
+"""CPU oracle for one MatRIS-MoE interaction block (TEST INFRASTRUCTURE ONLY).
+
+This package is the plain, slow reference the GPU library is checked
+against.  Only the test-suite, the smoke check and the CPU-baseline leg of
+the benchmark may import it; the product path never does.  It shares no code
+with the HIP library: the two meet only in the seeded input generator, which
+holds no arithmetic of the method.
+
+Everything is computed in float64 from the float32 inputs, with NumPy.  Each
+function follows the plain definition of its step; where the pages leave a
+step open the reading taken is stated in the function's docstring.
+
+Sources cited below:
+  [news]   ScienceAI news article on MatRIS-MoE and Janus
+           ("11.5B参数、1.2EFLOPS、训练从数周压到数小时 ..."), section on the
+           model architecture and on conservative training.
+  [review] xllm-io paper review of "Breaking the Training Barrier of
+           Billion-Parameter Universal Machine Learning Interatomic
+           Potentials"; section numbers refer to that review
+           (3.1 architecture / Fig. 1 / Table II, 3.2 algorithmic design,
+           3.3 forces and stresses, 3.4 Fig. 3 timeline, 3.5 kernels).
+
+Parity status per function is listed in ``PINS`` (what fixes each function
+independently of itself).
+"""
+
+PINS = {
+    "graph.radius_graph": "brute force (pure-Python loops) on tiny cells; lattice "
+                          "closed forms (sc, fcc, self images); symmetry; degree statistics",
+    "graph.radius_graph_rows": "equal to the full graph's rows on small cells",
+    "block.rbf / envelope": "closed forms at r=0, mu_k, r_c; analytic derivatives vs FD",
+    "block.edge_embedding": "single-basis special case; smooth vanishing at r_c",
+    "block.aggregate": "e=1, s=1 gives the degree; adjoint identity; atom permutation",
+    "block.route": "numpy stable argsort; gates sum to 1; k=1 gives gate 1",
+    "block.dispatch_tables": "numpy stable lexsort + bincount/cumsum",
+    "block.moe_forward": "shared experts reduce to one dense MLP; X=k=1; expert relabelling; "
+                         "scalar closed form",
+    "block.readout": "dimer closed form",
+    "block.block_vjp": "float64 central finite differences (positions, node features); "
+                       "translation/rotation/permutation invariance; sum of forces = 0; "
+                       "dimer closed form",
+}
