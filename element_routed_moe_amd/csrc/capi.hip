@@ -1,0 +1,292 @@
+// C ABI entry points of the interaction block (aggregation, mixture of
+// experts, readout, input gradient).  The radius graph lives in graph.hip.
+// Each entry point validates its arguments on the host, carves its scratch
+// buffers out of the caller's workspace and enqueues its kernels on the
+// caller's stream.
+#include <algorithm>
+
+#include "common.h"
+
+namespace mlip {
+
+int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                           int n_atoms, const float *W_e, const float *s, int De, float rc,
+                           float *e, float *a, hipStream_t stream);
+int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
+                    const float *W_e, const float *e, const float *s, const float *abar, int De,
+                    float rc, float *sbar, float *grad_pos, hipStream_t stream);
+int moe_route_dispatch(const int32_t *z, const float *logits, int N, int T, int X, int k,
+                       int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom,
+                       int32_t *slot, int32_t *local_rank, int32_t *blk_count, int32_t *n_type,
+                       int32_t *pre, int32_t *exp_count, int32_t *flags, hipStream_t stream);
+int moe_combine(const float *base, const float *rows, const int32_t *z, const float *gate,
+                const int32_t *slot, int N, int T, int k, int D, float *out, hipStream_t stream);
+int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, int B, int D,
+            float *eps, double *energy, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxTypes = 4096;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MLIP_OK;
+  MLIP_CHECK_ARG(ws != nullptr && ws_bytes >= need, "workspace too small: need %zu bytes, got %zu",
+                 need, ws_bytes);
+  MLIP_CHECK_ARG(aligned(ws, 256), "workspace must be 256-byte aligned");
+  return MLIP_OK;
+}
+
+int check_width(int32_t d, const char *name) {
+  MLIP_CHECK_ARG(d > 0 && d % 4 == 0 && d <= (1 << 20), "%s = %d must be a positive multiple of 4",
+                 name, d);
+  return MLIP_OK;
+}
+
+// ------------------------------------------------------------- workspaces --
+struct AggWs {
+  float *a;
+};
+AggWs carve_agg(void *base, int64_t N, int64_t De, size_t *bytes) {
+  Carver c(base);
+  AggWs w;
+  w.a = c.take<float>(size_t(N * De));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+struct MoeWs {
+  int32_t *flags, *local_rank, *blk_count, *n_type, *pre, *exp_count;
+  float *act, *Y;
+};
+MoeWs carve_moe(void *base, int64_t N, int64_t T, int64_t X, int64_t k, int64_t Dn, int64_t H,
+                size_t *bytes) {
+  Carver c(base);
+  MoeWs w;
+  w.flags = c.take<int32_t>(4);
+  w.local_rank = c.take<int32_t>(size_t(std::max<int64_t>(N, 1)));
+  w.blk_count = c.take<int32_t>(size_t(cdiv(std::max<int64_t>(N, 1), 256) * T));
+  w.n_type = c.take<int32_t>(size_t(T));
+  w.pre = c.take<int32_t>(size_t(X * T));
+  w.exp_count = c.take<int32_t>(size_t(X));
+  w.act = c.take<float>(size_t(N * k * H));
+  w.Y = c.take<float>(size_t(N * k * Dn));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+struct VjpWs {
+  float *Q, *Utok, *ubar, *abar, *sbar;
+};
+VjpWs carve_vjp(void *base, int64_t N, int64_t k, int64_t De, int64_t Dn, int64_t H, size_t *bytes) {
+  Carver c(base);
+  VjpWs w;
+  w.Q = c.take<float>(size_t(N * k * H));
+  w.Utok = c.take<float>(size_t(N * k * Dn));
+  w.ubar = c.take<float>(size_t(N * Dn));
+  w.abar = c.take<float>(size_t(N * De));
+  w.sbar = c.take<float>(size_t(N * De));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+}  // namespace
+}  // namespace mlip
+
+using namespace mlip;
+
+extern "C" {
+
+// ------------------------------------------------------------- aggregate ---
+size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge) {
+  size_t b = 0;
+  carve_agg(nullptr, std::max(n_atoms, 0), std::max(d_edge, 0), &b);
+  return b;
+}
+
+int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *h, const float *W_e, const float *W_d,
+                   const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
+                   float *e, float *s, float *u, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  if (int rc = check_width(d_edge, "d_edge")) return rc;
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (h && s && u), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom && e), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_e, 16) && aligned(W_d, 16) &&
+                     aligned(W_u, 16) && aligned(e, 16) && aligned(s, 16) && aligned(u, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_aggregate_workspace_size(n_atoms, d_edge))) return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  AggWs w = carve_agg(ws, n_atoms, d_edge, nullptr);
+
+  GemmArgs g;  // s = h @ W_d
+  g.A = h; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s; g.ldc = d_edge;
+  g.M = n_atoms; g.N = d_edge; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  if (int rc = launch_embed_aggregate(row_ptr, src, geom, n_atoms, W_e, s, d_edge, cutoff, e, w.a,
+                                      stream))
+    return rc;
+  GemmArgs g2;  // u = h + a @ W_u
+  g2.A = w.a; g2.lda = d_edge; g2.B = W_u; g2.ldb = d_node; g2.C = u; g2.ldc = d_node;
+  g2.R = h; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_edge;
+  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+// ------------------------------------------------------------------- MoE ---
+size_t mlip_moe_workspace_size(int32_t n_atoms, int32_t n_types, int32_t n_experts, int32_t top_k,
+                               int32_t d_node, int32_t d_hidden) {
+  size_t b = 0;
+  carve_moe(nullptr, std::max(n_atoms, 0), std::max(n_types, 1), std::max(n_experts, 1),
+            std::max(top_k, 1), std::max(d_node, 0), std::max(d_hidden, 0), &b);
+  return b;
+}
+
+int mlip_moe_forward(const float *u, const int32_t *z, const float *logits, const float *W1,
+                     const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                     int32_t top_k, int32_t d_node, int32_t d_hidden, int32_t *topk, float *gate,
+                     int32_t *exp_off, int32_t *tok_atom, int32_t *slot, float *P, float *h_out,
+                     void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_hidden, "d_hidden")) return rc;
+  MLIP_CHECK_ARG(logits && W1 && W2 && topk && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (u && z && tok_atom && slot && P && h_out), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(u, 16) && aligned(W1, 16) && aligned(W2, 16) && aligned(P, 16) &&
+                     aligned(h_out, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_moe_workspace_size(n_atoms, n_types, n_experts, top_k,
+                                                              d_node, d_hidden)))
+    return rc;
+  MoeWs w = carve_moe(ws, n_atoms, n_types, n_experts, top_k, d_node, d_hidden, nullptr);
+  const int M = n_atoms * top_k;
+  if (int rc = moe_route_dispatch(z, logits, n_atoms, n_types, n_experts, top_k, topk, gate,
+                                  exp_off, tok_atom, slot, w.local_rank, w.blk_count, w.n_type,
+                                  w.pre, w.exp_count, w.flags, stream))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  GemmArgs g;  // P = u[tok] @ W1[x], act = silu(P)
+  g.A = u; g.lda = d_node; g.a_rows = tok_atom;
+  g.B = W1; g.ldb = d_hidden; g.b_group_stride = int64_t(d_node) * d_hidden;
+  g.C = P; g.C2 = w.act; g.ldc = d_hidden;
+  g.group_off = exp_off; g.n_groups = n_experts;
+  g.M = M; g.N = d_hidden; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_SILU, K_GEMM_EXPERT_UP, stream)) return rc;
+  GemmArgs g2;  // Y = act @ W2[x]
+  g2.A = w.act; g2.lda = d_hidden;
+  g2.B = W2; g2.ldb = d_node; g2.b_group_stride = int64_t(d_hidden) * d_node;
+  g2.C = w.Y; g2.ldc = d_node;
+  g2.group_off = exp_off; g2.n_groups = n_experts;
+  g2.M = M; g2.N = d_node; g2.K = d_hidden;
+  if (int rc = launch_gemm(g2, false, EPI_STORE, K_GEMM_EXPERT_DOWN, stream)) return rc;
+  return moe_combine(u, w.Y, z, gate, slot, n_atoms, n_types, top_k, d_node, h_out, stream);
+}
+
+int mlip_moe_status(const void *ws, int32_t *bad_types, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(ws && bad_types, "null pointer argument");
+  int32_t f = 0;
+  MLIP_HIP(hipMemcpyAsync(&f, ws, sizeof(f), hipMemcpyDeviceToHost, stream));
+  MLIP_HIP(hipStreamSynchronize(stream));
+  *bad_types = (f & 1) ? 1 : 0;
+  return MLIP_OK;
+}
+
+// --------------------------------------------------------------- readout ---
+int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr, int32_t n_atoms,
+                 int32_t n_structs, int32_t d_node, float *eps, double *energy, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_structs >= 1, "n_atoms >= 0 and n_structs >= 1 required");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(w_r && struct_ptr && energy, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (h_out && eps), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(h_out, 16) && aligned(w_r, 16), "float arrays must be 16-byte aligned");
+  return readout(h_out, w_r, struct_ptr, n_atoms, n_structs, d_node, eps, energy, stream);
+}
+
+// ------------------------------------------------------------------- VJP ---
+size_t mlip_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_edge, int32_t d_node,
+                               int32_t d_hidden) {
+  size_t b = 0;
+  carve_vjp(nullptr, std::max(n_atoms, 0), std::max(top_k, 1), std::max(d_edge, 0),
+            std::max(d_node, 0), std::max(d_hidden, 0), &b);
+  return b;
+}
+
+int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *e, const float *s, const int32_t *z,
+                   const float *gate, const int32_t *exp_off, const int32_t *tok_atom,
+                   const int32_t *slot, const float *P, const float *W_e, const float *W_d,
+                   const float *W_u, const float *W1, const float *W2, int32_t n_rbf,
+                   int32_t d_edge, int32_t d_node, int32_t d_hidden, int32_t n_types,
+                   int32_t n_experts, int32_t top_k, float cutoff, const float *grad_out,
+                   float *grad_h, float *grad_pos, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_edge, "d_edge")) return rc;
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_hidden, "d_hidden")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u && W1 && W2 && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (s && z && tok_atom && slot && P && grad_out && grad_h && grad_pos),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom && e), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(e, 16) && aligned(s, 16) && aligned(P, 16) && aligned(grad_out, 16) &&
+                     aligned(grad_h, 16) && aligned(geom, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes,
+                        mlip_vjp_workspace_size(n_atoms, top_k, d_edge, d_node, d_hidden)))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  VjpWs w = carve_vjp(ws, n_atoms, top_k, d_edge, d_node, d_hidden, nullptr);
+  const int M = n_atoms * top_k;
+
+  GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
+  g1.A = grad_out; g1.lda = d_node; g1.a_rows = tok_atom;
+  g1.B = W2; g1.ldb = d_node; g1.b_group_stride = int64_t(d_hidden) * d_node;
+  g1.C = w.Q; g1.ldc = d_hidden; g1.R = P; g1.ldr = d_hidden;
+  g1.group_off = exp_off; g1.n_groups = n_experts;
+  g1.M = M; g1.N = d_hidden; g1.K = d_node;
+  if (int rc = launch_gemm(g1, true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN, stream)) return rc;
+  GemmArgs g2;  // U_tok = Q @ W1[x]^T
+  g2.A = w.Q; g2.lda = d_hidden;
+  g2.B = W1; g2.ldb = d_hidden; g2.b_group_stride = int64_t(d_node) * d_hidden;
+  g2.C = w.Utok; g2.ldc = d_node;
+  g2.group_off = exp_off; g2.n_groups = n_experts;
+  g2.M = M; g2.N = d_node; g2.K = d_hidden;
+  if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_VJP_UP, stream)) return rc;
+  // ubar = g + sum_r gate * U_tok[slot]
+  if (int rc = moe_combine(grad_out, w.Utok, z, gate, slot, n_atoms, n_types, top_k, d_node, w.ubar,
+                           stream))
+    return rc;
+  GemmArgs g3;  // abar = ubar @ W_u^T
+  g3.A = w.ubar; g3.lda = d_node; g3.B = W_u; g3.ldb = d_node; g3.C = w.abar; g3.ldc = d_edge;
+  g3.M = n_atoms; g3.N = d_edge; g3.K = d_node;
+  if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  if (int rc = launch_edge_vjp(row_ptr, src, geom, n_atoms, W_e, e, s, w.abar, d_edge, cutoff,
+                               w.sbar, grad_pos, stream))
+    return rc;
+  GemmArgs g4;  // grad_h = ubar + sbar @ W_d^T
+  g4.A = w.sbar; g4.lda = d_edge; g4.B = W_d; g4.ldb = d_edge; g4.C = grad_h; g4.ldc = d_node;
+  g4.R = w.ubar; g4.ldr = d_node; g4.M = n_atoms; g4.N = d_node; g4.K = d_edge;
+  return launch_gemm(g4, true, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,468 @@
+// Periodic radius graph on the GPU: cell list, per-receiver neighbour count,
+// CSR scan, per-receiver fill in canonical order, reverse-edge index.
+//
+// The graph follows the paper review of "Breaking the Training Barrier of
+// Billion-Parameter Universal MLIPs", section 3.1, Figure 1(a) (graph under
+// periodic repetition).  The edge predicate is the float64 formula written
+// in mlip.h; every double operation below is an explicit round-to-nearest
+// intrinsic so the compiler cannot contract or reorder it, which makes the
+// edge set identical to any other evaluation of the same formula.
+//
+// Cell list: along an axis whose cell is at least three bin widths (bin width
+// >= r_c) the candidates of an atom are the atoms of its own and the two
+// adjacent bins (wrapping across the cell boundary with a shift of +-1); along
+// a shorter axis there is one bin and every image shift S in
+// [-ceil(r_c/L), ceil(r_c/L)] is visited.  For positions wrapped into
+// [0, L) these shifts reach every image closer than r_c.
+#include "common.h"
+
+namespace mlip {
+
+namespace {
+
+constexpr int kMaxDeg = 1024;     // edges per row held in LDS by the fill pass
+constexpr int kMaxImages = 8;     // |S| bound along a short axis
+
+enum GraphFlags {
+  GF_NOT_ORTHO = 1,
+  GF_BAD_CELL = 2,
+  GF_POS_OUTSIDE = 4,
+  GF_TOO_MANY_IMAGES = 8,
+  GF_REV_MISSING = 16,
+};
+
+struct StructParams {
+  double C[9];     // lattice vectors as rows
+  double L[3];     // diagonal
+  int lo, hi;      // atom range
+  int nb[3];       // bins per axis (1 = image mode)
+  int nimg[3];     // image range for image-mode axes
+  int bin_base;    // first global bin id
+  int valid;
+};
+
+__global__ void graph_fill_i32(int32_t *p, int64_t n, int32_t v) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void graph_setup(const float *__restrict__ cell, const int32_t *__restrict__ struct_ptr,
+                            int n_structs, float cutoff, StructParams *__restrict__ prm,
+                            int32_t *__restrict__ flags) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_structs) return;
+  StructParams P;
+  for (int q = 0; q < 9; ++q) P.C[q] = double(cell[b * 9 + q]);
+  P.lo = struct_ptr[b];
+  P.hi = struct_ptr[b + 1];
+  P.bin_base = P.lo + b;
+  int f = 0;
+  const double rc = double(cutoff);
+  for (int a = 0; a < 3; ++a) {
+    for (int c = 0; c < 3; ++c)
+      if (c != a && P.C[a * 3 + c] != 0.0) f |= GF_NOT_ORTHO;
+    P.L[a] = P.C[a * 3 + a];
+    if (!(P.L[a] > 0.0) || !(P.L[a] < 1e30)) f |= GF_BAD_CELL;
+  }
+  int n_b = P.hi - P.lo;
+  if (f == 0) {
+    int64_t cap = n_b > 1 ? n_b : 1;
+    for (int a = 0; a < 3; ++a) {
+      double w = P.L[a] / (rc * (1.0 + 1e-5));
+      int nb = w >= 1024.0 ? 1024 : int(w);
+      P.nb[a] = nb >= 3 ? nb : 1;
+    }
+    // never more bins than atoms: bins only get wider, still >= r_c
+    while (int64_t(P.nb[0]) * P.nb[1] * P.nb[2] > cap) {
+      int a = 0;
+      if (P.nb[1] > P.nb[a]) a = 1;
+      if (P.nb[2] > P.nb[a]) a = 2;
+      P.nb[a] -= 1;
+      if (P.nb[a] < 3) P.nb[a] = 1;
+    }
+    for (int a = 0; a < 3; ++a) {
+      P.nimg[a] = 0;
+      if (P.nb[a] == 1) {
+        double n = ceil(rc / P.L[a]);
+        if (n > kMaxImages) {
+          f |= GF_TOO_MANY_IMAGES;
+          n = kMaxImages;
+        }
+        P.nimg[a] = int(n);
+      }
+    }
+  } else {
+    for (int a = 0; a < 3; ++a) {
+      P.nb[a] = 1;
+      P.nimg[a] = 0;
+      P.L[a] = 1.0;
+    }
+  }
+  P.valid = f == 0;
+  prm[b] = P;
+  if (f) atomicOr(flags, f);
+}
+
+__device__ inline int find_struct(const int32_t *__restrict__ struct_ptr, int n_structs, int i) {
+  int lo = 0, hi = n_structs;  // last b with struct_ptr[b] <= i
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (struct_ptr[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline int bin_coord(double x, double L, int nb) {
+  int c = int(x * double(nb) / L);
+  c = c < 0 ? 0 : c;
+  return c >= nb ? nb - 1 : c;
+}
+
+__global__ void graph_bin(const float *__restrict__ pos, const int32_t *__restrict__ struct_ptr,
+                          int n_structs, int n_atoms, const StructParams *__restrict__ prm,
+                          int32_t *__restrict__ atom_struct, int32_t *__restrict__ atom_bin,
+                          int32_t *__restrict__ bin_count, int32_t *__restrict__ flags) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_atoms) return;
+  int b = find_struct(struct_ptr, n_structs, i);
+  const StructParams &P = prm[b];
+  int c[3];
+  bool outside = false;
+  for (int a = 0; a < 3; ++a) {
+    float xf = pos[i * 3 + a];
+    double x = double(xf);
+    if (!(x >= 0.0) || !(x < P.L[a])) outside = true;
+    c[a] = bin_coord(x, P.L[a], P.nb[a]);
+  }
+  if (outside) atomicOr(flags, GF_POS_OUTSIDE);
+  int gb = P.bin_base + (c[2] * P.nb[1] + c[1]) * P.nb[0] + c[0];
+  atom_struct[i] = b;
+  atom_bin[i] = gb;
+  atomicAdd(&bin_count[gb], 1);
+}
+
+__global__ void graph_scatter(const float *__restrict__ pos, int n_atoms,
+                              const int32_t *__restrict__ atom_bin,
+                              const int32_t *__restrict__ bin_start, int32_t *__restrict__ bin_fill,
+                              float4 *__restrict__ binned) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_atoms) return;
+  int gb = atom_bin[i];
+  int p = atomicAdd(&bin_fill[gb], 1);
+  binned[bin_start[gb] + p] =
+      make_float4(pos[i * 3 + 0], pos[i * 3 + 1], pos[i * 3 + 2], __int_as_float(i));
+}
+
+// Candidate enumeration shared by the count and fill passes.  The visitor is
+// called once per candidate slot with (accept, j, S, d, d2); all lanes of the
+// wave call it the same number of times (inactive lanes with accept=false).
+template <typename Visit>
+__device__ inline void visit_candidates(int i, const float *__restrict__ pos,
+                                        const StructParams &P, int gbin_i,
+                                        const int32_t *__restrict__ bin_start,
+                                        const float4 *__restrict__ binned, double rc2,
+                                        Visit &&visit) {
+  const int lane = threadIdx.x & 63;
+  const double xi0 = double(pos[i * 3 + 0]);
+  const double xi1 = double(pos[i * 3 + 1]);
+  const double xi2 = double(pos[i * 3 + 2]);
+  int local = gbin_i - P.bin_base;
+  int bc[3];
+  bc[0] = local % P.nb[0];
+  bc[1] = (local / P.nb[0]) % P.nb[1];
+  bc[2] = local / (P.nb[0] * P.nb[1]);
+  int cnt[3];
+  for (int a = 0; a < 3; ++a) cnt[a] = P.nb[a] == 1 ? 2 * P.nimg[a] + 1 : 3;
+  for (int e2 = 0; e2 < cnt[2]; ++e2)
+    for (int e1 = 0; e1 < cnt[1]; ++e1)
+      for (int e0 = 0; e0 < cnt[0]; ++e0) {
+        int ee[3] = {e0, e1, e2};
+        int S[3], bb[3];
+        for (int a = 0; a < 3; ++a) {
+          if (P.nb[a] == 1) {
+            S[a] = ee[a] - P.nimg[a];
+            bb[a] = 0;
+          } else {
+            int v = bc[a] + ee[a] - 1;
+            S[a] = v < 0 ? -1 : (v >= P.nb[a] ? 1 : 0);
+            bb[a] = v - S[a] * P.nb[a];
+          }
+        }
+        const double s0 = double(S[0]), s1 = double(S[1]), s2 = double(S[2]);
+        double t[3];
+        for (int c = 0; c < 3; ++c)
+          t[c] = __dadd_rn(__dadd_rn(__dmul_rn(s0, P.C[0 * 3 + c]), __dmul_rn(s1, P.C[1 * 3 + c])),
+                           __dmul_rn(s2, P.C[2 * 3 + c]));
+        const bool zero_shift = S[0] == 0 && S[1] == 0 && S[2] == 0;
+        int gb = P.bin_base + (bb[2] * P.nb[1] + bb[1]) * P.nb[0] + bb[0];
+        int k0 = bin_start[gb], k1 = bin_start[gb + 1];
+        for (int k = k0; k < k1; k += 64) {
+          int kk = k + lane;
+          bool ok = false;
+          int j = -1;
+          double d0 = 0, d1 = 0, d2v = 0, dd = 0;
+          if (kk < k1) {
+            float4 q = binned[kk];
+            j = __float_as_int(q.w);
+            d0 = __dadd_rn(__dsub_rn(double(q.x), xi0), t[0]);
+            d1 = __dadd_rn(__dsub_rn(double(q.y), xi1), t[1]);
+            d2v = __dadd_rn(__dsub_rn(double(q.z), xi2), t[2]);
+            dd = __dadd_rn(__dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1)), __dmul_rn(d2v, d2v));
+            ok = dd < rc2 && !(zero_shift && j == i);
+          }
+          visit(ok, j, S, d0, d1, d2v, dd);
+        }
+      }
+}
+
+// One wave per receiver: number of neighbours.
+__global__ void __launch_bounds__(256) graph_count(const float *__restrict__ pos, int n_atoms,
+                                                   const StructParams *__restrict__ prm,
+                                                   const int32_t *__restrict__ atom_struct,
+                                                   const int32_t *__restrict__ atom_bin,
+                                                   const int32_t *__restrict__ bin_start,
+                                                   const float4 *__restrict__ binned, double rc2,
+                                                   int32_t *__restrict__ deg,
+                                                   int32_t *__restrict__ maxdeg) {
+  int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= n_atoms) return;
+  const StructParams &P = prm[atom_struct[i]];
+  int count = 0;
+  if (P.valid) {
+    visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2,
+                     [&](bool ok, int, const int *, double, double, double, double) {
+                       count += __popcll(__ballot(ok));
+                     });
+  }
+  if ((threadIdx.x & 63) == 0) {
+    deg[i] = count;
+    atomicMax(maxdeg, count);
+  }
+}
+
+__global__ void graph_summary(const int32_t *__restrict__ row_ptr, int n_atoms,
+                              const int32_t *__restrict__ flags, const int32_t *__restrict__ maxdeg,
+                              int32_t *__restrict__ out) {
+  out[0] = row_ptr[n_atoms];
+  out[1] = *flags;
+  out[2] = *maxdeg;
+}
+
+__device__ inline uint64_t edge_key(int j, int s0, int s1, int s2) {
+  return (uint64_t(uint32_t(j)) << 24) | (uint64_t(s0 + 128) << 16) | (uint64_t(s1 + 128) << 8) |
+         uint64_t(s2 + 128);
+}
+
+// One wave (one workgroup) per receiver: collect the row in LDS, order it by
+// (sender, shift) with a rank count, write it out.
+__global__ void __launch_bounds__(64) graph_fill(const float *__restrict__ pos, int n_atoms,
+                                                 const StructParams *__restrict__ prm,
+                                                 const int32_t *__restrict__ atom_struct,
+                                                 const int32_t *__restrict__ atom_bin,
+                                                 const int32_t *__restrict__ bin_start,
+                                                 const float4 *__restrict__ binned, double rc2,
+                                                 const int32_t *__restrict__ row_ptr,
+                                                 int32_t *__restrict__ src, char4 *__restrict__ shift,
+                                                 float4 *__restrict__ geom) {
+  __shared__ uint64_t keys[kMaxDeg];
+  __shared__ float4 gm[kMaxDeg];
+  int i = blockIdx.x;
+  if (i >= n_atoms) return;
+  const int lane = threadIdx.x;
+  const StructParams &P = prm[atom_struct[i]];
+  if (!P.valid) return;
+  int n = 0;
+  visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2,
+                   [&](bool ok, int j, const int *S, double d0, double d1, double d2v, double dd) {
+                     uint64_t m = __ballot(ok);
+                     if (ok) {
+                       int p = n + __popcll(m & ((uint64_t(1) << lane) - 1));
+                       if (p < kMaxDeg) {
+                         keys[p] = edge_key(j, S[0], S[1], S[2]);
+                         gm[p] = make_float4(__double2float_rn(d0), __double2float_rn(d1),
+                                             __double2float_rn(d2v),
+                                             __double2float_rn(__dsqrt_rn(dd)));
+                       }
+                     }
+                     n += __popcll(m);
+                   });
+  __syncthreads();
+  const int r0 = row_ptr[i];
+  const int deg = min(n, kMaxDeg);
+  for (int a = lane; a < deg; a += 64) {
+    uint64_t ka = keys[a];
+    int rank = 0;
+    for (int b = 0; b < deg; ++b) rank += keys[b] < ka;
+    int o = r0 + rank;
+    src[o] = int(ka >> 24);
+    shift[o] = make_char4(char(int((ka >> 16) & 255) - 128), char(int((ka >> 8) & 255) - 128),
+                          char(int(ka & 255) - 128), 0);
+    geom[o] = gm[a];
+  }
+}
+
+// One wave per receiver: reverse-edge index by binary search in the sender's row.
+__global__ void __launch_bounds__(256) graph_rev(int n_atoms, const int32_t *__restrict__ row_ptr,
+                                                 const int32_t *__restrict__ src,
+                                                 const char4 *__restrict__ shift,
+                                                 int32_t *__restrict__ rev,
+                                                 int32_t *__restrict__ flags) {
+  int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= n_atoms) return;
+  const int lane = threadIdx.x & 63;
+  const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+  for (int e = r0 + lane; e < r1; e += 64) {
+    int j = src[e];
+    char4 s = shift[e];
+    uint64_t want = edge_key(i, -int(s.x), -int(s.y), -int(s.z));
+    int lo = row_ptr[j], hi = row_ptr[j + 1];
+    while (lo < hi) {
+      int mid = (lo + hi) >> 1;
+      char4 t = shift[mid];
+      uint64_t km = edge_key(src[mid], t.x, t.y, t.z);
+      if (km < want) lo = mid + 1;
+      else hi = mid;
+    }
+    bool found = false;
+    if (lo < row_ptr[j + 1]) {
+      char4 t = shift[lo];
+      found = edge_key(src[lo], t.x, t.y, t.z) == want;
+    }
+    if (!found) atomicOr(flags, GF_REV_MISSING);
+    rev[e] = found ? lo : e;
+  }
+}
+
+struct GraphWs {
+  StructParams *prm;
+  int32_t *flags, *maxdeg, *readback;
+  int32_t *atom_struct, *atom_bin, *bin_count, *bin_start, *bin_fill, *scan_tmp;
+  float4 *binned;
+};
+
+GraphWs carve_graph(void *base, int64_t N, int64_t B, size_t *bytes) {
+  Carver c(base);
+  GraphWs w;
+  w.prm = c.take<StructParams>(size_t(B));
+  w.flags = c.take<int32_t>(4);
+  w.maxdeg = c.take<int32_t>(4);
+  w.readback = c.take<int32_t>(4);
+  int64_t nbins = N + B;
+  w.atom_struct = c.take<int32_t>(size_t(N));
+  w.atom_bin = c.take<int32_t>(size_t(N));
+  w.bin_count = c.take<int32_t>(size_t(nbins));
+  w.bin_start = c.take<int32_t>(size_t(nbins + 1));
+  w.bin_fill = c.take<int32_t>(size_t(nbins));
+  w.scan_tmp = c.take<int32_t>(scan_tmp_elems(std::max<int64_t>(nbins, N) + 1));
+  w.binned = c.take<float4>(size_t(N));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+inline unsigned nblk(int64_t n, int per) { return unsigned(cdiv(n < 1 ? 1 : n, per)); }
+
+}  // namespace
+}  // namespace mlip
+
+using namespace mlip;
+
+extern "C" {
+
+size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs) {
+  size_t bytes = 0;
+  carve_graph(nullptr, n_atoms < 0 ? 0 : n_atoms, n_structs < 1 ? 1 : n_structs, &bytes);
+  return bytes;
+}
+
+int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,
+                     int32_t n_atoms, int32_t n_structs, float cutoff, int64_t edge_capacity,
+                     int32_t *row_ptr, int32_t *src, int8_t *shift, int32_t *rev, float *geom,
+                     int64_t *n_edges, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_structs >= 1, "n_atoms must be >= 0 and n_structs >= 1");
+  MLIP_CHECK_ARG(cell && struct_ptr && row_ptr && n_edges, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || pos, "pos is null");
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  MLIP_CHECK_ARG(edge_capacity >= 0, "edge_capacity must be >= 0");
+  MLIP_CHECK_ARG(edge_capacity == 0 || (src && shift && rev && geom), "edge buffers are null");
+  size_t need = mlip_graph_workspace_size(n_atoms, n_structs);
+  MLIP_CHECK_ARG(ws && ws_bytes >= need, "workspace too small: need %zu bytes, got %zu", need,
+                 ws_bytes);
+  MLIP_CHECK_ARG((reinterpret_cast<uintptr_t>(ws) & 255) == 0, "workspace must be 256-byte aligned");
+  MLIP_CHECK_ARG((reinterpret_cast<uintptr_t>(geom) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(shift) & 3) == 0,
+                 "geom must be 16-byte and shift 4-byte aligned");
+
+  GraphWs w = carve_graph(ws, n_atoms, n_structs, nullptr);
+  const int64_t N = n_atoms, B = n_structs, nbins = N + B;
+  const double rc2 = double(cutoff) * double(cutoff);
+  int32_t host[4] = {0, 0, 0, 0};
+  {
+    ProfScope ps(K_GRAPH, stream);
+    graph_fill_i32<<<1, 64, 0, stream>>>(w.flags, 4, 0);
+    graph_fill_i32<<<1, 64, 0, stream>>>(w.maxdeg, 4, 0);
+    graph_fill_i32<<<nblk(nbins, 256), 256, 0, stream>>>(w.bin_count, nbins, 0);
+    graph_fill_i32<<<nblk(nbins, 256), 256, 0, stream>>>(w.bin_fill, nbins, 0);
+    MLIP_LAUNCHED();
+    graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, cutoff, w.prm, w.flags);
+    MLIP_LAUNCHED();
+    if (N > 0) {
+      graph_bin<<<nblk(N, 256), 256, 0, stream>>>(pos, struct_ptr, n_structs, n_atoms, w.prm,
+                                                   w.atom_struct, w.atom_bin, w.bin_count, w.flags);
+      MLIP_LAUNCHED();
+      int rc = exclusive_scan(w.bin_count, w.bin_start, nbins, true, w.scan_tmp, stream);
+      if (rc) return rc;
+      graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start,
+                                                       w.bin_fill, w.binned);
+      MLIP_LAUNCHED();
+      graph_count<<<nblk(N, 4), 256, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
+                                                   w.bin_start, w.binned, rc2, row_ptr, w.maxdeg);
+      MLIP_LAUNCHED();
+    }
+    int rc = exclusive_scan(row_ptr, row_ptr, N, true, w.scan_tmp, stream);
+    if (rc) return rc;
+    graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
+    MLIP_LAUNCHED();
+    MLIP_HIP(hipMemcpyAsync(host, w.readback, sizeof(host), hipMemcpyDeviceToHost, stream));
+    MLIP_HIP(hipStreamSynchronize(stream));
+  }
+  const int64_t E = host[0];
+  const int flags = host[1];
+  *n_edges = E;
+  if (flags & (GF_NOT_ORTHO | GF_BAD_CELL)) {
+    set_error("cell rejected: %s", (flags & GF_NOT_ORTHO) ? "only orthorhombic cells are supported"
+                                                          : "non-positive or non-finite cell edge");
+    return (flags & GF_NOT_ORTHO) ? MLIP_ERR_UNSUPPORTED : MLIP_ERR_INPUT;
+  }
+  if (flags & GF_POS_OUTSIDE) {
+    set_error("positions must be wrapped into their cell: 0 <= x < L along each axis");
+    return MLIP_ERR_INPUT;
+  }
+  if (flags & GF_TOO_MANY_IMAGES) {
+    set_error("cutoff spans more than %d cell lengths", kMaxImages);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  if (host[2] > kMaxDeg) {
+    set_error("a receiver has %d neighbours; at most %d are supported", host[2], kMaxDeg);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  if (E > edge_capacity) {
+    set_error("edge_capacity %lld < required %lld", (long long)edge_capacity, (long long)E);
+    return MLIP_ERR_CAPACITY;
+  }
+  if (N > 0 && E > 0) {
+    ProfScope ps(K_GRAPH, stream);
+    graph_fill<<<unsigned(N), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
+                                               w.bin_start, w.binned, rc2, row_ptr, src,
+                                               reinterpret_cast<char4 *>(shift),
+                                               reinterpret_cast<float4 *>(geom));
+    MLIP_LAUNCHED();
+    graph_rev<<<nblk(N, 4), 256, 0, stream>>>(n_atoms, row_ptr, src,
+                                              reinterpret_cast<const char4 *>(shift), rev, w.flags);
+    MLIP_LAUNCHED();
+  }
+  return MLIP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Element-type routing, element-grouped token dispatch, gate-weighted
+// combine, and the linear readout.
+//
+// Routing is static per element type (ScienceAI article, architecture
+// section; paper review of "Breaking the Training Barrier of
+// Billion-Parameter Universal MLIPs", section 3.2): every atom of type t goes
+// to the same k experts with the same gates, so the routing table is T x k
+// and the dispatch is a counting sort of atoms by type.  Tokens (atom, rank)
+// are laid out by (expert, element, atom) with prefix-sum offsets; the
+// positions are computed, not claimed with atomics, so the layout is
+// deterministic.  The combine gathers each atom's k expert outputs in rank
+// order, so no scatter (and no write contention) is needed at all.
+#include "common.h"
+
+namespace mlip {
+
+namespace {
+
+constexpr int RANK_BLOCK = 256;
+
+// top-k per element type (ties -> lower expert index) and softmax gates.
+// A NaN logit ranks below every number, so the k picks are always distinct.
+__global__ void route_kernel(const float *__restrict__ logits, int T, int X, int k,
+                             int32_t *__restrict__ topk, float *__restrict__ gate) {
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+    const float *l = logits + int64_t(t) * X;
+    int32_t *tk = topk + int64_t(t) * k;
+    float first = 0.f, sum = 0.f;
+    for (int r = 0; r < k; ++r) {
+      int best = -1;
+      float bv = 0.f;
+      for (int x = 0; x < X; ++x) {
+        bool taken = false;
+        for (int q = 0; q < r; ++q) taken |= tk[q] == x;
+        if (taken) continue;
+        float v = l[x];
+        if (v != v) v = -INFINITY;
+        if (best < 0 || v > bv) {
+          best = x;
+          bv = v;
+        }
+      }
+      tk[r] = best;
+      if (r == 0) first = bv;
+      const float w = expf(bv - first);
+      gate[int64_t(t) * k + r] = w;
+      sum += w;
+    }
+    const float inv = 1.f / sum;
+    for (int r = 0; r < k; ++r) gate[int64_t(t) * k + r] *= inv;
+  }
+}
+
+__global__ void moe_fill_i32(int32_t *p, int64_t n, int32_t v) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Per block of 256 atoms: rank of each atom among the earlier atoms of the
+// same type in the block, and the block's per-type counts.
+__global__ void __launch_bounds__(RANK_BLOCK) elem_rank_kernel(const int32_t *__restrict__ z, int N,
+                                                               int T, int32_t *__restrict__ local_rank,
+                                                               int32_t *__restrict__ blk_count,
+                                                               int32_t *__restrict__ flags) {
+  __shared__ int zs[RANK_BLOCK];
+  extern __shared__ int hist[];
+  const int i = blockIdx.x * RANK_BLOCK + threadIdx.x;
+  for (int t = threadIdx.x; t < T; t += RANK_BLOCK) hist[t] = 0;
+  int zi = -1;
+  if (i < N) {
+    zi = z[i];
+    if (zi < 0 || zi >= T) {
+      atomicOr(flags, 1);
+      zi = zi < 0 ? 0 : T - 1;
+    }
+  }
+  zs[threadIdx.x] = zi;
+  __syncthreads();
+  if (i < N) {
+    int r = 0;
+    for (int q = 0; q < int(threadIdx.x); ++q) r += zs[q] == zi;
+    local_rank[i] = r;
+    atomicAdd(&hist[zi], 1);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < T; t += RANK_BLOCK) blk_count[int64_t(blockIdx.x) * T + t] = hist[t];
+}
+
+// One workgroup: per-type block offsets (in place), type counts, the
+// (expert, type) offset table and the expert offsets.
+__global__ void __launch_bounds__(256) dispatch_tables_kernel(
+    int n_blocks, int T, int X, int k, const int32_t *__restrict__ topk,
+    int32_t *__restrict__ blk_count, int32_t *__restrict__ n_type, int32_t *__restrict__ pre,
+    int32_t *__restrict__ exp_count, int32_t *__restrict__ exp_off) {
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < n_blocks; ++b) {
+      const int64_t o = int64_t(b) * T + t;
+      const int c = blk_count[o];
+      blk_count[o] = run;
+      run += c;
+    }
+    n_type[t] = run;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < X; x += blockDim.x) {
+    int run = 0;
+    for (int t = 0; t < T; ++t) {
+      pre[int64_t(x) * T + t] = run;
+      bool hit = false;
+      for (int r = 0; r < k; ++r) hit |= topk[t * k + r] == x;
+      if (hit) run += n_type[t];
+    }
+    exp_count[x] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int x = 0; x < X; ++x) {
+      exp_off[x] = run;
+      run += exp_count[x];
+    }
+    exp_off[X] = run;
+  }
+}
+
+__global__ void dispatch_scatter_kernel(const int32_t *__restrict__ z, int N, int T, int k,
+                                        const int32_t *__restrict__ topk,
+                                        const int32_t *__restrict__ local_rank,
+                                        const int32_t *__restrict__ blk_base,
+                                        const int32_t *__restrict__ pre,
+                                        const int32_t *__restrict__ exp_off,
+                                        int32_t *__restrict__ tok_atom, int32_t *__restrict__ slot) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  int t = z[i];
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+  const int rank = blk_base[int64_t(i / RANK_BLOCK) * T + t] + local_rank[i];
+  for (int r = 0; r < k; ++r) {
+    const int x = topk[t * k + r];
+    const int p = exp_off[x] + pre[int64_t(x) * T + t] + rank;
+    tok_atom[p] = i;
+    slot[int64_t(i) * k + r] = p;
+  }
+}
+
+// out_i = base_i + sum_r gate[z_i, r] * rows[slot(i, r)], r in rank order.
+__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ base,
+                                                      const float *__restrict__ rows,
+                                                      const int32_t *__restrict__ z,
+                                                      const float *__restrict__ gate,
+                                                      const int32_t *__restrict__ slot, int T, int k,
+                                                      int D, float *__restrict__ out) {
+  const int i = blockIdx.x;
+  int t = z[i];
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+  const int D4 = D >> 2;
+  for (int c = threadIdx.x; c < D4; c += blockDim.x) {
+    float4 acc = reinterpret_cast<const float4 *>(base + int64_t(i) * D)[c];
+    for (int r = 0; r < k; ++r) {
+      const float gv = gate[t * k + r];
+      const float4 y = reinterpret_cast<const float4 *>(rows + int64_t(slot[int64_t(i) * k + r]) * D)[c];
+      acc.x += gv * y.x;
+      acc.y += gv * y.y;
+      acc.z += gv * y.z;
+      acc.w += gv * y.w;
+    }
+    reinterpret_cast<float4 *>(out + int64_t(i) * D)[c] = acc;
+  }
+}
+
+// eps_i = h_i . w_r (one wavefront per atom).
+__global__ void __launch_bounds__(256) readout_eps_kernel(const float *__restrict__ h,
+                                                          const float *__restrict__ w, int N, int D,
+                                                          float *__restrict__ eps) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= N) return;
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  const float4 *hr = reinterpret_cast<const float4 *>(h + int64_t(i) * D);
+  const float4 *wr = reinterpret_cast<const float4 *>(w);
+  for (int c = lane; c < (D >> 2); c += 64) {
+    const float4 a = hr[c], b = wr[c];
+    acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+  if (lane == 0) eps[i] = acc;
+}
+
+// E_b = sum of eps over structure b, in float64 with a fixed reduction tree.
+__global__ void __launch_bounds__(256) readout_energy_kernel(const float *__restrict__ eps,
+                                                             const int32_t *__restrict__ struct_ptr,
+                                                             double *__restrict__ energy) {
+  __shared__ double part[256];
+  const int b = blockIdx.x;
+  const int lo = struct_ptr[b], hi = struct_ptr[b + 1];
+  double acc = 0.0;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) acc += double(eps[i]);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s >= 1; s >>= 1) {
+    if (int(threadIdx.x) < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) energy[b] = part[0];
+}
+
+}  // namespace
+
+int moe_route_dispatch(const int32_t *z, const float *logits, int N, int T, int X, int k,
+                       int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom,
+                       int32_t *slot, int32_t *local_rank, int32_t *blk_count, int32_t *n_type,
+                       int32_t *pre, int32_t *exp_count, int32_t *flags, hipStream_t stream) {
+  ProfScope ps(K_ROUTE_DISPATCH, stream);
+  route_kernel<<<dim3(unsigned(cdiv(T, 64))), dim3(64), 0, stream>>>(logits, T, X, k, topk, gate);
+  MLIP_LAUNCHED();
+  moe_fill_i32<<<1, 64, 0, stream>>>(flags, 1, 0);
+  MLIP_LAUNCHED();
+  const int n_blocks = int(cdiv(N, RANK_BLOCK));
+  if (N > 0) {
+    elem_rank_kernel<<<dim3(unsigned(n_blocks)), dim3(RANK_BLOCK), size_t(T) * sizeof(int), stream>>>(
+        z, N, T, local_rank, blk_count, flags);
+    MLIP_LAUNCHED();
+  }
+  dispatch_tables_kernel<<<1, 256, 0, stream>>>(n_blocks, T, X, k, topk, blk_count, n_type, pre,
+                                                exp_count, exp_off);
+  MLIP_LAUNCHED();
+  if (N > 0) {
+    dispatch_scatter_kernel<<<dim3(unsigned(cdiv(N, 256))), dim3(256), 0, stream>>>(
+        z, N, T, k, topk, local_rank, blk_count, pre, exp_off, tok_atom, slot);
+    MLIP_LAUNCHED();
+  }
+  return MLIP_OK;
+}
+
+int moe_combine(const float *base, const float *rows, const int32_t *z, const float *gate,
+                const int32_t *slot, int N, int T, int k, int D, float *out, hipStream_t stream) {
+  if (N <= 0) return MLIP_OK;
+  ProfScope ps(K_COMBINE, stream);
+  const int threads = D / 4 >= 256 ? 256 : (D / 4 >= 128 ? 128 : 64);
+  combine_kernel<<<dim3(unsigned(N)), dim3(threads), 0, stream>>>(base, rows, z, gate, slot, T, k, D,
+                                                                   out);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, int B, int D,
+            float *eps, double *energy, hipStream_t stream) {
+  ProfScope ps(K_READOUT, stream);
+  if (N > 0) {
+    readout_eps_kernel<<<dim3(unsigned(cdiv(N, 4))), dim3(256), 0, stream>>>(h, w_r, N, D, eps);
+    MLIP_LAUNCHED();
+  }
+  readout_energy_kernel<<<dim3(unsigned(B)), dim3(256), 0, stream>>>(eps, struct_ptr, energy);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+}  // namespace mlip

@@ -1,0 +1,289 @@
+"""Python binding of libmlip.so (the C ABI in include/mlip.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the current HIP stream to
+the C entry point of the same name, and turns a negative status into an
+exception.  Nothing here computes any part of the block; when the library is
+missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmlip.so")
+
+MLIP_OK = 0
+MLIP_ERR_INVALID = -1
+MLIP_ERR_CAPACITY = -2
+MLIP_ERR_UNSUPPORTED = -3
+MLIP_ERR_HIP = -4
+MLIP_ERR_INPUT = -5
+N_RBF = 16
+
+
+class MlipError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mlip error {code}: {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with "
+                      f"`python -m element_routed_moe_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+_p, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+_SIGS = {
+    "mlip_last_error": (C.c_char_p, []),
+    "mlip_version": (C.c_int, []),
+    "mlip_graph_workspace_size": (_sz, [_i32, _i32]),
+    "mlip_build_graph": (C.c_int, [_p, _p, _p, _i32, _i32, _f32, _i64, _p, _p, _p, _p, _p,
+                                   C.POINTER(C.c_int64), _p, _sz, _p]),
+    "mlip_aggregate_workspace_size": (_sz, [_i32, _i32]),
+    "mlip_aggregate": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+                                 _p, _p, _p, _p, _sz, _p]),
+    "mlip_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "mlip_moe_forward": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_moe_status": (C.c_int, [_p, C.POINTER(C.c_int32), _p]),
+    "mlip_readout": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
+    "mlip_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "mlip_block_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
+                                 _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _f32, _p, _p, _p, _p, _sz, _p]),
+    "mlip_profile_enable": (C.c_int, [C.c_int]),
+    "mlip_profile_reset": (C.c_int, []),
+    "mlip_profile_count": (C.c_int, []),
+    "mlip_profile_get": (C.c_int, [C.c_int, C.POINTER(C.c_char_p), C.POINTER(C.c_int64),
+                                   C.POINTER(C.c_double)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(rc: int):
+    if rc != MLIP_OK:
+        raise MlipError(rc, _lib.mlip_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmlip must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------- entry points
+def mlip_build_graph(pos, cell, struct_ptr, cutoff: float, edge_capacity: Optional[int] = None,
+                     ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Periodic radius graph (CSR by receiver).  Returns row_ptr, src, shift, rev, geom, n_edges."""
+    dev = pos.device
+    N, B = int(pos.shape[0]), int(cell.shape[0])
+    if ws is None:
+        ws = _ws(_lib.mlip_graph_workspace_size(N, B), dev)
+    cap = int(edge_capacity) if edge_capacity is not None else max(64 * N, 1)
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        src = torch.empty(cap, dtype=torch.int32, device=dev)
+        shift = torch.empty((cap, 4), dtype=torch.int8, device=dev)
+        rev = torch.empty(cap, dtype=torch.int32, device=dev)
+        geom = torch.empty((cap, 4), dtype=torch.float32, device=dev)
+        ne = C.c_int64(0)
+        rc = _lib.mlip_build_graph(_ptr(pos), _ptr(cell), _ptr(struct_ptr), N, B, float(cutoff), cap,
+                                   _ptr(row_ptr), _ptr(src), _ptr(shift), _ptr(rev), _ptr(geom),
+                                   C.byref(ne), _ptr(ws), ws.numel(), _stream())
+        if rc == MLIP_ERR_CAPACITY:
+            cap = int(ne.value)
+            continue
+        _check(rc)
+        E = int(ne.value)
+        return dict(row_ptr=row_ptr, src=src[:E], shift=shift[:E], rev=rev[:E], geom=geom[:E],
+                    n_edges=E)
+    raise MlipError(MLIP_ERR_CAPACITY, "edge capacity could not be met")
+
+
+def mlip_aggregate(graph, h, W_e, W_d, W_u, cutoff: float, out: Optional[Dict] = None,
+                   ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(h.shape[0]), int(h.shape[1])
+    De = int(W_e.shape[1])
+    E = int(graph["n_edges"])
+    dev = h.device
+    if out is None:
+        out = dict(e=torch.empty((E, De), dtype=torch.float32, device=dev),
+                   s=torch.empty((N, De), dtype=torch.float32, device=dev),
+                   u=torch.empty((N, Dn), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = _ws(_lib.mlip_aggregate_workspace_size(N, De), dev)
+    _check(_lib.mlip_aggregate(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                               _ptr(h), _ptr(W_e), _ptr(W_d), _ptr(W_u), int(W_e.shape[0]), De, Dn,
+                               float(cutoff), _ptr(out["e"]), _ptr(out["s"]), _ptr(out["u"]),
+                               _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_moe_forward(u, z, logits, W1, W2, top_k: int, out: Optional[Dict] = None,
+                     ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(u.shape[0]), int(u.shape[1])
+    T, X = int(logits.shape[0]), int(logits.shape[1])
+    H = int(W1.shape[2])
+    k = int(top_k)
+    dev = u.device
+    if out is None:
+        out = dict(topk=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   exp_off=torch.empty(X + 1, dtype=torch.int32, device=dev),
+                   tok_atom=torch.empty(N * k, dtype=torch.int32, device=dev),
+                   slot=torch.empty((N, k), dtype=torch.int32, device=dev),
+                   P=torch.empty((N * k, H), dtype=torch.float32, device=dev),
+                   h_out=torch.empty((N, Dn), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = _ws(_lib.mlip_moe_workspace_size(N, T, X, k, Dn, H), dev)
+    out["ws"] = ws
+    _check(_lib.mlip_moe_forward(_ptr(u), _ptr(z), _ptr(logits), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
+                                 _ptr(out["topk"]), _ptr(out["gate"]), _ptr(out["exp_off"]),
+                                 _ptr(out["tok_atom"]), _ptr(out["slot"]), _ptr(out["P"]),
+                                 _ptr(out["h_out"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_moe_status(ws: torch.Tensor) -> bool:
+    """True when the last MoE forward with this workspace saw an out-of-range element type."""
+    bad = C.c_int32(0)
+    _check(_lib.mlip_moe_status(_ptr(ws), C.byref(bad), _stream()))
+    return bool(bad.value)
+
+
+def mlip_readout(h_out, w_r, struct_ptr, out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(h_out.shape[0]), int(h_out.shape[1])
+    B = int(struct_ptr.shape[0]) - 1
+    dev = h_out.device
+    if out is None:
+        out = dict(eps=torch.empty(N, dtype=torch.float32, device=dev),
+                   energy=torch.empty(B, dtype=torch.float64, device=dev))
+    _check(_lib.mlip_readout(_ptr(h_out), _ptr(w_r), _ptr(struct_ptr), N, B, Dn, _ptr(out["eps"]),
+                             _ptr(out["energy"]), _stream()))
+    return out
+
+
+def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top_k: int,
+                   grad_out, out: Optional[Dict] = None,
+                   ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(grad_out.shape[0]), int(grad_out.shape[1])
+    De = int(W_e.shape[1])
+    H = int(W1.shape[2])
+    X = int(W1.shape[0])
+    T = int(moe["gate"].shape[0])
+    E = int(graph["n_edges"])
+    dev = grad_out.device
+    if out is None:
+        out = dict(grad_h=torch.empty((N, Dn), dtype=torch.float32, device=dev),
+                   grad_pos=torch.empty((N, 3), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = _ws(_lib.mlip_vjp_workspace_size(N, top_k, De, Dn, H), dev)
+    _check(_lib.mlip_block_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                               _ptr(agg["e"]), _ptr(agg["s"]), _ptr(z), _ptr(moe["gate"]),
+                               _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]), _ptr(moe["slot"]),
+                               _ptr(moe["P"]), _ptr(W_e), _ptr(W_d), _ptr(W_u), _ptr(W1), _ptr(W2),
+                               int(W_e.shape[0]), De, Dn, H, T, X, int(top_k), float(cutoff),
+                               _ptr(grad_out), _ptr(out["grad_h"]), _ptr(out["grad_pos"]),
+                               _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ timing
+def profile_enable(on: bool = True):
+    _check(_lib.mlip_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check(_lib.mlip_profile_reset())
+
+
+def profile_read() -> Dict[str, Dict[str, float]]:
+    res = {}
+    for i in range(_lib.mlip_profile_count()):
+        name = C.c_char_p()
+        n = C.c_int64()
+        ms = C.c_double()
+        _check(_lib.mlip_profile_get(i, C.byref(name), C.byref(n), C.byref(ms)))
+        res[name.value.decode()] = dict(launches=int(n.value), total_ms=float(ms.value))
+    return res
+
+
+# ------------------------------------------------------------ one block step
+class Block:
+    """Device-resident inputs and buffers of one interaction block.
+
+    ``step()`` runs the whole path on the current stream: radius graph,
+    aggregation, mixture of experts, readout and the input gradient for the
+    given upstream gradient.
+    """
+
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None):
+        def dev(x, dt=None):
+            t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
+            return t.to(device=device, dtype=dt or t.dtype).contiguous()
+
+        self.device = device
+        self.pos = dev(inputs["pos"], torch.float32)
+        self.cell = dev(inputs["cell"], torch.float32)
+        self.struct_ptr = dev(inputs["struct_ptr"], torch.int32)
+        self.z = dev(inputs["z"], torch.int32)
+        self.h = dev(inputs["h"], torch.float32)
+        self.logits = dev(inputs["logits"], torch.float32)
+        self.W_e = dev(inputs["W_e"], torch.float32)
+        self.W_d = dev(inputs["W_d"], torch.float32)
+        self.W_u = dev(inputs["W_u"], torch.float32)
+        self.W1 = dev(inputs["W1"], torch.float32)
+        self.W2 = dev(inputs["W2"], torch.float32)
+        self.w_r = dev(inputs["w_r"], torch.float32)
+        self.cutoff = float(inputs["cutoff"])
+        self.top_k = int(inputs["top_k"])
+        if grad_out is None:
+            grad_out = self.w_r.expand(self.h.shape[0], -1)
+        self.grad_out = dev(grad_out, torch.float32)
+        N, Dn = self.h.shape
+        De, H = self.W_e.shape[1], self.W1.shape[2]
+        T, X = self.logits.shape
+        B = self.cell.shape[0]
+        self.ws_graph = _ws(_lib.mlip_graph_workspace_size(N, B), device)
+        self.ws_agg = _ws(_lib.mlip_aggregate_workspace_size(N, De), device)
+        self.ws_moe = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
+        self.ws_vjp = _ws(_lib.mlip_vjp_workspace_size(N, self.top_k, De, Dn, H), device)
+        self.edge_capacity = None
+        self.graph = self.agg = self.moe = self.ro = self.vjp = None
+
+    def step(self):
+        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
+                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
+        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
+            self.edge_capacity = g["n_edges"]
+        reuse = self.agg if (self.agg is not None and self.agg["e"].shape[0] == g["n_edges"]) else None
+        self.graph = g
+        self.agg = mlip_aggregate(g, self.h, self.W_e, self.W_d, self.W_u, self.cutoff,
+                                  out=reuse, ws=self.ws_agg)
+        self.moe = mlip_moe_forward(self.agg["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
+                                    out=self.moe, ws=self.ws_moe)
+        self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
+        self.vjp = mlip_block_vjp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u,
+                                  self.W1, self.W2, self.cutoff, self.top_k, self.grad_out,
+                                  out=self.vjp, ws=self.ws_vjp)
+        return self

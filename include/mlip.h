@@ -1,0 +1,209 @@
+/*
+ * mlip.h - C ABI of the MI355X (gfx950) library for one MatRIS-MoE
+ * interaction block: periodic radius graph, neighbour aggregation,
+ * element-routed top-k mixture of experts, readout, and the input gradient
+ * (VJP) that conservative forces need.
+ *
+ * Sources (cited by page title and section):
+ *   [news]   ScienceAI news article on MatRIS-MoE and Janus, sections on the
+ *            model architecture and on conservative training.
+ *   [review] xllm-io review of "Breaking the Training Barrier of
+ *            Billion-Parameter Universal Machine Learning Interatomic
+ *            Potentials": 3.1 (architecture, Fig. 1, Table II),
+ *            3.2 (sparse MoE design), 3.3 (forces and stresses),
+ *            3.5 (kernel notes).
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers unless marked (host).  The caller
+ *     owns every buffer; the library allocates no device memory.  Scratch
+ *     memory is passed as (ws, ws_bytes); its size comes from the matching
+ *     mlip_*_workspace_size() call and it must be 256-byte aligned.
+ *   - stream is a hipStream_t passed as void* (NULL = default stream).  All
+ *     work is enqueued asynchronously on it; only mlip_build_graph waits for
+ *     the stream (once, to learn the number of edges).
+ *   - Floating point data are float32, row-major.  Weight matrices are
+ *     stored "in x out": y = x @ W.
+ *   - Feature widths (d_edge, d_node, d_hidden) must be multiples of 4 and
+ *     n_rbf must be 16.
+ *   - Return value: MLIP_OK or a negative MLIP_ERR_* code; then
+ *     mlip_last_error() returns a message (thread-local).  Arguments are
+ *     validated on the host before anything is enqueued, so an error return
+ *     leaves the outputs untouched unless stated otherwise.
+ *   - Calls on one stream are ordered; calls that share a workspace must
+ *     not run concurrently on different streams.
+ */
+#ifndef MLIP_H
+#define MLIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLIP_OK 0
+#define MLIP_ERR_INVALID (-1)     /* bad argument (null pointer, bad size, ...) */
+#define MLIP_ERR_CAPACITY (-2)    /* output buffer too small; required size reported */
+#define MLIP_ERR_UNSUPPORTED (-3) /* valid input outside what the kernels handle */
+#define MLIP_ERR_HIP (-4)         /* HIP runtime error */
+#define MLIP_ERR_INPUT (-5)       /* input data rejected by a device-side check */
+
+#define MLIP_N_RBF 16
+
+const char *mlip_last_error(void);
+int mlip_version(void);
+
+/* ------------------------------------------------------------------------
+ * Periodic radius graph ([review] 3.1, Fig. 1(a): the structure is turned
+ * into a graph under periodic repetition of its cell).
+ *
+ * An edge i <- j with integer lattice shift S = (S0,S1,S2) exists when i and
+ * j belong to the same structure, (j,S) != (i,0) and
+ *     d  = (x_j - x_i) + ((S0*C[0] + S1*C[1]) + S2*C[2])      (float64)
+ *     d2 = (d.x*d.x + d.y*d.y) + d.z*d.z  <  cutoff*cutoff    (float64)
+ * evaluated in float64 from the float32 inputs in exactly this order with
+ * no fused multiply-add, so the edge set is reproducible bit for bit.
+ *
+ * pos        [n_atoms,3]      Cartesian positions; atom i of structure b must
+ *                             satisfy 0 <= pos[i][a] < C_b[a][a] (wrapped).
+ * cell       [n_structs,3,3]  rows are the lattice vectors; only orthorhombic
+ *                             cells (zero off-diagonal) are supported.
+ * struct_ptr [n_structs+1]    atoms of structure b are struct_ptr[b] ..
+ *                             struct_ptr[b+1]-1 (non-decreasing, 0 .. n_atoms).
+ * cutoff     r_c > 0 in the units of pos.
+ * edge_capacity              length of src/rev (and /4 of shift, geom).
+ *
+ * Outputs (edges sorted by receiver i, then sender j, then S0, S1, S2):
+ * row_ptr [n_atoms+1]  CSR offsets, row i = edges with receiver i.
+ * src     [E]          sender j of each edge.
+ * shift   [E,4] int8   (S0, S1, S2, 0).
+ * rev     [E]          index of the reverse edge (j <- i, -S).
+ * geom    [E,4] f32    (d.x, d.y, d.z, |d|) rounded to float32.
+ * n_edges (host)       E.
+ *
+ * Errors: MLIP_ERR_CAPACITY when E > edge_capacity (then *n_edges = E and
+ * only row_ptr has been written); MLIP_ERR_INPUT for positions outside
+ * their cell or non-orthorhombic / non-positive cells (host message says
+ * which); MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges or a
+ * shift exceeds +-127.  Synchronises the stream once.
+ * ------------------------------------------------------------------------ */
+size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs);
+int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,
+                     int32_t n_atoms, int32_t n_structs, float cutoff,
+                     int64_t edge_capacity, int32_t *row_ptr, int32_t *src,
+                     int8_t *shift, int32_t *rev, float *geom, int64_t *n_edges,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Edge embedding + neighbour aggregation + projections ([news] pair
+ * distances are embedded; [review] 3.5: gather neighbour features, modulate
+ * them, reduce onto the receiver).
+ *
+ *   e_e = f_c(r_e) * (phi(r_e) @ W_e)              [E, d_edge]
+ *        phi_k(r) = exp(-gamma (r - mu_k)^2), mu_k = k r_c/15,
+ *        gamma = 15^2/(2 r_c^2), f_c(r) = (cos(pi r/r_c)+1)/2 for r < r_c,
+ *        else 0 (r = geom[e].w)
+ *   s   = h @ W_d                                  [N, d_edge]
+ *   a_i = sum_{e in row i} e_e * s_src(e)          (elementwise)
+ *   u   = h + a @ W_u                              [N, d_node]
+ *
+ * row_ptr/src/geom: graph from mlip_build_graph (n_edges = row_ptr[N]).
+ * h [N,d_node], W_e [16,d_edge], W_d [d_node,d_edge], W_u [d_edge,d_node].
+ * Outputs e, s (kept for the VJP) and u.  Workspace holds a [N, d_edge].
+ * ------------------------------------------------------------------------ */
+size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge);
+int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                   int32_t n_atoms, int64_t n_edges, const float *h, const float *W_e,
+                   const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge,
+                   int32_t d_node, float cutoff, float *e, float *s, float *u,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Feature-update mixture of experts with static element-type routing
+ * ([news], [review] 3.2: each element type activates its own top-k experts,
+ * independently of the coordinates).
+ *
+ *   topk[t,:] = the k experts with the largest logits[t,:] (ties -> lower
+ *               index), in decreasing order; gate[t,:] = softmax of those k
+ *               logits.
+ *   tokens (i, r) are grouped by (expert, element, atom):
+ *     exp_off [X+1]  start of each expert's tokens,
+ *     tok_atom[N*k]  atom of each token in that order,
+ *     slot    [N,k]  position of token (i, r).
+ *   P = u[tok_atom] @ W1[x]  per expert x         [N*k, d_hidden] (kept)
+ *   h_out_i = u_i + sum_r gate[z_i,r] * (silu(P) @ W2[x])[slot(i,r)]
+ *
+ * u [N,d_node], z [N] element types in [0,n_types), logits [T,X],
+ * W1 [X,d_node,d_hidden], W2 [X,d_hidden,d_node].  Outputs topk [T,k] i32,
+ * gate [T,k], exp_off, tok_atom, slot, P (all kept for the VJP) and h_out.
+ * Element types outside [0,n_types) are clamped on the device and reported
+ * by mlip_moe_status().
+ * ------------------------------------------------------------------------ */
+size_t mlip_moe_workspace_size(int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                               int32_t top_k, int32_t d_node, int32_t d_hidden);
+int mlip_moe_forward(const float *u, const int32_t *z, const float *logits,
+                     const float *W1, const float *W2, int32_t n_atoms, int32_t n_types,
+                     int32_t n_experts, int32_t top_k, int32_t d_node, int32_t d_hidden,
+                     int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom,
+                     int32_t *slot, float *P, float *h_out, void *ws, size_t ws_bytes,
+                     void *stream);
+/* Waits for the stream; *bad_types (host) = 1 if the last mlip_moe_forward
+ * with this workspace saw an element type outside [0,n_types), else 0. */
+int mlip_moe_status(const void *ws, int32_t *bad_types, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Readout ([review] 3.1 Fig. 1(b) names a readout; the reading here is
+ * linear): eps_i = h_out_i . w_r, energy_b = sum_{i in b} eps_i in float64.
+ * eps [N] f32, energy [n_structs] f64.
+ * ------------------------------------------------------------------------ */
+int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr,
+                 int32_t n_atoms, int32_t n_structs, int32_t d_node, float *eps,
+                 double *energy, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Input gradient of the block ([news] conservative training; [review] 3.3:
+ * forces are obtained by differentiating the energy).  Given
+ * grad_out = dL/dh_out [N,d_node]:
+ *   ubar = grad_out + sum_r gate * ((grad_out @ W2^T) * silu'(P)) @ W1^T
+ *   abar = ubar @ W_u^T
+ *   grad_h = ubar + sbar @ W_d^T,  sbar_j = sum_{e: src(e)=j} e_e * abar_recv(e)
+ *   c_e = sum_c (abar_recv * s_src)_c * d e_e,c / d r_e
+ *   grad_pos_i = dL/dx_i = -sum_{e in row i} (c_e + c_rev(e)) d_e/|d_e|
+ * Routing depends only on the element types, so gates carry no gradient.
+ * With grad_out rows all equal to w_r, grad_pos = dE/dx and the forces are
+ * -grad_pos.
+ *
+ * Inputs are the graph, e and s from mlip_aggregate, the kept MoE state
+ * from mlip_moe_forward and the weights.  Outputs grad_h [N,d_node],
+ * grad_pos [N,3].
+ * ------------------------------------------------------------------------ */
+size_t mlip_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_edge,
+                               int32_t d_node, int32_t d_hidden);
+int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                   int32_t n_atoms, int64_t n_edges, const float *e, const float *s,
+                   const int32_t *z, const float *gate, const int32_t *exp_off,
+                   const int32_t *tok_atom, const int32_t *slot, const float *P,
+                   const float *W_e, const float *W_d, const float *W_u, const float *W1,
+                   const float *W2, int32_t n_rbf, int32_t d_edge, int32_t d_node,
+                   int32_t d_hidden, int32_t n_types, int32_t n_experts, int32_t top_k,
+                   float cutoff, const float *grad_out, float *grad_h, float *grad_pos,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing.  When enabled, every kernel launch of the library is
+ * bracketed by HIP events on its stream; mlip_profile_get() waits for the
+ * recorded events and returns, for the kernel class with index idx, its name
+ * (static string), the number of launches and their summed duration in
+ * milliseconds.  Classes are numbered 0 .. mlip_profile_count()-1.  Not
+ * thread-safe; meant for benchmarks.
+ * ------------------------------------------------------------------------ */
+int mlip_profile_enable(int enable);
+int mlip_profile_reset(void);
+int mlip_profile_count(void);
+int mlip_profile_get(int idx, const char **name, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLIP_H */

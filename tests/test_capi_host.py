@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every entry point declared in include/mlip.h, and rejects bad arguments
+before touching the device (no kernel is launched by these tests)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlip.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlip_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mlip():
+    from element_routed_moe_amd import mlip as m
+    return m
+
+
+def test_exports_every_declared_symbol(mlip):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(mlip._lib, n), n
+        assert n in mlip.EXPORTED, n
+    assert mlip._lib.mlip_version() == 1
+
+
+def test_workspace_sizes_are_monotone(mlip):
+    L = mlip._lib
+    assert L.mlip_graph_workspace_size(4096, 32) < L.mlip_graph_workspace_size(8192, 32)
+    a = L.mlip_aggregate_workspace_size(4096, 384)
+    assert a >= 4096 * 384 * 4
+    m = L.mlip_moe_workspace_size(4096, 16, 72, 4, 2560, 2560)
+    assert m >= 2 * 4096 * 4 * 2560 * 4          # SiLU activations + expert outputs
+    v = L.mlip_vjp_workspace_size(4096, 4, 384, 2560, 2560)
+    assert v >= 2 * 4096 * 4 * 2560 * 4
+    for s in (a, m, v):
+        assert s % 256 == 0
+
+
+def _err(mlip, rc, code):
+    assert rc == code, (rc, mlip._lib.mlip_last_error())
+    return mlip._lib.mlip_last_error().decode()
+
+
+def test_build_graph_rejects_bad_args(mlip):
+    L = mlip._lib
+    ne = C.c_int64(0)
+    fake = C.c_void_p(256)        # never dereferenced: validation fails first
+    rc = L.mlip_build_graph(fake, fake, fake, 10, 0, 5.0, 100, fake, fake, fake, fake, fake,
+                            C.byref(ne), fake, 1 << 20, None)
+    assert "n_structs" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_build_graph(fake, fake, fake, 10, 1, -1.0, 100, fake, fake, fake, fake, fake,
+                            C.byref(ne), fake, 1 << 20, None)
+    assert "cutoff" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_build_graph(fake, fake, fake, 10, 1, 5.0, 100, fake, fake, fake, fake, fake,
+                            C.byref(ne), fake, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+
+
+def test_aggregate_and_moe_reject_bad_args(mlip):
+    L = mlip._lib
+    f = C.c_void_p(256)
+    rc = L.mlip_aggregate(f, f, f, 10, 20, f, f, f, f, 8, 32, 64, 5.0, f, f, f, f, 1 << 30, None)
+    assert "n_rbf" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_aggregate(f, f, f, 10, 20, f, f, f, f, 16, 30, 64, 5.0, f, f, f, f, 1 << 30, None)
+    assert "d_edge" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_moe_forward(f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, f, f, f, f, f, f, f, 1 << 30, None)
+    assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_moe_forward(f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, f, f, f, f, f, None, 0, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_block_vjp(f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f, 16, 32, 64, 130,
+                          4, 8, 2, 5.0, f, f, f, f, 1 << 30, None)
+    assert "d_hidden" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+
+
+def test_profile_api_without_gpu(mlip):
+    names = list(mlip.profile_read())
+    assert "gemm_expert_up" in names and "edge_vjp" in names and len(names) == 11

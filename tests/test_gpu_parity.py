@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer outputs (graph, routing table, dispatch tables) must match bit for
+bit.  Floating-point outputs must satisfy
+    max |gpu - oracle| / max |oracle|  <=  2e-4
+per tensor, the bound the block is specified to (float32 arithmetic against
+a float64 oracle).
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+from element_routed_moe_amd import synth
+from oracle import block as OB
+from oracle import graph as OG
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+SMALL = ["tiny", "ragged", "celllist", "sparse", "top1"]
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mlip():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from element_routed_moe_amd import mlip as m
+    return m
+
+
+def rel(gpu, ref):
+    a = gpu.detach().cpu().numpy().astype(np.float64) if hasattr(gpu, "detach") else np.asarray(gpu, np.float64)
+    b = np.asarray(ref, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if b.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_full(name, upstream):
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    f = OB.block_forward(inp, g)
+    gup = synth.upstream_grad(cfg, inp, upstream)
+    v = OB.block_vjp(inp, g, f, gup.astype(np.float64))
+    tables = OB.dispatch_tables(inp["z"], f["topk"], cfg.n_experts)
+    return cfg, inp, g, f, v, gup, tables
+
+
+def run_gpu(mlip, inp, gup):
+    blk = mlip.Block(inp, device="cuda", grad_out=gup).step()
+    torch.cuda.synchronize()
+    return blk
+
+
+@pytest.mark.parametrize("name", SMALL + ["S_slice"])
+def test_graph_bit_exact(mlip, name):
+    cfg, inp, g, *_ = oracle_full(name, "energy")
+    _say(f"graph {name}: N={cfg.n_atoms} E={g['src'].size}")
+    dev = "cuda"
+    out = mlip.mlip_build_graph(torch.from_numpy(inp["pos"]).to(dev), torch.from_numpy(inp["cell"]).to(dev),
+                                torch.from_numpy(inp["struct_ptr"]).to(dev), float(inp["cutoff"]))
+    torch.cuda.synchronize()
+    assert out["n_edges"] == g["src"].size
+    assert np.array_equal(out["row_ptr"].cpu().numpy(), g["row_ptr"])
+    assert np.array_equal(out["src"].cpu().numpy(), g["src"])
+    sh = out["shift"].cpu().numpy()
+    assert np.array_equal(sh[:, :3].astype(np.int64), g["shift"]) and np.all(sh[:, 3] == 0)
+    assert np.array_equal(out["rev"].cpu().numpy(), g["rev"])
+    geo = out["geom"].cpu().numpy()
+    assert np.array_equal(geo, g["geom"]), np.max(np.abs(geo - g["geom"]))
+
+
+@pytest.mark.parametrize("name", SMALL + ["S_slice"])
+@pytest.mark.parametrize("upstream", ["energy", "random"])
+def test_block_parity(mlip, name, upstream):
+    cfg, inp, g, f, v, gup, (exp_off, tok_atom, slot) = oracle_full(name, upstream)
+    _say(f"block {name} upstream={upstream}: N={cfg.n_atoms} E={g['src'].size} "
+         f"De={cfg.d_edge} Dn={cfg.d_node} H={cfg.d_hidden} X={cfg.n_experts} k={cfg.top_k}")
+    blk = run_gpu(mlip, inp, gup)
+    # integer tables
+    assert np.array_equal(blk.moe["topk"].cpu().numpy(), f["topk"])
+    assert np.array_equal(blk.moe["exp_off"].cpu().numpy(), exp_off)
+    assert np.array_equal(blk.moe["tok_atom"].cpu().numpy(), tok_atom)
+    assert np.array_equal(blk.moe["slot"].cpu().numpy(), slot)
+    assert not mlip.mlip_moe_status(blk.ws_moe)
+    errs = {
+        "gate": rel(blk.moe["gate"], f["gate"]),
+        "e": rel(blk.agg["e"], f["e"]),
+        "s": rel(blk.agg["s"], f["s"]),
+        "u": rel(blk.agg["u"], f["u"]),
+        "h_out": rel(blk.moe["h_out"], f["h2"]),
+        "eps": rel(blk.ro["eps"], f["eps"]),
+        "energy": rel(blk.ro["energy"], f["E"]),
+        "grad_h": rel(blk.vjp["grad_h"], v["grad_h"]),
+        "grad_pos": rel(blk.vjp["grad_pos"], v["grad_pos"]),
+    }
+    # the kept pre-activations, in dispatch order
+    P_ref = np.concatenate([
+        (np.asarray(f["u"])[tok_atom[exp_off[x]:exp_off[x + 1]]] @ inp["W1"][x].astype(np.float64))
+        for x in range(cfg.n_experts)], axis=0) if cfg.n_atoms else np.zeros((0, cfg.d_hidden))
+    errs["P"] = rel(blk.moe["P"], P_ref)
+    _say(f"  errors {errs}")
+    bad = {k: e for k, e in errs.items() if not e <= TOL}
+    assert not bad, bad
+
+
+def test_deterministic(mlip):
+    cfg = synth.CONFIGS["ragged"]
+    inp = synth.make_inputs(cfg)
+    gup = synth.upstream_grad(cfg, inp, "random")
+    _say("determinism ragged")
+    a = run_gpu(mlip, inp, gup)
+    outs_a = [t.cpu().clone() for t in (a.agg["e"], a.agg["u"], a.moe["h_out"], a.vjp["grad_h"],
+                                        a.vjp["grad_pos"], a.ro["energy"])]
+    b = run_gpu(mlip, inp, gup)
+    outs_b = [t.cpu() for t in (b.agg["e"], b.agg["u"], b.moe["h_out"], b.vjp["grad_h"],
+                                b.vjp["grad_pos"], b.ro["energy"])]
+    for x, y in zip(outs_a, outs_b):
+        assert torch.equal(x, y)
+
+
+def test_empty_system(mlip):
+    _say("empty system")
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_inputs(cfg)
+    q = dict(inp)
+    q["pos"] = np.zeros((0, 3), np.float32)
+    q["struct_ptr"] = np.array([0, 0], np.int32)
+    q["z"] = np.zeros(0, np.int32)
+    q["h"] = np.zeros((0, cfg.d_node), np.float32)
+    blk = mlip.Block(q, device="cuda").step()
+    torch.cuda.synchronize()
+    assert blk.graph["n_edges"] == 0
+    assert blk.ro["energy"].cpu().numpy().tolist() == [0.0]
+    assert blk.vjp["grad_pos"].shape == (0, 3)
+
+
+def test_input_errors(mlip):
+    _say("input errors")
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_inputs(cfg)
+    dev = "cuda"
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    cell = torch.from_numpy(inp["cell"]).to(dev)
+    sp = torch.from_numpy(inp["struct_ptr"]).to(dev)
+    bad = pos.clone()
+    bad[3, 1] = 8.5                                # outside the 8 A cell
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_build_graph(bad, cell, sp, 5.0)
+    assert ei.value.code == mlip.MLIP_ERR_INPUT
+    skew = cell.clone()
+    skew[0, 1, 0] = 0.5
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_build_graph(pos, skew, sp, 5.0)
+    assert ei.value.code == mlip.MLIP_ERR_UNSUPPORTED
+    # a too-small edge capacity is reported with the required count, then met
+    g = mlip.mlip_build_graph(pos, cell, sp, 5.0, edge_capacity=10)
+    assert g["n_edges"] > 10
+    # element types outside [0, T) are clamped and reported
+    q = dict(inp)
+    q["z"] = inp["z"].copy()
+    q["z"][5] = 17
+    blk = mlip.Block(q, device="cuda").step()
+    assert mlip.mlip_moe_status(blk.ws_moe)
