@@ -1,0 +1,184 @@
+"""Throughput of one MatRIS-MoE interaction block (forward + force VJP) on one
+MI355X, in atoms/s, with the roofline position of the dominant kernel and the
+CPU oracle timed beside it.
+
+One step = the whole path on one batch of synthetic structures: periodic
+radius graph, edge embedding + aggregation, element-routed MoE (dispatch,
+expert GEMMs, combine), readout, and the input gradient (expert GEMMs
+transposed, aggregation transposed, edge/force part).  Inputs are resident in
+HBM before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S]
+
+Prints ONE JSON line.  ``--calibrate-copy`` instead runs a plain 1 GiB device
+copy (for scaling hardware byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "atoms/s per interaction block (fwd+force VJP) on 1 MI355X; % HBM/MFMA roofline"
+MFMA_FP32_PEAK_TFLOPS = 157.3      # MI355X dense FP32 matrix peak
+HBM_PEAK_GBS = 8000.0
+EXPERT_CLASSES = ("gemm_expert_up", "gemm_expert_down", "gemm_expert_vjp_down", "gemm_expert_vjp_up")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_expert_traffic_S.txt")
+
+
+def _kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "element_routed_moe_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """Bytes per launch from the committed hardware-counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256_16") != _kernel_source_hash():
+        return None
+    v = kv.get(f"{kernel}_bytes_per_launch")
+    return float(v) if v else None
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 28                       # 2^28 floats = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+
+
+def cpu_baseline(cfg, inp, n_structs: int):
+    """The float64 NumPy oracle on the first n_structs structures of the workload."""
+    import numpy as np
+    from oracle import block as OB
+    from oracle import graph as OG
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = int(inp["struct_ptr"][n_structs])
+    sub = dict(inp)
+    sub["pos"] = inp["pos"][:n]
+    sub["cell"] = inp["cell"][:n_structs]
+    sub["struct_ptr"] = inp["struct_ptr"][:n_structs + 1]
+    sub["z"] = inp["z"][:n]
+    sub["h"] = inp["h"][:n]
+    g_up = np.broadcast_to(inp["w_r"], (n, cfg.d_node)).astype(np.float64)
+    t0 = time.perf_counter()
+    gr = OG.radius_graph(sub["pos"], sub["cell"], sub["struct_ptr"], sub["cutoff"])
+    f = OB.block_forward(sub, gr)
+    OB.block_vjp(sub, gr, f, g_up)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "atoms/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_structs} of {cfg.n_structs} structures ({n} atoms, "
+                      f"{gr['src'].size} edges) of the {cfg.name} workload, float64 NumPy oracle, "
+                      f"graph + forward + VJP in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="S")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-structs", type=int, default=4)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the block would shard)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import numpy as np
+    import torch
+    from element_routed_moe_amd import mlip, synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = synth.CONFIGS[args.config]
+    inputs = synth.make_inputs(cfg)
+    blk = mlip.Block(inputs, device="cuda")
+    log(f"inputs resident for workload {cfg.name}: {cfg.n_atoms} atoms")
+    for _ in range(args.warmup):
+        blk.step()
+    torch.cuda.synchronize()
+    E = blk.graph["n_edges"]
+    log(f"warmup done ({args.warmup} steps, {E} edges)")
+
+    mlip.profile_reset()
+    mlip.profile_enable(True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        blk.step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mlip.profile_enable(False)
+    prof = mlip.profile_read()
+
+    ms_per_step = wall * 1e3 / args.steps
+    N = cfg.n_atoms
+    value = N * args.steps / wall
+
+    # dominant kernel: the expert GEMM class with the largest summed time
+    k = cfg.top_k
+    flops = {c: 2.0 * N * k * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES}
+    dom = max(EXPERT_CLASSES, key=lambda c: prof[c]["total_ms"])
+    avg_ms = prof[dom]["total_ms"] / max(prof[dom]["launches"], 1)
+    achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+            "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": _traffic(dom),
+            "avg_launch_ms": round(avg_ms, 4), "flop_per_launch": flops[dom]}
+
+    kernel_ms = {name: round(v["total_ms"] / args.steps, 4) for name, v in prof.items() if v["launches"]}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "atoms/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "atoms": N, "edges": int(E), "structures": cfg.n_structs,
+                   "cutoff": cfg.cutoff, "d_edge": cfg.d_edge, "d_node": cfg.d_node,
+                   "d_hidden": cfg.d_hidden, "experts": cfg.n_experts, "top_k": k,
+                   "element_types": cfg.n_types},
+        "edges_per_s": round(E * args.steps / wall, 1),
+        "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
+        "kernel_ms_per_step": kernel_ms,
+        "roofline": roof,
+    }
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs, min(args.cpu_structs, cfg.n_structs))
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

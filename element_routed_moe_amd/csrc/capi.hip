@@ -27,6 +27,7 @@ int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, 
 namespace {
 
 constexpr int kMaxTypes = 4096;
+constexpr int kMaxExperts = 1023;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -158,6 +159,7 @@ int mlip_moe_forward(const float *u, const int32_t *z, const float *logits, cons
   MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
   MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
                  "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
   MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
   if (int rc = check_width(d_node, "d_node")) return rc;
   if (int rc = check_width(d_hidden, "d_hidden")) return rc;
@@ -239,6 +241,7 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
   MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
                  "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
   MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
   if (int rc = check_width(d_edge, "d_edge")) return rc;
   if (int rc = check_width(d_node, "d_node")) return rc;

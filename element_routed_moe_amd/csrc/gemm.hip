@@ -11,18 +11,21 @@
 // gathers the A rows (the tokens of each expert) straight from the node
 // features, so no dispatched copy of the activations is ever written.
 //
-// Tiling: 128x128 output tile per 256-thread workgroup, 2x2 wavefronts of
-// 64x64, each as 2x2 blocks of v_mfma_f32_32x32x2_f32.  K advances 32 at a
-// time through double-buffered LDS with one barrier per step; the next
-// step's global loads are in flight while the current one is multiplied.
-// A and NT-B tiles sit in LDS as [row][k] (k contiguous, row stride 36
-// floats: 16-byte reads without bank conflicts); NN-B tiles as [k][n].
-// Each MFMA lane supplies the k-values k0 + 4*(lane/32) + q, q = 0..3, for
-// four consecutive MFMAs, so one 16-byte LDS read feeds four instructions.
+// Tiling: BM x BN output tile per 256-thread workgroup of 4 wavefronts in a
+// WM x WN grid; each wavefront owns (BM/WM) x (BN/WN) as 32x32 blocks of
+// v_mfma_f32_32x32x2_f32.  K advances BK at a time through double-buffered
+// LDS with one barrier per step; the next step's global loads are in flight
+// while the current one is multiplied.  A and NT-B tiles sit in LDS as
+// [row][k] (k contiguous, row stride BK+4 floats: 16-byte reads without bank
+// conflicts); NN-B tiles as [k][n].  Each MFMA lane supplies the k-values
+// k0 + 4*(lane/32) + q, q = 0..3, for four consecutive MFMAs, so one 16-byte
+// LDS read feeds four instructions.
 //
-// Tile order: workgroups are dealt round-robin to the 8 XCDs; each XCD is
-// given a contiguous range of tiles (m fastest), so the m-tiles that share a
-// weight tile (same expert, same n-tile) run on one XCD and share its L2.
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
+// given a contiguous range of tile indices; within it tiles run in groups of
+// 8 m-tiles x all n-tiles, m fastest.  The tiles resident on an XCD at one
+// time then share a few A row-blocks and a few expert weight tiles in its L2.
+// Expert row ranges are turned into tile ranges once per workgroup in LDS.
 #include "common.h"
 
 namespace mlip {
@@ -32,32 +35,72 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int THREADS = 256;
-constexpr int LDK = BK + 4;    // [row][k] tiles
-constexpr int LDN = BN + 4;    // [k][n] tiles
 constexpr int N_XCD = 8;
+constexpr int RASTER_M = 8;
+constexpr int MAX_GROUPS = 1024;
 
-__device__ inline float silu_f(float x) { return x / (1.f + __expf(-x)); }
-__device__ inline float dsilu_f(float x) {
-  const float sg = 1.f / (1.f + __expf(-x));
-  return sg * (1.f + x * (1.f - sg));
+// Exclusive scan over the 256 threads of the block (one value each).
+__device__ inline int block_scan_excl(int v, int *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += red[w];
+  return off + x - v;
 }
 
-template <bool BT, int EPI>
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG>
 __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
+  static_assert(WM * WN == 4, "four wavefronts");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  constexpr int LDK = BK + 4;
+  constexpr int LDN = BN + 4;
+  constexpr int KQ = BK / 4;                       // float4 per row of a k-slice
+  constexpr int A_LOADS = BM * KQ / THREADS;
+  constexpr int B_LOADS = BN * KQ / THREADS;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * KQ % THREADS == 0 && BN * KQ % THREADS == 0,
+                "load split");
+
   __shared__ float As[2][BM * LDK];
   __shared__ float Bs[2][BT ? (BN * LDK) : (BK * LDN)];
+  __shared__ int s_tiles[MAX_GROUPS + 1];
+  __shared__ int s_red[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
-  // ---- tile scheduling over (group, m-tile) x n-tile, XCD-contiguous ----
-  int Mt = 0;
+  // ---- tiles per group -> prefix in LDS ----
+  int Mt;
+  const int G = g.group_off ? g.n_groups : 1;
   if (g.group_off) {
-    for (int q = 0; q < g.n_groups; ++q) Mt += (g.group_off[q + 1] - g.group_off[q] + BM - 1) / BM;
+    constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
+    int cnt[PER], sum = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int gi = tid * PER + q;
+      cnt[q] = gi < G ? (g.group_off[gi + 1] - g.group_off[gi] + BM - 1) / BM : 0;
+      sum += cnt[q];
+    }
+    int run = block_scan_excl(sum, s_red);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int gi = tid * PER + q;
+      if (gi <= G) s_tiles[gi] = run;
+      run += cnt[q];
+    }
+    __syncthreads();
+    Mt = s_tiles[G];
   } else {
     Mt = (g.M + BM - 1) / BM;
   }
@@ -65,167 +108,232 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
   const int total = Mt * Nt;
   const int per = (total + N_XCD - 1) / N_XCD;
   const int L = blockIdx.x;
-  const int j = L / N_XCD, xcd = L - j * N_XCD;
-  if (j >= per) return;
-  const int T = xcd * per + j;
+  const int jx = L / N_XCD, xcd = L - jx * N_XCD;
+  if (jx >= per) return;
+  const int T = xcd * per + jx;
   if (T >= total) return;
-  const int nt = T / Mt;
-  int mt = T - nt * Mt;
-  int grp = 0, row0 = 0, rows = g.M;
+  const int group_size = RASTER_M * Nt;
+  const int first_m = (T / group_size) * RASTER_M;
+  const int gm = min(Mt - first_m, RASTER_M);
+  const int rr = T % group_size;
+  const int mt_glob = first_m + rr % gm;
+  const int nt = rr / gm;
+
+  int grp = 0, row0, rows;
   if (g.group_off) {
-    for (grp = 0; grp < g.n_groups; ++grp) {
-      const int lo = g.group_off[grp], cnt = g.group_off[grp + 1] - lo;
-      const int tiles = (cnt + BM - 1) / BM;
-      if (mt < tiles) {
-        row0 = lo + mt * BM;
-        rows = lo + cnt;
-        break;
-      }
-      mt -= tiles;
+    int lo = 0, hi = G;  // last group with s_tiles[grp] <= mt_glob
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tiles[mid] <= mt_glob) lo = mid;
+      else hi = mid;
     }
+    grp = lo;
+    row0 = g.group_off[grp] + (mt_glob - s_tiles[grp]) * BM;
+    rows = g.group_off[grp + 1];
   } else {
-    row0 = mt * BM;
+    row0 = mt_glob * BM;
+    rows = g.M;
   }
   const int n0 = nt * BN;
   const float *Bg = g.B + int64_t(grp) * g.b_group_stride;
 
   // ---- per-thread global load assignments ----
-  const int lr = tid >> 3;          // 0..31 row within a 32-row pass
-  const int lk = (tid & 7) * 4;     // k offset of the float4
-  const float *a_src[4];
-  bool a_ok[4];
+  const float *a_src[A_LOADS];
+  bool a_ok[A_LOADS];
+  int a_row[A_LOADS], a_kq[A_LOADS];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = row0 + lr + 32 * q;
+  for (int q = 0; q < A_LOADS; ++q) {
+    const int idx = tid + THREADS * q;
+    a_row[q] = idx / KQ;
+    a_kq[q] = (idx % KQ) * 4;
+    const int p = row0 + a_row[q];
     a_ok[q] = p < rows;
     int64_t arow = p;
     if (a_ok[q] && g.a_rows) arow = g.a_rows[p];
     a_src[q] = g.A + (a_ok[q] ? arow * g.lda : 0);
   }
-  const float *b_src[4];
-  bool b_ok[4];
-  int b_k[4];
+  const float *b_src[B_LOADS];
+  bool b_ok[B_LOADS];
+  int b_r[B_LOADS], b_c[B_LOADS];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < B_LOADS; ++q) {
+    const int idx = tid + THREADS * q;
     if (BT) {   // [N][K]: row n, float4 along k
-      const int n = n0 + lr + 32 * q;
+      b_r[q] = idx / KQ;
+      b_c[q] = (idx % KQ) * 4;
+      const int n = n0 + b_r[q];
       b_ok[q] = n < g.N;
       b_src[q] = Bg + (b_ok[q] ? int64_t(n) * g.ldb : 0);
-      b_k[q] = 0;
     } else {    // [K][N]: row k, float4 along n
-      const int n = n0 + (tid & 31) * 4;
+      b_r[q] = idx / (BN / 4);
+      b_c[q] = (idx % (BN / 4)) * 4;
+      const int n = n0 + b_c[q];
       b_ok[q] = n < g.N;
-      b_k[q] = (tid >> 5) + 8 * q;
       b_src[q] = Bg + (b_ok[q] ? n : 0);
     }
   }
 
-  floatx4 ra[4], rb[4];
+  // Loads are unconditional from always-valid addresses (row 0 / k 0 stand in
+  // for out-of-range elements); the zero mask is applied when the values are
+  // written to LDS, so nothing waits on a load before the multiply.
+  floatx4 ra[A_LOADS], rb[B_LOADS];
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto a_ok_k = [&](int q, int k0) { return a_ok[q] && k0 + a_kq[q] < g.K; };
+  auto b_ok_k = [&](int q, int k0) { return b_ok[q] && k0 + (BT ? b_c[q] : b_r[q]) < g.K; };
   auto load_global = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + lk;
-      ra[q] = (a_ok[q] && k < g.K) ? *reinterpret_cast<const floatx4 *>(a_src[q] + k)
-                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < A_LOADS; ++q) {
+      const int k = k0 + a_kq[q];
+      ra[q] = *reinterpret_cast<const floatx4 *>(a_src[q] + (a_ok_k(q, k0) ? k : 0));
+    }
+#pragma unroll
+    for (int q = 0; q < B_LOADS; ++q) {
       if (BT) {
-        rb[q] = (b_ok[q] && k < g.K) ? *reinterpret_cast<const floatx4 *>(b_src[q] + k)
-                                     : floatx4{0.f, 0.f, 0.f, 0.f};
+        const int k = k0 + b_c[q];
+        rb[q] = *reinterpret_cast<const floatx4 *>(b_src[q] + (b_ok_k(q, k0) ? k : 0));
       } else {
-        const int kb = k0 + b_k[q];
-        rb[q] = (b_ok[q] && kb < g.K)
-                    ? *reinterpret_cast<const floatx4 *>(b_src[q] + int64_t(kb) * g.ldb)
-                    : floatx4{0.f, 0.f, 0.f, 0.f};
+        const int kb = k0 + b_r[q];
+        rb[q] = *reinterpret_cast<const floatx4 *>(b_src[q] + (b_ok_k(q, k0) ? int64_t(kb) * g.ldb : 0));
       }
     }
   };
-  auto store_lds = [&](int buf) {
+  auto store_lds = [&](int buf, int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<floatx4 *>(&As[buf][(lr + 32 * q) * LDK + lk]) = ra[q];
-      if (BT) {
-        *reinterpret_cast<floatx4 *>(&Bs[buf][(lr + 32 * q) * LDK + lk]) = rb[q];
-      } else {
-        *reinterpret_cast<floatx4 *>(&Bs[buf][b_k[q] * LDN + (tid & 31) * 4]) = rb[q];
-      }
+    for (int q = 0; q < A_LOADS; ++q)
+      *reinterpret_cast<floatx4 *>(&As[buf][a_row[q] * LDK + a_kq[q]]) = a_ok_k(q, k0) ? ra[q] : zero4;
+#pragma unroll
+    for (int q = 0; q < B_LOADS; ++q) {
+      const floatx4 v = b_ok_k(q, k0) ? rb[q] : zero4;
+      if (BT) *reinterpret_cast<floatx4 *>(&Bs[buf][b_r[q] * LDK + b_c[q]]) = v;
+      else *reinterpret_cast<floatx4 *>(&Bs[buf][b_r[q] * LDN + b_c[q]]) = v;
     }
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < FM; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < FN; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
   const int nk = (g.K + BK - 1) / BK;
   load_global(0);
-  store_lds(0);
+  store_lds(0, 0);
   __syncthreads();
 
   const int l32 = lane & 31;
   const int kh = (lane >> 5) * 4;
+  // fragments of one 8-wide k group: FM A-values and FN B-values per k
+  struct Frag {
+    floatx4 a[FM], b[FN];
+  };
+  auto read_frag = [&](const float *Ab, const float *Bb, int kg, Frag &f) {
+#pragma unroll
+    for (int bi = 0; bi < FM; ++bi)
+      f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[(wm * WTM + bi * 32 + l32) * LDK + kg + kh]);
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) {
+      if (BT) {
+        f.b[bj] = *reinterpret_cast<const floatx4 *>(&Bb[(wn * WTN + bj * 32 + l32) * LDK + kg + kh]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f.b[bj][q] = Bb[(kg + kh + q) * LDN + wn * WTN + bj * 32 + l32];
+      }
+    }
+  };
+  // A wavefront whose rows all lie past the end of the group (the last,
+  // partial tile of an expert) leaves the matrix core to the other
+  // workgroup on its SIMD; it still loads and synchronises.
+  const bool wave_active = row0 + wm * WTM < rows;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_global((kt + 1) * BK);
     const float *Ab = As[cur];
     const float *Bb = Bs[cur];
+    if (!wave_active) {
+      if (kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
+      __syncthreads();
+      continue;
+    }
+    Frag f[2];
+    read_frag(Ab, Bb, 0, f[0]);
 #pragma unroll
-    for (int kg = 0; kg < BK; kg += 8) {
-      floatx4 af[2], bf[2];
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-        af[bi] = *reinterpret_cast<const floatx4 *>(&Ab[(wm * 64 + bi * 32 + l32) * LDK + kg + kh]);
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj) {
-        if (BT) {
-          bf[bj] = *reinterpret_cast<const floatx4 *>(&Bb[(wn * 64 + bj * 32 + l32) * LDK + kg + kh]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) bf[bj][q] = Bb[(kg + kh + q) * LDN + wn * 64 + bj * 32 + l32];
-        }
-      }
+    for (int kg = 0; kg < BK / 8; ++kg) {
+      // the next group's LDS reads are in flight while this group multiplies
+      if (kg + 1 < BK / 8) read_frag(Ab, Bb, (kg + 1) * 8, f[(kg + 1) & 1]);
+      const Frag &c = f[kg & 1];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < FM; ++bi)
 #pragma unroll
-          for (int bj = 0; bj < 2; ++bj)
-            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][q], bf[bj][q], acc[bi][bj], 0, 0, 0);
+          for (int bj = 0; bj < FN; ++bj)
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.a[bi][q], c.b[bj][q], acc[bi][bj], 0, 0, 0);
+#if GEMM_INTERLEAVE
+      if (kg + 1 < BK / 8) {
+        // one LDS read of the next group after each of the first MFMAs
+        constexpr int NR = FM + (BT ? FN : 4 * FN);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN - NR, 0);
+      }
+#endif
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+    if (kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
     __syncthreads();
   }
 
   // ---- epilogue: D[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 ----
+  // Residual / pre-activation values are fetched for the whole wave tile
+  // first (clamped, always-valid addresses), then combined and stored.
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
+  for (int bi = 0; bi < FM; ++bi) {
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-      const int col = n0 + wn * 64 + bj * 32 + l32;
-      if (col >= g.N) continue;
+    for (int bj = 0; bj < FN; ++bj) {
+      const int col = n0 + wn * WTN + bj * 32 + l32;
+      const bool col_ok = col < g.N;
+      const int colc = col_ok ? col : n0;
+      float rv[16];
+      if (EPI == EPI_RESID || EPI == EPI_DSILU) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = row0 + wm * WTM + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
+          const int pc = p < rows ? p : row0;
+          rv[r] = g.R[int64_t(pc) * g.ldr + colc];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int p = row0 + wm * 64 + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
-        if (p >= rows) continue;
-        float v = acc[bi][bj][r];
-        const int64_t o = int64_t(p) * g.ldc + col;
+        const int p = row0 + wm * WTM + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
+        const float v = acc[bi][bj][r];
+        float out, out2 = 0.f;
         if (EPI == EPI_STORE) {
-          g.C[o] = v;
+          out = v;
         } else if (EPI == EPI_RESID) {
-          g.C[o] = g.R[int64_t(p) * g.ldr + col] + v;
+          out = rv[r] + v;
         } else if (EPI == EPI_SILU) {
-          g.C[o] = v;
-          g.C2[o] = silu_f(v);
+          out = v;
+          out2 = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
         } else {
-          g.C[o] = v * dsilu_f(g.R[int64_t(p) * g.ldr + col]);
+          const float x = rv[r];
+          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-x));
+          out = v * (sg * (1.f + x * (1.f - sg)));
+        }
+        if (col_ok && p < rows) {
+          const int64_t o = int64_t(p) * g.ldc + col;
+          g.C[o] = out;
+          if (EPI == EPI_SILU) g.C2[o] = out2;
         }
       }
     }
   }
 }
 
-template <bool BT, int EPI>
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG>
 int launch_t(const GemmArgs &a, hipStream_t stream) {
   const int64_t mt_upper = cdiv(a.M, BM) + (a.group_off ? a.n_groups : 0);
   const int64_t total_upper = mt_upper * cdiv(a.N, BN);
@@ -235,9 +343,29 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
     set_error("GEMM too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
   }
-  gemm_kernel<BT, EPI><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
+  gemm_kernel<BM, BN, BK, WM, WN, BT, EPI, TAG><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
   MLIP_LAUNCHED();
   return MLIP_OK;
+}
+
+#ifndef GEMM_INTERLEAVE
+#define GEMM_INTERLEAVE 0
+#endif
+#ifndef EXPERT_TILE
+#define EXPERT_TILE 128, 128, 32, 2, 2
+#endif
+// Expert GEMMs: 128 x 128 tiles; in an expert's last tile a wavefront with no
+// rows skips its multiplies.
+template <bool BT, int EPI, int TAG>
+int launch_expert(const GemmArgs &a, hipStream_t s) {
+  return launch_t<EXPERT_TILE, BT, EPI, TAG>(a, s);
+}
+// Dense projections: 64 x 64 tiles when the output is narrow (enough
+// workgroups for 256 CUs), else 64 x 128.
+template <bool BT, int EPI, int TAG>
+int launch_dense(const GemmArgs &a, hipStream_t s) {
+  if (a.N <= 512) return launch_t<64, 64, 32, 2, 2, BT, EPI, TAG>(a, s);
+  return launch_t<64, 128, 32, 2, 2, BT, EPI, TAG>(a, s);
 }
 
 }  // namespace
@@ -248,14 +376,35 @@ int launch_gemm(const GemmArgs &a, bool bt, Epilogue epi, KClass cls, hipStream_
     set_error("GEMM dims must be multiples of 4 (K=%d N=%d)", a.K, a.N);
     return MLIP_ERR_UNSUPPORTED;
   }
-  ProfScope ps(cls, stream);
-  switch (epi) {
-    case EPI_STORE: return bt ? launch_t<true, EPI_STORE>(a, stream) : launch_t<false, EPI_STORE>(a, stream);
-    case EPI_RESID: return bt ? launch_t<true, EPI_RESID>(a, stream) : launch_t<false, EPI_RESID>(a, stream);
-    case EPI_SILU: return bt ? launch_t<true, EPI_SILU>(a, stream) : launch_t<false, EPI_SILU>(a, stream);
-    case EPI_DSILU: return bt ? launch_t<true, EPI_DSILU>(a, stream) : launch_t<false, EPI_DSILU>(a, stream);
+  if (a.group_off && a.n_groups > MAX_GROUPS) {
+    set_error("at most %d expert groups", MAX_GROUPS);
+    return MLIP_ERR_UNSUPPORTED;
   }
-  set_error("unknown epilogue");
+  ProfScope ps(cls, stream);
+  switch (cls) {
+    case K_GEMM_EXPERT_UP:
+      if (!bt && epi == EPI_SILU) return launch_expert<false, EPI_SILU, K_GEMM_EXPERT_UP>(a, stream);
+      break;
+    case K_GEMM_EXPERT_DOWN:
+      if (!bt && epi == EPI_STORE) return launch_expert<false, EPI_STORE, K_GEMM_EXPERT_DOWN>(a, stream);
+      break;
+    case K_GEMM_EXPERT_VJP_DOWN:
+      if (bt && epi == EPI_DSILU) return launch_expert<true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN>(a, stream);
+      break;
+    case K_GEMM_EXPERT_VJP_UP:
+      if (bt && epi == EPI_STORE) return launch_expert<true, EPI_STORE, K_GEMM_EXPERT_VJP_UP>(a, stream);
+      break;
+    case K_GEMM_DENSE:
+      if (!bt && epi == EPI_STORE) return launch_dense<false, EPI_STORE, K_GEMM_DENSE>(a, stream);
+      if (!bt && epi == EPI_RESID) return launch_dense<false, EPI_RESID, K_GEMM_DENSE>(a, stream);
+      if (bt && epi == EPI_STORE) return launch_dense<true, EPI_STORE, K_GEMM_DENSE>(a, stream);
+      if (bt && epi == EPI_RESID) return launch_dense<true, EPI_RESID, K_GEMM_DENSE>(a, stream);
+      break;
+    default:
+      break;
+  }
+  set_error("unsupported GEMM variant (class %d, transposed %d, epilogue %d)", int(cls), int(bt),
+            int(epi));
   return MLIP_ERR_INVALID;
 }
 

@@ -19,36 +19,59 @@ namespace {
 constexpr int RANK_BLOCK = 256;
 
 // top-k per element type (ties -> lower expert index) and softmax gates.
-// A NaN logit ranks below every number, so the k picks are always distinct.
-__global__ void route_kernel(const float *__restrict__ logits, int T, int X, int k,
-                             int32_t *__restrict__ topk, float *__restrict__ gate) {
-  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
-    const float *l = logits + int64_t(t) * X;
-    int32_t *tk = topk + int64_t(t) * k;
-    float first = 0.f, sum = 0.f;
-    for (int r = 0; r < k; ++r) {
-      int best = -1;
-      float bv = 0.f;
-      for (int x = 0; x < X; ++x) {
-        bool taken = false;
-        for (int q = 0; q < r; ++q) taken |= tk[q] == x;
-        if (taken) continue;
-        float v = l[x];
-        if (v != v) v = -INFINITY;
-        if (best < 0 || v > bv) {
-          best = x;
-          bv = v;
-        }
-      }
-      tk[r] = best;
-      if (r == 0) first = bv;
-      const float w = expf(bv - first);
-      gate[int64_t(t) * k + r] = w;
-      sum += w;
-    }
-    const float inv = 1.f / sum;
-    for (int r = 0; r < k; ++r) gate[int64_t(t) * k + r] *= inv;
+// One wavefront per type: the row of logits sits in registers (up to 16 per
+// lane), and each of the k picks is a wavefront arg-max.  A NaN logit ranks
+// below every number, so the k picks are always distinct.
+constexpr int ROUTE_MAX_X = 1024;
+__global__ void __launch_bounds__(64) route_kernel(const float *__restrict__ logits, int T, int X,
+                                                   int k, int32_t *__restrict__ topk,
+                                                   float *__restrict__ gate) {
+  constexpr int PER = ROUTE_MAX_X / 64;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (t >= T) return;
+  const float *l = logits + int64_t(t) * X;
+  float v[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int x = lane + 64 * c;
+    float w = x < X ? l[x] : -INFINITY;
+    v[c] = (w != w) ? -INFINITY : w;
   }
+  unsigned taken = 0;
+  float first = 0.f, sum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    int bx = 0x7fffffff;
+    float bv = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int x = lane + 64 * c;
+      if (x < X && !((taken >> c) & 1u) && (bx == 0x7fffffff || v[c] > bv)) {
+        bv = v[c];
+        bx = x;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 64);
+      const int ox = __shfl_xor(bx, d, 64);
+      if (ox != 0x7fffffff && (bx == 0x7fffffff || ov > bv || (ov == bv && ox < bx))) {
+        bv = ov;
+        bx = ox;
+      }
+    }
+    if ((bx & 63) == lane) taken |= 1u << (bx >> 6);
+    if (r == 0) first = bv;
+    const float w = expf(bv - first);
+    sum += w;
+    if (lane == 0) {
+      topk[int64_t(t) * k + r] = bx;
+      gate[int64_t(t) * k + r] = w;
+    }
+  }
+  __syncthreads();
+  const float inv = 1.f / sum;
+  for (int r = lane; r < k; r += 64) gate[int64_t(t) * k + r] *= inv;
 }
 
 __global__ void moe_fill_i32(int32_t *p, int64_t n, int32_t v) {
@@ -213,7 +236,7 @@ int moe_route_dispatch(const int32_t *z, const float *logits, int N, int T, int 
                        int32_t *slot, int32_t *local_rank, int32_t *blk_count, int32_t *n_type,
                        int32_t *pre, int32_t *exp_count, int32_t *flags, hipStream_t stream) {
   ProfScope ps(K_ROUTE_DISPATCH, stream);
-  route_kernel<<<dim3(unsigned(cdiv(T, 64))), dim3(64), 0, stream>>>(logits, T, X, k, topk, gate);
+  route_kernel<<<dim3(unsigned(T)), dim3(64), 0, stream>>>(logits, T, X, k, topk, gate);
   MLIP_LAUNCHED();
   moe_fill_i32<<<1, 64, 0, stream>>>(flags, 1, 0);
   MLIP_LAUNCHED();
