@@ -100,7 +100,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="S")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-structs", type=int, default=4)
+    ap.add_argument("--cpu-structs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 

@@ -49,7 +49,8 @@ int check_width(int32_t d, const char *name) {
 struct AggWs {
   float *a;
 };
-AggWs carve_agg(void *base, int64_t N, int64_t De, size_t *bytes) {
+AggWs carve_agg(void *base, int64_t N, int64_t De, int64_t Dn, size_t *bytes) {
+  (void)Dn;
   Carver c(base);
   AggWs w;
   w.a = c.take<float>(size_t(N * De));
@@ -100,9 +101,9 @@ using namespace mlip;
 extern "C" {
 
 // ------------------------------------------------------------- aggregate ---
-size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge) {
+size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node) {
   size_t b = 0;
-  carve_agg(nullptr, std::max(n_atoms, 0), std::max(d_edge, 0), &b);
+  carve_agg(nullptr, std::max(n_atoms, 0), std::max(d_edge, 0), std::max(d_node, 0), &b);
   return b;
 }
 
@@ -123,9 +124,10 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
   MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_e, 16) && aligned(W_d, 16) &&
                      aligned(W_u, 16) && aligned(e, 16) && aligned(s, 16) && aligned(u, 16),
                  "float arrays must be 16-byte aligned");
-  if (int rc = check_ws(ws, ws_bytes, mlip_aggregate_workspace_size(n_atoms, d_edge))) return rc;
+  if (int rc = check_ws(ws, ws_bytes, mlip_aggregate_workspace_size(n_atoms, d_edge, d_node)))
+    return rc;
   if (n_atoms == 0) return MLIP_OK;
-  AggWs w = carve_agg(ws, n_atoms, d_edge, nullptr);
+  AggWs w = carve_agg(ws, n_atoms, d_edge, d_node, nullptr);
 
   GemmArgs g;  // s = h @ W_d
   g.A = h; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s; g.ldc = d_edge;

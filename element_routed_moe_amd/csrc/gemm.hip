@@ -26,6 +26,8 @@
 // 8 m-tiles x all n-tiles, m fastest.  The tiles resident on an XCD at one
 // time then share a few A row-blocks and a few expert weight tiles in its L2.
 // Expert row ranges are turned into tile ranges once per workgroup in LDS.
+#include <algorithm>
+
 #include "common.h"
 
 namespace mlip {
@@ -242,20 +244,11 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
       }
     }
   };
-  // A wavefront whose rows all lie past the end of the group (the last,
-  // partial tile of an expert) leaves the matrix core to the other
-  // workgroup on its SIMD; it still loads and synchronises.
-  const bool wave_active = row0 + wm * WTM < rows;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_global((kt + 1) * BK);
     const float *Ab = As[cur];
     const float *Bb = Bs[cur];
-    if (!wave_active) {
-      if (kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
-      __syncthreads();
-      continue;
-    }
     Frag f[2];
     read_frag(Ab, Bb, 0, f[0]);
 #pragma unroll
@@ -270,18 +263,6 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int bj = 0; bj < FN; ++bj)
             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.a[bi][q], c.b[bj][q], acc[bi][bj], 0, 0, 0);
-#if GEMM_INTERLEAVE
-      if (kg + 1 < BK / 8) {
-        // one LDS read of the next group after each of the first MFMAs
-        constexpr int NR = FM + (BT ? FN : 4 * FN);
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN - NR, 0);
-      }
-#endif
     }
     if (kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
     __syncthreads();
@@ -348,17 +329,10 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
   return MLIP_OK;
 }
 
-#ifndef GEMM_INTERLEAVE
-#define GEMM_INTERLEAVE 0
-#endif
-#ifndef EXPERT_TILE
-#define EXPERT_TILE 128, 128, 32, 2, 2
-#endif
-// Expert GEMMs: 128 x 128 tiles; in an expert's last tile a wavefront with no
-// rows skips its multiplies.
+// Expert GEMMs: 128 x 128 tiles.
 template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
-  return launch_t<EXPERT_TILE, BT, EPI, TAG>(a, s);
+  return launch_t<128, 128, 32, 2, 2, BT, EPI, TAG>(a, s);
 }
 // Dense projections: 64 x 64 tiles when the output is narrow (enough
 // workgroups for 256 CUs), else 64 x 128.

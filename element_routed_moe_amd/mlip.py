@@ -44,7 +44,7 @@ _SIGS = {
     "mlip_graph_workspace_size": (_sz, [_i32, _i32]),
     "mlip_build_graph": (C.c_int, [_p, _p, _p, _i32, _i32, _f32, _i64, _p, _p, _p, _p, _p,
                                    C.POINTER(C.c_int64), _p, _sz, _p]),
-    "mlip_aggregate_workspace_size": (_sz, [_i32, _i32]),
+    "mlip_aggregate_workspace_size": (_sz, [_i32, _i32, _i32]),
     "mlip_aggregate": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                  _p, _p, _p, _p, _sz, _p]),
     "mlip_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -131,7 +131,7 @@ def mlip_aggregate(graph, h, W_e, W_d, W_u, cutoff: float, out: Optional[Dict] =
                    s=torch.empty((N, De), dtype=torch.float32, device=dev),
                    u=torch.empty((N, Dn), dtype=torch.float32, device=dev))
     if ws is None:
-        ws = _ws(_lib.mlip_aggregate_workspace_size(N, De), dev)
+        ws = _ws(_lib.mlip_aggregate_workspace_size(N, De, Dn), dev)
     _check(_lib.mlip_aggregate(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
                                _ptr(h), _ptr(W_e), _ptr(W_d), _ptr(W_u), int(W_e.shape[0]), De, Dn,
                                float(cutoff), _ptr(out["e"]), _ptr(out["s"]), _ptr(out["u"]),
@@ -265,7 +265,7 @@ class Block:
         T, X = self.logits.shape
         B = self.cell.shape[0]
         self.ws_graph = _ws(_lib.mlip_graph_workspace_size(N, B), device)
-        self.ws_agg = _ws(_lib.mlip_aggregate_workspace_size(N, De), device)
+        self.ws_agg = _ws(_lib.mlip_aggregate_workspace_size(N, De, Dn), device)
         self.ws_moe = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_vjp = _ws(_lib.mlip_vjp_workspace_size(N, self.top_k, De, Dn, H), device)
         self.edge_capacity = None

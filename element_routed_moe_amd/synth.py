@@ -134,6 +134,9 @@ S_SLICE = _reg(BlockConfig(
 SPARSE = _reg(BlockConfig(
     "sparse", [5, 3, 9], 3, 3.0, 3, 16, 36, 40, 44, 3, 3, seed=14, box=[30.0, 25.0, 28.0],
     description="dilute cells with isolated atoms (degree 0 rows), k = X"))
+WIDE_RAGGED = _reg(BlockConfig(
+    "wide_ragged", [150, 139], 2, 5.0, 5, 16, 100, 1028, 260, 5, 2, seed=16, box=[11.0, 10.5],
+    description="wide node features with ragged K/N tails (K-sliced projections)"))
 TOP1 = _reg(BlockConfig(
     "top1", [40, 33], 2, 4.0, 2, 16, 48, 68, 72, 5, 1, seed=15, box=[7.0, 6.5],
     description="top-1 routing (gate exactly 1), images because r_c > L/2"))

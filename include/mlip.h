@@ -112,7 +112,7 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
  * h [N,d_node], W_e [16,d_edge], W_d [d_node,d_edge], W_u [d_edge,d_node].
  * Outputs e, s (kept for the VJP) and u.  Workspace holds a [N, d_edge].
  * ------------------------------------------------------------------------ */
-size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge);
+size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node);
 int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom,
                    int32_t n_atoms, int64_t n_edges, const float *h, const float *W_e,
                    const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(mlip):
 def test_workspace_sizes_are_monotone(mlip):
     L = mlip._lib
     assert L.mlip_graph_workspace_size(4096, 32) < L.mlip_graph_workspace_size(8192, 32)
-    a = L.mlip_aggregate_workspace_size(4096, 384)
+    a = L.mlip_aggregate_workspace_size(4096, 384, 2560)
     assert a >= 4096 * 384 * 4
     m = L.mlip_moe_workspace_size(4096, 16, 72, 4, 2560, 2560)
     assert m >= 2 * 4096 * 4 * 2560 * 4          # SiLU activations + expert outputs
