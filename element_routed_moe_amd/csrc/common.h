@@ -85,6 +85,19 @@ struct Carver {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Workgroups are dealt round-robin to the 8 XCDs of the chip.  For a grid of
+// padded_grid(n) workgroups, xcd_block(n) gives each XCD a contiguous range
+// of the logical indices 0..n-1 (so neighbouring rows share one L2), or -1
+// for a padding workgroup.
+constexpr int kNumXcd = 8;
+inline int64_t padded_grid(int64_t n) { return cdiv(n, kNumXcd) * kNumXcd; }
+__device__ inline int64_t xcd_block(int64_t n) {
+  const int64_t per = (n + kNumXcd - 1) / kNumXcd;
+  const int64_t b = blockIdx.x;
+  const int64_t logical = (b % kNumXcd) * per + b / kNumXcd;
+  return logical < n ? logical : -1;
+}
+
 // ----------------------------------------------------------- scan / gemm ---
 // Exclusive prefix sum of n int32 values (out may alias in); out[n] gets the
 // total when write_total.  tmp needs scan_tmp_elems(n) int32 entries.

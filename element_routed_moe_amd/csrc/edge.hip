@@ -10,10 +10,10 @@
 // gathered, modulated and reduced onto the receiver); the gradient follows
 // section 3.3 of that review (forces from differentiating the energy).
 //
-// Layout: one 64-lane workgroup per (row, 128-column slice) in the forward,
-// one per row in the gradient.  Each lane owns two adjacent columns; the
-// per-edge radial scalars (16 basis values) are computed once per edge by
-// one lane and broadcast through LDS.
+// Layout: one 64-lane workgroup per (row, 128-column slice) in the forward;
+// in the gradient one workgroup per row whose wavefronts share the column
+// slices.  Each lane owns two adjacent columns; the per-edge radial scalars
+// (16 basis values) are computed once per edge and broadcast through LDS.
 #include "common.h"
 
 namespace mlip {
@@ -37,7 +37,14 @@ __device__ inline Radial make_radial(float rc) {
   return p;
 }
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+constexpr int UNROLL = 4;
+
+__device__ inline f2v ld2(const float *p) { return *reinterpret_cast<const f2v *>(p); }
+
 // Forward: e_e = f_c(r) * (phi(r) @ W_e), fused with a_i = sum_e e_e * s_src(e).
+// One wavefront per (row, 128-column slice).  Edges are taken UNROLL at a
+// time with all their gathers issued before any arithmetic.
 __global__ void __launch_bounds__(64) embed_aggregate_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, int n_slices, const float *__restrict__ W_e,
@@ -46,19 +53,20 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
   __shared__ float phi[EDGE_CHUNK][K + 1];
   __shared__ int jj[EDGE_CHUNK];
   const int lane = threadIdx.x;
-  const int i = blockIdx.x / n_slices;
-  const int slice = blockIdx.x - i * n_slices;
-  if (i >= n_atoms) return;
+  const int64_t blk = xcd_block(int64_t(n_atoms) * n_slices);
+  if (blk < 0) return;
+  const int i = int(blk / n_slices);
+  const int slice = int(blk - int64_t(i) * n_slices);
   const int c = slice * COLS + 2 * lane;
   const bool active = c < De;
+  const int cc = active ? c : 0;   // clamped column for always-valid addresses
   const Radial R = make_radial(rc);
 
-  float2 w[K];
+  f2v w[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k)
-    w[k] = active ? *reinterpret_cast<const float2 *>(W_e + k * De + c) : make_float2(0.f, 0.f);
+  for (int k = 0; k < K; ++k) w[k] = ld2(W_e + k * De + cc);
 
-  float2 acc = make_float2(0.f, 0.f);
+  f2v acc = {0.f, 0.f};
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
   for (int e0 = r0; e0 < r1; e0 += EDGE_CHUNK) {
     const int n = min(EDGE_CHUNK, r1 - e0);
@@ -73,49 +81,27 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
       jj[lane] = src[e0 + lane];
     }
     __syncthreads();
-    if (active) {
-      int m = 0;
-      for (; m + 2 <= n; m += 2) {
-        const int j0 = jj[m], j1 = jj[m + 1];
-        const float2 s0 = *reinterpret_cast<const float2 *>(s + int64_t(j0) * De + c);
-        const float2 s1 = *reinterpret_cast<const float2 *>(s + int64_t(j1) * De + c);
-        float2 v0 = make_float2(0.f, 0.f), v1 = make_float2(0.f, 0.f);
+    for (int m = 0; m < n; m += UNROLL) {
+      f2v sv[UNROLL];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float p0 = phi[m][k], p1 = phi[m + 1][k];
-          v0.x += p0 * w[k].x;
-          v0.y += p0 * w[k].y;
-          v1.x += p1 * w[k].x;
-          v1.y += p1 * w[k].y;
-        }
-        __builtin_nontemporal_store(v0.x, e_out + int64_t(e0 + m) * De + c);
-        __builtin_nontemporal_store(v0.y, e_out + int64_t(e0 + m) * De + c + 1);
-        __builtin_nontemporal_store(v1.x, e_out + int64_t(e0 + m + 1) * De + c);
-        __builtin_nontemporal_store(v1.y, e_out + int64_t(e0 + m + 1) * De + c + 1);
-        acc.x += v0.x * s0.x;
-        acc.y += v0.y * s0.y;
-        acc.x += v1.x * s1.x;
-        acc.y += v1.y * s1.y;
+      for (int u = 0; u < UNROLL; ++u) {
+        const int mm = min(m + u, n - 1);
+        sv[u] = ld2(s + int64_t(jj[mm]) * De + cc);
       }
-      if (m < n) {
-        const int j0 = jj[m];
-        const float2 s0 = *reinterpret_cast<const float2 *>(s + int64_t(j0) * De + c);
-        float2 v0 = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float p0 = phi[m][k];
-          v0.x += p0 * w[k].x;
-          v0.y += p0 * w[k].y;
+      for (int u = 0; u < UNROLL; ++u) {
+        if (m + u < n) {
+          f2v v = {0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < K; ++k) v += phi[m + u][k] * w[k];
+          if (active) __builtin_nontemporal_store(v, reinterpret_cast<f2v *>(e_out + int64_t(e0 + m + u) * De + c));
+          acc += v * sv[u];
         }
-        __builtin_nontemporal_store(v0.x, e_out + int64_t(e0 + m) * De + c);
-        __builtin_nontemporal_store(v0.y, e_out + int64_t(e0 + m) * De + c + 1);
-        acc.x += v0.x * s0.x;
-        acc.y += v0.y * s0.y;
       }
     }
     __syncthreads();
   }
-  if (active) *reinterpret_cast<float2 *>(a_out + int64_t(i) * De + c) = acc;
+  if (active) *reinterpret_cast<f2v *>(a_out + int64_t(i) * De + c) = acc;
 }
 
 // Gradient: for row i with senders j,
@@ -123,7 +109,10 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
 //   c_e + c_rev(e) = sum_c (abar_i s_j + abar_j s_i)_c * de_c/dr
 //   grad_pos_i = -sum_e (c_e + c_rev(e)) d_e / r_e
 // de_c/dr = sum_k W_e[k,c] g_k(r), g_k = f_c' phi_k + f_c phi_k'.
-__global__ void __launch_bounds__(64) edge_vjp_kernel(
+// One workgroup of NW wavefronts per row; wavefront w takes column slices
+// w, w+NW, ...; the per-edge radial terms are computed once per workgroup.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ W_e,
     const float *__restrict__ e, const float *__restrict__ s, const float *__restrict__ abar,
@@ -131,29 +120,38 @@ __global__ void __launch_bounds__(64) edge_vjp_kernel(
   __shared__ float gk[EDGE_CHUNK][K + 1];
   __shared__ float4 dir[EDGE_CHUNK];  // (dhat, unused)
   __shared__ int jj[EDGE_CHUNK];
-  const int lane = threadIdx.x;
-  const int i = blockIdx.x;
-  if (i >= n_atoms) return;
+  __shared__ float fred[NW][3];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
   const Radial R = make_radial(rc);
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
-  float f0 = 0.f, f1 = 0.f, f2 = 0.f;
+  const int n_slices = (De + COLS - 1) / COLS;
+  f2v fxy = {0.f, 0.f};
+  float fz = 0.f;
 
-  for (int c0 = 0; c0 < De; c0 += COLS) {
-    const int c = c0 + 2 * lane;
-    const bool active = c < De;
-    float2 w[K];
+  for (int sl0 = 0; sl0 < n_slices; sl0 += NW) {
+    const int sl = sl0 + wave;
+    const int c = sl * COLS + 2 * lane;
+    const bool active = sl < n_slices && c < De;
+    const int cc = active ? c : 0;
+    f2v w[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      w[k] = active ? *reinterpret_cast<const float2 *>(W_e + k * De + c) : make_float2(0.f, 0.f);
-    const float2 ai = active ? *reinterpret_cast<const float2 *>(abar + int64_t(i) * De + c)
-                             : make_float2(0.f, 0.f);
-    const float2 si = active ? *reinterpret_cast<const float2 *>(s + int64_t(i) * De + c)
-                             : make_float2(0.f, 0.f);
-    float2 sb = make_float2(0.f, 0.f);
+    for (int k = 0; k < K; ++k) w[k] = ld2(W_e + k * De + cc);
+    const f2v ai = ld2(abar + int64_t(i) * De + cc);
+    const f2v si = ld2(s + int64_t(i) * De + cc);
+    f2v sb = {0.f, 0.f};
     for (int e0 = r0; e0 < r1; e0 += EDGE_CHUNK) {
       const int n = min(EDGE_CHUNK, r1 - e0);
-      if (lane < n) {
-        const float4 g = geom[e0 + lane];
+      // radial terms: thread (wave w, lane l) computes basis functions
+      // k = w, w + NW, ... of edge l
+      {
+        const int ed = lane, part = wave;
+        if (ed < n) {
+        const float4 g = geom[e0 + ed];
         const float r = g.w;
         float fc = 0.f, dfc = 0.f;
         if (r < rc) {
@@ -162,48 +160,53 @@ __global__ void __launch_bounds__(64) edge_vjp_kernel(
           fc = 0.5f * (cs + 1.f);
           dfc = -0.5f * R.pi_over_rc * sn;
         }
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
+        for (int k = part; k < K; k += NW) {
           const float x = r - float(k) * R.mu_step;
           const float ph = __expf(-R.gamma * x * x);
-          gk[lane][k] = dfc * ph + fc * (-2.f * R.gamma * x * ph);
+          gk[ed][k] = dfc * ph + fc * (-2.f * R.gamma * x * ph);
         }
-        const float inv = r > 0.f ? 1.f / r : 0.f;
-        dir[lane] = make_float4(g.x * inv, g.y * inv, g.z * inv, 0.f);
-        jj[lane] = src[e0 + lane];
+        if (part == 0) {
+          const float inv = r > 0.f ? 1.f / r : 0.f;
+          dir[ed] = make_float4(g.x * inv, g.y * inv, g.z * inv, 0.f);
+          jj[ed] = src[e0 + ed];
+        }
+        }
       }
       __syncthreads();
       if (active) {
-        for (int m = 0; m < n; ++m) {
-          const int j = jj[m];
-          const int64_t eo = int64_t(e0 + m) * De + c;
-          const float2 ev = make_float2(__builtin_nontemporal_load(e + eo),
-                                        __builtin_nontemporal_load(e + eo + 1));
-          const float2 aj = *reinterpret_cast<const float2 *>(abar + int64_t(j) * De + c);
-          const float2 sj = *reinterpret_cast<const float2 *>(s + int64_t(j) * De + c);
-          sb.x += ev.x * aj.x;
-          sb.y += ev.y * aj.y;
-          float wx = 0.f, wy = 0.f;
+        for (int m = 0; m < n; m += UNROLL) {
+          f2v ev[UNROLL], aj[UNROLL], sj[UNROLL];
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            const float g = gk[m][k];
-            wx += g * w[k].x;
-            wy += g * w[k].y;
+          for (int u = 0; u < UNROLL; ++u) {
+            const int mm = min(m + u, n - 1);
+            const int j = jj[mm];
+            ev[u] = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(e + int64_t(e0 + mm) * De + c));
+            aj[u] = ld2(abar + int64_t(j) * De + c);
+            sj[u] = ld2(s + int64_t(j) * De + c);
           }
-          const float zx = ai.x * sj.x + aj.x * si.x;
-          const float zy = ai.y * sj.y + aj.y * si.y;
-          const float p = zx * wx + zy * wy;
-          const float4 dv = dir[m];
-          f0 += p * dv.x;
-          f1 += p * dv.y;
-          f2 += p * dv.z;
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            if (m + u < n) {
+              sb += ev[u] * aj[u];
+              f2v wv = {0.f, 0.f};
+#pragma unroll
+              for (int k = 0; k < K; ++k) wv += gk[m + u][k] * w[k];
+              const f2v z = ai * sj[u] + aj[u] * si;
+              const f2v pz = z * wv;
+              const float p = pz.x + pz.y;
+              const float4 dv = dir[m + u];
+              fxy += p * f2v{dv.x, dv.y};
+              fz += p * dv.z;
+            }
+          }
         }
       }
       __syncthreads();
     }
-    if (active) *reinterpret_cast<float2 *>(sbar + int64_t(i) * De + c) = sb;
+    if (active) *reinterpret_cast<f2v *>(sbar + int64_t(i) * De + c) = sb;
   }
-  // reduce the per-lane partial forces over the wavefront
+  // reduce the partial forces over the lanes, then over the wavefronts
+  float f0 = fxy.x, f1 = fxy.y, f2 = fz;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     f0 += __shfl_xor(f0, d, 64);
@@ -211,9 +214,21 @@ __global__ void __launch_bounds__(64) edge_vjp_kernel(
     f2 += __shfl_xor(f2, d, 64);
   }
   if (lane == 0) {
-    grad_pos[i * 3 + 0] = -f0;
-    grad_pos[i * 3 + 1] = -f1;
-    grad_pos[i * 3 + 2] = -f2;
+    fred[wave][0] = f0;
+    fred[wave][1] = f1;
+    fred[wave][2] = f2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    for (int w2 = 0; w2 < NW; ++w2) {
+      g0 += fred[w2][0];
+      g1 += fred[w2][1];
+      g2 += fred[w2][2];
+    }
+    grad_pos[i * 3 + 0] = -g0;
+    grad_pos[i * 3 + 1] = -g1;
+    grad_pos[i * 3 + 2] = -g2;
   }
 }
 
@@ -225,7 +240,7 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
   if (n_atoms <= 0) return MLIP_OK;
   const int n_slices = int(cdiv(De, COLS));
   ProfScope ps(K_EMBED_AGG, stream);
-  embed_aggregate_kernel<<<dim3(unsigned(int64_t(n_atoms) * n_slices)), dim3(64), 0, stream>>>(
+  embed_aggregate_kernel<<<dim3(unsigned(padded_grid(int64_t(n_atoms) * n_slices))), dim3(64), 0, stream>>>(
       row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, n_slices, W_e, s, De, rc, e, a);
   MLIP_LAUNCHED();
   return MLIP_OK;
@@ -236,9 +251,21 @@ int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geo
                     float rc, float *sbar, float *grad_pos, hipStream_t stream) {
   if (n_atoms <= 0) return MLIP_OK;
   ProfScope ps(K_EDGE_VJP, stream);
-  edge_vjp_kernel<<<dim3(unsigned(n_atoms)), dim3(64), 0, stream>>>(
-      row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, W_e, e, s, abar, De, rc, sbar,
-      grad_pos);
+  const int n_slices = int(cdiv(De, COLS));
+  const float4 *g4 = reinterpret_cast<const float4 *>(geom);
+  if (n_slices >= 4) {
+    edge_vjp_kernel<4><<<dim3(unsigned(padded_grid(n_atoms))), dim3(256), 0, stream>>>(
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+  } else if (n_slices == 3) {
+    edge_vjp_kernel<3><<<dim3(unsigned(padded_grid(n_atoms))), dim3(192), 0, stream>>>(
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+  } else if (n_slices == 2) {
+    edge_vjp_kernel<2><<<dim3(unsigned(padded_grid(n_atoms))), dim3(128), 0, stream>>>(
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+  } else {
+    edge_vjp_kernel<1><<<dim3(unsigned(padded_grid(n_atoms))), dim3(64), 0, stream>>>(
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+  }
   MLIP_LAUNCHED();
   return MLIP_OK;
 }

@@ -37,9 +37,18 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+#ifndef GEMM_RASTER
+#define GEMM_RASTER 8
+#endif
+#ifndef GEMM_XCD_REMAP
+#define GEMM_XCD_REMAP 1
+#endif
+#ifndef EXPERT_BK
+#define EXPERT_BK 32
+#endif
 constexpr int THREADS = 256;
 constexpr int N_XCD = 8;
-constexpr int RASTER_M = 8;
+constexpr int RASTER_M = GEMM_RASTER;
 constexpr int MAX_GROUPS = 1024;
 
 // Exclusive scan over the 256 threads of the block (one value each).
@@ -111,8 +120,8 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
   const int per = (total + N_XCD - 1) / N_XCD;
   const int L = blockIdx.x;
   const int jx = L / N_XCD, xcd = L - jx * N_XCD;
-  if (jx >= per) return;
-  const int T = xcd * per + jx;
+  if (GEMM_XCD_REMAP && jx >= per) return;
+  const int T = GEMM_XCD_REMAP ? xcd * per + jx : L;
   if (T >= total) return;
   const int group_size = RASTER_M * Nt;
   const int first_m = (T / group_size) * RASTER_M;
@@ -332,7 +341,7 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
 // Expert GEMMs: 128 x 128 tiles.
 template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
-  return launch_t<128, 128, 32, 2, 2, BT, EPI, TAG>(a, s);
+  return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG>(a, s);
 }
 // Dense projections: 64 x 64 tiles when the output is narrow (enough
 // workgroups for 256 CUs), else 64 x 128.

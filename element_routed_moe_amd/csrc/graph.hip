@@ -103,6 +103,8 @@ __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__res
   if (f) atomicOr(flags, f);
 }
 
+__device__ inline int cdiv_dev(int a, int b) { return (a + b - 1) / b; }
+
 __device__ inline int find_struct(const int32_t *__restrict__ struct_ptr, int n_structs, int i) {
   int lo = 0, hi = n_structs;  // last b with struct_ptr[b] <= i
   while (hi - lo > 1) {
@@ -157,61 +159,127 @@ __global__ void graph_scatter(const float *__restrict__ pos, int n_atoms,
 // Candidate enumeration shared by the count and fill passes.  The visitor is
 // called once per candidate slot with (accept, j, S, d, d2); all lanes of the
 // wave call it the same number of times (inactive lanes with accept=false).
+//
+// Along a binned axis the shift is fixed by the neighbouring bin.  Along an
+// image-mode axis only shifts with |x_j - x_i + S L| < r_c can give an edge
+// (|d_a| >= r_c implies d2 >= r_c^2 under round-to-nearest), so each
+// candidate atom carries the range of such S per axis, widened by 1e-9 of a
+// cell length; the (atom, shift) pairs of 64 atoms are then flattened over
+// the lanes with a prefix sum, and the exact float64 predicate decides.
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
 template <typename Visit>
 __device__ inline void visit_candidates(int i, const float *__restrict__ pos,
                                         const StructParams &P, int gbin_i,
                                         const int32_t *__restrict__ bin_start,
                                         const float4 *__restrict__ binned, double rc2,
-                                        Visit &&visit) {
+                                        double rc, Visit &&visit) {
   const int lane = threadIdx.x & 63;
-  const double xi0 = double(pos[i * 3 + 0]);
-  const double xi1 = double(pos[i * 3 + 1]);
-  const double xi2 = double(pos[i * 3 + 2]);
+  const double xi[3] = {double(pos[i * 3 + 0]), double(pos[i * 3 + 1]), double(pos[i * 3 + 2])};
   int local = gbin_i - P.bin_base;
   int bc[3];
   bc[0] = local % P.nb[0];
   bc[1] = (local / P.nb[0]) % P.nb[1];
   bc[2] = local / (P.nb[0] * P.nb[1]);
   int cnt[3];
-  for (int a = 0; a < 3; ++a) cnt[a] = P.nb[a] == 1 ? 2 * P.nimg[a] + 1 : 3;
+  for (int a = 0; a < 3; ++a) cnt[a] = P.nb[a] == 1 ? 1 : 3;
   for (int e2 = 0; e2 < cnt[2]; ++e2)
     for (int e1 = 0; e1 < cnt[1]; ++e1)
       for (int e0 = 0; e0 < cnt[0]; ++e0) {
-        int ee[3] = {e0, e1, e2};
-        int S[3], bb[3];
+        const int ee[3] = {e0, e1, e2};
+        int Sb[3], bb[3];
         for (int a = 0; a < 3; ++a) {
           if (P.nb[a] == 1) {
-            S[a] = ee[a] - P.nimg[a];
+            Sb[a] = 0;
             bb[a] = 0;
           } else {
-            int v = bc[a] + ee[a] - 1;
-            S[a] = v < 0 ? -1 : (v >= P.nb[a] ? 1 : 0);
-            bb[a] = v - S[a] * P.nb[a];
+            const int v = bc[a] + ee[a] - 1;
+            Sb[a] = v < 0 ? -1 : (v >= P.nb[a] ? 1 : 0);
+            bb[a] = v - Sb[a] * P.nb[a];
           }
         }
-        const double s0 = double(S[0]), s1 = double(S[1]), s2 = double(S[2]);
-        double t[3];
-        for (int c = 0; c < 3; ++c)
-          t[c] = __dadd_rn(__dadd_rn(__dmul_rn(s0, P.C[0 * 3 + c]), __dmul_rn(s1, P.C[1 * 3 + c])),
-                           __dmul_rn(s2, P.C[2 * 3 + c]));
-        const bool zero_shift = S[0] == 0 && S[1] == 0 && S[2] == 0;
-        int gb = P.bin_base + (bb[2] * P.nb[1] + bb[1]) * P.nb[0] + bb[0];
-        int k0 = bin_start[gb], k1 = bin_start[gb + 1];
-        for (int k = k0; k < k1; k += 64) {
-          int kk = k + lane;
-          bool ok = false;
-          int j = -1;
-          double d0 = 0, d1 = 0, d2v = 0, dd = 0;
+        const int gb = P.bin_base + (bb[2] * P.nb[1] + bb[1]) * P.nb[0] + bb[0];
+        const int k0 = bin_start[gb], k1 = bin_start[gb + 1];
+        for (int kb = k0; kb < k1; kb += 64) {
+          // this lane's candidate atom and its shift ranges
+          const int kk = kb + lane;
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          int lo[3] = {0, 0, 0}, span[3] = {1, 1, 1};
+          int count = 0;
           if (kk < k1) {
-            float4 q = binned[kk];
-            j = __float_as_int(q.w);
-            d0 = __dadd_rn(__dsub_rn(double(q.x), xi0), t[0]);
-            d1 = __dadd_rn(__dsub_rn(double(q.y), xi1), t[1]);
-            d2v = __dadd_rn(__dsub_rn(double(q.z), xi2), t[2]);
-            dd = __dadd_rn(__dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1)), __dmul_rn(d2v, d2v));
-            ok = dd < rc2 && !(zero_shift && j == i);
+            q = binned[kk];
+            count = 1;
+            const float qc[3] = {q.x, q.y, q.z};
+            for (int a = 0; a < 3; ++a) {
+              if (P.nb[a] != 1) {
+                lo[a] = Sb[a];
+                continue;
+              }
+              const double dx = __dsub_rn(double(qc[a]), xi[a]);
+              const double slack = 1e-9;
+              int l = int(ceil((-rc - dx) / P.L[a] - slack));
+              int h = int(floor((rc - dx) / P.L[a] + slack));
+              l = l < -P.nimg[a] ? -P.nimg[a] : l;
+              h = h > P.nimg[a] ? P.nimg[a] : h;
+              lo[a] = l;
+              span[a] = h >= l ? h - l + 1 : 0;
+              count *= span[a];
+            }
           }
-          visit(ok, j, S, d0, d1, d2v, dd);
+          const int incl = wave_incl_scan(count);
+          const int total = __shfl(incl, 63, 64);
+          for (int f0 = 0; f0 < total; f0 += 64) {
+            const int f = f0 + lane;
+            // owner lane: number of lanes whose inclusive prefix is <= f
+            int o = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) {
+              const int v = __shfl(incl, o + step - 1, 64);
+              if (v <= f) o += step;
+            }
+            o = o > 63 ? 63 : o;
+            // every lane takes part in every shuffle (a lane outside a branch
+            // would not supply its value)
+            const int prev_in = __shfl(incl, o > 0 ? o - 1 : 0, 64);
+            const int prev = o > 0 ? prev_in : 0;
+            int r = f - prev;
+            const float ox = __shfl(q.x, o, 64), oy = __shfl(q.y, o, 64), oz = __shfl(q.z, o, 64);
+            const int j = __float_as_int(__shfl(q.w, o, 64));
+            int S[3];
+            const int olo0 = __shfl(lo[0], o, 64), olo1 = __shfl(lo[1], o, 64), olo2 = __shfl(lo[2], o, 64);
+            // spans are >= 1 for every owner of a real slot; the max() only
+            // keeps the decode of padding slots (f >= total) well defined
+            const int osp0 = max(1, __shfl(span[0], o, 64)), osp1 = max(1, __shfl(span[1], o, 64));
+            S[0] = olo0 + r % osp0;
+            r /= osp0;
+            S[1] = olo1 + r % osp1;
+            r /= osp1;
+            S[2] = olo2 + r;
+            bool ok = false;
+            double d0 = 0, d1 = 0, d2v = 0, dd = 0;
+            if (f < total) {
+              const double s0 = double(S[0]), s1 = double(S[1]), s2 = double(S[2]);
+              double t[3];
+              for (int c = 0; c < 3; ++c)
+                t[c] = __dadd_rn(__dadd_rn(__dmul_rn(s0, P.C[0 * 3 + c]), __dmul_rn(s1, P.C[1 * 3 + c])),
+                                 __dmul_rn(s2, P.C[2 * 3 + c]));
+              d0 = __dadd_rn(__dsub_rn(double(ox), xi[0]), t[0]);
+              d1 = __dadd_rn(__dsub_rn(double(oy), xi[1]), t[1]);
+              d2v = __dadd_rn(__dsub_rn(double(oz), xi[2]), t[2]);
+              dd = __dadd_rn(__dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1)), __dmul_rn(d2v, d2v));
+              const bool zero_shift = S[0] == 0 && S[1] == 0 && S[2] == 0;
+              ok = dd < rc2 && !(zero_shift && j == i);
+            }
+            visit(ok, j, S, d0, d1, d2v, dd);
+          }
         }
       }
 }
@@ -223,14 +291,16 @@ __global__ void __launch_bounds__(256) graph_count(const float *__restrict__ pos
                                                    const int32_t *__restrict__ atom_bin,
                                                    const int32_t *__restrict__ bin_start,
                                                    const float4 *__restrict__ binned, double rc2,
-                                                   int32_t *__restrict__ deg,
+                                                   double rc, int32_t *__restrict__ deg,
                                                    int32_t *__restrict__ maxdeg) {
-  int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t blk = xcd_block(cdiv_dev(n_atoms, 4));
+  if (blk < 0) return;
+  int i = int(blk) * 4 + (threadIdx.x >> 6);
   if (i >= n_atoms) return;
   const StructParams &P = prm[atom_struct[i]];
   int count = 0;
   if (P.valid) {
-    visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2,
+    visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2, rc,
                      [&](bool ok, int, const int *, double, double, double, double) {
                        count += __popcll(__ballot(ok));
                      });
@@ -262,18 +332,19 @@ __global__ void __launch_bounds__(64) graph_fill(const float *__restrict__ pos, 
                                                  const int32_t *__restrict__ atom_bin,
                                                  const int32_t *__restrict__ bin_start,
                                                  const float4 *__restrict__ binned, double rc2,
-                                                 const int32_t *__restrict__ row_ptr,
+                                                 double rc, const int32_t *__restrict__ row_ptr,
                                                  int32_t *__restrict__ src, char4 *__restrict__ shift,
                                                  float4 *__restrict__ geom) {
   __shared__ uint64_t keys[kMaxDeg];
   __shared__ float4 gm[kMaxDeg];
-  int i = blockIdx.x;
-  if (i >= n_atoms) return;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  int i = int(blk);
   const int lane = threadIdx.x;
   const StructParams &P = prm[atom_struct[i]];
   if (!P.valid) return;
   int n = 0;
-  visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2,
+  visit_candidates(i, pos, P, atom_bin[i], bin_start, binned, rc2, rc,
                    [&](bool ok, int j, const int *S, double d0, double d1, double d2v, double dd) {
                      uint64_t m = __ballot(ok);
                      if (ok) {
@@ -416,8 +487,9 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
       graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start,
                                                        w.bin_fill, w.binned);
       MLIP_LAUNCHED();
-      graph_count<<<nblk(N, 4), 256, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
-                                                   w.bin_start, w.binned, rc2, row_ptr, w.maxdeg);
+      graph_count<<<unsigned(padded_grid(cdiv(N, 4))), 256, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
+                                                   w.bin_start, w.binned, rc2, double(cutoff), row_ptr,
+                                                   w.maxdeg);
       MLIP_LAUNCHED();
     }
     int rc = exclusive_scan(row_ptr, row_ptr, N, true, w.scan_tmp, stream);
@@ -453,8 +525,8 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
   }
   if (N > 0 && E > 0) {
     ProfScope ps(K_GRAPH, stream);
-    graph_fill<<<unsigned(N), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
-                                               w.bin_start, w.binned, rc2, row_ptr, src,
+    graph_fill<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
+                                               w.bin_start, w.binned, rc2, double(cutoff), row_ptr, src,
                                                reinterpret_cast<char4 *>(shift),
                                                reinterpret_cast<float4 *>(geom));
     MLIP_LAUNCHED();
