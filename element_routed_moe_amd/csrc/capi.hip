@@ -14,7 +14,9 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
                            float *e, float *a, hipStream_t stream);
 int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
                     const float *W_e, const float *e, const float *s, const float *abar, int De,
-                    float rc, float *sbar, float *grad_pos, hipStream_t stream);
+                    float rc, float *sbar, float *grad_pos, float *atom_virial, hipStream_t stream);
+int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs,
+                      double *grad_strain, hipStream_t stream);
 int moe_route_dispatch(const int32_t *z, const float *logits, int N, int T, int X, int k,
                        int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom,
                        int32_t *slot, int32_t *local_rank, int32_t *blk_count, int32_t *n_type,
@@ -79,11 +81,12 @@ MoeWs carve_moe(void *base, int64_t N, int64_t T, int64_t X, int64_t k, int64_t 
 }
 
 struct VjpWs {
-  float *Q, *Utok, *ubar, *abar, *sbar;
+  float *Q, *Utok, *ubar, *abar, *sbar, *virial;
 };
 VjpWs carve_vjp(void *base, int64_t N, int64_t k, int64_t De, int64_t Dn, int64_t H, size_t *bytes) {
   Carver c(base);
   VjpWs w;
+  w.virial = c.take<float>(size_t(N * 6));
   w.Q = c.take<float>(size_t(N * k * H));
   w.Utok = c.take<float>(size_t(N * k * Dn));
   w.ubar = c.take<float>(size_t(N * Dn));
@@ -235,7 +238,9 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    const float *W_u, const float *W1, const float *W2, int32_t n_rbf,
                    int32_t d_edge, int32_t d_node, int32_t d_hidden, int32_t n_types,
                    int32_t n_experts, int32_t top_k, float cutoff, const float *grad_out,
-                   float *grad_h, float *grad_pos, void *ws, size_t ws_bytes, void *stream_) {
+                   float *grad_h, float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
+                   float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
+                   void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
@@ -253,14 +258,20 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   MLIP_CHECK_ARG(n_atoms == 0 || (s && z && tok_atom && slot && P && grad_out && grad_h && grad_pos),
                  "null pointer argument");
   MLIP_CHECK_ARG(n_edges == 0 || (src && geom && e), "null edge pointer");
+  MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
+                 "grad_strain needs struct_ptr and n_structs >= 1");
   MLIP_CHECK_ARG(aligned(e, 16) && aligned(s, 16) && aligned(P, 16) && aligned(grad_out, 16) &&
                      aligned(grad_h, 16) && aligned(geom, 16),
                  "float arrays must be 16-byte aligned");
   if (int rc = check_ws(ws, ws_bytes,
                         mlip_vjp_workspace_size(n_atoms, top_k, d_edge, d_node, d_hidden)))
     return rc;
-  if (n_atoms == 0) return MLIP_OK;
+  if (n_atoms == 0) {
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    return MLIP_OK;
+  }
   VjpWs w = carve_vjp(ws, n_atoms, top_k, d_edge, d_node, d_hidden, nullptr);
+  float *vir = atom_virial ? atom_virial : w.virial;
   const int M = n_atoms * top_k;
 
   GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
@@ -286,8 +297,11 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   g3.M = n_atoms; g3.N = d_edge; g3.K = d_node;
   if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   if (int rc = launch_edge_vjp(row_ptr, src, geom, n_atoms, W_e, e, s, w.abar, d_edge, cutoff,
-                               w.sbar, grad_pos, stream))
+                               w.sbar, grad_pos, vir, stream))
     return rc;
+  if (grad_strain) {
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+  }
   GemmArgs g4;  // grad_h = ubar + sbar @ W_d^T
   g4.A = w.sbar; g4.lda = d_edge; g4.B = W_d; g4.ldb = d_edge; g4.C = grad_h; g4.ldc = d_node;
   g4.R = w.ubar; g4.ldr = d_node; g4.M = n_atoms; g4.N = d_node; g4.K = d_edge;

@@ -108,6 +108,8 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
 //   sbar_i = sum_e e_e * abar_j                (e is symmetric: e_rev(e) = e_e)
 //   c_e + c_rev(e) = sum_c (abar_i s_j + abar_j s_i)_c * de_c/dr
 //   grad_pos_i = -sum_e (c_e + c_rev(e)) d_e / r_e
+//   atom_virial_i = 1/2 sum_e (c_e + c_rev(e)) dhat_e (x) d_e    (strain gradient
+//                   dL/d(eps) = sum_e c_e dhat_e (x) d_e, shared by the two atoms)
 // de_c/dr = sum_k W_e[k,c] g_k(r), g_k = f_c' phi_k + f_c phi_k'.
 // One workgroup of NW wavefronts per row; wavefront w takes column slices
 // w, w+NW, ...; the per-edge radial terms are computed once per workgroup.
@@ -116,11 +118,13 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ W_e,
     const float *__restrict__ e, const float *__restrict__ s, const float *__restrict__ abar,
-    int De, float rc, float *__restrict__ sbar, float *__restrict__ grad_pos) {
+    int De, float rc, float *__restrict__ sbar, float *__restrict__ grad_pos,
+    float *__restrict__ atom_virial) {
   __shared__ float gk[EDGE_CHUNK][K + 1];
   __shared__ float4 dir[EDGE_CHUNK];  // (dhat, unused)
+  __shared__ float vq[EDGE_CHUNK][6]; // dhat_a d_b in the order xx yy zz yz xz xy
   __shared__ int jj[EDGE_CHUNK];
-  __shared__ float fred[NW][3];
+  __shared__ float fred[NW][9];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -132,6 +136,7 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
   const int n_slices = (De + COLS - 1) / COLS;
   f2v fxy = {0.f, 0.f};
   float fz = 0.f;
+  float vir[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   for (int sl0 = 0; sl0 < n_slices; sl0 += NW) {
     const int sl = sl0 + wave;
@@ -168,6 +173,12 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
         if (part == 0) {
           const float inv = r > 0.f ? 1.f / r : 0.f;
           dir[ed] = make_float4(g.x * inv, g.y * inv, g.z * inv, 0.f);
+          vq[ed][0] = g.x * g.x * inv;
+          vq[ed][1] = g.y * g.y * inv;
+          vq[ed][2] = g.z * g.z * inv;
+          vq[ed][3] = g.y * g.z * inv;
+          vq[ed][4] = g.x * g.z * inv;
+          vq[ed][5] = g.x * g.y * inv;
           jj[ed] = src[e0 + ed];
         }
         }
@@ -197,6 +208,8 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
               const float4 dv = dir[m + u];
               fxy += p * f2v{dv.x, dv.y};
               fz += p * dv.z;
+#pragma unroll
+              for (int q = 0; q < 6; ++q) vir[q] += p * vq[m + u][q];
             }
           }
         }
@@ -205,30 +218,22 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     }
     if (active) *reinterpret_cast<f2v *>(sbar + int64_t(i) * De + c) = sb;
   }
-  // reduce the partial forces over the lanes, then over the wavefronts
-  float f0 = fxy.x, f1 = fxy.y, f2 = fz;
+  // reduce the partial forces and virials over the lanes, then over the
+  // wavefronts; each edge term is shared half and half by its two atoms
+  float acc[9] = {fxy.x, fxy.y, fz, vir[0], vir[1], vir[2], vir[3], vir[4], vir[5]};
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    f0 += __shfl_xor(f0, d, 64);
-    f1 += __shfl_xor(f1, d, 64);
-    f2 += __shfl_xor(f2, d, 64);
-  }
-  if (lane == 0) {
-    fred[wave][0] = f0;
-    fred[wave][1] = f1;
-    fred[wave][2] = f2;
-  }
+  for (int q = 0; q < 9; ++q)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc[q] += __shfl_xor(acc[q], d, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < 9; ++q) fred[wave][q] = acc[q];
   __syncthreads();
-  if (tid == 0) {
-    float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-    for (int w2 = 0; w2 < NW; ++w2) {
-      g0 += fred[w2][0];
-      g1 += fred[w2][1];
-      g2 += fred[w2][2];
-    }
-    grad_pos[i * 3 + 0] = -g0;
-    grad_pos[i * 3 + 1] = -g1;
-    grad_pos[i * 3 + 2] = -g2;
+  if (tid < 9) {
+    float t = 0.f;
+    for (int w2 = 0; w2 < NW; ++w2) t += fred[w2][tid];
+    if (tid < 3) grad_pos[i * 3 + tid] = -t;
+    else atom_virial[int64_t(i) * 6 + (tid - 3)] = 0.5f * t;
   }
 }
 
@@ -246,25 +251,54 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
   return MLIP_OK;
 }
 
+// grad_strain_b = sum over the atoms of structure b of atom_virial (float64,
+// fixed reduction tree).
+__global__ void __launch_bounds__(256) strain_sum_kernel(const float *__restrict__ atom_virial,
+                                                         const int32_t *__restrict__ struct_ptr,
+                                                         double *__restrict__ grad_strain) {
+  __shared__ double part[6][256];
+  const int b = blockIdx.x;
+  const int lo = struct_ptr[b], hi = struct_ptr[b + 1];
+  double acc[6] = {0, 0, 0, 0, 0, 0};
+  for (int i = lo + threadIdx.x; i < hi; i += 256)
+    for (int q = 0; q < 6; ++q) acc[q] += double(atom_virial[int64_t(i) * 6 + q]);
+  for (int q = 0; q < 6; ++q) part[q][threadIdx.x] = acc[q];
+  __syncthreads();
+  for (int st = 128; st >= 1; st >>= 1) {
+    if (int(threadIdx.x) < st)
+      for (int q = 0; q < 6; ++q) part[q][threadIdx.x] += part[q][threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x < 6) grad_strain[b * 6 + threadIdx.x] = part[threadIdx.x][0];
+}
+
+int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs,
+                      double *grad_strain, hipStream_t stream) {
+  strain_sum_kernel<<<dim3(unsigned(n_structs)), dim3(256), 0, stream>>>(atom_virial, struct_ptr,
+                                                                        grad_strain);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
                     const float *W_e, const float *e, const float *s, const float *abar, int De,
-                    float rc, float *sbar, float *grad_pos, hipStream_t stream) {
+                    float rc, float *sbar, float *grad_pos, float *atom_virial, hipStream_t stream) {
   if (n_atoms <= 0) return MLIP_OK;
   ProfScope ps(K_EDGE_VJP, stream);
   const int n_slices = int(cdiv(De, COLS));
   const float4 *g4 = reinterpret_cast<const float4 *>(geom);
   if (n_slices >= 4) {
     edge_vjp_kernel<4><<<dim3(unsigned(padded_grid(n_atoms))), dim3(256), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
   } else if (n_slices == 3) {
     edge_vjp_kernel<3><<<dim3(unsigned(padded_grid(n_atoms))), dim3(192), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
   } else if (n_slices == 2) {
     edge_vjp_kernel<2><<<dim3(unsigned(padded_grid(n_atoms))), dim3(128), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
   } else {
     edge_vjp_kernel<1><<<dim3(unsigned(padded_grid(n_atoms))), dim3(64), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos);
+        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
   }
   MLIP_LAUNCHED();
   return MLIP_OK;

@@ -41,9 +41,19 @@ struct StructParams {
   int valid;
 };
 
-__global__ void graph_fill_i32(int32_t *p, int64_t n, int32_t v) {
-  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+// Zeroes the flags, the degree maximum and the two bin counters in one launch.
+__global__ void graph_zero(int32_t *__restrict__ flags, int32_t *__restrict__ maxdeg,
+                           int32_t *__restrict__ bin_count, int32_t *__restrict__ bin_fill,
+                           int64_t nbins) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < 4) {
+    flags[i] = 0;
+    maxdeg[i] = 0;
+  }
+  if (i < nbins) {
+    bin_count[i] = 0;
+    bin_fill[i] = 0;
+  }
 }
 
 __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__restrict__ struct_ptr,
@@ -284,19 +294,18 @@ __device__ inline void visit_candidates(int i, const float *__restrict__ pos,
       }
 }
 
-// One wave per receiver: number of neighbours.
-__global__ void __launch_bounds__(256) graph_count(const float *__restrict__ pos, int n_atoms,
-                                                   const StructParams *__restrict__ prm,
-                                                   const int32_t *__restrict__ atom_struct,
-                                                   const int32_t *__restrict__ atom_bin,
-                                                   const int32_t *__restrict__ bin_start,
-                                                   const float4 *__restrict__ binned, double rc2,
-                                                   double rc, int32_t *__restrict__ deg,
-                                                   int32_t *__restrict__ maxdeg) {
-  const int64_t blk = xcd_block(cdiv_dev(n_atoms, 4));
+// One wave (one workgroup) per receiver: number of neighbours.
+__global__ void __launch_bounds__(64) graph_count(const float *__restrict__ pos, int n_atoms,
+                                                  const StructParams *__restrict__ prm,
+                                                  const int32_t *__restrict__ atom_struct,
+                                                  const int32_t *__restrict__ atom_bin,
+                                                  const int32_t *__restrict__ bin_start,
+                                                  const float4 *__restrict__ binned, double rc2,
+                                                  double rc, int32_t *__restrict__ deg,
+                                                  int32_t *__restrict__ maxdeg) {
+  const int64_t blk = xcd_block(n_atoms);
   if (blk < 0) return;
-  int i = int(blk) * 4 + (threadIdx.x >> 6);
-  if (i >= n_atoms) return;
+  const int i = int(blk);
   const StructParams &P = prm[atom_struct[i]];
   int count = 0;
   if (P.valid) {
@@ -305,7 +314,7 @@ __global__ void __launch_bounds__(256) graph_count(const float *__restrict__ pos
                        count += __popcll(__ballot(ok));
                      });
   }
-  if ((threadIdx.x & 63) == 0) {
+  if (threadIdx.x == 0) {
     deg[i] = count;
     atomicMax(maxdeg, count);
   }
@@ -471,10 +480,8 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
   int32_t host[4] = {0, 0, 0, 0};
   {
     ProfScope ps(K_GRAPH, stream);
-    graph_fill_i32<<<1, 64, 0, stream>>>(w.flags, 4, 0);
-    graph_fill_i32<<<1, 64, 0, stream>>>(w.maxdeg, 4, 0);
-    graph_fill_i32<<<nblk(nbins, 256), 256, 0, stream>>>(w.bin_count, nbins, 0);
-    graph_fill_i32<<<nblk(nbins, 256), 256, 0, stream>>>(w.bin_fill, nbins, 0);
+    graph_zero<<<nblk(nbins, 256), 256, 0, stream>>>(w.flags, w.maxdeg, w.bin_count, w.bin_fill,
+                                                      nbins);
     MLIP_LAUNCHED();
     graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, cutoff, w.prm, w.flags);
     MLIP_LAUNCHED();
@@ -487,7 +494,7 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
       graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start,
                                                        w.bin_fill, w.binned);
       MLIP_LAUNCHED();
-      graph_count<<<unsigned(padded_grid(cdiv(N, 4))), 256, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
+      graph_count<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
                                                    w.bin_start, w.binned, rc2, double(cutoff), row_ptr,
                                                    w.maxdeg);
       MLIP_LAUNCHED();

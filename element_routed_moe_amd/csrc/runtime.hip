@@ -199,6 +199,31 @@ size_t scan_tmp_elems(int64_t n) { return size_t(cdiv(n, SCAN_TILE)) + 1; }
 
 __global__ void scan_zero_total(int32_t *out) { out[0] = 0; }
 
+__global__ void __launch_bounds__(SCAN_THREADS) scan_single(const int32_t *in, int32_t *out,
+                                                            int64_t n, int write_total) {
+  __shared__ int32_t lds[SCAN_THREADS / 64];
+  int32_t carry = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += SCAN_TILE) {
+    const int64_t base = c0 + int64_t(threadIdx.x) * SCAN_PER_THREAD;
+    int32_t v[SCAN_PER_THREAD];
+    int32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER_THREAD; ++j) {
+      v[j] = (base + j < n) ? in[base + j] : 0;
+      sum += v[j];
+    }
+    int32_t tot;
+    int32_t off = block_exclusive_scan(sum, &tot, lds) + carry;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER_THREAD; ++j) {
+      if (base + j < n) out[base + j] = off;
+      off += v[j];
+    }
+    carry += tot;
+  }
+  if (write_total && threadIdx.x == 0) out[n] = carry;
+}
+
 int exclusive_scan(const int32_t *in, int32_t *out, int64_t n, bool write_total, int32_t *tmp,
                    hipStream_t stream) {
   if (n <= 0) {
@@ -209,6 +234,12 @@ int exclusive_scan(const int32_t *in, int32_t *out, int64_t n, bool write_total,
     return MLIP_OK;
   }
   int64_t nt = cdiv(n, SCAN_TILE);
+  if (nt > 1 && nt <= 64) {
+    // small arrays: one workgroup walks the tiles with a running carry
+    scan_single<<<1, SCAN_THREADS, 0, stream>>>(in, out, n, write_total ? 1 : 0);
+    MLIP_LAUNCHED();
+    return MLIP_OK;
+  }
   if (nt > 1) {
     scan_tile_sums<<<dim3(unsigned(nt)), dim3(SCAN_THREADS), 0, stream>>>(in, n, tmp);
     MLIP_LAUNCHED();

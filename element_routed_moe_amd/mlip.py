@@ -55,7 +55,7 @@ _SIGS = {
     "mlip_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "mlip_block_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
                                  _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                 _f32, _p, _p, _p, _p, _sz, _p]),
+                                 _f32, _p, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]),
     "mlip_profile_enable": (C.c_int, [C.c_int]),
     "mlip_profile_reset": (C.c_int, []),
     "mlip_profile_count": (C.c_int, []),
@@ -184,7 +184,7 @@ def mlip_readout(h_out, w_r, struct_ptr, out: Optional[Dict] = None) -> Dict[str
 
 
 def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top_k: int,
-                   grad_out, out: Optional[Dict] = None,
+                   grad_out, struct_ptr=None, out: Optional[Dict] = None,
                    ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     N, Dn = int(grad_out.shape[0]), int(grad_out.shape[1])
     De = int(W_e.shape[1])
@@ -193,9 +193,13 @@ def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top
     T = int(moe["gate"].shape[0])
     E = int(graph["n_edges"])
     dev = grad_out.device
+    B = int(struct_ptr.shape[0]) - 1 if struct_ptr is not None else 0
     if out is None:
         out = dict(grad_h=torch.empty((N, Dn), dtype=torch.float32, device=dev),
-                   grad_pos=torch.empty((N, 3), dtype=torch.float32, device=dev))
+                   grad_pos=torch.empty((N, 3), dtype=torch.float32, device=dev),
+                   atom_virial=torch.empty((N, 6), dtype=torch.float32, device=dev))
+        if struct_ptr is not None:
+            out["grad_strain"] = torch.empty((B, 6), dtype=torch.float64, device=dev)
     if ws is None:
         ws = _ws(_lib.mlip_vjp_workspace_size(N, top_k, De, Dn, H), dev)
     _check(_lib.mlip_block_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
@@ -204,7 +208,8 @@ def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top
                                _ptr(moe["P"]), _ptr(W_e), _ptr(W_d), _ptr(W_u), _ptr(W1), _ptr(W2),
                                int(W_e.shape[0]), De, Dn, H, T, X, int(top_k), float(cutoff),
                                _ptr(grad_out), _ptr(out["grad_h"]), _ptr(out["grad_pos"]),
-                               _ptr(ws), ws.numel(), _stream()))
+                               _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
+                               _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))
     return out
 
 
@@ -234,7 +239,7 @@ class Block:
 
     ``step()`` runs the whole path on the current stream: radius graph,
     aggregation, mixture of experts, readout and the input gradient for the
-    given upstream gradient.
+    given upstream gradient (node features, positions and strain).
     """
 
     def __init__(self, inputs: Dict, device="cuda", grad_out=None):
@@ -285,5 +290,5 @@ class Block:
         self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
         self.vjp = mlip_block_vjp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u,
                                   self.W1, self.W2, self.cutoff, self.top_k, self.grad_out,
-                                  out=self.vjp, ws=self.ws_vjp)
+                                  struct_ptr=self.struct_ptr, out=self.vjp, ws=self.ws_vjp)
         return self

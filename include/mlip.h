@@ -163,20 +163,25 @@ int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr
 
 /* ------------------------------------------------------------------------
  * Input gradient of the block ([news] conservative training; [review] 3.3:
- * forces are obtained by differentiating the energy).  Given
+ * forces and stresses are obtained by differentiating the energy).  Given
  * grad_out = dL/dh_out [N,d_node]:
  *   ubar = grad_out + sum_r gate * ((grad_out @ W2^T) * silu'(P)) @ W1^T
  *   abar = ubar @ W_u^T
  *   grad_h = ubar + sbar @ W_d^T,  sbar_j = sum_{e: src(e)=j} e_e * abar_recv(e)
  *   c_e = sum_c (abar_recv * s_src)_c * d e_e,c / d r_e
  *   grad_pos_i = dL/dx_i = -sum_{e in row i} (c_e + c_rev(e)) d_e/|d_e|
+ *   dL/d(eps) = sum_e c_e (d_e/|d_e|) (x) d_e   for the homogeneous strain
+ *               x -> (I + eps) x of positions and cell vectors
+ *   atom_virial_i = half of the strain terms of the edges touching atom i
  * Routing depends only on the element types, so gates carry no gradient.
- * With grad_out rows all equal to w_r, grad_pos = dE/dx and the forces are
- * -grad_pos.
+ * With grad_out rows all equal to w_r, grad_pos = dE/dx (forces are
+ * -grad_pos) and grad_strain_b / V_b is the stress of structure b.
  *
  * Inputs are the graph, e and s from mlip_aggregate, the kept MoE state
  * from mlip_moe_forward and the weights.  Outputs grad_h [N,d_node],
- * grad_pos [N,3].
+ * grad_pos [N,3]; optional (may be NULL) atom_virial [N,6] f32 and
+ * grad_strain [n_structs,6] f64, both in the order xx, yy, zz, yz, xz, xy;
+ * struct_ptr/n_structs are read only when grad_strain is requested.
  * ------------------------------------------------------------------------ */
 size_t mlip_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_edge,
                                int32_t d_node, int32_t d_hidden);
@@ -188,7 +193,8 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    const float *W2, int32_t n_rbf, int32_t d_edge, int32_t d_node,
                    int32_t d_hidden, int32_t n_types, int32_t n_experts, int32_t top_k,
                    float cutoff, const float *grad_out, float *grad_h, float *grad_pos,
-                   void *ws, size_t ws_bytes, void *stream);
+                   const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
+                   double *grad_strain, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  When enabled, every kernel launch of the library is

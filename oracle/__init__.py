@@ -36,7 +36,8 @@ PINS = {
     "block.moe_forward": "shared experts reduce to one dense MLP; X=k=1; expert relabelling; "
                          "scalar closed form",
     "block.readout": "dimer closed form",
-    "block.block_vjp": "float64 central finite differences (positions, node features); "
-                       "translation/rotation/permutation invariance; sum of forces = 0; "
+    "block.block_vjp": "float64 central finite differences (positions, node features, "
+                       "homogeneous strain of positions and cell); translation/rotation/"
+                       "permutation invariance; sum of forces = 0; symmetric strain gradient; "
                        "dimer closed form",
 }

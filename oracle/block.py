@@ -224,11 +224,15 @@ def block_forward(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray]) -> D
 
 def block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray],
               fwd: Dict[str, np.ndarray], g: np.ndarray) -> Dict[str, np.ndarray]:
-    """Input gradient of one block: given g = dL/dh', return dL/dh and dL/dx.
+    """Input gradient of one block: given g = dL/dh', return dL/dh, dL/dx and
+    dL/d(strain).
 
-    With g_i = w_r for every atom, dL/dx is dE/dx and the forces are -dL/dx.
-    The chain rule is applied step by step in reverse; edge sums are plain
-    scatters over both endpoints of every edge.
+    With g_i = w_r for every atom, dL/dx is dE/dx and the forces are -dL/dx;
+    dL/d(strain) per structure divided by the cell volume is the stress
+    ([review] 3.3: forces and stresses both come from differentiating the
+    energy).  The strain is the homogeneous deformation x -> (I + eps) x of
+    positions and cell vectors.  The chain rule is applied step by step in
+    reverse; edge sums are plain scatters over both endpoints of every edge.
     """
     rc = _cutoff(inp)
     N = fwd["u"].shape[0]
@@ -249,7 +253,26 @@ def block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray],
     gpos = np.zeros((N, 3), f64)
     np.add.at(gpos, src, c[:, None] * dhat)
     np.add.at(gpos, recv, -c[:, None] * dhat)
-    return dict(ubar=ubar, abar=abar, sbar=sbar, grad_h=hbar, c=c, grad_pos=gpos)
+    # homogeneous strain x -> (I + eps) x of positions and cell:
+    # d_e -> (I + eps) d_e, so dL/deps_ab = sum_e c_e dhat_a d_b
+    outer = c[:, None, None] * dhat[:, :, None] * d[:, None, :]          # [E, 3, 3]
+    sp = np.asarray(inp["struct_ptr"], np.int64)
+    B = len(sp) - 1
+    sb_of_edge = np.searchsorted(sp, recv, side="right") - 1
+    gstrain = np.zeros((B, 3, 3), f64)
+    np.add.at(gstrain, sb_of_edge, outer)
+    # per-atom share: half of every edge term to each of its two atoms
+    av = np.zeros((N, 3, 3), f64)
+    np.add.at(av, recv, 0.5 * outer)
+    np.add.at(av, src, 0.5 * outer)
+    return dict(ubar=ubar, abar=abar, sbar=sbar, grad_h=hbar, c=c, grad_pos=gpos,
+                grad_strain=gstrain, atom_virial=voigt(av))
+
+
+def voigt(t: np.ndarray) -> np.ndarray:
+    """[..., 3, 3] -> [..., 6] in the order xx, yy, zz, yz, xz, xy."""
+    return np.stack([t[..., 0, 0], t[..., 1, 1], t[..., 2, 2],
+                     t[..., 1, 2], t[..., 0, 2], t[..., 0, 1]], axis=-1)
 
 
 def energy(inp: Dict[str, np.ndarray], pos: Optional[np.ndarray] = None,

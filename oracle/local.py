@@ -153,6 +153,7 @@ class LocalBlock:
         Dn = self.W_u.shape[1]
         grad_h = np.zeros((len(atoms), Dn), f64)
         grad_pos = np.zeros((len(atoms), 3), f64)
+        virial = np.zeros((len(atoms), 3, 3), f64)
         for n, i in enumerate(atoms):
             ii = idx[i]
             rw, cl = self.row(i), self.col(i)
@@ -163,6 +164,7 @@ class LocalBlock:
                 c = np.sum(abar[ii][None, :] * s_need[js] * de, axis=1)
                 dhat = np.where(rw["r"][:, None] > 0, rw["d"] / np.maximum(rw["r"], 1e-300)[:, None], 0.0)
                 grad_pos[n] -= (c[:, None] * dhat).sum(axis=0)
+                virial[n] += 0.5 * np.einsum("e,ea,eb->ab", c, dhat, rw["d"])
             # edges with sender i: sbar_i += e * abar_recv; contributes +c dhat
             sbar = np.zeros(self.W_u.shape[0], f64)
             if cl["r"].size:
@@ -173,5 +175,6 @@ class LocalBlock:
                 c = np.sum(abar[js] * s_need[ii][None, :] * de, axis=1)
                 dhat = np.where(cl["r"][:, None] > 0, cl["d"] / np.maximum(cl["r"], 1e-300)[:, None], 0.0)
                 grad_pos[n] += (c[:, None] * dhat).sum(axis=0)
+                virial[n] += 0.5 * np.einsum("e,ea,eb->ab", c, dhat, cl["d"])
             grad_h[n] = ubar[ii] + sbar @ self.W_d.T
-        return dict(grad_h=grad_h, grad_pos=grad_pos)
+        return dict(grad_h=grad_h, grad_pos=grad_pos, atom_virial=B.voigt(virial))

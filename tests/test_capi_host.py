@@ -76,9 +76,16 @@ def test_aggregate_and_moe_reject_bad_args(mlip):
     assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_moe_forward(f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, f, f, f, f, f, None, 0, None)
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
-    rc = L.mlip_block_vjp(f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f, 16, 32, 64, 130,
-                          4, 8, 2, 5.0, f, f, f, f, 1 << 30, None)
+    def vjp(d_hidden, struct_ptr, n_structs, grad_strain):
+        # graph (3), sizes (2), saved state (8), weights (5), dims (7), cutoff,
+        # grad_out/grad_h/grad_pos, struct_ptr/n_structs, atom_virial/grad_strain, ws
+        return L.mlip_block_vjp(f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f,
+                                16, 32, 64, d_hidden, 4, 8, 2, 5.0, f, f, f,
+                                struct_ptr, n_structs, None, grad_strain, f, 1 << 30, None)
+    rc = vjp(130, None, 0, None)
     assert "d_hidden" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = vjp(128, None, 0, f)
+    assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
 def test_profile_api_without_gpu(mlip):

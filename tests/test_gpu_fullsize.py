@@ -130,16 +130,20 @@ def test_fullsize(mlip, name):
     lf = lb.forward(fwd_atoms)
     errs = {"h_out": rel(blk.moe["h_out"].cpu().numpy()[fwd_atoms], lf["h2"]),
             "eps": rel(blk.ro["eps"].cpu().numpy()[fwd_atoms], lf["eps"])}
+    sp = inp["struct_ptr"]
     vjp_atoms = _sample_atoms(cfg, inp["z"], 3, seed=3)
     _say(f"{name}: oracle VJP at {len(vjp_atoms)} atoms")
     lv = lb.vjp(vjp_atoms, gup)
     errs["grad_h"] = rel(blk.vjp["grad_h"].cpu().numpy()[vjp_atoms], lv["grad_h"])
     errs["grad_pos"] = rel(blk.vjp["grad_pos"].cpu().numpy()[vjp_atoms], lv["grad_pos"])
-    # per-structure energies are the float64 sums of eps
+    errs["atom_virial"] = rel(blk.vjp["atom_virial"].cpu().numpy()[vjp_atoms], lv["atom_virial"])
+    av = blk.vjp["atom_virial"].cpu().numpy().astype(np.float64)
+    gs_ref = np.stack([av[sp[b]:sp[b + 1]].sum(0) for b in range(cfg.n_structs)])
+    # per-structure energies and strain gradients are float64 sums of per-atom terms
     eps = blk.ro["eps"].cpu().numpy().astype(np.float64)
-    sp = inp["struct_ptr"]
     e_ref = np.array([eps[sp[b]:sp[b + 1]].sum() for b in range(cfg.n_structs)])
     errs["energy_sum"] = rel(blk.ro["energy"].cpu().numpy(), e_ref)
+    errs["strain_sum"] = rel(blk.vjp["grad_strain"].cpu().numpy(), gs_ref)
     _say(f"{name}: errors {errs}")
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, bad

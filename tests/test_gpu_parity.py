@@ -104,6 +104,8 @@ def test_block_parity(mlip, name, upstream):
         "energy": rel(blk.ro["energy"], f["E"]),
         "grad_h": rel(blk.vjp["grad_h"], v["grad_h"]),
         "grad_pos": rel(blk.vjp["grad_pos"], v["grad_pos"]),
+        "atom_virial": rel(blk.vjp["atom_virial"], v["atom_virial"]),
+        "grad_strain": rel(blk.vjp["grad_strain"], OB.voigt(v["grad_strain"])),
     }
     # the kept pre-activations, in dispatch order
     P_ref = np.concatenate([

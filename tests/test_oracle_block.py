@@ -298,3 +298,48 @@ def test_local_oracle_matches_full(name):
     lv = lb.vjp(atoms, g_up)
     assert np.allclose(lv["grad_h"], v["grad_h"][atoms], atol=1e-10)
     assert np.allclose(lv["grad_pos"], v["grad_pos"][atoms], atol=1e-10)
+    assert np.allclose(lv["atom_virial"], v["atom_virial"][atoms], atol=1e-10)
+
+
+# ------------------------------------------------------------- strain ----
+def test_strain_gradient_fd():
+    """dL/d(eps) against central differences of x -> (I + eps) x (positions and cell)."""
+    cfg, inp = _tiny()
+    for kind in ("energy", "random"):
+        g, f = _full(inp)
+        g_up = synth.upstream_grad(cfg, inp, kind).astype(np.float64)
+        v = B.block_vjp(inp, g, f, g_up)
+        gs = v["grad_strain"][0]
+        assert np.allclose(gs, gs.T, atol=1e-10 * np.max(np.abs(gs)))
+        pos = inp["pos"].astype(np.float64)
+        cell = inp["cell"].astype(np.float64)
+        step = 1e-6
+        fd = np.zeros((3, 3))
+        for a in range(3):
+            for b in range(3):
+                vals = []
+                for sgn in (1.0, -1.0):
+                    F = np.eye(3)
+                    F[a, b] += sgn * step
+                    q = dict(inp, pos=pos @ F.T, cell=cell @ F.T)
+                    gr = G.radius_graph(q["pos"], q["cell"], q["struct_ptr"], q["cutoff"])
+                    vals.append(float(np.sum(B.block_forward(q, gr)["h2"] * g_up)))
+                fd[a, b] = (vals[0] - vals[1]) / (2 * step)
+        assert np.max(np.abs(fd - gs)) <= 1e-6 * np.max(np.abs(gs)), (fd, gs)
+        # the per-atom shares add up to the structure total
+        assert np.allclose(v["atom_virial"].sum(0), B.voigt(gs), atol=1e-10 * np.max(np.abs(gs)))
+
+
+def test_strain_gradient_dimer():
+    # dimer along x: only the xx component, equal to dE/dr * r
+    gold = {}
+    for line in open(os.path.join(GOLD, "dimer.txt")):
+        line = line.split("#")[0].split()
+        if line:
+            gold[line[0]] = float(line[1])
+    inp = _dimer()
+    g, f = _full(inp)
+    v = B.block_vjp(inp, g, f, np.ones((2, 1)))
+    gs = v["grad_strain"][0]
+    assert abs(gs[0, 0] - gold["dEdr"] * 2.0) < 1e-12
+    assert np.all(np.abs(gs.ravel()[1:]) < 1e-15)
