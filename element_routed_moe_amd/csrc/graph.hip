@@ -316,7 +316,8 @@ __global__ void __launch_bounds__(64) graph_count(const float *__restrict__ pos,
   }
   if (threadIdx.x == 0) {
     deg[i] = count;
-    atomicMax(maxdeg, count);
+    // most rows are not the longest: a plain read skips their atomics
+    if (count > __atomic_load_n(maxdeg, __ATOMIC_RELAXED)) atomicMax(maxdeg, count);
   }
 }
 
