@@ -37,18 +37,10 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-#ifndef GEMM_RASTER
-#define GEMM_RASTER 8
-#endif
-#ifndef GEMM_XCD_REMAP
-#define GEMM_XCD_REMAP 1
-#endif
-#ifndef EXPERT_BK
-#define EXPERT_BK 32
-#endif
 constexpr int THREADS = 256;
 constexpr int N_XCD = 8;
-constexpr int RASTER_M = GEMM_RASTER;
+constexpr int RASTER_M = 8;
+constexpr int EXPERT_BK = 32;
 constexpr int MAX_GROUPS = 1024;
 
 // Exclusive scan over the 256 threads of the block (one value each).
@@ -67,8 +59,12 @@ __device__ inline int block_scan_excl(int v, int *red) {
   return off + x - v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG>
-__global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
+// One BM x BN output tile: rows [row0, min(row0 + BM, rows)) of the A row
+// space, columns [n0, n0 + BN).  As / Bs are the two LDS stages, AST / BST
+// floats apart.
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int AST, int BST>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *Bs_, const float *Bg,
+                                          int row0, int rows, int n0) {
   static_assert(WM * WN == 4, "four wavefronts");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -80,73 +76,16 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
   constexpr int B_LOADS = BN * KQ / THREADS;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * KQ % THREADS == 0 && BN * KQ % THREADS == 0,
                 "load split");
-
-  __shared__ float As[2][BM * LDK];
-  __shared__ float Bs[2][BT ? (BN * LDK) : (BK * LDN)];
-  __shared__ int s_tiles[MAX_GROUPS + 1];
-  __shared__ int s_red[4];
+  static_assert(BM * LDK <= AST && (BT ? BN * LDK : BK * LDN) <= BST, "LDS stage size");
+  typedef float AStage[AST];
+  typedef float BStage[BST];
+  AStage *As = reinterpret_cast<AStage *>(As_);
+  BStage *Bs = reinterpret_cast<BStage *>(Bs_);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-
-  // ---- tiles per group -> prefix in LDS ----
-  int Mt;
-  const int G = g.group_off ? g.n_groups : 1;
-  if (g.group_off) {
-    constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
-    int cnt[PER], sum = 0;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int gi = tid * PER + q;
-      cnt[q] = gi < G ? (g.group_off[gi + 1] - g.group_off[gi] + BM - 1) / BM : 0;
-      sum += cnt[q];
-    }
-    int run = block_scan_excl(sum, s_red);
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int gi = tid * PER + q;
-      if (gi <= G) s_tiles[gi] = run;
-      run += cnt[q];
-    }
-    __syncthreads();
-    Mt = s_tiles[G];
-  } else {
-    Mt = (g.M + BM - 1) / BM;
-  }
-  const int Nt = (g.N + BN - 1) / BN;
-  const int total = Mt * Nt;
-  const int per = (total + N_XCD - 1) / N_XCD;
-  const int L = blockIdx.x;
-  const int jx = L / N_XCD, xcd = L - jx * N_XCD;
-  if (GEMM_XCD_REMAP && jx >= per) return;
-  const int T = GEMM_XCD_REMAP ? xcd * per + jx : L;
-  if (T >= total) return;
-  const int group_size = RASTER_M * Nt;
-  const int first_m = (T / group_size) * RASTER_M;
-  const int gm = min(Mt - first_m, RASTER_M);
-  const int rr = T % group_size;
-  const int mt_glob = first_m + rr % gm;
-  const int nt = rr / gm;
-
-  int grp = 0, row0, rows;
-  if (g.group_off) {
-    int lo = 0, hi = G;  // last group with s_tiles[grp] <= mt_glob
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_tiles[mid] <= mt_glob) lo = mid;
-      else hi = mid;
-    }
-    grp = lo;
-    row0 = g.group_off[grp] + (mt_glob - s_tiles[grp]) * BM;
-    rows = g.group_off[grp + 1];
-  } else {
-    row0 = mt_glob * BM;
-    rows = g.M;
-  }
-  const int n0 = nt * BN;
-  const float *Bg = g.B + int64_t(grp) * g.b_group_stride;
 
   // ---- per-thread global load assignments ----
   const float *a_src[A_LOADS];
@@ -323,32 +262,159 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG>
+// Expert GEMMs (group_off set, SPLIT): each group's rows are covered by
+// BM-row tiles, except that a remainder of at most BM/2 rows gets a BM/2-row
+// tile.  The two classes are dealt to the XCDs separately, full tiles first,
+// so every XCD receives its share of each and the short tiles run last.
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT>
+__global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
+  constexpr int LDK = BK + 4;
+  constexpr int LDN = BN + 4;
+  constexpr int AST = BM * LDK;
+  constexpr int BST = BT ? (BN * LDK) : (BK * LDN);
+  constexpr int HALF = BM / 2;
+  __shared__ __attribute__((aligned(16))) float As[2 * AST];
+  __shared__ __attribute__((aligned(16))) float Bs[2 * BST];
+  __shared__ int s_tiles[MAX_GROUPS + 1];
+  __shared__ int s_red[10];   // two scans' wave sums, then the two totals
+
+  const int tid = threadIdx.x;
+  const int G = g.group_off ? g.n_groups : 1;
+  const int Nt = (g.N + BN - 1) / BN;
+  const int L = blockIdx.x;
+  const int jx = L / N_XCD, xcd = L - jx * N_XCD;
+
+  // ---- m-tiles per group (full and, with SPLIT, half) -> prefix in LDS ----
+  int Mt, t_local;
+  bool half = false;
+  if (g.group_off) {
+    constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
+    int cf[PER], ch[PER], sf = 0, sh = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int gi = tid * PER + q;
+      const int c = gi < G ? g.group_off[gi + 1] - g.group_off[gi] : 0;
+      if (SPLIT) {
+        const int rem = c % BM;
+        cf[q] = c / BM + (rem > HALF ? 1 : 0);
+        ch[q] = (rem > 0 && rem <= HALF) ? 1 : 0;
+      } else {
+        cf[q] = (c + BM - 1) / BM;
+        ch[q] = 0;
+      }
+      sf += cf[q];
+      sh += ch[q];
+    }
+    int run_f = block_scan_excl(sf, s_red);
+    int run_h = SPLIT ? block_scan_excl(sh, s_red + 4) : 0;
+    int Mf = 0, Mh = 0;
+    if (tid == THREADS - 1) {
+      s_red[8] = run_f + sf;
+      s_red[9] = run_h + sh;
+    }
+    __syncthreads();
+    Mf = s_red[8];
+    Mh = SPLIT ? s_red[9] : 0;
+    const int per_f = (Mf * Nt + N_XCD - 1) / N_XCD;
+    const int per_h = (Mh * Nt + N_XCD - 1) / N_XCD;
+    if (jx < per_f) {
+      t_local = xcd * per_f + jx;
+      Mt = Mf;
+    } else {
+      if (!SPLIT || jx - per_f >= per_h) return;
+      t_local = xcd * per_h + (jx - per_f);
+      Mt = Mh;
+      half = true;
+    }
+    if (t_local >= Mt * Nt) return;
+    // prefix of this block's class only
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int gi = tid * PER + q;
+      if (gi <= G) s_tiles[gi] = half ? run_h : run_f;
+      run_f += cf[q];
+      run_h += ch[q];
+    }
+    __syncthreads();
+  } else {
+    Mt = (g.M + BM - 1) / BM;
+    const int per = (Mt * Nt + N_XCD - 1) / N_XCD;
+    if (jx >= per) return;
+    t_local = xcd * per + jx;
+    if (t_local >= Mt * Nt) return;
+  }
+  const int group_size = RASTER_M * Nt;
+  const int first_m = (t_local / group_size) * RASTER_M;
+  const int gm = min(Mt - first_m, RASTER_M);
+  const int rr = t_local % group_size;
+  const int mt_glob = first_m + rr % gm;
+  const int nt = rr / gm;
+
+  int grp = 0, row0, rows;
+  if (g.group_off) {
+    int lo = 0, hi = G;  // last group with s_tiles[grp] <= mt_glob
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tiles[mid] <= mt_glob) lo = mid;
+      else hi = mid;
+    }
+    grp = lo;
+    const int gbeg = g.group_off[grp];
+    rows = g.group_off[grp + 1];
+    if (half) row0 = gbeg + ((rows - gbeg) / BM) * BM;
+    else row0 = gbeg + (mt_glob - s_tiles[grp]) * BM;
+  } else {
+    row0 = mt_glob * BM;
+    rows = g.M;
+  }
+  const int n0 = nt * BN;
+  const float *Bg = g.B + int64_t(grp) * g.b_group_stride;
+  if constexpr (SPLIT) {
+    if (half) {
+      gemm_tile<HALF, BN, BK, WM, WN, BT, EPI, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+      return;
+    }
+  }
+  gemm_tile<BM, BN, BK, WM, WN, BT, EPI, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT>
 int launch_t(const GemmArgs &a, hipStream_t stream) {
-  const int64_t mt_upper = cdiv(a.M, BM) + (a.group_off ? a.n_groups : 0);
-  const int64_t total_upper = mt_upper * cdiv(a.N, BN);
-  const int64_t grid = cdiv(total_upper, N_XCD) * N_XCD;
+  // Upper bounds of the per-XCD tile counts the kernel derives on the device:
+  // full tiles <= (M + G*BM/2) / BM and half tiles <= G with SPLIT,
+  // ceil(M/BM) + G tiles without it; surplus workgroups return at once.
+  const int64_t nt = cdiv(a.N, BN);
+  int64_t per;
+  if (!a.group_off) {
+    per = cdiv(cdiv(a.M, BM) * nt, N_XCD);
+  } else if (SPLIT) {
+    const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * (BM / 2)) / BM;
+    per = cdiv(mf * nt, N_XCD) + cdiv(int64_t(a.n_groups) * nt, N_XCD);
+  } else {
+    per = cdiv((cdiv(a.M, BM) + a.n_groups) * nt, N_XCD);
+  }
+  const int64_t grid = per * N_XCD;
   if (grid <= 0) return MLIP_OK;
   if (grid > int64_t(0x7fffffff)) {
     set_error("GEMM too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
   }
-  gemm_kernel<BM, BN, BK, WM, WN, BT, EPI, TAG><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
+  gemm_kernel<BM, BN, BK, WM, WN, BT, EPI, TAG, SPLIT><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
 
-// Expert GEMMs: 128 x 128 tiles.
+// Expert GEMMs: 128 x 128 tiles, 64 x 128 for short group remainders.
 template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
-  return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG>(a, s);
+  return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG, true>(a, s);
 }
 // Dense projections: 64 x 64 tiles when the output is narrow (enough
 // workgroups for 256 CUs), else 64 x 128.
 template <bool BT, int EPI, int TAG>
 int launch_dense(const GemmArgs &a, hipStream_t s) {
-  if (a.N <= 512) return launch_t<64, 64, 32, 2, 2, BT, EPI, TAG>(a, s);
-  return launch_t<64, 128, 32, 2, 2, BT, EPI, TAG>(a, s);
+  if (a.N <= 512) return launch_t<64, 64, 32, 2, 2, BT, EPI, TAG, false>(a, s);
+  return launch_t<64, 128, 32, 2, 2, BT, EPI, TAG, false>(a, s);
 }
 
 }  // namespace
