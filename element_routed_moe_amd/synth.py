@@ -56,6 +56,8 @@ class BlockConfig:
     target_degree: Optional[float] = None
     zipf: Optional[float] = None             # None -> uniform element types
     description: str = ""
+    n_heads: int = 0                         # attention heads of the complete block
+    d_attn: int = 0                          # attention width Da (0: no complete block)
 
     def atoms_list(self) -> List[int]:
         if isinstance(self.atoms_per_struct, int):
@@ -97,24 +99,25 @@ def _reg(c: BlockConfig) -> BlockConfig:
 # The five workloads of the block: a tiny reference case, the S/M/L widths of
 # Table II, and one GPU's graph-partition share at S widths.
 TINY = _reg(BlockConfig(
-    "tiny", 64, 1, 5.0, 4, 16, 32, 64, 128, 8, 2, seed=0, box=8.0,
+    "tiny", 64, 1, 5.0, 4, 16, 32, 64, 128, 8, 2, seed=0, box=8.0, n_heads=4, d_attn=32,
     description="1 cubic cell of edge 8 A, 64 atoms, 4 uniform types, r_c 5 A, "
                 "De 32, Dn 64, 8 experts top-2, MLP 64->128->64"))
 S = _reg(BlockConfig(
     "S", 128, 32, 6.0, 16, 16, 384, 2560, 2560, 72, 4, seed=1, target_degree=50.0,
+    n_heads=8, d_attn=384,
     description="32 cells x 128 atoms, ~50 nbrs at 6 A, 16 uniform types, De 384, "
                 "Dn 2560, 72 experts top-4, MLP 2560->2560->2560"))
 M = _reg(BlockConfig(
     "M", 128, 128, 6.0, 32, 16, 1536, 1536, 1536, 40, 8, seed=2, target_degree=50.0,
-    zipf=1.1,
+    zipf=1.1, n_heads=4, d_attn=512,
     description="128 cells x 128 atoms, 32 Zipf(1.1) types, De=Dn=H=1536, 40 experts top-8"))
 L = _reg(BlockConfig(
     "L", 128, 64, 6.0, 64, 16, 1920, 1920, 1920, 72, 16, seed=3, target_degree=50.0,
-    zipf=1.1,
+    zipf=1.1, n_heads=4, d_attn=512,
     description="64 cells x 128 atoms, 64 Zipf(1.1) types, De=Dn=H=1920, 72 experts top-16"))
 SHARE = _reg(BlockConfig(
     "share", 262144, 1, 6.0, 89, 16, 384, 2560, 2560, 72, 4, seed=4, target_degree=60.0,
-    zipf=1.3,
+    zipf=1.3, n_heads=8, d_attn=384,
     description="one periodic supercell of 262144 atoms, ~60 nbrs at 6 A, 89 Zipf(1.3) "
                 "types, S widths"))
 
@@ -122,23 +125,27 @@ SHARE = _reg(BlockConfig(
 # see several tiles, ragged tails and uneven structures.
 RAGGED = _reg(BlockConfig(
     "ragged", [97, 130, 61, 1, 0, 200], 6, 5.5, 5, 16, 100, 132, 196, 7, 3, seed=11,
-    box=[10.5, 11.0, 9.25, 12.0, 7.0, 14.5],
+    box=[10.5, 11.0, 9.25, 12.0, 7.0, 14.5], n_heads=3, d_attn=72,
     description="6 uneven cells (incl. a 1-atom and an empty one), dims not tile multiples"))
 CELLLIST = _reg(BlockConfig(
     "celllist", 3000, 1, 5.0, 6, 16, 64, 96, 160, 9, 2, seed=12, target_degree=45.0,
-    zipf=1.2,
+    zipf=1.2, n_heads=2, d_attn=64,
     description="one 3000-atom cell large enough for a >=3 bins/axis cell list"))
 S_SLICE = _reg(BlockConfig(
     "S_slice", 128, 2, 6.0, 16, 16, 384, 2560, 2560, 72, 4, seed=13, target_degree=50.0,
+    n_heads=8, d_attn=384,
     description="two cells at the full S widths (production tiles at oracle-friendly size)"))
 SPARSE = _reg(BlockConfig(
     "sparse", [5, 3, 9], 3, 3.0, 3, 16, 36, 40, 44, 3, 3, seed=14, box=[30.0, 25.0, 28.0],
+    n_heads=3, d_attn=36,
     description="dilute cells with isolated atoms (degree 0 rows), k = X"))
 WIDE_RAGGED = _reg(BlockConfig(
     "wide_ragged", [150, 139], 2, 5.0, 5, 16, 100, 1028, 260, 5, 2, seed=16, box=[11.0, 10.5],
+    n_heads=5, d_attn=80,
     description="wide node features with ragged K/N tails (K-sliced projections)"))
 TOP1 = _reg(BlockConfig(
     "top1", [40, 33], 2, 4.0, 2, 16, 48, 68, 72, 5, 1, seed=15, box=[7.0, 6.5],
+    n_heads=1, d_attn=48,
     description="top-1 routing (gate exactly 1), images because r_c > L/2"))
 
 
@@ -194,6 +201,30 @@ def make_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, np.nd
     out["w_r"] = _normal(rng, (Dn,), 1.0 / math.sqrt(Dn))
     out["cutoff"] = np.float32(cfg.cutoff)
     out["top_k"] = int(cfg.top_k)
+    return out
+
+
+def make_full_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the complete block (MoE0, attention, MoE1): ``make_inputs``
+    plus the extra parameters, drawn from a second generator seeded with
+    (seed, 1) in this order: the MoE0 logit table logits0 ~ N(0,1) [T, X];
+    Wa_e [K, Da]; W_qkv [Dn, 3 Da] (columns q | k | v); W_o [Da, Dn];
+    W1_0 [X, Dn, H]; W2_0 [X, H, Dn] (weights ~ N(0, 1/fan_in)).  MoE1 uses
+    ``logits``, ``W1``, ``W2`` and the readout ``w_r`` of ``make_inputs``."""
+    if cfg.d_attn <= 0 or cfg.n_heads <= 0:
+        raise ValueError(f"config {cfg.name} has no attention width")
+    out = make_inputs(cfg, seed)
+    base = cfg.seed if seed is None else seed
+    rng = np.random.default_rng([base, 1])
+    T, X, K = cfg.n_types, cfg.n_experts, cfg.n_rbf
+    Dn, H, Da = cfg.d_node, cfg.d_hidden, cfg.d_attn
+    out["logits0"] = _normal(rng, (T, X), 1.0)
+    out["Wa_e"] = _normal(rng, (K, Da), 1.0 / math.sqrt(K))
+    out["W_qkv"] = _normal(rng, (Dn, 3 * Da), 1.0 / math.sqrt(Dn))
+    out["W_o"] = _normal(rng, (Da, Dn), 1.0 / math.sqrt(Da))
+    out["W1_0"] = _normal(rng, (X, Dn, H), 1.0 / math.sqrt(Dn))
+    out["W2_0"] = _normal(rng, (X, H, Dn), 1.0 / math.sqrt(H))
+    out["n_heads"] = int(cfg.n_heads)
     return out
 
 

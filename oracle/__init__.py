@@ -40,4 +40,13 @@ PINS = {
                        "homogeneous strain of positions and cell); translation/rotation/"
                        "permutation invariance; sum of forces = 0; symmetric strain gradient; "
                        "dimer closed form",
+    "attention.neighbour_softmax": "scipy.special.softmax of (score + log f_c) per receiver/head; "
+                                   "empty rows give 0",
+    "attention.attention_forward": "one neighbour -> weights 1 and the pinned aggregation; zero "
+                                   "query -> envelope-weighted mean; head relabelling / in-head "
+                                   "channel permutation invariance, cross-head move changes it",
+    "attention.full_block_forward": "translation/rotation/permutation invariance; energy "
+                                    "continuous (quadratic) across r_c",
+    "attention.full_block_vjp": "float64 central finite differences (positions, node features, "
+                                "strain per structure); sum of forces = 0; virial shares add up",
 }

@@ -236,7 +236,7 @@ def block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray],
     """
     rc = _cutoff(inp)
     N = fwd["u"].shape[0]
-    recv, src, r, d = graph["recv"], graph["src"], graph["r"], graph["d"]
+    recv, src, r = graph["recv"], graph["src"], graph["r"]
     g = np.asarray(g, f64)
     ubar = moe_vjp(fwd["u"], g, inp["z"], fwd["topk"], fwd["gate"], inp["W1"], inp["W2"])
     abar = ubar @ np.asarray(inp["W_u"], f64).T
@@ -247,26 +247,36 @@ def block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray],
     # dL/dr_e = sum_c (abar_recv * s_src)_c * (d e_e / d r)_c
     ebar = abar[recv] * fwd["s"][src]
     c = np.sum(ebar * edge_embedding_dr(r, inp["W_e"], rc), axis=1)
-    # r = |d|, d = x_src - x_recv + S.C  ->  dr/dx_src = d/r, dr/dx_recv = -d/r
+    gpos, gstrain, av = edge_forces(c, graph, N, inp["struct_ptr"])
+    return dict(ubar=ubar, abar=abar, sbar=sbar, grad_h=hbar, c=c, grad_pos=gpos,
+                grad_strain=gstrain, atom_virial=av)
+
+
+def edge_forces(c: np.ndarray, graph: Dict[str, np.ndarray], n_atoms: int,
+                struct_ptr: np.ndarray):
+    """Position gradient, strain gradient and per-atom virial from c_e = dL/dr_e.
+
+    r = |d|, d = x_src - x_recv + S.C, so dr/dx_src = d/r and dr/dx_recv = -d/r.
+    Under the homogeneous strain x -> (I + eps) x of positions and cell,
+    d_e -> (I + eps) d_e and dL/deps_ab = sum_e c_e dhat_a d_b; each atom of
+    an edge gets half of that edge's term in its virial (Voigt order).
+    """
+    recv, src, r, d = graph["recv"], graph["src"], graph["r"], graph["d"]
     with np.errstate(invalid="ignore", divide="ignore"):
         dhat = np.where(r[:, None] > 0, d / r[:, None], 0.0)
-    gpos = np.zeros((N, 3), f64)
+    gpos = np.zeros((n_atoms, 3), f64)
     np.add.at(gpos, src, c[:, None] * dhat)
     np.add.at(gpos, recv, -c[:, None] * dhat)
-    # homogeneous strain x -> (I + eps) x of positions and cell:
-    # d_e -> (I + eps) d_e, so dL/deps_ab = sum_e c_e dhat_a d_b
     outer = c[:, None, None] * dhat[:, :, None] * d[:, None, :]          # [E, 3, 3]
-    sp = np.asarray(inp["struct_ptr"], np.int64)
-    B = len(sp) - 1
+    sp = np.asarray(struct_ptr, np.int64)
+    nb = len(sp) - 1
     sb_of_edge = np.searchsorted(sp, recv, side="right") - 1
-    gstrain = np.zeros((B, 3, 3), f64)
+    gstrain = np.zeros((nb, 3, 3), f64)
     np.add.at(gstrain, sb_of_edge, outer)
-    # per-atom share: half of every edge term to each of its two atoms
-    av = np.zeros((N, 3, 3), f64)
+    av = np.zeros((n_atoms, 3, 3), f64)
     np.add.at(av, recv, 0.5 * outer)
     np.add.at(av, src, 0.5 * outer)
-    return dict(ubar=ubar, abar=abar, sbar=sbar, grad_h=hbar, c=c, grad_pos=gpos,
-                grad_strain=gstrain, atom_virial=voigt(av))
+    return gpos, gstrain, voigt(av)
 
 
 def voigt(t: np.ndarray) -> np.ndarray:
