@@ -1,0 +1,525 @@
+// Neighbour multi-head attention of the complete interaction block and its
+// input gradient.
+//
+// The paper review of "Breaking the Training Barrier of Billion-Parameter
+// Universal MLIPs" (section 3.2) replaces the separable attention of MatRIS
+// by multi-head self-attention whose cost stays O(N) at a fixed cutoff, with
+// sparse MoE layers before and after it; Table II gives the heads and width
+// (S: 8 x 48).  Attention runs over each atom's radius-graph neighbours:
+//   e_ij   = f_c(r) (phi(r) @ Wa_e)                    (attention width Da)
+//   s_ij^t = sum_{c in head t} q_ic k_jc e_ijc / sqrt(dh)
+//   a_ij^t = f_c(r_ij) exp(s_ij^t) / sum_l f_c(r_il) exp(s_il^t)
+//   o_ic   = sum_j a_ij^{t(c)} v_jc e_ijc
+// with [q | k | v] = h0 @ W_qkv computed by the dense GEMM beforehand.
+//
+// Layout: one 64-lane workgroup per receiver row, all heads in the one
+// wavefront.  Lane l serves head t = l / LPH and the CPL consecutive channels
+// t*dh + (l % LPH)*CPL ...; a head's dot products are summed over its LPH
+// lanes with xor shuffles (LPH a power of two, so groups never straddle).
+// The softmax is accumulated online (running maximum, rescaled sums).  The
+// per-edge radial terms are computed once per edge (lane = edge) and read
+// from LDS by every lane.  Rows are private to one wavefront: no atomics.
+//
+// Gradient, in two row passes (dL/do = obar, beta_i^t = <obar_i, o_i>_t):
+//   receiver pass (row i): gbar_ij^t = a_ij^t (<obar_i, v_j e_ij>_t - beta_i^t),
+//     qbar_i += gbar k_j e / sqrt(dh), dL/dr_ij = ebar . de/dr + fbar f_c'(r)
+//     with ebar = gbar q_i k_j / sqrt(dh) + a obar_i v_j and fbar the
+//     derivative through the envelope weight; gbar, a and dL/dr are stored
+//     per edge.
+//   sender pass (row j, edges j <- i): the reverse edge i <- j carries the
+//     receiver-pass values, so kbar_j = sum gbar_rev q_i e / sqrt(dh),
+//     vbar_j = sum a_rev obar_i e, and the forces and virial take
+//     dL/dr_e + dL/dr_rev(e) as in the aggregation's gradient.
+#include <cmath>
+
+#include "common.h"
+
+namespace mlip {
+
+namespace {
+
+constexpr int K = MLIP_N_RBF;
+constexpr int KQ = K / 4;
+constexpr int CHUNK = 64;
+constexpr int UNROLL = 2;
+
+// CPL consecutive floats (vector loads where CPL allows; the channel offset
+// is a multiple of CPL, and rows are multiples of 4 floats long)
+template <int CPL>
+__device__ inline void ldc(const float *p, float (&x)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4 *>(p)[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+  } else if constexpr (CPL % 2 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 2; ++q) {
+      const float2 v = reinterpret_cast<const float2 *>(p)[q];
+      x[2 * q] = v.x; x[2 * q + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) x[q] = p[q];
+  }
+}
+
+template <int CPL>
+__device__ inline void stc(float *p, const float (&x)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q)
+      reinterpret_cast<float4 *>(p)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  } else if constexpr (CPL % 2 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 2; ++q) reinterpret_cast<float2 *>(p)[q] = make_float2(x[2 * q], x[2 * q + 1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) p[q] = x[q];
+  }
+}
+
+// Sum over the lph lanes of one head (aligned power-of-two lane groups).
+__device__ inline float head_sum(float v, int lph) {
+  for (int d = lph >> 1; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// e_c = sum_k b[k] w[k][c] for the lane's channels, b read from LDS as float4
+template <int CPL>
+__device__ inline void basis_map(const float4 *b, const float (&w)[K][CPL], float (&e)[CPL]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) e[c] = 0.f;
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) {
+    const float4 p = b[kq];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      e[c] += p.x * w[4 * kq][c] + p.y * w[4 * kq + 1][c] + p.z * w[4 * kq + 2][c] + p.w * w[4 * kq + 3][c];
+  }
+}
+
+struct Lanes {
+  int t, c0;
+  bool active;
+};
+
+template <int CPL>
+__device__ inline Lanes lane_map(int lane, int nh, int lph) {
+  Lanes L;
+  const int dh = lph * CPL;
+  L.t = lane / lph;
+  L.active = L.t < nh;
+  L.c0 = L.active ? L.t * dh + (lane - L.t * lph) * CPL : 0;
+  if (!L.active) L.t = 0;
+  return L;
+}
+
+// ------------------------------------------------------------- forward ---
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_fwd_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
+    const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ Wa_e,
+    const float *__restrict__ qkv, int Da, int nh, int lph, float rc, float *__restrict__ o,
+    float2 *__restrict__ stats) {
+  __shared__ float4 phi[CHUNK][KQ];  // f_c(r) phi_k(r)
+  __shared__ float fcs[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const Lanes L = lane_map<CPL>(lane, nh, lph);
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(rc);
+  const int64_t ld = 3 * int64_t(Da);
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float q[CPL];
+  ldc<CPL>(qkv + int64_t(i) * ld + L.c0, q);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) q[c] *= isq;
+
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  float m = -INFINITY, Z = 0.f;
+  const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      const float r = geom[e0 + lane].w;
+      const float fc = r < rc ? 0.5f * (__cosf(r * R.pi_over_rc) + 1.f) : 0.f;
+      float ph[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float x = r - float(k) * R.mu_step;
+        ph[k] = fc * __expf(-R.gamma * x * x);
+      }
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq)
+        phi[lane][kq] = make_float4(ph[4 * kq], ph[4 * kq + 1], ph[4 * kq + 2], ph[4 * kq + 3]);
+      fcs[lane] = fc;
+      jj[lane] = src[e0 + lane];
+    }
+    __syncthreads();
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float kj[UNROLL][CPL], vj[UNROLL][CPL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int me = min(mm + u, n - 1);
+        const float *row = qkv + int64_t(jj[me]) * ld + L.c0;
+        ldc<CPL>(row + Da, kj[u]);
+        ldc<CPL>(row + 2 * Da, vj[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (mm + u < n) {
+          const int me = mm + u;
+          float e[CPL];
+          basis_map<CPL>(phi[me], w, e);
+          float part = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) part += q[c] * kj[u][c] * e[c];
+          const float s = head_sum(part, lph);
+          const float mn = fmaxf(m, s);
+          const float sc = __expf(m - mn);
+          const float wt = fcs[me] * __expf(s - mn);
+          Z = Z * sc + wt;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * sc + wt * (vj[u][c] * e[c]);
+          m = mn;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+    const float inv = Z > 0.f ? 1.f / Z : 0.f;
+    float out[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = acc[c] * inv;
+    stc<CPL>(o + int64_t(i) * Da + L.c0, out);
+    if (lane == L.t * lph) stats[int64_t(i) * nh + L.t] = make_float2(m, Z);
+  }
+}
+
+// ------------------------------------------------ gradient: receiver rows --
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
+    const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ Wa_e,
+    const float *__restrict__ qkv, const float *__restrict__ o, const float2 *__restrict__ stats,
+    const float *__restrict__ obar, int Da, int nh, int lph, float rc,
+    float *__restrict__ qkv_bar, float *__restrict__ edge_g, float *__restrict__ edge_a,
+    float *__restrict__ edge_c) {
+  __shared__ float4 phi[CHUNK][KQ];   // f_c phi_k
+  __shared__ float4 dph[CHUNK][KQ];   // d(f_c phi_k)/dr
+  __shared__ float fcs[CHUNK], dfcs[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const Lanes L = lane_map<CPL>(lane, nh, lph);
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(rc);
+  const int64_t ld = 3 * int64_t(Da);
+  const float on = L.active ? 1.f : 0.f;
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float q[CPL], ob[CPL], oo[CPL];
+  ldc<CPL>(qkv + int64_t(i) * ld + L.c0, q);
+  ldc<CPL>(obar + int64_t(i) * Da + L.c0, ob);
+  ldc<CPL>(o + int64_t(i) * Da + L.c0, oo);
+  float bpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    q[c] *= isq * on;
+    ob[c] *= on;
+    bpart += ob[c] * oo[c];
+  }
+  const float beta = head_sum(bpart, lph);
+  const float2 st = stats[int64_t(i) * nh + L.t];
+  const float m = L.active ? st.x : 0.f;
+  const float invZ = (L.active && st.y > 0.f) ? 1.f / st.y : 0.f;
+  const bool head_lead = L.active && lane == L.t * lph;
+
+  float qb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) qb[c] = 0.f;
+  const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      const float r = geom[e0 + lane].w;
+      float fc = 0.f, dfc = 0.f;
+      if (r < rc) {
+        float sn, cs;
+        __sincosf(r * R.pi_over_rc, &sn, &cs);
+        fc = 0.5f * (cs + 1.f);
+        dfc = -0.5f * R.pi_over_rc * sn;
+      }
+      float ph[K], dp[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float x = r - float(k) * R.mu_step;
+        const float p = __expf(-R.gamma * x * x);
+        ph[k] = fc * p;
+        dp[k] = dfc * p + fc * (-2.f * R.gamma * x * p);
+      }
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        phi[lane][kq] = make_float4(ph[4 * kq], ph[4 * kq + 1], ph[4 * kq + 2], ph[4 * kq + 3]);
+        dph[lane][kq] = make_float4(dp[4 * kq], dp[4 * kq + 1], dp[4 * kq + 2], dp[4 * kq + 3]);
+      }
+      fcs[lane] = fc;
+      dfcs[lane] = dfc;
+      jj[lane] = src[e0 + lane];
+    }
+    __syncthreads();
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float kj[UNROLL][CPL], vj[UNROLL][CPL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int me = min(mm + u, n - 1);
+        const float *row = qkv + int64_t(jj[me]) * ld + L.c0;
+        ldc<CPL>(row + Da, kj[u]);
+        ldc<CPL>(row + 2 * Da, vj[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (mm + u < n) {
+          const int me = mm + u;
+          float e[CPL], de[CPL];
+          basis_map<CPL>(phi[me], w, e);
+          basis_map<CPL>(dph[me], w, de);
+          float ps = 0.f, pa = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            ps += q[c] * kj[u][c] * e[c];
+            pa += ob[c] * vj[u][c] * e[c];
+          }
+          const float s = head_sum(ps, lph);
+          const float ab = head_sum(pa, lph);
+          const float wt = __expf(s - m);
+          const float alpha = fcs[me] * wt * invZ;
+          const float diff = ab - beta;
+          const float g = alpha * diff;
+          float cp = head_lead ? wt * invZ * diff * dfcs[me] : 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            cp += (g * q[c] * kj[u][c] + alpha * ob[c] * vj[u][c]) * de[c];
+            qb[c] += g * kj[u][c] * e[c];
+          }
+          const float ce = wave_sum(cp);
+          const int64_t eg = int64_t(e0 + me);
+          if (lane == 0) edge_c[eg] = ce;
+          if (head_lead) {
+            edge_g[eg * nh + L.t] = g;
+            edge_a[eg * nh + L.t] = alpha;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) qb[c] *= isq;
+    stc<CPL>(qkv_bar + int64_t(i) * ld + L.c0, qb);
+  }
+}
+
+// -------------------------------------------------- gradient: sender rows --
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_vjp_send_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
+    const int32_t *__restrict__ rev, const float4 *__restrict__ geom, int n_atoms,
+    const float *__restrict__ Wa_e, const float *__restrict__ qkv, const float *__restrict__ obar,
+    const float *__restrict__ edge_g, const float *__restrict__ edge_a,
+    const float *__restrict__ edge_c, int Da, int nh, int lph, float rc,
+    float *__restrict__ qkv_bar, float *__restrict__ grad_pos, float *__restrict__ atom_virial) {
+  __shared__ float4 phi[CHUNK][KQ];
+  __shared__ int jj[CHUNK], rr[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int j = int(blk);
+  const Lanes L = lane_map<CPL>(lane, nh, lph);
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(rc);
+  const int64_t ld = 3 * int64_t(Da);
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float kb[CPL], vb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) kb[c] = vb[c] = 0.f;
+  // lane-private partial force and virial over the edges this lane set up
+  float fx = 0.f, fy = 0.f, fz = 0.f;
+  float vir[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r0 = row_ptr[j], r1 = row_ptr[j + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      const int e = e0 + lane;
+      const float4 gm = geom[e];
+      const float r = gm.w;
+      const float fc = r < rc ? 0.5f * (__cosf(r * R.pi_over_rc) + 1.f) : 0.f;
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        float b[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float x = r - float(4 * kq + qq) * R.mu_step;
+          b[qq] = fc * __expf(-R.gamma * x * x);
+        }
+        phi[lane][kq] = make_float4(b[0], b[1], b[2], b[3]);
+      }
+      const int re = rev[e];
+      jj[lane] = src[e];
+      rr[lane] = re;
+      const float cc = edge_c[e] + edge_c[re];
+      const float inv = r > 0.f ? 1.f / r : 0.f;
+      const float p = cc * inv;
+      fx += p * gm.x;
+      fy += p * gm.y;
+      fz += p * gm.z;
+      vir[0] += p * gm.x * gm.x;
+      vir[1] += p * gm.y * gm.y;
+      vir[2] += p * gm.z * gm.z;
+      vir[3] += p * gm.y * gm.z;
+      vir[4] += p * gm.x * gm.z;
+      vir[5] += p * gm.x * gm.y;
+    }
+    __syncthreads();
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float qi[UNROLL][CPL], oi[UNROLL][CPL], gg[UNROLL], aa[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int me = min(mm + u, n - 1);
+        const int64_t ii = jj[me];
+        ldc<CPL>(qkv + ii * ld + L.c0, qi[u]);
+        ldc<CPL>(obar + ii * Da + L.c0, oi[u]);
+        const int64_t re = rr[me];
+        gg[u] = edge_g[re * nh + L.t];
+        aa[u] = edge_a[re * nh + L.t];
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (mm + u < n) {
+          float e[CPL];
+          basis_map<CPL>(phi[mm + u], w, e);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            kb[c] += gg[u] * qi[u][c] * e[c];
+            vb[c] += aa[u] * oi[u][c] * e[c];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) kb[c] *= isq;
+    stc<CPL>(qkv_bar + int64_t(j) * ld + Da + L.c0, kb);
+    stc<CPL>(qkv_bar + int64_t(j) * ld + 2 * Da + L.c0, vb);
+  }
+  fx = wave_sum(fx);
+  fy = wave_sum(fy);
+  fz = wave_sum(fz);
+#pragma unroll
+  for (int qv = 0; qv < 6; ++qv) vir[qv] = wave_sum(vir[qv]);
+  if (lane == 0) {
+    grad_pos[int64_t(j) * 3 + 0] = -fx;
+    grad_pos[int64_t(j) * 3 + 1] = -fy;
+    grad_pos[int64_t(j) * 3 + 2] = -fz;
+#pragma unroll
+    for (int qv = 0; qv < 6; ++qv) atom_virial[int64_t(j) * 6 + qv] = 0.5f * vir[qv];
+  }
+}
+
+template <int CPL>
+int launch_all(int which, const AttnArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(padded_grid(a.n_atoms))), block(64);
+  const float4 *g4 = reinterpret_cast<const float4 *>(a.geom);
+  if (which == 0) {
+    attn_fwd_kernel<CPL><<<grid, block, 0, stream>>>(a.row_ptr, a.src, g4, a.n_atoms, a.Wa_e, a.qkv,
+                                                     a.Da, a.nh, a.lph, a.rc, a.o,
+                                                     reinterpret_cast<float2 *>(a.stats));
+  } else if (which == 1) {
+    attn_vjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(
+        a.row_ptr, a.src, g4, a.n_atoms, a.Wa_e, a.qkv, a.o,
+        reinterpret_cast<const float2 *>(a.stats), a.obar, a.Da, a.nh, a.lph, a.rc, a.qkv_bar,
+        a.edge_g, a.edge_a, a.edge_c);
+  } else {
+    attn_vjp_send_kernel<CPL><<<grid, block, 0, stream>>>(
+        a.row_ptr, a.src, a.rev, g4, a.n_atoms, a.Wa_e, a.qkv, a.obar, a.edge_g, a.edge_a,
+        a.edge_c, a.Da, a.nh, a.lph, a.rc, a.qkv_bar, a.grad_pos, a.atom_virial);
+  }
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+int dispatch(int which, const AttnArgs &a, hipStream_t stream) {
+  switch (a.cpl) {
+    case 1: return launch_all<1>(which, a, stream);
+    case 2: return launch_all<2>(which, a, stream);
+    case 3: return launch_all<3>(which, a, stream);
+    case 4: return launch_all<4>(which, a, stream);
+    case 6: return launch_all<6>(which, a, stream);
+    case 8: return launch_all<8>(which, a, stream);
+    default: break;
+  }
+  set_error("no attention lane layout for %d channels per lane", a.cpl);
+  return MLIP_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int attn_lane_layout(int Da, int nh, int *cpl, int *lph) {
+  if (nh < 1 || Da % nh) return MLIP_ERR_INVALID;
+  const int dh = Da / nh;
+  const int options[] = {1, 2, 3, 4, 6, 8};
+  for (int c : options) {
+    if (dh % c) continue;
+    const int l = dh / c;
+    if ((l & (l - 1)) != 0 || int64_t(nh) * l > 64) continue;
+    *cpl = c;
+    *lph = l;
+    return MLIP_OK;
+  }
+  return MLIP_ERR_UNSUPPORTED;
+}
+
+int launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  ProfScope ps(K_ATTN_FWD, stream);
+  return dispatch(0, a, stream);
+}
+
+int launch_attn_vjp(const AttnArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  {
+    ProfScope ps(K_ATTN_VJP_RECV, stream);
+    if (int rc = dispatch(1, a, stream)) return rc;
+  }
+  ProfScope ps(K_ATTN_VJP_SEND, stream);
+  return dispatch(2, a, stream);
+}
+
+}  // namespace mlip

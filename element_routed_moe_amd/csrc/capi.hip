@@ -96,6 +96,58 @@ VjpWs carve_vjp(void *base, int64_t N, int64_t k, int64_t De, int64_t Dn, int64_
   return w;
 }
 
+struct MoeVjpWs {
+  float *Q, *Utok;
+};
+MoeVjpWs carve_moe_vjp(void *base, int64_t N, int64_t k, int64_t Dn, int64_t H, size_t *bytes) {
+  Carver c(base);
+  MoeVjpWs w;
+  w.Q = c.take<float>(size_t(N * k * H));
+  w.Utok = c.take<float>(size_t(N * k * Dn));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+struct AttnVjpWs {
+  float *obar, *qkv_bar, *edge_g, *edge_a, *edge_c, *virial;
+};
+AttnVjpWs carve_attn_vjp(void *base, int64_t N, int64_t E, int64_t Da, int64_t nh, size_t *bytes) {
+  Carver c(base);
+  AttnVjpWs w;
+  w.obar = c.take<float>(size_t(N * Da));
+  w.qkv_bar = c.take<float>(size_t(N * 3 * Da));
+  w.edge_g = c.take<float>(size_t(E * nh));
+  w.edge_a = c.take<float>(size_t(E * nh));
+  w.edge_c = c.take<float>(size_t(E));
+  w.virial = c.take<float>(size_t(N * 6));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+// dL/du = g + sum_r gate * ((g[tok] @ W2_x^T) * silu'(P)) @ W1_x^T, gathered back
+// by slot in rank order (two grouped GEMMs and the combine).
+int moe_vjp_core(const float *grad_out, const int32_t *z, const float *gate,
+                 const int32_t *exp_off, const int32_t *tok_atom, const int32_t *slot,
+                 const float *P, const float *W1, const float *W2, int N, int T, int X, int k,
+                 int Dn, int H, float *Q, float *Utok, float *grad_in, hipStream_t stream) {
+  const int M = N * k;
+  GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
+  g1.A = grad_out; g1.lda = Dn; g1.a_rows = tok_atom;
+  g1.B = W2; g1.ldb = Dn; g1.b_group_stride = int64_t(H) * Dn;
+  g1.C = Q; g1.ldc = H; g1.R = P; g1.ldr = H;
+  g1.group_off = exp_off; g1.n_groups = X;
+  g1.M = M; g1.N = H; g1.K = Dn;
+  if (int rc = launch_gemm(g1, true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN, stream)) return rc;
+  GemmArgs g2;  // U_tok = Q @ W1[x]^T
+  g2.A = Q; g2.lda = H;
+  g2.B = W1; g2.ldb = H; g2.b_group_stride = int64_t(Dn) * H;
+  g2.C = Utok; g2.ldc = Dn;
+  g2.group_off = exp_off; g2.n_groups = X;
+  g2.M = M; g2.N = Dn; g2.K = H;
+  if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_VJP_UP, stream)) return rc;
+  return moe_combine(grad_out, Utok, z, gate, slot, N, T, k, Dn, grad_in, stream);
+}
+
 }  // namespace
 }  // namespace mlip
 
@@ -272,25 +324,10 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   }
   VjpWs w = carve_vjp(ws, n_atoms, top_k, d_edge, d_node, d_hidden, nullptr);
   float *vir = atom_virial ? atom_virial : w.virial;
-  const int M = n_atoms * top_k;
 
-  GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
-  g1.A = grad_out; g1.lda = d_node; g1.a_rows = tok_atom;
-  g1.B = W2; g1.ldb = d_node; g1.b_group_stride = int64_t(d_hidden) * d_node;
-  g1.C = w.Q; g1.ldc = d_hidden; g1.R = P; g1.ldr = d_hidden;
-  g1.group_off = exp_off; g1.n_groups = n_experts;
-  g1.M = M; g1.N = d_hidden; g1.K = d_node;
-  if (int rc = launch_gemm(g1, true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN, stream)) return rc;
-  GemmArgs g2;  // U_tok = Q @ W1[x]^T
-  g2.A = w.Q; g2.lda = d_hidden;
-  g2.B = W1; g2.ldb = d_hidden; g2.b_group_stride = int64_t(d_node) * d_hidden;
-  g2.C = w.Utok; g2.ldc = d_node;
-  g2.group_off = exp_off; g2.n_groups = n_experts;
-  g2.M = M; g2.N = d_node; g2.K = d_hidden;
-  if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_VJP_UP, stream)) return rc;
-  // ubar = g + sum_r gate * U_tok[slot]
-  if (int rc = moe_combine(grad_out, w.Utok, z, gate, slot, n_atoms, n_types, top_k, d_node, w.ubar,
-                           stream))
+  if (int rc = moe_vjp_core(grad_out, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms,
+                            n_types, n_experts, top_k, d_node, d_hidden, w.Q, w.Utok, w.ubar,
+                            stream))
     return rc;
   GemmArgs g3;  // abar = ubar @ W_u^T
   g3.A = w.ubar; g3.lda = d_node; g3.B = W_u; g3.ldb = d_node; g3.C = w.abar; g3.ldc = d_edge;
@@ -306,6 +343,156 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   g4.A = w.sbar; g4.lda = d_edge; g4.B = W_d; g4.ldb = d_edge; g4.C = grad_h; g4.ldc = d_node;
   g4.R = w.ubar; g4.ldr = d_node; g4.M = n_atoms; g4.N = d_node; g4.K = d_edge;
   return launch_gemm(g4, true, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+// ------------------------------------------------------------ MoE VJP ----
+size_t mlip_moe_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node,
+                                   int32_t d_hidden) {
+  size_t b = 0;
+  carve_moe_vjp(nullptr, std::max(n_atoms, 0), std::max(top_k, 1), std::max(d_node, 0),
+                std::max(d_hidden, 0), &b);
+  return b;
+}
+
+int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
+                 const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W1,
+                 const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                 int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
+                 float *grad_in, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_hidden, "d_hidden")) return rc;
+  MLIP_CHECK_ARG(W1 && W2 && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (z && tok_atom && slot && P && grad_out && grad_in),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(aligned(P, 16) && aligned(grad_out, 16) && aligned(grad_in, 16) &&
+                     aligned(W1, 16) && aligned(W2, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_moe_vjp_workspace_size(n_atoms, top_k, d_node, d_hidden)))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  MoeVjpWs w = carve_moe_vjp(ws, n_atoms, top_k, d_node, d_hidden, nullptr);
+  return moe_vjp_core(grad_out, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms, n_types,
+                      n_experts, top_k, d_node, d_hidden, w.Q, w.Utok, grad_in, stream);
+}
+
+// ---------------------------------------------------------- attention ----
+static int check_attn_dims(int32_t d_node, int32_t d_attn, int32_t n_heads, float cutoff,
+                           int32_t n_rbf, int *cpl, int *lph) {
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_attn, "d_attn")) return rc;
+  MLIP_CHECK_ARG(n_heads >= 1 && d_attn % n_heads == 0, "d_attn = %d must be a multiple of "
+                 "n_heads = %d", d_attn, n_heads);
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  if (attn_lane_layout(d_attn, n_heads, cpl, lph) != MLIP_OK) {
+    set_error("unsupported attention shape: %d heads of width %d (need a width dh = c * 2^j, "
+              "c in {1,2,3,4,6,8}, with n_heads * 2^j <= 64)", n_heads, d_attn / n_heads);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  return MLIP_OK;
+}
+
+int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *h0, const float *W_qkv, const float *Wa_e,
+                   const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
+                   int32_t n_heads, float cutoff, float *qkv, float *o, float *stats, float *u,
+                   void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0, lph = 0;
+  if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (h0 && qkv && o && stats && u), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h0, 16) && aligned(W_qkv, 16) && aligned(Wa_e, 16) &&
+                     aligned(W_o, 16) && aligned(qkv, 16) && aligned(o, 16) && aligned(u, 16) &&
+                     aligned(stats, 8),
+                 "float arrays must be 16-byte aligned (stats 8-byte)");
+  if (n_atoms == 0) return MLIP_OK;
+  GemmArgs g;  // [q | k | v] = h0 @ W_qkv
+  g.A = h0; g.lda = d_node; g.B = W_qkv; g.ldb = 3 * int64_t(d_attn);
+  g.C = qkv; g.ldc = 3 * int64_t(d_attn);
+  g.M = n_atoms; g.N = 3 * d_attn; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  AttnArgs a;
+  a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;
+  a.Wa_e = Wa_e; a.qkv = qkv; a.o = o; a.stats = stats;
+  a.Da = d_attn; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
+  if (int rc = launch_attn_fwd(a, stream)) return rc;
+  GemmArgs g2;  // u = h0 + o @ W_o
+  g2.A = o; g2.lda = d_attn; g2.B = W_o; g2.ldb = d_node; g2.C = u; g2.ldc = d_node;
+  g2.R = h0; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_attn;
+  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+size_t mlip_attention_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_attn,
+                                         int32_t n_heads) {
+  size_t b = 0;
+  carve_attn_vjp(nullptr, std::max(n_atoms, 0), std::max<int64_t>(n_edges, 0),
+                 std::max(d_attn, 0), std::max(n_heads, 1), &b);
+  return b;
+}
+
+int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
+                       const float *geom, int32_t n_atoms, int64_t n_edges, const float *qkv,
+                       const float *o, const float *stats, const float *W_qkv, const float *Wa_e,
+                       const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
+                       int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
+                       float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
+                       float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
+                       void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0, lph = 0;
+  if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (qkv && o && stats && grad_u && grad_h0 && grad_pos),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && rev && geom), "null edge pointer");
+  MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
+                 "grad_strain needs struct_ptr and n_structs >= 1");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(qkv, 16) && aligned(o, 16) && aligned(stats, 8) &&
+                     aligned(W_qkv, 16) && aligned(Wa_e, 16) && aligned(W_o, 16) &&
+                     aligned(grad_u, 16) && aligned(grad_h0, 16),
+                 "float arrays must be 16-byte aligned (stats 8-byte)");
+  if (int rc = check_ws(ws, ws_bytes,
+                        mlip_attention_vjp_workspace_size(n_atoms, n_edges, d_attn, n_heads)))
+    return rc;
+  if (n_atoms == 0) {
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    return MLIP_OK;
+  }
+  AttnVjpWs w = carve_attn_vjp(ws, n_atoms, n_edges, d_attn, n_heads, nullptr);
+  float *vir = atom_virial ? atom_virial : w.virial;
+  GemmArgs g1;  // obar = ubar @ W_o^T
+  g1.A = grad_u; g1.lda = d_node; g1.B = W_o; g1.ldb = d_node; g1.C = w.obar; g1.ldc = d_attn;
+  g1.M = n_atoms; g1.N = d_attn; g1.K = d_node;
+  if (int rc = launch_gemm(g1, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  AttnArgs a;
+  a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = n_atoms;
+  a.Wa_e = Wa_e; a.qkv = qkv; a.o = const_cast<float *>(o);
+  a.stats = const_cast<float *>(stats); a.obar = w.obar; a.qkv_bar = w.qkv_bar;
+  a.edge_g = w.edge_g; a.edge_a = w.edge_a; a.edge_c = w.edge_c;
+  a.grad_pos = grad_pos; a.atom_virial = vir;
+  a.Da = d_attn; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
+  if (int rc = launch_attn_vjp(a, stream)) return rc;
+  if (grad_strain) {
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+  }
+  GemmArgs g2;  // grad_h0 = ubar + [qbar | kbar | vbar] @ W_qkv^T
+  g2.A = w.qkv_bar; g2.lda = 3 * int64_t(d_attn); g2.B = W_qkv; g2.ldb = 3 * int64_t(d_attn);
+  g2.C = grad_h0; g2.ldc = d_node; g2.R = grad_u; g2.ldr = d_node;
+  g2.M = n_atoms; g2.N = d_node; g2.K = 3 * d_attn;
+  return launch_gemm(g2, true, EPI_RESID, K_GEMM_DENSE, stream);
 }
 
 }  // extern "C"

@@ -57,6 +57,9 @@ enum KClass {
   K_GEMM_EXPERT_VJP_DOWN,  // Q = (g[tok] @ W2^T) * silu'(P)
   K_GEMM_EXPERT_VJP_UP,    // U = Q @ W1^T
   K_EDGE_VJP,
+  K_ATTN_FWD,              // neighbour attention, edge part
+  K_ATTN_VJP_RECV,         // attention VJP, receiver rows
+  K_ATTN_VJP_SEND,         // attention VJP, sender rows (via the reverse edge)
   K_NUM_CLASSES
 };
 
@@ -98,6 +101,23 @@ __device__ inline int64_t xcd_block(int64_t n) {
   return logical < n ? logical : -1;
 }
 
+// ------------------------------------------------------- radial basis -----
+// Constants of the pair-distance basis: K Gaussians exp(-gamma (r - k mu_step)^2),
+// k = 0..K-1, mu_step = r_c/(K-1), gamma = (K-1)^2 / (2 r_c^2), and the cosine
+// envelope f_c(r) = (cos(pi r / r_c) + 1)/2 for r < r_c.
+struct Radial {
+  float mu_step, gamma, pi_over_rc, rc;
+};
+
+__device__ inline Radial make_radial(float rc) {
+  Radial p;
+  p.rc = rc;
+  p.mu_step = rc / float(MLIP_N_RBF - 1);
+  p.gamma = float((MLIP_N_RBF - 1) * (MLIP_N_RBF - 1)) / (2.f * rc * rc);
+  p.pi_over_rc = 3.14159265358979323846f / rc;
+  return p;
+}
+
 // ----------------------------------------------------------- scan / gemm ---
 // Exclusive prefix sum of n int32 values (out may alias in); out[n] gets the
 // total when write_total.  tmp needs scan_tmp_elems(n) int32 entries.
@@ -131,5 +151,30 @@ struct GemmArgs {
 
 int launch_gemm(const GemmArgs &a, bool b_transposed, Epilogue epi, KClass cls,
                 hipStream_t stream);
+
+// ------------------------------------------------------------- attention ---
+struct AttnArgs {
+  const int32_t *row_ptr = nullptr, *src = nullptr, *rev = nullptr;
+  const float *geom = nullptr;
+  int n_atoms = 0;
+  const float *Wa_e = nullptr;   // [K][Da]
+  const float *qkv = nullptr;    // [N][3 Da]: q | k | v
+  float *o = nullptr;            // [N][Da]
+  float *stats = nullptr;        // [N][nh] (running max, weight sum)
+  const float *obar = nullptr;   // [N][Da]
+  float *qkv_bar = nullptr;      // [N][3 Da]
+  float *edge_g = nullptr, *edge_a = nullptr;  // [E][nh]
+  float *edge_c = nullptr;       // [E]
+  float *grad_pos = nullptr;     // [N][3]
+  float *atom_virial = nullptr;  // [N][6]
+  int Da = 0, nh = 0, cpl = 0, lph = 0;
+  float rc = 0.f;
+};
+
+// Channels per lane (cpl) and lanes per head (lph) for Da channels in nh heads,
+// one wavefront per row; MLIP_ERR_UNSUPPORTED when no layout fits.
+int attn_lane_layout(int Da, int nh, int *cpl, int *lph);
+int launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
+int launch_attn_vjp(const AttnArgs &a, hipStream_t stream);
 
 }  // namespace mlip

@@ -24,19 +24,6 @@ constexpr int K = MLIP_N_RBF;
 constexpr int EDGE_CHUNK = 64;
 constexpr int COLS = 128;  // columns per slice: 64 lanes x float2
 
-struct Radial {
-  float mu_step, gamma, pi_over_rc, rc;
-};
-
-__device__ inline Radial make_radial(float rc) {
-  Radial p;
-  p.rc = rc;
-  p.mu_step = rc / float(K - 1);
-  p.gamma = float((K - 1) * (K - 1)) / (2.f * rc * rc);
-  p.pi_over_rc = 3.14159265358979323846f / rc;
-  return p;
-}
-
 typedef float f2v __attribute__((ext_vector_type(2)));
 constexpr int UNROLL = 4;
 

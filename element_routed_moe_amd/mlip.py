@@ -56,6 +56,15 @@ _SIGS = {
     "mlip_block_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
                                  _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _p, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]),
+    "mlip_moe_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "mlip_moe_vjp": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _p, _p, _p, _sz, _p]),
+    "mlip_attention": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                 _f32, _p, _p, _p, _p, _p]),
+    "mlip_attention_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32]),
+    "mlip_attention_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32,
+                                     _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _p,
+                                     _sz, _p]),
     "mlip_profile_enable": (C.c_int, [C.c_int]),
     "mlip_profile_reset": (C.c_int, []),
     "mlip_profile_count": (C.c_int, []),
@@ -213,6 +222,68 @@ def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top
     return out
 
 
+def mlip_moe_vjp(moe, z, W1, W2, grad_out, out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dL/du of h' = u + MoE(u) for grad_out = dL/dh' (moe: the layer's forward state)."""
+    N, Dn = int(grad_out.shape[0]), int(grad_out.shape[1])
+    X, H = int(W1.shape[0]), int(W1.shape[2])
+    T, k = int(moe["gate"].shape[0]), int(moe["gate"].shape[1])
+    dev = grad_out.device
+    if out is None:
+        out = torch.empty((N, Dn), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(_lib.mlip_moe_vjp_workspace_size(N, k, Dn, H), dev)
+    _check(_lib.mlip_moe_vjp(_ptr(z), _ptr(moe["gate"]), _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]),
+                             _ptr(moe["slot"]), _ptr(moe["P"]), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
+                             _ptr(grad_out), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_attention(graph, h0, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float,
+                   out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(h0.shape[0]), int(h0.shape[1])
+    Da = int(W_o.shape[0])
+    E = int(graph["n_edges"])
+    dev = h0.device
+    if out is None:
+        out = dict(qkv=torch.empty((N, 3 * Da), dtype=torch.float32, device=dev),
+                   o=torch.empty((N, Da), dtype=torch.float32, device=dev),
+                   stats=torch.empty((N, int(n_heads), 2), dtype=torch.float32, device=dev),
+                   u=torch.empty((N, Dn), dtype=torch.float32, device=dev))
+    _check(_lib.mlip_attention(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                               _ptr(h0), _ptr(W_qkv), _ptr(Wa_e), _ptr(W_o), int(Wa_e.shape[0]), Dn,
+                               Da, int(n_heads), float(cutoff), _ptr(out["qkv"]), _ptr(out["o"]),
+                               _ptr(out["stats"]), _ptr(out["u"]), _stream()))
+    return out
+
+
+def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float, grad_u,
+                       struct_ptr=None, out: Optional[Dict] = None,
+                       ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(grad_u.shape[0]), int(grad_u.shape[1])
+    Da = int(W_o.shape[0])
+    E = int(graph["n_edges"])
+    dev = grad_u.device
+    B = int(struct_ptr.shape[0]) - 1 if struct_ptr is not None else 0
+    if out is None:
+        out = dict(grad_h0=torch.empty((N, Dn), dtype=torch.float32, device=dev),
+                   grad_pos=torch.empty((N, 3), dtype=torch.float32, device=dev),
+                   atom_virial=torch.empty((N, 6), dtype=torch.float32, device=dev))
+        if struct_ptr is not None:
+            out["grad_strain"] = torch.empty((B, 6), dtype=torch.float64, device=dev)
+    if ws is None or ws.numel() < _lib.mlip_attention_vjp_workspace_size(N, E, Da, int(n_heads)):
+        ws = _ws(_lib.mlip_attention_vjp_workspace_size(N, E, Da, int(n_heads)), dev)
+    out["ws"] = ws
+    _check(_lib.mlip_attention_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["rev"]),
+                                   _ptr(graph["geom"]), N, E, _ptr(att["qkv"]), _ptr(att["o"]),
+                                   _ptr(att["stats"]), _ptr(W_qkv), _ptr(Wa_e), _ptr(W_o),
+                                   int(Wa_e.shape[0]), Dn, Da, int(n_heads), float(cutoff),
+                                   _ptr(grad_u), _ptr(out["grad_h0"]), _ptr(out["grad_pos"]),
+                                   _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
+                                   _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 # ------------------------------------------------------------------ timing
 def profile_enable(on: bool = True):
     _check(_lib.mlip_profile_enable(1 if on else 0))
@@ -291,4 +362,77 @@ class Block:
         self.vjp = mlip_block_vjp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u,
                                   self.W1, self.W2, self.cutoff, self.top_k, self.grad_out,
                                   struct_ptr=self.struct_ptr, out=self.vjp, ws=self.ws_vjp)
+        return self
+
+
+class FullBlock:
+    """The complete interaction block: MoE0 -> neighbour attention -> MoE1.
+
+    ``step()`` runs on the current stream: radius graph, MoE0 on h, attention,
+    MoE1, readout, then the input gradient back through MoE1, the attention
+    (forces and virial) and MoE0 for the given upstream gradient dL/dh'.
+    """
+
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None):
+        def dev(x, dt=None):
+            t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
+            return t.to(device=device, dtype=dt or t.dtype).contiguous()
+
+        self.device = device
+        f32 = torch.float32
+        self.pos = dev(inputs["pos"], f32)
+        self.cell = dev(inputs["cell"], f32)
+        self.struct_ptr = dev(inputs["struct_ptr"], torch.int32)
+        self.z = dev(inputs["z"], torch.int32)
+        self.h = dev(inputs["h"], f32)
+        self.logits0 = dev(inputs["logits0"], f32)
+        self.W1_0 = dev(inputs["W1_0"], f32)
+        self.W2_0 = dev(inputs["W2_0"], f32)
+        self.W_qkv = dev(inputs["W_qkv"], f32)
+        self.Wa_e = dev(inputs["Wa_e"], f32)
+        self.W_o = dev(inputs["W_o"], f32)
+        self.logits = dev(inputs["logits"], f32)
+        self.W1 = dev(inputs["W1"], f32)
+        self.W2 = dev(inputs["W2"], f32)
+        self.w_r = dev(inputs["w_r"], f32)
+        self.cutoff = float(inputs["cutoff"])
+        self.top_k = int(inputs["top_k"])
+        self.n_heads = int(inputs["n_heads"])
+        if grad_out is None:
+            grad_out = self.w_r.expand(self.h.shape[0], -1)
+        self.grad_out = dev(grad_out, f32)
+        N, Dn = self.h.shape
+        H = self.W1.shape[2]
+        T, X = self.logits.shape
+        B = self.cell.shape[0]
+        self.ws_graph = _ws(_lib.mlip_graph_workspace_size(N, B), device)
+        self.ws_moe0 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
+        self.ws_moe1 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
+        self.ws_mvjp = _ws(_lib.mlip_moe_vjp_workspace_size(N, self.top_k, Dn, H), device)
+        self.ws_avjp = None
+        self.edge_capacity = None
+        self.graph = self.moe0 = self.att = self.moe = self.ro = None
+        self.ubar = self.avjp = self.grad_h = None
+
+    def step(self):
+        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
+                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
+        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
+            self.edge_capacity = g["n_edges"]
+        self.graph = g
+        self.moe0 = mlip_moe_forward(self.h, self.z, self.logits0, self.W1_0, self.W2_0, self.top_k,
+                                     out=self.moe0, ws=self.ws_moe0)
+        self.att = mlip_attention(g, self.moe0["h_out"], self.W_qkv, self.Wa_e, self.W_o,
+                                  self.n_heads, self.cutoff, out=self.att)
+        self.moe = mlip_moe_forward(self.att["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
+                                    out=self.moe, ws=self.ws_moe1)
+        self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
+        self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, self.grad_out, out=self.ubar,
+                                 ws=self.ws_mvjp)
+        self.avjp = mlip_attention_vjp(g, self.att, self.W_qkv, self.Wa_e, self.W_o, self.n_heads,
+                                       self.cutoff, self.ubar, struct_ptr=self.struct_ptr,
+                                       out=self.avjp, ws=self.ws_avjp)
+        self.ws_avjp = self.avjp["ws"]
+        self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
+                                   out=self.grad_h, ws=self.ws_mvjp)
         return self

@@ -2,7 +2,9 @@
  * mlip.h - C ABI of the MI355X (gfx950) library for one MatRIS-MoE
  * interaction block: periodic radius graph, neighbour aggregation,
  * element-routed top-k mixture of experts, readout, and the input gradient
- * (VJP) that conservative forces need.
+ * (VJP) that conservative forces and stresses need; plus the neighbour
+ * multi-head attention and the stand-alone MoE gradient that the complete
+ * block (MoE0, attention, MoE1) is built from.
  *
  * Sources (cited by page title and section):
  *   [news]   ScienceAI news article on MatRIS-MoE and Janus, sections on the
@@ -11,7 +13,7 @@
  *            Billion-Parameter Universal Machine Learning Interatomic
  *            Potentials": 3.1 (architecture, Fig. 1, Table II),
  *            3.2 (sparse MoE design), 3.3 (forces and stresses),
- *            3.5 (kernel notes).
+ *            3.4 (Fig. 3, operators of one block), 3.5 (kernel notes).
  *
  * Conventions for every entry point
  *   - Array arguments are DEVICE pointers unless marked (host).  The caller
@@ -195,6 +197,83 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    float cutoff, const float *grad_out, float *grad_h, float *grad_pos,
                    const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
                    double *grad_strain, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Input gradient of one mixture-of-experts layer on its own ([news],
+ * [review] 3.3: forces from differentiating the energy), for blocks that
+ * stack several MoE layers (the complete block below has one before and one
+ * after the attention).  With g = grad_out = dL/dh' for h' = u + MoE(u):
+ *     grad_in = g + sum_r gate[z_i,r] ((g @ W2_x^T) * silu'(P)) @ W1_x^T
+ * Gates carry no gradient (routing depends on z only).  z, gate, exp_off,
+ * tok_atom, slot and P are those written by the mlip_moe_forward call of
+ * this layer; W1, W2 as there.  grad_in [n_atoms, d_node] may not alias
+ * grad_out.  Workspace: mlip_moe_vjp_workspace_size().
+ * ------------------------------------------------------------------------ */
+size_t mlip_moe_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node,
+                                   int32_t d_hidden);
+int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
+                 const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W1,
+                 const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                 int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
+                 float *grad_in, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Neighbour multi-head attention of the complete interaction block
+ * ([review] 3.4 Fig. 3: a block is Tri, MoE0, Attn, MoE1; 3.2: MoE layers
+ * before and after a multi-head self-attention whose cost stays O(N) at a
+ * fixed cutoff; Table II: S = 8 heads, width 384; M, L = 4 heads, 512).
+ * The pages give no formula; the reading implemented (heads are contiguous
+ * channel blocks of width dh = d_attn / n_heads, t(c) the head of channel c):
+ *     [q | k | v] = h0 @ W_qkv                         (each d_attn wide)
+ *     e_ij   = f_c(r) (phi(r) @ Wa_e)                   (basis as in mlip_aggregate)
+ *     s_ij^t = sum_{c in head t} q_ic k_jc e_ijc / sqrt(dh)
+ *     a_ij^t = f_c(r_ij) exp(s_ij^t) / sum_{l in row i} f_c(r_il) exp(s_il^t)
+ *              (0 when that sum is 0: rows without neighbours)
+ *     o_ic   = sum_{j in row i} a_ij^{t(c)} v_jc e_ijc
+ *     u      = h0 + o @ W_o
+ * The envelope weights the softmax so that a pair crossing r_c changes the
+ * energy continuously.  The caller's graph is a mlip_build_graph result.
+ *
+ * h0     [n_atoms, d_node]      input node features (after MoE0).
+ * W_qkv  [d_node, 3*d_attn]     columns q | k | v.
+ * Wa_e   [n_rbf, d_attn]        pair embedding in attention width.
+ * W_o    [d_attn, d_node].
+ * n_heads: d_attn = n_heads * dh; a layout must exist with dh = c * 2^j,
+ *        c in {1,2,3,4,6,8} and n_heads * 2^j <= 64 (else MLIP_ERR_UNSUPPORTED):
+ *        e.g. 8 x 48, 4 x 128, 4 x 8, 2 x 32.
+ * Outputs: qkv [n_atoms, 3*d_attn], o [n_atoms, d_attn] and
+ *        stats [n_atoms, n_heads, 2] (running max of the scores, sum of the
+ *        weights exp(s - max) f_c) are kept for mlip_attention_vjp;
+ *        u [n_atoms, d_node] (may not alias h0).  No workspace.
+ * ------------------------------------------------------------------------ */
+int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *h0, const float *W_qkv, const float *Wa_e,
+                   const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
+                   int32_t n_heads, float cutoff, float *qkv, float *o, float *stats, float *u,
+                   void *stream);
+
+/* Input gradient of mlip_attention for grad_u = dL/du [n_atoms, d_node]:
+ *   grad_h0 [n_atoms, d_node]  = dL/dh0 (through the residual, q, k and v);
+ *   grad_pos [n_atoms, 3]      = dL/dx through the pair distances (forces are
+ *                               -grad_pos when L is the energy);
+ *   atom_virial [n_atoms, 6]   (optional) per-atom virial, Voigt order
+ *                               xx yy zz yz xz xy, as in mlip_block_vjp;
+ *   grad_strain [n_structs, 6] (optional, float64) dL/d(strain) per structure.
+ * rev is the reverse-edge index of the graph; qkv, o, stats come from the
+ * mlip_attention call of the same step.  Per-edge intermediates live in the
+ * workspace (mlip_attention_vjp_workspace_size, which grows with n_edges).
+ * Rows are reduced by one wavefront each; no atomics, so the result does not
+ * depend on scheduling. */
+size_t mlip_attention_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_attn,
+                                         int32_t n_heads);
+int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
+                       const float *geom, int32_t n_atoms, int64_t n_edges, const float *qkv,
+                       const float *o, const float *stats, const float *W_qkv, const float *Wa_e,
+                       const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
+                       int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
+                       float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
+                       float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
+                       void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  When enabled, every kernel launch of the library is

@@ -88,6 +88,33 @@ def test_aggregate_and_moe_reject_bad_args(mlip):
     assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
+def test_attention_and_moe_vjp_reject_bad_args(mlip):
+    L = mlip._lib
+    f = C.c_void_p(256)
+
+    def att(d_attn, n_heads, cutoff=5.0):
+        return L.mlip_attention(f, f, f, 10, 20, f, f, f, f, 16, 64, d_attn, n_heads, cutoff,
+                                f, f, f, f, None)
+    assert "n_heads" in _err(mlip, att(32, 3), mlip.MLIP_ERR_INVALID)
+    assert "d_attn" in _err(mlip, att(30, 3), mlip.MLIP_ERR_INVALID)
+    assert "cutoff" in _err(mlip, att(32, 4, cutoff=0.0), mlip.MLIP_ERR_INVALID)
+    # 5 heads of width 20: 20 is not c * 2^j with c in {1, 2, 3, 4, 6, 8}
+    assert "unsupported attention shape" in _err(mlip, att(100, 5), mlip.MLIP_ERR_UNSUPPORTED)
+    rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
+                              None, 0, None, f, f, 1 << 30, None)
+    assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
+                              None, 0, None, None, f, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    assert (L.mlip_attention_vjp_workspace_size(4096, 200000, 384, 8)
+            >= (200000 * (2 * 8 + 1) + 4096 * 4 * 384) * 4)
+    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, f, f, 1 << 30, None)
+    assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, f, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+
+
 def test_profile_api_without_gpu(mlip):
     names = list(mlip.profile_read())
-    assert "gemm_expert_up" in names and "edge_vjp" in names and len(names) == 11
+    assert "gemm_expert_up" in names and "edge_vjp" in names and "attn_fwd" in names
+    assert len(names) == 14
