@@ -8,7 +8,10 @@ expert GEMMs, combine), readout, and the input gradient (expert GEMMs
 transposed, aggregation transposed, edge/force part).  Inputs are resident in
 HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S] [--block core|full]
+
+``--block full`` times the complete block instead (MoE0 -> neighbour
+multi-head attention -> MoE1 -> readout, and its input gradient).
 
 Prints ONE JSON line.  ``--calibrate-copy`` instead runs a plain 1 GiB device
 copy (for scaling hardware byte counters).
@@ -64,9 +67,10 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
-def cpu_baseline(cfg, inp, n_structs: int):
+def cpu_baseline(cfg, inp, n_structs: int, full: bool = False):
     """The float64 NumPy oracle on the first n_structs structures of the workload."""
     import numpy as np
+    from oracle import attention as OA
     from oracle import block as OB
     from oracle import graph as OG
     try:
@@ -84,13 +88,18 @@ def cpu_baseline(cfg, inp, n_structs: int):
     g_up = np.broadcast_to(inp["w_r"], (n, cfg.d_node)).astype(np.float64)
     t0 = time.perf_counter()
     gr = OG.radius_graph(sub["pos"], sub["cell"], sub["struct_ptr"], sub["cutoff"])
-    f = OB.block_forward(sub, gr)
-    OB.block_vjp(sub, gr, f, g_up)
+    if full:
+        f = OA.full_block_forward(sub, gr)
+        OA.full_block_vjp(sub, gr, f, g_up)
+    else:
+        f = OB.block_forward(sub, gr)
+        OB.block_vjp(sub, gr, f, g_up)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "atoms/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n_structs} of {cfg.n_structs} structures ({n} atoms, "
-                      f"{gr['src'].size} edges) of the {cfg.name} workload, float64 NumPy oracle, "
-                      f"graph + forward + VJP in {dt:.2f} s"}
+                      f"{gr['src'].size} edges) of the {cfg.name} workload, float64 NumPy oracle"
+                      f"{' of the complete block' if full else ''}, graph + forward + VJP in "
+                      f"{dt:.2f} s"}
 
 
 def main():
@@ -99,14 +108,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="S")
+    ap.add_argument("--block", choices=("core", "full"), default="core")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-structs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the block would shard)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the block has no multi-GPU path",
+              file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
@@ -120,8 +130,9 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = synth.CONFIGS[args.config]
-    inputs = synth.make_inputs(cfg)
-    blk = mlip.Block(inputs, device="cuda")
+    full = args.block == "full"
+    inputs = synth.make_full_inputs(cfg) if full else synth.make_inputs(cfg)
+    blk = (mlip.FullBlock if full else mlip.Block)(inputs, device="cuda")
     log(f"inputs resident for workload {cfg.name}: {cfg.n_atoms} atoms")
     for _ in range(args.warmup):
         blk.step()
@@ -149,6 +160,7 @@ def main():
     value = N * args.steps / wall
 
     # dominant kernel: the expert GEMM class with the largest summed time
+    # (with --block full each class has two launches per step, one per MoE layer)
     k = cfg.top_k
     flops = {c: 2.0 * N * k * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES}
     dom = max(EXPERT_CLASSES, key=lambda c: prof[c]["total_ms"])
@@ -168,15 +180,20 @@ def main():
         "config": {"workload": cfg.name, "atoms": N, "edges": int(E), "structures": cfg.n_structs,
                    "cutoff": cfg.cutoff, "d_edge": cfg.d_edge, "d_node": cfg.d_node,
                    "d_hidden": cfg.d_hidden, "experts": cfg.n_experts, "top_k": k,
-                   "element_types": cfg.n_types},
+                   "element_types": cfg.n_types,
+                   "block": ("MoE0 + neighbour attention + MoE1" if full
+                             else "aggregation + MoE")},
         "edges_per_s": round(E * args.steps / wall, 1),
         "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
         "kernel_ms_per_step": kernel_ms,
         "roofline": roof,
     }
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    if full:
+        out["config"]["heads"] = cfg.n_heads
+        out["config"]["d_attn"] = cfg.d_attn
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inputs, min(args.cpu_structs, cfg.n_structs))
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs, min(args.cpu_structs, cfg.n_structs), full)
     print(json.dumps(out))
 
 

@@ -178,3 +178,132 @@ class LocalBlock:
                 virial[n] += 0.5 * np.einsum("e,ea,eb->ab", c, dhat, cl["d"])
             grad_h[n] = ubar[ii] + sbar @ self.W_d.T
         return dict(grad_h=grad_h, grad_pos=grad_pos, atom_virial=B.voigt(virial))
+
+
+class LocalFullBlock(LocalBlock):
+    """The complete block (``oracle.attention``) at a few sampled atoms.
+
+    The forward at atom i needs MoE0 at i and at its neighbours (q_i, k_j,
+    v_j) and the softmax over row i.  The input gradient at i needs, for i
+    and each neighbour j, the whole softmax of row j (so MoE0 on the
+    neighbours of the neighbours), dL/du there (MoE1 backwards), and the
+    receiver-side edge quantities of row j for the reverse edge j <- i.
+    Every per-atom step is the oracle's own step function on a subset of
+    atoms; MoE layers act atom by atom, so subsets give the same rows.
+    """
+
+    def __init__(self, inp: Dict[str, np.ndarray], use_tree: Optional[bool] = None):
+        super().__init__(inp, use_tree)
+        from . import attention as A
+        self.A = A
+        k = int(inp["top_k"])
+        self.topk0, self.gate0 = B.route(inp["logits0"], k)
+        self.nh = int(inp["n_heads"])
+        self.W_qkv = np.asarray(inp["W_qkv"], f64)
+        self.W_o = np.asarray(inp["W_o"], f64)
+        self.Da = self.W_o.shape[0]
+        self.dh = self.Da // self.nh
+        self._h0: Dict[int, np.ndarray] = {}
+        self._att: Dict[int, Dict] = {}
+
+    def h0(self, atoms) -> np.ndarray:
+        atoms = [int(a) for a in atoms]
+        todo = sorted(set(a for a in atoms if a not in self._h0))
+        if todo:
+            t = np.asarray(todo, np.int64)
+            h = np.asarray(self.inp["h"][t], f64)
+            out = B.moe_forward(h, self.z[t], self.topk0, self.gate0, self.inp["W1_0"], self.inp["W2_0"])
+            for n, a in enumerate(todo):
+                self._h0[a] = out[n]
+        return np.stack([self._h0[a] for a in atoms]) if atoms else np.zeros((0, self.W_qkv.shape[0]))
+
+    def qkv(self, atoms) -> np.ndarray:
+        return self.h0(atoms) @ self.W_qkv
+
+    def att_row(self, i: int) -> Dict:
+        """Softmax and output of row i (edges with receiver i)."""
+        if i in self._att:
+            return self._att[i]
+        rw = self.row(i)
+        Da, nh = self.Da, self.nh
+        qi = self.qkv([i])[0, :Da]
+        kv = self.qkv(rw["other"]) if rw["other"].size else np.zeros((0, 3 * Da))
+        kj, vj = kv[:, Da:2 * Da], kv[:, 2 * Da:]
+        e = B.edge_embedding(rw["r"], self.inp["Wa_e"], self.rc)
+        f = B.envelope(rw["r"], self.rc)
+        s = self.A.head_sum(qi[None, :] * kj * e, nh) / np.sqrt(self.dh)
+        recv = np.zeros(rw["r"].size, np.int64)
+        alpha, w, m, Z = self.A.neighbour_softmax(s, f, recv, 1)
+        ht = self.A.heads_of(Da, nh)
+        o = (alpha[:, ht] * vj * e).sum(axis=0) if rw["r"].size else np.zeros(Da)
+        u = self.h0([i])[0] + o @ self.W_o
+        res = dict(q=qi, k=kj, v=vj, e=e, f=f, s=s, alpha=alpha, w=w, Z=Z[0], o=o, u=u)
+        self._att[i] = res
+        return res
+
+    def forward(self, atoms: Iterable[int]) -> Dict[str, np.ndarray]:
+        atoms = np.asarray(list(atoms), np.int64)
+        u = np.stack([self.att_row(int(i))["u"] for i in atoms])
+        h2 = B.moe_forward(u, self.z[atoms], self.topk, self.gate, self.inp["W1"], self.inp["W2"])
+        eps = h2 @ np.asarray(self.inp["w_r"], f64)
+        return dict(u=u, h2=h2, eps=eps)
+
+    def vjp(self, atoms: Iterable[int], g_all: np.ndarray) -> Dict[str, np.ndarray]:
+        """grad_h, grad_pos and the per-atom virial at the sampled atoms."""
+        atoms = [int(i) for i in atoms]
+        J = set(atoms)
+        for i in atoms:
+            J.update(int(j) for j in self.row(i)["other"])
+        J = sorted(J)
+        Jarr = np.asarray(J, np.int64)
+        u = np.stack([self.att_row(j)["u"] for j in J])
+        ubar = B.moe_vjp(u, np.asarray(g_all[Jarr], f64), self.z[Jarr], self.topk, self.gate,
+                         self.inp["W1"], self.inp["W2"])
+        ub = {j: ubar[n] for n, j in enumerate(J)}
+        ht = self.A.heads_of(self.Da, self.nh)
+        sq = 1.0 / np.sqrt(self.dh)
+        Wa_e = self.inp["Wa_e"]
+        rowq = {}
+        for j in J:            # receiver-side quantities of every row touching the samples
+            a = self.att_row(j)
+            rw = self.row(j)
+            ob = ub[j] @ self.W_o.T
+            abar = self.A.head_sum(ob[None, :] * a["v"] * a["e"], self.nh)
+            beta = self.A.head_sum((ob * a["o"])[None, :], self.nh)[0]
+            diff = abar - beta[None, :]
+            gbar = a["alpha"] * diff
+            with np.errstate(invalid="ignore", divide="ignore"):
+                fbar = np.sum(np.where(a["Z"][None, :] > 0, a["w"] / a["Z"][None, :], 0.0) * diff, axis=1)
+            ebar = gbar[:, ht] * a["q"][None, :] * a["k"] * sq + a["alpha"][:, ht] * ob[None, :] * a["v"]
+            c = (np.sum(ebar * B.edge_embedding_dr(rw["r"], Wa_e, self.rc), axis=1)
+                 + fbar * B.envelope_dr(rw["r"], self.rc))
+            key = {(int(o), int(s[0]), int(s[1]), int(s[2])): n
+                   for n, (o, s) in enumerate(zip(rw["other"], rw["shift"]))}
+            rowq[j] = dict(ob=ob, gbar=gbar, c=c, key=key)
+        Dn = self.W_o.shape[1]
+        grad_h = np.zeros((len(atoms), Dn), f64)
+        grad_pos = np.zeros((len(atoms), 3), f64)
+        virial = np.zeros((len(atoms), 3, 3), f64)
+        for n, i in enumerate(atoms):
+            a, rw, qi_ = self.att_row(i), self.row(i), rowq[i]
+            Da = self.Da
+            qbar = (qi_["gbar"][:, ht] * a["k"] * a["e"]).sum(axis=0) * sq if rw["r"].size else np.zeros(Da)
+            kbar = np.zeros(Da)
+            vbar = np.zeros(Da)
+            for m, (j, S) in enumerate(zip(rw["other"], rw["shift"])):
+                j = int(j)
+                rj, aj = rowq[j], self.att_row(j)
+                r_idx = rj["key"][(i, -int(S[0]), -int(S[1]), -int(S[2]))]
+                e_m = a["e"][m]
+                kbar += rj["gbar"][r_idx][ht] * aj["q"] * e_m * sq
+                vbar += aj["alpha"][r_idx][ht] * rj["ob"] * e_m
+                cc = qi_["c"][m] + rj["c"][r_idx]
+                rr = rw["r"][m]
+                dhat = rw["d"][m] / rr if rr > 0 else np.zeros(3)
+                grad_pos[n] -= cc * dhat
+                virial[n] += 0.5 * cc * np.outer(dhat, rw["d"][m])
+            h0bar = ub[i] + np.concatenate([qbar, kbar, vbar]) @ self.W_qkv.T
+            grad_h[n] = B.moe_vjp(np.asarray(self.inp["h"][[i]], f64), h0bar[None, :],
+                                  self.z[[i]], self.topk0, self.gate0,
+                                  self.inp["W1_0"], self.inp["W2_0"])[0]
+        return dict(grad_h=grad_h, grad_pos=grad_pos, atom_virial=B.voigt(virial))

@@ -264,3 +264,23 @@ def test_energy_continuous_across_cutoff():
     assert jump < 1e-3 * inside
     # quadratic in the distance to r_c (f_c ~ (pi delta / r_c)^2 / 4 there)
     assert 50 < jump10 / jump < 200
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "top1"])
+def test_local_full_oracle_matches_full(name):
+    from oracle.local import LocalFullBlock
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_full_inputs(cfg)
+    g = _graph(inp)
+    f = A.full_block_forward(inp, g)
+    g_up = synth.upstream_grad(cfg, inp, "random").astype(np.float64)
+    v = A.full_block_vjp(inp, g, f, g_up)
+    atoms = np.random.default_rng(0).choice(cfg.n_atoms, size=min(8, cfg.n_atoms), replace=False)
+    lb = LocalFullBlock(inp)
+    lf = lb.forward(atoms)
+    assert np.allclose(lf["h2"], f["h2"][atoms], atol=1e-10)
+    assert np.allclose(lf["eps"], f["eps"][atoms], atol=1e-10)
+    lv = lb.vjp(atoms, g_up)
+    assert np.allclose(lv["grad_h"], v["grad_h"][atoms], atol=1e-10)
+    assert np.allclose(lv["grad_pos"], v["grad_pos"][atoms], atol=1e-10)
+    assert np.allclose(lv["atom_virial"], v["atom_virial"][atoms], atol=1e-10)
