@@ -124,6 +124,21 @@ AttnVjpWs carve_attn_vjp(void *base, int64_t N, int64_t E, int64_t Da, int64_t n
   return w;
 }
 
+struct TriVjpWs {
+  float *taubar, *sigma, *gvec, *sbar, *virial;
+};
+TriVjpWs carve_tri_vjp(void *base, int64_t N, int64_t E, int64_t Dt, size_t *bytes) {
+  Carver c(base);
+  TriVjpWs w;
+  w.taubar = c.take<float>(size_t(N * Dt));
+  w.sigma = c.take<float>(size_t(E * Dt));
+  w.gvec = c.take<float>(size_t(E * 4));
+  w.sbar = c.take<float>(size_t(N * Dt));
+  w.virial = c.take<float>(size_t(N * 6));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
 // dL/du = g + sum_r gate * ((g[tok] @ W2_x^T) * silu'(P)) @ W1_x^T, gathered back
 // by slot in rank order (two grouped GEMMs and the combine).
 int moe_vjp_core(const float *grad_out, const int32_t *z, const float *gate,
@@ -492,6 +507,105 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   g2.A = w.qkv_bar; g2.lda = 3 * int64_t(d_attn); g2.B = W_qkv; g2.ldb = 3 * int64_t(d_attn);
   g2.C = grad_h0; g2.ldc = d_node; g2.R = grad_u; g2.ldr = d_node;
   g2.M = n_atoms; g2.N = d_node; g2.K = 3 * d_attn;
+  return launch_gemm(g2, true, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+// --------------------------------------------------- three-body update ----
+static int check_tri_dims(int32_t d_node, int32_t d_tri, int32_t n_ang, float cutoff, int *cpl) {
+  MLIP_CHECK_ARG(n_ang == MLIP_N_ANG, "n_ang must be %d", MLIP_N_ANG);
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_tri, "d_tri")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  if (tri_lane_layout(d_tri, cpl) != MLIP_OK) {
+    set_error("d_tri = %d too wide for one wavefront per row (at most 512)", d_tri);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  return MLIP_OK;
+}
+
+int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+             int64_t n_edges, const float *h, const float *W_s, const float *W_ang, const float *W_T,
+             int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff, float *s, float *tau,
+             float *h_T, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0;
+  if (int rc = check_tri_dims(d_node, d_tri, n_ang, cutoff, &cpl)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_s && W_ang && W_T, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (h && s && tau && h_T), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_s, 16) && aligned(W_ang, 16) &&
+                     aligned(W_T, 16) && aligned(s, 16) && aligned(tau, 16) && aligned(h_T, 16),
+                 "float arrays must be 16-byte aligned");
+  if (n_atoms == 0) return MLIP_OK;
+  GemmArgs g;  // s = h @ W_s
+  g.A = h; g.lda = d_node; g.B = W_s; g.ldb = d_tri; g.C = s; g.ldc = d_tri;
+  g.M = n_atoms; g.N = d_tri; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  TriArgs a;
+  a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;
+  a.s = s; a.W_ang = W_ang; a.tau = tau; a.Dt = d_tri; a.cpl = cpl; a.rc = cutoff;
+  if (int rc = launch_tri_fwd(a, stream)) return rc;
+  GemmArgs g2;  // h_T = h + tau @ W_T
+  g2.A = tau; g2.lda = d_tri; g2.B = W_T; g2.ldb = d_node; g2.C = h_T; g2.ldc = d_node;
+  g2.R = h; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_tri;
+  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+size_t mlip_tri_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_tri) {
+  size_t b = 0;
+  carve_tri_vjp(nullptr, std::max(n_atoms, 0), std::max<int64_t>(n_edges, 0), std::max(d_tri, 0),
+                &b);
+  return b;
+}
+
+int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                 int32_t n_atoms, int64_t n_edges, const float *s, const float *W_s,
+                 const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
+                 int32_t d_tri, float cutoff, const float *grad_hT, float *grad_h,
+                 float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
+                 float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
+                 size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0;
+  if (int rc = check_tri_dims(d_node, d_tri, n_ang, cutoff, &cpl)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_s && W_ang && W_T, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (s && grad_hT && grad_h && grad_pos), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && rev && geom), "null edge pointer");
+  MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
+                 "grad_strain needs struct_ptr and n_structs >= 1");
+  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain,
+                 "accumulating into grad_strain needs the accumulated atom_virial");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(s, 16) && aligned(W_s, 16) && aligned(W_ang, 16) &&
+                     aligned(W_T, 16) && aligned(grad_hT, 16) && aligned(grad_h, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_tri_vjp_workspace_size(n_atoms, n_edges, d_tri)))
+    return rc;
+  if (n_atoms == 0) {
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    return MLIP_OK;
+  }
+  TriVjpWs w = carve_tri_vjp(ws, n_atoms, n_edges, d_tri, nullptr);
+  float *vir = atom_virial ? atom_virial : w.virial;
+  GemmArgs g1;  // taubar = grad_hT @ W_T^T
+  g1.A = grad_hT; g1.lda = d_node; g1.B = W_T; g1.ldb = d_node; g1.C = w.taubar; g1.ldc = d_tri;
+  g1.M = n_atoms; g1.N = d_tri; g1.K = d_node;
+  if (int rc = launch_gemm(g1, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  TriArgs a;
+  a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = n_atoms;
+  a.s = s; a.W_ang = W_ang; a.taubar = w.taubar; a.sigma = w.sigma; a.gvec = w.gvec;
+  a.sbar = w.sbar; a.grad_pos = grad_pos; a.atom_virial = vir;
+  a.accumulate = accumulate ? 1 : 0; a.Dt = d_tri; a.cpl = cpl; a.rc = cutoff;
+  if (int rc = launch_tri_vjp(a, stream)) return rc;
+  if (grad_strain) {
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+  }
+  GemmArgs g2;  // grad_h = grad_hT + sbar @ W_s^T
+  g2.A = w.sbar; g2.lda = d_tri; g2.B = W_s; g2.ldb = d_tri; g2.C = grad_h; g2.ldc = d_node;
+  g2.R = grad_hT; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_tri;
   return launch_gemm(g2, true, EPI_RESID, K_GEMM_DENSE, stream);
 }
 

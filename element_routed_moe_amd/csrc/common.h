@@ -60,6 +60,9 @@ enum KClass {
   K_ATTN_FWD,              // neighbour attention, edge part
   K_ATTN_VJP_RECV,         // attention VJP, receiver rows
   K_ATTN_VJP_SEND,         // attention VJP, sender rows (via the reverse edge)
+  K_TRI_FWD,               // three-body update, edge part
+  K_TRI_VJP_RECV,          // three-body VJP, receiver rows
+  K_TRI_VJP_SEND,          // three-body VJP, sender rows
   K_NUM_CLASSES
 };
 
@@ -176,5 +179,28 @@ struct AttnArgs {
 int attn_lane_layout(int Da, int nh, int *cpl, int *lph);
 int launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 int launch_attn_vjp(const AttnArgs &a, hipStream_t stream);
+
+// ------------------------------------------------------- three-body update -
+struct TriArgs {
+  const int32_t *row_ptr = nullptr, *src = nullptr, *rev = nullptr;
+  const float *geom = nullptr;
+  int n_atoms = 0;
+  const float *s = nullptr;       // [N][Dt] = h W_s
+  const float *W_ang = nullptr;   // [4][Dt]
+  float *tau = nullptr;           // [N][Dt]
+  const float *taubar = nullptr;  // [N][Dt]
+  float *sigma = nullptr;         // [E][Dt]
+  float *gvec = nullptr;          // [E][4]
+  float *sbar = nullptr;          // [N][Dt]
+  float *grad_pos = nullptr;      // [N][3]
+  float *atom_virial = nullptr;   // [N][6]
+  int accumulate = 0;
+  int Dt = 0, cpl = 0;
+  float rc = 0.f;
+};
+
+int tri_lane_layout(int Dt, int *cpl);
+int launch_tri_fwd(const TriArgs &a, hipStream_t stream);
+int launch_tri_vjp(const TriArgs &a, hipStream_t stream);
 
 }  // namespace mlip

@@ -1,0 +1,481 @@
+// Three-body angular update ("Tri") of the complete interaction block and
+// its input gradient.
+//
+// The ScienceAI article (architecture section) says three-body angles are
+// embedded; the paper review (section 3.4, Fig. 3) puts Tri first in every
+// interaction block.  The update implemented, for receiver i with edges e
+// (unit vectors dhat_e, envelopes f_e = f_c(r_e), senders j(e)):
+//   tau_ic = sum over ordered pairs e != e' of f_e f_e' (sum_l P_l(dhat_e.dhat_e') W_ang[l,c])
+//            s_j(e),c s_j(e'),c,              s = h W_s,  h_T = h + tau W_T.
+// The O(deg^2) pair sum is evaluated in O(deg) with the addition theorem of
+// the Legendre polynomials, P_l(u.v) = sum_m S_lm(u) S_lm(v) for unit u, v,
+// with S_lm the Schmidt semi-normalised real spherical harmonics (l <= 3,
+// 16 functions):
+//   A_lm,c = sum_e f_e S_lm(dhat_e) s_j(e),c,   B_c = sum_e f_e^2 s_j(e),c^2,
+//   tau_c  = sum_l W_ang[l,c] (sum_m A_lm,c^2 - B_c)          (P_l(1) = 1).
+//
+// Layout: one 64-lane workgroup per receiver row; lane l owns CPL
+// consecutive channels; the 16 harmonics of each edge (times f_e) are
+// computed once per edge and broadcast from LDS.  Gradient (taubar = dL/dtau):
+//   Abar_lm,c = 2 taubar_c W_ang[l,c] A_lm,c,   Bbar_c = -taubar_c sum_l W_ang[l,c];
+//   receiver pass (row i): sigma_e,c = sum_lm Abar_lm,c f_e S_lm(dhat_e) + 2 Bbar_c f_e^2 s_j,c
+//     is stored per edge (it is dL/ds_j(e) from this row); with one lane per
+//     edge, P_lm = sum_c Abar_lm,c s_j,c gives dL/dS_lm = f_e P_lm and
+//     dL/df_e = sum_lm S_lm P_lm + 2 f_e sum_c Bbar_c s_j,c^2, hence the edge
+//     vector dL/dd_e = dL/df_e f_c'(r) dhat + (I - dhat dhat^T) sum_lm dL/dS_lm grad S_lm / r.
+//   sender pass (row j, edges j <- i): sbar_j = sum of sigma over the reverse
+//     edges; forces and virial from dL/dd_e - dL/dd_rev(e).
+// No atomics anywhere.
+#include "common.h"
+
+namespace mlip {
+
+namespace {
+
+constexpr int NSH = 16;      // (l, m) for l = 0..3
+constexpr int NANG = 4;      // Legendre orders l = 0..3
+constexpr int CHUNK = 64;
+constexpr int UNROLL = 2;
+
+__device__ inline int l_of(int lm) { return lm == 0 ? 0 : (lm < 4 ? 1 : (lm < 9 ? 2 : 3)); }
+
+// Schmidt semi-normalised real harmonics at the unit vector (x, y, z)
+__device__ inline void harmonics(float x, float y, float z, float *S) {
+  const float r3 = 1.7320508075688772f, r15 = 3.872983346207417f;
+  const float a58 = 0.7905694150420949f, a38 = 0.6123724356957945f;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  S[0] = 1.f;
+  S[1] = x; S[2] = y; S[3] = z;
+  S[4] = r3 * x * y;
+  S[5] = r3 * y * z;
+  S[6] = 0.5f * (3.f * zz - 1.f);
+  S[7] = r3 * x * z;
+  S[8] = 0.5f * r3 * (xx - yy);
+  S[9] = a58 * y * (3.f * xx - yy);
+  S[10] = r15 * x * y * z;
+  S[11] = a38 * y * (5.f * zz - 1.f);
+  S[12] = 0.5f * z * (5.f * zz - 3.f);
+  S[13] = a38 * x * (5.f * zz - 1.f);
+  S[14] = 0.5f * r15 * z * (xx - yy);
+  S[15] = a58 * x * (xx - 3.f * yy);
+}
+
+// sum_lm w[lm] grad S_lm at (x, y, z) (gradient of the polynomial forms above)
+__device__ inline float3 harmonics_grad(float x, float y, float z, const float *w) {
+  const float r3 = 1.7320508075688772f, r15 = 3.872983346207417f;
+  const float a58 = 0.7905694150420949f, a38 = 0.6123724356957945f;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  float gx = w[1], gy = w[2], gz = w[3];
+  gx += r3 * (w[4] * y + w[7] * z + w[8] * x);
+  gy += r3 * (w[4] * x + w[5] * z - w[8] * y);
+  gz += r3 * (w[5] * y + w[7] * x) + 3.f * z * w[6];
+  gx += a58 * 6.f * x * y * w[9] + r15 * y * z * w[10] + a38 * (5.f * zz - 1.f) * w[13] +
+        r15 * x * z * w[14] + a58 * 3.f * (xx - yy) * w[15];
+  gy += a58 * 3.f * (xx - yy) * w[9] + r15 * x * z * w[10] + a38 * (5.f * zz - 1.f) * w[11] -
+        r15 * y * z * w[14] - a58 * 6.f * x * y * w[15];
+  gz += r15 * x * y * w[10] + a38 * 10.f * y * z * w[11] + 0.5f * (15.f * zz - 3.f) * w[12] +
+        a38 * 10.f * x * z * w[13] + 0.5f * r15 * (xx - yy) * w[14];
+  return make_float3(gx, gy, gz);
+}
+
+template <int CPL>
+__device__ inline void ldc(const float *p, float (&x)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4 *>(p)[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+  } else if constexpr (CPL % 2 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 2; ++q) {
+      const float2 v = reinterpret_cast<const float2 *>(p)[q];
+      x[2 * q] = v.x; x[2 * q + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) x[q] = p[q];
+  }
+}
+
+template <int CPL>
+__device__ inline void stc(float *p, const float (&x)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q)
+      reinterpret_cast<float4 *>(p)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  } else if constexpr (CPL % 2 == 0) {
+#pragma unroll
+    for (int q = 0; q < CPL / 2; ++q) reinterpret_cast<float2 *>(p)[q] = make_float2(x[2 * q], x[2 * q + 1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) p[q] = x[q];
+  }
+}
+
+// Per-edge prologue shared by the kernels: f_e S_lm(dhat_e) into LDS.
+struct EdgeGeo {
+  float fc, dfc, inv_r;
+  float3 u;
+};
+
+__device__ inline EdgeGeo edge_geo(float4 g, const Radial &R) {
+  EdgeGeo o;
+  const float r = g.w;
+  o.fc = 0.f;
+  o.dfc = 0.f;
+  if (r < R.rc) {
+    float sn, cs;
+    __sincosf(r * R.pi_over_rc, &sn, &cs);
+    o.fc = 0.5f * (cs + 1.f);
+    o.dfc = -0.5f * R.pi_over_rc * sn;
+  }
+  o.inv_r = r > 0.f ? 1.f / r : 0.f;
+  o.u = make_float3(g.x * o.inv_r, g.y * o.inv_r, g.z * o.inv_r);
+  return o;
+}
+
+// Accumulates A_lm,c and B_c of row i over its edges (channel layout).
+template <int CPL>
+__device__ inline void accumulate_row(const int32_t *__restrict__ src, const float4 *__restrict__ geom,
+                                      const float *__restrict__ s, int Dt, int c0, int r0, int r1,
+                                      const Radial &R, float (*ysh)[NSH], float *fsq, int *jj,
+                                      float (&A)[NSH][CPL], float (&Bs)[CPL]) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int lm = 0; lm < NSH; ++lm)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) A[lm][c] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) Bs[c] = 0.f;
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      const EdgeGeo G = edge_geo(geom[e0 + lane], R);
+      float S[NSH];
+      harmonics(G.u.x, G.u.y, G.u.z, S);
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) ysh[lane][lm] = G.fc * S[lm];
+      fsq[lane] = G.fc * G.fc;
+      jj[lane] = src[e0 + lane];
+    }
+    __syncthreads();
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float sj[UNROLL][CPL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) ldc<CPL>(s + int64_t(jj[min(mm + u, n - 1)]) * Dt + c0, sj[u]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (mm + u < n) {
+          const int me = mm + u;
+          const float fq = fsq[me];
+#pragma unroll
+          for (int lm = 0; lm < NSH; ++lm) {
+            const float y = ysh[me][lm];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) A[lm][c] += y * sj[u][c];
+          }
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) Bs[c] += fq * sj[u][c] * sj[u][c];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- forward ---
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_fwd_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
+    const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ s,
+    const float *__restrict__ W_ang, int Dt, float rc, float *__restrict__ tau) {
+  __shared__ float ysh[CHUNK][NSH];
+  __shared__ float fsq[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const bool active = lane * CPL < Dt;
+  const int c0 = active ? lane * CPL : 0;
+  const Radial R = make_radial(rc);
+  float A[NSH][CPL], Bs[CPL];
+  accumulate_row<CPL>(src, geom, s, Dt, c0, row_ptr[i], row_ptr[i + 1], R, ysh, fsq, jj, A, Bs);
+  if (!active) return;
+  float w[NANG][CPL];
+#pragma unroll
+  for (int l = 0; l < NANG; ++l) ldc<CPL>(W_ang + int64_t(l) * Dt + c0, w[l]);
+  float t[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float q[NANG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int lm = 0; lm < NSH; ++lm) q[l_of(lm)] += A[lm][c] * A[lm][c];
+    float acc = 0.f;
+#pragma unroll
+    for (int l = 0; l < NANG; ++l) acc += w[l][c] * (q[l] - Bs[c]);
+    t[c] = acc;
+  }
+  stc<CPL>(tau + int64_t(i) * Dt + c0, t);
+}
+
+// ------------------------------------------------ gradient: receiver rows --
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
+    const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ s,
+    const float *__restrict__ W_ang, const float *__restrict__ taubar, int Dt, float rc,
+    float *__restrict__ sigma, float4 *__restrict__ gvec) {
+  extern __shared__ float dyn[];           // Abar [NSH][Dt], then Bbar [Dt]
+  __shared__ float ysh[CHUNK][NSH];
+  __shared__ float fsq[CHUNK];
+  __shared__ int jj[CHUNK];
+  float *abar_s = dyn;
+  float *bbar_s = dyn + NSH * Dt;
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const bool active = lane * CPL < Dt;
+  const int c0 = active ? lane * CPL : 0;
+  const Radial R = make_radial(rc);
+  const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+  float A[NSH][CPL], Bs[CPL];
+  accumulate_row<CPL>(src, geom, s, Dt, c0, r0, r1, R, ysh, fsq, jj, A, Bs);
+
+  // Abar, Bbar for this row (registers for the channel pass, LDS for the edge pass)
+  {
+    float w[NANG][CPL], tb[CPL];
+#pragma unroll
+    for (int l = 0; l < NANG; ++l) ldc<CPL>(W_ang + int64_t(l) * Dt + c0, w[l]);
+    ldc<CPL>(taubar + int64_t(i) * Dt + c0, tb);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float wsum = 0.f;
+#pragma unroll
+      for (int l = 0; l < NANG; ++l) wsum += w[l][c];
+      Bs[c] = active ? -tb[c] * wsum : 0.f;           // Bs now holds Bbar
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) A[lm][c] = active ? 2.f * tb[c] * w[l_of(lm)][c] * A[lm][c] : 0.f;
+    }
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+        for (int lm = 0; lm < NSH; ++lm) abar_s[lm * Dt + c0 + c] = A[lm][c];
+        bbar_s[c0 + c] = Bs[c];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    EdgeGeo G = {0.f, 0.f, 0.f, make_float3(0.f, 0.f, 0.f)};
+    float S[NSH] = {};
+    int jmine = 0;
+    if (lane < n) {
+      G = edge_geo(geom[e0 + lane], R);
+      harmonics(G.u.x, G.u.y, G.u.z, S);
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) ysh[lane][lm] = G.fc * S[lm];
+      fsq[lane] = G.fc * G.fc;
+      jmine = src[e0 + lane];
+      jj[lane] = jmine;
+    }
+    __syncthreads();
+    // channel pass: sigma_e = sum_lm Abar_lm f S_lm + 2 Bbar f^2 s_j  (coalesced rows)
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float sj[UNROLL][CPL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) ldc<CPL>(s + int64_t(jj[min(mm + u, n - 1)]) * Dt + c0, sj[u]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (mm + u < n && active) {
+          const int me = mm + u;
+          float out[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) out[c] = 2.f * Bs[c] * fsq[me] * sj[u][c];
+#pragma unroll
+          for (int lm = 0; lm < NSH; ++lm) {
+            const float y = ysh[me][lm];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) out[c] += A[lm][c] * y;
+          }
+          stc<CPL>(sigma + int64_t(e0 + me) * Dt + c0, out);
+        }
+      }
+    }
+    // edge pass: lane = edge; P_lm = sum_c Abar_lm,c s_j,c and Q = sum_c Bbar_c s_j,c^2
+    if (lane < n) {
+      float P[NSH];
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) P[lm] = 0.f;
+      float Q = 0.f;
+      const float *srow = s + int64_t(jmine) * Dt;
+      for (int c = 0; c < Dt; c += 4) {          // Dt is a multiple of 4
+        const float4 v = *reinterpret_cast<const float4 *>(srow + c);
+        const float sv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Q += bbar_s[c + q] * sv[q] * sv[q];
+#pragma unroll
+          for (int lm = 0; lm < NSH; ++lm) P[lm] += abar_s[lm * Dt + c + q] * sv[q];
+        }
+      }
+      float fbar = 2.f * G.fc * Q;
+      float sbar_lm[NSH];
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) {
+        fbar += S[lm] * P[lm];
+        sbar_lm[lm] = G.fc * P[lm];
+      }
+      const float3 gu = harmonics_grad(G.u.x, G.u.y, G.u.z, sbar_lm);
+      const float rad = gu.x * G.u.x + gu.y * G.u.y + gu.z * G.u.z;
+      const float a = fbar * G.dfc;
+      gvec[e0 + lane] = make_float4(a * G.u.x + (gu.x - rad * G.u.x) * G.inv_r,
+                                    a * G.u.y + (gu.y - rad * G.u.y) * G.inv_r,
+                                    a * G.u.z + (gu.z - rad * G.u.z) * G.inv_r, 0.f);
+    }
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------- gradient: sender rows --
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_vjp_send_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ rev,
+    const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ sigma,
+    const float4 *__restrict__ gvec, int Dt, int accumulate, float *__restrict__ sbar,
+    float *__restrict__ grad_pos, float *__restrict__ atom_virial) {
+  __shared__ int rr[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(n_atoms);
+  if (blk < 0) return;
+  const int j = int(blk);
+  const bool active = lane * CPL < Dt;
+  const int c0 = active ? lane * CPL : 0;
+  float sb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sb[c] = 0.f;
+  float fx = 0.f, fy = 0.f, fz = 0.f;
+  float vir[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r0 = row_ptr[j], r1 = row_ptr[j + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      const int e = e0 + lane;
+      const int re = rev[e];
+      rr[lane] = re;
+      const float4 ge = gvec[e], gr = gvec[re], d = geom[e];
+      const float gx = ge.x - gr.x, gy = ge.y - gr.y, gz = ge.z - gr.z;   // d_rev = -d
+      fx += gx;
+      fy += gy;
+      fz += gz;
+      vir[0] += 0.5f * gx * d.x;
+      vir[1] += 0.5f * gy * d.y;
+      vir[2] += 0.5f * gz * d.z;
+      vir[3] += 0.25f * (gy * d.z + gz * d.y);
+      vir[4] += 0.25f * (gx * d.z + gz * d.x);
+      vir[5] += 0.25f * (gx * d.y + gy * d.x);
+    }
+    __syncthreads();
+    for (int mm = 0; mm < n; mm += UNROLL) {
+      float sg[UNROLL][CPL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        ldc<CPL>(sigma + int64_t(rr[min(mm + u, n - 1)]) * Dt + c0, sg[u]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (mm + u < n)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) sb[c] += sg[u][c];
+    }
+    __syncthreads();
+  }
+  if (active) stc<CPL>(sbar + int64_t(j) * Dt + c0, sb);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    fx += __shfl_xor(fx, d, 64);
+    fy += __shfl_xor(fy, d, 64);
+    fz += __shfl_xor(fz, d, 64);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) vir[q] += __shfl_xor(vir[q], d, 64);
+  }
+  if (lane == 0) {
+    float *gp = grad_pos + int64_t(j) * 3;
+    float *av = atom_virial + int64_t(j) * 6;
+    const float g3[3] = {-fx, -fy, -fz};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) gp[q] = accumulate ? gp[q] + g3[q] : g3[q];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) av[q] = accumulate ? av[q] + vir[q] : vir[q];
+  }
+}
+
+template <int CPL>
+int launch_cpl(int which, const TriArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(padded_grid(a.n_atoms))), block(64);
+  const float4 *g4 = reinterpret_cast<const float4 *>(a.geom);
+  if (which == 0) {
+    tri_fwd_kernel<CPL><<<grid, block, 0, stream>>>(a.row_ptr, a.src, g4, a.n_atoms, a.s, a.W_ang,
+                                                    a.Dt, a.rc, a.tau);
+  } else if (which == 1) {
+    const size_t dyn = size_t(NSH + 1) * a.Dt * sizeof(float);
+    tri_vjp_recv_kernel<CPL><<<grid, block, dyn, stream>>>(
+        a.row_ptr, a.src, g4, a.n_atoms, a.s, a.W_ang, a.taubar, a.Dt, a.rc, a.sigma,
+        reinterpret_cast<float4 *>(a.gvec));
+  } else {
+    tri_vjp_send_kernel<CPL><<<grid, block, 0, stream>>>(
+        a.row_ptr, a.rev, g4, a.n_atoms, a.sigma, reinterpret_cast<const float4 *>(a.gvec), a.Dt,
+        a.accumulate, a.sbar, a.grad_pos, a.atom_virial);
+  }
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+int dispatch(int which, const TriArgs &a, hipStream_t stream) {
+  switch (a.cpl) {
+    case 1: return launch_cpl<1>(which, a, stream);
+    case 2: return launch_cpl<2>(which, a, stream);
+    case 3: return launch_cpl<3>(which, a, stream);
+    case 4: return launch_cpl<4>(which, a, stream);
+    case 6: return launch_cpl<6>(which, a, stream);
+    case 8: return launch_cpl<8>(which, a, stream);
+    default: break;
+  }
+  set_error("no three-body lane layout for %d channels per lane", a.cpl);
+  return MLIP_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int tri_lane_layout(int Dt, int *cpl) {
+  const int options[] = {1, 2, 3, 4, 6, 8};
+  for (int c : options) {
+    if (Dt % c == 0 && Dt <= 64 * c) {
+      *cpl = c;
+      return MLIP_OK;
+    }
+  }
+  return MLIP_ERR_UNSUPPORTED;
+}
+
+int launch_tri_fwd(const TriArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  ProfScope ps(K_TRI_FWD, stream);
+  return dispatch(0, a, stream);
+}
+
+int launch_tri_vjp(const TriArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  {
+    ProfScope ps(K_TRI_VJP_RECV, stream);
+    if (int rc = dispatch(1, a, stream)) return rc;
+  }
+  ProfScope ps(K_TRI_VJP_SEND, stream);
+  return dispatch(2, a, stream);
+}
+
+}  // namespace mlip

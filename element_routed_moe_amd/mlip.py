@@ -24,6 +24,7 @@ MLIP_ERR_UNSUPPORTED = -3
 MLIP_ERR_HIP = -4
 MLIP_ERR_INPUT = -5
 N_RBF = 16
+N_ANG = 4
 
 
 class MlipError(RuntimeError):
@@ -65,6 +66,11 @@ _SIGS = {
     "mlip_attention_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32,
                                      _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _p,
                                      _sz, _p]),
+    "mlip_tri": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
+                           _p, _p]),
+    "mlip_tri_vjp_workspace_size": (_sz, [_i32, _i64, _i32]),
+    "mlip_tri_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+                               _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _sz, _p]),
     "mlip_profile_enable": (C.c_int, [C.c_int]),
     "mlip_profile_reset": (C.c_int, []),
     "mlip_profile_count": (C.c_int, []),
@@ -284,6 +290,44 @@ def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float
     return out
 
 
+def mlip_tri(graph, h, W_s, W_ang, W_T, cutoff: float, out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    N, Dn = int(h.shape[0]), int(h.shape[1])
+    Dt = int(W_s.shape[1])
+    E = int(graph["n_edges"])
+    dev = h.device
+    if out is None:
+        out = dict(s=torch.empty((N, Dt), dtype=torch.float32, device=dev),
+                   tau=torch.empty((N, Dt), dtype=torch.float32, device=dev),
+                   h_T=torch.empty((N, Dn), dtype=torch.float32, device=dev))
+    _check(_lib.mlip_tri(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E, _ptr(h),
+                         _ptr(W_s), _ptr(W_ang), _ptr(W_T), int(W_ang.shape[0]), Dn, Dt, float(cutoff),
+                         _ptr(out["s"]), _ptr(out["tau"]), _ptr(out["h_T"]), _stream()))
+    return out
+
+
+def mlip_tri_vjp(graph, tri, W_s, W_ang, W_T, cutoff: float, grad_hT, grad_pos, atom_virial=None,
+                 grad_strain=None, struct_ptr=None, accumulate: bool = False,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """dL/dh of the three-body update; grad_pos / atom_virial are written, or added
+    to when ``accumulate`` (then grad_strain is recomputed from atom_virial)."""
+    N, Dn = int(grad_hT.shape[0]), int(grad_hT.shape[1])
+    Dt = int(W_s.shape[1])
+    E = int(graph["n_edges"])
+    dev = grad_hT.device
+    B = int(struct_ptr.shape[0]) - 1 if struct_ptr is not None else 0
+    if out is None:
+        out = torch.empty((N, Dn), dtype=torch.float32, device=dev)
+    need = _lib.mlip_tri_vjp_workspace_size(N, E, Dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_tri_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["rev"]),
+                             _ptr(graph["geom"]), N, E, _ptr(tri["s"]), _ptr(W_s), _ptr(W_ang), _ptr(W_T),
+                             int(W_ang.shape[0]), Dn, Dt, float(cutoff), _ptr(grad_hT), _ptr(out),
+                             _ptr(grad_pos), _ptr(struct_ptr), B, _ptr(atom_virial), _ptr(grad_strain),
+                             1 if accumulate else 0, _ptr(ws), ws.numel(), _stream()))
+    return out, ws
+
+
 # ------------------------------------------------------------------ timing
 def profile_enable(on: bool = True):
     _check(_lib.mlip_profile_enable(1 if on else 0))
@@ -366,11 +410,13 @@ class Block:
 
 
 class FullBlock:
-    """The complete interaction block: MoE0 -> neighbour attention -> MoE1.
+    """The complete interaction block: Tri -> MoE0 -> neighbour attention -> MoE1.
 
-    ``step()`` runs on the current stream: radius graph, MoE0 on h, attention,
-    MoE1, readout, then the input gradient back through MoE1, the attention
-    (forces and virial) and MoE0 for the given upstream gradient dL/dh'.
+    ``step()`` runs on the current stream: radius graph, the three-body update
+    (when the inputs carry its weights), MoE0, attention, MoE1, readout, then
+    the input gradient back through MoE1, the attention, MoE0 and Tri
+    (forces and virial of both geometric operators) for the given upstream
+    gradient dL/dh'.
     """
 
     def __init__(self, inputs: Dict, device="cuda", grad_out=None):
@@ -398,6 +444,11 @@ class FullBlock:
         self.cutoff = float(inputs["cutoff"])
         self.top_k = int(inputs["top_k"])
         self.n_heads = int(inputs["n_heads"])
+        self.has_tri = "W_ang" in inputs
+        if self.has_tri:
+            self.W_s = dev(inputs["W_s"], f32)
+            self.W_ang = dev(inputs["W_ang"], f32)
+            self.W_T = dev(inputs["W_T"], f32)
         if grad_out is None:
             grad_out = self.w_r.expand(self.h.shape[0], -1)
         self.grad_out = dev(grad_out, f32)
@@ -409,10 +460,10 @@ class FullBlock:
         self.ws_moe0 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_moe1 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_mvjp = _ws(_lib.mlip_moe_vjp_workspace_size(N, self.top_k, Dn, H), device)
-        self.ws_avjp = None
+        self.ws_avjp = self.ws_tvjp = None
         self.edge_capacity = None
-        self.graph = self.moe0 = self.att = self.moe = self.ro = None
-        self.ubar = self.avjp = self.grad_h = None
+        self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
+        self.ubar = self.avjp = self.grad_hT = self.grad_h = None
 
     def step(self):
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
@@ -420,7 +471,11 @@ class FullBlock:
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
         self.graph = g
-        self.moe0 = mlip_moe_forward(self.h, self.z, self.logits0, self.W1_0, self.W2_0, self.top_k,
+        h = self.h
+        if self.has_tri:
+            self.tri = mlip_tri(g, self.h, self.W_s, self.W_ang, self.W_T, self.cutoff, out=self.tri)
+            h = self.tri["h_T"]
+        self.moe0 = mlip_moe_forward(h, self.z, self.logits0, self.W1_0, self.W2_0, self.top_k,
                                      out=self.moe0, ws=self.ws_moe0)
         self.att = mlip_attention(g, self.moe0["h_out"], self.W_qkv, self.Wa_e, self.W_o,
                                   self.n_heads, self.cutoff, out=self.att)
@@ -433,6 +488,15 @@ class FullBlock:
                                        self.cutoff, self.ubar, struct_ptr=self.struct_ptr,
                                        out=self.avjp, ws=self.ws_avjp)
         self.ws_avjp = self.avjp["ws"]
-        self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
-                                   out=self.grad_h, ws=self.ws_mvjp)
+        if self.has_tri:
+            self.grad_hT = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
+                                        out=self.grad_hT, ws=self.ws_mvjp)
+            self.grad_h, self.ws_tvjp = mlip_tri_vjp(
+                g, self.tri, self.W_s, self.W_ang, self.W_T, self.cutoff, self.grad_hT,
+                self.avjp["grad_pos"], atom_virial=self.avjp["atom_virial"],
+                grad_strain=self.avjp["grad_strain"], struct_ptr=self.struct_ptr, accumulate=True,
+                out=self.grad_h, ws=self.ws_tvjp)
+        else:
+            self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
+                                       out=self.grad_h, ws=self.ws_mvjp)
         return self

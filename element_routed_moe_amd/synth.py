@@ -33,6 +33,7 @@ from typing import Dict, List, Optional, Sequence, Union
 import numpy as np
 
 IntOrList = Union[int, Sequence[int]]
+N_ANG = 4          # Legendre orders l = 0..3 of the three-body update
 FloatOrList = Union[float, Sequence[float]]
 
 
@@ -209,8 +210,12 @@ def make_full_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, 
     plus the extra parameters, drawn from a second generator seeded with
     (seed, 1) in this order: the MoE0 logit table logits0 ~ N(0,1) [T, X];
     Wa_e [K, Da]; W_qkv [Dn, 3 Da] (columns q | k | v); W_o [Da, Dn];
-    W1_0 [X, Dn, H]; W2_0 [X, H, Dn] (weights ~ N(0, 1/fan_in)).  MoE1 uses
-    ``logits``, ``W1``, ``W2`` and the readout ``w_r`` of ``make_inputs``."""
+    W1_0 [X, Dn, H]; W2_0 [X, H, Dn] (weights ~ N(0, 1/fan_in)); then the
+    three-body update: W_s [Dn, Dt] ~ N(0, 1/Dn), W_ang [L, Dt] ~ N(0, 1/L)
+    scaled by 1/50 (about one over the number of neighbour pairs' square
+    root, so that the pair sum stays of order one), W_T [Dt, Dn] ~ N(0, 1/Dt),
+    with Dt = Da and L = N_ANG.  MoE1 uses ``logits``, ``W1``, ``W2`` and the
+    readout ``w_r`` of ``make_inputs``."""
     if cfg.d_attn <= 0 or cfg.n_heads <= 0:
         raise ValueError(f"config {cfg.name} has no attention width")
     out = make_inputs(cfg, seed)
@@ -224,6 +229,9 @@ def make_full_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, 
     out["W_o"] = _normal(rng, (Da, Dn), 1.0 / math.sqrt(Da))
     out["W1_0"] = _normal(rng, (X, Dn, H), 1.0 / math.sqrt(Dn))
     out["W2_0"] = _normal(rng, (X, H, Dn), 1.0 / math.sqrt(H))
+    out["W_s"] = _normal(rng, (Dn, Da), 1.0 / math.sqrt(Dn))
+    out["W_ang"] = _normal(rng, (N_ANG, Da), 1.0 / (math.sqrt(N_ANG) * 50.0))
+    out["W_T"] = _normal(rng, (Da, Dn), 1.0 / math.sqrt(Da))
     out["n_heads"] = int(cfg.n_heads)
     return out
 

@@ -2,9 +2,10 @@
  * mlip.h - C ABI of the MI355X (gfx950) library for one MatRIS-MoE
  * interaction block: periodic radius graph, neighbour aggregation,
  * element-routed top-k mixture of experts, readout, and the input gradient
- * (VJP) that conservative forces and stresses need; plus the neighbour
- * multi-head attention and the stand-alone MoE gradient that the complete
- * block (MoE0, attention, MoE1) is built from.
+ * (VJP) that conservative forces and stresses need; plus the three-body
+ * update, the neighbour multi-head attention and the stand-alone MoE
+ * gradient that the complete block (Tri, MoE0, attention, MoE1) is built
+ * from.
  *
  * Sources (cited by page title and section):
  *   [news]   ScienceAI news article on MatRIS-MoE and Janus, sections on the
@@ -52,6 +53,7 @@ extern "C" {
 #define MLIP_ERR_INPUT (-5)       /* input data rejected by a device-side check */
 
 #define MLIP_N_RBF 16
+#define MLIP_N_ANG 4   /* Legendre orders l = 0..3 of the three-body update */
 
 const char *mlip_last_error(void);
 int mlip_version(void);
@@ -274,6 +276,53 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                        float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
                        float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
                        void *stream);
+
+/* ------------------------------------------------------------------------
+ * Three-body angular update ("Tri") of the complete block ([news]
+ * architecture section: three-body angles are embedded; [review] 3.4 Fig. 3:
+ * Tri is the first operator of every block).  The pages give no formula; the
+ * reading implemented, for receiver i with edges e (unit vectors dhat_e,
+ * envelopes f_e = f_c(r_e) as in mlip_aggregate, senders j(e)):
+ *     s      = h @ W_s                                    [n_atoms, d_tri]
+ *     tau_ic = sum over ordered pairs e != e' of row i of
+ *              f_e f_e' (sum_l P_l(dhat_e . dhat_e') W_ang[l,c]) s_j(e),c s_j(e'),c
+ *     h_T    = h + tau @ W_T
+ * with P_l the Legendre polynomials, l = 0 .. n_ang-1 (n_ang must be
+ * MLIP_N_ANG).  The pair sum is evaluated exactly through the addition
+ * theorem of the Legendre polynomials (16 real spherical harmonics per edge),
+ * so the cost is O(edges), not O(edges x degree).  Edges of zero length are
+ * outside the contract.
+ *
+ * W_s [d_node, d_tri], W_ang [n_ang, d_tri], W_T [d_tri, d_node];
+ * d_tri <= 512 (one wavefront per row).  Outputs s (kept for mlip_tri_vjp),
+ * tau [n_atoms, d_tri] and h_T [n_atoms, d_node] (may not alias h).
+ * ------------------------------------------------------------------------ */
+int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+             int64_t n_edges, const float *h, const float *W_s, const float *W_ang, const float *W_T,
+             int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff, float *s, float *tau,
+             float *h_T, void *stream);
+
+/* Input gradient of mlip_tri for grad_hT = dL/dh_T:
+ *   grad_h [n_atoms, d_node] = dL/dh;
+ *   grad_pos [n_atoms, 3], atom_virial [n_atoms, 6] (optional, Voigt order,
+ *     each edge's symmetrised dL/dd_e (x) d_e shared half and half by its two
+ *     atoms), grad_strain [n_structs, 6] (optional, float64, the per-structure
+ *     sum of atom_virial) as in mlip_block_vjp;
+ *   accumulate != 0: grad_pos and atom_virial are ADDED to (so the forces of
+ *     a whole block can be collected, e.g. after mlip_attention_vjp), and
+ *     grad_strain, if given, is recomputed from the accumulated atom_virial
+ *     (which must then be given).
+ * rev is the reverse-edge index; s comes from the mlip_tri call of the step.
+ * Per-edge intermediates (d_tri floats per edge) live in the workspace
+ * (mlip_tri_vjp_workspace_size).  No atomics. */
+size_t mlip_tri_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_tri);
+int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                 int32_t n_atoms, int64_t n_edges, const float *s, const float *W_s,
+                 const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
+                 int32_t d_tri, float cutoff, const float *grad_hT, float *grad_h,
+                 float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
+                 float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
+                 size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  When enabled, every kernel launch of the library is

@@ -29,6 +29,8 @@ The pages give no formula for any of it.  Readings taken here:
   softmax denominator by a finite amount and the energy would jump, which
   the smooth energy surface the pages require rules out.
 * MoE1 and the readout are those of ``oracle.block``:  h' = u + MoE1(u).
+* Tri, the three-body update of ``oracle.tri``, runs first when the inputs
+  carry its weights (``W_ang``): h_T = Tri(h) feeds MoE0.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import block as B
+from . import tri as TR
 
 f64 = np.float64
 
@@ -151,19 +154,25 @@ def attention_vjp(fw: Dict, graph: Dict[str, np.ndarray], W_qkv: np.ndarray, Wa_
 
 # ------------------------------------------------------- complete block ----
 def full_block_forward(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray]) -> Dict:
-    """h -> MoE0 -> attention -> MoE1 -> readout, on a prebuilt radius graph."""
+    """h -> (Tri) -> MoE0 -> attention -> MoE1 -> readout, on a prebuilt radius graph."""
     rc = B._cutoff(inp)
-    h = np.asarray(inp["h"], f64)
+    h_in = np.asarray(inp["h"], f64)
     k = int(inp["top_k"])
     nh = int(inp["n_heads"])
+    tri = None
+    if "W_ang" in inp:
+        tri = TR.tri_forward(h_in, graph, inp["W_s"], inp["W_ang"], inp["W_T"], rc)
+        h = tri["hT"]
+    else:
+        h = h_in
     topk0, gate0 = B.route(inp["logits0"], k)
     h0 = B.moe_forward(h, inp["z"], topk0, gate0, inp["W1_0"], inp["W2_0"])
     att = attention_forward(h0, graph, inp["W_qkv"], inp["Wa_e"], inp["W_o"], nh, rc)
     topk, gate = B.route(inp["logits"], k)
     h2 = B.moe_forward(att["u"], inp["z"], topk, gate, inp["W1"], inp["W2"])
     eps, E = B.readout(h2, inp["w_r"], inp["struct_ptr"])
-    return dict(h=h, topk0=topk0, gate0=gate0, att=att, u=att["u"], topk=topk, gate=gate,
-                h2=h2, eps=eps, E=E)
+    return dict(h=h, tri=tri, topk0=topk0, gate0=gate0, att=att, u=att["u"], topk=topk,
+                gate=gate, h2=h2, eps=eps, E=E)
 
 
 def full_block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray], fwd: Dict,
@@ -178,9 +187,20 @@ def full_block_vjp(inp: Dict[str, np.ndarray], graph: Dict[str, np.ndarray], fwd
     hbar = B.moe_vjp(fwd["h"], ab["grad_h0"], inp["z"], fwd["topk0"], fwd["gate0"],
                      inp["W1_0"], inp["W2_0"])
     N = hbar.shape[0]
-    gpos, gstrain, av = B.edge_forces(ab["c"], graph, N, inp["struct_ptr"])
-    return dict(ubar=ubar, grad_h0=ab["grad_h0"], c=ab["c"], grad_h=hbar, grad_pos=gpos,
-                grad_strain=gstrain, atom_virial=av, att=ab)
+    r, d = graph["r"], graph["d"]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        dhat = np.where(r[:, None] > 0, d / r[:, None], 0.0)
+    gvec = ab["c"][:, None] * dhat
+    tb = None
+    hT_bar = hbar
+    if fwd["tri"] is not None:
+        tb = TR.tri_vjp(fwd["tri"], graph, inp["W_s"], inp["W_ang"], inp["W_T"], rc, hT_bar)
+        hbar = tb["grad_h"]
+        gvec = gvec + tb["gvec"]
+    gpos, gstrain, av = B.edge_forces_vec(gvec, graph, N, inp["struct_ptr"])
+    return dict(ubar=ubar, grad_h0=ab["grad_h0"], grad_hT=hT_bar, c=ab["c"], gvec=gvec,
+                grad_h=hbar, grad_pos=gpos, grad_strain=gstrain, atom_virial=av, att=ab,
+                tri=tb)
 
 
 def full_energy(inp: Dict[str, np.ndarray], pos: Optional[np.ndarray] = None,

@@ -256,26 +256,38 @@ def edge_forces(c: np.ndarray, graph: Dict[str, np.ndarray], n_atoms: int,
                 struct_ptr: np.ndarray):
     """Position gradient, strain gradient and per-atom virial from c_e = dL/dr_e.
 
-    r = |d|, d = x_src - x_recv + S.C, so dr/dx_src = d/r and dr/dx_recv = -d/r.
-    Under the homogeneous strain x -> (I + eps) x of positions and cell,
-    d_e -> (I + eps) d_e and dL/deps_ab = sum_e c_e dhat_a d_b; each atom of
-    an edge gets half of that edge's term in its virial (Voigt order).
+    r = |d|, d = x_src - x_recv + S.C, so dL/dd_e = c_e dhat_e (see ``edge_forces_vec``).
     """
-    recv, src, r, d = graph["recv"], graph["src"], graph["r"], graph["d"]
+    r, d = graph["r"], graph["d"]
     with np.errstate(invalid="ignore", divide="ignore"):
         dhat = np.where(r[:, None] > 0, d / r[:, None], 0.0)
+    return edge_forces_vec(c[:, None] * dhat, graph, n_atoms, struct_ptr)
+
+
+def edge_forces_vec(gvec: np.ndarray, graph: Dict[str, np.ndarray], n_atoms: int,
+                    struct_ptr: np.ndarray):
+    """Position gradient, strain gradient and per-atom virial from g_e = dL/dd_e.
+
+    d_e = x_src - x_recv + S.C, so dL/dx_src += g_e and dL/dx_recv -= g_e.
+    Under the homogeneous strain x -> (I + eps) x of positions and cell,
+    d_e -> (I + eps) d_e and dL/deps_ab = sum_e g_e,a d_e,b.  Each atom of an
+    edge gets half of the symmetric part of that edge's term in its virial
+    (Voigt order).
+    """
+    recv, src, d = graph["recv"], graph["src"], graph["d"]
     gpos = np.zeros((n_atoms, 3), f64)
-    np.add.at(gpos, src, c[:, None] * dhat)
-    np.add.at(gpos, recv, -c[:, None] * dhat)
-    outer = c[:, None, None] * dhat[:, :, None] * d[:, None, :]          # [E, 3, 3]
+    np.add.at(gpos, src, gvec)
+    np.add.at(gpos, recv, -gvec)
+    outer = gvec[:, :, None] * d[:, None, :]                            # [E, 3, 3]
     sp = np.asarray(struct_ptr, np.int64)
     nb = len(sp) - 1
     sb_of_edge = np.searchsorted(sp, recv, side="right") - 1
     gstrain = np.zeros((nb, 3, 3), f64)
     np.add.at(gstrain, sb_of_edge, outer)
+    sym = 0.5 * (outer + outer.transpose(0, 2, 1))
     av = np.zeros((n_atoms, 3, 3), f64)
-    np.add.at(av, recv, 0.5 * outer)
-    np.add.at(av, src, 0.5 * outer)
+    np.add.at(av, recv, 0.5 * sym)
+    np.add.at(av, src, 0.5 * sym)
     return gpos, gstrain, voigt(av)
 
 

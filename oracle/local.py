@@ -181,21 +181,24 @@ class LocalBlock:
 
 
 class LocalFullBlock(LocalBlock):
-    """The complete block (``oracle.attention``) at a few sampled atoms.
+    """The complete block (``oracle.attention``, with ``oracle.tri`` first) at a
+    few sampled atoms.
 
-    The forward at atom i needs MoE0 at i and at its neighbours (q_i, k_j,
-    v_j) and the softmax over row i.  The input gradient at i needs, for i
-    and each neighbour j, the whole softmax of row j (so MoE0 on the
-    neighbours of the neighbours), dL/du there (MoE1 backwards), and the
-    receiver-side edge quantities of row j for the reverse edge j <- i.
-    Every per-atom step is the oracle's own step function on a subset of
-    atoms; MoE layers act atom by atom, so subsets give the same rows.
+    The forward at atom i needs Tri and MoE0 at i and at its neighbours
+    (q_i, k_j, v_j) and the softmax over row i.  The input gradient at i needs
+    the attention's receiver-side quantities of every row within two hops
+    (for the reverse edges and for kbar, vbar of the neighbours), hence Tri
+    and MoE0 up to three hops out.  Every per-atom step is the oracle's own
+    step function on a subset of atoms; MoE layers act atom by atom, and the
+    Tri and attention rows are per receiver, so subsets give the same rows.
     """
 
     def __init__(self, inp: Dict[str, np.ndarray], use_tree: Optional[bool] = None):
         super().__init__(inp, use_tree)
         from . import attention as A
+        from . import tri as TR
         self.A = A
+        self.TR = TR
         k = int(inp["top_k"])
         self.topk0, self.gate0 = B.route(inp["logits0"], k)
         self.nh = int(inp["n_heads"])
@@ -203,16 +206,45 @@ class LocalFullBlock(LocalBlock):
         self.W_o = np.asarray(inp["W_o"], f64)
         self.Da = self.W_o.shape[0]
         self.dh = self.Da // self.nh
+        self.has_tri = "W_ang" in inp
+        if self.has_tri:
+            self.W_s = np.asarray(inp["W_s"], f64)
+            self.W_ang = np.asarray(inp["W_ang"], f64)
+            self.W_T = np.asarray(inp["W_T"], f64)
+        self._hT: Dict[int, np.ndarray] = {}
         self._h0: Dict[int, np.ndarray] = {}
         self._att: Dict[int, Dict] = {}
+
+    # ---------------------------------------------------------------- Tri ---
+    def _unit_row(self, rw):
+        r = rw["r"]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            return np.where(r[:, None] > 0, rw["d"] / r[:, None], 0.0)
+
+    def s_tri(self, atoms) -> np.ndarray:
+        return np.asarray(self.inp["h"][np.asarray(atoms, np.int64)], f64) @ self.W_s
+
+    def hT(self, atoms) -> np.ndarray:
+        atoms = [int(a) for a in atoms]
+        for a in atoms:
+            if a in self._hT:
+                continue
+            h = np.asarray(self.inp["h"][a], f64)
+            if self.has_tri:
+                rw = self.row(a)
+                tau = self.TR.tri_row(self._unit_row(rw), B.envelope(rw["r"], self.rc),
+                                      self.s_tri(rw["other"]), self.W_ang)
+                h = h + tau @ self.W_T
+            self._hT[a] = h
+        return np.stack([self._hT[a] for a in atoms])
 
     def h0(self, atoms) -> np.ndarray:
         atoms = [int(a) for a in atoms]
         todo = sorted(set(a for a in atoms if a not in self._h0))
         if todo:
             t = np.asarray(todo, np.int64)
-            h = np.asarray(self.inp["h"][t], f64)
-            out = B.moe_forward(h, self.z[t], self.topk0, self.gate0, self.inp["W1_0"], self.inp["W2_0"])
+            out = B.moe_forward(self.hT(todo), self.z[t], self.topk0, self.gate0,
+                                self.inp["W1_0"], self.inp["W2_0"])
             for n, a in enumerate(todo):
                 self._h0[a] = out[n]
         return np.stack([self._h0[a] for a in atoms]) if atoms else np.zeros((0, self.W_qkv.shape[0]))
@@ -248,23 +280,27 @@ class LocalFullBlock(LocalBlock):
         eps = h2 @ np.asarray(self.inp["w_r"], f64)
         return dict(u=u, h2=h2, eps=eps)
 
+    def _nbrs(self, atoms):
+        out = set(int(a) for a in atoms)
+        for a in atoms:
+            out.update(int(j) for j in self.row(int(a))["other"])
+        return sorted(out)
+
     def vjp(self, atoms: Iterable[int], g_all: np.ndarray) -> Dict[str, np.ndarray]:
         """grad_h, grad_pos and the per-atom virial at the sampled atoms."""
         atoms = [int(i) for i in atoms]
-        J = set(atoms)
-        for i in atoms:
-            J.update(int(j) for j in self.row(i)["other"])
-        J = sorted(J)
-        Jarr = np.asarray(J, np.int64)
-        u = np.stack([self.att_row(j)["u"] for j in J])
-        ubar = B.moe_vjp(u, np.asarray(g_all[Jarr], f64), self.z[Jarr], self.topk, self.gate,
+        J1 = self._nbrs(atoms)          # rows whose edge gradients reach the samples
+        J2 = self._nbrs(J1)             # rows whose attention terms reach J1
+        J2arr = np.asarray(J2, np.int64)
+        u = np.stack([self.att_row(j)["u"] for j in J2])
+        ubar = B.moe_vjp(u, np.asarray(g_all[J2arr], f64), self.z[J2arr], self.topk, self.gate,
                          self.inp["W1"], self.inp["W2"])
-        ub = {j: ubar[n] for n, j in enumerate(J)}
+        ub = {j: ubar[n] for n, j in enumerate(J2)}
         ht = self.A.heads_of(self.Da, self.nh)
         sq = 1.0 / np.sqrt(self.dh)
         Wa_e = self.inp["Wa_e"]
         rowq = {}
-        for j in J:            # receiver-side quantities of every row touching the samples
+        for j in J2:           # attention receiver-side quantities
             a = self.att_row(j)
             rw = self.row(j)
             ob = ub[j] @ self.W_o.T
@@ -279,31 +315,51 @@ class LocalFullBlock(LocalBlock):
                  + fbar * B.envelope_dr(rw["r"], self.rc))
             key = {(int(o), int(s[0]), int(s[1]), int(s[2])): n
                    for n, (o, s) in enumerate(zip(rw["other"], rw["shift"]))}
-            rowq[j] = dict(ob=ob, gbar=gbar, c=c, key=key)
+            rowq[j] = dict(ob=ob, gbar=gbar, c=c, key=key, gvec=c[:, None] * self._unit_row(rw))
+        Da = self.Da
+        h0bar = {}
+        for m in J1:            # dL/dh0 through the residual, q, k and v
+            a, rw, qm = self.att_row(m), self.row(m), rowq[m]
+            qbar = (qm["gbar"][:, ht] * a["k"] * a["e"]).sum(axis=0) * sq if rw["r"].size else np.zeros(Da)
+            kbar = np.zeros(Da)
+            vbar = np.zeros(Da)
+            for n, (j, S) in enumerate(zip(rw["other"], rw["shift"])):
+                j = int(j)
+                rj, aj = rowq[j], self.att_row(j)
+                r_idx = rj["key"][(m, -int(S[0]), -int(S[1]), -int(S[2]))]
+                kbar += rj["gbar"][r_idx][ht] * aj["q"] * a["e"][n] * sq
+                vbar += aj["alpha"][r_idx][ht] * rj["ob"] * a["e"][n]
+            h0bar[m] = ub[m] + np.concatenate([qbar, kbar, vbar]) @ self.W_qkv.T
+        J1arr = np.asarray(J1, np.int64)
+        hTb = B.moe_vjp(self.hT(J1), np.stack([h0bar[m] for m in J1]), self.z[J1arr],
+                        self.topk0, self.gate0, self.inp["W1_0"], self.inp["W2_0"])
+        hT_bar = {m: hTb[n] for n, m in enumerate(J1)}
+        sbar_tri = {}
+        if self.has_tri:        # Tri rows of J1: sender gradients and edge vectors
+            for m in J1:
+                rw = self.row(m)
+                r = rw["r"]
+                sb, gv = self.TR.tri_row_vjp(self._unit_row(rw), r, B.envelope(r, self.rc),
+                                             B.envelope_dr(r, self.rc), self.s_tri(rw["other"]),
+                                             self.W_ang, hT_bar[m] @ self.W_T.T)
+                rowq[m]["gvec"] = rowq[m]["gvec"] + gv
+                for n, j in enumerate(rw["other"]):
+                    sbar_tri[int(j)] = sbar_tri.get(int(j), 0.0) + sb[n]
         Dn = self.W_o.shape[1]
         grad_h = np.zeros((len(atoms), Dn), f64)
         grad_pos = np.zeros((len(atoms), 3), f64)
         virial = np.zeros((len(atoms), 3, 3), f64)
         for n, i in enumerate(atoms):
-            a, rw, qi_ = self.att_row(i), self.row(i), rowq[i]
-            Da = self.Da
-            qbar = (qi_["gbar"][:, ht] * a["k"] * a["e"]).sum(axis=0) * sq if rw["r"].size else np.zeros(Da)
-            kbar = np.zeros(Da)
-            vbar = np.zeros(Da)
+            rw, ri = self.row(i), rowq[i]
             for m, (j, S) in enumerate(zip(rw["other"], rw["shift"])):
-                j = int(j)
-                rj, aj = rowq[j], self.att_row(j)
+                rj = rowq[int(j)]
                 r_idx = rj["key"][(i, -int(S[0]), -int(S[1]), -int(S[2]))]
-                e_m = a["e"][m]
-                kbar += rj["gbar"][r_idx][ht] * aj["q"] * e_m * sq
-                vbar += aj["alpha"][r_idx][ht] * rj["ob"] * e_m
-                cc = qi_["c"][m] + rj["c"][r_idx]
-                rr = rw["r"][m]
-                dhat = rw["d"][m] / rr if rr > 0 else np.zeros(3)
-                grad_pos[n] -= cc * dhat
-                virial[n] += 0.5 * cc * np.outer(dhat, rw["d"][m])
-            h0bar = ub[i] + np.concatenate([qbar, kbar, vbar]) @ self.W_qkv.T
-            grad_h[n] = B.moe_vjp(np.asarray(self.inp["h"][[i]], f64), h0bar[None, :],
-                                  self.z[[i]], self.topk0, self.gate0,
-                                  self.inp["W1_0"], self.inp["W2_0"])[0]
+                g = ri["gvec"][m] - rj["gvec"][r_idx]       # d_rev = -d
+                grad_pos[n] -= g
+                t = np.outer(g, rw["d"][m])
+                virial[n] += 0.25 * (t + t.T)
+            gh = hT_bar[i]
+            if self.has_tri and i in sbar_tri:
+                gh = gh + sbar_tri[i] @ self.W_s.T
+            grad_h[n] = gh
         return dict(grad_h=grad_h, grad_pos=grad_pos, atom_virial=B.voigt(virial))

@@ -114,7 +114,26 @@ def test_attention_and_moe_vjp_reject_bad_args(mlip):
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
+def test_tri_rejects_bad_args(mlip):
+    L = mlip._lib
+    f = C.c_void_p(256)
+
+    def tri(n_ang=4, d_tri=32, cutoff=5.0):
+        return L.mlip_tri(f, f, f, 10, 20, f, f, f, f, n_ang, 64, d_tri, cutoff, f, f, f, None)
+    assert "n_ang" in _err(mlip, tri(n_ang=3), mlip.MLIP_ERR_INVALID)
+    assert "d_tri" in _err(mlip, tri(d_tri=30), mlip.MLIP_ERR_INVALID)
+    assert "too wide" in _err(mlip, tri(d_tri=516), mlip.MLIP_ERR_UNSUPPORTED)
+
+    def vjp(accumulate, atom_virial, grad_strain, ws_bytes=1 << 30):
+        return L.mlip_tri_vjp(f, f, f, f, 10, 20, f, f, f, f, 4, 64, 32, 5.0, f, f, f, f, 1,
+                              atom_virial, grad_strain, accumulate, f, ws_bytes, None)
+    assert "accumulated atom_virial" in _err(mlip, vjp(1, None, f), mlip.MLIP_ERR_INVALID)
+    assert "workspace" in _err(mlip, vjp(0, f, f, 16), mlip.MLIP_ERR_INVALID)
+    assert L.mlip_tri_vjp_workspace_size(4096, 200000, 384) >= 200000 * (384 + 4) * 4
+
+
 def test_profile_api_without_gpu(mlip):
     names = list(mlip.profile_read())
     assert "gemm_expert_up" in names and "edge_vjp" in names and "attn_fwd" in names
-    assert len(names) == 14
+    assert "tri_fwd" in names and "tri_vjp_send" in names
+    assert len(names) == 17

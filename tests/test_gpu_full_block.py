@@ -1,6 +1,6 @@
-"""GPU parity of the complete interaction block (MoE0 -> neighbour attention
--> MoE1 -> readout, and its input gradient) against the CPU oracle
-(``oracle.attention``), through the C ABI.
+"""GPU parity of the complete interaction block (Tri -> MoE0 -> neighbour
+attention -> MoE1 -> readout, and its input gradient) against the CPU oracle
+(``oracle.attention`` with ``oracle.tri``), through the C ABI.
 
 Integer outputs (MoE0 routing and dispatch tables) must match bit for bit;
 floating-point tensors must satisfy max|gpu - oracle| / max|oracle| <= 2e-4.
@@ -90,6 +90,10 @@ def test_full_block_matches_oracle(mlip, name, upstream, q_scale):
     assert np.array_equal(blk.moe0["slot"].cpu().numpy(), slot)
     att = f["att"]
     N = cfg.n_atoms
+    tri_errs = {}
+    if f["tri"] is not None:
+        tri_errs = {"tau": rel(blk.tri["tau"], f["tri"]["tau"]), "h_T": rel(blk.tri["h_T"], f["tri"]["hT"]),
+                    "grad_hT": rel(blk.grad_hT, v["grad_hT"])}
     deg = np.diff(g["row_ptr"])
     has = deg > 0
     stats = blk.att["stats"].cpu().numpy().astype(np.float64)
@@ -114,6 +118,7 @@ def test_full_block_matches_oracle(mlip, name, upstream, q_scale):
     m_ref = np.stack([att["s"][g["row_ptr"][i]:g["row_ptr"][i + 1]].max(axis=0)
                       for i in np.nonzero(has)[0]]) if has.any() else np.zeros((0, cfg.n_heads))
     errs["max_score"] = float(np.max(np.abs(m_gpu - m_ref))) if m_ref.size else 0.0
+    errs.update(tri_errs)
     _say(f"{name}: errors {errs}")
     bad = {k: e for k, e in errs.items() if not e <= TOL}
     assert not bad, bad
