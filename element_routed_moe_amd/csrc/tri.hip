@@ -19,10 +19,11 @@
 // computed once per edge and broadcast from LDS.  Gradient (taubar = dL/dtau):
 //   Abar_lm,c = 2 taubar_c W_ang[l,c] A_lm,c,   Bbar_c = -taubar_c sum_l W_ang[l,c];
 //   receiver pass (row i): sigma_e,c = sum_lm Abar_lm,c f_e S_lm(dhat_e) + 2 Bbar_c f_e^2 s_j,c
-//     is stored per edge (it is dL/ds_j(e) from this row); with one lane per
-//     edge, P_lm = sum_c Abar_lm,c s_j,c gives dL/dS_lm = f_e P_lm and
-//     dL/df_e = sum_lm S_lm P_lm + 2 f_e sum_c Bbar_c s_j,c^2, hence the edge
-//     vector dL/dd_e = dL/df_e f_c'(r) dhat + (I - dhat dhat^T) sum_lm dL/dS_lm grad S_lm / r.
+//     is stored per edge (it is dL/ds_j(e) from this row); in the same
+//     channel loop P_lm = sum_c Abar_lm,c s_j,c and Q = sum_c Bbar_c s_j,c^2
+//     are summed over the lanes, and then, one lane per edge,
+//     dL/dS_lm = f_e P_lm and dL/df_e = sum_lm S_lm P_lm + 2 f_e Q give the
+//     edge vector dL/dd_e = dL/df_e f_c'(r) dhat + (I - dhat dhat^T) sum_lm dL/dS_lm grad S_lm / r.
 //   sender pass (row j, edges j <- i): sbar_j = sum of sigma over the reverse
 //     edges; forces and virial from dL/dd_e - dL/dd_rev(e).
 // No atomics anywhere.
@@ -220,6 +221,34 @@ __global__ void __launch_bounds__(64) tri_fwd_kernel(
   stc<CPL>(tau + int64_t(i) * Dt + c0, t);
 }
 
+// Sums 16 per-lane values over the wavefront in 17 shuffles: at each step a
+// lane keeps half of its values and adds the partner's copy of them.
+// Afterwards lane l holds the total of value l >> 2.
+__device__ inline float reduce16(const float (&v)[NSH]) {
+  const int lane = threadIdx.x & 63;
+  float a8[8], a4[4], a2[2];
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    a8[q] = (b5 ? v[q + 8] : v[q]) + __shfl_xor(b5 ? v[q] : v[q + 8], 32, 64);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    a4[q] = (b4 ? a8[q + 4] : a8[q]) + __shfl_xor(b4 ? a8[q] : a8[q + 4], 16, 64);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    a2[q] = (b3 ? a4[q + 2] : a4[q]) + __shfl_xor(b3 ? a4[q] : a4[q + 2], 8, 64);
+  float a1 = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4, 64);
+  a1 += __shfl_xor(a1, 2, 64);
+  a1 += __shfl_xor(a1, 1, 64);
+  return a1;
+}
+
+__device__ inline float wave_total(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
 // ------------------------------------------------ gradient: receiver rows --
 template <int CPL>
 __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
@@ -227,12 +256,12 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ s,
     const float *__restrict__ W_ang, const float *__restrict__ taubar, int Dt, float rc,
     float *__restrict__ sigma, float4 *__restrict__ gvec) {
-  extern __shared__ float dyn[];           // Abar [NSH][Dt], then Bbar [Dt]
-  __shared__ float ysh[CHUNK][NSH];
-  __shared__ float fsq[CHUNK];
+  __shared__ float ysh[CHUNK][NSH];     // f_e S_lm(dhat_e)
+  __shared__ float shv[CHUNK][NSH];     // S_lm(dhat_e)
+  __shared__ float pq[CHUNK][NSH + 1];  // sum_c Abar_lm,c s_j,c and sum_c Bbar_c s_j,c^2
+  __shared__ float4 geo[CHUNK];         // (dhat, 1/r)
+  __shared__ float fcs[CHUNK], dfcs[CHUNK], fsq[CHUNK];
   __shared__ int jj[CHUNK];
-  float *abar_s = dyn;
-  float *bbar_s = dyn + NSH * Dt;
   const int lane = threadIdx.x;
   const int64_t blk = xcd_block(n_atoms);
   if (blk < 0) return;
@@ -244,7 +273,7 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
   float A[NSH][CPL], Bs[CPL];
   accumulate_row<CPL>(src, geom, s, Dt, c0, r0, r1, R, ysh, fsq, jj, A, Bs);
 
-  // Abar, Bbar for this row (registers for the channel pass, LDS for the edge pass)
+  // Abar and Bbar of this row, in place of A and B (zero on idle lanes)
   {
     float w[NANG][CPL], tb[CPL];
 #pragma unroll
@@ -255,88 +284,83 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
       float wsum = 0.f;
 #pragma unroll
       for (int l = 0; l < NANG; ++l) wsum += w[l][c];
-      Bs[c] = active ? -tb[c] * wsum : 0.f;           // Bs now holds Bbar
+      Bs[c] = active ? -tb[c] * wsum : 0.f;
 #pragma unroll
       for (int lm = 0; lm < NSH; ++lm) A[lm][c] = active ? 2.f * tb[c] * w[l_of(lm)][c] * A[lm][c] : 0.f;
     }
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-#pragma unroll
-        for (int lm = 0; lm < NSH; ++lm) abar_s[lm * Dt + c0 + c] = A[lm][c];
-        bbar_s[c0 + c] = Bs[c];
-      }
-    }
   }
-  __syncthreads();
 
   for (int e0 = r0; e0 < r1; e0 += CHUNK) {
     const int n = min(CHUNK, r1 - e0);
-    EdgeGeo G = {0.f, 0.f, 0.f, make_float3(0.f, 0.f, 0.f)};
-    float S[NSH] = {};
-    int jmine = 0;
     if (lane < n) {
-      G = edge_geo(geom[e0 + lane], R);
+      const EdgeGeo G = edge_geo(geom[e0 + lane], R);
+      float S[NSH];
       harmonics(G.u.x, G.u.y, G.u.z, S);
 #pragma unroll
-      for (int lm = 0; lm < NSH; ++lm) ysh[lane][lm] = G.fc * S[lm];
+      for (int lm = 0; lm < NSH; ++lm) {
+        ysh[lane][lm] = G.fc * S[lm];
+        shv[lane][lm] = S[lm];
+      }
+      geo[lane] = make_float4(G.u.x, G.u.y, G.u.z, G.inv_r);
+      fcs[lane] = G.fc;
+      dfcs[lane] = G.dfc;
       fsq[lane] = G.fc * G.fc;
-      jmine = src[e0 + lane];
-      jj[lane] = jmine;
+      jj[lane] = src[e0 + lane];
     }
     __syncthreads();
-    // channel pass: sigma_e = sum_lm Abar_lm f S_lm + 2 Bbar f^2 s_j  (coalesced rows)
+    // channel pass: sigma_e rows, and the channel sums P_lm, Q of every edge
     for (int mm = 0; mm < n; mm += UNROLL) {
       float sj[UNROLL][CPL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) ldc<CPL>(s + int64_t(jj[min(mm + u, n - 1)]) * Dt + c0, sj[u]);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        if (mm + u < n && active) {
+        if (mm + u < n) {
           const int me = mm + u;
-          float out[CPL];
+          float out[CPL], P[NSH], Q = 0.f;
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) out[c] = 2.f * Bs[c] * fsq[me] * sj[u][c];
+          for (int c = 0; c < CPL; ++c) {
+            out[c] = 2.f * Bs[c] * fsq[me] * sj[u][c];
+            Q += Bs[c] * sj[u][c] * sj[u][c];
+          }
 #pragma unroll
           for (int lm = 0; lm < NSH; ++lm) {
             const float y = ysh[me][lm];
+            float p = 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) out[c] += A[lm][c] * y;
+            for (int c = 0; c < CPL; ++c) {
+              out[c] += A[lm][c] * y;
+              p += A[lm][c] * sj[u][c];
+            }
+            P[lm] = p;
           }
-          stc<CPL>(sigma + int64_t(e0 + me) * Dt + c0, out);
+          if (active) stc<CPL>(sigma + int64_t(e0 + me) * Dt + c0, out);
+          const float ptot = reduce16(P);
+          const float qtot = wave_total(Q);
+          if ((lane & 3) == 0) pq[me][lane >> 2] = ptot;
+          if (lane == 0) pq[me][NSH] = qtot;
         }
       }
     }
-    // edge pass: lane = edge; P_lm = sum_c Abar_lm,c s_j,c and Q = sum_c Bbar_c s_j,c^2
+    __syncthreads();
+    // edge pass: dL/dS_lm = f P_lm, dL/df = sum_lm S_lm P_lm + 2 f Q, then the edge vector
     if (lane < n) {
-      float P[NSH];
-#pragma unroll
-      for (int lm = 0; lm < NSH; ++lm) P[lm] = 0.f;
-      float Q = 0.f;
-      const float *srow = s + int64_t(jmine) * Dt;
-      for (int c = 0; c < Dt; c += 4) {          // Dt is a multiple of 4
-        const float4 v = *reinterpret_cast<const float4 *>(srow + c);
-        const float sv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Q += bbar_s[c + q] * sv[q] * sv[q];
-#pragma unroll
-          for (int lm = 0; lm < NSH; ++lm) P[lm] += abar_s[lm * Dt + c + q] * sv[q];
-        }
-      }
-      float fbar = 2.f * G.fc * Q;
+      const float fc = fcs[lane];
+      float fbar = 2.f * fc * pq[lane][NSH];
       float sbar_lm[NSH];
 #pragma unroll
       for (int lm = 0; lm < NSH; ++lm) {
-        fbar += S[lm] * P[lm];
-        sbar_lm[lm] = G.fc * P[lm];
+        const float p = pq[lane][lm];
+        fbar += shv[lane][lm] * p;
+        sbar_lm[lm] = fc * p;
       }
-      const float3 gu = harmonics_grad(G.u.x, G.u.y, G.u.z, sbar_lm);
-      const float rad = gu.x * G.u.x + gu.y * G.u.y + gu.z * G.u.z;
-      const float a = fbar * G.dfc;
-      gvec[e0 + lane] = make_float4(a * G.u.x + (gu.x - rad * G.u.x) * G.inv_r,
-                                    a * G.u.y + (gu.y - rad * G.u.y) * G.inv_r,
-                                    a * G.u.z + (gu.z - rad * G.u.z) * G.inv_r, 0.f);
+      const float4 g = geo[lane];
+      const float3 gu = harmonics_grad(g.x, g.y, g.z, sbar_lm);
+      const float rad = gu.x * g.x + gu.y * g.y + gu.z * g.z;
+      const float a = fbar * dfcs[lane];
+      gvec[e0 + lane] = make_float4(a * g.x + (gu.x - rad * g.x) * g.w,
+                                    a * g.y + (gu.y - rad * g.y) * g.w,
+                                    a * g.z + (gu.z - rad * g.z) * g.w, 0.f);
     }
     __syncthreads();
   }
@@ -422,8 +446,7 @@ int launch_cpl(int which, const TriArgs &a, hipStream_t stream) {
     tri_fwd_kernel<CPL><<<grid, block, 0, stream>>>(a.row_ptr, a.src, g4, a.n_atoms, a.s, a.W_ang,
                                                     a.Dt, a.rc, a.tau);
   } else if (which == 1) {
-    const size_t dyn = size_t(NSH + 1) * a.Dt * sizeof(float);
-    tri_vjp_recv_kernel<CPL><<<grid, block, dyn, stream>>>(
+    tri_vjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(
         a.row_ptr, a.src, g4, a.n_atoms, a.s, a.W_ang, a.taubar, a.Dt, a.rc, a.sigma,
         reinterpret_cast<float4 *>(a.gvec));
   } else {
