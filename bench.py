@@ -10,8 +10,11 @@ HBM before the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S] [--block core|full]
 
-``--block full`` times the complete block instead (MoE0 -> neighbour
-multi-head attention -> MoE1 -> readout, and its input gradient).
+``--block full`` times the complete block instead (Tri -> MoE0 -> neighbour
+multi-head attention -> MoE1 -> readout, and its input gradient);
+``--block stack`` times a model of ``--blocks`` complete blocks on one graph
+(element embedding, the blocks, readout, forces and stress through all of
+them), with the block weights drawn on the GPU from a seeded generator.
 
 Prints ONE JSON line.  ``--calibrate-copy`` instead runs a plain 1 GiB device
 copy (for scaling hardware byte counters).
@@ -108,7 +111,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="S")
-    ap.add_argument("--block", choices=("core", "full"), default="core")
+    ap.add_argument("--block", choices=("core", "full", "stack"), default="core")
+    ap.add_argument("--blocks", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-structs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -131,8 +135,15 @@ def main():
 
     cfg = synth.CONFIGS[args.config]
     full = args.block == "full"
-    inputs = synth.make_full_inputs(cfg) if full else synth.make_inputs(cfg)
-    blk = (mlip.FullBlock if full else mlip.Block)(inputs, device="cuda")
+    stack = args.block == "stack"
+    if stack:
+        shared, _ = synth.make_stack_inputs(cfg, 0)
+        params = synth.device_stack_params(cfg, args.blocks, "cuda")
+        blk = mlip.Stack(shared, params, device="cuda")
+        inputs = shared
+    else:
+        inputs = synth.make_full_inputs(cfg) if full else synth.make_inputs(cfg)
+        blk = (mlip.FullBlock if full else mlip.Block)(inputs, device="cuda")
     log(f"inputs resident for workload {cfg.name}: {cfg.n_atoms} atoms")
     for _ in range(args.warmup):
         blk.step()
@@ -181,7 +192,8 @@ def main():
                    "cutoff": cfg.cutoff, "d_edge": cfg.d_edge, "d_node": cfg.d_node,
                    "d_hidden": cfg.d_hidden, "experts": cfg.n_experts, "top_k": k,
                    "element_types": cfg.n_types,
-                   "block": ("MoE0 + neighbour attention + MoE1" if full
+                   "block": ("Tri + MoE0 + neighbour attention + MoE1" if full else
+                             f"{args.blocks} x (Tri + MoE0 + neighbour attention + MoE1)" if stack
                              else "aggregation + MoE")},
         "edges_per_s": round(E * args.steps / wall, 1),
         "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
@@ -189,9 +201,13 @@ def main():
         "roofline": roof,
     }
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
-    if full:
+    if full or stack:
         out["config"]["heads"] = cfg.n_heads
         out["config"]["d_attn"] = cfg.d_attn
+    if stack:
+        # the float64 oracle of a whole stack at these widths is out of reach of
+        # a bounded CPU sample; the per-block baseline is in the --block full line
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, min(args.cpu_structs, cfg.n_structs), full)
     print(json.dumps(out))

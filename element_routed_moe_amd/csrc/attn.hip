@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
     const int32_t *__restrict__ rev, const float4 *__restrict__ geom, int n_atoms,
     const float *__restrict__ Wa_e, const float *__restrict__ qkv, const float *__restrict__ obar,
     const float *__restrict__ edge_g, const float *__restrict__ edge_a,
-    const float *__restrict__ edge_c, int Da, int nh, int lph, float rc,
+    const float *__restrict__ edge_c, int Da, int nh, int lph, float rc, int accumulate,
     float *__restrict__ qkv_bar, float *__restrict__ grad_pos, float *__restrict__ atom_virial) {
   __shared__ float4 phi[CHUNK][KQ];
   __shared__ int jj[CHUNK], rr[CHUNK];
@@ -445,11 +445,13 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
 #pragma unroll
   for (int qv = 0; qv < 6; ++qv) vir[qv] = wave_sum(vir[qv]);
   if (lane == 0) {
-    grad_pos[int64_t(j) * 3 + 0] = -fx;
-    grad_pos[int64_t(j) * 3 + 1] = -fy;
-    grad_pos[int64_t(j) * 3 + 2] = -fz;
+    float *gp = grad_pos + int64_t(j) * 3;
+    float *av = atom_virial + int64_t(j) * 6;
+    const float g3[3] = {-fx, -fy, -fz};
 #pragma unroll
-    for (int qv = 0; qv < 6; ++qv) atom_virial[int64_t(j) * 6 + qv] = 0.5f * vir[qv];
+    for (int q = 0; q < 3; ++q) gp[q] = accumulate ? gp[q] + g3[q] : g3[q];
+#pragma unroll
+    for (int qv = 0; qv < 6; ++qv) av[qv] = accumulate ? av[qv] + 0.5f * vir[qv] : 0.5f * vir[qv];
   }
 }
 
@@ -469,7 +471,7 @@ int launch_all(int which, const AttnArgs &a, hipStream_t stream) {
   } else {
     attn_vjp_send_kernel<CPL><<<grid, block, 0, stream>>>(
         a.row_ptr, a.src, a.rev, g4, a.n_atoms, a.Wa_e, a.qkv, a.obar, a.edge_g, a.edge_a,
-        a.edge_c, a.Da, a.nh, a.lph, a.rc, a.qkv_bar, a.grad_pos, a.atom_virial);
+        a.edge_c, a.Da, a.nh, a.lph, a.rc, a.accumulate, a.qkv_bar, a.grad_pos, a.atom_virial);
   }
   MLIP_LAUNCHED();
   return MLIP_OK;

@@ -25,6 +25,8 @@ int moe_combine(const float *base, const float *rows, const int32_t *z, const fl
                 const int32_t *slot, int N, int T, int k, int D, float *out, hipStream_t stream);
 int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, int B, int D,
             float *eps, double *energy, hipStream_t stream);
+int embed_atoms(const int32_t *z, const float *table, int N, int T, int D, float *h,
+                hipStream_t stream);
 
 namespace {
 
@@ -462,13 +464,15 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                        const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                        int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
                        float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                       float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
-                       void *stream_) {
+                       float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
+                       size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
   int cpl = 0, lph = 0;
   if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
+  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain,
+                 "accumulating into grad_strain needs the accumulated atom_virial");
   MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o, "null pointer argument");
   MLIP_CHECK_ARG(n_atoms == 0 || (qkv && o && stats && grad_u && grad_h0 && grad_pos),
                  "null pointer argument");
@@ -497,7 +501,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   a.Wa_e = Wa_e; a.qkv = qkv; a.o = const_cast<float *>(o);
   a.stats = const_cast<float *>(stats); a.obar = w.obar; a.qkv_bar = w.qkv_bar;
   a.edge_g = w.edge_g; a.edge_a = w.edge_a; a.edge_c = w.edge_c;
-  a.grad_pos = grad_pos; a.atom_virial = vir;
+  a.grad_pos = grad_pos; a.atom_virial = vir; a.accumulate = accumulate ? 1 : 0;
   a.Da = d_attn; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
   if (int rc = launch_attn_vjp(a, stream)) return rc;
   if (grad_strain) {
@@ -607,6 +611,19 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   g2.A = w.sbar; g2.lda = d_tri; g2.B = W_s; g2.ldb = d_tri; g2.C = grad_h; g2.ldc = d_node;
   g2.R = grad_hT; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_tri;
   return launch_gemm(g2, true, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+// ------------------------------------------------------ atom embedding ----
+int mlip_embed_atoms(const int32_t *z, const float *table, int32_t n_atoms, int32_t n_types,
+                     int32_t d_node, float *h, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(table && (n_atoms == 0 || (z && h)), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(table, 16) && aligned(h, 16), "float arrays must be 16-byte aligned");
+  if (n_atoms == 0) return MLIP_OK;
+  return embed_atoms(z, table, n_atoms, n_types, d_node, h, stream);
 }
 
 }  // extern "C"

@@ -170,6 +170,7 @@ struct AttnArgs {
   float *edge_c = nullptr;       // [E]
   float *grad_pos = nullptr;     // [N][3]
   float *atom_virial = nullptr;  // [N][6]
+  int accumulate = 0;            // add to grad_pos / atom_virial instead of writing
   int Da = 0, nh = 0, cpl = 0, lph = 0;
   float rc = 0.f;
 };

@@ -268,6 +268,26 @@ int moe_combine(const float *base, const float *rows, const int32_t *z, const fl
   return MLIP_OK;
 }
 
+// h[i] = table[z[i]] (float4 columns; rows of an out-of-range type are zero).
+__global__ void __launch_bounds__(256) embed_atoms_kernel(const int32_t *__restrict__ z,
+                                                          const float4 *__restrict__ table, int N, int T,
+                                                          int D4, float4 *__restrict__ h) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(N) * D4) return;
+  const int i = int(idx / D4), c = int(idx - int64_t(i) * D4);
+  const int t = z[i];
+  h[idx] = (t >= 0 && t < T) ? table[int64_t(t) * D4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+int embed_atoms(const int32_t *z, const float *table, int N, int T, int D, float *h,
+                hipStream_t stream) {
+  const int D4 = D / 4;
+  embed_atoms_kernel<<<dim3(unsigned(cdiv(int64_t(N) * D4, 256))), dim3(256), 0, stream>>>(
+      z, reinterpret_cast<const float4 *>(table), N, T, D4, reinterpret_cast<float4 *>(h));
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, int B, int D,
             float *eps, double *energy, hipStream_t stream) {
   ProfScope ps(K_READOUT, stream);

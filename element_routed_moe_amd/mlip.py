@@ -64,8 +64,9 @@ _SIGS = {
                                  _f32, _p, _p, _p, _p, _p]),
     "mlip_attention_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32]),
     "mlip_attention_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32,
-                                     _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _p,
-                                     _sz, _p]),
+                                     _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _i32,
+                                     _p, _sz, _p]),
+    "mlip_embed_atoms": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
     "mlip_tri": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
                            _p, _p]),
     "mlip_tri_vjp_workspace_size": (_sz, [_i32, _i64, _i32]),
@@ -265,7 +266,8 @@ def mlip_attention(graph, h0, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float,
 
 def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float, grad_u,
                        struct_ptr=None, out: Optional[Dict] = None,
-                       ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                       ws: Optional[torch.Tensor] = None,
+                       accumulate: bool = False) -> Dict[str, torch.Tensor]:
     N, Dn = int(grad_u.shape[0]), int(grad_u.shape[1])
     Da = int(W_o.shape[0])
     E = int(graph["n_edges"])
@@ -286,7 +288,17 @@ def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float
                                    int(Wa_e.shape[0]), Dn, Da, int(n_heads), float(cutoff),
                                    _ptr(grad_u), _ptr(out["grad_h0"]), _ptr(out["grad_pos"]),
                                    _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
-                                   _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))
+                                   _ptr(out.get("grad_strain")), 1 if accumulate else 0, _ptr(ws),
+                                   ws.numel(), _stream()))
+    return out
+
+
+def mlip_embed_atoms(z, table, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    N = int(z.shape[0])
+    T, Dn = int(table.shape[0]), int(table.shape[1])
+    if out is None:
+        out = torch.empty((N, Dn), dtype=torch.float32, device=table.device)
+    _check(_lib.mlip_embed_atoms(_ptr(z), _ptr(table), N, T, Dn, _ptr(out), _stream()))
     return out
 
 
@@ -413,46 +425,49 @@ class FullBlock:
     """The complete interaction block: Tri -> MoE0 -> neighbour attention -> MoE1.
 
     ``step()`` runs on the current stream: radius graph, the three-body update
-    (when the inputs carry its weights), MoE0, attention, MoE1, readout, then
+    (when the parameters include it), MoE0, attention, MoE1, readout, then
     the input gradient back through MoE1, the attention, MoE0 and Tri
     (forces and virial of both geometric operators) for the given upstream
-    gradient dL/dh'.
+    gradient dL/dh'.  ``forward`` / ``backward`` run one block on a given
+    graph, as the layers of a ``Stack`` do.
     """
 
-    def __init__(self, inputs: Dict, device="cuda", grad_out=None):
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None, params: Optional[Dict] = None):
         def dev(x, dt=None):
             t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
             return t.to(device=device, dtype=dt or t.dtype).contiguous()
 
         self.device = device
         f32 = torch.float32
+        params = inputs if params is None else params
         self.pos = dev(inputs["pos"], f32)
         self.cell = dev(inputs["cell"], f32)
         self.struct_ptr = dev(inputs["struct_ptr"], torch.int32)
         self.z = dev(inputs["z"], torch.int32)
-        self.h = dev(inputs["h"], f32)
-        self.logits0 = dev(inputs["logits0"], f32)
-        self.W1_0 = dev(inputs["W1_0"], f32)
-        self.W2_0 = dev(inputs["W2_0"], f32)
-        self.W_qkv = dev(inputs["W_qkv"], f32)
-        self.Wa_e = dev(inputs["Wa_e"], f32)
-        self.W_o = dev(inputs["W_o"], f32)
-        self.logits = dev(inputs["logits"], f32)
-        self.W1 = dev(inputs["W1"], f32)
-        self.W2 = dev(inputs["W2"], f32)
+        self.h = dev(inputs["h"], f32) if "h" in inputs else None
+        self.logits0 = dev(params["logits0"], f32)
+        self.W1_0 = dev(params["W1_0"], f32)
+        self.W2_0 = dev(params["W2_0"], f32)
+        self.W_qkv = dev(params["W_qkv"], f32)
+        self.Wa_e = dev(params["Wa_e"], f32)
+        self.W_o = dev(params["W_o"], f32)
+        self.logits = dev(params["logits"], f32)
+        self.W1 = dev(params["W1"], f32)
+        self.W2 = dev(params["W2"], f32)
         self.w_r = dev(inputs["w_r"], f32)
         self.cutoff = float(inputs["cutoff"])
         self.top_k = int(inputs["top_k"])
         self.n_heads = int(inputs["n_heads"])
-        self.has_tri = "W_ang" in inputs
+        self.has_tri = "W_ang" in params
         if self.has_tri:
-            self.W_s = dev(inputs["W_s"], f32)
-            self.W_ang = dev(inputs["W_ang"], f32)
-            self.W_T = dev(inputs["W_T"], f32)
+            self.W_s = dev(params["W_s"], f32)
+            self.W_ang = dev(params["W_ang"], f32)
+            self.W_T = dev(params["W_T"], f32)
+        N = int(self.z.shape[0])
+        Dn = int(self.W_o.shape[1])
         if grad_out is None:
-            grad_out = self.w_r.expand(self.h.shape[0], -1)
+            grad_out = self.w_r.expand(N, -1)
         self.grad_out = dev(grad_out, f32)
-        N, Dn = self.h.shape
         H = self.W1.shape[2]
         T, X = self.logits.shape
         B = self.cell.shape[0]
@@ -465,15 +480,10 @@ class FullBlock:
         self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
         self.ubar = self.avjp = self.grad_hT = self.grad_h = None
 
-    def step(self):
-        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
-                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
-        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
-            self.edge_capacity = g["n_edges"]
-        self.graph = g
-        h = self.h
+    def forward(self, g, h):
+        """One block on graph g for input features h; returns h' (MoE1 output)."""
         if self.has_tri:
-            self.tri = mlip_tri(g, self.h, self.W_s, self.W_ang, self.W_T, self.cutoff, out=self.tri)
+            self.tri = mlip_tri(g, h, self.W_s, self.W_ang, self.W_T, self.cutoff, out=self.tri)
             h = self.tri["h_T"]
         self.moe0 = mlip_moe_forward(h, self.z, self.logits0, self.W1_0, self.W2_0, self.top_k,
                                      out=self.moe0, ws=self.ws_moe0)
@@ -481,12 +491,21 @@ class FullBlock:
                                   self.n_heads, self.cutoff, out=self.att)
         self.moe = mlip_moe_forward(self.att["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
                                     out=self.moe, ws=self.ws_moe1)
-        self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
-        self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, self.grad_out, out=self.ubar,
+        return self.moe["h_out"]
+
+    def backward(self, g, grad_out, forces: Optional[Dict] = None, accumulate: bool = False):
+        """Input gradient for grad_out = dL/dh'; forces (grad_pos, atom_virial,
+        grad_strain) are written, or added to the given buffers when accumulate."""
+        self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, grad_out, out=self.ubar,
                                  ws=self.ws_mvjp)
+        out = None
+        if forces is not None:
+            gh0 = self.avjp["grad_h0"] if self.avjp is not None else torch.empty_like(grad_out)
+            out = dict(forces, grad_h0=gh0)
         self.avjp = mlip_attention_vjp(g, self.att, self.W_qkv, self.Wa_e, self.W_o, self.n_heads,
                                        self.cutoff, self.ubar, struct_ptr=self.struct_ptr,
-                                       out=self.avjp, ws=self.ws_avjp)
+                                       out=out if out is not None else self.avjp, ws=self.ws_avjp,
+                                       accumulate=accumulate)
         self.ws_avjp = self.avjp["ws"]
         if self.has_tri:
             self.grad_hT = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
@@ -499,4 +518,69 @@ class FullBlock:
         else:
             self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
                                        out=self.grad_h, ws=self.ws_mvjp)
+        return self.grad_h
+
+    def step(self):
+        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
+                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
+        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
+            self.edge_capacity = g["n_edges"]
+        self.graph = g
+        h_out = self.forward(g, self.h)
+        self.ro = mlip_readout(h_out, self.w_r, self.struct_ptr, out=self.ro)
+        self.backward(g, self.grad_out)
+        return self
+
+
+class Stack:
+    """A model of several complete blocks on one radius graph.
+
+    ``step()``: radius graph; h^(0) = element embedding of z; the blocks in
+    order; readout of the last block; then the input gradient of the energy
+    (or of the given upstream gradient) back through every block, collecting
+    forces, per-atom virials and the strain gradient of all blocks.
+    Workspaces are shared between blocks (they run one after another).
+    """
+
+    def __init__(self, shared: Dict, blocks, device="cuda", grad_out=None):
+        f32 = torch.float32
+
+        def dev(x, dt=None):
+            t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
+            return t.to(device=device, dtype=dt or t.dtype).contiguous()
+
+        self.layers = [FullBlock(shared, device=device, params=p, grad_out=grad_out) for p in blocks]
+        first = self.layers[0]
+        for L in self.layers[1:]:        # one set of workspaces for all layers
+            L.ws_graph, L.ws_moe0, L.ws_moe1, L.ws_mvjp = (first.ws_graph, first.ws_moe0,
+                                                           first.ws_moe1, first.ws_mvjp)
+        self.emb = dev(shared["emb"], f32)
+        self.first = first
+        N = int(first.z.shape[0])
+        B = int(first.cell.shape[0])
+        self.forces = dict(grad_pos=torch.empty((N, 3), dtype=f32, device=device),
+                           atom_virial=torch.empty((N, 6), dtype=f32, device=device),
+                           grad_strain=torch.empty((B, 6), dtype=torch.float64, device=device))
+        self.graph = self.h0 = self.ro = self.grad_h0 = None
+        self.edge_capacity = None
+
+    def step(self):
+        L0 = self.first
+        g = mlip_build_graph(L0.pos, L0.cell, L0.struct_ptr, L0.cutoff,
+                             edge_capacity=self.edge_capacity, ws=L0.ws_graph)
+        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
+            self.edge_capacity = g["n_edges"]
+        self.graph = g
+        self.h0 = mlip_embed_atoms(L0.z, self.emb, out=self.h0)
+        h = self.h0
+        for L in self.layers:
+            h = L.forward(g, h)
+        self.ro = mlip_readout(h, L0.w_r, L0.struct_ptr, out=self.ro)
+        grad = L0.grad_out
+        for n, L in enumerate(reversed(self.layers)):
+            ws_a, ws_t = self.layers[-1].ws_avjp, self.layers[-1].ws_tvjp
+            if L is not self.layers[-1]:
+                L.ws_avjp, L.ws_tvjp = ws_a, ws_t      # share the per-edge workspaces
+            grad = L.backward(g, grad, forces=self.forces, accumulate=n > 0)
+        self.grad_h0 = grad
         return self

@@ -236,6 +236,83 @@ def make_full_inputs(cfg: BlockConfig, seed: Optional[int] = None) -> Dict[str, 
     return out
 
 
+N_BLOCKS = 6       # interaction blocks per model (Table II: 6 layers at every size)
+
+# Without any normalisation layer (the pages name none) a deep stack of
+# random-init residual blocks grows its features geometrically (the three-body
+# term is quadratic in them); the stack therefore draws the output weight of
+# every residual branch at RESID_SCALE times N(0, 1/fan_in), which keeps six
+# blocks at feature scale ~1.
+RESID_SCALE = 0.3
+
+_BLOCK_PARAM_SHAPES = (   # (name, shape(cfg), fan_in(cfg) or None for N(0, 1), extra scale), in draw order
+    ("logits0", lambda c: (c.n_types, c.n_experts), None, 1.0),
+    ("logits", lambda c: (c.n_types, c.n_experts), None, 1.0),
+    ("Wa_e", lambda c: (c.n_rbf, c.d_attn), lambda c: c.n_rbf, 1.0),
+    ("W_qkv", lambda c: (c.d_node, 3 * c.d_attn), lambda c: c.d_node, 1.0),
+    ("W_o", lambda c: (c.d_attn, c.d_node), lambda c: c.d_attn, RESID_SCALE),
+    ("W1_0", lambda c: (c.n_experts, c.d_node, c.d_hidden), lambda c: c.d_node, 1.0),
+    ("W2_0", lambda c: (c.n_experts, c.d_hidden, c.d_node), lambda c: c.d_hidden, RESID_SCALE),
+    ("W_s", lambda c: (c.d_node, c.d_attn), lambda c: c.d_node, 1.0),
+    ("W_ang", lambda c: (N_ANG, c.d_attn), lambda c: N_ANG * 2500.0, 1.0),
+    ("W_T", lambda c: (c.d_attn, c.d_node), lambda c: c.d_attn, RESID_SCALE),
+    ("W1", lambda c: (c.n_experts, c.d_node, c.d_hidden), lambda c: c.d_node, 1.0),
+    ("W2", lambda c: (c.n_experts, c.d_hidden, c.d_node), lambda c: c.d_hidden, RESID_SCALE),
+)
+
+
+def make_stack_inputs(cfg: BlockConfig, n_blocks: int = N_BLOCKS, seed: Optional[int] = None):
+    """Inputs of a stack of complete blocks on one graph: (shared, blocks).
+
+    shared: positions, cells, struct_ptr and z drawn exactly as in
+    ``make_inputs`` (same generator, same first two draws); then, from a
+    generator seeded (seed, 2): the element embedding emb ~ N(0,1) [T, Dn]
+    and the readout w_r ~ N(0, 1/Dn).  blocks[b]: the parameters of block b
+    from a generator seeded (seed, 100 + b), drawn in the order of
+    ``_BLOCK_PARAM_SHAPES`` (weights ~ N(0, 1/fan_in), residual-branch
+    outputs times RESID_SCALE; W_ang as in ``make_full_inputs``)."""
+    base = cfg.seed if seed is None else seed
+    rng = np.random.default_rng(base)
+    pos, cells, struct_ptr = make_positions(cfg, rng)
+    z = make_types(cfg, rng)
+    shared = dict(pos=pos, cell=cells, struct_ptr=struct_ptr, z=z, cutoff=np.float32(cfg.cutoff),
+                  top_k=int(cfg.top_k), n_heads=int(cfg.n_heads))
+    r2 = np.random.default_rng([base, 2])
+    shared["emb"] = _normal(r2, (cfg.n_types, cfg.d_node), 1.0)
+    shared["w_r"] = _normal(r2, (cfg.d_node,), 1.0 / math.sqrt(cfg.d_node))
+    blocks = []
+    for b in range(n_blocks):
+        rb = np.random.default_rng([base, 100 + b])
+        blocks.append({name: _normal(rb, shape(cfg), sc if fan is None else sc / math.sqrt(fan(cfg)))
+                       for name, shape, fan, sc in _BLOCK_PARAM_SHAPES})
+    return shared, blocks
+
+
+def device_stack_params(cfg: BlockConfig, n_blocks: int, device, seed: Optional[int] = None):
+    """Block parameters of a stack generated on the GPU (the S-width stack holds
+    about 45 GB of expert weights, too much to draw on the host): a seeded
+    torch generator on the device, seeded with seed * 1000 + 100 + b for block
+    b, same names, shapes, order and scales as ``make_stack_inputs``.  The two
+    logit tables (routing, drawn first) come from the host generator exactly
+    as there, so routing and expert loads match the host-drawn stack."""
+    import torch
+    base = cfg.seed if seed is None else seed
+    blocks = []
+    for b in range(n_blocks):
+        g = torch.Generator(device=device)
+        g.manual_seed(base * 1000 + 100 + b)
+        rb = np.random.default_rng([base, 100 + b])
+        p = {}
+        for name, shape, fan, sc in _BLOCK_PARAM_SHAPES:
+            if name in ("logits0", "logits"):
+                p[name] = torch.from_numpy(_normal(rb, shape(cfg), 1.0)).to(device)
+                continue
+            t = torch.randn(shape(cfg), generator=g, device=device, dtype=torch.float32)
+            p[name] = t.mul_(sc / math.sqrt(fan(cfg)))
+        blocks.append(p)
+    return blocks
+
+
 def upstream_grad(cfg: BlockConfig, inputs: Dict[str, np.ndarray], kind: str = "energy",
                   seed: int = 99) -> np.ndarray:
     """Upstream gradient dL/dh' [N, Dn] f32 for the block's VJP.

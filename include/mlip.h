@@ -262,10 +262,13 @@ int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom
  *                               xx yy zz yz xz xy, as in mlip_block_vjp;
  *   grad_strain [n_structs, 6] (optional, float64) dL/d(strain) per structure.
  * rev is the reverse-edge index of the graph; qkv, o, stats come from the
- * mlip_attention call of the same step.  Per-edge intermediates live in the
- * workspace (mlip_attention_vjp_workspace_size, which grows with n_edges).
- * Rows are reduced by one wavefront each; no atomics, so the result does not
- * depend on scheduling. */
+ * mlip_attention call of the same step.  accumulate != 0 adds to grad_pos and
+ * atom_virial instead of writing them (grad_strain, if given, is then
+ * recomputed from the accumulated atom_virial, which must be given), so the
+ * forces of several blocks on one graph can be collected.  Per-edge
+ * intermediates live in the workspace (mlip_attention_vjp_workspace_size,
+ * which grows with n_edges).  Rows are reduced by one wavefront each; no
+ * atomics, so the result does not depend on scheduling. */
 size_t mlip_attention_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_attn,
                                          int32_t n_heads);
 int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
@@ -274,8 +277,8 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                        const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                        int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
                        float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                       float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
-                       void *stream);
+                       float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Three-body angular update ("Tri") of the complete block ([news]
@@ -323,6 +326,17 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
                  float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
                  float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Element embedding of the input node features ([news] architecture
+ * section: atoms are embedded; [review] 3.1 Fig. 1(b): feature embedding
+ * before the interaction blocks): h[i] = table[z[i]] for table
+ * [n_types, d_node].  Rows of atoms whose type is outside [0, n_types) are
+ * set to zero (the MoE routing of the same step reports such types through
+ * mlip_moe_status).
+ * ------------------------------------------------------------------------ */
+int mlip_embed_atoms(const int32_t *z, const float *table, int32_t n_atoms, int32_t n_types,
+                     int32_t d_node, float *h, void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  When enabled, every kernel launch of the library is

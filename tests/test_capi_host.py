@@ -101,11 +101,16 @@ def test_attention_and_moe_vjp_reject_bad_args(mlip):
     # 5 heads of width 20: 20 is not c * 2^j with c in {1, 2, 3, 4, 6, 8}
     assert "unsupported attention shape" in _err(mlip, att(100, 5), mlip.MLIP_ERR_UNSUPPORTED)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
-                              None, 0, None, f, f, 1 << 30, None)
+                              None, 0, None, f, 0, f, 1 << 30, None)
     assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
-                              None, 0, None, None, f, 16, None)
+                              f, 1, None, f, 1, f, 1 << 30, None)
+    assert "accumulated atom_virial" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
+                              None, 0, None, None, 0, f, 16, None)
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_embed_atoms(f, f, 10, 0, 64, f, None)
+    assert "n_types" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     assert (L.mlip_attention_vjp_workspace_size(4096, 200000, 384, 8)
             >= (200000 * (2 * 8 + 1) + 4096 * 4 * 384) * 4)
     rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, f, f, 1 << 30, None)
