@@ -40,7 +40,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int THREADS = 256;
 constexpr int N_XCD = 8;
 constexpr int RASTER_M = 8;
-constexpr int EXPERT_BK = 32;
+constexpr int EXPERT_BK_NN = 16;   // [K][N] weights: 41 KB of LDS, three workgroups per CU
+constexpr int EXPERT_BK_NT = 32;   // [N][K] weights: 75-78 KB of LDS, two per CU (measured faster)
 constexpr int MAX_GROUPS = 1024;
 
 // Exclusive scan over the 256 threads of the block (one value each).
@@ -407,7 +408,7 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
 // Expert GEMMs: 128 x 128 tiles, 64 x 128 for short group remainders.
 template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
-  return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG, true>(a, s);
+  return launch_t<128, 128, BT ? EXPERT_BK_NT : EXPERT_BK_NN, 2, 2, BT, EPI, TAG, true>(a, s);
 }
 // Dense projections: 64 x 64 tiles when the output is narrow (enough
 // workgroups for 256 CUs), else 64 x 128.
