@@ -192,7 +192,7 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
   MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
   MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u, "null pointer argument");
   MLIP_CHECK_ARG(n_atoms == 0 || (h && s && u), "null pointer argument");
-  MLIP_CHECK_ARG(n_edges == 0 || (src && geom && e), "null edge pointer");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
   MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_e, 16) && aligned(W_d, 16) &&
                      aligned(W_u, 16) && aligned(e, 16) && aligned(s, 16) && aligned(u, 16),
                  "float arrays must be 16-byte aligned");
@@ -326,7 +326,7 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u && W1 && W2 && gate && exp_off, "null pointer argument");
   MLIP_CHECK_ARG(n_atoms == 0 || (s && z && tok_atom && slot && P && grad_out && grad_h && grad_pos),
                  "null pointer argument");
-  MLIP_CHECK_ARG(n_edges == 0 || (src && geom && e), "null edge pointer");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
   MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
                  "grad_strain needs struct_ptr and n_structs >= 1");
   MLIP_CHECK_ARG(aligned(e, 16) && aligned(s, 16) && aligned(P, 16) && aligned(grad_out, 16) &&

@@ -31,7 +31,10 @@ __device__ inline f2v ld2(const float *p) { return *reinterpret_cast<const f2v *
 
 // Forward: e_e = f_c(r) * (phi(r) @ W_e), fused with a_i = sum_e e_e * s_src(e).
 // One wavefront per (row, 128-column slice).  Edges are taken UNROLL at a
-// time with all their gathers issued before any arithmetic.
+// time with all their gathers issued before any arithmetic.  e is written to
+// HBM only when the caller asks for it (STORE_E); the gradient can rebuild it
+// from the 16 basis values at 16 FMAs per element instead of reading it back.
+template <bool STORE_E>
 __global__ void __launch_bounds__(64) embed_aggregate_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, int n_slices, const float *__restrict__ W_e,
@@ -81,7 +84,8 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
           f2v v = {0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < K; ++k) v += phi[m + u][k] * w[k];
-          if (active) __builtin_nontemporal_store(v, reinterpret_cast<f2v *>(e_out + int64_t(e0 + m + u) * De + c));
+          if (STORE_E && active)
+            __builtin_nontemporal_store(v, reinterpret_cast<f2v *>(e_out + int64_t(e0 + m + u) * De + c));
           acc += v * sv[u];
         }
       }
@@ -100,7 +104,9 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
 // de_c/dr = sum_k W_e[k,c] g_k(r), g_k = f_c' phi_k + f_c phi_k'.
 // One workgroup of NW wavefronts per row; wavefront w takes column slices
 // w, w+NW, ...; the per-edge radial terms are computed once per workgroup.
-template <int NW>
+// Without a stored e (HAVE_E false) e_e = sum_k W_e[k,c] f_c phi_k is rebuilt
+// from the same radial terms.
+template <int NW, bool HAVE_E>
 __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ W_e,
@@ -108,6 +114,7 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     int De, float rc, float *__restrict__ sbar, float *__restrict__ grad_pos,
     float *__restrict__ atom_virial) {
   __shared__ float gk[EDGE_CHUNK][K + 1];
+  __shared__ float pk[HAVE_E ? 1 : EDGE_CHUNK][K + 1];   // f_c phi_k when e is rebuilt
   __shared__ float4 dir[EDGE_CHUNK];  // (dhat, unused)
   __shared__ float vq[EDGE_CHUNK][6]; // dhat_a d_b in the order xx yy zz yz xz xy
   __shared__ int jj[EDGE_CHUNK];
@@ -156,6 +163,7 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
           const float x = r - float(k) * R.mu_step;
           const float ph = __expf(-R.gamma * x * x);
           gk[ed][k] = dfc * ph + fc * (-2.f * R.gamma * x * ph);
+          if (!HAVE_E) pk[ed][k] = fc * ph;
         }
         if (part == 0) {
           const float inv = r > 0.f ? 1.f / r : 0.f;
@@ -178,13 +186,20 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
           for (int u = 0; u < UNROLL; ++u) {
             const int mm = min(m + u, n - 1);
             const int j = jj[mm];
-            ev[u] = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(e + int64_t(e0 + mm) * De + c));
+            if (HAVE_E)
+              ev[u] = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(e + int64_t(e0 + mm) * De + c));
             aj[u] = ld2(abar + int64_t(j) * De + c);
             sj[u] = ld2(s + int64_t(j) * De + c);
           }
 #pragma unroll
           for (int u = 0; u < UNROLL; ++u) {
             if (m + u < n) {
+              if (!HAVE_E) {
+                f2v v = {0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < K; ++k) v += pk[m + u][k] * w[k];
+                ev[u] = v;
+              }
               sb += ev[u] * aj[u];
               f2v wv = {0.f, 0.f};
 #pragma unroll
@@ -232,8 +247,13 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
   if (n_atoms <= 0) return MLIP_OK;
   const int n_slices = int(cdiv(De, COLS));
   ProfScope ps(K_EMBED_AGG, stream);
-  embed_aggregate_kernel<<<dim3(unsigned(padded_grid(int64_t(n_atoms) * n_slices))), dim3(64), 0, stream>>>(
-      row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, n_slices, W_e, s, De, rc, e, a);
+  const dim3 grid(unsigned(padded_grid(int64_t(n_atoms) * n_slices)));
+  if (e)
+    embed_aggregate_kernel<true><<<grid, dim3(64), 0, stream>>>(
+        row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, n_slices, W_e, s, De, rc, e, a);
+  else
+    embed_aggregate_kernel<false><<<grid, dim3(64), 0, stream>>>(
+        row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, n_slices, W_e, s, De, rc, e, a);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
@@ -274,19 +294,24 @@ int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geo
   ProfScope ps(K_EDGE_VJP, stream);
   const int n_slices = int(cdiv(De, COLS));
   const float4 *g4 = reinterpret_cast<const float4 *>(geom);
-  if (n_slices >= 4) {
-    edge_vjp_kernel<4><<<dim3(unsigned(padded_grid(n_atoms))), dim3(256), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
-  } else if (n_slices == 3) {
-    edge_vjp_kernel<3><<<dim3(unsigned(padded_grid(n_atoms))), dim3(192), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
-  } else if (n_slices == 2) {
-    edge_vjp_kernel<2><<<dim3(unsigned(padded_grid(n_atoms))), dim3(128), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
+  const dim3 grid(unsigned(padded_grid(n_atoms)));
+  const int nw = n_slices >= 4 ? 4 : n_slices;
+#define MLIP_EDGE_VJP(NWV, HE)                                                                   \
+  edge_vjp_kernel<NWV, HE><<<grid, dim3(64 * NWV), 0, stream>>>(row_ptr, src, g4, n_atoms, W_e, e, \
+                                                                 s, abar, De, rc, sbar, grad_pos,  \
+                                                                 atom_virial)
+  if (e) {
+    if (nw == 4) MLIP_EDGE_VJP(4, true);
+    else if (nw == 3) MLIP_EDGE_VJP(3, true);
+    else if (nw == 2) MLIP_EDGE_VJP(2, true);
+    else MLIP_EDGE_VJP(1, true);
   } else {
-    edge_vjp_kernel<1><<<dim3(unsigned(padded_grid(n_atoms))), dim3(64), 0, stream>>>(
-        row_ptr, src, g4, n_atoms, W_e, e, s, abar, De, rc, sbar, grad_pos, atom_virial);
+    if (nw == 4) MLIP_EDGE_VJP(4, false);
+    else if (nw == 3) MLIP_EDGE_VJP(3, false);
+    else if (nw == 2) MLIP_EDGE_VJP(2, false);
+    else MLIP_EDGE_VJP(1, false);
   }
+#undef MLIP_EDGE_VJP
   MLIP_LAUNCHED();
   return MLIP_OK;
 }

@@ -137,13 +137,15 @@ def mlip_build_graph(pos, cell, struct_ptr, cutoff: float, edge_capacity: Option
 
 
 def mlip_aggregate(graph, h, W_e, W_d, W_u, cutoff: float, out: Optional[Dict] = None,
-                   ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                   ws: Optional[torch.Tensor] = None, store_e: bool = True) -> Dict[str, torch.Tensor]:
+    """Edge embedding + aggregation; out["e"] is None when the edge features are
+    not kept (the VJP then rebuilds them)."""
     N, Dn = int(h.shape[0]), int(h.shape[1])
     De = int(W_e.shape[1])
     E = int(graph["n_edges"])
     dev = h.device
     if out is None:
-        out = dict(e=torch.empty((E, De), dtype=torch.float32, device=dev),
+        out = dict(e=torch.empty((E, De), dtype=torch.float32, device=dev) if store_e else None,
                    s=torch.empty((N, De), dtype=torch.float32, device=dev),
                    u=torch.empty((N, Dn), dtype=torch.float32, device=dev))
     if ws is None:
@@ -366,10 +368,12 @@ class Block:
 
     ``step()`` runs the whole path on the current stream: radius graph,
     aggregation, mixture of experts, readout and the input gradient for the
-    given upstream gradient (node features, positions and strain).
+    given upstream gradient (node features, positions and strain).  The edge
+    features are kept in memory only with ``store_edge_features`` (the input
+    gradient rebuilds them otherwise).
     """
 
-    def __init__(self, inputs: Dict, device="cuda", grad_out=None):
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None, store_edge_features: bool = False):
         def dev(x, dt=None):
             t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
             return t.to(device=device, dtype=dt or t.dtype).contiguous()
@@ -401,6 +405,7 @@ class Block:
         self.ws_moe = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_vjp = _ws(_lib.mlip_vjp_workspace_size(N, self.top_k, De, Dn, H), device)
         self.edge_capacity = None
+        self.store_e = bool(store_edge_features)
         self.graph = self.agg = self.moe = self.ro = self.vjp = None
 
     def step(self):
@@ -408,10 +413,12 @@ class Block:
                              edge_capacity=self.edge_capacity, ws=self.ws_graph)
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
-        reuse = self.agg if (self.agg is not None and self.agg["e"].shape[0] == g["n_edges"]) else None
+        reuse = self.agg
+        if reuse is not None and reuse["e"] is not None and reuse["e"].shape[0] != g["n_edges"]:
+            reuse = None
         self.graph = g
         self.agg = mlip_aggregate(g, self.h, self.W_e, self.W_d, self.W_u, self.cutoff,
-                                  out=reuse, ws=self.ws_agg)
+                                  out=reuse, ws=self.ws_agg, store_e=self.store_e)
         self.moe = mlip_moe_forward(self.agg["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
                                     out=self.moe, ws=self.ws_moe)
         self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)

@@ -114,7 +114,11 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
  *
  * row_ptr/src/geom: graph from mlip_build_graph (n_edges = row_ptr[N]).
  * h [N,d_node], W_e [16,d_edge], W_d [d_node,d_edge], W_u [d_edge,d_node].
- * Outputs e, s (kept for the VJP) and u.  Workspace holds a [N, d_edge].
+ * Outputs s (kept for the VJP), u and, if e is not NULL, the edge features
+ * e [E, d_edge].  e is optional: mlip_block_vjp rebuilds it from the
+ * geometry when it is not kept (16 multiply-adds per element against an
+ * E x d_edge write and read: 312 MB each way at the S widths, 24 GB at the
+ * 262144-atom share).  Workspace holds a [N, d_edge].
  * ------------------------------------------------------------------------ */
 size_t mlip_aggregate_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node);
 int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom,
@@ -181,8 +185,9 @@ int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr
  * With grad_out rows all equal to w_r, grad_pos = dE/dx (forces are
  * -grad_pos) and grad_strain_b / V_b is the stress of structure b.
  *
- * Inputs are the graph, e and s from mlip_aggregate, the kept MoE state
- * from mlip_moe_forward and the weights.  Outputs grad_h [N,d_node],
+ * Inputs are the graph, s and (optional, may be NULL: then rebuilt from
+ * geom and W_e) e from mlip_aggregate, the kept MoE state from
+ * mlip_moe_forward and the weights.  Outputs grad_h [N,d_node],
  * grad_pos [N,3]; optional (may be NULL) atom_virial [N,6] f32 and
  * grad_strain [n_structs,6] f64, both in the order xx, yy, zz, yz, xz, xy;
  * struct_ptr/n_structs are read only when grad_strain is requested.

@@ -57,8 +57,8 @@ def oracle_full(name, upstream):
     return cfg, inp, g, f, v, gup, tables
 
 
-def run_gpu(mlip, inp, gup):
-    blk = mlip.Block(inp, device="cuda", grad_out=gup).step()
+def run_gpu(mlip, inp, gup, store_e=True):
+    blk = mlip.Block(inp, device="cuda", grad_out=gup, store_edge_features=store_e).step()
     torch.cuda.synchronize()
     return blk
 
@@ -82,12 +82,13 @@ def test_graph_bit_exact(mlip, name):
 
 
 @pytest.mark.parametrize("name", SMALL + ["S_slice"])
-@pytest.mark.parametrize("upstream", ["energy", "random"])
-def test_block_parity(mlip, name, upstream):
+@pytest.mark.parametrize("upstream,store_e", [("energy", True), ("random", False)])
+def test_block_parity(mlip, name, upstream, store_e):
+    """store_e: the edge features are kept and compared, else the VJP rebuilds them."""
     cfg, inp, g, f, v, gup, (exp_off, tok_atom, slot) = oracle_full(name, upstream)
-    _say(f"block {name} upstream={upstream}: N={cfg.n_atoms} E={g['src'].size} "
+    _say(f"block {name} upstream={upstream} store_e={store_e}: N={cfg.n_atoms} E={g['src'].size} "
          f"De={cfg.d_edge} Dn={cfg.d_node} H={cfg.d_hidden} X={cfg.n_experts} k={cfg.top_k}")
-    blk = run_gpu(mlip, inp, gup)
+    blk = run_gpu(mlip, inp, gup, store_e)
     # integer tables
     assert np.array_equal(blk.moe["topk"].cpu().numpy(), f["topk"])
     assert np.array_equal(blk.moe["exp_off"].cpu().numpy(), exp_off)
@@ -96,7 +97,6 @@ def test_block_parity(mlip, name, upstream):
     assert not mlip.mlip_moe_status(blk.ws_moe)
     errs = {
         "gate": rel(blk.moe["gate"], f["gate"]),
-        "e": rel(blk.agg["e"], f["e"]),
         "s": rel(blk.agg["s"], f["s"]),
         "u": rel(blk.agg["u"], f["u"]),
         "h_out": rel(blk.moe["h_out"], f["h2"]),
@@ -107,6 +107,10 @@ def test_block_parity(mlip, name, upstream):
         "atom_virial": rel(blk.vjp["atom_virial"], v["atom_virial"]),
         "grad_strain": rel(blk.vjp["grad_strain"], OB.voigt(v["grad_strain"])),
     }
+    if store_e:
+        errs["e"] = rel(blk.agg["e"], f["e"])
+    else:
+        assert blk.agg["e"] is None
     # the kept pre-activations, in dispatch order
     P_ref = np.concatenate([
         (np.asarray(f["u"])[tok_atom[exp_off[x]:exp_off[x + 1]]] @ inp["W1"][x].astype(np.float64))
