@@ -29,6 +29,17 @@ constexpr int UNROLL = 4;
 
 __device__ inline f2v ld2(const float *p) { return *reinterpret_cast<const f2v *>(p); }
 
+// sum_k b[k] w[k] for a 16-aligned LDS row b of K floats (four 16-byte reads)
+__device__ inline f2v basis_dot(const float *b, const f2v (&w)[K]) {
+  f2v v = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < K / 4; ++q) {
+    const float4 t = reinterpret_cast<const float4 *>(b)[q];
+    v += t.x * w[4 * q] + t.y * w[4 * q + 1] + t.z * w[4 * q + 2] + t.w * w[4 * q + 3];
+  }
+  return v;
+}
+
 // Forward: e_e = f_c(r) * (phi(r) @ W_e), fused with a_i = sum_e e_e * s_src(e).
 // One wavefront per (row, 128-column slice).  Edges are taken UNROLL at a
 // time with all their gathers issued before any arithmetic.  e is written to
@@ -40,7 +51,8 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
     const float4 *__restrict__ geom, int n_atoms, int n_slices, const float *__restrict__ W_e,
     const float *__restrict__ s, int De, float rc, float *__restrict__ e_out,
     float *__restrict__ a_out) {
-  __shared__ float phi[EDGE_CHUNK][K + 1];
+  // rows of 16 floats: every lane reads the same row (broadcast), 4 x 16 bytes
+  __shared__ __attribute__((aligned(16))) float phi[EDGE_CHUNK][K];
   __shared__ int jj[EDGE_CHUNK];
   const int lane = threadIdx.x;
   const int64_t blk = xcd_block(int64_t(n_atoms) * n_slices);
@@ -81,9 +93,7 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         if (m + u < n) {
-          f2v v = {0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < K; ++k) v += phi[m + u][k] * w[k];
+          const f2v v = basis_dot(phi[m + u], w);
           if (STORE_E && active)
             __builtin_nontemporal_store(v, reinterpret_cast<f2v *>(e_out + int64_t(e0 + m + u) * De + c));
           acc += v * sv[u];
@@ -113,10 +123,11 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
     const float *__restrict__ e, const float *__restrict__ s, const float *__restrict__ abar,
     int De, float rc, float *__restrict__ sbar, float *__restrict__ grad_pos,
     float *__restrict__ atom_virial) {
-  __shared__ float gk[EDGE_CHUNK][K + 1];
-  __shared__ float pk[HAVE_E ? 1 : EDGE_CHUNK][K + 1];   // f_c phi_k when e is rebuilt
+  // rows of 16 / 8 floats: broadcast reads of 16 bytes
+  __shared__ __attribute__((aligned(16))) float gk[EDGE_CHUNK][K];
+  __shared__ __attribute__((aligned(16))) float pk[HAVE_E ? 1 : EDGE_CHUNK][K];   // f_c phi_k when e is rebuilt
   __shared__ float4 dir[EDGE_CHUNK];  // (dhat, unused)
-  __shared__ float vq[EDGE_CHUNK][6]; // dhat_a d_b in the order xx yy zz yz xz xy
+  __shared__ __attribute__((aligned(16))) float vq[EDGE_CHUNK][8]; // dhat_a d_b: xx yy zz yz xz xy, 2 pad
   __shared__ int jj[EDGE_CHUNK];
   __shared__ float fred[NW][9];
   const int tid = threadIdx.x;
@@ -194,24 +205,23 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
 #pragma unroll
           for (int u = 0; u < UNROLL; ++u) {
             if (m + u < n) {
-              if (!HAVE_E) {
-                f2v v = {0.f, 0.f};
-#pragma unroll
-                for (int k = 0; k < K; ++k) v += pk[m + u][k] * w[k];
-                ev[u] = v;
-              }
+              if (!HAVE_E) ev[u] = basis_dot(pk[m + u], w);
               sb += ev[u] * aj[u];
-              f2v wv = {0.f, 0.f};
-#pragma unroll
-              for (int k = 0; k < K; ++k) wv += gk[m + u][k] * w[k];
+              const f2v wv = basis_dot(gk[m + u], w);
               const f2v z = ai * sj[u] + aj[u] * si;
               const f2v pz = z * wv;
               const float p = pz.x + pz.y;
               const float4 dv = dir[m + u];
               fxy += p * f2v{dv.x, dv.y};
               fz += p * dv.z;
-#pragma unroll
-              for (int q = 0; q < 6; ++q) vir[q] += p * vq[m + u][q];
+              const float4 v0 = reinterpret_cast<const float4 *>(vq[m + u])[0];
+              const float4 v1 = reinterpret_cast<const float4 *>(vq[m + u])[1];
+              vir[0] += p * v0.x;
+              vir[1] += p * v0.y;
+              vir[2] += p * v0.z;
+              vir[3] += p * v0.w;
+              vir[4] += p * v1.x;
+              vir[5] += p * v1.y;
             }
           }
         }
