@@ -15,7 +15,8 @@
 // WM x WN grid; each wavefront owns (BM/WM) x (BN/WN) as 32x32 blocks of
 // v_mfma_f32_32x32x2_f32.  K advances BK at a time through double-buffered
 // LDS with one barrier per step; the next step's global loads are in flight
-// while the current one is multiplied.  A and NT-B tiles sit in LDS as
+// while the current one is multiplied, and are written to the other LDS
+// buffer halfway through the step's multiplies.  A and NT-B tiles sit in LDS as
 // [row][k] (k contiguous, row stride BK+4 floats: 16-byte reads without bank
 // conflicts); NN-B tiles as [k][n].  Each MFMA lane supplies the k-values
 // k0 + 4*(lane/32) + q, q = 0..3, for four consecutive MFMAs, so one 16-byte
@@ -200,6 +201,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
     const float *Bb = Bs[cur];
     Frag f[2];
     read_frag(Ab, Bb, 0, f[0]);
+    // [N][K] weights: the multiplying wave takes issue priority over the
+    // other wave of its SIMD while that one loads and stores (measured faster
+    // there; the [K][N] variant is not helped)
+    if constexpr (BT) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kg = 0; kg < BK / 8; ++kg) {
       // the next group's LDS reads are in flight while this group multiplies
@@ -212,8 +217,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
 #pragma unroll
           for (int bj = 0; bj < FN; ++bj)
             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.a[bi][q], c.b[bj][q], acc[bi][bj], 0, 0, 0);
+      // halfway through the step the next tile goes to the other LDS buffer
+      // (last read before the previous barrier), so the stores overlap the
+      // remaining multiplies
+      if (kg == BK / 16 - 1 && kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
+    if constexpr (BT) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
 
