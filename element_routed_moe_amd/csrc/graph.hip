@@ -8,12 +8,16 @@
 // intrinsic so the compiler cannot contract or reorder it, which makes the
 // edge set identical to any other evaluation of the same formula.
 //
-// Cell list: along an axis whose cell is at least three bin widths (bin width
-// >= r_c) the candidates of an atom are the atoms of its own and the two
-// adjacent bins (wrapping across the cell boundary with a shift of +-1); along
-// a shorter axis there is one bin and every image shift S in
-// [-ceil(r_c/L), ceil(r_c/L)] is visited.  For positions wrapped into
-// [0, L) these shifts reach every image closer than r_c.
+// Cell list in fractional coordinates f = x C^-1 (rows of C are the lattice
+// vectors; any cell with non-zero volume, either handedness).  w_a, the distance between the
+// lattice planes spanned by the other two vectors, sets the bins along axis
+// a: with n_a = floor(w_a / r_c) >= 3 bins every bin is at least r_c thick,
+// so the candidates of an atom are the atoms of its own and the two adjacent
+// bins per axis (wrapping across the cell with a shift of +-1).  Along an
+// axis with fewer than three bins there is one bin, and a candidate's image
+// shifts S_a are those with |d . n_a| < r_c for the plane normal n_a, i.e.
+// S_a in [-r_c/w_a - (f_j - f_i)_a, r_c/w_a - (f_j - f_i)_a] (widened by 1e-9).
+// For orthorhombic cells f_a = x_a / L_a and w_a = L_a.
 #include "common.h"
 
 namespace mlip {
@@ -24,16 +28,20 @@ constexpr int kMaxDeg = 1024;     // edges per row held in LDS by the fill pass
 constexpr int kMaxImages = 8;     // |S| bound along a short axis
 
 enum GraphFlags {
-  GF_NOT_ORTHO = 1,
   GF_BAD_CELL = 2,
   GF_POS_OUTSIDE = 4,
   GF_TOO_MANY_IMAGES = 8,
   GF_REV_MISSING = 16,
 };
 
+// accepted rounding of a general cell's fractional coordinates outside [0, 1)
+constexpr double kFracTol = 1e-6;
+
 struct StructParams {
   double C[9];     // lattice vectors as rows
-  double L[3];     // diagonal
+  double Ci[9];    // C^-1: fractional coordinates f = x C^-1 (row vectors)
+  double w[3];     // lattice-plane spacings (cell edge for orthorhombic cells)
+  int ortho;       // diagonal cell: f_a = x_a / C_aa exactly
   int lo, hi;      // atom range
   int nb[3];       // bins per axis (1 = image mode)
   int nimg[3];     // image range for image-mode axes
@@ -68,17 +76,40 @@ __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__res
   P.bin_base = P.lo + b;
   int f = 0;
   const double rc = double(cutoff);
+  const double *C = P.C;
+  P.ortho = 1;
+  for (int a = 0; a < 3; ++a)
+    for (int c = 0; c < 3; ++c) {
+      if (c != a && C[a * 3 + c] != 0.0) P.ortho = 0;
+      if (!(fabs(C[a * 3 + c]) < 1e30)) f |= GF_BAD_CELL;
+    }
+  // cross products of the rows: X[a] = C[a+1] x C[a+2]; det = C[0] . X[0]
+  double X[9];
   for (int a = 0; a < 3; ++a) {
-    for (int c = 0; c < 3; ++c)
-      if (c != a && P.C[a * 3 + c] != 0.0) f |= GF_NOT_ORTHO;
-    P.L[a] = P.C[a * 3 + a];
-    if (!(P.L[a] > 0.0) || !(P.L[a] < 1e30)) f |= GF_BAD_CELL;
+    const double *u = C + ((a + 1) % 3) * 3, *v = C + ((a + 2) % 3) * 3;
+    X[a * 3 + 0] = u[1] * v[2] - u[2] * v[1];
+    X[a * 3 + 1] = u[2] * v[0] - u[0] * v[2];
+    X[a * 3 + 2] = u[0] * v[1] - u[1] * v[0];
+  }
+  // either handedness is a valid basis; only a flat (or non-finite) cell is not
+  const double det = C[0] * X[0] + C[1] * X[1] + C[2] * X[2];
+  if (!(fabs(det) > 0.0) || !(fabs(det) < 1e300)) f |= GF_BAD_CELL;
+  for (int a = 0; a < 3; ++a) {
+    // C^-1 has the cross products as columns: (C^-1)_{c,a} = X[a]_c / det
+    for (int c = 0; c < 3; ++c) P.Ci[c * 3 + a] = X[a * 3 + c] / det;
+    const double nx = sqrt(X[a * 3] * X[a * 3] + X[a * 3 + 1] * X[a * 3 + 1] + X[a * 3 + 2] * X[a * 3 + 2]);
+    P.w[a] = P.ortho ? C[a * 3 + a] : fabs(det) / nx;
+    if (!(P.w[a] > 0.0)) f |= GF_BAD_CELL;
   }
   int n_b = P.hi - P.lo;
   if (f == 0) {
     int64_t cap = n_b > 1 ? n_b : 1;
+    // a general cell accepts fractional coordinates up to kFracTol outside
+    // [0, 1) and clamps them into the edge bins; the bins are thickened so a
+    // pair closer than r_c still lands in adjacent bins after that move
+    const double tol = P.ortho ? 0.0 : kFracTol;
     for (int a = 0; a < 3; ++a) {
-      double w = P.L[a] / (rc * (1.0 + 1e-5));
+      double w = P.w[a] / (rc * (1.0 + 1e-5) + 2.0 * tol * P.w[a]);
       int nb = w >= 1024.0 ? 1024 : int(w);
       P.nb[a] = nb >= 3 ? nb : 1;
     }
@@ -93,7 +124,8 @@ __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__res
     for (int a = 0; a < 3; ++a) {
       P.nimg[a] = 0;
       if (P.nb[a] == 1) {
-        double n = ceil(rc / P.L[a]);
+        // |S_a| < r_c / w_a + 1 (+ 2 kFracTol for a general cell)
+        double n = ceil(rc / P.w[a]) + (P.ortho ? 0.0 : 1.0);
         if (n > kMaxImages) {
           f |= GF_TOO_MANY_IMAGES;
           n = kMaxImages;
@@ -105,7 +137,7 @@ __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__res
     for (int a = 0; a < 3; ++a) {
       P.nb[a] = 1;
       P.nimg[a] = 0;
-      P.L[a] = 1.0;
+      P.w[a] = 1.0;
     }
   }
   P.valid = f == 0;
@@ -131,6 +163,11 @@ __device__ inline int bin_coord(double x, double L, int nb) {
   return c >= nb ? nb - 1 : c;
 }
 
+// fractional coordinate a of the Cartesian point x (f = x C^-1)
+__device__ inline double frac(const StructParams &P, const double *x, int a) {
+  return x[0] * P.Ci[0 * 3 + a] + x[1] * P.Ci[1 * 3 + a] + x[2] * P.Ci[2 * 3 + a];
+}
+
 __global__ void graph_bin(const float *__restrict__ pos, const int32_t *__restrict__ struct_ptr,
                           int n_structs, int n_atoms, const StructParams *__restrict__ prm,
                           int32_t *__restrict__ atom_struct, int32_t *__restrict__ atom_bin,
@@ -141,11 +178,19 @@ __global__ void graph_bin(const float *__restrict__ pos, const int32_t *__restri
   const StructParams &P = prm[b];
   int c[3];
   bool outside = false;
+  const double x[3] = {double(pos[i * 3 + 0]), double(pos[i * 3 + 1]), double(pos[i * 3 + 2])};
   for (int a = 0; a < 3; ++a) {
-    float xf = pos[i * 3 + a];
-    double x = double(xf);
-    if (!(x >= 0.0) || !(x < P.L[a])) outside = true;
-    c[a] = bin_coord(x, P.L[a], P.nb[a]);
+    if (P.ortho) {
+      // orthorhombic: 0 <= x_a < L_a exactly
+      if (!(x[a] >= 0.0) || !(x[a] < P.w[a])) outside = true;
+      c[a] = bin_coord(x[a], P.w[a], P.nb[a]);
+    } else {
+      // general cell: fractional coordinates in [0, 1) up to the rounding of
+      // float32 positions (the bins' extra 2 kFracTol w_a covers the clamp)
+      const double fa = frac(P, x, a);
+      if (!(fa >= -kFracTol) || !(fa < 1.0 + kFracTol)) outside = true;
+      c[a] = bin_coord(fa, 1.0, P.nb[a]);
+    }
   }
   if (outside) atomicOr(flags, GF_POS_OUTSIDE);
   int gb = P.bin_base + (c[2] * P.nb[1] + c[1]) * P.nb[0] + c[0];
@@ -228,15 +273,18 @@ __device__ inline void visit_candidates(int i, const float *__restrict__ pos,
             q = binned[kk];
             count = 1;
             const float qc[3] = {q.x, q.y, q.z};
+            const double dxyz[3] = {double(qc[0]) - xi[0], double(qc[1]) - xi[1], double(qc[2]) - xi[2]};
             for (int a = 0; a < 3; ++a) {
               if (P.nb[a] != 1) {
                 lo[a] = Sb[a];
                 continue;
               }
-              const double dx = __dsub_rn(double(qc[a]), xi[a]);
+              // (f_j - f_i)_a; the exact predicate below decides, so this
+              // range only has to contain every shift that can give an edge
+              const double df = frac(P, dxyz, a);
               const double slack = 1e-9;
-              int l = int(ceil((-rc - dx) / P.L[a] - slack));
-              int h = int(floor((rc - dx) / P.L[a] + slack));
+              int l = int(ceil(-rc / P.w[a] - df - slack));
+              int h = int(floor(rc / P.w[a] - df + slack));
               l = l < -P.nimg[a] ? -P.nimg[a] : l;
               h = h > P.nimg[a] ? P.nimg[a] : h;
               lo[a] = l;
@@ -510,17 +558,18 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
   const int64_t E = host[0];
   const int flags = host[1];
   *n_edges = E;
-  if (flags & (GF_NOT_ORTHO | GF_BAD_CELL)) {
-    set_error("cell rejected: %s", (flags & GF_NOT_ORTHO) ? "only orthorhombic cells are supported"
-                                                          : "non-positive or non-finite cell edge");
-    return (flags & GF_NOT_ORTHO) ? MLIP_ERR_UNSUPPORTED : MLIP_ERR_INPUT;
+  if (flags & GF_BAD_CELL) {
+    set_error("cell rejected: non-finite entries or zero volume (rows must be a lattice basis; "
+              "a diagonal cell needs positive edges)");
+    return MLIP_ERR_INPUT;
   }
   if (flags & GF_POS_OUTSIDE) {
-    set_error("positions must be wrapped into their cell: 0 <= x < L along each axis");
+    set_error("positions must be wrapped into their cell: fractional coordinates x C^-1 in [0, 1) "
+              "(0 <= x < L along each axis of an orthorhombic cell)");
     return MLIP_ERR_INPUT;
   }
   if (flags & GF_TOO_MANY_IMAGES) {
-    set_error("cutoff spans more than %d cell lengths", kMaxImages);
+    set_error("cutoff spans more than %d lattice-plane spacings of a cell", kMaxImages);
     return MLIP_ERR_UNSUPPORTED;
   }
   if (host[2] > kMaxDeg) {

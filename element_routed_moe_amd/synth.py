@@ -59,6 +59,7 @@ class BlockConfig:
     description: str = ""
     n_heads: int = 0                         # attention heads of the complete block
     d_attn: int = 0                          # attention width Da (0: no complete block)
+    shape: Optional[Sequence[Sequence[float]]] = None  # lattice rows in units of the box edge
 
     def atoms_list(self) -> List[int]:
         if isinstance(self.atoms_per_struct, int):
@@ -73,7 +74,8 @@ class BlockConfig:
             assert self.target_degree is not None
             # expected neighbours = n * (4/3) pi r_c^3 / L^3  ->  solve for L
             vol_sphere = 4.0 / 3.0 * math.pi * self.cutoff ** 3
-            return [(max(m, 1) * vol_sphere / self.target_degree) ** (1.0 / 3.0) for m in n]
+            det = 1.0 if self.shape is None else float(np.linalg.det(np.asarray(self.shape, np.float64)))
+            return [(max(m, 1) * vol_sphere / (self.target_degree * det)) ** (1.0 / 3.0) for m in n]
         if isinstance(self.box, (int, float)):
             return [float(self.box)] * self.n_structs
         out = [float(v) for v in self.box]
@@ -150,17 +152,36 @@ TOP1 = _reg(BlockConfig(
     description="top-1 routing (gate exactly 1), images because r_c > L/2"))
 
 
+TRICLINIC_SHAPE = ((1.0, 0.1, -0.05), (0.35, 0.95, 0.08), (-0.3, 0.25, 0.9))
+TRICLINIC = _reg(BlockConfig(
+    "triclinic", [90, 120, 75], 3, 5.0, 5, 16, 40, 72, 96, 6, 2, seed=17, box=[9.0, 10.5, 8.5],
+    n_heads=2, d_attn=32, shape=TRICLINIC_SHAPE,
+    description="3 triclinic cells (all nine cell entries non-zero), one image bin per axis"))
+TRICLINIC_CL = _reg(BlockConfig(
+    "triclinic_cl", 2000, 1, 4.5, 4, 16, 40, 72, 96, 6, 2, seed=18, target_degree=45.0,
+    n_heads=2, d_attn=32, shape=TRICLINIC_SHAPE,
+    description="one 2000-atom triclinic cell with >= 3 bins per axis (fractional cell list)"))
+
+
 def make_positions(cfg: BlockConfig, rng: np.random.Generator):
-    """Positions [N,3] f32 (wrapped into [0,L)), cells [B,3,3] f32, struct_ptr [B+1] i32."""
+    """Positions [N,3] f32 (wrapped into the cell), cells [B,3,3] f32, struct_ptr [B+1] i32.
+
+    Cubic cells: x = U[0,1)^3 * L rounded to float32.  A config with a
+    ``shape`` uses the cell L * shape (rows = lattice vectors, rounded to
+    float32) and x = f C with f ~ U[0,1)^3, rounded to float32."""
     counts = cfg.atoms_list()
     boxes = cfg.boxes()
     pos_parts = []
     cells = np.zeros((cfg.n_structs, 3, 3), dtype=np.float32)
     for b, (n, L_b) in enumerate(zip(counts, boxes)):
         Lf = np.float32(L_b)
-        cells[b] = np.diag([Lf, Lf, Lf])
-        p = (rng.random((n, 3)) * L_b).astype(np.float32)
-        p[p >= Lf] = np.float32(0.0)
+        if cfg.shape is None:
+            cells[b] = np.diag([Lf, Lf, Lf])
+            p = (rng.random((n, 3)) * L_b).astype(np.float32)
+            p[p >= Lf] = np.float32(0.0)
+        else:
+            cells[b] = (np.asarray(cfg.shape, np.float64) * L_b).astype(np.float32)
+            p = (rng.random((n, 3)) @ cells[b].astype(np.float64)).astype(np.float32)
         pos_parts.append(p)
     pos = np.concatenate(pos_parts, axis=0) if pos_parts else np.zeros((0, 3), np.float32)
     struct_ptr = np.zeros(cfg.n_structs + 1, dtype=np.int32)

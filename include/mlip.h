@@ -69,10 +69,14 @@ int mlip_version(void);
  * evaluated in float64 from the float32 inputs in exactly this order with
  * no fused multiply-add, so the edge set is reproducible bit for bit.
  *
- * pos        [n_atoms,3]      Cartesian positions; atom i of structure b must
- *                             satisfy 0 <= pos[i][a] < C_b[a][a] (wrapped).
- * cell       [n_structs,3,3]  rows are the lattice vectors; only orthorhombic
- *                             cells (zero off-diagonal) are supported.
+ * pos        [n_atoms,3]      Cartesian positions, wrapped into their cell:
+ *                             fractional coordinates f = x C_b^-1 in [0, 1)
+ *                             (for a diagonal cell exactly 0 <= x_a < C_b[a][a];
+ *                             for any other cell up to 1e-6 outside, i.e. the
+ *                             rounding of float32 positions).
+ * cell       [n_structs,3,3]  rows are the lattice vectors: any basis with
+ *                             det != 0 (triclinic included); a diagonal cell
+ *                             needs positive diagonal entries.
  * struct_ptr [n_structs+1]    atoms of structure b are struct_ptr[b] ..
  *                             struct_ptr[b+1]-1 (non-decreasing, 0 .. n_atoms).
  * cutoff     r_c > 0 in the units of pos.
@@ -88,9 +92,10 @@ int mlip_version(void);
  *
  * Errors: MLIP_ERR_CAPACITY when E > edge_capacity (then *n_edges = E and
  * only row_ptr has been written); MLIP_ERR_INPUT for positions outside
- * their cell or non-orthorhombic / non-positive cells (host message says
- * which); MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges or a
- * shift exceeds +-127.  Synchronises the stream once.
+ * their cell or a cell with non-finite entries or det = 0 (host message
+ * says which); MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges, a
+ * shift exceeds +-127 or a cell is so thin that more than 8 images per axis
+ * reach the cutoff.  Synchronises the stream once.
  * ------------------------------------------------------------------------ */
 size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs);
 int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,

@@ -20,7 +20,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-4
-SMALL = ["tiny", "ragged", "celllist", "sparse", "top1", "wide_ragged"]
+SMALL = ["tiny", "ragged", "celllist", "sparse", "top1", "wide_ragged", "triclinic"]
 
 
 def _say(msg):

@@ -20,7 +20,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-4
-SMALL = ["tiny", "ragged", "celllist", "sparse", "top1", "wide_ragged"]
+SMALL = ["tiny", "ragged", "celllist", "sparse", "top1", "wide_ragged", "triclinic", "triclinic_cl"]
 
 
 def _say(msg):
@@ -121,6 +121,46 @@ def test_block_parity(mlip, name, upstream, store_e):
     assert not bad, bad
 
 
+def _rotated(inp, seed):
+    """The same structures turned by a random rotation (cell rows and positions)."""
+    Q, _ = np.linalg.qr(np.random.default_rng(seed).standard_normal((3, 3)))
+    Q *= np.sign(np.linalg.det(Q))
+    q = dict(inp)
+    q["pos"] = (inp["pos"].astype(np.float64) @ Q.T).astype(np.float32)
+    q["cell"] = (inp["cell"].astype(np.float64) @ Q.T).astype(np.float32)
+    return q
+
+
+@pytest.mark.parametrize("name,hand", [("tiny", 1), ("ragged", 1), ("celllist", -1)])
+def test_general_cell_graph_and_rotation(mlip, name, hand):
+    """Rotated cubic cells (nine non-zero entries; hand=-1 also reverses the
+    row order, a left-handed basis): the graph matches the oracle bit for bit
+    and the edge multiset and energy match those of the unrotated cells."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    q = _rotated(inp, 7)
+    if hand < 0:
+        q["cell"] = np.ascontiguousarray(q["cell"][:, ::-1, :])
+    _say(f"rotated {name} (hand {hand}): N={cfg.n_atoms}")
+    g = OG.radius_graph(q["pos"], q["cell"], q["struct_ptr"], q["cutoff"])
+    dev = "cuda"
+    out = mlip.mlip_build_graph(torch.from_numpy(q["pos"]).to(dev), torch.from_numpy(q["cell"]).to(dev),
+                                torch.from_numpy(q["struct_ptr"]).to(dev), float(q["cutoff"]))
+    torch.cuda.synchronize()
+    assert out["n_edges"] == g["src"].size
+    assert np.array_equal(out["row_ptr"].cpu().numpy(), g["row_ptr"])
+    assert np.array_equal(out["src"].cpu().numpy(), g["src"])
+    assert np.array_equal(out["shift"].cpu().numpy()[:, :3].astype(np.int64), g["shift"])
+    assert np.array_equal(out["rev"].cpu().numpy(), g["rev"])
+    assert np.array_equal(out["geom"].cpu().numpy(), g["geom"])
+    # same edges as the unrotated cell up to pairs within rounding of r_c
+    g0 = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    assert abs(g0["src"].size - g["src"].size) <= max(2, g0["src"].size // 10000)
+    e0 = run_gpu(mlip, inp, None).ro["energy"].cpu().numpy()
+    e1 = run_gpu(mlip, q, None).ro["energy"].cpu().numpy()
+    assert np.max(np.abs(e1 - e0)) <= TOL * max(np.max(np.abs(e0)), 1e-30)
+
+
 def test_deterministic(mlip):
     cfg = synth.CONFIGS["ragged"]
     inp = synth.make_inputs(cfg)
@@ -165,11 +205,21 @@ def test_input_errors(mlip):
     with pytest.raises(mlip.MlipError) as ei:
         mlip.mlip_build_graph(bad, cell, sp, 5.0)
     assert ei.value.code == mlip.MLIP_ERR_INPUT
+    flat = cell.clone()
+    flat[0, 2] = flat[0, 0] + flat[0, 1]           # third row in the plane of the first two
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_build_graph(pos, flat, sp, 5.0)
+    assert ei.value.code == mlip.MLIP_ERR_INPUT
+    neg = cell.clone()
+    neg[0, 1, 1] = -8.0                            # diagonal cell with a negative edge
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_build_graph(pos, neg, sp, 5.0)
+    assert ei.value.code == mlip.MLIP_ERR_INPUT
     skew = cell.clone()
-    skew[0, 1, 0] = 0.5
+    skew[0, 1, 0] = 4.0                            # atoms with f_0 = x/8 - y/16 < 0 leave the cell
     with pytest.raises(mlip.MlipError) as ei:
         mlip.mlip_build_graph(pos, skew, sp, 5.0)
-    assert ei.value.code == mlip.MLIP_ERR_UNSUPPORTED
+    assert ei.value.code == mlip.MLIP_ERR_INPUT
     # a too-small edge capacity is reported with the required count, then met
     g = mlip.mlip_build_graph(pos, cell, sp, 5.0, edge_capacity=10)
     assert g["n_edges"] > 10
