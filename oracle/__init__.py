@@ -49,4 +49,14 @@ PINS = {
                                     "continuous (quadratic) across r_c",
     "attention.full_block_vjp": "float64 central finite differences (positions, node features, "
                                 "strain per structure); sum of forces = 0; virial shares add up",
+    "tri.legendre": "numpy.polynomial.legendre values",
+    "tri.tri_row / tri_forward": "P_0 and P_1 closed forms (squared sums minus squares); a "
+                                 "three-atom angle against numpy Legendre values",
+    "tri.tri_vjp": "float64 central finite differences (positions, strain, node features), "
+                   "alone and inside the complete block",
+    "stack.stack_forward / stack_vjp": "float64 central finite differences through 2 and 6 "
+                                       "blocks (positions, strain); sum of forces = 0; rotation",
+    "train.loss_grads": "energies/forces equal block.block_forward/block_vjp; every parameter "
+                        "gradient vs float64 central finite differences of L built from "
+                        "oracle.block; the energy part equals block_vjp's input gradient",
 }

@@ -1,0 +1,117 @@
+"""Parameter gradients of an energy + force loss through one interaction
+block (oracle; test infrastructure only).
+
+[review] 3.3: the forces are the negative gradient of the energy, and the
+potential is trained on energies and forces together, so the training
+gradient differentiates the force once more ("double backward").  The pages
+name no loss form.  Reading taken: the loss is any scalar L(E, F) of the
+per-structure energies and the forces; what the block has to deliver is
+
+    dL/dtheta = sum_b Ebar_b dE_b/dtheta + sum_i Fbar_i . dF_i/dtheta,
+
+with Ebar = dL/dE and Fbar = dL/dF supplied by the caller (for a squared
+error, Ebar = 2 w_E (E - E_ref), Fbar = 2 w_F (F - F_ref)).  theta covers
+every parameter of the block (W_e, W_d, W_u, W1, W2, the routing logits, the
+readout w_r) and the input node features h.
+
+This module writes the block's energy as plain float64 PyTorch CPU
+operations on the same radius graph as ``oracle.block`` and takes both
+derivatives with torch.autograd: first F = -dE/dx with the graph of that
+derivative kept, then the gradient of L.  The block's steps are restated
+here from their definitions (``oracle.block`` holds the readings); the two
+implementations are checked against each other in the tests, and the
+second derivatives against central finite differences of L built from
+``oracle.block``'s energies and forces.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+import torch
+
+from . import block as B
+
+f64 = torch.float64
+PARAMS = ("W_e", "W_d", "W_u", "W1", "W2", "logits", "w_r", "h")
+
+
+def _t(x):
+    return torch.as_tensor(np.asarray(x, np.float64), dtype=f64)
+
+
+def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Tensor) -> torch.Tensor:
+    """E_b of one block as a differentiable function of positions and parameters."""
+    rc = B._cutoff(inp)
+    K = prm["W_e"].shape[0]
+    recv = torch.as_tensor(graph["recv"], dtype=torch.long)
+    src = torch.as_tensor(graph["src"], dtype=torch.long)
+    N = prm["h"].shape[0]
+    # d_e = x_src - x_recv + S . C of the receiver's structure
+    sp = np.asarray(inp["struct_ptr"], np.int64)
+    sb = np.searchsorted(sp, np.asarray(graph["recv"]), side="right") - 1
+    cell = _t(inp["cell"])[torch.as_tensor(sb, dtype=torch.long)]            # [E, 3, 3]
+    S = _t(graph["shift"])
+    d = pos[src] - pos[recv] + torch.einsum("ea,eab->eb", S, cell)
+    r = torch.sqrt((d * d).sum(1))
+    # e = f_c(r) (phi(r) @ W_e)
+    mu = torch.arange(K, dtype=f64) * rc / (K - 1)
+    gamma = (K - 1) ** 2 / (2.0 * rc * rc)
+    phi = torch.exp(-gamma * (r[:, None] - mu) ** 2)
+    fc = torch.where(r < rc, 0.5 * (torch.cos(np.pi * r / rc) + 1.0), torch.zeros_like(r))
+    e = fc[:, None] * (phi @ prm["W_e"])
+    # aggregation and up projection
+    s = prm["h"] @ prm["W_d"]
+    a = torch.zeros(N, e.shape[1], dtype=f64).index_add(0, recv, e * s[src])
+    u = prm["h"] + a @ prm["W_u"]
+    # static element routing: the chosen experts depend on the logits' order
+    # only, the gates are the softmax of the chosen logits
+    k = int(inp["top_k"])
+    topk, _ = B.route(prm["logits"].detach().numpy(), k)
+    z = torch.as_tensor(np.asarray(inp["z"], np.int64))
+    T = prm["logits"].shape[0]
+    chosen = prm["logits"][torch.arange(T)[:, None], torch.as_tensor(topk)]
+    gate = torch.softmax(chosen, dim=1)                                       # [T, k]
+    h2 = u
+    for r_ in range(k):
+        x_of_atom = torch.as_tensor(topk)[z, r_]
+        g_of_atom = gate[z, r_]
+        for x in range(prm["W1"].shape[0]):
+            idx = torch.nonzero(x_of_atom == x).flatten()
+            if idx.numel() == 0:
+                continue
+            y = torch.nn.functional.silu(u[idx] @ prm["W1"][x]) @ prm["W2"][x]
+            h2 = h2.index_add(0, idx, g_of_atom[idx, None] * y)
+    eps = h2 @ prm["w_r"]
+    nb = len(sp) - 1
+    sbat = torch.as_tensor(np.searchsorted(sp, np.arange(N), side="right") - 1, dtype=torch.long)
+    return torch.zeros(nb, dtype=f64).index_add(0, sbat, eps)
+
+
+def loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict[str, np.ndarray]:
+    """E, F and dL/dtheta for L with dL/dE = Ebar [B], dL/dF = Fbar [N, 3]."""
+    prm = {name: _t(inp[name]).requires_grad_(True) for name in PARAMS}
+    pos = _t(inp["pos"]).requires_grad_(True)
+    E = _energy(inp, graph, prm, pos)
+    (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
+    F = -dEdx
+    L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
+    grads = torch.autograd.grad(L, [prm[n] for n in PARAMS], allow_unused=True)
+    out = {"E": E.detach().numpy(), "F": F.detach().numpy()}
+    for n, g in zip(PARAMS, grads):
+        out["d_" + n] = np.zeros(prm[n].shape) if g is None else g.detach().numpy()
+    return out
+
+
+def loss_value(inp: Dict, Ebar: np.ndarray, Fbar: np.ndarray, **override) -> float:
+    """L = Ebar . E + Fbar . F with E and F from ``oracle.block`` (no autograd);
+    keyword arguments replace inputs (for finite differences)."""
+    from .graph import radius_graph
+    q = dict(inp)
+    q.update(override)
+    g = radius_graph(q["pos"], q["cell"], q["struct_ptr"], B._cutoff(q))
+    f = B.block_forward(q, g)
+    N = f["u"].shape[0]
+    gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, f["u"].shape[1]))
+    v = B.block_vjp(q, g, f, gup)
+    return float(np.dot(f["E"], Ebar) + np.sum(-v["grad_pos"] * Fbar))

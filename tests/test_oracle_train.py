@@ -1,0 +1,87 @@
+"""Pins of the training-gradient oracle (``oracle.train``), CPU only.
+
+* its energies and forces equal ``oracle.block``'s (an independent restatement
+  of the block in PyTorch against the NumPy one);
+* every parameter's gradient of L = Ebar . E + Fbar . F matches float64
+  central finite differences of L, where L is built from ``oracle.block``'s
+  energy and forces (so the second derivatives are pinned by first
+  derivatives that are themselves pinned by finite differences of E);
+* with Fbar = 0 the node-feature gradient is ``oracle.block``'s input
+  gradient for the upstream Ebar_b w_r.
+"""
+import numpy as np
+import pytest
+
+from element_routed_moe_amd import synth
+from oracle import block as B
+from oracle import graph as G
+from oracle import train as TR
+
+torch = pytest.importorskip("torch")
+
+
+def _setup(name, seed=5):
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    g = G.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    rng = np.random.default_rng(seed)
+    Ebar = rng.standard_normal(cfg.n_structs)
+    Fbar = rng.standard_normal((cfg.n_atoms, 3))
+    return cfg, inp, g, Ebar, Fbar
+
+
+@pytest.mark.parametrize("name", ["tiny", "sparse"])
+def test_energy_and_forces_match_numpy_oracle(name):
+    cfg, inp, g, Ebar, Fbar = _setup(name)
+    out = TR.loss_grads(inp, g, Ebar, Fbar)
+    f = B.block_forward(inp, g)
+    gup = np.broadcast_to(inp["w_r"].astype(np.float64), (cfg.n_atoms, cfg.d_node))
+    v = B.block_vjp(inp, g, f, gup)
+    assert np.allclose(out["E"], f["E"], rtol=1e-12, atol=1e-12 * np.abs(f["E"]).max())
+    assert np.allclose(out["F"], -v["grad_pos"], rtol=0, atol=1e-12 * np.abs(v["grad_pos"]).max())
+
+
+def _fd_entries(rng, arr, grad, n):
+    """n entries: the largest-gradient ones of a random subset, plus random ones."""
+    flat = np.abs(grad).ravel()
+    cand = rng.choice(flat.size, size=min(flat.size, 64), replace=False)
+    big = cand[np.argsort(-flat[cand])[: n // 2]]
+    rnd = rng.choice(flat.size, size=n - big.size, replace=False)
+    return [np.unravel_index(int(q), arr.shape) for q in np.concatenate([big, rnd])]
+
+
+@pytest.mark.parametrize("name", ["tiny", "top1"])
+def test_param_grads_match_finite_differences(name):
+    cfg, inp, g, Ebar, Fbar = _setup(name)
+    out = TR.loss_grads(inp, g, Ebar, Fbar)
+    rng = np.random.default_rng(11)
+    step = 1e-5
+    for p in TR.PARAMS:
+        base = np.asarray(inp[p], np.float64)
+        grad = out["d_" + p]
+        assert grad.shape == base.shape
+        scale = np.max(np.abs(grad))
+        if p == "logits" and cfg.top_k == 1:
+            assert scale == 0.0                      # one chosen expert: gate 1 whatever the logit
+            continue
+        assert scale > 0, p
+        for idx in _fd_entries(rng, base, grad, 4):
+            up, dn = base.copy(), base.copy()
+            up[idx] += step
+            dn[idx] -= step
+            fd = (TR.loss_value(inp, Ebar, Fbar, **{p: up}) - TR.loss_value(inp, Ebar, Fbar, **{p: dn})) / (2 * step)
+            assert abs(fd - grad[idx]) <= 1e-6 * scale, (p, idx, fd, grad[idx])
+
+
+def test_energy_part_is_first_order_gradient():
+    cfg, inp, g, Ebar, _ = _setup("ragged")
+    out = TR.loss_grads(inp, g, Ebar, np.zeros((cfg.n_atoms, 3)))
+    f = B.block_forward(inp, g)
+    sp = inp["struct_ptr"]
+    lam = np.repeat(Ebar, np.diff(sp))                       # Ebar of each atom's structure
+    gup = lam[:, None] * inp["w_r"].astype(np.float64)[None, :]
+    v = B.block_vjp(inp, g, f, gup)
+    assert np.max(np.abs(out["d_h"] - v["grad_h"])) <= 1e-12 * np.max(np.abs(v["grad_h"]))
+    # d/dw_r of sum_b Ebar_b E_b = sum_i Ebar_b(i) h'_i
+    ref = (lam[:, None] * f["h2"]).sum(0)
+    assert np.max(np.abs(out["d_w_r"] - ref)) <= 1e-12 * np.max(np.abs(ref))
