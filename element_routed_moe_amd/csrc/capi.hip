@@ -27,6 +27,8 @@ int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, 
             float *eps, double *energy, hipStream_t stream);
 int embed_atoms(const int32_t *z, const float *table, int N, int T, int D, float *h,
                 hipStream_t stream);
+int launch_readout_seed(const float *w_r, const double *Ebar, const int32_t *struct_ptr, int N, int B,
+                        int D, float *g, hipStream_t stream);
 
 namespace {
 
@@ -141,20 +143,69 @@ TriVjpWs carve_tri_vjp(void *base, int64_t N, int64_t E, int64_t Dt, size_t *byt
   return w;
 }
 
+struct JvpWs {
+  float *act_dot, *Y_dot;
+};
+JvpWs carve_jvp(void *base, int64_t N, int64_t k, int64_t Dn, int64_t H, size_t *bytes) {
+  Carver c(base);
+  JvpWs w;
+  w.act_dot = c.take<float>(size_t(N * k * H));
+  w.Y_dot = c.take<float>(size_t(N * k * Dn));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+struct TanVjpWs {
+  float *D_dot, *act, *act_dot, *D, *dg, *gt, *U_dot, *ubar_dot, *abar, *abar_dot, *sbar,
+      *sbar_dot, *dwe_part, *split;
+  double *G;
+};
+TanVjpWs carve_tan_vjp(void *base, int64_t N, int64_t T, int64_t k, int64_t De, int64_t Dn,
+                       int64_t H, size_t *bytes) {
+  Carver c(base);
+  TanVjpWs w;
+  const int64_t M = N * k;
+  w.D_dot = c.take<float>(size_t(M * H));
+  w.act = c.take<float>(size_t(M * H));
+  w.act_dot = c.take<float>(size_t(M * H));
+  w.D = c.take<float>(size_t(M * H));
+  w.dg = c.take<float>(size_t(std::max<int64_t>(M, 1)));
+  w.gt = c.take<float>(size_t(std::max<int64_t>(M, 1)));
+  w.U_dot = c.take<float>(size_t(M * Dn));
+  w.ubar_dot = c.take<float>(size_t(N * Dn));
+  w.abar = c.take<float>(size_t(N * De));
+  w.abar_dot = c.take<float>(size_t(N * De));
+  w.sbar = c.take<float>(size_t(N * De));
+  w.sbar_dot = c.take<float>(size_t(N * De));
+  w.dwe_part = c.take<float>(size_t(int64_t(edge_tan_groups(int(N))) * MLIP_N_RBF * De));
+  // split-K scratch of the two dense weight gradients (the larger of the two)
+  WgradArgs u, d;
+  u.P = d.P = int(N);
+  u.Mo = int(De); u.No = int(Dn);
+  d.Mo = int(Dn); d.No = int(De);
+  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(u), wgrad_split_floats(d))));
+  w.G = c.take<double>(size_t(T * k));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
 // dL/du = g + sum_r gate * ((g[tok] @ W2_x^T) * silu'(P)) @ W1_x^T, gathered back
 // by slot in rank order (two grouped GEMMs and the combine).
+// With q_save, the product g[tok] @ W2^T is also kept (before the silu' factor).
 int moe_vjp_core(const float *grad_out, const int32_t *z, const float *gate,
                  const int32_t *exp_off, const int32_t *tok_atom, const int32_t *slot,
                  const float *P, const float *W1, const float *W2, int N, int T, int X, int k,
-                 int Dn, int H, float *Q, float *Utok, float *grad_in, hipStream_t stream) {
+                 int Dn, int H, float *Q, float *Utok, float *grad_in, hipStream_t stream,
+                 float *q_save = nullptr) {
   const int M = N * k;
   GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
   g1.A = grad_out; g1.lda = Dn; g1.a_rows = tok_atom;
   g1.B = W2; g1.ldb = Dn; g1.b_group_stride = int64_t(H) * Dn;
-  g1.C = Q; g1.ldc = H; g1.R = P; g1.ldr = H;
+  g1.C = Q; g1.C2 = q_save; g1.ldc = H; g1.R = P; g1.ldr = H;
   g1.group_off = exp_off; g1.n_groups = X;
   g1.M = M; g1.N = H; g1.K = Dn;
-  if (int rc = launch_gemm(g1, true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN, stream)) return rc;
+  if (int rc = launch_gemm(g1, true, q_save ? EPI_DSILU_Q : EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN, stream))
+    return rc;
   GemmArgs g2;  // U_tok = Q @ W1[x]^T
   g2.A = Q; g2.lda = H;
   g2.B = W1; g2.ldb = H; g2.b_group_stride = int64_t(Dn) * H;
@@ -308,8 +359,8 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    int32_t d_edge, int32_t d_node, int32_t d_hidden, int32_t n_types,
                    int32_t n_experts, int32_t top_k, float cutoff, const float *grad_out,
                    float *grad_h, float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                   float *atom_virial, double *grad_strain, void *ws, size_t ws_bytes,
-                   void *stream_) {
+                   float *atom_virial, double *grad_strain, float *ubar_out, float *q_out,
+                   void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
@@ -339,12 +390,14 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
     if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
     return MLIP_OK;
   }
+  MLIP_CHECK_ARG(aligned(ubar_out, 16) && aligned(q_out, 16), "float arrays must be 16-byte aligned");
   VjpWs w = carve_vjp(ws, n_atoms, top_k, d_edge, d_node, d_hidden, nullptr);
   float *vir = atom_virial ? atom_virial : w.virial;
+  if (ubar_out) w.ubar = ubar_out;
 
   if (int rc = moe_vjp_core(grad_out, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms,
                             n_types, n_experts, top_k, d_node, d_hidden, w.Q, w.Utok, w.ubar,
-                            stream))
+                            stream, q_out))
     return rc;
   GemmArgs g3;  // abar = ubar @ W_u^T
   g3.A = w.ubar; g3.lda = d_node; g3.B = W_u; g3.ldb = d_node; g3.C = w.abar; g3.ldc = d_edge;
@@ -611,6 +664,258 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   g2.A = w.sbar; g2.lda = d_tri; g2.B = W_s; g2.ldb = d_tri; g2.C = grad_h; g2.ldc = d_node;
   g2.R = grad_hT; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_tri;
   return launch_gemm(g2, true, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+// ----------------------------------------------- training gradient: JVP ---
+size_t mlip_block_jvp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node,
+                                     int32_t d_hidden) {
+  size_t b = 0;
+  carve_jvp(nullptr, std::max(n_atoms, 0), std::max(top_k, 1), std::max(d_node, 0),
+            std::max(d_hidden, 0), &b);
+  return b;
+}
+
+static int check_block_dims(int32_t n_atoms, int64_t n_edges, int32_t n_rbf, int32_t d_edge,
+                            int32_t d_node, int32_t d_hidden, int32_t n_types, int32_t n_experts,
+                            int32_t top_k, float cutoff) {
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_edge, "d_edge")) return rc;
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_hidden, "d_hidden")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  return MLIP_OK;
+}
+
+int mlip_block_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *grad_forces, const float *h_dot, const float *s,
+                   const int32_t *z, const float *gate, const int32_t *exp_off,
+                   const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W_e,
+                   const float *W_d, const float *W_u, const float *W1, const float *W2,
+                   int32_t n_rbf, int32_t d_edge, int32_t d_node, int32_t d_hidden,
+                   int32_t n_types, int32_t n_experts, int32_t top_k, float cutoff, float *a,
+                   float *s_dot, float *a_dot, float *u_dot, float *P_dot, float *h_out_dot,
+                   void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (int rc = check_block_dims(n_atoms, n_edges, n_rbf, d_edge, d_node, d_hidden, n_types,
+                                n_experts, top_k, cutoff))
+    return rc;
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u && W1 && W2 && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && s && z && tok_atom && slot && P && a_dot && u_dot &&
+                                  P_dot),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(!h_dot || s_dot, "h_dot needs s_dot");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h_dot, 16) && aligned(s, 16) && aligned(P, 16) &&
+                     aligned(a, 16) && aligned(s_dot, 16) && aligned(a_dot, 16) &&
+                     aligned(u_dot, 16) && aligned(P_dot, 16) && aligned(h_out_dot, 16) &&
+                     aligned(W_e, 16) && aligned(W_d, 16) && aligned(W_u, 16) && aligned(W1, 16) &&
+                     aligned(W2, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_block_jvp_workspace_size(n_atoms, top_k, d_node, d_hidden)))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  JvpWs w = carve_jvp(ws, n_atoms, top_k, d_node, d_hidden, nullptr);
+  const int M = n_atoms * top_k;
+  if (h_dot) {
+    GemmArgs g;  // s_dot = h_dot @ W_d
+    g.A = h_dot; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s_dot; g.ldc = d_edge;
+    g.M = n_atoms; g.N = d_edge; g.K = d_node;
+    if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  }
+  EdgeTanArgs et;  // a_dot = sum_e e_dot * s_src + e * s_dot_src, a = sum_e e * s_src
+  et.row_ptr = row_ptr; et.src = src; et.geom = geom; et.n_atoms = n_atoms;
+  et.x_dot = grad_forces; et.x_sign = -1.f; et.W_e = W_e;
+  et.X = s; et.Y = h_dot ? s_dot : nullptr; et.out1 = a_dot; et.out2 = a;
+  et.De = d_edge; et.rc = cutoff;
+  if (int rc = launch_edge_tan(et, stream)) return rc;
+  GemmArgs g2;  // u_dot = h_dot + a_dot @ W_u
+  g2.A = a_dot; g2.lda = d_edge; g2.B = W_u; g2.ldb = d_node; g2.C = u_dot; g2.ldc = d_node;
+  g2.R = h_dot; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_edge;
+  if (int rc = launch_gemm(g2, false, h_dot ? EPI_RESID : EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  GemmArgs g3;  // P_dot = u_dot[tok] @ W1[x], act_dot = silu'(P) * P_dot
+  g3.A = u_dot; g3.lda = d_node; g3.a_rows = tok_atom;
+  g3.B = W1; g3.ldb = d_hidden; g3.b_group_stride = int64_t(d_node) * d_hidden;
+  g3.C = P_dot; g3.C2 = w.act_dot; g3.ldc = d_hidden; g3.R = P; g3.ldr = d_hidden;
+  g3.group_off = exp_off; g3.n_groups = n_experts;
+  g3.M = M; g3.N = d_hidden; g3.K = d_node;
+  if (int rc = launch_gemm(g3, false, EPI_TAN, K_GEMM_EXPERT_TAN, stream)) return rc;
+  if (!h_out_dot) return MLIP_OK;
+  GemmArgs g4;  // Y_dot = act_dot @ W2[x]
+  g4.A = w.act_dot; g4.lda = d_hidden;
+  g4.B = W2; g4.ldb = d_node; g4.b_group_stride = int64_t(d_hidden) * d_node;
+  g4.C = w.Y_dot; g4.ldc = d_node;
+  g4.group_off = exp_off; g4.n_groups = n_experts;
+  g4.M = M; g4.N = d_node; g4.K = d_hidden;
+  if (int rc = launch_gemm(g4, false, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+  return moe_combine(u_dot, w.Y_dot, z, gate, slot, n_atoms, n_types, top_k, d_node, h_out_dot,
+                     stream);
+}
+
+// ------------------------------------- training gradient: tangent of VJP ---
+size_t mlip_block_tangent_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t top_k,
+                                             int32_t d_edge, int32_t d_node, int32_t d_hidden) {
+  size_t b = 0;
+  carve_tan_vjp(nullptr, std::max(n_atoms, 0), std::max(n_types, 1), std::max(top_k, 1),
+                std::max(d_edge, 0), std::max(d_node, 0), std::max(d_hidden, 0), &b);
+  return b;
+}
+
+int mlip_block_tangent_vjp(
+    const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms, int64_t n_edges,
+    const float *grad_forces, const float *h_dot, const float *h, const float *s,
+    const float *s_dot, const float *a, const float *a_dot, const float *u, const float *u_dot,
+    const int32_t *z, const int32_t *topk, const float *gate, const int32_t *exp_off,
+    const int32_t *tok_atom, const int32_t *slot, const float *P, const float *P_dot,
+    const float *grad_out, const float *ubar, const float *Q, const float *grad_out_dot,
+    const float *W_e, const float *W_d, const float *W_u, const float *W1, const float *W2,
+    int32_t n_rbf, int32_t d_edge, int32_t d_node, int32_t d_hidden, int32_t n_types,
+    int32_t n_experts, int32_t top_k, float cutoff, float *grad_h_dot, float *d_W_e,
+    float *d_W_d, float *d_W_u, float *d_W1, float *d_W2, float *d_gate, float *d_logits,
+    void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (int rc = check_block_dims(n_atoms, n_edges, n_rbf, d_edge, d_node, d_hidden, n_types,
+                                n_experts, top_k, cutoff))
+    return rc;
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u && W1 && W2 && topk && gate && exp_off && d_W_e &&
+                     d_W_d && d_W_u && d_W1 && d_W2,
+                 "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && h && s && a && a_dot && u && u_dot && z &&
+                                  tok_atom && slot && P && P_dot && grad_out && ubar && Q),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(!h_dot || s_dot, "h_dot needs s_dot");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h_dot, 16) && aligned(h, 16) && aligned(s, 16) &&
+                     aligned(s_dot, 16) && aligned(a, 16) && aligned(a_dot, 16) && aligned(u, 16) &&
+                     aligned(u_dot, 16) && aligned(P, 16) && aligned(P_dot, 16) &&
+                     aligned(grad_out, 16) && aligned(ubar, 16) && aligned(Q, 16) &&
+                     aligned(grad_out_dot, 16) && aligned(grad_h_dot, 16) && aligned(W_e, 16) &&
+                     aligned(W_d, 16) && aligned(W_u, 16) && aligned(W1, 16) && aligned(W2, 16) &&
+                     aligned(d_W_e, 16) && aligned(d_W_d, 16) && aligned(d_W_u, 16) &&
+                     aligned(d_W1, 16) && aligned(d_W2, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_block_tangent_vjp_workspace_size(
+                                          n_atoms, n_types, top_k, d_edge, d_node, d_hidden)))
+    return rc;
+  TanVjpWs w = carve_tan_vjp(ws, n_atoms, n_types, top_k, d_edge, d_node, d_hidden, nullptr);
+  const int N = n_atoms, M = n_atoms * top_k;
+  const int De = d_edge, Dn = d_node, H = d_hidden, X = n_experts, k = top_k;
+
+  if (N > 0) {
+    // ---- MoE: Q_dot = g_dot[tok] @ W2^T, then the token-wise tangents ----
+    if (grad_out_dot) {
+      GemmArgs g;
+      g.A = grad_out_dot; g.lda = Dn; g.a_rows = tok_atom;
+      g.B = W2; g.ldb = Dn; g.b_group_stride = int64_t(H) * Dn;
+      g.C = w.D_dot; g.ldc = H;
+      g.group_off = exp_off; g.n_groups = X;
+      g.M = M; g.N = H; g.K = Dn;
+      if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+    }
+    if (int rc = launch_moe_tan(P, P_dot, Q, grad_out_dot ? w.D_dot : nullptr, M, H, w.act, w.act_dot,
+                                w.D, w.D_dot, w.dg, stream))
+      return rc;
+    GemmArgs g2;  // U_dot = D_dot @ W1^T; ubar_dot = g_dot + sum_r gate * U_dot[slot]
+    g2.A = w.D_dot; g2.lda = H;
+    g2.B = W1; g2.ldb = H; g2.b_group_stride = int64_t(Dn) * H;
+    g2.C = w.U_dot; g2.ldc = Dn;
+    g2.group_off = exp_off; g2.n_groups = X;
+    g2.M = M; g2.N = Dn; g2.K = H;
+    if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+    if (int rc = moe_combine(grad_out_dot, w.U_dot, z, gate, slot, N, n_types, k, Dn, w.ubar_dot,
+                             stream))
+      return rc;
+    // ---- projections: abar = ubar W_u^T, abar_dot = ubar_dot W_u^T ----
+    GemmArgs g3;
+    g3.A = ubar; g3.lda = Dn; g3.B = W_u; g3.ldb = Dn; g3.C = w.abar; g3.ldc = De;
+    g3.M = N; g3.N = De; g3.K = Dn;
+    if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+    g3.A = w.ubar_dot; g3.C = w.abar_dot;
+    if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  }
+  // ---- edges: sbar_dot, sbar (with h_dot) and the W_e gradient ----
+  EdgeTanArgs et;
+  et.row_ptr = row_ptr; et.src = src; et.geom = geom; et.n_atoms = N;
+  et.x_dot = grad_forces; et.x_sign = -1.f; et.W_e = W_e;
+  et.X = w.abar; et.Y = w.abar_dot; et.out1 = w.sbar_dot; et.out2 = h_dot ? w.sbar : nullptr;
+  et.R1 = s; et.R2 = h_dot ? s_dot : nullptr; et.dwe = d_W_e; et.dwe_part = w.dwe_part;
+  et.De = De; et.rc = cutoff;
+  if (int rc = launch_edge_tan(et, stream)) return rc;
+  if (grad_h_dot && N > 0) {
+    GemmArgs g;  // grad_h_dot = ubar_dot + sbar_dot W_d^T
+    g.A = w.sbar_dot; g.lda = De; g.B = W_d; g.ldb = De; g.C = grad_h_dot; g.ldc = Dn;
+    g.R = w.ubar_dot; g.ldr = Dn; g.M = N; g.N = Dn; g.K = De;
+    if (int rc = launch_gemm(g, true, EPI_RESID, K_GEMM_DENSE, stream)) return rc;
+  }
+  // ---- weight gradients ----
+  {
+    WgradArgs q;  // d W_u = sum_i a_dot_i^T ubar_i + a_i^T ubar_dot_i
+    q.A0 = a_dot; q.B0 = ubar; q.A1 = a; q.B1 = w.ubar_dot; q.lda = De; q.ldb = Dn;
+    q.P = N; q.Mo = De; q.No = Dn; q.C = d_W_u;
+    if (int rc = launch_wgrad(q, w.split, stream)) return rc;
+  }
+  {
+    WgradArgs q;  // d W_d = sum_i h_dot_i^T sbar_i + h_i^T sbar_dot_i
+    q.A0 = h; q.B0 = w.sbar_dot;
+    if (h_dot) { q.A1 = h_dot; q.B1 = w.sbar; }
+    q.lda = Dn; q.ldb = De; q.P = N; q.Mo = Dn; q.No = De; q.C = d_W_d;
+    if (int rc = launch_wgrad(q, w.split, stream)) return rc;
+  }
+  if (int rc = launch_token_gate(z, gate, slot, N, n_types, k, w.gt, stream)) return rc;
+  {
+    WgradArgs q;  // d W1_x = sum_t gate_t (u_dot[i]^T D_t + u[i]^T D_dot_t)
+    q.A0 = u_dot; q.B0 = w.D; q.A1 = u; q.B1 = w.D_dot; q.lda = Dn; q.ldb = H;
+    q.a_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off; q.n_groups = X;
+    q.P = M; q.Mo = Dn; q.No = H; q.C = d_W1;
+    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
+  }
+  {
+    WgradArgs q;  // d W2_x = sum_t gate_t (act_dot_t^T g[i] + act_t^T g_dot[i])
+    q.A0 = w.act_dot; q.B0 = grad_out;
+    if (grad_out_dot) { q.A1 = w.act; q.B1 = grad_out_dot; }
+    q.lda = H; q.ldb = Dn; q.b_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off;
+    q.n_groups = X; q.P = M; q.Mo = H; q.No = Dn; q.C = d_W2;
+    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
+  }
+  return launch_gate_grad(w.dg, z, topk, gate, exp_off, tok_atom, n_types, X, k, w.G, d_gate,
+                          d_logits, stream);
+}
+
+// ------------------------------------------------------- readout grads ---
+int mlip_readout_vjp(const float *w_r, const double *grad_energy, const int32_t *struct_ptr,
+                     int32_t n_atoms, int32_t n_structs, int32_t d_node, float *grad_h_out,
+                     void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_structs >= 1, "n_atoms >= 0 and n_structs >= 1 required");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(w_r && struct_ptr && (n_atoms == 0 || grad_h_out), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(w_r, 16) && aligned(grad_h_out, 16), "float arrays must be 16-byte aligned");
+  if (n_atoms == 0) return MLIP_OK;
+  return launch_readout_seed(w_r, grad_energy, struct_ptr, n_atoms, n_structs, d_node, grad_h_out,
+                             stream);
+}
+
+size_t mlip_readout_grad_workspace_size(int32_t n_atoms, int32_t d_node) {
+  return size_t(readout_grad_part_floats(std::max(n_atoms, 0), std::max(d_node, 0))) * sizeof(float);
+}
+
+int mlip_readout_grad(const float *h_out, const float *h_out_dot, const double *grad_energy,
+                      const int32_t *struct_ptr, int32_t n_atoms, int32_t n_structs, int32_t d_node,
+                      float *d_w_r, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_structs >= 1, "n_atoms >= 0 and n_structs >= 1 required");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(struct_ptr && d_w_r && (n_atoms == 0 || h_out), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(h_out, 16) && aligned(h_out_dot, 16), "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_readout_grad_workspace_size(n_atoms, d_node))) return rc;
+  return launch_readout_grad(h_out, h_out_dot, grad_energy, struct_ptr, n_atoms, n_structs, d_node,
+                             static_cast<float *>(ws), d_w_r, stream);
 }
 
 // ------------------------------------------------------ atom embedding ----

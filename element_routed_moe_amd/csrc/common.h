@@ -63,6 +63,10 @@ enum KClass {
   K_TRI_FWD,               // three-body update, edge part
   K_TRI_VJP_RECV,          // three-body VJP, receiver rows
   K_TRI_VJP_SEND,          // three-body VJP, sender rows
+  K_GEMM_EXPERT_TAN,       // expert GEMMs of the tangent passes (training gradient)
+  K_GEMM_WGRAD,            // weight-gradient GEMMs (sums over tokens / atoms)
+  K_EDGE_TAN,              // edge passes of the tangents (and the W_e gradient)
+  K_MOE_TAN,               // token-wise MoE tangents, gate and readout gradients
   K_NUM_CLASSES
 };
 
@@ -133,6 +137,8 @@ enum Epilogue {
   EPI_RESID = 1,   // C = R + A B
   EPI_SILU = 2,    // C = A B, C2 = silu(A B)
   EPI_DSILU = 3,   // C = (A B) * silu'(R)
+  EPI_DSILU_Q = 4, // C = (A B) * silu'(R), C2 = A B
+  EPI_TAN = 5,     // C = A B, C2 = (A B) * silu'(R)
 };
 
 struct GemmArgs {
@@ -154,6 +160,54 @@ struct GemmArgs {
 
 int launch_gemm(const GemmArgs &a, bool b_transposed, Epilogue epi, KClass cls,
                 hipStream_t stream);
+
+// ------------------------------------------------------ training gradient -
+// Weight-gradient sums on the matrix cores:
+//   C_g = sum over rows p of group g of scale[p] * (A0[ar(p)]^T B0[br(p)] + A1[ar(p)]^T B1[br(p)])
+// with ar / br optional row gathers; C is [G][Mo][No] (row-major, dense).
+struct WgradArgs {
+  const float *A0 = nullptr, *A1 = nullptr;   // rows of Mo floats, stride lda (A1/B1: optional term)
+  const float *B0 = nullptr, *B1 = nullptr;   // rows of No floats, stride ldb
+  int64_t lda = 0, ldb = 0;
+  const int32_t *a_rows = nullptr, *b_rows = nullptr;
+  const float *scale = nullptr;               // per-row factor on the A operand
+  const int32_t *group_off = nullptr;         // [G+1]; nullptr -> one group [0, P)
+  int n_groups = 1, P = 0, Mo = 0, No = 0;
+  float *C = nullptr;
+};
+// Floats of split-K scratch an ungrouped weight gradient needs (0: none).
+int64_t wgrad_split_floats(const WgradArgs &a);
+int launch_wgrad(const WgradArgs &a, float *split_ws, hipStream_t stream);
+
+// One sweep over the CSR rows (see second.hip): out1 = W_e . T, out2 = W_e . U
+// and, with R1, the W_e gradient sum_i R1_i T + R2_i U.
+struct EdgeTanArgs {
+  const int32_t *row_ptr = nullptr, *src = nullptr;
+  const float *geom = nullptr;
+  int n_atoms = 0;
+  const float *x_dot = nullptr;               // [N][3]; the direction is x_sign * x_dot
+  float x_sign = 1.f;
+  const float *W_e = nullptr;                 // [K][De]
+  const float *X = nullptr, *Y = nullptr;     // [N][De] sender rows (Y optional)
+  float *out1 = nullptr, *out2 = nullptr;     // [N][De] (out2 optional)
+  const float *R1 = nullptr, *R2 = nullptr;   // [N][De] (R1 null: no W_e gradient; R2 optional)
+  float *dwe = nullptr;                       // [K][De]
+  float *dwe_part = nullptr;                  // [edge_tan_groups(N)][K][De] scratch
+  int De = 0;
+  float rc = 0.f;
+};
+int edge_tan_groups(int n_atoms);
+int launch_edge_tan(const EdgeTanArgs &a, hipStream_t stream);
+int launch_moe_tan(const float *P, const float *P_dot, const float *Q, const float *Q_dot, int M, int H,
+                   float *act, float *act_dot, float *D, float *D_dot, float *dg, hipStream_t stream);
+int launch_token_gate(const int32_t *z, const float *gate, const int32_t *slot, int N, int T, int k,
+                      float *gt, hipStream_t stream);
+int launch_gate_grad(const float *dg, const int32_t *z, const int32_t *topk, const float *gate,
+                     const int32_t *exp_off, const int32_t *tok_atom, int T, int X, int k, double *G,
+                     float *d_gate, float *d_logits, hipStream_t stream);
+int64_t readout_grad_part_floats(int N, int D);
+int launch_readout_grad(const float *h, const float *h_dot, const double *Ebar, const int32_t *struct_ptr,
+                        int N, int B, int D, float *part, float *d_w_r, hipStream_t stream);
 
 // ------------------------------------------------------------- attention ---
 struct AttnArgs {

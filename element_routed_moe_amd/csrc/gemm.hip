@@ -237,7 +237,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
       const bool col_ok = col < g.N;
       const int colc = col_ok ? col : n0;
       float rv[16];
-      if (EPI == EPI_RESID || EPI == EPI_DSILU) {
+      if (EPI == EPI_RESID || EPI == EPI_DSILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int p = row0 + wm * WTM + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
@@ -258,14 +258,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
           out = v;
           out2 = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
         } else {
+          // silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the saved pre-activation
           const float x = rv[r];
           const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-x));
-          out = v * (sg * (1.f + x * (1.f - sg)));
+          const float d1 = sg * (1.f + x * (1.f - sg));
+          if (EPI == EPI_TAN) {
+            out = v;
+            out2 = v * d1;
+          } else {
+            out = v * d1;
+            out2 = v;
+          }
         }
         if (col_ok && p < rows) {
           const int64_t o = int64_t(p) * g.ldc + col;
           g.C[o] = out;
-          if (EPI == EPI_SILU) g.C2[o] = out2;
+          if (EPI == EPI_SILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) g.C2[o] = out2;
         }
       }
     }
@@ -449,6 +457,12 @@ int launch_gemm(const GemmArgs &a, bool bt, Epilogue epi, KClass cls, hipStream_
       break;
     case K_GEMM_EXPERT_VJP_DOWN:
       if (bt && epi == EPI_DSILU) return launch_expert<true, EPI_DSILU, K_GEMM_EXPERT_VJP_DOWN>(a, stream);
+      if (bt && epi == EPI_DSILU_Q) return launch_expert<true, EPI_DSILU_Q, K_GEMM_EXPERT_VJP_DOWN>(a, stream);
+      break;
+    case K_GEMM_EXPERT_TAN:
+      if (!bt && epi == EPI_TAN) return launch_expert<false, EPI_TAN, K_GEMM_EXPERT_TAN>(a, stream);
+      if (!bt && epi == EPI_STORE) return launch_expert<false, EPI_STORE, K_GEMM_EXPERT_TAN>(a, stream);
+      if (bt && epi == EPI_STORE) return launch_expert<true, EPI_STORE, K_GEMM_EXPERT_TAN>(a, stream);
       break;
     case K_GEMM_EXPERT_VJP_UP:
       if (bt && epi == EPI_STORE) return launch_expert<true, EPI_STORE, K_GEMM_EXPERT_VJP_UP>(a, stream);

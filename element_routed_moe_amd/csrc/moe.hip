@@ -167,7 +167,8 @@ __global__ void dispatch_scatter_kernel(const int32_t *__restrict__ z, int N, in
   }
 }
 
-// out_i = base_i + sum_r gate[z_i, r] * rows[slot(i, r)], r in rank order.
+// out_i = base_i + sum_r gate[z_i, r] * rows[slot(i, r)], r in rank order
+// (base may be null: 0).
 __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ base,
                                                       const float *__restrict__ rows,
                                                       const int32_t *__restrict__ z,
@@ -179,7 +180,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
   t = t < 0 ? 0 : (t >= T ? T - 1 : t);
   const int D4 = D >> 2;
   for (int c = threadIdx.x; c < D4; c += blockDim.x) {
-    float4 acc = reinterpret_cast<const float4 *>(base + int64_t(i) * D)[c];
+    float4 acc = base ? reinterpret_cast<const float4 *>(base + int64_t(i) * D)[c]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = 0; r < k; ++r) {
       const float gv = gate[t * k + r];
       const float4 y = reinterpret_cast<const float4 *>(rows + int64_t(slot[int64_t(i) * k + r]) * D)[c];

@@ -21,7 +21,8 @@ static const char *kClassNames[K_NUM_CLASSES] = {
     "graph",          "embed_aggregate",     "gemm_dense",         "route_dispatch",
     "gemm_expert_up", "gemm_expert_down",    "combine",            "readout",
     "gemm_expert_vjp_down", "gemm_expert_vjp_up", "edge_vjp", "attn_fwd",
-    "attn_vjp_recv", "attn_vjp_send", "tri_fwd", "tri_vjp_recv", "tri_vjp_send"};
+    "attn_vjp_recv", "attn_vjp_send", "tri_fwd", "tri_vjp_recv", "tri_vjp_send",
+    "gemm_expert_tan", "gemm_wgrad", "edge_tan", "moe_tan"};
 
 struct ProfRec {
   int k;

@@ -56,7 +56,19 @@ _SIGS = {
     "mlip_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "mlip_block_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
                                  _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                 _f32, _p, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]),
+                                 _f32, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_block_jvp_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "mlip_block_jvp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                 _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_block_tangent_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "mlip_block_tangent_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
+                                         _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                         _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_readout_vjp": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p]),
+    "mlip_readout_grad_workspace_size": (_sz, [_i32, _i32]),
+    "mlip_readout_grad": (C.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _sz, _p]),
     "mlip_moe_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "mlip_moe_vjp": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _p, _p, _p, _sz, _p]),
@@ -203,7 +215,8 @@ def mlip_readout(h_out, w_r, struct_ptr, out: Optional[Dict] = None) -> Dict[str
 
 def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top_k: int,
                    grad_out, struct_ptr=None, out: Optional[Dict] = None,
-                   ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                   ws: Optional[torch.Tensor] = None, keep: bool = False) -> Dict[str, torch.Tensor]:
+    """Input gradient; with ``keep`` also out["ubar"] and out["Q"] for the training gradient."""
     N, Dn = int(grad_out.shape[0]), int(grad_out.shape[1])
     De = int(W_e.shape[1])
     H = int(W1.shape[2])
@@ -218,6 +231,9 @@ def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top
                    atom_virial=torch.empty((N, 6), dtype=torch.float32, device=dev))
         if struct_ptr is not None:
             out["grad_strain"] = torch.empty((B, 6), dtype=torch.float64, device=dev)
+    if keep and "ubar" not in out:
+        out["ubar"] = torch.empty((N, Dn), dtype=torch.float32, device=dev)
+        out["Q"] = torch.empty((N * int(top_k), H), dtype=torch.float32, device=dev)
     if ws is None:
         ws = _ws(_lib.mlip_vjp_workspace_size(N, top_k, De, Dn, H), dev)
     _check(_lib.mlip_block_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
@@ -227,7 +243,102 @@ def mlip_block_vjp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top
                                int(W_e.shape[0]), De, Dn, H, T, X, int(top_k), float(cutoff),
                                _ptr(grad_out), _ptr(out["grad_h"]), _ptr(out["grad_pos"]),
                                _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
-                               _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))
+                               _ptr(out.get("grad_strain")), _ptr(out.get("ubar") if keep else None),
+                               _ptr(out.get("Q") if keep else None), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_block_jvp(graph, agg, moe, z, W_e, W_d, W_u, W1, W2, cutoff: float, top_k: int,
+                   grad_forces, h_dot=None, want_h_out_dot: bool = True, out: Optional[Dict] = None,
+                   ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Forward tangents along x_dot = -grad_forces (and h_dot): a, s_dot, a_dot, u_dot, P_dot, h_out_dot."""
+    N, De = int(agg["s"].shape[0]), int(W_e.shape[1])
+    Dn, H, X = int(W_u.shape[1]), int(W1.shape[2]), int(W1.shape[0])
+    T, k = int(moe["gate"].shape[0]), int(top_k)
+    E = int(graph["n_edges"])
+    dev = agg["s"].device
+    f32 = torch.float32
+    if out is None:
+        out = dict(a=torch.empty((N, De), dtype=f32, device=dev),
+                   s_dot=torch.empty((N, De), dtype=f32, device=dev) if h_dot is not None else None,
+                   a_dot=torch.empty((N, De), dtype=f32, device=dev),
+                   u_dot=torch.empty((N, Dn), dtype=f32, device=dev),
+                   P_dot=torch.empty((N * k, H), dtype=f32, device=dev),
+                   h_out_dot=torch.empty((N, Dn), dtype=f32, device=dev) if want_h_out_dot else None)
+    need = _lib.mlip_block_jvp_workspace_size(N, k, Dn, H)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_block_jvp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                               _ptr(grad_forces), _ptr(h_dot), _ptr(agg["s"]), _ptr(z), _ptr(moe["gate"]),
+                               _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]), _ptr(moe["slot"]),
+                               _ptr(moe["P"]), _ptr(W_e), _ptr(W_d), _ptr(W_u), _ptr(W1), _ptr(W2),
+                               int(W_e.shape[0]), De, Dn, H, T, X, k, float(cutoff), _ptr(out["a"]),
+                               _ptr(out["s_dot"]), _ptr(out["a_dot"]), _ptr(out["u_dot"]),
+                               _ptr(out["P_dot"]), _ptr(out["h_out_dot"]), _ptr(ws), ws.numel(),
+                               _stream()))
+    out["ws"] = ws
+    return out
+
+
+def mlip_block_tangent_vjp(graph, h, agg, moe, jvp, vjp, z, W_e, W_d, W_u, W1, W2, cutoff: float,
+                           top_k: int, grad_forces, grad_out, grad_out_dot=None, h_dot=None,
+                           want_grad_h_dot: bool = True, out: Optional[Dict] = None,
+                           ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Weight gradients (and dL/dh) of the tangent of the block's VJP; ``vjp`` holds ubar and Q."""
+    N, De = int(h.shape[0]), int(W_e.shape[1])
+    Dn, H, X = int(h.shape[1]), int(W1.shape[2]), int(W1.shape[0])
+    T, k = int(moe["gate"].shape[0]), int(top_k)
+    E = int(graph["n_edges"])
+    dev = h.device
+    f32 = torch.float32
+    if out is None:
+        out = dict(d_W_e=torch.empty(tuple(W_e.shape), dtype=f32, device=dev),
+                   d_W_d=torch.empty(tuple(W_d.shape), dtype=f32, device=dev),
+                   d_W_u=torch.empty(tuple(W_u.shape), dtype=f32, device=dev),
+                   d_W1=torch.empty(tuple(W1.shape), dtype=f32, device=dev),
+                   d_W2=torch.empty(tuple(W2.shape), dtype=f32, device=dev),
+                   d_gate=torch.empty((T, k), dtype=f32, device=dev),
+                   d_logits=torch.empty((T, X), dtype=f32, device=dev),
+                   grad_h_dot=torch.empty((N, Dn), dtype=f32, device=dev) if want_grad_h_dot else None)
+    need = _lib.mlip_block_tangent_vjp_workspace_size(N, T, k, De, Dn, H)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_block_tangent_vjp(
+        _ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E, _ptr(grad_forces),
+        _ptr(h_dot), _ptr(h), _ptr(agg["s"]), _ptr(jvp["s_dot"]), _ptr(jvp["a"]), _ptr(jvp["a_dot"]),
+        _ptr(agg["u"]), _ptr(jvp["u_dot"]), _ptr(z), _ptr(moe["topk"]), _ptr(moe["gate"]),
+        _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]), _ptr(moe["slot"]), _ptr(moe["P"]), _ptr(jvp["P_dot"]),
+        _ptr(grad_out), _ptr(vjp["ubar"]), _ptr(vjp["Q"]), _ptr(grad_out_dot), _ptr(W_e), _ptr(W_d),
+        _ptr(W_u), _ptr(W1), _ptr(W2), int(W_e.shape[0]), De, Dn, H, T, X, k, float(cutoff),
+        _ptr(out["grad_h_dot"]), _ptr(out["d_W_e"]), _ptr(out["d_W_d"]), _ptr(out["d_W_u"]),
+        _ptr(out["d_W1"]), _ptr(out["d_W2"]), _ptr(out["d_gate"]), _ptr(out["d_logits"]), _ptr(ws),
+        ws.numel(), _stream()))
+    out["ws"] = ws
+    return out
+
+
+def mlip_readout_vjp(w_r, struct_ptr, n_atoms: int, grad_energy=None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grad_h_out_i = grad_energy[b(i)] w_r (grad_energy None: w_r)."""
+    Dn = int(w_r.shape[0])
+    B = int(struct_ptr.shape[0]) - 1
+    if out is None:
+        out = torch.empty((int(n_atoms), Dn), dtype=torch.float32, device=w_r.device)
+    _check(_lib.mlip_readout_vjp(_ptr(w_r), _ptr(grad_energy), _ptr(struct_ptr), int(n_atoms), B, Dn,
+                                 _ptr(out), _stream()))
+    return out
+
+
+def mlip_readout_grad(h_out, struct_ptr, grad_energy=None, h_out_dot=None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d_w_r = sum_i grad_energy[b(i)] h_out_i + h_out_dot_i."""
+    N, Dn = int(h_out.shape[0]), int(h_out.shape[1])
+    B = int(struct_ptr.shape[0]) - 1
+    if out is None:
+        out = torch.empty(Dn, dtype=torch.float32, device=h_out.device)
+    ws = _ws(_lib.mlip_readout_grad_workspace_size(N, Dn), h_out.device)
+    _check(_lib.mlip_readout_grad(_ptr(h_out), _ptr(h_out_dot), _ptr(grad_energy), _ptr(struct_ptr), N, B,
+                                  Dn, _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 
@@ -373,7 +484,8 @@ class Block:
     gradient rebuilds them otherwise).
     """
 
-    def __init__(self, inputs: Dict, device="cuda", grad_out=None, store_edge_features: bool = False):
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None, store_edge_features: bool = False,
+                 train: bool = False):
         def dev(x, dt=None):
             t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
             return t.to(device=device, dtype=dt or t.dtype).contiguous()
@@ -406,7 +518,9 @@ class Block:
         self.ws_vjp = _ws(_lib.mlip_vjp_workspace_size(N, self.top_k, De, Dn, H), device)
         self.edge_capacity = None
         self.store_e = bool(store_edge_features)
+        self.train = bool(train)
         self.graph = self.agg = self.moe = self.ro = self.vjp = None
+        self.jvp = self.tan = None
 
     def step(self):
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
@@ -424,8 +538,33 @@ class Block:
         self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
         self.vjp = mlip_block_vjp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u,
                                   self.W1, self.W2, self.cutoff, self.top_k, self.grad_out,
-                                  struct_ptr=self.struct_ptr, out=self.vjp, ws=self.ws_vjp)
+                                  struct_ptr=self.struct_ptr, out=self.vjp, ws=self.ws_vjp,
+                                  keep=self.train)
         return self
+
+    def train_grad(self, grad_energy, grad_forces) -> Dict[str, torch.Tensor]:
+        """Parameter gradients of a loss L(E, F) after ``step()`` (built with
+        ``train=True`` and the force seed grad_out = w_r): grad_energy = dL/dE
+        [B] float64, grad_forces = dL/dF [N, 3] float32, both on the device.
+        Returns d_W_e, d_W_d, d_W_u, d_W1, d_W2, d_logits, d_gate, d_w_r and
+        d_h (= dL/dh of the input features)."""
+        if not self.train or self.vjp is None:
+            raise RuntimeError("train_grad needs Block(train=True) and a step() first")
+        g = self.graph
+        self.jvp = mlip_block_jvp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u, self.W1,
+                                  self.W2, self.cutoff, self.top_k, grad_forces,
+                                  out=self.jvp, ws=None if self.jvp is None else self.jvp["ws"])
+        seed_dot = mlip_readout_vjp(self.w_r, self.struct_ptr, self.h.shape[0], grad_energy=grad_energy)
+        self.tan = mlip_block_tangent_vjp(g, self.h, self.agg, self.moe, self.jvp, self.vjp, self.z, self.W_e,
+                                          self.W_d, self.W_u, self.W1, self.W2, self.cutoff, self.top_k,
+                                          grad_forces, self.grad_out, grad_out_dot=seed_dot, out=self.tan,
+                                          ws=None if self.tan is None else self.tan["ws"])
+        d_w_r = mlip_readout_grad(self.moe["h_out"], self.struct_ptr, grad_energy=grad_energy,
+                                  h_out_dot=self.jvp["h_out_dot"])
+        res = {k: v for k, v in self.tan.items() if k not in ("ws", "grad_h_dot")}
+        res["d_h"] = self.tan["grad_h_dot"]
+        res["d_w_r"] = d_w_r
+        return res
 
 
 class FullBlock:

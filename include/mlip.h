@@ -196,6 +196,10 @@ int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr
  * grad_pos [N,3]; optional (may be NULL) atom_virial [N,6] f32 and
  * grad_strain [n_structs,6] f64, both in the order xx, yy, zz, yz, xz, xy;
  * struct_ptr/n_structs are read only when grad_strain is requested.
+ * For the training gradient (mlip_block_tangent_vjp) two intermediates can
+ * be kept (may be NULL): ubar_out [N,d_node] = ubar above and
+ * q_out [N*top_k, d_hidden] = grad_out[tok] @ W2_x^T in dispatch order
+ * (before the silu' factor).
  * ------------------------------------------------------------------------ */
 size_t mlip_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_edge,
                                int32_t d_node, int32_t d_hidden);
@@ -208,7 +212,94 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    int32_t d_hidden, int32_t n_types, int32_t n_experts, int32_t top_k,
                    float cutoff, const float *grad_out, float *grad_h, float *grad_pos,
                    const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
-                   double *grad_strain, void *ws, size_t ws_bytes, void *stream);
+                   double *grad_strain, float *ubar_out, float *q_out, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Training gradient of the block: parameter gradients of a loss on energies
+ * and forces ([review] 3.3: the potential is fitted to energies and to the
+ * forces obtained by differentiating the energy, so training differentiates
+ * the force once more).  For L(E, F) with grad_energy = dL/dE [n_structs]
+ * (f64) and grad_forces = dL/dF [N,3]:
+ *   dL/dtheta = sum_b dL/dE_b dE_b/dtheta + sum_i dL/dF_i . dF_i/dtheta,
+ * computed as the derivative of the reverse-mode gradient along the
+ * position direction x_dot = -grad_forces (forward over reverse), with the
+ * reverse pass seeded by grad_out = w_r (the force seed) and its tangent by
+ * grad_out_dot = dL/dE_b(i) w_r (mlip_readout_vjp).  Sequence for one block:
+ *   forward (mlip_aggregate, mlip_moe_forward, mlip_readout), then
+ *   mlip_block_vjp with grad_out = w_r keeping ubar_out and q_out (F = -grad_pos),
+ *   the caller's loss gives grad_energy and grad_forces, then
+ *   mlip_block_jvp (forward tangents), mlip_readout_vjp (grad_out_dot),
+ *   mlip_block_tangent_vjp (weight gradients, dL/dh) and
+ *   mlip_readout_grad (dL/dw_r).
+ * A stack passes h_dot upward (h_out_dot of the block below) in the JVPs
+ * and grad_out_dot downward (grad_h_dot of the block above) in the tangent
+ * VJPs, top block first.
+ *
+ * mlip_block_jvp: tangents of the forward along x_dot = -grad_forces [N,3]
+ * and h_dot [N,d_node] (may be NULL: 0).  With r_dot_e = dhat_e .
+ * (x_dot_src - x_dot_recv), e_dot = r_dot d e/d r:
+ *   s_dot = h_dot W_d;  a_dot_i = sum_{e in row i} e_dot_e * s_src + e_e * s_dot_src
+ *   u_dot = h_dot + a_dot W_u;  P_dot = u_dot[tok] W1_x (dispatch order)
+ *   h_out_dot = u_dot + sum_r gate * (silu'(P) * P_dot) W2_x   (may be NULL)
+ * and the primal aggregate a (may be NULL) of the same sweep.  s, z, gate,
+ * exp_off, tok_atom, slot, P: the forward's.  Outputs a, s_dot (needed when
+ * h_dot is given), a_dot, u_dot [N,d_node], P_dot [N*top_k, d_hidden].
+ * Workspace: mlip_block_jvp_workspace_size().
+ *
+ * mlip_block_tangent_vjp: the derivative, along (x_dot, h_dot, grad_out_dot),
+ * of the block's reverse-mode gradient for the upstream grad_out.  Inputs:
+ * the graph, grad_forces and h_dot as in the JVP; h, s, u from the forward
+ * (u = mlip_aggregate's output), s_dot, a, a_dot, u_dot, P_dot from the JVP;
+ * the forward's z, topk, gate, exp_off, tok_atom, slot, P; grad_out, ubar
+ * and Q (ubar_out, q_out of mlip_block_vjp); grad_out_dot [N,d_node] (may
+ * be NULL: 0).  Outputs (dense row-major, written, not accumulated):
+ *   d_W_e [n_rbf,d_edge], d_W_d [d_node,d_edge], d_W_u [d_edge,d_node],
+ *   d_W1 [n_experts,d_node,d_hidden], d_W2 [n_experts,d_hidden,d_node]
+ *   (experts without tokens get 0), d_gate [n_types,top_k] (may be NULL),
+ *   d_logits [n_types,n_experts] (may be NULL; gates are the softmax of the
+ *   chosen logits, the others get 0), grad_h_dot [N,d_node] = dL/dh of the
+ *   block input (may be NULL).
+ * Workspace: mlip_block_tangent_vjp_workspace_size().
+ *
+ * mlip_readout_vjp: grad_h_out_i = grad_energy[b(i)] w_r (grad_energy NULL:
+ * 1, the force seed).  mlip_readout_grad: d_w_r = sum_i grad_energy[b(i)]
+ * h_out_i + h_out_dot_i (either term may be NULL); workspace:
+ * mlip_readout_grad_workspace_size().
+ * Every reduction runs in a fixed order: results are reproducible.
+ * ------------------------------------------------------------------------ */
+size_t mlip_block_jvp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node,
+                                     int32_t d_hidden);
+int mlip_block_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   int64_t n_edges, const float *grad_forces, const float *h_dot, const float *s,
+                   const int32_t *z, const float *gate, const int32_t *exp_off,
+                   const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W_e,
+                   const float *W_d, const float *W_u, const float *W1, const float *W2,
+                   int32_t n_rbf, int32_t d_edge, int32_t d_node, int32_t d_hidden,
+                   int32_t n_types, int32_t n_experts, int32_t top_k, float cutoff, float *a,
+                   float *s_dot, float *a_dot, float *u_dot, float *P_dot, float *h_out_dot,
+                   void *ws, size_t ws_bytes, void *stream);
+size_t mlip_block_tangent_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t top_k,
+                                             int32_t d_edge, int32_t d_node, int32_t d_hidden);
+int mlip_block_tangent_vjp(
+    const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms, int64_t n_edges,
+    const float *grad_forces, const float *h_dot, const float *h, const float *s,
+    const float *s_dot, const float *a, const float *a_dot, const float *u, const float *u_dot,
+    const int32_t *z, const int32_t *topk, const float *gate, const int32_t *exp_off,
+    const int32_t *tok_atom, const int32_t *slot, const float *P, const float *P_dot,
+    const float *grad_out, const float *ubar, const float *Q, const float *grad_out_dot,
+    const float *W_e, const float *W_d, const float *W_u, const float *W1, const float *W2,
+    int32_t n_rbf, int32_t d_edge, int32_t d_node, int32_t d_hidden, int32_t n_types,
+    int32_t n_experts, int32_t top_k, float cutoff, float *grad_h_dot, float *d_W_e,
+    float *d_W_d, float *d_W_u, float *d_W1, float *d_W2, float *d_gate, float *d_logits,
+    void *ws, size_t ws_bytes, void *stream);
+int mlip_readout_vjp(const float *w_r, const double *grad_energy, const int32_t *struct_ptr,
+                     int32_t n_atoms, int32_t n_structs, int32_t d_node, float *grad_h_out,
+                     void *stream);
+size_t mlip_readout_grad_workspace_size(int32_t n_atoms, int32_t d_node);
+int mlip_readout_grad(const float *h_out, const float *h_out_dot, const double *grad_energy,
+                      const int32_t *struct_ptr, int32_t n_atoms, int32_t n_structs, int32_t d_node,
+                      float *d_w_r, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Input gradient of one mixture-of-experts layer on its own ([news],

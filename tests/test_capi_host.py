@@ -81,7 +81,7 @@ def test_aggregate_and_moe_reject_bad_args(mlip):
         # grad_out/grad_h/grad_pos, struct_ptr/n_structs, atom_virial/grad_strain, ws
         return L.mlip_block_vjp(f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f,
                                 16, 32, 64, d_hidden, 4, 8, 2, 5.0, f, f, f,
-                                struct_ptr, n_structs, None, grad_strain, f, 1 << 30, None)
+                                struct_ptr, n_structs, None, grad_strain, None, None, f, 1 << 30, None)
     rc = vjp(130, None, 0, None)
     assert "d_hidden" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = vjp(128, None, 0, f)
@@ -141,4 +141,36 @@ def test_profile_api_without_gpu(mlip):
     names = list(mlip.profile_read())
     assert "gemm_expert_up" in names and "edge_vjp" in names and "attn_fwd" in names
     assert "tri_fwd" in names and "tri_vjp_send" in names
-    assert len(names) == 17
+    assert "gemm_wgrad" in names and "edge_tan" in names and "moe_tan" in names
+    assert len(names) == 21
+
+
+def test_training_entry_points_reject_bad_args(mlip):
+    L = mlip._lib
+    f = C.c_void_p(256)
+
+    def jvp(h_dot, s_dot, d_hidden=128, ws_bytes=1 << 30):
+        # graph (3), sizes (2), grad_forces, h_dot, s, z, gate, exp_off, tok_atom, slot, P,
+        # weights (5), dims (7), cutoff, a, s_dot, a_dot, u_dot, P_dot, h_out_dot, ws
+        return L.mlip_block_jvp(f, f, f, 10, 20, f, h_dot, f, f, f, f, f, f, f, f, f, f, f, f,
+                                16, 32, 64, d_hidden, 4, 8, 2, 5.0, f, s_dot, f, f, f, None, f,
+                                ws_bytes, None)
+    assert "h_dot needs s_dot" in _err(mlip, jvp(f, None), mlip.MLIP_ERR_INVALID)
+    assert "d_hidden" in _err(mlip, jvp(None, None, d_hidden=130), mlip.MLIP_ERR_INVALID)
+    assert "workspace" in _err(mlip, jvp(None, None, ws_bytes=16), mlip.MLIP_ERR_INVALID)
+
+    def tan(top_k=2, d_W1=f, ws_bytes=1 << 30):
+        return L.mlip_block_tangent_vjp(f, f, f, 10, 20, f, None, f, f, None, f, f, f, f, f, f, f, f,
+                                        f, f, f, f, f, f, f, None, f, f, f, f, f, 16, 32, 64, 128, 4,
+                                        8, top_k, 5.0, f, f, f, f, d_W1, f, None, None, f, ws_bytes,
+                                        None)
+    assert "top_k" in _err(mlip, tan(top_k=9), mlip.MLIP_ERR_INVALID)
+    assert "null pointer" in _err(mlip, tan(d_W1=None), mlip.MLIP_ERR_INVALID)
+    assert "workspace" in _err(mlip, tan(ws_bytes=16), mlip.MLIP_ERR_INVALID)
+    t = L.mlip_block_tangent_vjp_workspace_size(4096, 16, 4, 384, 2560, 2560)
+    assert t >= 4 * (4096 * 4 * 2560 * 4)          # four token-order [M, H] buffers
+    assert L.mlip_block_jvp_workspace_size(4096, 4, 2560, 2560) >= 2 * 4096 * 4 * 2560 * 4
+    rc = L.mlip_readout_grad(f, None, None, f, 10, 1, 64, f, f, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_readout_vjp(f, None, f, 10, 0, 64, f, None)
+    assert "n_structs" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
