@@ -8,13 +8,17 @@ expert GEMMs, combine), readout, and the input gradient (expert GEMMs
 transposed, aggregation transposed, edge/force part).  Inputs are resident in
 HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S] [--block core|full]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S] [--block core|full|stack|train]
 
 ``--block full`` times the complete block instead (Tri -> MoE0 -> neighbour
 multi-head attention -> MoE1 -> readout, and its input gradient);
 ``--block stack`` times a model of ``--blocks`` complete blocks on one graph
 (element embedding, the blocks, readout, forces and stress through all of
 them), with the block weights drawn on the GPU from a seeded generator.
+``--block train`` times one training step of the block: forward, forces, and
+the parameter gradients of a loss on energies and forces (forward tangents
+and the tangent of the input gradient), for seeded loss upstreams dL/dE and
+dL/dF.
 
 Prints ONE JSON line.  ``--calibrate-copy`` instead runs a plain 1 GiB device
 copy (for scaling hardware byte counters).
@@ -32,6 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "atoms/s per interaction block (fwd+force VJP) on 1 MI355X; % HBM/MFMA roofline"
+TRAIN_METRIC = ("atoms/s per interaction-block training step (fwd, forces, energy+force loss "
+                "parameter gradients) on 1 MI355X")
 MFMA_FP32_PEAK_TFLOPS = 157.3      # MI355X dense FP32 matrix peak
 HBM_PEAK_GBS = 8000.0
 EXPERT_CLASSES = ("gemm_expert_up", "gemm_expert_down", "gemm_expert_vjp_down", "gemm_expert_vjp_up")
@@ -105,13 +111,33 @@ def cpu_baseline(cfg, inp, n_structs: int, full: bool = False):
                       f"{dt:.2f} s"}
 
 
+def cpu_baseline_train(cfg, inp, n_structs: int, Ebar, Fbar):
+    """The float64 autograd oracle of the training gradient on the first n_structs structures."""
+    import numpy as np
+    import torch
+    from oracle import graph as OG
+    from oracle import train as TR
+    n = int(inp["struct_ptr"][n_structs])
+    sub = dict(inp)
+    sub["pos"], sub["z"], sub["h"] = inp["pos"][:n], inp["z"][:n], inp["h"][:n]
+    sub["cell"], sub["struct_ptr"] = inp["cell"][:n_structs], inp["struct_ptr"][:n_structs + 1]
+    t0 = time.perf_counter()
+    gr = OG.radius_graph(sub["pos"], sub["cell"], sub["struct_ptr"], sub["cutoff"])
+    TR.loss_grads(sub, gr, np.asarray(Ebar[:n_structs], np.float64), np.asarray(Fbar[:n], np.float64))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "atoms/s", "cores": int(torch.get_num_threads()), "kind": "oracle",
+            "sample": f"first {n_structs} of {cfg.n_structs} structures ({n} atoms, {gr['src'].size} "
+                      f"edges) of the {cfg.name} workload, float64 PyTorch-autograd oracle of the "
+                      f"training gradient (graph, energy, forces, all parameter gradients) in {dt:.2f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="S")
-    ap.add_argument("--block", choices=("core", "full", "stack"), default="core")
+    ap.add_argument("--block", choices=("core", "full", "stack", "train"), default="core")
     ap.add_argument("--blocks", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-structs", type=int, default=32)
@@ -136,17 +162,33 @@ def main():
     cfg = synth.CONFIGS[args.config]
     full = args.block == "full"
     stack = args.block == "stack"
+    train = args.block == "train"
     if stack:
         shared, _ = synth.make_stack_inputs(cfg, 0)
         params = synth.device_stack_params(cfg, args.blocks, "cuda")
         blk = mlip.Stack(shared, params, device="cuda")
         inputs = shared
+    elif train:
+        inputs = synth.make_inputs(cfg)
+        blk = mlip.Block(inputs, device="cuda", train=True)
+        # seeded loss upstreams: dL/dE ~ N(0,1) per structure, dL/dF ~ N(0,1) per component
+        rng = np.random.default_rng(41)
+        Ebar_h = rng.standard_normal(cfg.n_structs)
+        Fbar_h = rng.standard_normal((cfg.n_atoms, 3)).astype(np.float32)
+        Ebar = torch.tensor(Ebar_h, dtype=torch.float64, device="cuda")
+        Fbar = torch.from_numpy(Fbar_h).to("cuda")
     else:
         inputs = synth.make_full_inputs(cfg) if full else synth.make_inputs(cfg)
         blk = (mlip.FullBlock if full else mlip.Block)(inputs, device="cuda")
+
+    def one_step():
+        blk.step()
+        if train:
+            blk.train_grad(Ebar, Fbar)
+
     log(f"inputs resident for workload {cfg.name}: {cfg.n_atoms} atoms")
     for _ in range(args.warmup):
-        blk.step()
+        one_step()
     torch.cuda.synchronize()
     E = blk.graph["n_edges"]
     log(f"warmup done ({args.warmup} steps, {E} edges)")
@@ -159,7 +201,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        blk.step()
+        one_step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -170,21 +212,33 @@ def main():
     N = cfg.n_atoms
     value = N * args.steps / wall
 
-    # dominant kernel: the expert GEMM class with the largest summed time
-    # (with --block full each class has two launches per step, one per MoE layer)
+    # dominant kernel: the matrix-core class with the largest summed time
+    # (with --block full each class has two launches per step, one per MoE layer).
+    # Algorithmic flops per launch: 2 M Dn H for every expert GEMM (M = N k
+    # tokens); a training step's weight gradients are priced per step:
+    # d W1 and d W2 each 2 terms x 2 M Dn H, d W_u and d W_d each 2 x 2 N De Dn.
     k = cfg.top_k
-    flops = {c: 2.0 * N * k * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES}
-    dom = max(EXPERT_CLASSES, key=lambda c: prof[c]["total_ms"])
+    Mtok = N * k
+    flops = {c: 2.0 * Mtok * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES + ("gemm_expert_tan",)}
+    wgrad_step = 2 * (2 * 2.0 * Mtok * cfg.d_node * cfg.d_hidden) + 2 * (2 * 2.0 * N * cfg.d_edge * cfg.d_node)
+    classes = [c for c in flops if c in prof and prof[c]["launches"]]
+    if "gemm_wgrad" in prof and prof["gemm_wgrad"]["launches"]:
+        classes.append("gemm_wgrad")
+        flops["gemm_wgrad"] = wgrad_step / (prof["gemm_wgrad"]["launches"] / args.steps)
+    dom = max(classes, key=lambda c: prof[c]["total_ms"])
     avg_ms = prof[dom]["total_ms"] / max(prof[dom]["launches"], 1)
     achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
             "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": _traffic(dom),
+            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
+            "traffic": _traffic(dom) if dom in EXPERT_CLASSES else None,
             "avg_launch_ms": round(avg_ms, 4), "flop_per_launch": flops[dom]}
+    if dom == "gemm_wgrad":
+        roof["flop_per_launch_note"] = "mean over the step's weight-gradient launches"
 
     kernel_ms = {name: round(v["total_ms"] / args.steps, 4) for name, v in prof.items() if v["launches"]}
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "atoms/s", "n_gpus": 1,
+        "metric": TRAIN_METRIC if train else METRIC, "value": round(value, 1), "unit": "atoms/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
@@ -194,6 +248,7 @@ def main():
                    "element_types": cfg.n_types,
                    "block": ("Tri + MoE0 + neighbour attention + MoE1" if full else
                              f"{args.blocks} x (Tri + MoE0 + neighbour attention + MoE1)" if stack
+                             else "aggregation + MoE, training gradient" if train
                              else "aggregation + MoE")},
         "edges_per_s": round(E * args.steps / wall, 1),
         "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
@@ -208,7 +263,9 @@ def main():
         # the float64 oracle of a whole stack at these widths is out of reach of
         # a bounded CPU sample; the per-block baseline is in the --block full line
         args.no_cpu_baseline = True
-    if not args.no_cpu_baseline:
+    if train and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(cfg, inputs, 1, Ebar_h, Fbar_h)
+    elif not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, min(args.cpu_structs, cfg.n_structs), full)
     print(json.dumps(out))
 

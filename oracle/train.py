@@ -76,7 +76,7 @@ def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Ten
     for r_ in range(k):
         x_of_atom = torch.as_tensor(topk)[z, r_]
         g_of_atom = gate[z, r_]
-        for x in range(prm["W1"].shape[0]):
+        for x in range(len(prm["W1"])):
             idx = torch.nonzero(x_of_atom == x).flatten()
             if idx.numel() == 0:
                 continue
@@ -88,18 +88,37 @@ def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Ten
     return torch.zeros(nb, dtype=f64).index_add(0, sbat, eps)
 
 
-def loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict[str, np.ndarray]:
-    """E, F and dL/dtheta for L with dL/dE = Ebar [B], dL/dF = Fbar [N, 3]."""
-    prm = {name: _t(inp[name]).requires_grad_(True) for name in PARAMS}
+def loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray,
+               experts=None) -> Dict[str, np.ndarray]:
+    """E, F and dL/dtheta for L with dL/dE = Ebar [B], dL/dF = Fbar [N, 3].
+
+    With ``experts`` (a list of expert indices) the W1 / W2 gradients are
+    taken for those experts only, returned in that order as d_W1 [len, Dn, H]
+    and d_W2 [len, H, Dn] (for very wide layers)."""
+    names = [n for n in PARAMS if experts is None or n not in ("W1", "W2")]
+    prm = {name: _t(inp[name]).requires_grad_(True) for name in names}
+    wrt = [prm[n] for n in names]
+    if experts is not None:
+        for n in ("W1", "W2"):
+            full = _t(inp[n])
+            leaves = {int(x): full[int(x)].clone().requires_grad_(True) for x in experts}
+            prm[n] = [leaves[x] if x in leaves else full[x] for x in range(full.shape[0])]
+            wrt += [leaves[int(x)] for x in experts]
     pos = _t(inp["pos"]).requires_grad_(True)
     E = _energy(inp, graph, prm, pos)
     (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
     F = -dEdx
     L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
-    grads = torch.autograd.grad(L, [prm[n] for n in PARAMS], allow_unused=True)
+    grads = torch.autograd.grad(L, wrt, allow_unused=True)
     out = {"E": E.detach().numpy(), "F": F.detach().numpy()}
-    for n, g in zip(PARAMS, grads):
-        out["d_" + n] = np.zeros(prm[n].shape) if g is None else g.detach().numpy()
+    for n, g, t in zip(names, grads, wrt):
+        out["d_" + n] = np.zeros(t.shape) if g is None else g.detach().numpy()
+    if experts is not None:
+        rest = list(zip(grads[len(names):], wrt[len(names):]))
+        m = len(experts)
+        for q, n in enumerate(("W1", "W2")):
+            out["d_" + n] = np.stack([np.zeros(t.shape) if g is None else g.detach().numpy()
+                                      for g, t in rest[q * m:(q + 1) * m]])
     return out
 
 

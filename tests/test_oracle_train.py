@@ -85,3 +85,14 @@ def test_energy_part_is_first_order_gradient():
     # d/dw_r of sum_b Ebar_b E_b = sum_i Ebar_b(i) h'_i
     ref = (lam[:, None] * f["h2"]).sum(0)
     assert np.max(np.abs(out["d_w_r"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_expert_subset_matches_full():
+    cfg, inp, g, Ebar, Fbar = _setup("tiny")
+    full = TR.loss_grads(inp, g, Ebar, Fbar)
+    sub = TR.loss_grads(inp, g, Ebar, Fbar, experts=[5, 0])
+    for n in ("W1", "W2"):
+        assert np.array_equal(sub["d_" + n], full["d_" + n][[5, 0]])
+    for n in TR.PARAMS:
+        if n not in ("W1", "W2"):
+            assert np.allclose(sub["d_" + n], full["d_" + n], rtol=0, atol=1e-13 * np.abs(full["d_" + n]).max())
