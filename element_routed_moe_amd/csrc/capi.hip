@@ -177,7 +177,7 @@ TanVjpWs carve_tan_vjp(void *base, int64_t N, int64_t T, int64_t k, int64_t De, 
   w.abar_dot = c.take<float>(size_t(N * De));
   w.sbar = c.take<float>(size_t(N * De));
   w.sbar_dot = c.take<float>(size_t(N * De));
-  w.dwe_part = c.take<float>(size_t(int64_t(edge_tan_groups(int(N))) * MLIP_N_RBF * De));
+  w.dwe_part = c.take<float>(size_t(edge_tan_part_floats(int(N), int(De))));
   // split-K scratch of the two dense weight gradients (the larger of the two)
   WgradArgs u, d;
   u.P = d.P = int(N);

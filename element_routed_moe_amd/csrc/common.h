@@ -192,11 +192,12 @@ struct EdgeTanArgs {
   float *out1 = nullptr, *out2 = nullptr;     // [N][De] (out2 optional)
   const float *R1 = nullptr, *R2 = nullptr;   // [N][De] (R1 null: no W_e gradient; R2 optional)
   float *dwe = nullptr;                       // [K][De]
-  float *dwe_part = nullptr;                  // [edge_tan_groups(N)][K][De] scratch
+  float *dwe_part = nullptr;                  // edge_tan_part_floats(N, De) scratch
   int De = 0;
   float rc = 0.f;
 };
 int edge_tan_groups(int n_atoms);
+int64_t edge_tan_part_floats(int n_atoms, int De);   // size of dwe_part
 int launch_edge_tan(const EdgeTanArgs &a, hipStream_t stream);
 int launch_moe_tan(const float *P, const float *P_dot, const float *Q, const float *Q_dot, int M, int H,
                    float *act, float *act_dot, float *D, float *D_dot, float *dg, hipStream_t stream);

@@ -42,14 +42,26 @@ constexpr int K = MLIP_N_RBF;
 // ----------------------------------------------------------------- wgrad --
 // 128 x 128 output tile per 256-thread workgroup (2 x 2 wavefronts of
 // 64 x 64, each 2 x 2 blocks of v_mfma_f32_32x32x2_f32).  K runs over the
-// rows p (tokens or atoms) 16 at a time.  Both operands arrive as rows of
+// rows p (tokens or atoms) WK at a time.  Both operands arrive as rows of
 // the output's M or N extent, so they are staged in LDS as [k][m] / [k][n]
 // (512-byte coalesced row segments per k) and each lane reads its MFMA
 // values one float at a time, consecutive lanes on consecutive addresses.
+// The rows are gathered (token -> atom) along K, so the gather indices of a
+// step are fetched one step before its loads.
+//
+// Tile order: a tile's cost is its group's row count, which varies widely
+// between experts, so tiles are not given to the XCDs in contiguous ranges
+// (whole experts per XCD): workgroup b takes tile b, and the hardware deals
+// consecutive workgroups to the 8 XCDs in turn, so every XCD gets an equal
+// share of every expert.
+#ifndef WGRAD_BK
+#define WGRAD_BK 16
+#endif
 constexpr int WB = 128;
-constexpr int WK = 16;
+constexpr int WK = WGRAD_BK;
 constexpr int WLD = WB + 4;
 constexpr int W_THREADS = 256;
+constexpr int W_LOADS = WK * WB / 4 / W_THREADS;   // float4 per thread per operand and step
 
 __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_split, int64_t rows_per_split,
                                                           float *__restrict__ part) {
@@ -58,8 +70,8 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
   const int mt = (g.Mo + WB - 1) / WB, nt = (g.No + WB - 1) / WB;
   const int G = g.group_off ? g.n_groups : 1;
   const int64_t per_group = int64_t(mt) * nt;
-  const int64_t t = xcd_block(int64_t(G) * per_group * k_split);
-  if (t < 0) return;
+  const int64_t t = blockIdx.x;
+  if (t >= int64_t(G) * per_group * k_split) return;
   // order: split, then group, then n-tile, then m-tile (m fastest)
   const int64_t tiles = int64_t(G) * per_group;
   const int split = int(t / tiles);
@@ -84,34 +96,42 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, kh = (lane >> 5) * 4;
 
-  floatx4 ra[2], rb[2];
-  float sa[2];
-  bool oka[2], okb[2];
+  floatx4 ra[W_LOADS], rb[W_LOADS];
+  float sa[W_LOADS];
+  bool oka[W_LOADS], okb[W_LOADS];
+  int64_t ia[W_LOADS], ib[W_LOADS];   // gather rows of the next step to load (-1: none)
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto fetch_idx = [&](int s) {
+    const int term = s >= steps_term ? 1 : 0;
+    const int k0 = p0 + (s - term * steps_term) * WK;
+#pragma unroll
+    for (int q = 0; q < W_LOADS; ++q) {
+      const int p = k0 + ((tid + W_THREADS * q) >> 5);
+      const bool vp = p < p1;
+      ia[q] = vp ? (g.a_rows ? int64_t(g.a_rows[p]) : int64_t(p)) : -1;
+      ib[q] = vp ? (g.b_rows ? int64_t(g.b_rows[p]) : int64_t(p)) : -1;
+    }
+  };
   auto load = [&](int s) {
     const int term = s >= steps_term ? 1 : 0;
     const int k0 = p0 + (s - term * steps_term) * WK;
     const float *A = term ? g.A1 : g.A0;
     const float *B = term ? g.B1 : g.B0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < W_LOADS; ++q) {
       const int idx = tid + W_THREADS * q;
       const int row = idx >> 5, col = (idx & 31) * 4;
-      const int p = k0 + row;
-      const bool vp = p < p1;
       const int mc = m0 + col, nc = n0 + col;
-      oka[q] = vp && mc < g.Mo;
-      okb[q] = vp && nc < g.No;
-      const int64_t ar = vp ? (g.a_rows ? g.a_rows[p] : p) : 0;
-      const int64_t br = vp ? (g.b_rows ? g.b_rows[p] : p) : 0;
-      ra[q] = *reinterpret_cast<const floatx4 *>(A + (oka[q] ? ar * g.lda + mc : 0));
-      rb[q] = *reinterpret_cast<const floatx4 *>(B + (okb[q] ? br * g.ldb + nc : 0));
-      sa[q] = (oka[q] && g.scale) ? g.scale[p] : 1.f;
+      oka[q] = ia[q] >= 0 && mc < g.Mo;
+      okb[q] = ib[q] >= 0 && nc < g.No;
+      ra[q] = *reinterpret_cast<const floatx4 *>(A + (oka[q] ? ia[q] * g.lda + mc : 0));
+      rb[q] = *reinterpret_cast<const floatx4 *>(B + (okb[q] ? ib[q] * g.ldb + nc : 0));
+      sa[q] = (oka[q] && g.scale) ? g.scale[k0 + row] : 1.f;
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < W_LOADS; ++q) {
       const int idx = tid + W_THREADS * q;
       const int row = idx >> 5, col = (idx & 31) * 4;
       *reinterpret_cast<floatx4 *>(&As[buf][row * WLD + col]) = oka[q] ? ra[q] * sa[q] : zero4;
@@ -128,12 +148,17 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
   if (nsteps > 0) {
+    fetch_idx(0);
     load(0);
+    if (nsteps > 1) fetch_idx(1);
     store(0);
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
       const int cur = s & 1;
-      if (s + 1 < nsteps) load(s + 1);
+      if (s + 1 < nsteps) {
+        load(s + 1);
+        if (s + 2 < nsteps) fetch_idx(s + 2);
+      }
       const float *Ab = As[cur];
       const float *Bb = Bs[cur];
 #pragma unroll
@@ -337,7 +362,20 @@ __global__ void __launch_bounds__(64) edge_tan_kernel(EdgeTanArgs g, int n_group
   }
 }
 
-// dW_e[k][c] = sum over row groups of the partials, in group order.
+// dW_e[k][c] = sum over row groups of the partials, in two fixed-order
+// stages: blocks of DWE_SPAN consecutive groups (coalesced rows of KD floats),
+// then the block sums.
+constexpr int DWE_SPAN = 32;
+__global__ void __launch_bounds__(256) dwe_stage1_kernel(const float *__restrict__ part, int n_groups,
+                                                         int KD, float *__restrict__ part2) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= KD) return;
+  const int q0 = blockIdx.y * DWE_SPAN, q1 = min(n_groups, q0 + DWE_SPAN);
+  float s = 0.f;
+  for (int q = q0; q < q1; ++q) s += part[int64_t(q) * KD + idx];
+  part2[int64_t(blockIdx.y) * KD + idx] = s;
+}
+
 __global__ void __launch_bounds__(256) dwe_sum_kernel(const float *__restrict__ part, int n_groups,
                                                       int KD, float *__restrict__ dwe) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -576,8 +614,7 @@ int launch_wgrad(const WgradArgs &a, float *split_ws, hipStream_t stream) {
     set_error("weight-gradient split workspace missing");
     return MLIP_ERR_INVALID;
   }
-  const int64_t n = tiles * G * ks;
-  const int64_t grid = padded_grid(n);
+  const int64_t grid = tiles * G * ks;
   if (grid > int64_t(0x7fffffff)) {
     set_error("weight-gradient GEMM too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
@@ -594,6 +631,10 @@ int launch_wgrad(const WgradArgs &a, float *split_ws, hipStream_t stream) {
 }
 
 int edge_tan_groups(int n_atoms) { return std::max(1, std::min(n_atoms, ET_MAX_GROUPS)); }
+int64_t edge_tan_part_floats(int n_atoms, int De) {
+  const int n = edge_tan_groups(n_atoms);
+  return (int64_t(n) + cdiv(n, DWE_SPAN)) * K * De;
+}
 
 int launch_edge_tan(const EdgeTanArgs &a, hipStream_t stream) {
   ProfScope ps(K_EDGE_TAN, stream);
@@ -625,7 +666,12 @@ int launch_edge_tan(const EdgeTanArgs &a, hipStream_t stream) {
   MLIP_LAUNCHED();
   if (dw) {
     const int KD = K * a.De;
-    dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(a.dwe_part, n_groups, KD, a.dwe);
+    const int n2 = int(cdiv(n_groups, DWE_SPAN));
+    float *part2 = a.dwe_part + int64_t(n_groups) * KD;
+    dwe_stage1_kernel<<<dim3(unsigned(cdiv(KD, 256)), unsigned(n2)), dim3(256), 0, stream>>>(
+        a.dwe_part, n_groups, KD, part2);
+    MLIP_LAUNCHED();
+    dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(part2, n2, KD, a.dwe);
     MLIP_LAUNCHED();
   }
   return MLIP_OK;
