@@ -40,20 +40,25 @@ def _t(x):
     return torch.as_tensor(np.asarray(x, np.float64), dtype=f64)
 
 
-def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Tensor) -> torch.Tensor:
-    """E_b of one block as a differentiable function of positions and parameters."""
-    rc = B._cutoff(inp)
-    K = prm["W_e"].shape[0]
+def _distances(inp: Dict, graph: Dict, pos: torch.Tensor) -> torch.Tensor:
+    """r_e = |x_src - x_recv + S . C| (cell of the receiver's structure)."""
     recv = torch.as_tensor(graph["recv"], dtype=torch.long)
     src = torch.as_tensor(graph["src"], dtype=torch.long)
-    N = prm["h"].shape[0]
-    # d_e = x_src - x_recv + S . C of the receiver's structure
     sp = np.asarray(inp["struct_ptr"], np.int64)
     sb = np.searchsorted(sp, np.asarray(graph["recv"]), side="right") - 1
     cell = _t(inp["cell"])[torch.as_tensor(sb, dtype=torch.long)]            # [E, 3, 3]
     S = _t(graph["shift"])
     d = pos[src] - pos[recv] + torch.einsum("ea,eab->eb", S, cell)
-    r = torch.sqrt((d * d).sum(1))
+    return torch.sqrt((d * d).sum(1))
+
+
+def _block(inp: Dict, graph: Dict, r: torch.Tensor, prm: Dict, h: torch.Tensor) -> torch.Tensor:
+    """h' of one block (aggregation + MoE) for node features h."""
+    rc = B._cutoff(inp)
+    K = prm["W_e"].shape[0]
+    recv = torch.as_tensor(graph["recv"], dtype=torch.long)
+    src = torch.as_tensor(graph["src"], dtype=torch.long)
+    N = h.shape[0]
     # e = f_c(r) (phi(r) @ W_e)
     mu = torch.arange(K, dtype=f64) * rc / (K - 1)
     gamma = (K - 1) ** 2 / (2.0 * rc * rc)
@@ -61,9 +66,9 @@ def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Ten
     fc = torch.where(r < rc, 0.5 * (torch.cos(np.pi * r / rc) + 1.0), torch.zeros_like(r))
     e = fc[:, None] * (phi @ prm["W_e"])
     # aggregation and up projection
-    s = prm["h"] @ prm["W_d"]
+    s = h @ prm["W_d"]
     a = torch.zeros(N, e.shape[1], dtype=f64).index_add(0, recv, e * s[src])
-    u = prm["h"] + a @ prm["W_u"]
+    u = h + a @ prm["W_u"]
     # static element routing: the chosen experts depend on the logits' order
     # only, the gates are the softmax of the chosen logits
     k = int(inp["top_k"])
@@ -82,10 +87,22 @@ def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Ten
                 continue
             y = torch.nn.functional.silu(u[idx] @ prm["W1"][x]) @ prm["W2"][x]
             h2 = h2.index_add(0, idx, g_of_atom[idx, None] * y)
-    eps = h2 @ prm["w_r"]
-    nb = len(sp) - 1
+    return h2
+
+
+def _readout(inp: Dict, h2: torch.Tensor, w_r: torch.Tensor) -> torch.Tensor:
+    """E_b = sum over structure b of h'_i . w_r."""
+    sp = np.asarray(inp["struct_ptr"], np.int64)
+    N = h2.shape[0]
+    eps = h2 @ w_r
     sbat = torch.as_tensor(np.searchsorted(sp, np.arange(N), side="right") - 1, dtype=torch.long)
-    return torch.zeros(nb, dtype=f64).index_add(0, sbat, eps)
+    return torch.zeros(len(sp) - 1, dtype=f64).index_add(0, sbat, eps)
+
+
+def _energy(inp: Dict, graph: Dict, prm: Dict[str, torch.Tensor], pos: torch.Tensor) -> torch.Tensor:
+    """E_b of one block as a differentiable function of positions and parameters."""
+    r = _distances(inp, graph, pos)
+    return _readout(inp, _block(inp, graph, r, prm, prm["h"]), prm["w_r"])
 
 
 def loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray,
@@ -134,3 +151,65 @@ def loss_value(inp: Dict, Ebar: np.ndarray, Fbar: np.ndarray, **override) -> flo
     gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, f["u"].shape[1]))
     v = B.block_vjp(q, g, f, gup)
     return float(np.dot(f["E"], Ebar) + np.sum(-v["grad_pos"] * Fbar))
+
+
+BLOCK_PARAMS = ("W_e", "W_d", "W_u", "W1", "W2", "logits")
+
+
+def stack_loss_grads(inp: Dict, graph: Dict, blocks, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict:
+    """The same loss through blocks chained on one graph, h^(b+1) = Block_b(h^(b)),
+    h^(0) = inp["h"], readout on the last.  Returns E, F, d_h, d_w_r and
+    ``blocks``: one dict of d_<param> per block."""
+    h0 = _t(inp["h"]).requires_grad_(True)
+    w_r = _t(inp["w_r"]).requires_grad_(True)
+    prms = [{n: _t(b[n]).requires_grad_(True) for n in BLOCK_PARAMS} for b in blocks]
+    pos = _t(inp["pos"]).requires_grad_(True)
+    r = _distances(inp, graph, pos)
+    h = h0
+    for prm in prms:
+        h = _block(inp, graph, r, prm, h)
+    E = _readout(inp, h, w_r)
+    (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
+    F = -dEdx
+    L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
+    wrt = [h0, w_r] + [prm[n] for prm in prms for n in BLOCK_PARAMS]
+    grads = torch.autograd.grad(L, wrt, allow_unused=True)
+    np_ = lambda g, t: np.zeros(t.shape) if g is None else g.detach().numpy()
+    out = {"E": E.detach().numpy(), "F": F.detach().numpy(), "d_h": np_(grads[0], h0),
+           "d_w_r": np_(grads[1], w_r), "blocks": []}
+    q = 2
+    for prm in prms:
+        out["blocks"].append({"d_" + n: np_(grads[q + j], prm[n]) for j, n in enumerate(BLOCK_PARAMS)})
+        q += len(BLOCK_PARAMS)
+    return out
+
+
+def stack_loss_value(inp: Dict, blocks, Ebar: np.ndarray, Fbar: np.ndarray, h=None, w_r=None) -> float:
+    """L of chained blocks with E and F from ``oracle.block`` (no autograd):
+    forwards in order, input gradients in reverse, forces summed over blocks."""
+    from .graph import radius_graph
+    q = dict(inp)
+    if h is not None:
+        q["h"] = h
+    if w_r is not None:
+        q["w_r"] = w_r
+    g = radius_graph(q["pos"], q["cell"], q["struct_ptr"], B._cutoff(q))
+    hcur = np.asarray(q["h"], np.float64)
+    ins, fwds = [], []
+    for b in blocks:
+        qb = dict(q)
+        qb.update(b)
+        qb["h"] = hcur
+        f = B.block_forward(qb, g)
+        ins.append(qb)
+        fwds.append(f)
+        hcur = f["h2"]
+    N = hcur.shape[0]
+    gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, hcur.shape[1])).copy()
+    gpos = np.zeros((N, 3))
+    for qb, f in zip(reversed(ins), reversed(fwds)):
+        v = B.block_vjp(qb, g, f, gup)
+        gpos += v["grad_pos"]
+        gup = v["grad_h"]
+    E = fwds[-1]["E"]
+    return float(np.dot(E, Ebar) + np.sum(-gpos * Fbar))

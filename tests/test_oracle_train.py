@@ -96,3 +96,49 @@ def test_expert_subset_matches_full():
     for n in TR.PARAMS:
         if n not in ("W1", "W2"):
             assert np.allclose(sub["d_" + n], full["d_" + n], rtol=0, atol=1e-13 * np.abs(full["d_" + n]).max())
+
+
+def _two_blocks(name):
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    other = synth.make_inputs(cfg, seed=cfg.seed + 1000)
+    blocks = [{n: inp[n] for n in TR.BLOCK_PARAMS}, {n: other[n] for n in TR.BLOCK_PARAMS}]
+    return cfg, inp, blocks
+
+
+def test_stack_of_one_equals_single_block():
+    cfg, inp, g, Ebar, Fbar = _setup("tiny")
+    one = TR.loss_grads(inp, g, Ebar, Fbar)
+    st = TR.stack_loss_grads(inp, g, [{n: inp[n] for n in TR.BLOCK_PARAMS}], Ebar, Fbar)
+    for n in TR.BLOCK_PARAMS:
+        assert np.allclose(st["blocks"][0]["d_" + n], one["d_" + n], rtol=0,
+                           atol=1e-12 * np.abs(one["d_" + n]).max())
+    assert np.allclose(st["d_h"], one["d_h"], rtol=0, atol=1e-12 * np.abs(one["d_h"]).max())
+
+
+def test_two_block_grads_match_finite_differences():
+    cfg, inp, blocks = _two_blocks("tiny")
+    g = G.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    rng = np.random.default_rng(5)
+    Ebar, Fbar = rng.standard_normal(cfg.n_structs), rng.standard_normal((cfg.n_atoms, 3))
+    out = TR.stack_loss_grads(inp, g, blocks, Ebar, Fbar)
+    step = 1e-5
+    checks = [("h", None), ("w_r", None)] + [(n, b) for b in range(2) for n in ("W_e", "W_d", "W_u", "W1", "W2", "logits")]
+    for name, b in checks:
+        base = np.asarray(inp[name] if b is None else blocks[b][name], np.float64)
+        grad = out["d_" + name] if b is None else out["blocks"][b]["d_" + name]
+        scale = np.max(np.abs(grad))
+        assert scale > 0, (name, b)
+        for idx in _fd_entries(rng, base, grad, 2):
+            vals = []
+            for sgn in (1.0, -1.0):
+                x = base.copy()
+                x[idx] += sgn * step
+                if b is None:
+                    vals.append(TR.stack_loss_value(inp, blocks, Ebar, Fbar, **{name: x}))
+                else:
+                    bl = [dict(bb) for bb in blocks]
+                    bl[b][name] = x
+                    vals.append(TR.stack_loss_value(inp, bl, Ebar, Fbar))
+            fd = (vals[0] - vals[1]) / (2 * step)
+            assert abs(fd - grad[idx]) <= 1e-6 * scale, (name, b, idx, fd, grad[idx])
