@@ -40,6 +40,16 @@ def _t(x):
     return torch.as_tensor(np.asarray(x, np.float64), dtype=f64)
 
 
+def _vectors(inp: Dict, graph: Dict, pos: torch.Tensor) -> torch.Tensor:
+    """d_e = x_src - x_recv + S . C (cell of the receiver's structure)."""
+    recv = torch.as_tensor(graph["recv"], dtype=torch.long)
+    src = torch.as_tensor(graph["src"], dtype=torch.long)
+    sp = np.asarray(inp["struct_ptr"], np.int64)
+    sb = np.searchsorted(sp, np.asarray(graph["recv"]), side="right") - 1
+    cell = _t(inp["cell"])[torch.as_tensor(sb, dtype=torch.long)]            # [E, 3, 3]
+    return pos[src] - pos[recv] + torch.einsum("ea,eab->eb", _t(graph["shift"]), cell)
+
+
 def _distances(inp: Dict, graph: Dict, pos: torch.Tensor) -> torch.Tensor:
     """r_e = |x_src - x_recv + S . C| (cell of the receiver's structure)."""
     recv = torch.as_tensor(graph["recv"], dtype=torch.long)
@@ -213,3 +223,136 @@ def stack_loss_value(inp: Dict, blocks, Ebar: np.ndarray, Fbar: np.ndarray, h=No
         gup = v["grad_h"]
     E = fwds[-1]["E"]
     return float(np.dot(E, Ebar) + np.sum(-gpos * Fbar))
+
+
+# ------------------------------------------------------- complete block ----
+# The readings of oracle.attention and oracle.tri, restated in PyTorch:
+# Tri as the plain sum over ordered pairs of distinct edges of a row, MoE0,
+# neighbour attention with the envelope-weighted softmax, MoE1.
+
+FULL_PARAMS = ("W_s", "W_ang", "W_T", "logits0", "W1_0", "W2_0", "W_qkv", "Wa_e", "W_o",
+               "logits", "W1", "W2")
+
+
+def _basis(r: torch.Tensor, K: int, rc: float):
+    mu = torch.arange(K, dtype=f64) * rc / (K - 1)
+    gamma = (K - 1) ** 2 / (2.0 * rc * rc)
+    phi = torch.exp(-gamma * (r[:, None] - mu) ** 2)
+    fc = torch.where(r < rc, 0.5 * (torch.cos(np.pi * r / rc) + 1.0), torch.zeros_like(r))
+    return phi, fc
+
+
+def _moe(u: torch.Tensor, z: np.ndarray, logits: torch.Tensor, W1, W2, k: int) -> torch.Tensor:
+    """u + sum_r gate_r silu(u W1_x) W2_x with element routing (as in _block)."""
+    topk, _ = B.route(logits.detach().numpy(), k)
+    zt = torch.as_tensor(np.asarray(z, np.int64))
+    T = logits.shape[0]
+    gate = torch.softmax(logits[torch.arange(T)[:, None], torch.as_tensor(topk)], dim=1)
+    out = u
+    for r_ in range(k):
+        x_of_atom = torch.as_tensor(topk)[zt, r_]
+        g_of_atom = gate[zt, r_]
+        for x in range(len(W1)):
+            idx = torch.nonzero(x_of_atom == x).flatten()
+            if idx.numel():
+                y = torch.nn.functional.silu(u[idx] @ W1[x]) @ W2[x]
+                out = out.index_add(0, idx, g_of_atom[idx, None] * y)
+    return out
+
+
+def _row_pairs(recv: np.ndarray):
+    """Ordered pairs (e, e') of distinct edges with the same receiver."""
+    E = recv.size
+    starts = np.searchsorted(recv, np.arange(recv.max() + 2 if E else 1))
+    a, b = [], []
+    for i in range(len(starts) - 1):
+        lo, hi = starts[i], starts[i + 1]
+        if hi - lo < 2:
+            continue
+        ee = np.arange(lo, hi)
+        A, Bm = np.meshgrid(ee, ee, indexing="ij")
+        m = A != Bm
+        a.append(A[m])
+        b.append(Bm[m])
+    if not a:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(a), np.concatenate(b)
+
+
+def _full_block(inp: Dict, graph: Dict, d: torch.Tensor, prm: Dict, h: torch.Tensor) -> torch.Tensor:
+    rc = B._cutoff(inp)
+    recv_np = np.asarray(graph["recv"])
+    recv = torch.as_tensor(recv_np, dtype=torch.long)
+    src = torch.as_tensor(graph["src"], dtype=torch.long)
+    N = h.shape[0]
+    k = int(inp["top_k"])
+    r = torch.sqrt((d * d).sum(1))
+    dhat = d / torch.where(r > 0, r, torch.ones_like(r))[:, None]
+    if "W_ang" in prm:
+        s = h @ prm["W_s"]
+        _, fc = _basis(r, prm["Wa_e"].shape[0], rc)
+        pa, pb = _row_pairs(recv_np)
+        pa_t, pb_t = torch.as_tensor(pa), torch.as_tensor(pb)
+        x = (dhat[pa_t] * dhat[pb_t]).sum(1)
+        L = prm["W_ang"].shape[0]
+        P = [torch.ones_like(x), x]
+        for l in range(1, L - 1):
+            P.append(((2 * l + 1) * x * P[l] - l * P[l - 1]) / (l + 1))
+        G = sum(P[l][:, None] * prm["W_ang"][l][None, :] for l in range(L))
+        term = (fc[pa_t] * fc[pb_t])[:, None] * G * s[src[pa_t]] * s[src[pb_t]]
+        tau = torch.zeros(N, s.shape[1], dtype=f64).index_add(0, recv[pa_t], term)
+        h = h + tau @ prm["W_T"]
+    h0 = _moe(h, inp["z"], prm["logits0"], prm["W1_0"], prm["W2_0"], k)
+    nh = int(inp["n_heads"])
+    Da = prm["W_o"].shape[0]
+    dh = Da // nh
+    qkv = h0 @ prm["W_qkv"]
+    q, kk, v = qkv[:, :Da], qkv[:, Da:2 * Da], qkv[:, 2 * Da:]
+    phi, fc = _basis(r, prm["Wa_e"].shape[0], rc)
+    e = fc[:, None] * (phi @ prm["Wa_e"])
+    sc = (q[recv] * kk[src] * e).reshape(-1, nh, dh).sum(2) / np.sqrt(dh)     # [E, nh]
+    # envelope-weighted softmax per receiver and head (the per-row maximum is
+    # a constant shift: it changes nothing but the range of exp)
+    m = torch.full((N, nh), -np.inf, dtype=f64).scatter_reduce(
+        0, recv[:, None].expand(-1, nh), sc.detach(), reduce="amax", include_self=False)
+    w = torch.exp(sc - m[recv])
+    Z = torch.zeros(N, nh, dtype=f64).index_add(0, recv, fc[:, None] * w)
+    Zr = Z[recv]
+    alpha = torch.where(Zr > 0, fc[:, None] * w / torch.where(Zr > 0, Zr, torch.ones_like(Zr)),
+                        torch.zeros_like(w))
+    A = alpha.repeat_interleave(dh, dim=1)
+    o = torch.zeros(N, Da, dtype=f64).index_add(0, recv, A * v[src] * e)
+    u = h0 + o @ prm["W_o"]
+    return _moe(u, inp["z"], prm["logits"], prm["W1"], prm["W2"], k)
+
+
+def full_loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict[str, np.ndarray]:
+    """E, F and dL/dtheta of L = Ebar . E + Fbar . F through one complete block
+    (Tri when the inputs carry W_ang), for every parameter, w_r and h."""
+    names = [n for n in FULL_PARAMS if n in inp] + ["w_r", "h"]
+    prm = {n: _t(inp[n]).requires_grad_(True) for n in names}
+    pos = _t(inp["pos"]).requires_grad_(True)
+    d = _vectors(inp, graph, pos)
+    E = _readout(inp, _full_block(inp, graph, d, prm, prm["h"]), prm["w_r"])
+    (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
+    F = -dEdx
+    L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
+    grads = torch.autograd.grad(L, [prm[n] for n in names], allow_unused=True)
+    out = {"E": E.detach().numpy(), "F": F.detach().numpy()}
+    for n, g in zip(names, grads):
+        out["d_" + n] = np.zeros(prm[n].shape) if g is None else g.detach().numpy()
+    return out
+
+
+def full_loss_value(inp: Dict, Ebar: np.ndarray, Fbar: np.ndarray, **override) -> float:
+    """L with E and F from oracle.attention's complete block (no autograd)."""
+    from . import attention as A
+    from .graph import radius_graph
+    q = dict(inp)
+    q.update(override)
+    g = radius_graph(q["pos"], q["cell"], q["struct_ptr"], B._cutoff(q))
+    f = A.full_block_forward(q, g)
+    N = f["h2"].shape[0]
+    gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, f["h2"].shape[1]))
+    v = A.full_block_vjp(q, g, f, gup)
+    return float(np.dot(f["E"], Ebar) + np.sum(-v["grad_pos"] * Fbar))

@@ -142,3 +142,38 @@ def test_two_block_grads_match_finite_differences():
                     vals.append(TR.stack_loss_value(inp, bl, Ebar, Fbar))
             fd = (vals[0] - vals[1]) / (2 * step)
             assert abs(fd - grad[idx]) <= 1e-6 * scale, (name, b, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("name", ["tiny", "top1"])
+def test_complete_block_grads_match_finite_differences(name):
+    """The complete block (Tri, MoE0, attention, MoE1): E and F equal
+    oracle.attention's; every parameter's gradient matches central FD of L
+    built from oracle.attention's energies and forces."""
+    from oracle import attention as A
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_full_inputs(cfg)
+    assert "W_ang" in inp
+    g = G.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    rng = np.random.default_rng(7)
+    Ebar, Fbar = rng.standard_normal(cfg.n_structs), rng.standard_normal((cfg.n_atoms, 3))
+    out = TR.full_loss_grads(inp, g, Ebar, Fbar)
+    f = A.full_block_forward(inp, g)
+    v = A.full_block_vjp(inp, g, f, np.broadcast_to(inp["w_r"].astype(np.float64), (cfg.n_atoms, cfg.d_node)))
+    assert np.allclose(out["E"], f["E"], rtol=1e-12, atol=1e-12 * np.abs(f["E"]).max())
+    assert np.allclose(out["F"], -v["grad_pos"], rtol=0, atol=1e-12 * np.abs(v["grad_pos"]).max())
+    step = 1e-5
+    for p in list(TR.FULL_PARAMS) + ["w_r", "h"]:
+        base = np.asarray(inp[p], np.float64)
+        grad = out["d_" + p]
+        scale = np.max(np.abs(grad))
+        if p.startswith("logits") and cfg.top_k == 1:
+            assert scale == 0.0
+            continue
+        assert scale > 0, p
+        for idx in _fd_entries(rng, base, grad, 2):
+            up, dn = base.copy(), base.copy()
+            up[idx] += step
+            dn[idx] -= step
+            fd = (TR.full_loss_value(inp, Ebar, Fbar, **{p: up})
+                  - TR.full_loss_value(inp, Ebar, Fbar, **{p: dn})) / (2 * step)
+            assert abs(fd - grad[idx]) <= 1e-6 * scale, (p, idx, fd, grad[idx])
