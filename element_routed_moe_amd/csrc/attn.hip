@@ -491,6 +491,347 @@ int dispatch(int which, const AttnArgs &a, hipStream_t stream) {
   return MLIP_ERR_UNSUPPORTED;
 }
 
+// ------------------------------------------------------------ tangents ---
+// Training gradient: derivatives of the forward and of the gradient above
+// along a position direction x_dot (with r_dot_e = dhat_e . (x_dot_j - x_dot_i),
+// the same on both directions of an edge) and feature tangents q_dot, k_dot,
+// v_dot (from h0_dot W_qkv).  With e_dot = r_dot de/dr and f_dot = r_dot f_c':
+//   s_dot = sum_t q_dot k e + q k_dot e + q k e_dot        (q scaled by 1/sqrt(dh))
+//   a_dot = a s_dot + f_dot w / Z - a T,   T_i^t = sum_l a_il s_dot_il + f_dot_il w_il / Z_i
+//   o_dot = sum_j a_dot v e + a (v_dot e + v e_dot)
+//         = sum_j (a s_dot + f_dot w / Z) v e + a (v_dot e + v e_dot) - T o   (one pass)
+// and, for the gradient, with beta = <obar, o>_t, gbar = a (<obar, v e>_t - beta):
+//   gbar_dot = a_dot (<obar, v e> - beta) + a (<obar_dot, v e> + <obar, v_dot e + v e_dot> - beta_dot)
+//   qbar_dot_i = sum_j gbar_dot k e + gbar (k_dot e + k e_dot)              (x 1/sqrt(dh))
+//   kbar_dot_j = sum_i gbar_dot q e + gbar (q_dot e + q e_dot)              (x 1/sqrt(dh))
+//   vbar_dot_j = sum_i a_dot obar e + a (obar_dot e + obar e_dot)
+//   ebar = gbar q k + a obar v,  ebar_dot its tangent (written per edge for the
+//   Wa_e gradient).  The position part of the gradient's tangent (a Hessian
+//   product) is not formed: parameter gradients do not need it.
+
+// radial terms of the chunk's edges for the tangents (lane = edge)
+template <int KK>
+__device__ inline void tan_radial(const AttnTanArgs &a, const float4 *geom, const Radial &R, int e, int i,
+                                  float xi0, float xi1, float xi2, float4 (*phi)[KQ], float4 (*dph)[KQ],
+                                  float *fcs, float *fdot, float *rdot, int lane) {
+  const float4 gm = geom[e];
+  const float r = gm.w;
+  const int j = a.src[e];
+  float rd = 0.f;
+  if (r > 0.f)
+    rd = a.x_sign * (gm.x * (a.x_dot[3 * j] - xi0) + gm.y * (a.x_dot[3 * j + 1] - xi1) +
+                     gm.z * (a.x_dot[3 * j + 2] - xi2)) / r;
+  float fc = 0.f, dfc = 0.f;
+  if (r < a.rc) {
+    float sn, cs;
+    __sincosf(r * R.pi_over_rc, &sn, &cs);
+    fc = 0.5f * (cs + 1.f);
+    dfc = -0.5f * R.pi_over_rc * sn;
+  }
+  float ph[KK], dp[KK];
+#pragma unroll
+  for (int k = 0; k < KK; ++k) {
+    const float x = r - float(k) * R.mu_step;
+    const float p = __expf(-R.gamma * x * x);
+    ph[k] = fc * p;
+    dp[k] = dfc * p + fc * (-2.f * R.gamma * x * p);
+  }
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) {
+    phi[lane][kq] = make_float4(ph[4 * kq], ph[4 * kq + 1], ph[4 * kq + 2], ph[4 * kq + 3]);
+    dph[lane][kq] = make_float4(dp[4 * kq], dp[4 * kq + 1], dp[4 * kq + 2], dp[4 * kq + 3]);
+  }
+  fcs[lane] = fc;
+  fdot[lane] = dfc * rd;
+  rdot[lane] = rd;
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_jvp_kernel(AttnTanArgs a) {
+  __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
+  __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(a.n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const Lanes L = lane_map<CPL>(lane, a.nh, a.lph);
+  const int Da = a.Da, nh = a.nh, lph = a.lph;
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(a.rc);
+  const int64_t ld = 3 * int64_t(Da);
+  const float on = L.active ? 1.f : 0.f;
+  const float4 *geom = reinterpret_cast<const float4 *>(a.geom);
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(a.Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float q[CPL], qd[CPL], X[CPL];
+  ldc<CPL>(a.qkv + int64_t(i) * ld + L.c0, q);
+  ldc<CPL>(a.qkv_dot + int64_t(i) * ld + L.c0, qd);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    q[c] *= isq * on;
+    qd[c] *= isq * on;
+    X[c] = 0.f;
+  }
+  const float2 st = reinterpret_cast<const float2 *>(a.stats)[int64_t(i) * nh + L.t];
+  const float m = L.active ? st.x : 0.f;
+  const float invZ = (L.active && st.y > 0.f) ? 1.f / st.y : 0.f;
+  const float xi0 = a.x_dot[3 * i], xi1 = a.x_dot[3 * i + 1], xi2 = a.x_dot[3 * i + 2];
+  float Tsum = 0.f;
+  const int r0 = a.row_ptr[i], r1 = a.row_ptr[i + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      tan_radial<K>(a, geom, R, e0 + lane, i, xi0, xi1, xi2, phi, dph, fcs, fdot, rdot, lane);
+      jj[lane] = a.src[e0 + lane];
+    }
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      float kj[CPL], vj[CPL], kd[CPL], vd[CPL];
+      const int64_t j = jj[me];
+      ldc<CPL>(a.qkv + j * ld + Da + L.c0, kj);
+      ldc<CPL>(a.qkv + j * ld + 2 * Da + L.c0, vj);
+      ldc<CPL>(a.qkv_dot + j * ld + Da + L.c0, kd);
+      ldc<CPL>(a.qkv_dot + j * ld + 2 * Da + L.c0, vd);
+      float e[CPL], de[CPL];
+      basis_map<CPL>(phi[me], w, e);
+      basis_map<CPL>(dph[me], w, de);
+      const float rd = rdot[me];
+      float ps = 0.f, psd = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        de[c] *= rd;
+        ps += q[c] * kj[c] * e[c];
+        psd += qd[c] * kj[c] * e[c] + q[c] * kd[c] * e[c] + q[c] * kj[c] * de[c];
+      }
+      const float s = head_sum(ps, lph);
+      const float sd = head_sum(psd, lph);
+      const float wt = __expf(s - m);
+      const float al = fcs[me] * wt * invZ;
+      const float fw = fdot[me] * wt * invZ;
+      Tsum += al * sd + fw;
+      const float cf = al * sd + fw;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) X[c] += cf * vj[c] * e[c] + al * (vd[c] * e[c] + vj[c] * de[c]);
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+    float oo[CPL], od[CPL];
+    ldc<CPL>(a.o + int64_t(i) * Da + L.c0, oo);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) od[c] = X[c] - Tsum * oo[c];
+    stc<CPL>(a.o_dot + int64_t(i) * Da + L.c0, od);
+    if (lane == L.t * lph) a.tstat[int64_t(i) * nh + L.t] = Tsum;
+  }
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
+  __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
+  __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(a.n_atoms);
+  if (blk < 0) return;
+  const int i = int(blk);
+  const Lanes L = lane_map<CPL>(lane, a.nh, a.lph);
+  const int Da = a.Da, nh = a.nh, lph = a.lph;
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(a.rc);
+  const int64_t ld = 3 * int64_t(Da);
+  const float on = L.active ? 1.f : 0.f;
+  const float4 *geom = reinterpret_cast<const float4 *>(a.geom);
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(a.Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float q[CPL], qd[CPL], ob[CPL], obd[CPL], qbd[CPL];
+  float bp = 0.f, bpd = 0.f;
+  {
+    float oo[CPL], od[CPL];
+    ldc<CPL>(a.qkv + int64_t(i) * ld + L.c0, q);
+    ldc<CPL>(a.qkv_dot + int64_t(i) * ld + L.c0, qd);
+    ldc<CPL>(a.obar + int64_t(i) * Da + L.c0, ob);
+    ldc<CPL>(a.obar_dot + int64_t(i) * Da + L.c0, obd);
+    ldc<CPL>(a.o + int64_t(i) * Da + L.c0, oo);
+    ldc<CPL>(a.o_dot + int64_t(i) * Da + L.c0, od);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      q[c] *= isq * on;
+      qd[c] *= isq * on;
+      ob[c] *= on;
+      obd[c] *= on;
+      bp += ob[c] * oo[c];
+      bpd += obd[c] * oo[c] + ob[c] * od[c];
+      qbd[c] = 0.f;
+    }
+  }
+  const float beta = head_sum(bp, lph);
+  const float betad = head_sum(bpd, lph);
+  const float2 st = reinterpret_cast<const float2 *>(a.stats)[int64_t(i) * nh + L.t];
+  const float m = L.active ? st.x : 0.f;
+  const float invZ = (L.active && st.y > 0.f) ? 1.f / st.y : 0.f;
+  const float T = L.active ? a.tstat[int64_t(i) * nh + L.t] : 0.f;
+  const bool head_lead = L.active && lane == L.t * lph;
+  const float xi0 = a.x_dot[3 * i], xi1 = a.x_dot[3 * i + 1], xi2 = a.x_dot[3 * i + 2];
+  const int r0 = a.row_ptr[i], r1 = a.row_ptr[i + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      tan_radial<K>(a, geom, R, e0 + lane, i, xi0, xi1, xi2, phi, dph, fcs, fdot, rdot, lane);
+      jj[lane] = a.src[e0 + lane];
+    }
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      float kj[CPL], vj[CPL], kd[CPL], vd[CPL];
+      const int64_t j = jj[me];
+      ldc<CPL>(a.qkv + j * ld + Da + L.c0, kj);
+      ldc<CPL>(a.qkv + j * ld + 2 * Da + L.c0, vj);
+      ldc<CPL>(a.qkv_dot + j * ld + Da + L.c0, kd);
+      ldc<CPL>(a.qkv_dot + j * ld + 2 * Da + L.c0, vd);
+      float e[CPL], de[CPL];
+      basis_map<CPL>(phi[me], w, e);
+      basis_map<CPL>(dph[me], w, de);
+      const float rd = rdot[me];
+      float ps = 0.f, psd = 0.f, pa = 0.f, pad = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        de[c] *= rd;
+        ps += q[c] * kj[c] * e[c];
+        psd += qd[c] * kj[c] * e[c] + q[c] * kd[c] * e[c] + q[c] * kj[c] * de[c];
+        pa += ob[c] * vj[c] * e[c];
+        pad += obd[c] * vj[c] * e[c] + ob[c] * vd[c] * e[c] + ob[c] * vj[c] * de[c];
+      }
+      const float s = head_sum(ps, lph);
+      const float sd = head_sum(psd, lph);
+      const float ab = head_sum(pa, lph);
+      const float abd = head_sum(pad, lph);
+      const float wt = __expf(s - m);
+      const float al = fcs[me] * wt * invZ;
+      const float ald = al * sd + fdot[me] * wt * invZ - al * T;
+      const float diff = ab - beta;
+      const float g = al * diff;
+      const float gd = ald * diff + al * (abd - betad);
+      float eb[CPL], ebd[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        qbd[c] += gd * kj[c] * e[c] + g * (kd[c] * e[c] + kj[c] * de[c]);
+        eb[c] = g * q[c] * kj[c] + al * ob[c] * vj[c];
+        ebd[c] = gd * q[c] * kj[c] + g * (qd[c] * kj[c] + q[c] * kd[c]) + ald * ob[c] * vj[c] +
+                 al * (obd[c] * vj[c] + ob[c] * vd[c]);
+      }
+      const int64_t eg = int64_t(e0 + me);
+      if (L.active) {
+        stc<CPL>(a.ebar + eg * Da + L.c0, eb);
+        stc<CPL>(a.ebar_dot + eg * Da + L.c0, ebd);
+      }
+      if (head_lead) {
+        a.edge_g[eg * nh + L.t] = g;
+        a.edge_gd[eg * nh + L.t] = gd;
+        a.edge_a[eg * nh + L.t] = al;
+        a.edge_ad[eg * nh + L.t] = ald;
+      }
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) qbd[c] *= isq;
+    stc<CPL>(a.qkv_bar_dot + int64_t(i) * ld + L.c0, qbd);
+  }
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(64) attn_tvjp_send_kernel(AttnTanArgs a) {
+  __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
+  __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
+  __shared__ int jj[CHUNK], rr[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(a.n_atoms);
+  if (blk < 0) return;
+  const int j = int(blk);
+  const Lanes L = lane_map<CPL>(lane, a.nh, a.lph);
+  const int Da = a.Da, nh = a.nh, lph = a.lph;
+  const float isq = 1.f / sqrtf(float(lph * CPL));
+  const Radial R = make_radial(a.rc);
+  const int64_t ld = 3 * int64_t(Da);
+  const float4 *geom = reinterpret_cast<const float4 *>(a.geom);
+
+  float w[K][CPL];
+#pragma unroll
+  for (int k = 0; k < K; ++k) ldc<CPL>(a.Wa_e + int64_t(k) * Da + L.c0, w[k]);
+  float kbd[CPL], vbd[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) kbd[c] = vbd[c] = 0.f;
+  const float xj0 = a.x_dot[3 * j], xj1 = a.x_dot[3 * j + 1], xj2 = a.x_dot[3 * j + 2];
+  const int r0 = a.row_ptr[j], r1 = a.row_ptr[j + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) {
+      tan_radial<K>(a, geom, R, e0 + lane, j, xj0, xj1, xj2, phi, dph, fcs, fdot, rdot, lane);
+      jj[lane] = a.src[e0 + lane];
+      rr[lane] = a.rev[e0 + lane];
+    }
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      // edge j <- i; its reverse i <- j carries the receiver-pass values
+      const int64_t ii = jj[me];
+      const int64_t re = rr[me];
+      float qi[CPL], qdi[CPL], oi[CPL], odi[CPL];
+      ldc<CPL>(a.qkv + ii * ld + L.c0, qi);
+      ldc<CPL>(a.qkv_dot + ii * ld + L.c0, qdi);
+      ldc<CPL>(a.obar + ii * Da + L.c0, oi);
+      ldc<CPL>(a.obar_dot + ii * Da + L.c0, odi);
+      const float g = a.edge_g[re * nh + L.t], gd = a.edge_gd[re * nh + L.t];
+      const float al = a.edge_a[re * nh + L.t], ald = a.edge_ad[re * nh + L.t];
+      float e[CPL], de[CPL];
+      basis_map<CPL>(phi[me], w, e);
+      basis_map<CPL>(dph[me], w, de);
+      const float rd = rdot[me];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        de[c] *= rd;
+        kbd[c] += gd * qi[c] * e[c] + g * (qdi[c] * e[c] + qi[c] * de[c]);
+        vbd[c] += ald * oi[c] * e[c] + al * (odi[c] * e[c] + oi[c] * de[c]);
+      }
+    }
+    __syncthreads();
+  }
+  if (L.active) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) kbd[c] *= isq;
+    stc<CPL>(a.qkv_bar_dot + int64_t(j) * ld + Da + L.c0, kbd);
+    stc<CPL>(a.qkv_bar_dot + int64_t(j) * ld + 2 * Da + L.c0, vbd);
+  }
+}
+
+template <int CPL>
+int launch_tan(int which, const AttnTanArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(padded_grid(a.n_atoms))), block(64);
+  if (which == 0) attn_jvp_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  else if (which == 1) attn_tvjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  else attn_tvjp_send_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+int dispatch_tan(int which, const AttnTanArgs &a, hipStream_t stream) {
+  switch (a.cpl) {
+    case 1: return launch_tan<1>(which, a, stream);
+    case 2: return launch_tan<2>(which, a, stream);
+    case 3: return launch_tan<3>(which, a, stream);
+    case 4: return launch_tan<4>(which, a, stream);
+    case 6: return launch_tan<6>(which, a, stream);
+    case 8: return launch_tan<8>(which, a, stream);
+    default: break;
+  }
+  set_error("no attention lane layout for %d channels per lane", a.cpl);
+  return MLIP_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 int attn_lane_layout(int Da, int nh, int *cpl, int *lph) {
@@ -522,6 +863,19 @@ int launch_attn_vjp(const AttnArgs &a, hipStream_t stream) {
   }
   ProfScope ps(K_ATTN_VJP_SEND, stream);
   return dispatch(2, a, stream);
+}
+
+int launch_attn_jvp(const AttnTanArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  ProfScope ps(K_ATTN_TAN, stream);
+  return dispatch_tan(0, a, stream);
+}
+
+int launch_attn_tvjp(const AttnTanArgs &a, hipStream_t stream) {
+  if (a.n_atoms <= 0) return MLIP_OK;
+  ProfScope ps(K_ATTN_TAN, stream);
+  if (int rc = dispatch_tan(1, a, stream)) return rc;
+  return dispatch_tan(2, a, stream);
 }
 
 }  // namespace mlip

@@ -155,40 +155,6 @@ JvpWs carve_jvp(void *base, int64_t N, int64_t k, int64_t Dn, int64_t H, size_t 
   return w;
 }
 
-struct TanVjpWs {
-  float *D_dot, *act, *act_dot, *D, *dg, *gt, *U_dot, *ubar_dot, *abar, *abar_dot, *sbar,
-      *sbar_dot, *dwe_part, *split;
-  double *G;
-};
-TanVjpWs carve_tan_vjp(void *base, int64_t N, int64_t T, int64_t k, int64_t De, int64_t Dn,
-                       int64_t H, size_t *bytes) {
-  Carver c(base);
-  TanVjpWs w;
-  const int64_t M = N * k;
-  w.D_dot = c.take<float>(size_t(M * H));
-  w.act = c.take<float>(size_t(M * H));
-  w.act_dot = c.take<float>(size_t(M * H));
-  w.D = c.take<float>(size_t(M * H));
-  w.dg = c.take<float>(size_t(std::max<int64_t>(M, 1)));
-  w.gt = c.take<float>(size_t(std::max<int64_t>(M, 1)));
-  w.U_dot = c.take<float>(size_t(M * Dn));
-  w.ubar_dot = c.take<float>(size_t(N * Dn));
-  w.abar = c.take<float>(size_t(N * De));
-  w.abar_dot = c.take<float>(size_t(N * De));
-  w.sbar = c.take<float>(size_t(N * De));
-  w.sbar_dot = c.take<float>(size_t(N * De));
-  w.dwe_part = c.take<float>(size_t(edge_tan_part_floats(int(N), int(De))));
-  // split-K scratch of the two dense weight gradients (the larger of the two)
-  WgradArgs u, d;
-  u.P = d.P = int(N);
-  u.Mo = int(De); u.No = int(Dn);
-  d.Mo = int(Dn); d.No = int(De);
-  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(u), wgrad_split_floats(d))));
-  w.G = c.take<double>(size_t(T * k));
-  if (bytes) *bytes = c.bytes();
-  return w;
-}
-
 // dL/du = g + sum_r gate * ((g[tok] @ W2_x^T) * silu'(P)) @ W1_x^T, gathered back
 // by slot in rank order (two grouped GEMMs and the combine).
 // With q_save, the product g[tok] @ W2^T is also kept (before the silu' factor).
@@ -214,6 +180,154 @@ int moe_vjp_core(const float *grad_out, const int32_t *z, const float *gate,
   g2.M = M; g2.N = Dn; g2.K = H;
   if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_VJP_UP, stream)) return rc;
   return moe_combine(grad_out, Utok, z, gate, slot, N, T, k, Dn, grad_in, stream);
+}
+
+// Forward tangent of h' = u + MoE(u): P_dot = u_dot[tok] W1_x (and act_dot =
+// silu'(P) P_dot), h_out_dot = u_dot + sum_r gate * act_dot W2_x (when asked).
+int moe_jvp_core(const float *u_dot, const int32_t *z, const float *gate, const int32_t *exp_off,
+                 const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W1,
+                 const float *W2, int N, int T, int X, int k, int Dn, int H, float *P_dot,
+                 float *act_dot, float *Y_dot, float *h_out_dot, hipStream_t stream) {
+  const int M = N * k;
+  GemmArgs g3;  // P_dot = u_dot[tok] @ W1[x], act_dot = silu'(P) * P_dot
+  g3.A = u_dot; g3.lda = Dn; g3.a_rows = tok_atom;
+  g3.B = W1; g3.ldb = H; g3.b_group_stride = int64_t(Dn) * H;
+  g3.C = P_dot; g3.C2 = act_dot; g3.ldc = H; g3.R = P; g3.ldr = H;
+  g3.group_off = exp_off; g3.n_groups = X;
+  g3.M = M; g3.N = H; g3.K = Dn;
+  if (int rc = launch_gemm(g3, false, EPI_TAN, K_GEMM_EXPERT_TAN, stream)) return rc;
+  if (!h_out_dot) return MLIP_OK;
+  GemmArgs g4;  // Y_dot = act_dot @ W2[x]
+  g4.A = act_dot; g4.lda = H;
+  g4.B = W2; g4.ldb = Dn; g4.b_group_stride = int64_t(H) * Dn;
+  g4.C = Y_dot; g4.ldc = Dn;
+  g4.group_off = exp_off; g4.n_groups = X;
+  g4.M = M; g4.N = Dn; g4.K = H;
+  if (int rc = launch_gemm(g4, false, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+  return moe_combine(u_dot, Y_dot, z, gate, slot, N, T, k, Dn, h_out_dot, stream);
+}
+
+struct MoeTanWs {
+  float *D_dot, *act, *act_dot, *D, *dg, *gt, *U_dot;
+  double *G;
+};
+MoeTanWs carve_moe_tan(Carver &c, int64_t N, int64_t T, int64_t k, int64_t Dn, int64_t H) {
+  MoeTanWs w;
+  const int64_t M = N * k;
+  w.D_dot = c.take<float>(size_t(M * H));
+  w.act = c.take<float>(size_t(M * H));
+  w.act_dot = c.take<float>(size_t(M * H));
+  w.D = c.take<float>(size_t(M * H));
+  w.dg = c.take<float>(size_t(std::max<int64_t>(M, 1)));
+  w.gt = c.take<float>(size_t(std::max<int64_t>(M, 1)));
+  w.U_dot = c.take<float>(size_t(M * Dn));
+  w.G = c.take<double>(size_t(T * k));
+  return w;
+}
+
+// Tangent of the MoE layer's gradient along (u_dot, grad_out_dot): grad_in_dot
+// = g_dot + sum_r gate * D_dot W1_x^T and the weight, gate and logit gradients
+// (D = silu'(P) Q, Q = g[tok] W2^T kept by the primal gradient).
+int moe_tvjp_core(const int32_t *z, const int32_t *topk, const float *gate, const int32_t *exp_off,
+                  const int32_t *tok_atom, const int32_t *slot, const float *P, const float *P_dot,
+                  const float *W1, const float *W2, int N, int T, int X, int k, int Dn, int H,
+                  const float *u, const float *u_dot, const float *grad_out, const float *Q,
+                  const float *grad_out_dot, const MoeTanWs &w, float *grad_in_dot, float *d_W1,
+                  float *d_W2, float *d_gate, float *d_logits, hipStream_t stream) {
+  const int M = N * k;
+  if (N > 0) {
+    if (grad_out_dot) {
+      GemmArgs g;  // Q_dot = g_dot[tok] @ W2^T (into D_dot, turned into D_dot in place below)
+      g.A = grad_out_dot; g.lda = Dn; g.a_rows = tok_atom;
+      g.B = W2; g.ldb = Dn; g.b_group_stride = int64_t(H) * Dn;
+      g.C = w.D_dot; g.ldc = H;
+      g.group_off = exp_off; g.n_groups = X;
+      g.M = M; g.N = H; g.K = Dn;
+      if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+    }
+    if (int rc = launch_moe_tan(P, P_dot, Q, grad_out_dot ? w.D_dot : nullptr, M, H, w.act, w.act_dot,
+                                w.D, w.D_dot, w.dg, stream))
+      return rc;
+    if (grad_in_dot) {
+      GemmArgs g2;  // U_dot = D_dot @ W1^T; grad_in_dot = g_dot + sum_r gate * U_dot[slot]
+      g2.A = w.D_dot; g2.lda = H;
+      g2.B = W1; g2.ldb = H; g2.b_group_stride = int64_t(Dn) * H;
+      g2.C = w.U_dot; g2.ldc = Dn;
+      g2.group_off = exp_off; g2.n_groups = X;
+      g2.M = M; g2.N = Dn; g2.K = H;
+      if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
+      if (int rc = moe_combine(grad_out_dot, w.U_dot, z, gate, slot, N, T, k, Dn, grad_in_dot, stream))
+        return rc;
+    }
+  }
+  if (int rc = launch_token_gate(z, gate, slot, N, T, k, w.gt, stream)) return rc;
+  {
+    WgradArgs q;  // d W1_x = sum_t gate_t (u_dot[i]^T D_t + u[i]^T D_dot_t)
+    q.A0 = u_dot; q.B0 = w.D; q.A1 = u; q.B1 = w.D_dot; q.lda = Dn; q.ldb = H;
+    q.a_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off; q.n_groups = X;
+    q.P = M; q.Mo = Dn; q.No = H; q.C = d_W1;
+    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
+  }
+  {
+    WgradArgs q;  // d W2_x = sum_t gate_t (act_dot_t^T g[i] + act_t^T g_dot[i])
+    q.A0 = w.act_dot; q.B0 = grad_out;
+    if (grad_out_dot) { q.A1 = w.act; q.B1 = grad_out_dot; }
+    q.lda = H; q.ldb = Dn; q.b_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off;
+    q.n_groups = X; q.P = M; q.Mo = H; q.No = Dn; q.C = d_W2;
+    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
+  }
+  return launch_gate_grad(w.dg, z, topk, gate, exp_off, tok_atom, T, X, k, w.G, d_gate, d_logits, stream);
+}
+
+struct TanVjpWs {
+  float *ubar_dot, *abar, *abar_dot, *sbar, *sbar_dot, *dwe_part, *split;
+};
+TanVjpWs carve_tan_vjp(void *base, int64_t N, int64_t T, int64_t k, int64_t De, int64_t Dn,
+                       int64_t H, size_t *bytes, MoeTanWs *moe) {
+  Carver c(base);
+  TanVjpWs w;
+  MoeTanWs m = carve_moe_tan(c, N, T, k, Dn, H);
+  if (moe) *moe = m;
+  w.ubar_dot = c.take<float>(size_t(N * Dn));
+  w.abar = c.take<float>(size_t(N * De));
+  w.abar_dot = c.take<float>(size_t(N * De));
+  w.sbar = c.take<float>(size_t(N * De));
+  w.sbar_dot = c.take<float>(size_t(N * De));
+  w.dwe_part = c.take<float>(size_t(edge_tan_part_floats(int(N), int(De))));
+  // split-K scratch of the two dense weight gradients (the larger of the two)
+  WgradArgs u, d;
+  u.P = d.P = int(N);
+  u.Mo = int(De); u.No = int(Dn);
+  d.Mo = int(Dn); d.No = int(De);
+  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(u), wgrad_split_floats(d))));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+struct AttnTanWs {
+  float *obar, *obar_dot, *qkv_bar_dot, *eg, *egd, *ea, *ead, *ebar, *ebar_dot, *part, *split;
+};
+AttnTanWs carve_attn_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t Da, int64_t nh,
+                         size_t *bytes) {
+  Carver c(base);
+  AttnTanWs w;
+  w.obar = c.take<float>(size_t(N * Da));
+  w.obar_dot = c.take<float>(size_t(N * Da));
+  w.qkv_bar_dot = c.take<float>(size_t(N * 3 * Da));
+  w.eg = c.take<float>(size_t(E * nh));
+  w.egd = c.take<float>(size_t(E * nh));
+  w.ea = c.take<float>(size_t(E * nh));
+  w.ead = c.take<float>(size_t(E * nh));
+  w.ebar = c.take<float>(size_t(E * Da));
+  w.ebar_dot = c.take<float>(size_t(E * Da));
+  w.part = c.take<float>(size_t(edge_tan_part_floats(int(N), int(Da))));
+  WgradArgs a, b;
+  a.P = b.P = int(N);
+  a.Mo = int(Dn); a.No = int(3 * Da);
+  b.Mo = int(Da); b.No = int(Dn);
+  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(a), wgrad_split_floats(b))));
+  if (bytes) *bytes = c.bytes();
+  return w;
 }
 
 }  // namespace
@@ -428,7 +542,7 @@ int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
                  const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W1,
                  const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
                  int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
-                 float *grad_in, void *ws, size_t ws_bytes, void *stream_) {
+                 float *grad_in, float *q_out, void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
   MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
@@ -447,9 +561,10 @@ int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
   if (int rc = check_ws(ws, ws_bytes, mlip_moe_vjp_workspace_size(n_atoms, top_k, d_node, d_hidden)))
     return rc;
   if (n_atoms == 0) return MLIP_OK;
+  MLIP_CHECK_ARG(aligned(q_out, 16), "float arrays must be 16-byte aligned");
   MoeVjpWs w = carve_moe_vjp(ws, n_atoms, top_k, d_node, d_hidden, nullptr);
   return moe_vjp_core(grad_out, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms, n_types,
-                      n_experts, top_k, d_node, d_hidden, w.Q, w.Utok, grad_in, stream);
+                      n_experts, top_k, d_node, d_hidden, w.Q, w.Utok, grad_in, stream, q_out);
 }
 
 // ---------------------------------------------------------- attention ----
@@ -517,11 +632,12 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                        const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                        int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
                        float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                       float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
-                       size_t ws_bytes, void *stream_) {
+                       float *atom_virial, double *grad_strain, int32_t accumulate,
+                       float *qkv_bar_out, void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(aligned(qkv_bar_out, 16), "float arrays must be 16-byte aligned");
   int cpl = 0, lph = 0;
   if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
   MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain,
@@ -545,6 +661,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   }
   AttnVjpWs w = carve_attn_vjp(ws, n_atoms, n_edges, d_attn, n_heads, nullptr);
   float *vir = atom_virial ? atom_virial : w.virial;
+  if (qkv_bar_out) w.qkv_bar = qkv_bar_out;
   GemmArgs g1;  // obar = ubar @ W_o^T
   g1.A = grad_u; g1.lda = d_node; g1.B = W_o; g1.ldb = d_node; g1.C = w.obar; g1.ldc = d_attn;
   g1.M = n_atoms; g1.N = d_attn; g1.K = d_node;
@@ -739,23 +856,8 @@ int mlip_block_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom
   g2.A = a_dot; g2.lda = d_edge; g2.B = W_u; g2.ldb = d_node; g2.C = u_dot; g2.ldc = d_node;
   g2.R = h_dot; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_edge;
   if (int rc = launch_gemm(g2, false, h_dot ? EPI_RESID : EPI_STORE, K_GEMM_DENSE, stream)) return rc;
-  GemmArgs g3;  // P_dot = u_dot[tok] @ W1[x], act_dot = silu'(P) * P_dot
-  g3.A = u_dot; g3.lda = d_node; g3.a_rows = tok_atom;
-  g3.B = W1; g3.ldb = d_hidden; g3.b_group_stride = int64_t(d_node) * d_hidden;
-  g3.C = P_dot; g3.C2 = w.act_dot; g3.ldc = d_hidden; g3.R = P; g3.ldr = d_hidden;
-  g3.group_off = exp_off; g3.n_groups = n_experts;
-  g3.M = M; g3.N = d_hidden; g3.K = d_node;
-  if (int rc = launch_gemm(g3, false, EPI_TAN, K_GEMM_EXPERT_TAN, stream)) return rc;
-  if (!h_out_dot) return MLIP_OK;
-  GemmArgs g4;  // Y_dot = act_dot @ W2[x]
-  g4.A = w.act_dot; g4.lda = d_hidden;
-  g4.B = W2; g4.ldb = d_node; g4.b_group_stride = int64_t(d_hidden) * d_node;
-  g4.C = w.Y_dot; g4.ldc = d_node;
-  g4.group_off = exp_off; g4.n_groups = n_experts;
-  g4.M = M; g4.N = d_node; g4.K = d_hidden;
-  if (int rc = launch_gemm(g4, false, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
-  return moe_combine(u_dot, w.Y_dot, z, gate, slot, n_atoms, n_types, top_k, d_node, h_out_dot,
-                     stream);
+  return moe_jvp_core(u_dot, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms, n_types, n_experts,
+                      top_k, d_node, d_hidden, P_dot, w.act_dot, w.Y_dot, h_out_dot, stream);
 }
 
 // ------------------------------------- training gradient: tangent of VJP ---
@@ -763,7 +865,7 @@ size_t mlip_block_tangent_vjp_workspace_size(int32_t n_atoms, int32_t n_types, i
                                              int32_t d_edge, int32_t d_node, int32_t d_hidden) {
   size_t b = 0;
   carve_tan_vjp(nullptr, std::max(n_atoms, 0), std::max(n_types, 1), std::max(top_k, 1),
-                std::max(d_edge, 0), std::max(d_node, 0), std::max(d_hidden, 0), &b);
+                std::max(d_edge, 0), std::max(d_node, 0), std::max(d_hidden, 0), &b, nullptr);
   return b;
 }
 
@@ -803,34 +905,17 @@ int mlip_block_tangent_vjp(
   if (int rc = check_ws(ws, ws_bytes, mlip_block_tangent_vjp_workspace_size(
                                           n_atoms, n_types, top_k, d_edge, d_node, d_hidden)))
     return rc;
-  TanVjpWs w = carve_tan_vjp(ws, n_atoms, n_types, top_k, d_edge, d_node, d_hidden, nullptr);
-  const int N = n_atoms, M = n_atoms * top_k;
-  const int De = d_edge, Dn = d_node, H = d_hidden, X = n_experts, k = top_k;
+  MoeTanWs mw;
+  TanVjpWs w = carve_tan_vjp(ws, n_atoms, n_types, top_k, d_edge, d_node, d_hidden, nullptr, &mw);
+  const int N = n_atoms;
+  const int De = d_edge, Dn = d_node;
 
+  // MoE: gradient tangent into ubar_dot, W1 / W2 / gate / logit gradients
+  if (int rc = moe_tvjp_core(z, topk, gate, exp_off, tok_atom, slot, P, P_dot, W1, W2, N, n_types,
+                             n_experts, top_k, Dn, d_hidden, u, u_dot, grad_out, Q, grad_out_dot, mw,
+                             w.ubar_dot, d_W1, d_W2, d_gate, d_logits, stream))
+    return rc;
   if (N > 0) {
-    // ---- MoE: Q_dot = g_dot[tok] @ W2^T, then the token-wise tangents ----
-    if (grad_out_dot) {
-      GemmArgs g;
-      g.A = grad_out_dot; g.lda = Dn; g.a_rows = tok_atom;
-      g.B = W2; g.ldb = Dn; g.b_group_stride = int64_t(H) * Dn;
-      g.C = w.D_dot; g.ldc = H;
-      g.group_off = exp_off; g.n_groups = X;
-      g.M = M; g.N = H; g.K = Dn;
-      if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
-    }
-    if (int rc = launch_moe_tan(P, P_dot, Q, grad_out_dot ? w.D_dot : nullptr, M, H, w.act, w.act_dot,
-                                w.D, w.D_dot, w.dg, stream))
-      return rc;
-    GemmArgs g2;  // U_dot = D_dot @ W1^T; ubar_dot = g_dot + sum_r gate * U_dot[slot]
-    g2.A = w.D_dot; g2.lda = H;
-    g2.B = W1; g2.ldb = H; g2.b_group_stride = int64_t(Dn) * H;
-    g2.C = w.U_dot; g2.ldc = Dn;
-    g2.group_off = exp_off; g2.n_groups = X;
-    g2.M = M; g2.N = Dn; g2.K = H;
-    if (int rc = launch_gemm(g2, true, EPI_STORE, K_GEMM_EXPERT_TAN, stream)) return rc;
-    if (int rc = moe_combine(grad_out_dot, w.U_dot, z, gate, slot, N, n_types, k, Dn, w.ubar_dot,
-                             stream))
-      return rc;
     // ---- projections: abar = ubar W_u^T, abar_dot = ubar_dot W_u^T ----
     GemmArgs g3;
     g3.A = ubar; g3.lda = Dn; g3.B = W_u; g3.ldb = Dn; g3.C = w.abar; g3.ldc = De;
@@ -853,38 +938,17 @@ int mlip_block_tangent_vjp(
     g.R = w.ubar_dot; g.ldr = Dn; g.M = N; g.N = Dn; g.K = De;
     if (int rc = launch_gemm(g, true, EPI_RESID, K_GEMM_DENSE, stream)) return rc;
   }
-  // ---- weight gradients ----
   {
     WgradArgs q;  // d W_u = sum_i a_dot_i^T ubar_i + a_i^T ubar_dot_i
     q.A0 = a_dot; q.B0 = ubar; q.A1 = a; q.B1 = w.ubar_dot; q.lda = De; q.ldb = Dn;
     q.P = N; q.Mo = De; q.No = Dn; q.C = d_W_u;
     if (int rc = launch_wgrad(q, w.split, stream)) return rc;
   }
-  {
-    WgradArgs q;  // d W_d = sum_i h_dot_i^T sbar_i + h_i^T sbar_dot_i
-    q.A0 = h; q.B0 = w.sbar_dot;
-    if (h_dot) { q.A1 = h_dot; q.B1 = w.sbar; }
-    q.lda = Dn; q.ldb = De; q.P = N; q.Mo = Dn; q.No = De; q.C = d_W_d;
-    if (int rc = launch_wgrad(q, w.split, stream)) return rc;
-  }
-  if (int rc = launch_token_gate(z, gate, slot, N, n_types, k, w.gt, stream)) return rc;
-  {
-    WgradArgs q;  // d W1_x = sum_t gate_t (u_dot[i]^T D_t + u[i]^T D_dot_t)
-    q.A0 = u_dot; q.B0 = w.D; q.A1 = u; q.B1 = w.D_dot; q.lda = Dn; q.ldb = H;
-    q.a_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off; q.n_groups = X;
-    q.P = M; q.Mo = Dn; q.No = H; q.C = d_W1;
-    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
-  }
-  {
-    WgradArgs q;  // d W2_x = sum_t gate_t (act_dot_t^T g[i] + act_t^T g_dot[i])
-    q.A0 = w.act_dot; q.B0 = grad_out;
-    if (grad_out_dot) { q.A1 = w.act; q.B1 = grad_out_dot; }
-    q.lda = H; q.ldb = Dn; q.b_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off;
-    q.n_groups = X; q.P = M; q.Mo = H; q.No = Dn; q.C = d_W2;
-    if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
-  }
-  return launch_gate_grad(w.dg, z, topk, gate, exp_off, tok_atom, n_types, X, k, w.G, d_gate,
-                          d_logits, stream);
+  WgradArgs q;  // d W_d = sum_i h_dot_i^T sbar_i + h_i^T sbar_dot_i
+  q.A0 = h; q.B0 = w.sbar_dot;
+  if (h_dot) { q.A1 = h_dot; q.B1 = w.sbar; }
+  q.lda = Dn; q.ldb = De; q.P = N; q.Mo = Dn; q.No = De; q.C = d_W_d;
+  return launch_wgrad(q, w.split, stream);
 }
 
 // ------------------------------------------------------- readout grads ---
@@ -916,6 +980,192 @@ int mlip_readout_grad(const float *h_out, const float *h_out_dot, const double *
   if (int rc = check_ws(ws, ws_bytes, mlip_readout_grad_workspace_size(n_atoms, d_node))) return rc;
   return launch_readout_grad(h_out, h_out_dot, grad_energy, struct_ptr, n_atoms, n_structs, d_node,
                              static_cast<float *>(ws), d_w_r, stream);
+}
+
+// ------------------------------------------- MoE layer: training tangents ---
+size_t mlip_moe_jvp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node, int32_t d_hidden) {
+  return mlip_block_jvp_workspace_size(n_atoms, top_k, d_node, d_hidden);
+}
+
+static int check_moe_dims(int32_t n_atoms, int32_t n_types, int32_t n_experts, int32_t top_k,
+                          int32_t d_node, int32_t d_hidden) {
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  return check_width(d_hidden, "d_hidden");
+}
+
+int mlip_moe_jvp(const int32_t *z, const float *gate, const int32_t *exp_off, const int32_t *tok_atom,
+                 const int32_t *slot, const float *P, const float *W1, const float *W2, int32_t n_atoms,
+                 int32_t n_types, int32_t n_experts, int32_t top_k, int32_t d_node, int32_t d_hidden,
+                 const float *u_dot, float *P_dot, float *h_out_dot, void *ws, size_t ws_bytes,
+                 void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (int rc = check_moe_dims(n_atoms, n_types, n_experts, top_k, d_node, d_hidden)) return rc;
+  MLIP_CHECK_ARG(W1 && W2 && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (z && tok_atom && slot && P && u_dot && P_dot), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(P, 16) && aligned(u_dot, 16) && aligned(P_dot, 16) && aligned(h_out_dot, 16) &&
+                     aligned(W1, 16) && aligned(W2, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_moe_jvp_workspace_size(n_atoms, top_k, d_node, d_hidden)))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  JvpWs w = carve_jvp(ws, n_atoms, top_k, d_node, d_hidden, nullptr);
+  return moe_jvp_core(u_dot, z, gate, exp_off, tok_atom, slot, P, W1, W2, n_atoms, n_types, n_experts,
+                      top_k, d_node, d_hidden, P_dot, w.act_dot, w.Y_dot, h_out_dot, stream);
+}
+
+size_t mlip_moe_tangent_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t top_k,
+                                           int32_t d_node, int32_t d_hidden) {
+  Carver c(nullptr);
+  carve_moe_tan(c, std::max(n_atoms, 0), std::max(n_types, 1), std::max(top_k, 1), std::max(d_node, 0),
+                std::max(d_hidden, 0));
+  return c.bytes();
+}
+
+int mlip_moe_tangent_vjp(const int32_t *z, const int32_t *topk, const float *gate,
+                         const int32_t *exp_off, const int32_t *tok_atom, const int32_t *slot,
+                         const float *P, const float *P_dot, const float *W1, const float *W2,
+                         int32_t n_atoms, int32_t n_types, int32_t n_experts, int32_t top_k,
+                         int32_t d_node, int32_t d_hidden, const float *u, const float *u_dot,
+                         const float *grad_out, const float *Q, const float *grad_out_dot,
+                         float *grad_in_dot, float *d_W1, float *d_W2, float *d_gate, float *d_logits,
+                         void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (int rc = check_moe_dims(n_atoms, n_types, n_experts, top_k, d_node, d_hidden)) return rc;
+  MLIP_CHECK_ARG(W1 && W2 && topk && gate && exp_off && d_W1 && d_W2, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (z && tok_atom && slot && P && P_dot && u && u_dot && grad_out && Q),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(aligned(P, 16) && aligned(P_dot, 16) && aligned(u, 16) && aligned(u_dot, 16) &&
+                     aligned(grad_out, 16) && aligned(Q, 16) && aligned(grad_out_dot, 16) &&
+                     aligned(grad_in_dot, 16) && aligned(W1, 16) && aligned(W2, 16) &&
+                     aligned(d_W1, 16) && aligned(d_W2, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_moe_tangent_vjp_workspace_size(n_atoms, n_types, top_k,
+                                                                          d_node, d_hidden)))
+    return rc;
+  Carver c(ws);
+  MoeTanWs w = carve_moe_tan(c, n_atoms, n_types, top_k, d_node, d_hidden);
+  return moe_tvjp_core(z, topk, gate, exp_off, tok_atom, slot, P, P_dot, W1, W2, n_atoms, n_types,
+                       n_experts, top_k, d_node, d_hidden, u, u_dot, grad_out, Q, grad_out_dot, w,
+                       grad_in_dot, d_W1, d_W2, d_gate, d_logits, stream);
+}
+
+// ------------------------------------------- attention: training tangents ---
+int mlip_attention_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                       int64_t n_edges, const float *grad_forces, const float *h0_dot, const float *qkv,
+                       const float *o, const float *stats, const float *W_qkv, const float *Wa_e,
+                       const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn, int32_t n_heads,
+                       float cutoff, float *qkv_dot, float *o_dot, float *tstat, float *u_dot,
+                       void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0, lph = 0;
+  if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && h0_dot && qkv && o && stats && qkv_dot && o_dot &&
+                                  tstat && u_dot),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h0_dot, 16) && aligned(qkv, 16) && aligned(o, 16) &&
+                     aligned(stats, 8) && aligned(W_qkv, 16) && aligned(Wa_e, 16) && aligned(W_o, 16) &&
+                     aligned(qkv_dot, 16) && aligned(o_dot, 16) && aligned(u_dot, 16),
+                 "float arrays must be 16-byte aligned (stats 8-byte)");
+  if (n_atoms == 0) return MLIP_OK;
+  GemmArgs g;  // [q_dot | k_dot | v_dot] = h0_dot W_qkv
+  g.A = h0_dot; g.lda = d_node; g.B = W_qkv; g.ldb = 3 * int64_t(d_attn); g.C = qkv_dot;
+  g.ldc = 3 * int64_t(d_attn); g.M = n_atoms; g.N = 3 * d_attn; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  AttnTanArgs a;
+  a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;
+  a.x_dot = grad_forces; a.x_sign = -1.f; a.Wa_e = Wa_e; a.qkv = qkv; a.qkv_dot = qkv_dot;
+  a.o = o; a.o_dot = o_dot; a.stats = stats; a.tstat = tstat;
+  a.Da = d_attn; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
+  if (int rc = launch_attn_jvp(a, stream)) return rc;
+  GemmArgs g2;  // u_dot = h0_dot + o_dot W_o
+  g2.A = o_dot; g2.lda = d_attn; g2.B = W_o; g2.ldb = d_node; g2.C = u_dot; g2.ldc = d_node;
+  g2.R = h0_dot; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_attn;
+  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
+size_t mlip_attention_tangent_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_node,
+                                                 int32_t d_attn, int32_t n_heads) {
+  size_t b = 0;
+  carve_attn_tan(nullptr, std::max(n_atoms, 0), std::max<int64_t>(n_edges, 0), std::max(d_node, 0),
+                 std::max(d_attn, 0), std::max(n_heads, 1), &b);
+  return b;
+}
+
+int mlip_attention_tangent_vjp(
+    const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom, int32_t n_atoms,
+    int64_t n_edges, const float *grad_forces, const float *h0, const float *h0_dot, const float *qkv,
+    const float *qkv_dot, const float *o, const float *o_dot, const float *stats, const float *tstat,
+    const float *qkv_bar, const float *W_qkv, const float *Wa_e, const float *W_o, int32_t n_rbf,
+    int32_t d_node, int32_t d_attn, int32_t n_heads, float cutoff, const float *grad_u,
+    const float *grad_u_dot, float *grad_h0_dot, float *d_W_qkv, float *d_Wa_e, float *d_W_o, void *ws,
+    size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0, lph = 0;
+  if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o && d_W_qkv && d_Wa_e && d_W_o, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && h0 && h0_dot && qkv && qkv_dot && o && o_dot && stats &&
+                                  tstat && qkv_bar && grad_u && grad_u_dot),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && rev && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h0, 16) && aligned(h0_dot, 16) && aligned(qkv, 16) &&
+                     aligned(qkv_dot, 16) && aligned(o, 16) && aligned(o_dot, 16) && aligned(stats, 8) &&
+                     aligned(qkv_bar, 16) && aligned(W_qkv, 16) && aligned(Wa_e, 16) && aligned(W_o, 16) &&
+                     aligned(grad_u, 16) && aligned(grad_u_dot, 16) && aligned(grad_h0_dot, 16) &&
+                     aligned(d_W_qkv, 16) && aligned(d_Wa_e, 16) && aligned(d_W_o, 16),
+                 "float arrays must be 16-byte aligned (stats 8-byte)");
+  if (int rc = check_ws(ws, ws_bytes, mlip_attention_tangent_vjp_workspace_size(n_atoms, n_edges, d_node,
+                                                                                d_attn, n_heads)))
+    return rc;
+  AttnTanWs w = carve_attn_tan(ws, n_atoms, n_edges, d_node, d_attn, n_heads, nullptr);
+  const int N = n_atoms, Da = d_attn, Dn = d_node;
+  if (N > 0) {
+    GemmArgs g;  // obar = ubar W_o^T, obar_dot = ubar_dot W_o^T
+    g.A = grad_u; g.lda = Dn; g.B = W_o; g.ldb = Dn; g.C = w.obar; g.ldc = Da;
+    g.M = N; g.N = Da; g.K = Dn;
+    if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+    g.A = grad_u_dot; g.C = w.obar_dot;
+    if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+    AttnTanArgs a;
+    a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = N;
+    a.x_dot = grad_forces; a.x_sign = -1.f; a.Wa_e = Wa_e; a.qkv = qkv; a.qkv_dot = qkv_dot;
+    a.o = o; a.o_dot = const_cast<float *>(o_dot); a.stats = stats; a.tstat = const_cast<float *>(tstat);
+    a.obar = w.obar; a.obar_dot = w.obar_dot; a.qkv_bar_dot = w.qkv_bar_dot;
+    a.edge_g = w.eg; a.edge_gd = w.egd; a.edge_a = w.ea; a.edge_ad = w.ead;
+    a.ebar = w.ebar; a.ebar_dot = w.ebar_dot;
+    a.Da = Da; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
+    if (int rc = launch_attn_tvjp(a, stream)) return rc;
+  }
+  if (int rc = launch_edge_basis_grad(row_ptr, src, geom, N, grad_forces, -1.f, w.ebar, w.ebar_dot, Da,
+                                      cutoff, w.part, d_Wa_e, stream))
+    return rc;
+  if (grad_h0_dot && N > 0) {
+    GemmArgs g;  // grad_h0_dot = ubar_dot + [q|k|v]bar_dot W_qkv^T
+    g.A = w.qkv_bar_dot; g.lda = 3 * int64_t(Da); g.B = W_qkv; g.ldb = 3 * int64_t(Da);
+    g.C = grad_h0_dot; g.ldc = Dn; g.R = grad_u_dot; g.ldr = Dn; g.M = N; g.N = Dn; g.K = 3 * Da;
+    if (int rc = launch_gemm(g, true, EPI_RESID, K_GEMM_DENSE, stream)) return rc;
+  }
+  {
+    WgradArgs q;  // d W_qkv = sum_i h0_dot_i^T [q|k|v]bar_i + h0_i^T [q|k|v]bar_dot_i
+    q.A0 = h0_dot; q.B0 = qkv_bar; q.A1 = h0; q.B1 = w.qkv_bar_dot; q.lda = Dn; q.ldb = 3 * int64_t(Da);
+    q.P = N; q.Mo = Dn; q.No = 3 * Da; q.C = d_W_qkv;
+    if (int rc = launch_wgrad(q, w.split, stream)) return rc;
+  }
+  WgradArgs q;  // d W_o = sum_i o_dot_i^T ubar_i + o_i^T ubar_dot_i
+  q.A0 = o_dot; q.B0 = grad_u; q.A1 = o; q.B1 = grad_u_dot; q.lda = Da; q.ldb = Dn;
+  q.P = N; q.Mo = Da; q.No = Dn; q.C = d_W_o;
+  return launch_wgrad(q, w.split, stream);
 }
 
 // ------------------------------------------------------ atom embedding ----

@@ -67,6 +67,7 @@ enum KClass {
   K_GEMM_WGRAD,            // weight-gradient GEMMs (sums over tokens / atoms)
   K_EDGE_TAN,              // edge passes of the tangents (and the W_e gradient)
   K_MOE_TAN,               // token-wise MoE tangents, gate and readout gradients
+  K_ATTN_TAN,              // attention tangents (training gradient)
   K_NUM_CLASSES
 };
 
@@ -235,6 +236,35 @@ struct AttnArgs {
 int attn_lane_layout(int Da, int nh, int *cpl, int *lph);
 int launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 int launch_attn_vjp(const AttnArgs &a, hipStream_t stream);
+
+// Tangents of the attention for the training gradient (attn.hip).
+struct AttnTanArgs {
+  const int32_t *row_ptr = nullptr, *src = nullptr, *rev = nullptr;
+  const float *geom = nullptr;
+  int n_atoms = 0;
+  const float *x_dot = nullptr;   // [N][3]; position direction x_sign * x_dot
+  float x_sign = 1.f;
+  const float *Wa_e = nullptr;
+  const float *qkv = nullptr, *qkv_dot = nullptr;   // [N][3 Da]
+  const float *o = nullptr;                         // [N][Da]
+  float *o_dot = nullptr;                           // [N][Da] (JVP output, VJP-tangent input)
+  const float *stats = nullptr;                     // [N][nh] (max, weight sum)
+  float *tstat = nullptr;                           // [N][nh] T = sum a s_dot + f_dot w / Z
+  const float *obar = nullptr, *obar_dot = nullptr; // [N][Da]
+  float *qkv_bar_dot = nullptr;                     // [N][3 Da]
+  float *edge_g = nullptr, *edge_gd = nullptr, *edge_a = nullptr, *edge_ad = nullptr;  // [E][nh]
+  float *ebar = nullptr, *ebar_dot = nullptr;       // [E][Da]
+  int Da = 0, nh = 0, cpl = 0, lph = 0;
+  float rc = 0.f;
+};
+int launch_attn_jvp(const AttnTanArgs &a, hipStream_t stream);
+int launch_attn_tvjp(const AttnTanArgs &a, hipStream_t stream);
+// sum_e beta_e (x) X_e + alpha_e (x) Y_e over all edges (rows of X, Y indexed
+// by edge), alpha = f_c phi, beta = r_dot d(f_c phi)/dr: the gradient of a
+// K x D basis map e = f_c (phi W) given per-edge dL/de (X) and its tangent (Y).
+int launch_edge_basis_grad(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
+                           const float *x_dot, float x_sign, const float *X, const float *Y, int D,
+                           float rc, float *part, float *dW, hipStream_t stream);
 
 // ------------------------------------------------------- three-body update -
 struct TriArgs {

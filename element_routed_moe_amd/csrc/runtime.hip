@@ -22,7 +22,7 @@ static const char *kClassNames[K_NUM_CLASSES] = {
     "gemm_expert_up", "gemm_expert_down",    "combine",            "readout",
     "gemm_expert_vjp_down", "gemm_expert_vjp_up", "edge_vjp", "attn_fwd",
     "attn_vjp_recv", "attn_vjp_send", "tri_fwd", "tri_vjp_recv", "tri_vjp_send",
-    "gemm_expert_tan", "gemm_wgrad", "edge_tan", "moe_tan"};
+    "gemm_expert_tan", "gemm_wgrad", "edge_tan", "moe_tan", "attn_tan"};
 
 struct ProfRec {
   int k;

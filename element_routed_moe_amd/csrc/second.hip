@@ -362,6 +362,82 @@ __global__ void __launch_bounds__(64) edge_tan_kernel(EdgeTanArgs g, int n_group
   }
 }
 
+// sum over edges of beta_e,k X_e,c + alpha_e,k Y_e,c with per-edge rows X, Y
+// (not gathered): the W gradient of a basis map e = f_c (phi W) from dL/de
+// (X) and its tangent (Y) when the basis moves with r_dot.  Same row groups,
+// slices and partial sums as edge_tan.
+__global__ void __launch_bounds__(64) edge_basis_grad_kernel(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src, const float4 *__restrict__ geom,
+    int n_atoms, const float *__restrict__ x_dot, float x_sign, const float *__restrict__ X,
+    const float *__restrict__ Y, int D, float rc, int n_groups, int rows_per, int n_slices,
+    float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float bas[ET_CHUNK][2 * K];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(int64_t(n_groups) * n_slices);
+  if (blk < 0) return;
+  const int rg = int(blk / n_slices);
+  const int slice = int(blk - int64_t(rg) * n_slices);
+  const int c = slice * ET_COLS + 2 * lane;
+  const bool active = c < D;
+  const int cc = active ? c : 0;
+  const Radial R = make_radial(rc);
+  f2v dw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) dw[k] = f2v{0.f, 0.f};
+  const int i0 = rg * rows_per;
+  const int i1 = min(n_atoms, i0 + rows_per);
+  for (int i = i0; i < i1; ++i) {
+    const float xi0 = x_dot[3 * i], xi1 = x_dot[3 * i + 1], xi2 = x_dot[3 * i + 2];
+    const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+    for (int e0 = r0; e0 < r1; e0 += ET_CHUNK) {
+      const int n = min(ET_CHUNK, r1 - e0);
+      __syncthreads();
+      if (lane < n) {
+        const int e = e0 + lane;
+        const float4 gm = geom[e];
+        const int j = src[e];
+        const float r = gm.w;
+        float rdot = 0.f;
+        if (r > 0.f)
+          rdot = x_sign * (gm.x * (x_dot[3 * j] - xi0) + gm.y * (x_dot[3 * j + 1] - xi1) +
+                           gm.z * (x_dot[3 * j + 2] - xi2)) / r;
+        float fc = 0.f, dfc = 0.f;
+        if (r < rc) {
+          float sn, cs;
+          __sincosf(r * R.pi_over_rc, &sn, &cs);
+          fc = 0.5f * (cs + 1.f);
+          dfc = -0.5f * R.pi_over_rc * sn;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float x = r - float(k) * R.mu_step;
+          const float ph = __expf(-R.gamma * x * x);
+          bas[lane][k] = fc * ph;
+          bas[lane][K + k] = rdot * (dfc * ph + fc * (-2.f * R.gamma * x * ph));
+        }
+      }
+      __syncthreads();
+      for (int q = 0; q < n; ++q) {
+        const int64_t e = e0 + q;
+        const f2v xv = ld2(X + e * D + cc), yv = ld2(Y + e * D + cc);
+        const float4 *b4 = reinterpret_cast<const float4 *>(bas[q]);
+#pragma unroll
+        for (int k4 = 0; k4 < K / 4; ++k4) {
+          const float4 al = b4[k4], be = b4[K / 4 + k4];
+          dw[4 * k4] += be.x * xv + al.x * yv;
+          dw[4 * k4 + 1] += be.y * xv + al.y * yv;
+          dw[4 * k4 + 2] += be.z * xv + al.z * yv;
+          dw[4 * k4 + 3] += be.w * xv + al.w * yv;
+        }
+      }
+    }
+  }
+  if (active) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) st2(part + (int64_t(rg) * K + k) * D + c, dw[k]);
+  }
+}
+
 // dW_e[k][c] = sum over row groups of the partials, in two fixed-order
 // stages: blocks of DWE_SPAN consecutive groups (coalesced rows of KD floats),
 // then the block sums.
@@ -674,6 +750,34 @@ int launch_edge_tan(const EdgeTanArgs &a, hipStream_t stream) {
     dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(part2, n2, KD, a.dwe);
     MLIP_LAUNCHED();
   }
+  return MLIP_OK;
+}
+
+int launch_edge_basis_grad(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
+                           const float *x_dot, float x_sign, const float *X, const float *Y, int D,
+                           float rc, float *part, float *dW, hipStream_t stream) {
+  ProfScope ps(K_EDGE_TAN, stream);
+  const int KD = K * D;
+  if (n_atoms <= 0) {
+    dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(part, 0, KD, dW);
+    MLIP_LAUNCHED();
+    return MLIP_OK;
+  }
+  const int n_groups = edge_tan_groups(n_atoms);
+  const int rows_per = int(cdiv(n_atoms, n_groups));
+  const int n_slices = int(cdiv(D, ET_COLS));
+  const int64_t grid = padded_grid(int64_t(n_groups) * n_slices);
+  edge_basis_grad_kernel<<<dim3(unsigned(grid)), dim3(64), 0, stream>>>(
+      row_ptr, src, reinterpret_cast<const float4 *>(geom), n_atoms, x_dot, x_sign, X, Y, D, rc, n_groups,
+      rows_per, n_slices, part);
+  MLIP_LAUNCHED();
+  const int n2 = int(cdiv(n_groups, DWE_SPAN));
+  float *part2 = part + int64_t(n_groups) * KD;
+  dwe_stage1_kernel<<<dim3(unsigned(cdiv(KD, 256)), unsigned(n2)), dim3(256), 0, stream>>>(part, n_groups, KD,
+                                                                                           part2);
+  MLIP_LAUNCHED();
+  dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(part2, n2, KD, dW);
+  MLIP_LAUNCHED();
   return MLIP_OK;
 }
 

@@ -71,13 +71,25 @@ _SIGS = {
     "mlip_readout_grad": (C.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _sz, _p]),
     "mlip_moe_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "mlip_moe_vjp": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
-                               _p, _p, _p, _sz, _p]),
+                               _p, _p, _p, _p, _sz, _p]),
+    "mlip_moe_jvp_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "mlip_moe_jvp": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _p, _p, _p, _p, _sz, _p]),
+    "mlip_moe_tangent_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "mlip_moe_tangent_vjp": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_attention_jvp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+                                     _i32, _i32, _f32, _p, _p, _p, _p, _p]),
+    "mlip_attention_tangent_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32]),
+    "mlip_attention_tangent_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
+                                             _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
+                                             _p, _p, _p, _p, _sz, _p]),
     "mlip_attention": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                  _f32, _p, _p, _p, _p, _p]),
     "mlip_attention_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32]),
     "mlip_attention_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32,
                                      _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _i32,
-                                     _p, _sz, _p]),
+                                     _p, _p, _sz, _p]),
     "mlip_embed_atoms": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
     "mlip_tri": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
                            _p, _p]),
@@ -343,8 +355,9 @@ def mlip_readout_grad(h_out, struct_ptr, grad_energy=None, h_out_dot=None,
 
 
 def mlip_moe_vjp(moe, z, W1, W2, grad_out, out: Optional[torch.Tensor] = None,
-                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """dL/du of h' = u + MoE(u) for grad_out = dL/dh' (moe: the layer's forward state)."""
+                 ws: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dL/du of h' = u + MoE(u) for grad_out = dL/dh' (moe: the layer's forward state);
+    q_out (optional) keeps Q = grad_out[tok] W2^T for the training tangents."""
     N, Dn = int(grad_out.shape[0]), int(grad_out.shape[1])
     X, H = int(W1.shape[0]), int(W1.shape[2])
     T, k = int(moe["gate"].shape[0]), int(moe["gate"].shape[1])
@@ -355,7 +368,105 @@ def mlip_moe_vjp(moe, z, W1, W2, grad_out, out: Optional[torch.Tensor] = None,
         ws = _ws(_lib.mlip_moe_vjp_workspace_size(N, k, Dn, H), dev)
     _check(_lib.mlip_moe_vjp(_ptr(z), _ptr(moe["gate"]), _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]),
                              _ptr(moe["slot"]), _ptr(moe["P"]), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
-                             _ptr(grad_out), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+                             _ptr(grad_out), _ptr(out), _ptr(q_out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_moe_jvp(moe, z, W1, W2, u_dot, want_h_out_dot: bool = True, out: Optional[Dict] = None,
+                 ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Forward tangent of one MoE layer: P_dot and h_out_dot = u_dot + sum gate silu'(P) P_dot W2."""
+    N, Dn = int(u_dot.shape[0]), int(u_dot.shape[1])
+    X, H = int(W1.shape[0]), int(W1.shape[2])
+    T, k = int(moe["gate"].shape[0]), int(moe["gate"].shape[1])
+    dev = u_dot.device
+    if out is None:
+        out = dict(P_dot=torch.empty((N * k, H), dtype=torch.float32, device=dev),
+                   h_out_dot=torch.empty((N, Dn), dtype=torch.float32, device=dev) if want_h_out_dot else None)
+    need = _lib.mlip_moe_jvp_workspace_size(N, k, Dn, H)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_moe_jvp(_ptr(z), _ptr(moe["gate"]), _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]),
+                             _ptr(moe["slot"]), _ptr(moe["P"]), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
+                             _ptr(u_dot), _ptr(out["P_dot"]), _ptr(out["h_out_dot"]), _ptr(ws), ws.numel(),
+                             _stream()))
+    out["ws"] = ws
+    return out
+
+
+def mlip_moe_tangent_vjp(moe, z, W1, W2, u, u_dot, P_dot, grad_out, Q, grad_out_dot=None,
+                         want_grad_in_dot: bool = True, out: Optional[Dict] = None,
+                         ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Tangent of one MoE layer's gradient: grad_in_dot, d_W1, d_W2, d_gate, d_logits."""
+    N, Dn = int(u.shape[0]), int(u.shape[1])
+    X, H = int(W1.shape[0]), int(W1.shape[2])
+    T, k = int(moe["gate"].shape[0]), int(moe["gate"].shape[1])
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = dict(grad_in_dot=torch.empty((N, Dn), dtype=f32, device=dev) if want_grad_in_dot else None,
+                   d_W1=torch.empty(tuple(W1.shape), dtype=f32, device=dev),
+                   d_W2=torch.empty(tuple(W2.shape), dtype=f32, device=dev),
+                   d_gate=torch.empty((T, k), dtype=f32, device=dev),
+                   d_logits=torch.empty((T, X), dtype=f32, device=dev))
+    need = _lib.mlip_moe_tangent_vjp_workspace_size(N, T, k, Dn, H)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_moe_tangent_vjp(_ptr(z), _ptr(moe["topk"]), _ptr(moe["gate"]), _ptr(moe["exp_off"]),
+                                     _ptr(moe["tok_atom"]), _ptr(moe["slot"]), _ptr(moe["P"]), _ptr(P_dot),
+                                     _ptr(W1), _ptr(W2), N, T, X, k, Dn, H, _ptr(u), _ptr(u_dot),
+                                     _ptr(grad_out), _ptr(Q), _ptr(grad_out_dot), _ptr(out["grad_in_dot"]),
+                                     _ptr(out["d_W1"]), _ptr(out["d_W2"]), _ptr(out["d_gate"]),
+                                     _ptr(out["d_logits"]), _ptr(ws), ws.numel(), _stream()))
+    out["ws"] = ws
+    return out
+
+
+def mlip_attention_jvp(graph, att, h0_dot, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float, grad_forces,
+                       out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    """Forward tangent of the attention: qkv_dot, o_dot, tstat, u_dot."""
+    N, Dn = int(h0_dot.shape[0]), int(h0_dot.shape[1])
+    Da = int(W_o.shape[0])
+    E = int(graph["n_edges"])
+    dev = h0_dot.device
+    f32 = torch.float32
+    if out is None:
+        out = dict(qkv_dot=torch.empty((N, 3 * Da), dtype=f32, device=dev),
+                   o_dot=torch.empty((N, Da), dtype=f32, device=dev),
+                   tstat=torch.empty((N, int(n_heads)), dtype=f32, device=dev),
+                   u_dot=torch.empty((N, Dn), dtype=f32, device=dev))
+    _check(_lib.mlip_attention_jvp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                                   _ptr(grad_forces), _ptr(h0_dot), _ptr(att["qkv"]), _ptr(att["o"]),
+                                   _ptr(att["stats"]), _ptr(W_qkv), _ptr(Wa_e), _ptr(W_o), int(Wa_e.shape[0]),
+                                   Dn, Da, int(n_heads), float(cutoff), _ptr(out["qkv_dot"]),
+                                   _ptr(out["o_dot"]), _ptr(out["tstat"]), _ptr(out["u_dot"]), _stream()))
+    return out
+
+
+def mlip_attention_tangent_vjp(graph, att, ajvp, h0, h0_dot, qkv_bar, W_qkv, Wa_e, W_o, n_heads: int,
+                               cutoff: float, grad_forces, grad_u, grad_u_dot, want_grad_h0_dot: bool = True,
+                               out: Optional[Dict] = None, ws: Optional[torch.Tensor] = None):
+    """Tangent of the attention's gradient: grad_h0_dot, d_W_qkv, d_Wa_e, d_W_o."""
+    N, Dn = int(h0.shape[0]), int(h0.shape[1])
+    Da = int(W_o.shape[0])
+    E = int(graph["n_edges"])
+    dev = h0.device
+    f32 = torch.float32
+    if out is None:
+        out = dict(grad_h0_dot=torch.empty((N, Dn), dtype=f32, device=dev) if want_grad_h0_dot else None,
+                   d_W_qkv=torch.empty(tuple(W_qkv.shape), dtype=f32, device=dev),
+                   d_Wa_e=torch.empty(tuple(Wa_e.shape), dtype=f32, device=dev),
+                   d_W_o=torch.empty(tuple(W_o.shape), dtype=f32, device=dev))
+    need = _lib.mlip_attention_tangent_vjp_workspace_size(N, E, Dn, Da, int(n_heads))
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_attention_tangent_vjp(
+        _ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["rev"]), _ptr(graph["geom"]), N, E,
+        _ptr(grad_forces), _ptr(h0), _ptr(h0_dot), _ptr(att["qkv"]), _ptr(ajvp["qkv_dot"]), _ptr(att["o"]),
+        _ptr(ajvp["o_dot"]), _ptr(att["stats"]), _ptr(ajvp["tstat"]), _ptr(qkv_bar), _ptr(W_qkv), _ptr(Wa_e),
+        _ptr(W_o), int(Wa_e.shape[0]), Dn, Da, int(n_heads), float(cutoff), _ptr(grad_u), _ptr(grad_u_dot),
+        _ptr(out["grad_h0_dot"]), _ptr(out["d_W_qkv"]), _ptr(out["d_Wa_e"]), _ptr(out["d_W_o"]), _ptr(ws),
+        ws.numel(), _stream()))
+    out["ws"] = ws
     return out
 
 
@@ -380,7 +491,8 @@ def mlip_attention(graph, h0, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float,
 def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float, grad_u,
                        struct_ptr=None, out: Optional[Dict] = None,
                        ws: Optional[torch.Tensor] = None,
-                       accumulate: bool = False) -> Dict[str, torch.Tensor]:
+                       accumulate: bool = False, keep: bool = False) -> Dict[str, torch.Tensor]:
+    """Attention gradient; with ``keep`` also out["qkv_bar"] for the training tangents."""
     N, Dn = int(grad_u.shape[0]), int(grad_u.shape[1])
     Da = int(W_o.shape[0])
     E = int(graph["n_edges"])
@@ -395,13 +507,16 @@ def mlip_attention_vjp(graph, att, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float
     if ws is None or ws.numel() < _lib.mlip_attention_vjp_workspace_size(N, E, Da, int(n_heads)):
         ws = _ws(_lib.mlip_attention_vjp_workspace_size(N, E, Da, int(n_heads)), dev)
     out["ws"] = ws
+    if keep and out.get("qkv_bar") is None:
+        out["qkv_bar"] = torch.empty((N, 3 * Da), dtype=torch.float32, device=dev)
     _check(_lib.mlip_attention_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["rev"]),
                                    _ptr(graph["geom"]), N, E, _ptr(att["qkv"]), _ptr(att["o"]),
                                    _ptr(att["stats"]), _ptr(W_qkv), _ptr(Wa_e), _ptr(W_o),
                                    int(Wa_e.shape[0]), Dn, Da, int(n_heads), float(cutoff),
                                    _ptr(grad_u), _ptr(out["grad_h0"]), _ptr(out["grad_pos"]),
                                    _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
-                                   _ptr(out.get("grad_strain")), 1 if accumulate else 0, _ptr(ws),
+                                   _ptr(out.get("grad_strain")), 1 if accumulate else 0,
+                                   _ptr(out.get("qkv_bar") if keep else None), _ptr(ws),
                                    ws.numel(), _stream()))
     return out
 
@@ -578,12 +693,14 @@ class FullBlock:
     graph, as the layers of a ``Stack`` do.
     """
 
-    def __init__(self, inputs: Dict, device="cuda", grad_out=None, params: Optional[Dict] = None):
+    def __init__(self, inputs: Dict, device="cuda", grad_out=None, params: Optional[Dict] = None,
+                 train: bool = False):
         def dev(x, dt=None):
             t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
             return t.to(device=device, dtype=dt or t.dtype).contiguous()
 
         self.device = device
+        self.train = bool(train)
         f32 = torch.float32
         params = inputs if params is None else params
         self.pos = dev(inputs["pos"], f32)
@@ -625,9 +742,16 @@ class FullBlock:
         self.edge_capacity = None
         self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
         self.ubar = self.avjp = self.grad_hT = self.grad_h = None
+        self.g_up = self.Q0 = self.Q1 = None
+        self.h_in = None
+        if self.train:
+            M = N * self.top_k
+            self.Q0 = torch.empty((M, H), dtype=f32, device=device)
+            self.Q1 = torch.empty((M, H), dtype=f32, device=device)
 
     def forward(self, g, h):
         """One block on graph g for input features h; returns h' (MoE1 output)."""
+        self.h_in = h
         if self.has_tri:
             self.tri = mlip_tri(g, h, self.W_s, self.W_ang, self.W_T, self.cutoff, out=self.tri)
             h = self.tri["h_T"]
@@ -642,8 +766,9 @@ class FullBlock:
     def backward(self, g, grad_out, forces: Optional[Dict] = None, accumulate: bool = False):
         """Input gradient for grad_out = dL/dh'; forces (grad_pos, atom_virial,
         grad_strain) are written, or added to the given buffers when accumulate."""
+        self.g_up = grad_out
         self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, grad_out, out=self.ubar,
-                                 ws=self.ws_mvjp)
+                                 ws=self.ws_mvjp, q_out=self.Q1)
         out = None
         if forces is not None:
             gh0 = self.avjp["grad_h0"] if self.avjp is not None else torch.empty_like(grad_out)
@@ -651,11 +776,11 @@ class FullBlock:
         self.avjp = mlip_attention_vjp(g, self.att, self.W_qkv, self.Wa_e, self.W_o, self.n_heads,
                                        self.cutoff, self.ubar, struct_ptr=self.struct_ptr,
                                        out=out if out is not None else self.avjp, ws=self.ws_avjp,
-                                       accumulate=accumulate)
+                                       accumulate=accumulate, keep=self.train)
         self.ws_avjp = self.avjp["ws"]
         if self.has_tri:
             self.grad_hT = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
-                                        out=self.grad_hT, ws=self.ws_mvjp)
+                                        out=self.grad_hT, ws=self.ws_mvjp, q_out=self.Q0)
             self.grad_h, self.ws_tvjp = mlip_tri_vjp(
                 g, self.tri, self.W_s, self.W_ang, self.W_T, self.cutoff, self.grad_hT,
                 self.avjp["grad_pos"], atom_virial=self.avjp["atom_virial"],
@@ -663,8 +788,58 @@ class FullBlock:
                 out=self.grad_h, ws=self.ws_tvjp)
         else:
             self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
-                                       out=self.grad_h, ws=self.ws_mvjp)
+                                       out=self.grad_h, ws=self.ws_mvjp, q_out=self.Q0)
         return self.grad_h
+
+    def jvp(self, g, grad_forces, h_dot=None):
+        """Forward tangents along x_dot = -grad_forces and h_dot (None: 0) after
+        ``forward``; returns h_out_dot."""
+        if not self.train:
+            raise RuntimeError("tangents need FullBlock(train=True)")
+        if self.has_tri:
+            raise NotImplementedError("training tangents of the three-body update are not built")
+        hT_dot = h_dot if h_dot is not None else torch.zeros_like(self.h_in)
+        self.hT_dot = hT_dot
+        self.m0jvp = mlip_moe_jvp(self.moe0, self.z, self.W1_0, self.W2_0, hT_dot,
+                                  out=getattr(self, "m0jvp", None))
+        self.ajvp = mlip_attention_jvp(g, self.att, self.m0jvp["h_out_dot"], self.W_qkv, self.Wa_e, self.W_o,
+                                       self.n_heads, self.cutoff, grad_forces, out=getattr(self, "ajvp", None))
+        self.m1jvp = mlip_moe_jvp(self.moe, self.z, self.W1, self.W2, self.ajvp["u_dot"],
+                                  out=getattr(self, "m1jvp", None))
+        return self.m1jvp["h_out_dot"]
+
+    def tangent_vjp(self, g, grad_forces, grad_out_dot) -> Dict[str, torch.Tensor]:
+        """Tangent of ``backward`` along (x_dot, h_dot, grad_out_dot) after
+        ``jvp``: the parameter gradients of the block and d_h (the tangent of
+        dL/dh, i.e. the upstream of the block below)."""
+        m1 = mlip_moe_tangent_vjp(self.moe, self.z, self.W1, self.W2, self.att["u"], self.ajvp["u_dot"],
+                                  self.m1jvp["P_dot"], self.g_up, self.Q1, grad_out_dot=grad_out_dot,
+                                  out=getattr(self, "m1tan", None))
+        self.m1tan = m1
+        at = mlip_attention_tangent_vjp(g, self.att, self.ajvp, self.moe0["h_out"], self.m0jvp["h_out_dot"],
+                                        self.avjp["qkv_bar"], self.W_qkv, self.Wa_e, self.W_o, self.n_heads,
+                                        self.cutoff, grad_forces, self.ubar, m1["grad_in_dot"],
+                                        out=getattr(self, "atan", None))
+        self.atan = at
+        m0 = mlip_moe_tangent_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.h_in, self.hT_dot,
+                                  self.m0jvp["P_dot"], self.avjp["grad_h0"], self.Q0,
+                                  grad_out_dot=at["grad_h0_dot"], out=getattr(self, "m0tan", None))
+        self.m0tan = m0
+        return dict(d_W1=m1["d_W1"], d_W2=m1["d_W2"], d_logits=m1["d_logits"],
+                    d_W_qkv=at["d_W_qkv"], d_Wa_e=at["d_Wa_e"], d_W_o=at["d_W_o"],
+                    d_W1_0=m0["d_W1"], d_W2_0=m0["d_W2"], d_logits0=m0["d_logits"], d_h=m0["grad_in_dot"])
+
+    def train_grad(self, grad_energy, grad_forces) -> Dict[str, torch.Tensor]:
+        """Parameter gradients of a loss L(E, F) after ``step()`` (built with
+        ``train=True`` and the force seed): grad_energy = dL/dE [B] float64,
+        grad_forces = dL/dF [N, 3] float32 on the device."""
+        g = self.graph
+        h_out_dot = self.jvp(g, grad_forces)
+        seed_dot = mlip_readout_vjp(self.w_r, self.struct_ptr, int(self.z.shape[0]), grad_energy=grad_energy)
+        res = self.tangent_vjp(g, grad_forces, seed_dot)
+        res["d_w_r"] = mlip_readout_grad(self.moe["h_out"], self.struct_ptr, grad_energy=grad_energy,
+                                         h_out_dot=h_out_dot)
+        return res
 
     def step(self):
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,

@@ -310,7 +310,9 @@ int mlip_readout_grad(const float *h_out, const float *h_out_dot, const double *
  * Gates carry no gradient (routing depends on z only).  z, gate, exp_off,
  * tok_atom, slot and P are those written by the mlip_moe_forward call of
  * this layer; W1, W2 as there.  grad_in [n_atoms, d_node] may not alias
- * grad_out.  Workspace: mlip_moe_vjp_workspace_size().
+ * grad_out.  Workspace: mlip_moe_vjp_workspace_size().  q_out (may be NULL)
+ * keeps Q = grad_out[tok] @ W2_x^T [n_atoms*top_k, d_hidden] in dispatch
+ * order for mlip_moe_tangent_vjp.
  * ------------------------------------------------------------------------ */
 size_t mlip_moe_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node,
                                    int32_t d_hidden);
@@ -318,7 +320,7 @@ int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
                  const int32_t *tok_atom, const int32_t *slot, const float *P, const float *W1,
                  const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
                  int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
-                 float *grad_in, void *ws, size_t ws_bytes, void *stream);
+                 float *grad_in, float *q_out, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Neighbour multi-head attention of the complete interaction block
@@ -378,8 +380,66 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                        const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                        int32_t n_heads, float cutoff, const float *grad_u, float *grad_h0,
                        float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                       float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
-                       size_t ws_bytes, void *stream);
+                       float *atom_virial, double *grad_strain, int32_t accumulate,
+                       float *qkv_bar_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Training tangents of the complete block's layers ([review] 3.3: training
+ * differentiates the force once more; see the training gradient of the
+ * core block below for the scheme).  x_dot = -grad_forces throughout.
+ *
+ * mlip_moe_jvp: for h' = u + MoE(u) (state of its mlip_moe_forward),
+ *   P_dot = u_dot[tok] W1_x (dispatch order), h_out_dot = u_dot + sum_r gate
+ *   * (silu'(P) * P_dot) W2_x (may be NULL).  Workspace:
+ *   mlip_moe_jvp_workspace_size().
+ * mlip_moe_tangent_vjp: the derivative along (u_dot, grad_out_dot) of the
+ *   layer's gradient for the upstream grad_out (Q = q_out of its
+ *   mlip_moe_vjp): grad_in_dot = grad_out_dot + sum_r gate * D_dot W1_x^T
+ *   (may be NULL), d_W1 [X,d_node,d_hidden], d_W2 [X,d_hidden,d_node],
+ *   d_gate [T,k] and d_logits [T,X] (both may be NULL).  grad_out_dot may be
+ *   NULL (0).  Workspace: mlip_moe_tangent_vjp_workspace_size().
+ * mlip_attention_jvp: [q|k|v]_dot = h0_dot W_qkv, o_dot (with the pair
+ *   embedding and envelope moving with r_dot) and u_dot = h0_dot + o_dot W_o;
+ *   also tstat [N,n_heads] = sum_j a s_dot + f_dot w / Z, which the tangent
+ *   VJP reads.  qkv, o, stats: the forward's.  No workspace.
+ * mlip_attention_tangent_vjp: the derivative along (x_dot, h0_dot,
+ *   grad_u_dot) of the attention's gradient for the upstream grad_u (qkv_bar
+ *   = qkv_bar_out of its mlip_attention_vjp): grad_h0_dot [N,d_node] (may be
+ *   NULL), d_W_qkv [d_node,3 d_attn], d_Wa_e [n_rbf,d_attn], d_W_o
+ *   [d_attn,d_node].  Workspace: mlip_attention_tangent_vjp_workspace_size().
+ * ------------------------------------------------------------------------ */
+size_t mlip_moe_jvp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_node, int32_t d_hidden);
+int mlip_moe_jvp(const int32_t *z, const float *gate, const int32_t *exp_off, const int32_t *tok_atom,
+                 const int32_t *slot, const float *P, const float *W1, const float *W2, int32_t n_atoms,
+                 int32_t n_types, int32_t n_experts, int32_t top_k, int32_t d_node, int32_t d_hidden,
+                 const float *u_dot, float *P_dot, float *h_out_dot, void *ws, size_t ws_bytes,
+                 void *stream);
+size_t mlip_moe_tangent_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t top_k,
+                                           int32_t d_node, int32_t d_hidden);
+int mlip_moe_tangent_vjp(const int32_t *z, const int32_t *topk, const float *gate,
+                         const int32_t *exp_off, const int32_t *tok_atom, const int32_t *slot,
+                         const float *P, const float *P_dot, const float *W1, const float *W2,
+                         int32_t n_atoms, int32_t n_types, int32_t n_experts, int32_t top_k,
+                         int32_t d_node, int32_t d_hidden, const float *u, const float *u_dot,
+                         const float *grad_out, const float *Q, const float *grad_out_dot,
+                         float *grad_in_dot, float *d_W1, float *d_W2, float *d_gate, float *d_logits,
+                         void *ws, size_t ws_bytes, void *stream);
+int mlip_attention_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                       int64_t n_edges, const float *grad_forces, const float *h0_dot, const float *qkv,
+                       const float *o, const float *stats, const float *W_qkv, const float *Wa_e,
+                       const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn, int32_t n_heads,
+                       float cutoff, float *qkv_dot, float *o_dot, float *tstat, float *u_dot,
+                       void *stream);
+size_t mlip_attention_tangent_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_node,
+                                                 int32_t d_attn, int32_t n_heads);
+int mlip_attention_tangent_vjp(
+    const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom, int32_t n_atoms,
+    int64_t n_edges, const float *grad_forces, const float *h0, const float *h0_dot, const float *qkv,
+    const float *qkv_dot, const float *o, const float *o_dot, const float *stats, const float *tstat,
+    const float *qkv_bar, const float *W_qkv, const float *Wa_e, const float *W_o, int32_t n_rbf,
+    int32_t d_node, int32_t d_attn, int32_t n_heads, float cutoff, const float *grad_u,
+    const float *grad_u_dot, float *grad_h0_dot, float *d_W_qkv, float *d_Wa_e, float *d_W_o, void *ws,
+    size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Three-body angular update ("Tri") of the complete block ([news]

@@ -101,21 +101,21 @@ def test_attention_and_moe_vjp_reject_bad_args(mlip):
     # 5 heads of width 20: 20 is not c * 2^j with c in {1, 2, 3, 4, 6, 8}
     assert "unsupported attention shape" in _err(mlip, att(100, 5), mlip.MLIP_ERR_UNSUPPORTED)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
-                              None, 0, None, f, 0, f, 1 << 30, None)
+                              None, 0, None, f, 0, None, f, 1 << 30, None)
     assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
-                              f, 1, None, f, 1, f, 1 << 30, None)
+                              f, 1, None, f, 1, None, f, 1 << 30, None)
     assert "accumulated atom_virial" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
-                              None, 0, None, None, 0, f, 16, None)
+                              None, 0, None, None, 0, None, f, 16, None)
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_embed_atoms(f, f, 10, 0, 64, f, None)
     assert "n_types" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     assert (L.mlip_attention_vjp_workspace_size(4096, 200000, 384, 8)
             >= (200000 * (2 * 8 + 1) + 4096 * 4 * 384) * 4)
-    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, f, f, 1 << 30, None)
+    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, f, None, f, 1 << 30, None)
     assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
-    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, f, 16, None)
+    rc = L.mlip_moe_vjp(f, f, f, f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, None, f, 16, None)
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
@@ -142,7 +142,7 @@ def test_profile_api_without_gpu(mlip):
     assert "gemm_expert_up" in names and "edge_vjp" in names and "attn_fwd" in names
     assert "tri_fwd" in names and "tri_vjp_send" in names
     assert "gemm_wgrad" in names and "edge_tan" in names and "moe_tan" in names
-    assert len(names) == 21
+    assert len(names) == 22
 
 
 def test_training_entry_points_reject_bad_args(mlip):
@@ -174,3 +174,14 @@ def test_training_entry_points_reject_bad_args(mlip):
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_readout_vjp(f, None, f, 10, 0, 64, f, None)
     assert "n_structs" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    # layer tangents of the complete block
+    rc = L.mlip_moe_jvp(f, f, f, f, f, f, f, f, 10, 4, 8, 9, 64, 128, f, f, None, f, 1 << 30, None)
+    assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_moe_tangent_vjp(f, f, f, f, f, f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, f, f, f, None,
+                                None, f, f, None, None, f, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_attention_jvp(f, f, f, 10, 20, f, None, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f, f, None)
+    assert "null pointer" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_attention_tangent_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f, 16, 64, 100,
+                                      5, 5.0, f, f, None, f, f, f, f, 1 << 30, None)
+    assert "unsupported attention shape" in _err(mlip, rc, mlip.MLIP_ERR_UNSUPPORTED)
