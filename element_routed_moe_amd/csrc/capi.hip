@@ -330,6 +330,27 @@ AttnTanWs carve_attn_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t D
   return w;
 }
 
+struct TriTanWs {
+  float *taubar, *taubar_dot, *sigma_dot, *wang_part, *wang_part2, *sbar_dot, *split;
+};
+TriTanWs carve_tri_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t Dt, size_t *bytes) {
+  Carver c(base);
+  TriTanWs w;
+  w.taubar = c.take<float>(size_t(N * Dt));
+  w.taubar_dot = c.take<float>(size_t(N * Dt));
+  w.sigma_dot = c.take<float>(size_t(E * Dt));
+  w.wang_part = c.take<float>(size_t(N * MLIP_N_ANG * Dt));
+  w.wang_part2 = c.take<float>(size_t(std::max<int64_t>(cdiv(N, 32), 1) * MLIP_N_ANG * Dt));
+  w.sbar_dot = c.take<float>(size_t(N * Dt));
+  WgradArgs a, b;
+  a.P = b.P = int(N);
+  a.Mo = int(Dn); a.No = int(Dt);
+  b.Mo = int(Dt); b.No = int(Dn);
+  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(a), wgrad_split_floats(b))));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
 }  // namespace
 }  // namespace mlip
 
@@ -739,11 +760,12 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
                  const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
                  int32_t d_tri, float cutoff, const float *grad_hT, float *grad_h,
                  float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                 float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
-                 size_t ws_bytes, void *stream_) {
+                 float *atom_virial, double *grad_strain, int32_t accumulate, float *sbar_out,
+                 void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(aligned(sbar_out, 16), "float arrays must be 16-byte aligned");
   int cpl = 0;
   if (int rc = check_tri_dims(d_node, d_tri, n_ang, cutoff, &cpl)) return rc;
   MLIP_CHECK_ARG(row_ptr && W_s && W_ang && W_T, "null pointer argument");
@@ -764,6 +786,7 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   }
   TriVjpWs w = carve_tri_vjp(ws, n_atoms, n_edges, d_tri, nullptr);
   float *vir = atom_virial ? atom_virial : w.virial;
+  if (sbar_out) w.sbar = sbar_out;
   GemmArgs g1;  // taubar = grad_hT @ W_T^T
   g1.A = grad_hT; g1.lda = d_node; g1.B = W_T; g1.ldb = d_node; g1.C = w.taubar; g1.ldc = d_tri;
   g1.M = n_atoms; g1.N = d_tri; g1.K = d_node;
@@ -1165,6 +1188,106 @@ int mlip_attention_tangent_vjp(
   WgradArgs q;  // d W_o = sum_i o_dot_i^T ubar_i + o_i^T ubar_dot_i
   q.A0 = o_dot; q.B0 = grad_u; q.A1 = o; q.B1 = grad_u_dot; q.lda = Da; q.ldb = Dn;
   q.P = N; q.Mo = Da; q.No = Dn; q.C = d_W_o;
+  return launch_wgrad(q, w.split, stream);
+}
+
+// ------------------------------------ three-body update: training tangents ---
+int mlip_tri_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                 int64_t n_edges, const float *grad_forces, const float *h_dot, const float *s,
+                 const float *W_s, const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
+                 int32_t d_tri, float cutoff, float *s_dot, float *tau_dot, float *hT_dot, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0;
+  if (int rc = check_tri_dims(d_node, d_tri, n_ang, cutoff, &cpl)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_s && W_ang && W_T, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && s && tau_dot && hT_dot), "null pointer argument");
+  MLIP_CHECK_ARG(!h_dot || s_dot, "h_dot needs s_dot");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h_dot, 16) && aligned(s, 16) && aligned(W_s, 16) &&
+                     aligned(W_ang, 16) && aligned(W_T, 16) && aligned(s_dot, 16) && aligned(tau_dot, 16) &&
+                     aligned(hT_dot, 16),
+                 "float arrays must be 16-byte aligned");
+  if (n_atoms == 0) return MLIP_OK;
+  if (h_dot) {
+    GemmArgs g;  // s_dot = h_dot W_s
+    g.A = h_dot; g.lda = d_node; g.B = W_s; g.ldb = d_tri; g.C = s_dot; g.ldc = d_tri;
+    g.M = n_atoms; g.N = d_tri; g.K = d_node;
+    if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  }
+  if (int rc = launch_tri_jvp(row_ptr, src, geom, n_atoms, grad_forces, -1.f, s, h_dot ? s_dot : nullptr, W_ang,
+                              d_tri, cutoff, tau_dot, stream))
+    return rc;
+  GemmArgs g2;  // hT_dot = h_dot + tau_dot W_T
+  g2.A = tau_dot; g2.lda = d_tri; g2.B = W_T; g2.ldb = d_node; g2.C = hT_dot; g2.ldc = d_node;
+  g2.R = h_dot; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_tri;
+  return launch_gemm(g2, false, h_dot ? EPI_RESID : EPI_STORE, K_GEMM_DENSE, stream);
+}
+
+size_t mlip_tri_tangent_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_node, int32_t d_tri) {
+  size_t b = 0;
+  carve_tri_tan(nullptr, std::max(n_atoms, 0), std::max<int64_t>(n_edges, 0), std::max(d_node, 0),
+                std::max(d_tri, 0), &b);
+  return b;
+}
+
+int mlip_tri_tangent_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                         int32_t n_atoms, int64_t n_edges, const float *grad_forces, const float *h,
+                         const float *h_dot, const float *s, const float *s_dot, const float *tau,
+                         const float *tau_dot, const float *sbar, const float *W_s, const float *W_ang,
+                         const float *W_T, int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff,
+                         const float *grad_hT, const float *grad_hT_dot, float *grad_h_dot, float *d_W_s,
+                         float *d_W_ang, float *d_W_T, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  int cpl = 0;
+  if (int rc = check_tri_dims(d_node, d_tri, n_ang, cutoff, &cpl)) return rc;
+  MLIP_CHECK_ARG(row_ptr && W_s && W_ang && W_T && d_W_s && d_W_ang && d_W_T, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (grad_forces && h && s && tau && tau_dot && sbar && grad_hT && grad_hT_dot),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(!h_dot || s_dot, "h_dot needs s_dot");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && rev && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(h_dot, 16) && aligned(s, 16) &&
+                     aligned(s_dot, 16) && aligned(tau, 16) && aligned(tau_dot, 16) && aligned(sbar, 16) &&
+                     aligned(W_s, 16) && aligned(W_ang, 16) && aligned(W_T, 16) && aligned(grad_hT, 16) &&
+                     aligned(grad_hT_dot, 16) && aligned(grad_h_dot, 16) && aligned(d_W_s, 16) &&
+                     aligned(d_W_ang, 16) && aligned(d_W_T, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_tri_tangent_vjp_workspace_size(n_atoms, n_edges, d_node, d_tri)))
+    return rc;
+  TriTanWs w = carve_tri_tan(ws, n_atoms, n_edges, d_node, d_tri, nullptr);
+  const int N = n_atoms, Dt = d_tri, Dn = d_node;
+  if (N > 0) {
+    GemmArgs g;  // taubar = grad_hT W_T^T, taubar_dot = grad_hT_dot W_T^T
+    g.A = grad_hT; g.lda = Dn; g.B = W_T; g.ldb = Dn; g.C = w.taubar; g.ldc = Dt;
+    g.M = N; g.N = Dt; g.K = Dn;
+    if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+    g.A = grad_hT_dot; g.C = w.taubar_dot;
+    if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+    if (int rc = launch_tri_tvjp(row_ptr, src, rev, geom, N, grad_forces, -1.f, s, h_dot ? s_dot : nullptr,
+                                 W_ang, w.taubar, w.taubar_dot, Dt, cutoff, w.sigma_dot, w.wang_part,
+                                 w.sbar_dot, stream))
+      return rc;
+  }
+  if (int rc = launch_row_sum(w.wang_part, N, MLIP_N_ANG * Dt, w.wang_part2, d_W_ang, stream)) return rc;
+  if (grad_h_dot && N > 0) {
+    GemmArgs g;  // grad_h_dot = grad_hT_dot + sbar_dot W_s^T
+    g.A = w.sbar_dot; g.lda = Dt; g.B = W_s; g.ldb = Dt; g.C = grad_h_dot; g.ldc = Dn;
+    g.R = grad_hT_dot; g.ldr = Dn; g.M = N; g.N = Dn; g.K = Dt;
+    if (int rc = launch_gemm(g, true, EPI_RESID, K_GEMM_DENSE, stream)) return rc;
+  }
+  {
+    WgradArgs q;  // d W_s = sum_i h_i^T sbar_dot_i + h_dot_i^T sbar_i
+    q.A0 = h; q.B0 = w.sbar_dot;
+    if (h_dot) { q.A1 = h_dot; q.B1 = sbar; }
+    q.lda = Dn; q.ldb = Dt; q.P = N; q.Mo = Dn; q.No = Dt; q.C = d_W_s;
+    if (int rc = launch_wgrad(q, w.split, stream)) return rc;
+  }
+  WgradArgs q;  // d W_T = sum_i tau_dot_i^T grad_hT_i + tau_i^T grad_hT_dot_i
+  q.A0 = tau_dot; q.B0 = grad_hT; q.A1 = tau; q.B1 = grad_hT_dot; q.lda = Dt; q.ldb = Dn;
+  q.P = N; q.Mo = Dt; q.No = Dn; q.C = d_W_T;
   return launch_wgrad(q, w.split, stream);
 }
 

@@ -288,5 +288,17 @@ struct TriArgs {
 int tri_lane_layout(int Dt, int *cpl);
 int launch_tri_fwd(const TriArgs &a, hipStream_t stream);
 int launch_tri_vjp(const TriArgs &a, hipStream_t stream);
+// Training tangents of the three-body update (tri.hip): tau_dot; and the
+// tangent of the gradient: sigma_dot [E][Dt] (scratch), per-row W_ang
+// gradient shares wang_part [N][4][Dt], sbar_dot [N][Dt].
+int launch_tri_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
+                   const float *x_dot, float x_sign, const float *s, const float *s_dot, const float *W_ang,
+                   int Dt, float rc, float *tau_dot, hipStream_t stream);
+int launch_tri_tvjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                    int n_atoms, const float *x_dot, float x_sign, const float *s, const float *s_dot,
+                    const float *W_ang, const float *taubar, const float *taubar_dot, int Dt, float rc,
+                    float *sigma_dot, float *wang_part, float *sbar_dot, hipStream_t stream);
+// sum over n rows of [n][KD] (fixed order, two stages; part2 holds cdiv(n, 32) x KD)
+int launch_row_sum(const float *rows, int n, int KD, float *part2, float *out, hipStream_t stream);
 
 }  // namespace mlip

@@ -781,6 +781,19 @@ int launch_edge_basis_grad(const int32_t *row_ptr, const int32_t *src, const flo
   return MLIP_OK;
 }
 
+int launch_row_sum(const float *rows, int n, int KD, float *part2, float *out, hipStream_t stream) {
+  ProfScope ps(K_EDGE_TAN, stream);
+  const int n2 = int(cdiv(std::max(n, 0), DWE_SPAN));
+  if (n2 > 0) {
+    dwe_stage1_kernel<<<dim3(unsigned(cdiv(KD, 256)), unsigned(n2)), dim3(256), 0, stream>>>(rows, n, KD,
+                                                                                             part2);
+    MLIP_LAUNCHED();
+  }
+  dwe_sum_kernel<<<dim3(unsigned(cdiv(KD, 256))), dim3(256), 0, stream>>>(part2, n2, KD, out);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 int launch_moe_tan(const float *P, const float *P_dot, const float *Q, const float *Q_dot, int M, int H,
                    float *act, float *act_dot, float *D, float *D_dot, float *dg, hipStream_t stream) {
   if (M <= 0) return MLIP_OK;

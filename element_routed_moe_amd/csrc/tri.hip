@@ -31,6 +31,8 @@
 
 namespace mlip {
 
+int tri_lane_layout(int Dt, int *cpl);
+
 namespace {
 
 constexpr int NSH = 16;      // (l, m) for l = 0..3
@@ -472,6 +474,318 @@ int dispatch(int which, const TriArgs &a, hipStream_t stream) {
   return MLIP_ERR_UNSUPPORTED;
 }
 
+// ------------------------------------------------------------ tangents ---
+// Training gradient: derivatives along the position direction x_dot (d_dot =
+// x_dot_j - x_dot_i, r_dot = dhat . d_dot, dhat_dot = (d_dot - dhat r_dot) / r,
+// f_dot = f_c' r_dot) and the feature tangent s_dot = h_dot W_s:
+//   y_e = f S(dhat),  y_dot = f_dot S + f (grad S . dhat_dot)
+//   A_dot = sum_e y_dot s_j + y s_dot_j,   B_dot = sum_e 2 f f_dot s_j^2 + 2 f^2 s_j s_dot_j
+//   tau_dot = sum_l W_ang[l] (2 sum_m A A_dot - B_dot)
+// and of the gradient (Abar = 2 taubar W A, Bbar = -taubar sum_l W):
+//   sigma_dot_e = sum_lm (Abar_dot y + Abar y_dot) + 2 Bbar_dot f^2 s_j + 2 Bbar (2 f f_dot s_j + f^2 s_dot_j)
+//   dW_ang[l] += taubar_dot (sum_m A^2 - B) + taubar (2 sum_m A A_dot - B_dot)    (per row)
+// The channels of a row are split over "slices" (workgroups of the same row)
+// so that A and A_dot of 16 harmonics fit the registers; the per-edge
+// harmonics are computed once per slice.
+
+// directional derivatives grad S_lm . v of the 16 harmonics at (x, y, z)
+__device__ inline void harmonics_dir(float x, float y, float z, float vx, float vy, float vz, float *D) {
+  const float r3 = 1.7320508075688772f, r15 = 3.872983346207417f;
+  const float a58 = 0.7905694150420949f, a38 = 0.6123724356957945f;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  D[0] = 0.f;
+  D[1] = vx; D[2] = vy; D[3] = vz;
+  D[4] = r3 * (y * vx + x * vy);
+  D[5] = r3 * (z * vy + y * vz);
+  D[6] = 3.f * z * vz;
+  D[7] = r3 * (z * vx + x * vz);
+  D[8] = r3 * (x * vx - y * vy);
+  D[9] = a58 * (6.f * x * y * vx + 3.f * (xx - yy) * vy);
+  D[10] = r15 * (y * z * vx + x * z * vy + x * y * vz);
+  D[11] = a38 * ((5.f * zz - 1.f) * vy + 10.f * y * z * vz);
+  D[12] = 0.5f * (15.f * zz - 3.f) * vz;
+  D[13] = a38 * ((5.f * zz - 1.f) * vx + 10.f * x * z * vz);
+  D[14] = r15 * (x * z * vx - y * z * vy + 0.5f * (xx - yy) * vz);
+  D[15] = a58 * (3.f * (xx - yy) * vx - 6.f * x * y * vy);
+}
+
+struct TriTanRow {
+  const int32_t *src;
+  const float4 *geom;
+  const float *s, *s_dot;   // s_dot may be null
+  const float *x_dot;
+  float x_sign;
+  int Dt, c0, i;
+};
+
+// y, y_dot, f^2 and 2 f f_dot of the chunk's edges into LDS (lane = edge)
+__device__ inline void tan_edge_terms(const TriTanRow &t, const Radial &R, int e, float xi0, float xi1,
+                                      float xi2, float (*ysh)[NSH], float (*ydt)[NSH], float *fsq,
+                                      float *ffd, int *jj, int lane) {
+  const EdgeGeo G = edge_geo(t.geom[e], R);
+  const int j = t.src[e];
+  const float dx = t.x_sign * (t.x_dot[3 * j] - xi0), dy = t.x_sign * (t.x_dot[3 * j + 1] - xi1),
+              dz = t.x_sign * (t.x_dot[3 * j + 2] - xi2);
+  const float rd = G.u.x * dx + G.u.y * dy + G.u.z * dz;
+  const float vx = (dx - G.u.x * rd) * G.inv_r, vy = (dy - G.u.y * rd) * G.inv_r,
+              vz = (dz - G.u.z * rd) * G.inv_r;
+  float S[NSH], D[NSH];
+  harmonics(G.u.x, G.u.y, G.u.z, S);
+  harmonics_dir(G.u.x, G.u.y, G.u.z, vx, vy, vz, D);
+  const float fd = G.dfc * rd;
+#pragma unroll
+  for (int lm = 0; lm < NSH; ++lm) {
+    ysh[lane][lm] = G.fc * S[lm];
+    ydt[lane][lm] = fd * S[lm] + G.fc * D[lm];
+  }
+  fsq[lane] = G.fc * G.fc;
+  ffd[lane] = 2.f * G.fc * fd;
+  jj[lane] = j;
+}
+
+template <int CPL>
+__device__ inline void tan_accumulate(const TriTanRow &t, int r0, int r1, const Radial &R, float (*ysh)[NSH],
+                                      float (*ydt)[NSH], float *fsq, float *ffd, int *jj,
+                                      float (&A)[NSH][CPL], float (&Ad)[NSH][CPL], float (&Bs)[CPL],
+                                      float (&Bd)[CPL]) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int lm = 0; lm < NSH; ++lm)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) A[lm][c] = Ad[lm][c] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) Bs[c] = Bd[c] = 0.f;
+  const float xi0 = t.x_dot[3 * t.i], xi1 = t.x_dot[3 * t.i + 1], xi2 = t.x_dot[3 * t.i + 2];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) tan_edge_terms(t, R, e0 + lane, xi0, xi1, xi2, ysh, ydt, fsq, ffd, jj, lane);
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      float sj[CPL], sd[CPL];
+      const int64_t j = jj[me];
+      ldc<CPL>(t.s + j * t.Dt + t.c0, sj);
+      if (t.s_dot) ldc<CPL>(t.s_dot + j * t.Dt + t.c0, sd);
+      else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sd[c] = 0.f;
+      }
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) {
+        const float y = ysh[me][lm], yd = ydt[me][lm];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          A[lm][c] += y * sj[c];
+          Ad[lm][c] += yd * sj[c] + y * sd[c];
+        }
+      }
+      const float fq = fsq[me], fd2 = ffd[me];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        Bs[c] += fq * sj[c] * sj[c];
+        Bd[c] += fd2 * sj[c] * sj[c] + 2.f * fq * sj[c] * sd[c];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+struct TriTanArgs {
+  const int32_t *row_ptr, *src, *rev;
+  const float *geom;
+  int n_atoms;
+  const float *x_dot;
+  float x_sign;
+  const float *s, *s_dot, *W_ang, *taubar, *taubar_dot;
+  float *tau_dot, *sigma_dot, *wang_part, *sbar_dot;
+  int Dt, n_slices;
+  float rc;
+};
+
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_jvp_kernel(TriTanArgs a) {
+  __shared__ float ysh[CHUNK][NSH], ydt[CHUNK][NSH];
+  __shared__ float fsq[CHUNK], ffd[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(int64_t(a.n_atoms) * a.n_slices);
+  if (blk < 0) return;
+  const int i = int(blk / a.n_slices), slice = int(blk - int64_t(i) * a.n_slices);
+  const int cc = (slice * 64 + lane) * CPL;
+  const bool active = cc < a.Dt;
+  TriTanRow t{a.src, reinterpret_cast<const float4 *>(a.geom), a.s, a.s_dot, a.x_dot, a.x_sign, a.Dt,
+              active ? cc : 0, i};
+  const Radial R = make_radial(a.rc);
+  float A[NSH][CPL], Ad[NSH][CPL], Bs[CPL], Bd[CPL];
+  tan_accumulate<CPL>(t, a.row_ptr[i], a.row_ptr[i + 1], R, ysh, ydt, fsq, ffd, jj, A, Ad, Bs, Bd);
+  if (!active) return;
+  float w[NANG][CPL], out[CPL];
+#pragma unroll
+  for (int l = 0; l < NANG; ++l) ldc<CPL>(a.W_ang + int64_t(l) * a.Dt + t.c0, w[l]);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float qd[NANG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int lm = 0; lm < NSH; ++lm) qd[l_of(lm)] += 2.f * A[lm][c] * Ad[lm][c];
+    float acc = 0.f;
+#pragma unroll
+    for (int l = 0; l < NANG; ++l) acc += w[l][c] * (qd[l] - Bd[c]);
+    out[c] = acc;
+  }
+  stc<CPL>(a.tau_dot + int64_t(i) * a.Dt + t.c0, out);
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_tvjp_recv_kernel(TriTanArgs a) {
+  __shared__ float ysh[CHUNK][NSH], ydt[CHUNK][NSH];
+  __shared__ float fsq[CHUNK], ffd[CHUNK];
+  __shared__ int jj[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(int64_t(a.n_atoms) * a.n_slices);
+  if (blk < 0) return;
+  const int i = int(blk / a.n_slices), slice = int(blk - int64_t(i) * a.n_slices);
+  const int cc = (slice * 64 + lane) * CPL;
+  const bool active = cc < a.Dt;
+  TriTanRow t{a.src, reinterpret_cast<const float4 *>(a.geom), a.s, a.s_dot, a.x_dot, a.x_sign, a.Dt,
+              active ? cc : 0, i};
+  const Radial R = make_radial(a.rc);
+  const int r0 = a.row_ptr[i], r1 = a.row_ptr[i + 1];
+  float A[NSH][CPL], Ad[NSH][CPL], Bs[CPL], Bd[CPL];
+  tan_accumulate<CPL>(t, r0, r1, R, ysh, ydt, fsq, ffd, jj, A, Ad, Bs, Bd);
+  // W_ang gradient share of this row, then Abar / Abar_dot / Bbar / Bbar_dot in place
+  {
+    float w[NANG][CPL], tb[CPL], tbd[CPL];
+#pragma unroll
+    for (int l = 0; l < NANG; ++l) ldc<CPL>(a.W_ang + int64_t(l) * a.Dt + t.c0, w[l]);
+    ldc<CPL>(a.taubar + int64_t(i) * a.Dt + t.c0, tb);
+    ldc<CPL>(a.taubar_dot + int64_t(i) * a.Dt + t.c0, tbd);
+    float wp[NANG][CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float q[NANG] = {0.f, 0.f, 0.f, 0.f}, qd[NANG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) {
+        q[l_of(lm)] += A[lm][c] * A[lm][c];
+        qd[l_of(lm)] += 2.f * A[lm][c] * Ad[lm][c];
+      }
+      float wsum = 0.f;
+#pragma unroll
+      for (int l = 0; l < NANG; ++l) {
+        wp[l][c] = tbd[c] * (q[l] - Bs[c]) + tb[c] * (qd[l] - Bd[c]);
+        wsum += w[l][c];
+      }
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) {
+        const float wl = w[l_of(lm)][c];
+        const float ab = 2.f * tb[c] * wl * A[lm][c];
+        Ad[lm][c] = active ? 2.f * (tbd[c] * wl * A[lm][c] + tb[c] * wl * Ad[lm][c]) : 0.f;
+        A[lm][c] = active ? ab : 0.f;
+      }
+      Bs[c] = active ? -tb[c] * wsum : 0.f;
+      Bd[c] = active ? -tbd[c] * wsum : 0.f;
+    }
+    if (active) {
+#pragma unroll
+      for (int l = 0; l < NANG; ++l) stc<CPL>(a.wang_part + (int64_t(i) * NANG + l) * a.Dt + t.c0, wp[l]);
+    }
+  }
+  // edges again: sigma_dot_e
+  const float xi0 = a.x_dot[3 * i], xi1 = a.x_dot[3 * i + 1], xi2 = a.x_dot[3 * i + 2];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) tan_edge_terms(t, R, e0 + lane, xi0, xi1, xi2, ysh, ydt, fsq, ffd, jj, lane);
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      float sj[CPL], sd[CPL], out[CPL];
+      const int64_t j = jj[me];
+      ldc<CPL>(a.s + j * a.Dt + t.c0, sj);
+      if (a.s_dot) ldc<CPL>(a.s_dot + j * a.Dt + t.c0, sd);
+      else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sd[c] = 0.f;
+      }
+      const float fq = fsq[me], fd2 = ffd[me];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        out[c] = 2.f * Bd[c] * fq * sj[c] + 2.f * Bs[c] * (fd2 * sj[c] + fq * sd[c]);
+#pragma unroll
+      for (int lm = 0; lm < NSH; ++lm) {
+        const float y = ysh[me][lm], yd = ydt[me][lm];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) out[c] += Ad[lm][c] * y + A[lm][c] * yd;
+      }
+      if (active) stc<CPL>(a.sigma_dot + int64_t(e0 + me) * a.Dt + t.c0, out);
+    }
+    __syncthreads();
+  }
+}
+
+// sbar_dot_j = sum over the edges j <- i of sigma_dot of the reverse edge
+template <int CPL>
+__global__ void __launch_bounds__(64) tri_tvjp_send_kernel(TriTanArgs a) {
+  __shared__ int rr[CHUNK];
+  const int lane = threadIdx.x;
+  const int64_t blk = xcd_block(int64_t(a.n_atoms) * a.n_slices);
+  if (blk < 0) return;
+  const int j = int(blk / a.n_slices), slice = int(blk - int64_t(j) * a.n_slices);
+  const int cc = (slice * 64 + lane) * CPL;
+  const bool active = cc < a.Dt;
+  const int c0 = active ? cc : 0;
+  float sb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sb[c] = 0.f;
+  const int r0 = a.row_ptr[j], r1 = a.row_ptr[j + 1];
+  for (int e0 = r0; e0 < r1; e0 += CHUNK) {
+    const int n = min(CHUNK, r1 - e0);
+    if (lane < n) rr[lane] = a.rev[e0 + lane];
+    __syncthreads();
+    for (int me = 0; me < n; ++me) {
+      float sg[CPL];
+      ldc<CPL>(a.sigma_dot + int64_t(rr[me]) * a.Dt + c0, sg);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) sb[c] += sg[c];
+    }
+    __syncthreads();
+  }
+  if (active) stc<CPL>(a.sbar_dot + int64_t(j) * a.Dt + c0, sb);
+}
+
+template <int CPL>
+int launch_tan_cpl(int which, const TriTanArgs &a, hipStream_t stream) {
+  const dim3 grid(unsigned(padded_grid(int64_t(a.n_atoms) * a.n_slices))), block(64);
+  if (which == 0) tri_jvp_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  else if (which == 1) tri_tvjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  else tri_tvjp_send_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+// channels per lane of the tangent kernels: at most 4 (A and A_dot in
+// registers); wider rows are split into two slices
+int tan_layout(int Dt, int *cpl_t, int *n_slices) {
+  int cpl = 0;
+  if (tri_lane_layout(Dt, &cpl) != MLIP_OK) return MLIP_ERR_UNSUPPORTED;
+  *cpl_t = cpl <= 4 ? cpl : cpl / 2;
+  *n_slices = int(cdiv(Dt, 64 * *cpl_t));
+  return MLIP_OK;
+}
+
+int dispatch_tan(int which, TriTanArgs a, hipStream_t stream) {
+  int c = 0;
+  if (tan_layout(a.Dt, &c, &a.n_slices) != MLIP_OK) {
+    set_error("d_tri = %d has no three-body lane layout", a.Dt);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  switch (c) {
+    case 1: return launch_tan_cpl<1>(which, a, stream);
+    case 2: return launch_tan_cpl<2>(which, a, stream);
+    case 3: return launch_tan_cpl<3>(which, a, stream);
+    case 4: return launch_tan_cpl<4>(which, a, stream);
+    default: break;
+  }
+  set_error("no three-body tangent layout for %d channels per lane", c);
+  return MLIP_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 int tri_lane_layout(int Dt, int *cpl) {
@@ -499,6 +813,36 @@ int launch_tri_vjp(const TriArgs &a, hipStream_t stream) {
   }
   ProfScope ps(K_TRI_VJP_SEND, stream);
   return dispatch(2, a, stream);
+}
+
+int launch_tri_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
+                   const float *x_dot, float x_sign, const float *s, const float *s_dot, const float *W_ang,
+                   int Dt, float rc, float *tau_dot, hipStream_t stream) {
+  if (n_atoms <= 0) return MLIP_OK;
+  ProfScope ps(K_TRI_FWD, stream);
+  TriTanArgs a{};
+  a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;
+  a.x_dot = x_dot; a.x_sign = x_sign; a.s = s; a.s_dot = s_dot; a.W_ang = W_ang;
+  a.tau_dot = tau_dot; a.Dt = Dt; a.rc = rc;
+  return dispatch_tan(0, a, stream);
+}
+
+int launch_tri_tvjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                    int n_atoms, const float *x_dot, float x_sign, const float *s, const float *s_dot,
+                    const float *W_ang, const float *taubar, const float *taubar_dot, int Dt, float rc,
+                    float *sigma_dot, float *wang_part, float *sbar_dot, hipStream_t stream) {
+  if (n_atoms <= 0) return MLIP_OK;
+  TriTanArgs a{};
+  a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = n_atoms;
+  a.x_dot = x_dot; a.x_sign = x_sign; a.s = s; a.s_dot = s_dot; a.W_ang = W_ang;
+  a.taubar = taubar; a.taubar_dot = taubar_dot; a.sigma_dot = sigma_dot; a.wang_part = wang_part;
+  a.sbar_dot = sbar_dot; a.Dt = Dt; a.rc = rc;
+  {
+    ProfScope ps(K_TRI_VJP_RECV, stream);
+    if (int rc2 = dispatch_tan(1, a, stream)) return rc2;
+  }
+  ProfScope ps(K_TRI_VJP_SEND, stream);
+  return dispatch_tan(2, a, stream);
 }
 
 }  // namespace mlip

@@ -95,7 +95,12 @@ _SIGS = {
                            _p, _p]),
     "mlip_tri_vjp_workspace_size": (_sz, [_i32, _i64, _i32]),
     "mlip_tri_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
-                               _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _sz, _p]),
+                               _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
+    "mlip_tri_jvp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+                               _p, _p, _p, _p]),
+    "mlip_tri_tangent_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32]),
+    "mlip_tri_tangent_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                       _p, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "mlip_profile_enable": (C.c_int, [C.c_int]),
     "mlip_profile_reset": (C.c_int, []),
     "mlip_profile_count": (C.c_int, []),
@@ -547,7 +552,8 @@ def mlip_tri(graph, h, W_s, W_ang, W_T, cutoff: float, out: Optional[Dict] = Non
 
 def mlip_tri_vjp(graph, tri, W_s, W_ang, W_T, cutoff: float, grad_hT, grad_pos, atom_virial=None,
                  grad_strain=None, struct_ptr=None, accumulate: bool = False,
-                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 sbar_out: Optional[torch.Tensor] = None):
     """dL/dh of the three-body update; grad_pos / atom_virial are written, or added
     to when ``accumulate`` (then grad_strain is recomputed from atom_virial)."""
     N, Dn = int(grad_hT.shape[0]), int(grad_hT.shape[1])
@@ -564,8 +570,54 @@ def mlip_tri_vjp(graph, tri, W_s, W_ang, W_T, cutoff: float, grad_hT, grad_pos, 
                              _ptr(graph["geom"]), N, E, _ptr(tri["s"]), _ptr(W_s), _ptr(W_ang), _ptr(W_T),
                              int(W_ang.shape[0]), Dn, Dt, float(cutoff), _ptr(grad_hT), _ptr(out),
                              _ptr(grad_pos), _ptr(struct_ptr), B, _ptr(atom_virial), _ptr(grad_strain),
-                             1 if accumulate else 0, _ptr(ws), ws.numel(), _stream()))
+                             1 if accumulate else 0, _ptr(sbar_out), _ptr(ws), ws.numel(), _stream()))
     return out, ws
+
+
+def mlip_tri_jvp(graph, tri, W_s, W_ang, W_T, cutoff: float, grad_forces, h_dot=None,
+                 out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    """Forward tangent of the three-body update: s_dot (with h_dot), tau_dot, hT_dot."""
+    N, Dt = int(tri["s"].shape[0]), int(W_s.shape[1])
+    Dn = int(W_s.shape[0])
+    E = int(graph["n_edges"])
+    dev = tri["s"].device
+    f32 = torch.float32
+    if out is None:
+        out = dict(s_dot=torch.empty((N, Dt), dtype=f32, device=dev) if h_dot is not None else None,
+                   tau_dot=torch.empty((N, Dt), dtype=f32, device=dev),
+                   hT_dot=torch.empty((N, Dn), dtype=f32, device=dev))
+    _check(_lib.mlip_tri_jvp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                             _ptr(grad_forces), _ptr(h_dot), _ptr(tri["s"]), _ptr(W_s), _ptr(W_ang), _ptr(W_T),
+                             int(W_ang.shape[0]), Dn, Dt, float(cutoff), _ptr(out["s_dot"]), _ptr(out["tau_dot"]),
+                             _ptr(out["hT_dot"]), _stream()))
+    return out
+
+
+def mlip_tri_tangent_vjp(graph, tri, tjvp, h, sbar, W_s, W_ang, W_T, cutoff: float, grad_forces, grad_hT,
+                         grad_hT_dot, h_dot=None, want_grad_h_dot: bool = True, out: Optional[Dict] = None,
+                         ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Tangent of the three-body update's gradient: grad_h_dot, d_W_s, d_W_ang, d_W_T."""
+    N, Dn = int(h.shape[0]), int(h.shape[1])
+    Dt = int(W_s.shape[1])
+    E = int(graph["n_edges"])
+    dev = h.device
+    f32 = torch.float32
+    if out is None:
+        out = dict(grad_h_dot=torch.empty((N, Dn), dtype=f32, device=dev) if want_grad_h_dot else None,
+                   d_W_s=torch.empty(tuple(W_s.shape), dtype=f32, device=dev),
+                   d_W_ang=torch.empty(tuple(W_ang.shape), dtype=f32, device=dev),
+                   d_W_T=torch.empty(tuple(W_T.shape), dtype=f32, device=dev))
+    need = _lib.mlip_tri_tangent_vjp_workspace_size(N, E, Dn, Dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(_lib.mlip_tri_tangent_vjp(
+        _ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["rev"]), _ptr(graph["geom"]), N, E,
+        _ptr(grad_forces), _ptr(h), _ptr(h_dot), _ptr(tri["s"]), _ptr(tjvp["s_dot"]), _ptr(tri["tau"]),
+        _ptr(tjvp["tau_dot"]), _ptr(sbar), _ptr(W_s), _ptr(W_ang), _ptr(W_T), int(W_ang.shape[0]), Dn, Dt,
+        float(cutoff), _ptr(grad_hT), _ptr(grad_hT_dot), _ptr(out["grad_h_dot"]), _ptr(out["d_W_s"]),
+        _ptr(out["d_W_ang"]), _ptr(out["d_W_T"]), _ptr(ws), ws.numel(), _stream()))
+    out["ws"] = ws
+    return out
 
 
 # ------------------------------------------------------------------ timing
@@ -742,12 +794,14 @@ class FullBlock:
         self.edge_capacity = None
         self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
         self.ubar = self.avjp = self.grad_hT = self.grad_h = None
-        self.g_up = self.Q0 = self.Q1 = None
+        self.g_up = self.Q0 = self.Q1 = self.tri_sbar = None
         self.h_in = None
         if self.train:
             M = N * self.top_k
             self.Q0 = torch.empty((M, H), dtype=f32, device=device)
             self.Q1 = torch.empty((M, H), dtype=f32, device=device)
+            if self.has_tri:
+                self.tri_sbar = torch.empty((N, int(self.W_s.shape[1])), dtype=f32, device=device)
 
     def forward(self, g, h):
         """One block on graph g for input features h; returns h' (MoE1 output)."""
@@ -785,7 +839,7 @@ class FullBlock:
                 g, self.tri, self.W_s, self.W_ang, self.W_T, self.cutoff, self.grad_hT,
                 self.avjp["grad_pos"], atom_virial=self.avjp["atom_virial"],
                 grad_strain=self.avjp["grad_strain"], struct_ptr=self.struct_ptr, accumulate=True,
-                out=self.grad_h, ws=self.ws_tvjp)
+                out=self.grad_h, ws=self.ws_tvjp, sbar_out=self.tri_sbar)
         else:
             self.grad_h = mlip_moe_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.avjp["grad_h0"],
                                        out=self.grad_h, ws=self.ws_mvjp, q_out=self.Q0)
@@ -796,9 +850,13 @@ class FullBlock:
         ``forward``; returns h_out_dot."""
         if not self.train:
             raise RuntimeError("tangents need FullBlock(train=True)")
+        self.h_dot = h_dot
         if self.has_tri:
-            raise NotImplementedError("training tangents of the three-body update are not built")
-        hT_dot = h_dot if h_dot is not None else torch.zeros_like(self.h_in)
+            self.tjvp = mlip_tri_jvp(g, self.tri, self.W_s, self.W_ang, self.W_T, self.cutoff, grad_forces,
+                                     h_dot=h_dot, out=getattr(self, "tjvp", None))
+            hT_dot = self.tjvp["hT_dot"]
+        else:
+            hT_dot = h_dot if h_dot is not None else torch.zeros_like(self.h_in)
         self.hT_dot = hT_dot
         self.m0jvp = mlip_moe_jvp(self.moe0, self.z, self.W1_0, self.W2_0, hT_dot,
                                   out=getattr(self, "m0jvp", None))
@@ -821,13 +879,21 @@ class FullBlock:
                                         self.cutoff, grad_forces, self.ubar, m1["grad_in_dot"],
                                         out=getattr(self, "atan", None))
         self.atan = at
-        m0 = mlip_moe_tangent_vjp(self.moe0, self.z, self.W1_0, self.W2_0, self.h_in, self.hT_dot,
+        hT = self.tri["h_T"] if self.has_tri else self.h_in
+        m0 = mlip_moe_tangent_vjp(self.moe0, self.z, self.W1_0, self.W2_0, hT, self.hT_dot,
                                   self.m0jvp["P_dot"], self.avjp["grad_h0"], self.Q0,
                                   grad_out_dot=at["grad_h0_dot"], out=getattr(self, "m0tan", None))
         self.m0tan = m0
-        return dict(d_W1=m1["d_W1"], d_W2=m1["d_W2"], d_logits=m1["d_logits"],
-                    d_W_qkv=at["d_W_qkv"], d_Wa_e=at["d_Wa_e"], d_W_o=at["d_W_o"],
-                    d_W1_0=m0["d_W1"], d_W2_0=m0["d_W2"], d_logits0=m0["d_logits"], d_h=m0["grad_in_dot"])
+        res = dict(d_W1=m1["d_W1"], d_W2=m1["d_W2"], d_logits=m1["d_logits"],
+                   d_W_qkv=at["d_W_qkv"], d_Wa_e=at["d_Wa_e"], d_W_o=at["d_W_o"],
+                   d_W1_0=m0["d_W1"], d_W2_0=m0["d_W2"], d_logits0=m0["d_logits"], d_h=m0["grad_in_dot"])
+        if self.has_tri:
+            tt = mlip_tri_tangent_vjp(g, self.tri, self.tjvp, self.h_in, self.tri_sbar, self.W_s, self.W_ang,
+                                      self.W_T, self.cutoff, grad_forces, self.grad_hT, m0["grad_in_dot"],
+                                      h_dot=self.h_dot, out=getattr(self, "ttan", None))
+            self.ttan = tt
+            res.update(d_W_s=tt["d_W_s"], d_W_ang=tt["d_W_ang"], d_W_T=tt["d_W_T"], d_h=tt["grad_h_dot"])
+        return res
 
     def train_grad(self, grad_energy, grad_forces) -> Dict[str, torch.Tensor]:
         """Parameter gradients of a loss L(E, F) after ``step()`` (built with

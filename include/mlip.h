@@ -485,8 +485,35 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
                  const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
                  int32_t d_tri, float cutoff, const float *grad_hT, float *grad_h,
                  float *grad_pos, const int32_t *struct_ptr, int32_t n_structs,
-                 float *atom_virial, double *grad_strain, int32_t accumulate, void *ws,
+                 float *atom_virial, double *grad_strain, int32_t accumulate, float *sbar_out, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Training tangents of the three-body update ([review] 3.3; the scheme of
+ * the core block's training gradient), x_dot = -grad_forces.  sbar_out of
+ * mlip_tri_vjp (may be NULL) keeps sbar = dL/ds [N,d_tri] for them.
+ *
+ * mlip_tri_jvp: s_dot = h_dot W_s (when h_dot, may be NULL: 0),
+ *   tau_dot [N,d_tri] (with r_dot, dhat_dot and the harmonics' directional
+ *   derivatives), hT_dot = h_dot + tau_dot W_T.  s: mlip_tri's.
+ * mlip_tri_tangent_vjp: the derivative along (x_dot, h_dot, grad_hT_dot) of
+ *   the update's gradient for the upstream grad_hT: grad_h_dot (may be
+ *   NULL), d_W_s [d_node,d_tri], d_W_ang [n_ang,d_tri], d_W_T [d_tri,d_node].
+ *   Inputs h, s, tau (forward), s_dot, tau_dot (JVP), sbar (sbar_out).
+ *   Workspace: mlip_tri_tangent_vjp_workspace_size().
+ * ------------------------------------------------------------------------ */
+int mlip_tri_jvp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                 int64_t n_edges, const float *grad_forces, const float *h_dot, const float *s,
+                 const float *W_s, const float *W_ang, const float *W_T, int32_t n_ang, int32_t d_node,
+                 int32_t d_tri, float cutoff, float *s_dot, float *tau_dot, float *hT_dot, void *stream);
+size_t mlip_tri_tangent_vjp_workspace_size(int32_t n_atoms, int64_t n_edges, int32_t d_node, int32_t d_tri);
+int mlip_tri_tangent_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev, const float *geom,
+                         int32_t n_atoms, int64_t n_edges, const float *grad_forces, const float *h,
+                         const float *h_dot, const float *s, const float *s_dot, const float *tau,
+                         const float *tau_dot, const float *sbar, const float *W_s, const float *W_ang,
+                         const float *W_T, int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff,
+                         const float *grad_hT, const float *grad_hT_dot, float *grad_h_dot, float *d_W_s,
+                         float *d_W_ang, float *d_W_T, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Element embedding of the input node features ([news] architecture

@@ -131,7 +131,7 @@ def test_tri_rejects_bad_args(mlip):
 
     def vjp(accumulate, atom_virial, grad_strain, ws_bytes=1 << 30):
         return L.mlip_tri_vjp(f, f, f, f, 10, 20, f, f, f, f, 4, 64, 32, 5.0, f, f, f, f, 1,
-                              atom_virial, grad_strain, accumulate, f, ws_bytes, None)
+                              atom_virial, grad_strain, accumulate, None, f, ws_bytes, None)
     assert "accumulated atom_virial" in _err(mlip, vjp(1, None, f), mlip.MLIP_ERR_INVALID)
     assert "workspace" in _err(mlip, vjp(0, f, f, 16), mlip.MLIP_ERR_INVALID)
     assert L.mlip_tri_vjp_workspace_size(4096, 200000, 384) >= 200000 * (384 + 4) * 4
@@ -185,3 +185,8 @@ def test_training_entry_points_reject_bad_args(mlip):
     rc = L.mlip_attention_tangent_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, f, f, f, f, f, f, f, 16, 64, 100,
                                       5, 5.0, f, f, None, f, f, f, f, 1 << 30, None)
     assert "unsupported attention shape" in _err(mlip, rc, mlip.MLIP_ERR_UNSUPPORTED)
+    rc = L.mlip_tri_jvp(f, f, f, 10, 20, f, f, f, f, f, f, 4, 64, 32, 5.0, None, f, f, None)
+    assert "h_dot needs s_dot" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_tri_tangent_vjp(f, f, f, f, 10, 20, f, f, None, f, None, f, f, f, f, f, f, 4, 64, 32, 5.0,
+                                f, f, None, f, f, f, f, 16, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)

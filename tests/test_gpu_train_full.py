@@ -3,9 +3,9 @@ neighbour attention -> MoE1 -> readout) against ``oracle.train.full_loss_grads``
 
 Loss upstreams are seeded random (dL/dE per structure, dL/dF per component);
 every gradient tensor (both MoE layers' experts and logits, W_qkv, Wa_e,
-W_o, w_r and dL/dh) must satisfy max|gpu - oracle| / max|oracle| <= 2e-4.
-These cases leave out the three-body update (its training tangents are a
-separate piece).
+W_o, the three-body W_s, W_ang, W_T, w_r and dL/dh) must satisfy
+max|gpu - oracle| / max|oracle| <= 2e-4.  Cases run with and without the
+three-body update.
 """
 import sys
 
@@ -52,14 +52,20 @@ def _no_tri(inp):
     return q
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "sparse", "top1", "wide_ragged", "triclinic"])
-def test_full_block_train_grad(mlip, name):
+CASES = ([(n, False) for n in ["tiny", "ragged", "sparse", "top1", "wide_ragged", "triclinic"]]
+         + [(n, True) for n in ["tiny", "sparse", "top1", "wide_ragged", "triclinic"]])
+
+
+@pytest.mark.parametrize("name,tri", CASES)
+def test_full_block_train_grad(mlip, name, tri):
     cfg = synth.CONFIGS[name]
-    inp = _no_tri(synth.make_full_inputs(cfg))
+    inp = synth.make_full_inputs(cfg)
+    if not tri:
+        inp = _no_tri(inp)
     rng = np.random.default_rng(29)
     Ebar = rng.standard_normal(cfg.n_structs)
     Fbar = rng.standard_normal((cfg.n_atoms, 3)).astype(np.float32)
-    _say(f"{name}: oracle (N={cfg.n_atoms}, heads {cfg.n_heads} x {cfg.d_attn // cfg.n_heads})")
+    _say(f"{name} (tri={tri}): oracle (N={cfg.n_atoms}, heads {cfg.n_heads} x {cfg.d_attn // cfg.n_heads})")
     g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
     ref = TR.full_loss_grads(inp, g, Ebar, Fbar.astype(np.float64))
     _say(f"{name}: GPU")
@@ -67,7 +73,8 @@ def test_full_block_train_grad(mlip, name):
     res = blk.train_grad(torch.tensor(Ebar, dtype=torch.float64, device="cuda"),
                          torch.from_numpy(Fbar).to("cuda"))
     torch.cuda.synchronize()
-    errs = {k: rel(res[k], ref[k]) for k in KEYS}
+    keys = KEYS + (["d_W_s", "d_W_ang", "d_W_T"] if tri else [])
+    errs = {k: rel(res[k], ref[k]) for k in keys}
     errs["F"] = rel(-blk.avjp["grad_pos"], ref["F"])
     _say(f"{name}: errors {errs}")
     bad = {k: e for k, e in errs.items() if not e <= TOL}
