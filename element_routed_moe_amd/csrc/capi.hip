@@ -27,6 +27,8 @@ int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, 
             float *eps, double *energy, hipStream_t stream);
 int embed_atoms(const int32_t *z, const float *table, int N, int T, int D, float *h,
                 hipStream_t stream);
+int embed_grad(const int32_t *z, const float *grad_h, int N, int T, int D, float *d_table,
+               hipStream_t stream);
 int launch_readout_seed(const float *w_r, const double *Ebar, const int32_t *struct_ptr, int N, int B,
                         int D, float *g, hipStream_t stream);
 
@@ -1302,6 +1304,17 @@ int mlip_embed_atoms(const int32_t *z, const float *table, int32_t n_atoms, int3
   MLIP_CHECK_ARG(aligned(table, 16) && aligned(h, 16), "float arrays must be 16-byte aligned");
   if (n_atoms == 0) return MLIP_OK;
   return embed_atoms(z, table, n_atoms, n_types, d_node, h, stream);
+}
+
+int mlip_embed_grad(const int32_t *z, const float *grad_h, int32_t n_atoms, int32_t n_types, int32_t d_node,
+                    float *d_table, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(d_table && (n_atoms == 0 || (z && grad_h)), "null pointer argument");
+  MLIP_CHECK_ARG(aligned(grad_h, 16) && aligned(d_table, 16), "float arrays must be 16-byte aligned");
+  return embed_grad(z, grad_h, n_atoms, n_types, d_node, d_table, stream);
 }
 
 }  // extern "C"

@@ -290,6 +290,36 @@ int embed_atoms(const int32_t *z, const float *table, int N, int T, int D, float
   return MLIP_OK;
 }
 
+// d_table[t] = sum over atoms with z_i = t of grad_h_i (atoms in index order;
+// one thread per (type, float4 column), the type test is uniform per wave).
+__global__ void __launch_bounds__(64) embed_grad_kernel(const int32_t *__restrict__ z,
+                                                        const float4 *__restrict__ grad_h, int N, int D4,
+                                                        float4 *__restrict__ d_table) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 64 + threadIdx.x;
+  if (c >= D4) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < N; ++i) {
+    if (z[i] != t) continue;
+    const float4 v = grad_h[int64_t(i) * D4 + c];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  d_table[int64_t(t) * D4 + c] = acc;
+}
+
+int embed_grad(const int32_t *z, const float *grad_h, int N, int T, int D, float *d_table,
+               hipStream_t stream) {
+  ProfScope ps(K_MOE_TAN, stream);
+  const int D4 = D / 4;
+  embed_grad_kernel<<<dim3(unsigned(cdiv(D4, 64)), unsigned(T)), dim3(64), 0, stream>>>(
+      z, reinterpret_cast<const float4 *>(grad_h), N, D4, reinterpret_cast<float4 *>(d_table));
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, int B, int D,
             float *eps, double *energy, hipStream_t stream) {
   ProfScope ps(K_READOUT, stream);

@@ -91,6 +91,7 @@ _SIGS = {
                                      _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _i32,
                                      _p, _p, _sz, _p]),
     "mlip_embed_atoms": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
+    "mlip_embed_grad": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
     "mlip_tri": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
                            _p, _p]),
     "mlip_tri_vjp_workspace_size": (_sz, [_i32, _i64, _i32]),
@@ -535,6 +536,15 @@ def mlip_embed_atoms(z, table, out: Optional[torch.Tensor] = None) -> torch.Tens
     return out
 
 
+def mlip_embed_grad(z, grad_h, n_types: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d_table[t] = sum of grad_h over the atoms of type t."""
+    N, Dn = int(grad_h.shape[0]), int(grad_h.shape[1])
+    if out is None:
+        out = torch.empty((int(n_types), Dn), dtype=torch.float32, device=grad_h.device)
+    _check(_lib.mlip_embed_grad(_ptr(z), _ptr(grad_h), N, int(n_types), Dn, _ptr(out), _stream()))
+    return out
+
+
 def mlip_tri(graph, h, W_s, W_ang, W_T, cutoff: float, out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
     N, Dn = int(h.shape[0]), int(h.shape[1])
     Dt = int(W_s.shape[1])
@@ -929,14 +939,15 @@ class Stack:
     Workspaces are shared between blocks (they run one after another).
     """
 
-    def __init__(self, shared: Dict, blocks, device="cuda", grad_out=None):
+    def __init__(self, shared: Dict, blocks, device="cuda", grad_out=None, train: bool = False):
         f32 = torch.float32
 
         def dev(x, dt=None):
             t = torch.from_numpy(x) if not isinstance(x, torch.Tensor) else x
             return t.to(device=device, dtype=dt or t.dtype).contiguous()
 
-        self.layers = [FullBlock(shared, device=device, params=p, grad_out=grad_out) for p in blocks]
+        self.layers = [FullBlock(shared, device=device, params=p, grad_out=grad_out, train=train)
+                       for p in blocks]
         first = self.layers[0]
         for L in self.layers[1:]:        # one set of workspaces for all layers
             L.ws_graph, L.ws_moe0, L.ws_moe1, L.ws_mvjp = (first.ws_graph, first.ws_moe0,
@@ -971,3 +982,25 @@ class Stack:
             grad = L.backward(g, grad, forces=self.forces, accumulate=n > 0)
         self.grad_h0 = grad
         return self
+
+    def train_grad(self, grad_energy, grad_forces):
+        """Parameter gradients of a loss L(E, F) after ``step()`` (built with
+        ``train=True`` and the force seed): forward tangents block by block
+        (h_dot of a block = h_out_dot of the one below; the embedding does
+        not move), then the tangents of the input gradients from the top
+        (grad_out_dot of a block = d_h of the one above).  Returns a list of
+        per-block gradient dicts and d_emb, d_w_r."""
+        g = self.graph
+        L0 = self.first
+        h_dot = None
+        for L in self.layers:
+            h_dot = L.jvp(g, grad_forces, h_dot)
+        g_dot = mlip_readout_vjp(L0.w_r, L0.struct_ptr, int(L0.z.shape[0]), grad_energy=grad_energy)
+        per_block = [None] * len(self.layers)
+        for b in range(len(self.layers) - 1, -1, -1):
+            per_block[b] = self.layers[b].tangent_vjp(g, grad_forces, g_dot)
+            g_dot = per_block[b]["d_h"]
+        d_emb = mlip_embed_grad(L0.z, g_dot, int(self.emb.shape[0]))
+        d_w_r = mlip_readout_grad(self.layers[-1].moe["h_out"], L0.struct_ptr, grad_energy=grad_energy,
+                                  h_out_dot=h_dot)
+        return dict(blocks=per_block, d_emb=d_emb, d_w_r=d_w_r)

@@ -526,6 +526,14 @@ int mlip_tri_tangent_vjp(const int32_t *row_ptr, const int32_t *src, const int32
 int mlip_embed_atoms(const int32_t *z, const float *table, int32_t n_atoms, int32_t n_types,
                      int32_t d_node, float *h, void *stream);
 
+/* Gradient of the element embedding h_i = table[z_i] for grad_h = dL/dh
+ * [n_atoms, d_node]: d_table[t] = sum over atoms with z_i = t of grad_h_i
+ * ([n_types, d_node], written; types without atoms get 0).  For a stack's
+ * training gradient grad_h is the first block's dL/dh.  Atoms are summed in
+ * index order (reproducible); out-of-range types are skipped. */
+int mlip_embed_grad(const int32_t *z, const float *grad_h, int32_t n_atoms, int32_t n_types, int32_t d_node,
+                    float *d_table, void *stream);
+
 /* ------------------------------------------------------------------------
  * Kernel timing.  When enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream; mlip_profile_get() waits for the

@@ -356,3 +356,47 @@ def full_loss_value(inp: Dict, Ebar: np.ndarray, Fbar: np.ndarray, **override) -
     gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, f["h2"].shape[1]))
     v = A.full_block_vjp(q, g, f, gup)
     return float(np.dot(f["E"], Ebar) + np.sum(-v["grad_pos"] * Fbar))
+
+
+# ------------------------------------------------------------- the stack ----
+def stack_full_loss_grads(shared: Dict, blocks, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict:
+    """The loss through a stack of complete blocks (``oracle.stack``): h^(0) =
+    Emb[z], blocks in order, readout of the last.  Returns E, F, d_emb, d_w_r
+    and ``blocks``: one dict of d_<param> per block."""
+    emb = _t(shared["emb"]).requires_grad_(True)
+    w_r = _t(shared["w_r"]).requires_grad_(True)
+    names = [[n for n in FULL_PARAMS if n in b] for b in blocks]
+    prms = [{n: _t(b[n]).requires_grad_(True) for n in nm} for b, nm in zip(blocks, names)]
+    pos = _t(shared["pos"]).requires_grad_(True)
+    d = _vectors(shared, graph, pos)
+    h = emb[torch.as_tensor(np.asarray(shared["z"], np.int64))]
+    for prm in prms:
+        h = _full_block(shared, graph, d, prm, h)
+    E = _readout(shared, h, w_r)
+    (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
+    F = -dEdx
+    L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
+    wrt = [emb, w_r] + [prm[n] for prm, nm in zip(prms, names) for n in nm]
+    grads = torch.autograd.grad(L, wrt, allow_unused=True)
+    np_ = lambda g, t: np.zeros(t.shape) if g is None else g.detach().numpy()
+    out = {"E": E.detach().numpy(), "F": F.detach().numpy(), "d_emb": np_(grads[0], emb),
+           "d_w_r": np_(grads[1], w_r), "blocks": []}
+    q = 2
+    for prm, nm in zip(prms, names):
+        out["blocks"].append({"d_" + n: np_(grads[q + j], prm[n]) for j, n in enumerate(nm)})
+        q += len(nm)
+    return out
+
+
+def stack_full_loss_value(shared: Dict, blocks, Ebar: np.ndarray, Fbar: np.ndarray, **override) -> float:
+    """L of the stack with E and F from ``oracle.stack`` (no autograd)."""
+    from . import stack as ST
+    from .graph import radius_graph
+    q = dict(shared)
+    q.update(override)
+    g = radius_graph(q["pos"], q["cell"], q["struct_ptr"], B._cutoff(q))
+    f = ST.stack_forward(q, blocks, g)
+    N = f["h_out"].shape[0]
+    gup = np.broadcast_to(np.asarray(q["w_r"], np.float64), (N, f["h_out"].shape[1]))
+    v = ST.stack_vjp(q, g, f, gup)
+    return float(np.dot(f["E"], Ebar) + np.sum(-v["grad_pos"] * Fbar))

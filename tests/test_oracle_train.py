@@ -177,3 +177,38 @@ def test_complete_block_grads_match_finite_differences(name):
             fd = (TR.full_loss_value(inp, Ebar, Fbar, **{p: up})
                   - TR.full_loss_value(inp, Ebar, Fbar, **{p: dn})) / (2 * step)
             assert abs(fd - grad[idx]) <= 1e-6 * scale, (p, idx, fd, grad[idx])
+
+
+def test_stack_of_complete_blocks_matches_finite_differences():
+    """Two complete blocks with the element embedding: E/F equal oracle.stack's;
+    the embedding, w_r and a sample of both blocks' parameters against FD of L
+    built from oracle.stack's energies and forces."""
+    from oracle import stack as ST
+    cfg = synth.CONFIGS["tiny"]
+    shared, blocks = synth.make_stack_inputs(cfg, 2)
+    g = G.radius_graph(shared["pos"], shared["cell"], shared["struct_ptr"], shared["cutoff"])
+    rng = np.random.default_rng(13)
+    Ebar, Fbar = rng.standard_normal(cfg.n_structs), rng.standard_normal((cfg.n_atoms, 3))
+    out = TR.stack_full_loss_grads(shared, blocks, g, Ebar, Fbar)
+    f = ST.stack_forward(shared, blocks, g)
+    assert np.allclose(out["E"], f["E"], rtol=1e-12, atol=1e-12 * np.abs(f["E"]).max())
+    step = 1e-5
+    checks = [("emb", None), ("w_r", None)] + [(n, b) for b in range(2) for n in ("W_ang", "W1_0", "W_qkv", "Wa_e", "logits", "W2")]
+    for name, b in checks:
+        base = np.asarray(shared[name] if b is None else blocks[b][name], np.float64)
+        grad = out["d_" + name] if b is None else out["blocks"][b]["d_" + name]
+        scale = np.max(np.abs(grad))
+        assert scale > 0, (name, b)
+        for idx in _fd_entries(rng, base, grad, 2):
+            vals = []
+            for sgn in (1.0, -1.0):
+                x = base.copy()
+                x[idx] += sgn * step
+                if b is None:
+                    vals.append(TR.stack_full_loss_value(shared, blocks, Ebar, Fbar, **{name: x}))
+                else:
+                    bl = [dict(bb) for bb in blocks]
+                    bl[b][name] = x
+                    vals.append(TR.stack_full_loss_value(shared, bl, Ebar, Fbar))
+            fd = (vals[0] - vals[1]) / (2 * step)
+            assert abs(fd - grad[idx]) <= 1e-6 * scale, (name, b, idx, fd, grad[idx])
