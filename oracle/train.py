@@ -326,21 +326,42 @@ def _full_block(inp: Dict, graph: Dict, d: torch.Tensor, prm: Dict, h: torch.Ten
     return _moe(u, inp["z"], prm["logits"], prm["W1"], prm["W2"], k)
 
 
-def full_loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray) -> Dict[str, np.ndarray]:
+def full_loss_grads(inp: Dict, graph: Dict, Ebar: np.ndarray, Fbar: np.ndarray,
+                    experts=None) -> Dict[str, np.ndarray]:
     """E, F and dL/dtheta of L = Ebar . E + Fbar . F through one complete block
-    (Tri when the inputs carry W_ang), for every parameter, w_r and h."""
-    names = [n for n in FULL_PARAMS if n in inp] + ["w_r", "h"]
+    (Tri when the inputs carry W_ang), for every parameter, w_r and h.
+
+    With ``experts = (sel1, sel0)`` the expert weights of MoE1 (W1, W2) and
+    MoE0 (W1_0, W2_0) get gradients for those experts only, stacked in that
+    order (for very wide layers)."""
+    big = {"W1": 0, "W2": 0, "W1_0": 1, "W2_0": 1}
+    names = [n for n in FULL_PARAMS if n in inp and (experts is None or n not in big)] + ["w_r", "h"]
     prm = {n: _t(inp[n]).requires_grad_(True) for n in names}
+    wrt = [prm[n] for n in names]
+    extra = []
+    if experts is not None:
+        for n, which in big.items():
+            full = _t(inp[n])
+            sel = [int(x) for x in experts[which]]
+            leaves = {x: full[x].clone().requires_grad_(True) for x in sel}
+            prm[n] = [leaves[x] if x in leaves else full[x] for x in range(full.shape[0])]
+            extra.append((n, [leaves[x] for x in sel]))
+            wrt += extra[-1][1]
     pos = _t(inp["pos"]).requires_grad_(True)
     d = _vectors(inp, graph, pos)
     E = _readout(inp, _full_block(inp, graph, d, prm, prm["h"]), prm["w_r"])
     (dEdx,) = torch.autograd.grad(E.sum(), pos, create_graph=True)
     F = -dEdx
     L = (E * _t(Ebar)).sum() + (F * _t(Fbar)).sum()
-    grads = torch.autograd.grad(L, [prm[n] for n in names], allow_unused=True)
+    grads = torch.autograd.grad(L, wrt, allow_unused=True)
     out = {"E": E.detach().numpy(), "F": F.detach().numpy()}
+    np_ = lambda g, t: np.zeros(t.shape) if g is None else g.detach().numpy()
     for n, g in zip(names, grads):
-        out["d_" + n] = np.zeros(prm[n].shape) if g is None else g.detach().numpy()
+        out["d_" + n] = np_(g, prm[n])
+    q = len(names)
+    for n, leaves in extra:
+        out["d_" + n] = np.stack([np_(grads[q + j], t) for j, t in enumerate(leaves)])
+        q += len(leaves)
     return out
 
 

@@ -212,3 +212,17 @@ def test_stack_of_complete_blocks_matches_finite_differences():
                     vals.append(TR.stack_full_loss_value(shared, bl, Ebar, Fbar))
             fd = (vals[0] - vals[1]) / (2 * step)
             assert abs(fd - grad[idx]) <= 1e-6 * scale, (name, b, idx, fd, grad[idx])
+
+
+def test_complete_block_expert_subset_matches_full():
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_full_inputs(cfg)
+    g = G.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    rng = np.random.default_rng(3)
+    Ebar, Fbar = rng.standard_normal(cfg.n_structs), rng.standard_normal((cfg.n_atoms, 3))
+    full = TR.full_loss_grads(inp, g, Ebar, Fbar)
+    sub = TR.full_loss_grads(inp, g, Ebar, Fbar, experts=([3, 0], [7]))
+    for n, sel in (("W1", [3, 0]), ("W2", [3, 0]), ("W1_0", [7]), ("W2_0", [7])):
+        assert np.allclose(sub["d_" + n], full["d_" + n][sel], rtol=0, atol=1e-13 * np.abs(full["d_" + n]).max())
+    for n in ("W_qkv", "W_ang", "logits0", "h"):
+        assert np.allclose(sub["d_" + n], full["d_" + n], rtol=0, atol=1e-12 * np.abs(full["d_" + n]).max())
