@@ -8,7 +8,8 @@ expert GEMMs, combine), readout, and the input gradient (expert GEMMs
 transposed, aggregation transposed, edge/force part).  Inputs are resident in
 HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S] [--block core|full|stack|train]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config S]
+                    [--block core|full|stack|train|full-train|stack-train]
 
 ``--block full`` times the complete block instead (Tri -> MoE0 -> neighbour
 multi-head attention -> MoE1 -> readout, and its input gradient);
@@ -18,7 +19,9 @@ them), with the block weights drawn on the GPU from a seeded generator.
 ``--block train`` times one training step of the block: forward, forces, and
 the parameter gradients of a loss on energies and forces (forward tangents
 and the tangent of the input gradient), for seeded loss upstreams dL/dE and
-dL/dF.
+dL/dF; ``--block full-train`` the same for the complete block and
+``--block stack-train`` for the stack of ``--blocks`` complete blocks (all
+parameter gradients, the element embedding's included).
 
 Prints ONE JSON line.  ``--calibrate-copy`` instead runs a plain 1 GiB device
 copy (for scaling hardware byte counters).
@@ -137,7 +140,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="S")
-    ap.add_argument("--block", choices=("core", "full", "stack", "train"), default="core")
+    ap.add_argument("--block", choices=("core", "full", "stack", "train", "full-train", "stack-train"),
+                    default="core")
     ap.add_argument("--blocks", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-structs", type=int, default=32)
@@ -160,26 +164,28 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = synth.CONFIGS[args.config]
-    full = args.block == "full"
-    stack = args.block == "stack"
-    train = args.block == "train"
-    if stack:
-        shared, _ = synth.make_stack_inputs(cfg, 0)
-        params = synth.device_stack_params(cfg, args.blocks, "cuda")
-        blk = mlip.Stack(shared, params, device="cuda")
-        inputs = shared
-    elif train:
-        inputs = synth.make_inputs(cfg)
-        blk = mlip.Block(inputs, device="cuda", train=True)
+    train = args.block.endswith("train")
+    full = args.block in ("full", "full-train")
+    stack = args.block in ("stack", "stack-train")
+    if train:
         # seeded loss upstreams: dL/dE ~ N(0,1) per structure, dL/dF ~ N(0,1) per component
         rng = np.random.default_rng(41)
         Ebar_h = rng.standard_normal(cfg.n_structs)
         Fbar_h = rng.standard_normal((cfg.n_atoms, 3)).astype(np.float32)
         Ebar = torch.tensor(Ebar_h, dtype=torch.float64, device="cuda")
         Fbar = torch.from_numpy(Fbar_h).to("cuda")
+    if stack:
+        shared, _ = synth.make_stack_inputs(cfg, 0)
+        params = synth.device_stack_params(cfg, args.blocks, "cuda")
+        blk = mlip.Stack(shared, params, device="cuda", train=train)
+        inputs = shared
+    elif train and not full:
+        inputs = synth.make_inputs(cfg)
+        blk = mlip.Block(inputs, device="cuda", train=True)
     else:
         inputs = synth.make_full_inputs(cfg) if full else synth.make_inputs(cfg)
-        blk = (mlip.FullBlock if full else mlip.Block)(inputs, device="cuda")
+        blk = (mlip.FullBlock(inputs, device="cuda", train=train) if full
+               else mlip.Block(inputs, device="cuda"))
 
     def one_step():
         blk.step()
@@ -220,7 +226,16 @@ def main():
     k = cfg.top_k
     Mtok = N * k
     flops = {c: 2.0 * Mtok * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES + ("gemm_expert_tan",)}
-    wgrad_step = 2 * (2 * 2.0 * Mtok * cfg.d_node * cfg.d_hidden) + 2 * (2 * 2.0 * N * cfg.d_edge * cfg.d_node)
+    Dn, H, Da = cfg.d_node, cfg.d_hidden, cfg.d_attn
+    moe_wgrad = 2 * (2 * 2.0 * Mtok * Dn * H)                    # d W1, d W2: two terms each
+    if full or stack:
+        # per complete block: both MoE layers, W_qkv and W_o (two terms), W_T (two terms) and
+        # W_s (one term when the block's input does not move, i.e. the first block)
+        blk_w = 2 * moe_wgrad + 2 * 2.0 * N * Dn * 3 * Da + 2 * 2.0 * N * Da * Dn + 2 * 2.0 * N * Da * Dn
+        nb = args.blocks if stack else 1
+        wgrad_step = nb * (blk_w + 2.0 * N * Dn * Da) + (nb - 1) * 2.0 * N * Dn * Da
+    else:
+        wgrad_step = moe_wgrad + 2 * (2 * 2.0 * N * cfg.d_edge * Dn)
     classes = [c for c in flops if c in prof and prof[c]["launches"]]
     if "gemm_wgrad" in prof and prof["gemm_wgrad"]["launches"]:
         classes.append("gemm_wgrad")
@@ -246,10 +261,9 @@ def main():
                    "cutoff": cfg.cutoff, "d_edge": cfg.d_edge, "d_node": cfg.d_node,
                    "d_hidden": cfg.d_hidden, "experts": cfg.n_experts, "top_k": k,
                    "element_types": cfg.n_types,
-                   "block": ("Tri + MoE0 + neighbour attention + MoE1" if full else
-                             f"{args.blocks} x (Tri + MoE0 + neighbour attention + MoE1)" if stack
-                             else "aggregation + MoE, training gradient" if train
-                             else "aggregation + MoE")},
+                   "block": (("Tri + MoE0 + neighbour attention + MoE1" if full else
+                              f"{args.blocks} x (Tri + MoE0 + neighbour attention + MoE1)" if stack
+                              else "aggregation + MoE") + (", training gradient" if train else ""))},
         "edges_per_s": round(E * args.steps / wall, 1),
         "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
         "kernel_ms_per_step": kernel_ms,
@@ -259,9 +273,9 @@ def main():
     if full or stack:
         out["config"]["heads"] = cfg.n_heads
         out["config"]["d_attn"] = cfg.d_attn
-    if stack:
-        # the float64 oracle of a whole stack at these widths is out of reach of
-        # a bounded CPU sample; the per-block baseline is in the --block full line
+    if stack or (train and full):
+        # the float64 oracle of these at S widths is beyond a bounded CPU sample (tens of GB of
+        # float64 expert weights and gradients); the per-block baselines are in the other lines
         args.no_cpu_baseline = True
     if train and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_train(cfg, inputs, 1, Ebar_h, Fbar_h)
