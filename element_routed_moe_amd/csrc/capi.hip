@@ -663,7 +663,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   MLIP_CHECK_ARG(aligned(qkv_bar_out, 16), "float arrays must be 16-byte aligned");
   int cpl = 0, lph = 0;
   if (int rc = check_attn_dims(d_node, d_attn, n_heads, cutoff, n_rbf, &cpl, &lph)) return rc;
-  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain,
+  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain || n_atoms == 0,
                  "accumulating into grad_strain needs the accumulated atom_virial");
   MLIP_CHECK_ARG(row_ptr && W_qkv && Wa_e && W_o, "null pointer argument");
   MLIP_CHECK_ARG(n_atoms == 0 || (qkv && o && stats && grad_u && grad_h0 && grad_pos),
@@ -775,7 +775,7 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   MLIP_CHECK_ARG(n_edges == 0 || (src && rev && geom), "null edge pointer");
   MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
                  "grad_strain needs struct_ptr and n_structs >= 1");
-  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain,
+  MLIP_CHECK_ARG(!accumulate || atom_virial || !grad_strain || n_atoms == 0,
                  "accumulating into grad_strain needs the accumulated atom_virial");
   MLIP_CHECK_ARG(aligned(geom, 16) && aligned(s, 16) && aligned(W_s, 16) && aligned(W_ang, 16) &&
                      aligned(W_T, 16) && aligned(grad_hT, 16) && aligned(grad_h, 16),

@@ -367,7 +367,8 @@ int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom
  * rev is the reverse-edge index of the graph; qkv, o, stats come from the
  * mlip_attention call of the same step.  accumulate != 0 adds to grad_pos and
  * atom_virial instead of writing them (grad_strain, if given, is then
- * recomputed from the accumulated atom_virial, which must be given), so the
+ * recomputed from the accumulated atom_virial, which must be given unless
+ * n_atoms is 0), so the
  * forces of several blocks on one graph can be collected.  Per-edge
  * intermediates live in the workspace (mlip_attention_vjp_workspace_size,
  * which grows with n_edges).  Rows are reduced by one wavefront each; no
@@ -475,7 +476,7 @@ int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int3
  *   accumulate != 0: grad_pos and atom_virial are ADDED to (so the forces of
  *     a whole block can be collected, e.g. after mlip_attention_vjp), and
  *     grad_strain, if given, is recomputed from the accumulated atom_virial
- *     (which must then be given).
+ *     (which must then be given unless n_atoms is 0).
  * rev is the reverse-edge index; s comes from the mlip_tri call of the step.
  * Per-edge intermediates (d_tri floats per edge) live in the workspace
  * (mlip_tri_vjp_workspace_size).  No atomics. */

@@ -79,3 +79,34 @@ def test_full_block_train_grad(mlip, name, tri):
     _say(f"{name}: errors {errs}")
     bad = {k: e for k, e in errs.items() if not e <= TOL}
     assert not bad, bad
+
+
+def test_full_block_train_grad_deterministic(mlip):
+    cfg = synth.CONFIGS["ragged"]
+    inp = synth.make_full_inputs(cfg)
+    rng = np.random.default_rng(3)
+    Eb = torch.tensor(rng.standard_normal(cfg.n_structs), dtype=torch.float64, device="cuda")
+    Fb = torch.from_numpy(rng.standard_normal((cfg.n_atoms, 3)).astype(np.float32)).to("cuda")
+    _say("determinism: ragged with Tri, two calls")
+    blk = mlip.FullBlock(inp, device="cuda", train=True).step()
+    first = {k: v.clone() for k, v in blk.train_grad(Eb, Fb).items()}
+    second = blk.train_grad(Eb, Fb)
+    torch.cuda.synchronize()
+    for k in first:
+        assert torch.equal(first[k], second[k]), k
+
+
+def test_full_block_train_grad_empty_system(mlip):
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_full_inputs(cfg)
+    inp["pos"] = inp["pos"][:0]
+    inp["z"] = inp["z"][:0]
+    inp["h"] = inp["h"][:0]
+    inp["struct_ptr"] = np.array([0, 0], np.int32)
+    _say("empty system, complete block")
+    blk = mlip.FullBlock(inp, device="cuda", train=True).step()
+    res = blk.train_grad(torch.tensor([0.5], dtype=torch.float64, device="cuda"),
+                         torch.zeros((0, 3), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    for k, v in res.items():
+        assert not torch.any(v != 0), k
