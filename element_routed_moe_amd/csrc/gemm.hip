@@ -13,14 +13,14 @@
 //
 // Tiling: BM x BN output tile per 256-thread workgroup of 4 wavefronts in a
 // WM x WN grid; each wavefront owns (BM/WM) x (BN/WN) as 32x32 blocks of
-// v_mfma_f32_32x32x2_f32.  K advances BK at a time through double-buffered
-// LDS with one barrier per step; the next step's global loads are in flight
-// while the current one is multiplied, and are written to the other LDS
-// buffer halfway through the step's multiplies.  A and NT-B tiles sit in LDS as
-// [row][k] (k contiguous, row stride BK+4 floats: 16-byte reads without bank
-// conflicts); NN-B tiles as [k][n].  Each MFMA lane supplies the k-values
-// k0 + 4*(lane/32) + q, q = 0..3, for four consecutive MFMAs, so one 16-byte
-// LDS read feeds four instructions.
+// v_mfma_f32_32x32x2_f32.  K advances BK at a time through an S-stage LDS
+// ring: each step's A and B tiles are copied from global memory straight into
+// LDS (global_load_lds_dwordx4, no register staging), S - 1 steps ahead of
+// the step being multiplied, with one barrier per step.  Tiles sit in LDS
+// unpadded with XOR-swizzled 16-byte chunks (A and NT-B as [row][k], NN-B as
+// [k][n]), so the MFMA fragment reads are free of bank conflicts.  Each MFMA
+// lane supplies the k-values k0 + 4*(lane/32) + q, q = 0..3, for four
+// consecutive MFMAs, so one 16-byte LDS read feeds four instructions.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
 // given a contiguous range of tile indices; within it tiles run in groups of
@@ -28,6 +28,7 @@
 // time then share a few A row-blocks and a few expert weight tiles in its L2.
 // Expert row ranges are turned into tile ranges once per workgroup in LDS.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -41,8 +42,10 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int THREADS = 256;
 constexpr int N_XCD = 8;
 constexpr int RASTER_M = 8;
-constexpr int EXPERT_BK_NN = 16;   // [K][N] weights: 41 KB of LDS, three workgroups per CU
-constexpr int EXPERT_BK_NT = 32;   // [N][K] weights: 75-78 KB of LDS, two per CU (measured faster)
+constexpr int EXPERT_BK = 16;   // k per pipeline step of the expert GEMMs
+constexpr int EXPERT_S = 3;     // LDS stages: 3 x 16 KB, three workgroups per CU
+constexpr int DENSE_BK = 32;
+constexpr int DENSE_S = 2;
 constexpr int MAX_GROUPS = 1024;
 
 // Exclusive scan over the 256 threads of the block (one value each).
@@ -61,104 +64,117 @@ __device__ inline int block_scan_excl(int v, int *red) {
   return off + x - v;
 }
 
-// One BM x BN output tile: rows [row0, min(row0 + BM, rows)) of the A row
-// space, columns [n0, n0 + BN).  As / Bs are the two LDS stages, AST / BST
-// floats apart.
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int AST, int BST>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *Bs_, const float *Bg,
-                                          int row0, int rows, int n0) {
+#define GPTR(p) ((const __attribute__((address_space(1))) void *)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for the k loop: this wave's LDS accesses are complete
+// (lgkmcnt 0) and no memory access is moved across it.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so the
+// copies of later stages stay in flight; each wave waits for its own copies
+// of a stage (wait_vm) before the barrier that publishes the stage.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One BM x BN output tile.  Each k-step's A and B tiles are copied from
+// global memory straight into LDS (global_load_lds_dwordx4: every lane moves
+// one 16-byte chunk to base + 16*lane), S stages deep, one barrier per step.
+// LDS layouts (no padding, XOR-swizzled 16-byte chunks so that MFMA fragment
+// reads are free of bank conflicts):
+//   A, NT-B: [row][BK], chunk kq of row r stored at kq ^ ((r / (64/BK)) % (BK/4))
+//   NN-B:    [k][BN],   4-column chunk c of row k stored at c ^ (8 * ((k/4) & 1))
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int S, int AST, int BST>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, float *const *Bs,
+                                          const float *Bg, int row0, int rows, int n0) {
   static_assert(WM * WN == 4, "four wavefronts");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  constexpr int LDK = BK + 4;
-  constexpr int LDN = BN + 4;
-  constexpr int KQ = BK / 4;                       // float4 per row of a k-slice
-  constexpr int A_LOADS = BM * KQ / THREADS;
+  constexpr int KQ = BK / 4;                        // 16-byte chunks per row of a k-slice
+  constexpr int RPB = 64 / BK;                      // rows per 64-bank line
+  constexpr int A_LOADS = BM * KQ / THREADS;        // DMA instructions per wave per step
   constexpr int B_LOADS = BN * KQ / THREADS;
+  constexpr int NL = A_LOADS + B_LOADS;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * KQ % THREADS == 0 && BN * KQ % THREADS == 0,
                 "load split");
-  static_assert(BM * LDK <= AST && (BT ? BN * LDK : BK * LDN) <= BST, "LDS stage size");
-  typedef float AStage[AST];
-  typedef float BStage[BST];
-  AStage *As = reinterpret_cast<AStage *>(As_);
-  BStage *Bs = reinterpret_cast<BStage *>(Bs_);
+  static_assert(BM * BK <= AST && BN * BK <= BST, "LDS stage size");
+  static_assert(S >= 2 && S <= 4, "stages");
+  static_assert(BT || BN % 64 == 0, "NN-B swizzle needs 64-column multiples");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- per-thread global load assignments ----
+  // ---- per-lane DMA sources (k offset 0); LDS chunk c = (q*4 + wave)*64 + lane ----
   const float *a_src[A_LOADS];
-  bool a_ok[A_LOADS];
-  int a_row[A_LOADS], a_kq[A_LOADS];
+  int a_kc[A_LOADS];     // k offset (floats) of this lane's chunk within a step
 #pragma unroll
   for (int q = 0; q < A_LOADS; ++q) {
-    const int idx = tid + THREADS * q;
-    a_row[q] = idx / KQ;
-    a_kq[q] = (idx % KQ) * 4;
-    const int p = row0 + a_row[q];
-    a_ok[q] = p < rows;
-    int64_t arow = p;
-    if (a_ok[q] && g.a_rows) arow = g.a_rows[p];
-    a_src[q] = g.A + (a_ok[q] ? arow * g.lda : 0);
+    const int c = (q * 4 + wave) * 64 + lane;
+    const int r = c / KQ, s = c % KQ;
+    a_kc[q] = 4 * (s ^ ((r / RPB) % KQ));
+    int p = row0 + r;
+    p = p < rows ? p : row0;             // padding rows read a valid row; never stored
+    const int64_t arow = g.a_rows ? int64_t(g.a_rows[p]) : int64_t(p);
+    a_src[q] = g.A + arow * g.lda;
   }
   const float *b_src[B_LOADS];
-  bool b_ok[B_LOADS];
-  int b_r[B_LOADS], b_c[B_LOADS];
+  int b_kc[B_LOADS];     // NT: k offset of the chunk; NN: k row of the chunk
 #pragma unroll
   for (int q = 0; q < B_LOADS; ++q) {
-    const int idx = tid + THREADS * q;
-    if (BT) {   // [N][K]: row n, float4 along k
-      b_r[q] = idx / KQ;
-      b_c[q] = (idx % KQ) * 4;
-      const int n = n0 + b_r[q];
-      b_ok[q] = n < g.N;
-      b_src[q] = Bg + (b_ok[q] ? int64_t(n) * g.ldb : 0);
-    } else {    // [K][N]: row k, float4 along n
-      b_r[q] = idx / (BN / 4);
-      b_c[q] = (idx % (BN / 4)) * 4;
-      const int n = n0 + b_c[q];
-      b_ok[q] = n < g.N;
-      b_src[q] = Bg + (b_ok[q] ? n : 0);
+    const int c = (q * 4 + wave) * 64 + lane;
+    if (BT) {
+      const int r = c / KQ, s = c % KQ;
+      b_kc[q] = 4 * (s ^ ((r / RPB) % KQ));
+      int n = n0 + r;
+      n = n < g.N ? n : n0;
+      b_src[q] = Bg + int64_t(n) * g.ldb;
+    } else {
+      const int k = c / (BN / 4), s = c % (BN / 4);
+      b_kc[q] = k;
+      int n = n0 + 4 * (s ^ (8 * ((k >> 2) & 1)));
+      n = n < g.N ? n : n0;
+      b_src[q] = Bg + n;
     }
   }
+  const int nk = (g.K + BK - 1) / BK;
+  const bool k_tail = (g.K % BK) != 0;
 
-  // Loads are unconditional from always-valid addresses (row 0 / k 0 stand in
-  // for out-of-range elements); the zero mask is applied when the values are
-  // written to LDS, so nothing waits on a load before the multiply.
-  floatx4 ra[A_LOADS], rb[B_LOADS];
-  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  auto a_ok_k = [&](int q, int k0) { return a_ok[q] && k0 + a_kq[q] < g.K; };
-  auto b_ok_k = [&](int q, int k0) { return b_ok[q] && k0 + (BT ? b_c[q] : b_r[q]) < g.K; };
-  auto load_global = [&](int k0) {
+  auto issue = [&](float *a_dst, float *b_dst, int kt) {
+    const int k0 = kt * BK;
+    // chunks past K re-read k = 0 (always in range) and are zeroed below
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
-      const int k = k0 + a_kq[q];
-      ra[q] = *reinterpret_cast<const floatx4 *>(a_src[q] + (a_ok_k(q, k0) ? k : 0));
+      const int k = k0 + a_kc[q];
+      __builtin_amdgcn_global_load_lds(GPTR(a_src[q] + (k < g.K ? k : 0)), LPTR(a_dst + (q * 4 + wave) * 256), 16,
+                                       0, 0);
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-      if (BT) {
-        const int k = k0 + b_c[q];
-        rb[q] = *reinterpret_cast<const floatx4 *>(b_src[q] + (b_ok_k(q, k0) ? k : 0));
-      } else {
-        const int kb = k0 + b_r[q];
-        rb[q] = *reinterpret_cast<const floatx4 *>(b_src[q] + (b_ok_k(q, k0) ? int64_t(kb) * g.ldb : 0));
-      }
+      const int k = k0 + b_kc[q];
+      const int64_t off = BT ? int64_t(k < g.K ? k : 0) : int64_t(k < g.K ? k : 0) * g.ldb;
+      __builtin_amdgcn_global_load_lds(GPTR(b_src[q] + off), LPTR(b_dst + (q * 4 + wave) * 256), 16, 0, 0);
     }
   };
-  auto store_lds = [&](int buf, int k0) {
+  // K tail: after its loads have landed, each lane zeroes the chunks it
+  // loaded that lie past K (before the barrier that publishes the stage)
+  auto zero_tail = [&](float *a_dst, float *b_dst, int kt) {
+    const int k0 = kt * BK;
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q)
-      *reinterpret_cast<floatx4 *>(&As[buf][a_row[q] * LDK + a_kq[q]]) = a_ok_k(q, k0) ? ra[q] : zero4;
+      if (k0 + a_kc[q] >= g.K) *reinterpret_cast<floatx4 *>(a_dst + ((q * 4 + wave) * 64 + lane) * 4) = z;
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
-      const floatx4 v = b_ok_k(q, k0) ? rb[q] : zero4;
-      if (BT) *reinterpret_cast<floatx4 *>(&Bs[buf][b_r[q] * LDK + b_c[q]]) = v;
-      else *reinterpret_cast<floatx4 *>(&Bs[buf][b_r[q] * LDN + b_c[q]]) = v;
-    }
+    for (int q = 0; q < B_LOADS; ++q)
+      if (k0 + b_kc[q] >= g.K) *reinterpret_cast<floatx4 *>(b_dst + ((q * 4 + wave) * 64 + lane) * 4) = z;
   };
 
   floatx16 acc[FM][FN];
@@ -169,47 +185,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-  const int nk = (g.K + BK - 1) / BK;
-  load_global(0);
-  store_lds(0, 0);
-  __syncthreads();
-
   const int l32 = lane & 31;
-  const int kh = (lane >> 5) * 4;
-  // fragments of one 8-wide k group: FM A-values and FN B-values per k
+  const int half = lane >> 5;
+  // per-lane LDS fragment offsets (floats): A row r, logical chunk 2j + half
+  int a_off[FM], a_x[FM];
+#pragma unroll
+  for (int bi = 0; bi < FM; ++bi) {
+    const int r = wm * WTM + bi * 32 + l32;
+    a_off[bi] = r * BK;
+    a_x[bi] = half ^ ((r / RPB) % KQ);
+  }
+  int b_off[FN], b_x[FN];
+#pragma unroll
+  for (int bj = 0; bj < FN; ++bj) {
+    const int n = wn * WTN + bj * 32 + l32;
+    if (BT) {
+      b_off[bj] = n * BK;
+      b_x[bj] = half ^ ((n / RPB) % KQ);
+    } else {
+      b_off[bj] = (4 * half) * BN + (n ^ (32 * half));
+      b_x[bj] = 0;
+    }
+  }
   struct Frag {
     floatx4 a[FM], b[FN];
   };
-  auto read_frag = [&](const float *Ab, const float *Bb, int kg, Frag &f) {
+  auto read_frag = [&](const float *Ab, const float *Bb, int j, Frag &f) {   // k group 8j .. 8j+7
 #pragma unroll
     for (int bi = 0; bi < FM; ++bi)
-      f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[(wm * WTM + bi * 32 + l32) * LDK + kg + kh]);
+      f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[a_off[bi] + 4 * ((2 * j) ^ a_x[bi])]);
 #pragma unroll
     for (int bj = 0; bj < FN; ++bj) {
       if (BT) {
-        f.b[bj] = *reinterpret_cast<const floatx4 *>(&Bb[(wn * WTN + bj * 32 + l32) * LDK + kg + kh]);
+        f.b[bj] = *reinterpret_cast<const floatx4 *>(&Bb[b_off[bj] + 4 * ((2 * j) ^ b_x[bj])]);
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f.b[bj][q] = Bb[(kg + kh + q) * LDN + wn * WTN + bj * 32 + l32];
+        for (int q = 0; q < 4; ++q) f.b[bj][q] = Bb[b_off[bj] + (8 * j + q) * BN];
       }
     }
   };
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const float *Ab = As[cur];
-    const float *Bb = Bs[cur];
+  auto compute = [&](const float *Ab, const float *Bb) {
     Frag f[2];
     read_frag(Ab, Bb, 0, f[0]);
-    // [N][K] weights: the multiplying wave takes issue priority over the
-    // other wave of its SIMD while that one loads and stores (measured faster
-    // there; the [K][N] variant is not helped)
-    if constexpr (BT) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kg = 0; kg < BK / 8; ++kg) {
-      // the next group's LDS reads are in flight while this group multiplies
-      if (kg + 1 < BK / 8) read_frag(Ab, Bb, (kg + 1) * 8, f[(kg + 1) & 1]);
-      const Frag &c = f[kg & 1];
+    for (int j = 0; j < BK / 8; ++j) {
+      if (j + 1 < BK / 8) read_frag(Ab, Bb, j + 1, f[(j + 1) & 1]);
+      const Frag &c = f[j & 1];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -217,16 +238,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
 #pragma unroll
           for (int bj = 0; bj < FN; ++bj)
             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.a[bi][q], c.b[bj][q], acc[bi][bj], 0, 0, 0);
-      // halfway through the step the next tile goes to the other LDS buffer
-      // (last read before the previous barrier), so the stores overlap the
-      // remaining multiplies
-      if (kg == BK / 16 - 1 && kt + 1 < nk) store_lds(cur ^ 1, (kt + 1) * BK);
     }
-    if constexpr (BT) __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
+  };
+  // Step kt reads stage kt % S.  Every step issues the copy of step
+  // kt + S - 1 (clamped to the last step: past the end the copy is a dummy
+  // into a stage no later step reads), so exactly (S - 2) * NL copies are
+  // younger than step kt's at its top, on every path through the loop.
+  auto step = [&](auto sc, int kt) {
+    constexpr int s = decltype(sc)::value;
+    wait_vm<(S - 2) * NL>();
+    if (k_tail && kt == nk - 1) zero_tail(As[s], Bs[s], kt);
+    lds_barrier();
+    issue(As[(s + S - 1) % S], Bs[(s + S - 1) % S], min(kt + S - 1, nk - 1));
+    compute(As[s], Bs[s]);
+  };
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(As[s], Bs[s], min(s, nk - 1));
+  // whole groups of S steps (the loop's back edge only follows step S - 1),
+  // then the remaining nk % S steps, which continue at stage 0
+  int kt = 0;
+  for (; kt + S <= nk; kt += S) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S >= 3) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+    if constexpr (S >= 4) step(std::integral_constant<int, 3 % S>{}, kt + 3);
   }
+  if (kt < nk) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if constexpr (S >= 3) {
+      if (kt + 1 < nk) {
+        step(std::integral_constant<int, 1>{}, kt + 1);
+        if constexpr (S >= 4) {
+          if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+        }
+      }
+    }
+  }
+  wait_vm<0>();   // no copy may land in LDS after the workgroup ends
 
   // ---- epilogue: D[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 ----
+  const int kh = half * 4;
   // Residual / pre-activation values are fetched for the whole wave tile
   // first (clamped, always-valid addresses), then combined and stored.
 #pragma unroll
@@ -284,15 +336,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *As_, float *
 // BM-row tiles, except that a remainder of at most BM/2 rows gets a BM/2-row
 // tile.  The two classes are dealt to the XCDs separately, full tiles first,
 // so every XCD receives its share of each and the short tiles run last.
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT>
-__global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
-  constexpr int LDK = BK + 4;
-  constexpr int LDN = BN + 4;
-  constexpr int AST = BM * LDK;
-  constexpr int BST = BT ? (BN * LDK) : (BK * LDN);
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
+__global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
+  constexpr int AST = BM * BK;
+  constexpr int BST = BN * BK;
   constexpr int HALF = BM / 2;
-  __shared__ __attribute__((aligned(16))) float As[2 * AST];
-  __shared__ __attribute__((aligned(16))) float Bs[2 * BST];
+  // one array per stage, so the compiler can tell a stage being read from the
+  // stages whose copies are still in flight
+  __shared__ __attribute__((aligned(16))) float A0[AST], A1[AST], A2[S >= 3 ? AST : 4], A3[S >= 4 ? AST : 4];
+  __shared__ __attribute__((aligned(16))) float B0[BST], B1[BST], B2[S >= 3 ? BST : 4], B3[S >= 4 ? BST : 4];
+  float *const As[4] = {A0, A1, A2, A3};
+  float *const Bs[4] = {B0, B1, B2, B3};
   __shared__ int s_tiles[MAX_GROUPS + 1];
   __shared__ int s_red[10];   // two scans' wave sums, then the two totals
 
@@ -389,14 +443,14 @@ __global__ void __launch_bounds__(THREADS) gemm_kernel(GemmArgs g) {
   const float *Bg = g.B + int64_t(grp) * g.b_group_stride;
   if constexpr (SPLIT) {
     if (half) {
-      gemm_tile<HALF, BN, BK, WM, WN, BT, EPI, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+      gemm_tile<HALF, BN, BK, WM, WN, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
       return;
     }
   }
-  gemm_tile<BM, BN, BK, WM, WN, BT, EPI, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+  gemm_tile<BM, BN, BK, WM, WN, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT>
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
 int launch_t(const GemmArgs &a, hipStream_t stream) {
   // Upper bounds of the per-XCD tile counts the kernel derives on the device:
   // full tiles <= (M + G*BM/2) / BM and half tiles <= G with SPLIT,
@@ -417,7 +471,7 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
     set_error("GEMM too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
   }
-  gemm_kernel<BM, BN, BK, WM, WN, BT, EPI, TAG, SPLIT><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
+  gemm_kernel<BM, BN, BK, WM, WN, BT, EPI, TAG, SPLIT, S><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
@@ -425,14 +479,14 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
 // Expert GEMMs: 128 x 128 tiles, 64 x 128 for short group remainders.
 template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
-  return launch_t<128, 128, BT ? EXPERT_BK_NT : EXPERT_BK_NN, 2, 2, BT, EPI, TAG, true>(a, s);
+  return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG, true, EXPERT_S>(a, s);
 }
 // Dense projections: 64 x 64 tiles when the output is narrow (enough
 // workgroups for 256 CUs), else 64 x 128.
 template <bool BT, int EPI, int TAG>
 int launch_dense(const GemmArgs &a, hipStream_t s) {
-  if (a.N <= 512) return launch_t<64, 64, 32, 2, 2, BT, EPI, TAG, false>(a, s);
-  return launch_t<64, 128, 32, 2, 2, BT, EPI, TAG, false>(a, s);
+  if (a.N <= 512) return launch_t<64, 64, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
+  return launch_t<64, 128, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
 }
 
 }  // namespace
