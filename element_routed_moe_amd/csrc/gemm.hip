@@ -99,12 +99,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   constexpr int KQ = BK / 4;                        // 16-byte chunks per row of a k-slice
   constexpr int RPB = 64 / BK;                      // rows per 64-bank line
-  constexpr int A_LOADS = BM * KQ / THREADS;        // DMA instructions per wave per step
+  // copy instructions per step: one 1 KB chunk-row (64 lanes x 16 bytes) each
+  constexpr int NIA = BM * KQ / 64;
+  constexpr int A_LOADS = (NIA + 3) / 4;            // per wave; spare slots copy into a sink
   constexpr int B_LOADS = BN * KQ / THREADS;
-  constexpr int NL = A_LOADS + B_LOADS;
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * KQ % THREADS == 0 && BN * KQ % THREADS == 0,
-                "load split");
+  constexpr int NL = A_LOADS + B_LOADS;             // the same on every wave
+  static_assert(NIA * 64 == BM * KQ && B_LOADS >= 1 && BN * KQ % THREADS == 0, "load split");
   static_assert(BM * BK <= AST && BN * BK <= BST, "LDS stage size");
+  static_assert(NIA % 4 == 0 || (NIA + 1) * 256 <= AST, "room for the A sink");
   static_assert(S >= 2 && S <= 4, "stages");
   static_assert(BT || BN % 64 == 0, "NN-B swizzle needs 64-column multiples");
 
@@ -114,11 +116,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- per-lane DMA sources (k offset 0); LDS chunk c = (q*4 + wave)*64 + lane ----
+  // When BM rows do not make a multiple of four chunk-rows (BM = 32), the
+  // waves without a chunk-row of their own re-copy chunk-row 0 into the unused
+  // LDS just past the tile, so that every wave issues the same number of
+  // copies and one vmcnt value fits them all.
   const float *a_src[A_LOADS];
   int a_kc[A_LOADS];     // k offset (floats) of this lane's chunk within a step
+  int a_dof[A_LOADS];    // LDS offset (floats) of the slot's chunk-row
 #pragma unroll
   for (int q = 0; q < A_LOADS; ++q) {
-    const int c = (q * 4 + wave) * 64 + lane;
+    const int ci = q * 4 + wave;
+    const bool real = ci < NIA;
+    a_dof[q] = (real ? ci : NIA) * 256;
+    const int c = (real ? ci : 0) * 64 + lane;
     const int r = c / KQ, s = c % KQ;
     a_kc[q] = 4 * (s ^ ((r / RPB) % KQ));
     int p = row0 + r;
@@ -154,8 +164,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
       const int k = k0 + a_kc[q];
-      __builtin_amdgcn_global_load_lds(GPTR(a_src[q] + (k < g.K ? k : 0)), LPTR(a_dst + (q * 4 + wave) * 256), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(GPTR(a_src[q] + (k < g.K ? k : 0)), LPTR(a_dst + a_dof[q]), 16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
@@ -171,7 +180,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q)
-      if (k0 + a_kc[q] >= g.K) *reinterpret_cast<floatx4 *>(a_dst + ((q * 4 + wave) * 64 + lane) * 4) = z;
+      if (k0 + a_kc[q] >= g.K) *reinterpret_cast<floatx4 *>(a_dst + a_dof[q] + lane * 4) = z;
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q)
       if (k0 + b_kc[q] >= g.K) *reinterpret_cast<floatx4 *>(b_dst + ((q * 4 + wave) * 64 + lane) * 4) = z;
@@ -332,15 +341,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   }
 }
 
-// Expert GEMMs (group_off set, SPLIT): each group's rows are covered by
-// BM-row tiles, except that a remainder of at most BM/2 rows gets a BM/2-row
-// tile.  The two classes are dealt to the XCDs separately, full tiles first,
-// so every XCD receives its share of each and the short tiles run last.
+// Expert GEMMs (group_off set, SPLIT, BM = 128): each group's rows are
+// covered by 128-row tiles, except that a remainder of at most 64 rows gets
+// one short tile of 32 or 64 rows (the fewer that cover it), which keeps the
+// padded MFMA work of small experts low.  Full and short tiles are dealt to
+// the XCDs separately, full tiles first, so every XCD receives its share of
+// each and the short tiles run last.
 template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
 __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   constexpr int AST = BM * BK;
   constexpr int BST = BN * BK;
-  constexpr int HALF = BM / 2;
+  constexpr int REM_MAX = BM / 2;   // longest remainder given a short tile
+  static_assert(!SPLIT || BM == 128, "short tiles are 32 and 64 rows");
   // one array per stage, so the compiler can tell a stage being read from the
   // stages whose copies are still in flight
   __shared__ __attribute__((aligned(16))) float A0[AST], A1[AST], A2[S >= 3 ? AST : 4], A3[S >= 4 ? AST : 4];
@@ -356,9 +368,9 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   const int L = blockIdx.x;
   const int jx = L / N_XCD, xcd = L - jx * N_XCD;
 
-  // ---- m-tiles per group (full and, with SPLIT, half) -> prefix in LDS ----
+  // ---- m-tiles per group (full and, with SPLIT, short) -> prefix in LDS ----
   int Mt, t_local;
-  bool half = false;
+  bool short_tile = false;
   if (g.group_off) {
     constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
     int cf[PER], ch[PER], sf = 0, sh = 0;
@@ -368,8 +380,8 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
       const int c = gi < G ? g.group_off[gi + 1] - g.group_off[gi] : 0;
       if (SPLIT) {
         const int rem = c % BM;
-        cf[q] = c / BM + (rem > HALF ? 1 : 0);
-        ch[q] = (rem > 0 && rem <= HALF) ? 1 : 0;
+        cf[q] = c / BM + (rem > REM_MAX ? 1 : 0);
+        ch[q] = (rem > 0 && rem <= REM_MAX) ? 1 : 0;
       } else {
         cf[q] = (c + BM - 1) / BM;
         ch[q] = 0;
@@ -396,14 +408,14 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
       if (!SPLIT || jx - per_f >= per_h) return;
       t_local = xcd * per_h + (jx - per_f);
       Mt = Mh;
-      half = true;
+      short_tile = true;
     }
     if (t_local >= Mt * Nt) return;
     // prefix of this block's class only
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int gi = tid * PER + q;
-      if (gi <= G) s_tiles[gi] = half ? run_h : run_f;
+      if (gi <= G) s_tiles[gi] = short_tile ? run_h : run_f;
       run_f += cf[q];
       run_h += ch[q];
     }
@@ -433,7 +445,7 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
     grp = lo;
     const int gbeg = g.group_off[grp];
     rows = g.group_off[grp + 1];
-    if (half) row0 = gbeg + ((rows - gbeg) / BM) * BM;
+    if (short_tile) row0 = gbeg + ((rows - gbeg) / BM) * BM;
     else row0 = gbeg + (mt_glob - s_tiles[grp]) * BM;
   } else {
     row0 = mt_glob * BM;
@@ -442,8 +454,10 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   const int n0 = nt * BN;
   const float *Bg = g.B + int64_t(grp) * g.b_group_stride;
   if constexpr (SPLIT) {
-    if (half) {
-      gemm_tile<HALF, BN, BK, WM, WN, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+    if (short_tile) {
+      const int rem = rows - row0;
+      if (rem <= 32) gemm_tile<32, BN, BK, 1, 4, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+      else gemm_tile<64, BN, BK, 2, 2, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
       return;
     }
   }
@@ -453,14 +467,14 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
 template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
 int launch_t(const GemmArgs &a, hipStream_t stream) {
   // Upper bounds of the per-XCD tile counts the kernel derives on the device:
-  // full tiles <= (M + G*BM/2) / BM and half tiles <= G with SPLIT,
+  // full tiles <= (M + G*(BM/2 - 1)) / BM and short tiles <= G with SPLIT,
   // ceil(M/BM) + G tiles without it; surplus workgroups return at once.
   const int64_t nt = cdiv(a.N, BN);
   int64_t per;
   if (!a.group_off) {
     per = cdiv(cdiv(a.M, BM) * nt, N_XCD);
   } else if (SPLIT) {
-    const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * (BM / 2)) / BM;
+    const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * (BM / 2 - 1)) / BM;
     per = cdiv(mf * nt, N_XCD) + cdiv(int64_t(a.n_groups) * nt, N_XCD);
   } else {
     per = cdiv((cdiv(a.M, BM) + a.n_groups) * nt, N_XCD);
