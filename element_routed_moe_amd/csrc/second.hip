@@ -27,6 +27,8 @@
 // point atomics), so the results do not depend on scheduling.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace mlip {
@@ -43,11 +45,18 @@ constexpr int K = MLIP_N_RBF;
 // 128 x 128 output tile per 256-thread workgroup (2 x 2 wavefronts of
 // 64 x 64, each 2 x 2 blocks of v_mfma_f32_32x32x2_f32).  K runs over the
 // rows p (tokens or atoms) WK at a time.  Both operands arrive as rows of
-// the output's M or N extent, so they are staged in LDS as [k][m] / [k][n]
-// (512-byte coalesced row segments per k) and each lane reads its MFMA
-// values one float at a time, consecutive lanes on consecutive addresses.
-// The rows are gathered (token -> atom) along K, so the gather indices of a
-// step are fetched one step before its loads.
+// the output's M or N extent, so a step's tiles are [k][m] / [k][n]: 16 rows
+// of 512 bytes, copied from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging) through a WS-stage ring,
+// WS - 1 steps ahead of the step being multiplied, one barrier per step.
+// In LDS the 4-column chunk c of k-row k sits at c ^ (8 * ((k/4) & 1)), so
+// the two half-waves of an MFMA read (k-rows 4 apart) hit different banks;
+// each lane reads its MFMA values one float at a time.
+// The rows are gathered (token -> atom) along K: the gather indices of a
+// step are loaded one step before its copies are issued.  A per-row factor
+// on A (the gate) is copied into LDS with the step (4 bytes per lane) and
+// applied as the A values are read.  Rows past the group's end are copied
+// from a valid row and zeroed in LDS before the stage is published.
 //
 // Tile order: a tile's cost is its group's row count, which varies widely
 // between experts, so tiles are not given to the XCDs in contiguous ranges
@@ -56,14 +65,47 @@ constexpr int K = MLIP_N_RBF;
 // share of every expert.
 constexpr int WB = 128;
 constexpr int WK = 16;   // rows per K step (32 measured 11% slower at S)
-constexpr int WLD = WB + 4;
+constexpr int WS = 3;    // LDS stages: 3 x 17 KB, three workgroups per CU
 constexpr int W_THREADS = 256;
-constexpr int W_LOADS = WK * WB / 4 / W_THREADS;   // float4 per thread per operand and step
+constexpr int W_SLOTS = WK * WB / 4 / W_THREADS;   // 16-byte copies per lane per operand and step
 
-__global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_split, int64_t rows_per_split,
-                                                          float *__restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float As[2][WK * WLD];
-  __shared__ __attribute__((aligned(16))) float Bs[2][WK * WLD];
+#define W_GPTR(p) ((const __attribute__((address_space(1))) void *)(p))
+#define W_LPTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void w_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Barrier that waits for this wave's LDS accesses but not for its
+// outstanding global loads (the copies of later stages stay in flight),
+// and across which the compiler moves no memory access.
+__device__ __forceinline__ void w_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool GA, bool GB, bool SC>
+__global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_split, int64_t rows_per_split,
+                                                             float *__restrict__ part) {
+  // One array per stage for the A tile, the B tile and the row factors, and
+  // one per stage for the gather indices, so the compiler can tell the stage
+  // being read from the stages whose copies are still in flight.  Only LDS
+  // copies are in flight in the k loop (the indices too travel through LDS):
+  // mixed with ordinary loads, the waitcnt insertion can no longer count
+  // them in order and drains the counter before LDS reads.
+  // The row factors and the gather indices of a step are the same for every
+  // wave: all four copy them to one shared 64-entry region (concurrent copies
+  // of identical values), which keeps the LDS within three workgroups per CU.
+  constexpr int STG = 2 * WK * WB + (SC ? 64 : 0);
+  constexpr int NG = (GA ? 1 : 0) + (GB ? 1 : 0);   // gathered operands
+  constexpr int XST = NG ? NG * 64 : 4;
+  __shared__ __attribute__((aligned(16))) float L0[STG], L1[STG], L2[STG];
+  __shared__ __attribute__((aligned(16))) int X0[XST], X1[XST], X2[XST];
+  float *const As[WS] = {L0, L1, L2};
+  float *const Bs[WS] = {L0 + WK * WB, L1 + WK * WB, L2 + WK * WB};
+  float *const Ss[WS] = {L0 + 2 * WK * WB, L1 + 2 * WK * WB, L2 + 2 * WK * WB};
+  int *const Xs[WS] = {X0, X1, X2};
+  static_assert(WS == 3, "the k loop is written for three stages");
+
   const int mt = (g.Mo + WB - 1) / WB, nt = (g.No + WB - 1) / WB;
   const int G = g.group_off ? g.n_groups : 1;
   const int64_t per_group = int64_t(mt) * nt;
@@ -91,50 +133,7 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, kh = (lane >> 5) * 4;
-
-  floatx4 ra[W_LOADS], rb[W_LOADS];
-  float sa[W_LOADS];
-  bool oka[W_LOADS], okb[W_LOADS];
-  int64_t ia[W_LOADS], ib[W_LOADS];   // gather rows of the next step to load (-1: none)
-  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  auto fetch_idx = [&](int s) {
-    const int term = s >= steps_term ? 1 : 0;
-    const int k0 = p0 + (s - term * steps_term) * WK;
-#pragma unroll
-    for (int q = 0; q < W_LOADS; ++q) {
-      const int p = k0 + ((tid + W_THREADS * q) >> 5);
-      const bool vp = p < p1;
-      ia[q] = vp ? (g.a_rows ? int64_t(g.a_rows[p]) : int64_t(p)) : -1;
-      ib[q] = vp ? (g.b_rows ? int64_t(g.b_rows[p]) : int64_t(p)) : -1;
-    }
-  };
-  auto load = [&](int s) {
-    const int term = s >= steps_term ? 1 : 0;
-    const int k0 = p0 + (s - term * steps_term) * WK;
-    const float *A = term ? g.A1 : g.A0;
-    const float *B = term ? g.B1 : g.B0;
-#pragma unroll
-    for (int q = 0; q < W_LOADS; ++q) {
-      const int idx = tid + W_THREADS * q;
-      const int row = idx >> 5, col = (idx & 31) * 4;
-      const int mc = m0 + col, nc = n0 + col;
-      oka[q] = ia[q] >= 0 && mc < g.Mo;
-      okb[q] = ib[q] >= 0 && nc < g.No;
-      ra[q] = *reinterpret_cast<const floatx4 *>(A + (oka[q] ? ia[q] * g.lda + mc : 0));
-      rb[q] = *reinterpret_cast<const floatx4 *>(B + (okb[q] ? ib[q] * g.ldb + nc : 0));
-      sa[q] = (oka[q] && g.scale) ? g.scale[k0 + row] : 1.f;
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < W_LOADS; ++q) {
-      const int idx = tid + W_THREADS * q;
-      const int row = idx >> 5, col = (idx & 31) * 4;
-      *reinterpret_cast<floatx4 *>(&As[buf][row * WLD + col]) = oka[q] ? ra[q] * sa[q] : zero4;
-      *reinterpret_cast<floatx4 *>(&Bs[buf][row * WLD + col]) = okb[q] ? rb[q] : zero4;
-    }
-  };
+  const int l32 = lane & 31, half = lane >> 5, kh = half * 4;
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -145,28 +144,92 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
   if (nsteps > 0) {
-    fetch_idx(0);
-    load(0);
-    if (nsteps > 1) fetch_idx(1);
-    store(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < nsteps) {
-        load(s + 1);
-        if (s + 2 < nsteps) fetch_idx(s + 2);
+    // copy slot q of this lane: chunk c = (q*4 + wave)*64 + lane of the
+    // [WK][WB] tile, k-row kr = c / 32, stored chunk c % 32
+    int kr[W_SLOTS], ca[W_SLOTS], cb[W_SLOTS], lofs[W_SLOTS];
+#pragma unroll
+    for (int q = 0; q < W_SLOTS; ++q) {
+      const int c = (q * 4 + wave) * 64 + lane;
+      kr[q] = c >> 5;
+      const int col = 4 * ((c & 31) ^ (8 * ((kr[q] >> 2) & 1)));
+      ca[q] = m0 + col < g.Mo ? m0 + col : m0;   // columns past the edge copy a valid one; never stored
+      cb[q] = n0 + col < g.No ? n0 + col : n0;
+      lofs[q] = c * 4;
+    }
+    // step s -> (term, first row); steps past the last one are clamped to it
+    auto step_rows = [&](int s, int &term, int &k0) {
+      s = s < nsteps ? s : nsteps - 1;
+      term = s >= steps_term ? 1 : 0;
+      k0 = p0 + (s - term * steps_term) * WK;
+    };
+    // this lane's row of the step (lanes past WK repeat row 0); rows past p1 take p0
+    auto lane_row = [&](int k0) {
+      const int p = k0 + (lane < WK ? lane : 0);
+      return p < p1 ? p : p0;
+    };
+    // every wave copies the step's WK gather indices to the shared X[set]
+    auto issue_idx = [&](int set, int s) {
+      int term, k0;
+      step_rows(s, term, k0);
+      const int p = lane_row(k0);
+      if (GA) __builtin_amdgcn_global_load_lds(W_GPTR(g.a_rows + p), W_LPTR(Xs[set]), 4, 0, 0);
+      if (GB) __builtin_amdgcn_global_load_lds(W_GPTR(g.b_rows + p), W_LPTR(Xs[set] + (GA ? 64 : 0)), 4, 0, 0);
+    };
+    auto issue = [&](int st, int set, int s) {
+      int term, k0;
+      step_rows(s, term, k0);
+      const float *A = term ? g.A1 : g.A0;
+      const float *B = term ? g.B1 : g.B0;
+      int64_t ra[W_SLOTS], rb[W_SLOTS];
+#pragma unroll
+      for (int q = 0; q < W_SLOTS; ++q) {
+        int p = k0 + kr[q];
+        p = p < p1 ? p : p0;
+        ra[q] = GA ? int64_t(Xs[set][kr[q]]) : int64_t(p);
+        rb[q] = GB ? int64_t(Xs[set][(GA ? 64 : 0) + kr[q]]) : int64_t(p);
       }
-      const float *Ab = As[cur];
-      const float *Bb = Bs[cur];
+#pragma unroll
+      for (int q = 0; q < W_SLOTS; ++q)
+        __builtin_amdgcn_global_load_lds(W_GPTR(A + ra[q] * g.lda + ca[q]), W_LPTR(As[st] + (q * 4 + wave) * 256), 16,
+                                         0, 0);
+#pragma unroll
+      for (int q = 0; q < W_SLOTS; ++q)
+        __builtin_amdgcn_global_load_lds(W_GPTR(B + rb[q] * g.ldb + cb[q]), W_LPTR(Bs[st] + (q * 4 + wave) * 256), 16,
+                                         0, 0);
+      if (SC) __builtin_amdgcn_global_load_lds(W_GPTR(g.scale + lane_row(k0)), W_LPTR(Ss[st]), 4, 0, 0);
+    };
+    constexpr int NIDX = NG;
+    constexpr int NL = 2 * W_SLOTS + (SC ? 1 : 0);
+    // Rows past p1 (the last step of a term): each lane zeroes the chunks it
+    // copied, after they have landed and before the barrier.
+    auto zero_tail = [&](int st, int s) {
+      int term, k0;
+      step_rows(s, term, k0);
+      if (k0 + WK <= p1) return;
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < W_SLOTS; ++q) {
+        if (k0 + kr[q] >= p1) {
+          *reinterpret_cast<floatx4 *>(As[st] + lofs[q]) = z;
+          *reinterpret_cast<floatx4 *>(Bs[st] + lofs[q]) = z;
+        }
+      }
+    };
+    auto compute = [&](int st) {
+      const float *Ab = As[st];
+      const float *Bb = Bs[st];
 #pragma unroll
       for (int kg = 0; kg < WK; kg += 8) {
+        floatx4 sc = {1.f, 1.f, 1.f, 1.f};
+        if (SC) sc = *reinterpret_cast<const floatx4 *>(Ss[st] + kg + kh);
         float a[2][4], b[2][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const int row = (kg + kh + q) * WB;
 #pragma unroll
-          for (int bi = 0; bi < 2; ++bi) a[bi][q] = Ab[(kg + kh + q) * WLD + wm * 64 + bi * 32 + l32];
+          for (int bi = 0; bi < 2; ++bi) a[bi][q] = Ab[row + ((wm * 64 + bi * 32 + l32) ^ (32 * half))] * sc[q];
 #pragma unroll
-          for (int bj = 0; bj < 2; ++bj) b[bj][q] = Bb[(kg + kh + q) * WLD + wn * 64 + bj * 32 + l32];
+          for (int bj = 0; bj < 2; ++bj) b[bj][q] = Bb[row + ((wn * 64 + bj * 32 + l32) ^ (32 * half))];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -176,9 +239,46 @@ __global__ void __launch_bounds__(W_THREADS) wgrad_kernel(WgradArgs g, int k_spl
             for (int bj = 0; bj < 2; ++bj)
               acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[bi][q], b[bj][q], acc[bi][bj], 0, 0, 0);
       }
-      if (s + 1 < nsteps) store(cur ^ 1);
-      __syncthreads();
+    };
+    // Issue order, one pair per step: the gather indices of step j + 1, then
+    // the tiles of step j.  At the top of step kt one pair (indices of kt + 2,
+    // tiles of kt + 1) is younger than step kt's tiles; after the barrier the
+    // indices of kt + 2 are awaited (only the tiles of kt + 1 stay in flight),
+    // read back, and the pair (indices of kt + 3, tiles of kt + 2) is issued.
+    auto step = [&](auto sc_, int kt) {
+      constexpr int s = decltype(sc_)::value;
+      w_wait_vm<NIDX + NL>();
+      zero_tail(s, kt);
+      w_lds_barrier();
+      if (NIDX) {
+        w_wait_vm<NL>();
+        issue_idx(s, kt + WS);
+      }
+      issue((s + WS - 1) % WS, (s + WS - 1) % WS, kt + WS - 1);
+      compute(s);
+    };
+    if (NIDX) {
+      issue_idx(0, 0);
+      w_wait_vm<0>();
+      issue_idx(1, 1);
     }
+    issue(0, 0, 0);
+    if (NIDX) {
+      w_wait_vm<NL>();
+      issue_idx(2, 2);
+    }
+    issue(1, 1, 1);
+    int kt = 0;
+    for (; kt + WS <= nsteps; kt += WS) {
+      step(std::integral_constant<int, 0>{}, kt);
+      step(std::integral_constant<int, 1>{}, kt + 1);
+      step(std::integral_constant<int, 2>{}, kt + 2);
+    }
+    if (kt < nsteps) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nsteps) step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    w_wait_vm<0>();   // no copy may land in LDS after the workgroup ends
   }
 
   // output element (m, n): m = 8*(r/4) + 4*(lane/32) + r%4 of the block, n = lane%32
@@ -692,7 +792,18 @@ int launch_wgrad(const WgradArgs &a, float *split_ws, hipStream_t stream) {
     set_error("weight-gradient GEMM too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
   }
-  wgrad_kernel<<<dim3(unsigned(grid)), dim3(W_THREADS), 0, stream>>>(a, ks, rows_per_split, split_ws);
+  const int variant = (a.a_rows ? 4 : 0) | (a.b_rows ? 2 : 0) | (a.scale ? 1 : 0);
+  const dim3 gd = dim3(unsigned(grid)), bd = dim3(W_THREADS);
+  switch (variant) {
+    case 0: wgrad_kernel<false, false, false><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 1: wgrad_kernel<false, false, true><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 2: wgrad_kernel<false, true, false><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 3: wgrad_kernel<false, true, true><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 4: wgrad_kernel<true, false, false><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 5: wgrad_kernel<true, false, true><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    case 6: wgrad_kernel<true, true, false><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+    default: wgrad_kernel<true, true, true><<<gd, bd, 0, stream>>>(a, ks, rows_per_split, split_ws); break;
+  }
   MLIP_LAUNCHED();
   if (ks > 1) {
     const int64_t n4 = int64_t(a.Mo) * a.No / 4;
