@@ -109,6 +109,29 @@ __device__ inline int64_t xcd_block(int64_t n) {
   return logical < n ? logical : -1;
 }
 
+// ------------------------------------------- global -> LDS copies (gfx950) --
+// global_load_lds_dwordx4 / _dword: each lane of a wave copies 16 (or 4)
+// bytes from its own global address to a wave-uniform LDS base + 16 (4) x
+// lane, without passing through registers.  The copies count on vmcnt.
+#define MLIP_GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void *)(p))
+#define MLIP_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt vmcnt(N), the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for pipelined k loops: this wave's LDS accesses are
+// complete (lgkmcnt 0) and the compiler moves no memory access across it.
+// Unlike __syncthreads() it does not wait for outstanding global loads, so
+// the LDS copies of later stages stay in flight; each wave waits for its own
+// copies of a stage (wait_vmcnt) before the barrier that publishes it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------- radial basis -----
 // Constants of the pair-distance basis: K Gaussians exp(-gamma (r - k mu_step)^2),
 // k = 0..K-1, mu_step = r_c/(K-1), gamma = (K-1)^2 / (2 r_c^2), and the cosine

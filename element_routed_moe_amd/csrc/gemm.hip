@@ -64,25 +64,6 @@ __device__ inline int block_scan_excl(int v, int *red) {
   return off + x - v;
 }
 
-#define GPTR(p) ((const __attribute__((address_space(1))) void *)(p))
-#define LPTR(p) ((__attribute__((address_space(3))) void *)(p))
-
-// s_waitcnt vmcnt(N), other counters untouched
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier for the k loop: this wave's LDS accesses are complete
-// (lgkmcnt 0) and no memory access is moved across it.  Unlike
-// __syncthreads() it does not wait for outstanding global loads, so the
-// copies of later stages stay in flight; each wave waits for its own copies
-// of a stage (wait_vm) before the barrier that publishes the stage.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // One BM x BN output tile.  Each k-step's A and B tiles are copied from
 // global memory straight into LDS (global_load_lds_dwordx4: every lane moves
 // one 16-byte chunk to base + 16*lane), S stages deep, one barrier per step.
@@ -164,13 +145,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
       const int k = k0 + a_kc[q];
-      __builtin_amdgcn_global_load_lds(GPTR(a_src[q] + (k < g.K ? k : 0)), LPTR(a_dst + a_dof[q]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(a_src[q] + (k < g.K ? k : 0)), MLIP_LDS_PTR(a_dst + a_dof[q]), 16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
       const int k = k0 + b_kc[q];
       const int64_t off = BT ? int64_t(k < g.K ? k : 0) : int64_t(k < g.K ? k : 0) * g.ldb;
-      __builtin_amdgcn_global_load_lds(GPTR(b_src[q] + off), LPTR(b_dst + (q * 4 + wave) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(b_src[q] + off), MLIP_LDS_PTR(b_dst + (q * 4 + wave) * 256), 16, 0, 0);
     }
   };
   // K tail: after its loads have landed, each lane zeroes the chunks it
@@ -255,7 +236,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   // younger than step kt's at its top, on every path through the loop.
   auto step = [&](auto sc, int kt) {
     constexpr int s = decltype(sc)::value;
-    wait_vm<(S - 2) * NL>();
+    wait_vmcnt<(S - 2) * NL>();
     if (k_tail && kt == nk - 1) zero_tail(As[s], Bs[s], kt);
     lds_barrier();
     issue(As[(s + S - 1) % S], Bs[(s + S - 1) % S], min(kt + S - 1, nk - 1));
@@ -284,7 +265,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
       }
     }
   }
-  wait_vm<0>();   // no copy may land in LDS after the workgroup ends
+  wait_vmcnt<0>();   // no copy may land in LDS after the workgroup ends
 
   // ---- epilogue: D[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 ----
   const int kh = half * 4;

@@ -69,20 +69,6 @@ constexpr int WS = 3;    // LDS stages: 3 x 17 KB, three workgroups per CU
 constexpr int W_THREADS = 256;
 constexpr int W_SLOTS = WK * WB / 4 / W_THREADS;   // 16-byte copies per lane per operand and step
 
-#define W_GPTR(p) ((const __attribute__((address_space(1))) void *)(p))
-#define W_LPTR(p) ((__attribute__((address_space(3))) void *)(p))
-
-// s_waitcnt vmcnt(N), other counters untouched
-template <int N>
-__device__ __forceinline__ void w_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-// Barrier that waits for this wave's LDS accesses but not for its
-// outstanding global loads (the copies of later stages stay in flight),
-// and across which the compiler moves no memory access.
-__device__ __forceinline__ void w_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 template <bool GA, bool GB, bool SC>
 __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_split, int64_t rows_per_split,
                                                              float *__restrict__ part) {
@@ -172,8 +158,8 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
       int term, k0;
       step_rows(s, term, k0);
       const int p = lane_row(k0);
-      if (GA) __builtin_amdgcn_global_load_lds(W_GPTR(g.a_rows + p), W_LPTR(Xs[set]), 4, 0, 0);
-      if (GB) __builtin_amdgcn_global_load_lds(W_GPTR(g.b_rows + p), W_LPTR(Xs[set] + (GA ? 64 : 0)), 4, 0, 0);
+      if (GA) __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(g.a_rows + p), MLIP_LDS_PTR(Xs[set]), 4, 0, 0);
+      if (GB) __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(g.b_rows + p), MLIP_LDS_PTR(Xs[set] + (GA ? 64 : 0)), 4, 0, 0);
     };
     auto issue = [&](int st, int set, int s) {
       int term, k0;
@@ -190,13 +176,13 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
       }
 #pragma unroll
       for (int q = 0; q < W_SLOTS; ++q)
-        __builtin_amdgcn_global_load_lds(W_GPTR(A + ra[q] * g.lda + ca[q]), W_LPTR(As[st] + (q * 4 + wave) * 256), 16,
+        __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(A + ra[q] * g.lda + ca[q]), MLIP_LDS_PTR(As[st] + (q * 4 + wave) * 256), 16,
                                          0, 0);
 #pragma unroll
       for (int q = 0; q < W_SLOTS; ++q)
-        __builtin_amdgcn_global_load_lds(W_GPTR(B + rb[q] * g.ldb + cb[q]), W_LPTR(Bs[st] + (q * 4 + wave) * 256), 16,
+        __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(B + rb[q] * g.ldb + cb[q]), MLIP_LDS_PTR(Bs[st] + (q * 4 + wave) * 256), 16,
                                          0, 0);
-      if (SC) __builtin_amdgcn_global_load_lds(W_GPTR(g.scale + lane_row(k0)), W_LPTR(Ss[st]), 4, 0, 0);
+      if (SC) __builtin_amdgcn_global_load_lds(MLIP_GLOBAL_PTR(g.scale + lane_row(k0)), MLIP_LDS_PTR(Ss[st]), 4, 0, 0);
     };
     constexpr int NIDX = NG;
     constexpr int NL = 2 * W_SLOTS + (SC ? 1 : 0);
@@ -247,11 +233,11 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
     // read back, and the pair (indices of kt + 3, tiles of kt + 2) is issued.
     auto step = [&](auto sc_, int kt) {
       constexpr int s = decltype(sc_)::value;
-      w_wait_vm<NIDX + NL>();
+      wait_vmcnt<NIDX + NL>();
       zero_tail(s, kt);
-      w_lds_barrier();
+      lds_barrier();
       if (NIDX) {
-        w_wait_vm<NL>();
+        wait_vmcnt<NL>();
         issue_idx(s, kt + WS);
       }
       issue((s + WS - 1) % WS, (s + WS - 1) % WS, kt + WS - 1);
@@ -259,12 +245,12 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
     };
     if (NIDX) {
       issue_idx(0, 0);
-      w_wait_vm<0>();
+      wait_vmcnt<0>();
       issue_idx(1, 1);
     }
     issue(0, 0, 0);
     if (NIDX) {
-      w_wait_vm<NL>();
+      wait_vmcnt<NL>();
       issue_idx(2, 2);
     }
     issue(1, 1, 1);
@@ -278,7 +264,7 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
       step(std::integral_constant<int, 0>{}, kt);
       if (kt + 1 < nsteps) step(std::integral_constant<int, 1>{}, kt + 1);
     }
-    w_wait_vm<0>();   // no copy may land in LDS after the workgroup ends
+    wait_vmcnt<0>();   // no copy may land in LDS after the workgroup ends
   }
 
   // output element (m, n): m = 8*(r/4) + 4*(lane/32) + r%4 of the block, n = lane%32
