@@ -552,8 +552,17 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
     if (rc) return rc;
     graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
     MLIP_LAUNCHED();
-    MLIP_HIP(hipMemcpyAsync(host, w.readback, sizeof(host), hipMemcpyDeviceToHost, stream));
-    MLIP_HIP(hipStreamSynchronize(stream));
+    // the one host sync of the build: E, the error flags and the largest
+    // degree, read into a pinned per-thread buffer (a pageable target takes
+    // the staged copy path), then polled rather than slept on
+    static thread_local int32_t *pinned = nullptr;
+    if (!pinned) MLIP_HIP(hipHostMalloc(reinterpret_cast<void **>(&pinned), sizeof(host), hipHostMallocPortable));
+    MLIP_HIP(hipMemcpyAsync(pinned, w.readback, sizeof(host), hipMemcpyDeviceToHost, stream));
+    hipError_t q;
+    while ((q = hipStreamQuery(stream)) == hipErrorNotReady) {
+    }
+    MLIP_HIP(q);
+    for (int t = 0; t < 4; ++t) host[t] = pinned[t];
   }
   const int64_t E = host[0];
   const int flags = host[1];
