@@ -139,30 +139,40 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 # --------------------------------------------------------------- entry points
 def mlip_build_graph(pos, cell, struct_ptr, cutoff: float, edge_capacity: Optional[int] = None,
-                     ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
-    """Periodic radius graph (CSR by receiver).  Returns row_ptr, src, shift, rev, geom, n_edges."""
+                     ws: Optional[torch.Tensor] = None, buffers: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+    """Periodic radius graph (CSR by receiver).  Returns row_ptr, src, shift, rev, geom, n_edges.
+
+    ``buffers`` (the "buffers" entry of an earlier result) lends its arrays
+    when their capacity suffices, so a repeated build allocates nothing; the
+    earlier result's tensors are then overwritten."""
     dev = pos.device
     N, B = int(pos.shape[0]), int(cell.shape[0])
     if ws is None:
         ws = _ws(_lib.mlip_graph_workspace_size(N, B), dev)
     cap = int(edge_capacity) if edge_capacity is not None else max(64 * N, 1)
-    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
     for _ in range(2):
-        src = torch.empty(cap, dtype=torch.int32, device=dev)
-        shift = torch.empty((cap, 4), dtype=torch.int8, device=dev)
-        rev = torch.empty(cap, dtype=torch.int32, device=dev)
-        geom = torch.empty((cap, 4), dtype=torch.float32, device=dev)
+        if buffers is not None and buffers["src"].shape[0] >= cap and buffers["row_ptr"].shape[0] == N + 1:
+            row_ptr, src, shift, rev, geom = (buffers[k] for k in ("row_ptr", "src", "shift", "rev", "geom"))
+            cap = int(src.shape[0])
+        else:
+            row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+            src = torch.empty(cap, dtype=torch.int32, device=dev)
+            shift = torch.empty((cap, 4), dtype=torch.int8, device=dev)
+            rev = torch.empty(cap, dtype=torch.int32, device=dev)
+            geom = torch.empty((cap, 4), dtype=torch.float32, device=dev)
+            buffers = dict(row_ptr=row_ptr, src=src, shift=shift, rev=rev, geom=geom)
         ne = C.c_int64(0)
         rc = _lib.mlip_build_graph(_ptr(pos), _ptr(cell), _ptr(struct_ptr), N, B, float(cutoff), cap,
                                    _ptr(row_ptr), _ptr(src), _ptr(shift), _ptr(rev), _ptr(geom),
                                    C.byref(ne), _ptr(ws), ws.numel(), _stream())
         if rc == MLIP_ERR_CAPACITY:
             cap = int(ne.value)
+            buffers = None
             continue
         _check(rc)
         E = int(ne.value)
         return dict(row_ptr=row_ptr, src=src[:E], shift=shift[:E], rev=rev[:E], geom=geom[:E],
-                    n_edges=E)
+                    n_edges=E, buffers=buffers)
     raise MlipError(MLIP_ERR_CAPACITY, "edge capacity could not be met")
 
 
@@ -701,7 +711,8 @@ class Block:
 
     def step(self):
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
-                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
+                             edge_capacity=self.edge_capacity, ws=self.ws_graph,
+                             buffers=None if self.graph is None else self.graph["buffers"])
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
         reuse = self.agg
@@ -919,7 +930,8 @@ class FullBlock:
 
     def step(self):
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
-                             edge_capacity=self.edge_capacity, ws=self.ws_graph)
+                             edge_capacity=self.edge_capacity, ws=self.ws_graph,
+                             buffers=None if self.graph is None else self.graph["buffers"])
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
         self.graph = g
@@ -965,7 +977,8 @@ class Stack:
     def step(self):
         L0 = self.first
         g = mlip_build_graph(L0.pos, L0.cell, L0.struct_ptr, L0.cutoff,
-                             edge_capacity=self.edge_capacity, ws=L0.ws_graph)
+                             edge_capacity=self.edge_capacity, ws=L0.ws_graph,
+                             buffers=None if self.graph is None else self.graph["buffers"])
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
         self.graph = g
