@@ -55,13 +55,13 @@ int check_width(int32_t d, const char *name) {
 
 // ------------------------------------------------------------- workspaces --
 struct AggWs {
-  float *a;
+  float *a, *split;
 };
 AggWs carve_agg(void *base, int64_t N, int64_t De, int64_t Dn, size_t *bytes) {
-  (void)Dn;
   Carver c(base);
   AggWs w;
   w.a = c.take<float>(size_t(N * De));
+  w.split = c.take<float>(size_t(dense_split_floats(N, De, Dn)));   // s = h W_d split over K
   if (bytes) *bytes = c.bytes();
   return w;
 }
@@ -87,11 +87,12 @@ MoeWs carve_moe(void *base, int64_t N, int64_t T, int64_t X, int64_t k, int64_t 
 }
 
 struct VjpWs {
-  float *Q, *Utok, *ubar, *abar, *sbar, *virial;
+  float *Q, *Utok, *ubar, *abar, *sbar, *virial, *split;
 };
 VjpWs carve_vjp(void *base, int64_t N, int64_t k, int64_t De, int64_t Dn, int64_t H, size_t *bytes) {
   Carver c(base);
   VjpWs w;
+  w.split = c.take<float>(size_t(dense_split_floats(N, De, Dn)));   // abar = ubar W_u^T split over K
   w.virial = c.take<float>(size_t(N * 6));
   w.Q = c.take<float>(size_t(N * k * H));
   w.Utok = c.take<float>(size_t(N * k * Dn));
@@ -392,6 +393,7 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
   GemmArgs g;  // s = h @ W_d
   g.A = h; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s; g.ldc = d_edge;
   g.M = n_atoms; g.N = d_edge; g.K = d_node;
+  g.k_split = dense_k_split(n_atoms, d_edge, d_node); g.split_ws = w.split;
   if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   if (int rc = launch_embed_aggregate(row_ptr, src, geom, n_atoms, W_e, s, d_edge, cutoff, e, w.a,
                                       stream))
@@ -539,6 +541,7 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
   GemmArgs g3;  // abar = ubar @ W_u^T
   g3.A = w.ubar; g3.lda = d_node; g3.B = W_u; g3.ldb = d_node; g3.C = w.abar; g3.ldc = d_edge;
   g3.M = n_atoms; g3.N = d_edge; g3.K = d_node;
+  g3.k_split = dense_k_split(n_atoms, d_edge, d_node); g3.split_ws = w.split;
   if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   if (int rc = launch_edge_vjp(row_ptr, src, geom, n_atoms, W_e, e, s, w.abar, d_edge, cutoff,
                                w.sbar, grad_pos, vir, stream))

@@ -180,10 +180,19 @@ struct GemmArgs {
   const int32_t *group_off = nullptr;  // [G+1] row ranges; nullptr -> one group [0, M)
   int n_groups = 1;
   int M = 0, N = 0, K = 0;
+  // Dense GEMMs only: split K into k_split parts whose products go to
+  // split_ws ([k_split][M][N]) and are then summed in part order (with the
+  // epilogue), when the output has too few tiles to fill the GPU.
+  float *split_ws = nullptr;
+  int k_split = 1;
 };
 
 int launch_gemm(const GemmArgs &a, bool b_transposed, Epilogue epi, KClass cls,
                 hipStream_t stream);
+// K parts a dense M x N x K GEMM is split into (1: none), and the floats of
+// split_ws it then needs.
+int dense_k_split(int64_t M, int64_t N, int64_t K);
+int64_t dense_split_floats(int64_t M, int64_t N, int64_t K);
 
 // ------------------------------------------------------ training gradient -
 // Weight-gradient sums on the matrix cores:

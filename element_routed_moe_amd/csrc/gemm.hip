@@ -243,29 +243,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     compute(As[s], Bs[s]);
   };
 
+  if (nk > 0) {   // K = 0: the product is zero
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(As[s], Bs[s], min(s, nk - 1));
-  // whole groups of S steps (the loop's back edge only follows step S - 1),
-  // then the remaining nk % S steps, which continue at stage 0
-  int kt = 0;
-  for (; kt + S <= nk; kt += S) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    if constexpr (S >= 3) step(std::integral_constant<int, 2 % S>{}, kt + 2);
-    if constexpr (S >= 4) step(std::integral_constant<int, 3 % S>{}, kt + 3);
-  }
-  if (kt < nk) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if constexpr (S >= 3) {
-      if (kt + 1 < nk) {
-        step(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (S >= 4) {
-          if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+    for (int s = 0; s < S - 1; ++s) issue(As[s], Bs[s], min(s, nk - 1));
+    // whole groups of S steps (the loop's back edge only follows step S - 1),
+    // then the remaining nk % S steps, which continue at stage 0
+    int kt = 0;
+    for (; kt + S <= nk; kt += S) {
+      step(std::integral_constant<int, 0>{}, kt);
+      step(std::integral_constant<int, 1>{}, kt + 1);
+      if constexpr (S >= 3) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+      if constexpr (S >= 4) step(std::integral_constant<int, 3 % S>{}, kt + 3);
+    }
+    if (kt < nk) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if constexpr (S >= 3) {
+        if (kt + 1 < nk) {
+          step(std::integral_constant<int, 1>{}, kt + 1);
+          if constexpr (S >= 4) {
+            if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+          }
         }
       }
     }
+    wait_vmcnt<0>();   // no copy may land in LDS after the workgroup ends
   }
-  wait_vmcnt<0>();   // no copy may land in LDS after the workgroup ends
 
   // ---- epilogue: D[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 ----
   const int kh = half * 4;
@@ -350,8 +352,9 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   const int jx = L / N_XCD, xcd = L - jx * N_XCD;
 
   // ---- m-tiles per group (full and, with SPLIT, short) -> prefix in LDS ----
-  int Mt, t_local;
+  int Mt, t_local, part = 0;
   bool short_tile = false;
+  const int ks = (!SPLIT && g.split_ws && g.k_split > 1) ? g.k_split : 1;
   if (g.group_off) {
     constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
     int cf[PER], ch[PER], sf = 0, sh = 0;
@@ -403,10 +406,12 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
     __syncthreads();
   } else {
     Mt = (g.M + BM - 1) / BM;
-    const int per = (Mt * Nt + N_XCD - 1) / N_XCD;
+    const int per = (Mt * Nt * ks + N_XCD - 1) / N_XCD;
     if (jx >= per) return;
     t_local = xcd * per + jx;
-    if (t_local >= Mt * Nt) return;
+    if (t_local >= Mt * Nt * ks) return;
+    part = t_local / (Mt * Nt);
+    t_local -= part * (Mt * Nt);
   }
   const int group_size = RASTER_M * Nt;
   const int first_m = (t_local / group_size) * RASTER_M;
@@ -442,7 +447,48 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
       return;
     }
   }
+  if (!SPLIT && ks > 1) {
+    // K part `part`: its raw product goes to split_ws[part]; the parts are
+    // summed (with the epilogue) by split_epilogue_kernel
+    const int Ks = ((g.K + ks - 1) / ks + BK - 1) / BK * BK;
+    const int kb = min(part * Ks, g.K);
+    GemmArgs gp = g;
+    gp.A = g.A + kb;
+    gp.B = BT ? g.B + kb : g.B + int64_t(kb) * g.ldb;
+    gp.K = min(g.K - kb, Ks);
+    gp.C = g.split_ws + int64_t(part) * g.M * g.N;
+    gp.ldc = g.N;
+    gemm_tile<BM, BN, BK, WM, WN, BT, EPI_STORE, S, AST, BST>(gp, As, Bs, gp.B, row0, rows, n0);
+    return;
+  }
   gemm_tile<BM, BN, BK, WM, WN, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
+}
+
+// C = (R +) the sum of the k_split parts in split_ws, in part order.
+template <bool RESID>
+__global__ void __launch_bounds__(256) split_epilogue_kernel(const float4 *__restrict__ part, int ks, int64_t mn4,
+                                                             int n4, const float *__restrict__ R, int64_t ldr,
+                                                             float *__restrict__ C, int64_t ldc) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= mn4) return;
+  const int64_t m = i / n4;
+  const int c = int(i - m * n4) * 4;
+  float4 v = part[i];
+  for (int q = 1; q < ks; ++q) {
+    const float4 t = part[int64_t(q) * mn4 + i];
+    v.x += t.x;
+    v.y += t.y;
+    v.z += t.z;
+    v.w += t.w;
+  }
+  if (RESID) {
+    const float4 r = *reinterpret_cast<const float4 *>(R + m * ldr + c);
+    v.x += r.x;
+    v.y += r.y;
+    v.z += r.z;
+    v.w += r.w;
+  }
+  *reinterpret_cast<float4 *>(C + m * ldc + c) = v;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
@@ -453,7 +499,8 @@ int launch_t(const GemmArgs &a, hipStream_t stream) {
   const int64_t nt = cdiv(a.N, BN);
   int64_t per;
   if (!a.group_off) {
-    per = cdiv(cdiv(a.M, BM) * nt, N_XCD);
+    const int64_t ks = (!SPLIT && a.split_ws && a.k_split > 1) ? a.k_split : 1;
+    per = cdiv(cdiv(a.M, BM) * nt * ks, N_XCD);
   } else if (SPLIT) {
     const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * (BM / 2 - 1)) / BM;
     per = cdiv(mf * nt, N_XCD) + cdiv(int64_t(a.n_groups) * nt, N_XCD);
@@ -480,11 +527,41 @@ int launch_expert(const GemmArgs &a, hipStream_t s) {
 // workgroups for 256 CUs), else 64 x 128.
 template <bool BT, int EPI, int TAG>
 int launch_dense(const GemmArgs &a, hipStream_t s) {
-  if (a.N <= 512) return launch_t<64, 64, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
-  return launch_t<64, 128, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
+  static_assert(EPI == EPI_STORE || EPI == EPI_RESID, "dense epilogues");
+  const bool split = a.split_ws && a.k_split > 1;
+  int rc = a.N <= 512 ? launch_t<64, 64, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s)
+                      : launch_t<64, 128, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
+  if (rc || !split) return rc;
+  if ((a.ldc & 3) || (EPI == EPI_RESID && (a.ldr & 3))) {
+    set_error("split-K GEMM needs ldc and ldr multiples of 4");
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  const int64_t mn4 = int64_t(a.M) * a.N / 4;
+  const dim3 grid(unsigned(cdiv(mn4, 256)));
+  split_epilogue_kernel<EPI == EPI_RESID><<<grid, dim3(256), 0, s>>>(
+      reinterpret_cast<const float4 *>(a.split_ws), a.k_split, mn4, a.N / 4, a.R, a.ldr, a.C, a.ldc);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
 }
 
 }  // namespace
+
+// A dense output with fewer tiles than the GPU holds workgroups (64 x 64
+// tiles, four per CU) leaves CUs idle for the whole K loop; splitting K into
+// up to 4 parts of at least 256 fills them.
+int dense_k_split(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  const int64_t bn = N <= 512 ? 64 : 128;
+  const int64_t tiles = cdiv(M, 64) * cdiv(N, bn);
+  const int64_t slots = 256 * (N <= 512 ? 4 : 3);
+  int64_t ks = std::min<int64_t>(4, slots / std::max<int64_t>(tiles, 1));
+  while (ks > 1 && K / ks < 256) --ks;
+  return int(std::max<int64_t>(ks, 1));
+}
+int64_t dense_split_floats(int64_t M, int64_t N, int64_t K) {
+  const int ks = dense_k_split(M, N, K);
+  return ks > 1 ? int64_t(ks) * M * N : 0;
+}
 
 int launch_gemm(const GemmArgs &a, bool bt, Epilogue epi, KClass cls, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0) return MLIP_OK;
