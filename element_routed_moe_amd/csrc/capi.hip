@@ -116,11 +116,12 @@ MoeVjpWs carve_moe_vjp(void *base, int64_t N, int64_t k, int64_t Dn, int64_t H, 
 }
 
 struct AttnVjpWs {
-  float *obar, *qkv_bar, *edge_g, *edge_a, *edge_c, *virial;
+  float *obar, *qkv_bar, *edge_g, *edge_a, *edge_c, *virial, *split;
 };
 AttnVjpWs carve_attn_vjp(void *base, int64_t N, int64_t E, int64_t Da, int64_t nh, size_t *bytes) {
   Carver c(base);
   AttnVjpWs w;
+  w.split = c.take<float>(size_t(dense_split_floats_max(N, Da)));   // obar = ubar W_o^T split over K
   w.obar = c.take<float>(size_t(N * Da));
   w.qkv_bar = c.take<float>(size_t(N * 3 * Da));
   w.edge_g = c.take<float>(size_t(E * nh));
@@ -132,11 +133,12 @@ AttnVjpWs carve_attn_vjp(void *base, int64_t N, int64_t E, int64_t Da, int64_t n
 }
 
 struct TriVjpWs {
-  float *taubar, *sigma, *gvec, *sbar, *virial;
+  float *taubar, *sigma, *gvec, *sbar, *virial, *split;
 };
 TriVjpWs carve_tri_vjp(void *base, int64_t N, int64_t E, int64_t Dt, size_t *bytes) {
   Carver c(base);
   TriVjpWs w;
+  w.split = c.take<float>(size_t(dense_split_floats_max(N, Dt)));   // taubar = grad_hT W_T^T split over K
   w.taubar = c.take<float>(size_t(N * Dt));
   w.sigma = c.take<float>(size_t(E * Dt));
   w.gvec = c.take<float>(size_t(E * 4));
@@ -691,6 +693,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   GemmArgs g1;  // obar = ubar @ W_o^T
   g1.A = grad_u; g1.lda = d_node; g1.B = W_o; g1.ldb = d_node; g1.C = w.obar; g1.ldc = d_attn;
   g1.M = n_atoms; g1.N = d_attn; g1.K = d_node;
+  g1.k_split = dense_k_split(n_atoms, d_attn, d_node); g1.split_ws = w.split;
   if (int rc = launch_gemm(g1, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   AttnArgs a;
   a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = n_atoms;
@@ -795,6 +798,7 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   GemmArgs g1;  // taubar = grad_hT @ W_T^T
   g1.A = grad_hT; g1.lda = d_node; g1.B = W_T; g1.ldb = d_node; g1.C = w.taubar; g1.ldc = d_tri;
   g1.M = n_atoms; g1.N = d_tri; g1.K = d_node;
+  g1.k_split = dense_k_split(n_atoms, d_tri, d_node); g1.split_ws = w.split;
   if (int rc = launch_gemm(g1, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   TriArgs a;
   a.row_ptr = row_ptr; a.src = src; a.rev = rev; a.geom = geom; a.n_atoms = n_atoms;

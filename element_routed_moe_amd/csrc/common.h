@@ -193,6 +193,8 @@ int launch_gemm(const GemmArgs &a, bool b_transposed, Epilogue epi, KClass cls,
 // split_ws it then needs.
 int dense_k_split(int64_t M, int64_t N, int64_t K);
 int64_t dense_split_floats(int64_t M, int64_t N, int64_t K);
+// The most split_ws an M x N output can need, for any K.
+int64_t dense_split_floats_max(int64_t M, int64_t N);
 
 // ------------------------------------------------------ training gradient -
 // Weight-gradient sums on the matrix cores:

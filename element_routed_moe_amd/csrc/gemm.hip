@@ -546,22 +546,35 @@ int launch_dense(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// A dense output with fewer tiles than the GPU holds workgroups (64 x 64
-// tiles, four per CU) leaves CUs idle for the whole K loop; splitting K into
-// up to 4 parts of at least 256 fills them.
+// A dense output with few tiles leaves CUs idle (or a partly filled last
+// round of workgroups) for the whole K loop.  Splitting K into ks parts turns
+// one tile into ks shorter ones; the count is the one (up to 4, parts of at
+// least 256) that minimises rounds(ks) / ks, the K loops' duration in units of
+// the unsplit loop, plus a tenth for the summing pass, where rounds(ks) is
+// the number of rounds of resident workgroups (four 64 x 64 or three 64 x 128
+// tiles per CU) the tiles take.  Outputs of two rounds or more are not split.
 int dense_k_split(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  if (M <= 0 || N <= 0 || K < 512) return 1;
   const int64_t bn = N <= 512 ? 64 : 128;
   const int64_t tiles = cdiv(M, 64) * cdiv(N, bn);
   const int64_t slots = 256 * (N <= 512 ? 4 : 3);
-  int64_t ks = std::min<int64_t>(4, slots / std::max<int64_t>(tiles, 1));
-  while (ks > 1 && K / ks < 256) --ks;
-  return int(std::max<int64_t>(ks, 1));
+  if (tiles >= 2 * slots) return 1;
+  int best = 1;
+  double best_cost = double(cdiv(tiles, slots));
+  for (int ks = 2; ks <= 4 && K / ks >= 256; ++ks) {
+    const double cost = double(cdiv(tiles * ks, slots)) / ks + 0.1;
+    if (cost < best_cost - 1e-9) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 int64_t dense_split_floats(int64_t M, int64_t N, int64_t K) {
   const int ks = dense_k_split(M, N, K);
   return ks > 1 ? int64_t(ks) * M * N : 0;
 }
+int64_t dense_split_floats_max(int64_t M, int64_t N) { return dense_split_floats(M, N, int64_t(1) << 30); }
 
 int launch_gemm(const GemmArgs &a, bool bt, Epilogue epi, KClass cls, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0) return MLIP_OK;
