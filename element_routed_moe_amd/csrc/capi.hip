@@ -612,11 +612,15 @@ static int check_attn_dims(int32_t d_node, int32_t d_attn, int32_t n_heads, floa
   return MLIP_OK;
 }
 
+size_t mlip_attention_workspace_size(int32_t n_atoms, int32_t d_attn) {
+  return size_t(dense_split_floats_max(std::max(n_atoms, 0), 3 * int64_t(std::max(d_attn, 0)))) * sizeof(float);
+}
+
 int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
                    int64_t n_edges, const float *h0, const float *W_qkv, const float *Wa_e,
                    const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                    int32_t n_heads, float cutoff, float *qkv, float *o, float *stats, float *u,
-                   void *stream_) {
+                   void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
@@ -629,11 +633,18 @@ int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom
                      aligned(W_o, 16) && aligned(qkv, 16) && aligned(o, 16) && aligned(u, 16) &&
                      aligned(stats, 8),
                  "float arrays must be 16-byte aligned (stats 8-byte)");
+  if (ws) {
+    if (int rc = check_ws(ws, ws_bytes, mlip_attention_workspace_size(n_atoms, d_attn))) return rc;
+  }
   if (n_atoms == 0) return MLIP_OK;
   GemmArgs g;  // [q | k | v] = h0 @ W_qkv
   g.A = h0; g.lda = d_node; g.B = W_qkv; g.ldb = 3 * int64_t(d_attn);
   g.C = qkv; g.ldc = 3 * int64_t(d_attn);
   g.M = n_atoms; g.N = 3 * d_attn; g.K = d_node;
+  if (ws) {   // K split over the workspace when the output has few tiles
+    g.k_split = dense_k_split(n_atoms, 3 * int64_t(d_attn), d_node);
+    g.split_ws = static_cast<float *>(ws);
+  }
   if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   AttnArgs a;
   a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;
@@ -726,10 +737,14 @@ static int check_tri_dims(int32_t d_node, int32_t d_tri, int32_t n_ang, float cu
   return MLIP_OK;
 }
 
+size_t mlip_tri_workspace_size(int32_t n_atoms, int32_t d_tri) {
+  return size_t(dense_split_floats_max(std::max(n_atoms, 0), std::max(d_tri, 0))) * sizeof(float);
+}
+
 int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
              int64_t n_edges, const float *h, const float *W_s, const float *W_ang, const float *W_T,
              int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff, float *s, float *tau,
-             float *h_T, void *stream_) {
+             float *h_T, void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
@@ -741,10 +756,17 @@ int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int3
   MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_s, 16) && aligned(W_ang, 16) &&
                      aligned(W_T, 16) && aligned(s, 16) && aligned(tau, 16) && aligned(h_T, 16),
                  "float arrays must be 16-byte aligned");
+  if (ws) {
+    if (int rc = check_ws(ws, ws_bytes, mlip_tri_workspace_size(n_atoms, d_tri))) return rc;
+  }
   if (n_atoms == 0) return MLIP_OK;
   GemmArgs g;  // s = h @ W_s
   g.A = h; g.lda = d_node; g.B = W_s; g.ldb = d_tri; g.C = s; g.ldc = d_tri;
   g.M = n_atoms; g.N = d_tri; g.K = d_node;
+  if (ws) {   // K split over the workspace when the output has few tiles
+    g.k_split = dense_k_split(n_atoms, d_tri, d_node);
+    g.split_ws = static_cast<float *>(ws);
+  }
   if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
   TriArgs a;
   a.row_ptr = row_ptr; a.src = src; a.geom = geom; a.n_atoms = n_atoms;

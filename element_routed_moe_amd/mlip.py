@@ -85,7 +85,8 @@ _SIGS = {
                                              _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
                                              _p, _p, _p, _p, _sz, _p]),
     "mlip_attention": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
-                                 _f32, _p, _p, _p, _p, _p]),
+                                 _f32, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_attention_workspace_size": (_sz, [_i32, _i32]),
     "mlip_attention_vjp_workspace_size": (_sz, [_i32, _i64, _i32, _i32]),
     "mlip_attention_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _i32,
                                      _i32, _i32, _i32, _f32, _p, _p, _p, _p, _i32, _p, _p, _i32,
@@ -93,7 +94,8 @@ _SIGS = {
     "mlip_embed_atoms": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
     "mlip_embed_grad": (C.c_int, [_p, _p, _i32, _i32, _i32, _p, _p]),
     "mlip_tri": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
-                           _p, _p]),
+                           _p, _p, _sz, _p]),
+    "mlip_tri_workspace_size": (_sz, [_i32, _i32]),
     "mlip_tri_vjp_workspace_size": (_sz, [_i32, _i64, _i32]),
     "mlip_tri_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
@@ -487,11 +489,16 @@ def mlip_attention_tangent_vjp(graph, att, ajvp, h0, h0_dot, qkv_bar, W_qkv, Wa_
 
 
 def mlip_attention(graph, h0, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float,
-                   out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+                   out: Optional[Dict] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     N, Dn = int(h0.shape[0]), int(h0.shape[1])
     Da = int(W_o.shape[0])
     E = int(graph["n_edges"])
     dev = h0.device
+    need = _lib.mlip_attention_workspace_size(N, Da)
+    if ws is None and out is not None:
+        ws = out.get("ws")
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, dev)
     if out is None:
         out = dict(qkv=torch.empty((N, 3 * Da), dtype=torch.float32, device=dev),
                    o=torch.empty((N, Da), dtype=torch.float32, device=dev),
@@ -500,7 +507,9 @@ def mlip_attention(graph, h0, W_qkv, Wa_e, W_o, n_heads: int, cutoff: float,
     _check(_lib.mlip_attention(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
                                _ptr(h0), _ptr(W_qkv), _ptr(Wa_e), _ptr(W_o), int(Wa_e.shape[0]), Dn,
                                Da, int(n_heads), float(cutoff), _ptr(out["qkv"]), _ptr(out["o"]),
-                               _ptr(out["stats"]), _ptr(out["u"]), _stream()))
+                               _ptr(out["stats"]), _ptr(out["u"]), _ptr(ws) if need else None,
+                               ws.numel() if need else 0, _stream()))
+    out["ws"] = ws if need else None
     return out
 
 
@@ -555,18 +564,26 @@ def mlip_embed_grad(z, grad_h, n_types: int, out: Optional[torch.Tensor] = None)
     return out
 
 
-def mlip_tri(graph, h, W_s, W_ang, W_T, cutoff: float, out: Optional[Dict] = None) -> Dict[str, torch.Tensor]:
+def mlip_tri(graph, h, W_s, W_ang, W_T, cutoff: float, out: Optional[Dict] = None,
+             ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     N, Dn = int(h.shape[0]), int(h.shape[1])
     Dt = int(W_s.shape[1])
     E = int(graph["n_edges"])
     dev = h.device
+    need = _lib.mlip_tri_workspace_size(N, Dt)
+    if ws is None and out is not None:
+        ws = out.get("ws")
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, dev)
     if out is None:
         out = dict(s=torch.empty((N, Dt), dtype=torch.float32, device=dev),
                    tau=torch.empty((N, Dt), dtype=torch.float32, device=dev),
                    h_T=torch.empty((N, Dn), dtype=torch.float32, device=dev))
     _check(_lib.mlip_tri(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E, _ptr(h),
                          _ptr(W_s), _ptr(W_ang), _ptr(W_T), int(W_ang.shape[0]), Dn, Dt, float(cutoff),
-                         _ptr(out["s"]), _ptr(out["tau"]), _ptr(out["h_T"]), _stream()))
+                         _ptr(out["s"]), _ptr(out["tau"]), _ptr(out["h_T"]), _ptr(ws) if need else None,
+                         ws.numel() if need else 0, _stream()))
+    out["ws"] = ws if need else None
     return out
 
 

@@ -349,13 +349,20 @@ int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,
  * Outputs: qkv [n_atoms, 3*d_attn], o [n_atoms, d_attn] and
  *        stats [n_atoms, n_heads, 2] (running max of the scores, sum of the
  *        weights exp(s - max) f_c) are kept for mlip_attention_vjp;
- *        u [n_atoms, d_node] (may not alias h0).  No workspace.
+ *        u [n_atoms, d_node] (may not alias h0).
+ * ws: optional workspace of mlip_attention_workspace_size(n_atoms, d_attn)
+ *        bytes (256-byte aligned; null, or a size of 0 bytes, is allowed).  With
+ *        it, the q|k|v projection splits its K = d_node loop when the output
+ *        has too few tiles to fill the GPU and sums the parts in a fixed order;
+ *        without it the projection runs unsplit.  The results are the same up
+ *        to rounding order.
  * ------------------------------------------------------------------------ */
 int mlip_attention(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
                    int64_t n_edges, const float *h0, const float *W_qkv, const float *Wa_e,
                    const float *W_o, int32_t n_rbf, int32_t d_node, int32_t d_attn,
                    int32_t n_heads, float cutoff, float *qkv, float *o, float *stats, float *u,
-                   void *stream);
+                   void *ws, size_t ws_bytes, void *stream);
+size_t mlip_attention_workspace_size(int32_t n_atoms, int32_t d_attn);
 
 /* Input gradient of mlip_attention for grad_u = dL/du [n_atoms, d_node]:
  *   grad_h0 [n_atoms, d_node]  = dL/dh0 (through the residual, q, k and v);
@@ -461,11 +468,16 @@ int mlip_attention_tangent_vjp(
  * W_s [d_node, d_tri], W_ang [n_ang, d_tri], W_T [d_tri, d_node];
  * d_tri <= 512 (one wavefront per row).  Outputs s (kept for mlip_tri_vjp),
  * tau [n_atoms, d_tri] and h_T [n_atoms, d_node] (may not alias h).
+ * ws: optional workspace of mlip_tri_workspace_size(n_atoms, d_tri) bytes
+ * (256-byte aligned; null is allowed): with it the s projection splits its
+ * K = d_node loop when the output has too few tiles to fill the GPU, the
+ * parts summed in a fixed order; without it the projection runs unsplit.
  * ------------------------------------------------------------------------ */
 int mlip_tri(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
              int64_t n_edges, const float *h, const float *W_s, const float *W_ang, const float *W_T,
              int32_t n_ang, int32_t d_node, int32_t d_tri, float cutoff, float *s, float *tau,
-             float *h_T, void *stream);
+             float *h_T, void *ws, size_t ws_bytes, void *stream);
+size_t mlip_tri_workspace_size(int32_t n_atoms, int32_t d_tri);
 
 /* Input gradient of mlip_tri for grad_hT = dL/dh_T:
  *   grad_h [n_atoms, d_node] = dL/dh;

@@ -94,12 +94,18 @@ def test_attention_and_moe_vjp_reject_bad_args(mlip):
 
     def att(d_attn, n_heads, cutoff=5.0):
         return L.mlip_attention(f, f, f, 10, 20, f, f, f, f, 16, 64, d_attn, n_heads, cutoff,
-                                f, f, f, f, None)
+                                f, f, f, f, None, 0, None)
     assert "n_heads" in _err(mlip, att(32, 3), mlip.MLIP_ERR_INVALID)
     assert "d_attn" in _err(mlip, att(30, 3), mlip.MLIP_ERR_INVALID)
     assert "cutoff" in _err(mlip, att(32, 4, cutoff=0.0), mlip.MLIP_ERR_INVALID)
     # 5 heads of width 20: 20 is not c * 2^j with c in {1, 2, 3, 4, 6, 8}
     assert "unsupported attention shape" in _err(mlip, att(100, 5), mlip.MLIP_ERR_UNSUPPORTED)
+    # an optional workspace, when given, must have the size the query reports
+    need = L.mlip_attention_workspace_size(4096, 384)
+    assert need >= 2 * 4096 * 3 * 384 * 4      # 576 tiles of 64 x 128: the K loop is split
+    assert L.mlip_attention_workspace_size(262144, 384) == 0   # enough tiles: never split
+    rc = L.mlip_attention(f, f, f, 4096, 20, f, f, f, f, 16, 2560, 384, 8, 5.0, f, f, f, f, f, need - 1, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
     rc = L.mlip_attention_vjp(f, f, f, f, 10, 20, f, f, f, f, f, f, 16, 64, 32, 4, 5.0, f, f, f,
                               None, 0, None, f, 0, None, f, 1 << 30, None)
     assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
@@ -124,10 +130,14 @@ def test_tri_rejects_bad_args(mlip):
     f = C.c_void_p(256)
 
     def tri(n_ang=4, d_tri=32, cutoff=5.0):
-        return L.mlip_tri(f, f, f, 10, 20, f, f, f, f, n_ang, 64, d_tri, cutoff, f, f, f, None)
+        return L.mlip_tri(f, f, f, 10, 20, f, f, f, f, n_ang, 64, d_tri, cutoff, f, f, f, None, 0, None)
     assert "n_ang" in _err(mlip, tri(n_ang=3), mlip.MLIP_ERR_INVALID)
     assert "d_tri" in _err(mlip, tri(d_tri=30), mlip.MLIP_ERR_INVALID)
     assert "too wide" in _err(mlip, tri(d_tri=516), mlip.MLIP_ERR_UNSUPPORTED)
+    need = L.mlip_tri_workspace_size(4096, 384)
+    assert need > 0 and L.mlip_tri_workspace_size(262144, 384) == 0
+    rc = L.mlip_tri(f, f, f, 4096, 20, f, f, f, f, 4, 2560, 384, 5.0, f, f, f, f, need - 1, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
     def vjp(accumulate, atom_virial, grad_strain, ws_bytes=1 << 30):
         return L.mlip_tri_vjp(f, f, f, f, 10, 20, f, f, f, f, 4, 64, 32, 5.0, f, f, f, f, 1,
