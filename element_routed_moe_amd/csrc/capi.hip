@@ -330,7 +330,10 @@ AttnTanWs carve_attn_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t D
   a.P = b.P = int(N);
   a.Mo = int(Dn); a.No = int(3 * Da);
   b.Mo = int(Da); b.No = int(Dn);
-  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(a), wgrad_split_floats(b))));
+  // shared in stream order by the split-K parts of obar / obar_dot (first) and
+  // of the dense weight gradients (last)
+  w.split = c.take<float>(size_t(std::max({wgrad_split_floats(a), wgrad_split_floats(b),
+                                           dense_split_floats_max(N, Da)})));
   if (bytes) *bytes = c.bytes();
   return w;
 }
@@ -351,7 +354,10 @@ TriTanWs carve_tri_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t Dt,
   a.P = b.P = int(N);
   a.Mo = int(Dn); a.No = int(Dt);
   b.Mo = int(Dt); b.No = int(Dn);
-  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(a), wgrad_split_floats(b))));
+  // shared in stream order by the split-K parts of taubar / taubar_dot (first)
+  // and of the dense weight gradients (last)
+  w.split = c.take<float>(size_t(std::max({wgrad_split_floats(a), wgrad_split_floats(b),
+                                           dense_split_floats_max(N, Dt)})));
   if (bytes) *bytes = c.bytes();
   return w;
 }
@@ -1188,6 +1194,7 @@ int mlip_attention_tangent_vjp(
     GemmArgs g;  // obar = ubar W_o^T, obar_dot = ubar_dot W_o^T
     g.A = grad_u; g.lda = Dn; g.B = W_o; g.ldb = Dn; g.C = w.obar; g.ldc = Da;
     g.M = N; g.N = Da; g.K = Dn;
+    g.k_split = dense_k_split(N, Da, Dn); g.split_ws = w.split;
     if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
     g.A = grad_u_dot; g.C = w.obar_dot;
     if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
@@ -1294,6 +1301,7 @@ int mlip_tri_tangent_vjp(const int32_t *row_ptr, const int32_t *src, const int32
     GemmArgs g;  // taubar = grad_hT W_T^T, taubar_dot = grad_hT_dot W_T^T
     g.A = grad_hT; g.lda = Dn; g.B = W_T; g.ldb = Dn; g.C = w.taubar; g.ldc = Dt;
     g.M = N; g.N = Dt; g.K = Dn;
+    g.k_split = dense_k_split(N, Dt, Dn); g.split_ws = w.split;
     if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
     g.A = grad_hT_dot; g.C = w.taubar_dot;
     if (int rc = launch_gemm(g, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
