@@ -299,12 +299,14 @@ TanVjpWs carve_tan_vjp(void *base, int64_t N, int64_t T, int64_t k, int64_t De, 
   w.sbar = c.take<float>(size_t(N * De));
   w.sbar_dot = c.take<float>(size_t(N * De));
   w.dwe_part = c.take<float>(size_t(edge_tan_part_floats(int(N), int(De))));
-  // split-K scratch of the two dense weight gradients (the larger of the two)
+  // split-K scratch, shared in stream order by abar / abar_dot (first) and
+  // the two dense weight gradients (last)
   WgradArgs u, d;
   u.P = d.P = int(N);
   u.Mo = int(De); u.No = int(Dn);
   d.Mo = int(Dn); d.No = int(De);
-  w.split = c.take<float>(size_t(std::max(wgrad_split_floats(u), wgrad_split_floats(d))));
+  w.split = c.take<float>(size_t(std::max({wgrad_split_floats(u), wgrad_split_floats(d),
+                                           dense_split_floats_max(N, De)})));
   if (bytes) *bytes = c.bytes();
   return w;
 }
@@ -980,6 +982,7 @@ int mlip_block_tangent_vjp(
     GemmArgs g3;
     g3.A = ubar; g3.lda = Dn; g3.B = W_u; g3.ldb = Dn; g3.C = w.abar; g3.ldc = De;
     g3.M = N; g3.N = De; g3.K = Dn;
+    g3.k_split = dense_k_split(N, De, Dn); g3.split_ws = w.split;
     if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
     g3.A = w.ubar_dot; g3.C = w.abar_dot;
     if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
