@@ -18,6 +18,8 @@
 // shifts S_a are those with |d . n_a| < r_c for the plane normal n_a, i.e.
 // S_a in [-r_c/w_a - (f_j - f_i)_a, r_c/w_a - (f_j - f_i)_a] (widened by 1e-9).
 // For orthorhombic cells f_a = x_a / L_a and w_a = L_a.
+#include <thread>
+
 #include "common.h"
 
 namespace mlip {
@@ -553,14 +555,15 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
     graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
     MLIP_LAUNCHED();
     // the one host sync of the build: E, the error flags and the largest
-    // degree, read into a pinned per-thread buffer (a pageable target takes
-    // the staged copy path), then polled rather than slept on
+    // degree, read into a pinned buffer kept per host thread for the life of
+    // the process (a pageable target takes the staged copy path), then
+    // polled rather than slept on, so the launches that follow go out as soon
+    // as the stream drains (the calling thread yields between polls)
     static thread_local int32_t *pinned = nullptr;
     if (!pinned) MLIP_HIP(hipHostMalloc(reinterpret_cast<void **>(&pinned), sizeof(host), hipHostMallocPortable));
     MLIP_HIP(hipMemcpyAsync(pinned, w.readback, sizeof(host), hipMemcpyDeviceToHost, stream));
     hipError_t q;
-    while ((q = hipStreamQuery(stream)) == hipErrorNotReady) {
-    }
+    while ((q = hipStreamQuery(stream)) == hipErrorNotReady) std::this_thread::yield();
     MLIP_HIP(q);
     for (int t = 0; t < 4; ++t) host[t] = pinned[t];
   }

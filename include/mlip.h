@@ -95,7 +95,11 @@ int mlip_version(void);
  * their cell or a cell with non-finite entries or det = 0 (host message
  * says which); MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges, a
  * shift exceeds +-127 or a cell is so thin that more than 8 images per axis
- * reach the cutoff.  Synchronises the stream once.
+ * reach the cutoff.  Synchronises the stream once: the calling thread polls
+ * the stream (yielding between polls) until all work queued on it, earlier
+ * work included, has finished, so that it can read E; the read goes through
+ * a small pinned host buffer allocated on a thread's first call and kept for
+ * the life of the process.
  * ------------------------------------------------------------------------ */
 size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs);
 int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,
