@@ -16,6 +16,8 @@ namespace mlip {
 
 namespace {
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 constexpr int RANK_BLOCK = 256;
 
 // top-k per element type (ties -> lower expert index) and softmax gates.
@@ -168,29 +170,62 @@ __global__ void dispatch_scatter_kernel(const int32_t *__restrict__ z, int N, in
 }
 
 // out_i = base_i + sum_r gate[z_i, r] * rows[slot(i, r)], r in rank order
-// (base may be null: 0).
+// (base may be null: 0).  Two wavefronts per atom, each on alternate 64-wide
+// float4 column chunks; the atom's k gates and row indices are uniform (scalar
+// loads), and all k + 1 rows of a column chunk are loaded before they are
+// summed.  KT > 0: k fixed at compile time.
+template <int KT>
 __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ base,
                                                       const float *__restrict__ rows,
                                                       const int32_t *__restrict__ z,
                                                       const float *__restrict__ gate,
-                                                      const int32_t *__restrict__ slot, int T, int k,
-                                                      int D, float *__restrict__ out) {
-  const int i = blockIdx.x;
+                                                      const int32_t *__restrict__ slot, int N, int T,
+                                                      int k_rt, int D, float *__restrict__ out) {
+  constexpr int KMAX = KT > 0 ? KT : 1;
+  const int i = blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (i >= N) return;
+  const int lane = threadIdx.x & 127;   // column chunk offset of this wavefront pair
+  const int k = KT > 0 ? KT : k_rt;
   int t = z[i];
   t = t < 0 ? 0 : (t >= T ? T - 1 : t);
   const int D4 = D >> 2;
-  for (int c = threadIdx.x; c < D4; c += blockDim.x) {
-    float4 acc = base ? reinterpret_cast<const float4 *>(base + int64_t(i) * D)[c]
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int r = 0; r < k; ++r) {
-      const float gv = gate[t * k + r];
-      const float4 y = reinterpret_cast<const float4 *>(rows + int64_t(slot[int64_t(i) * k + r]) * D)[c];
-      acc.x += gv * y.x;
-      acc.y += gv * y.y;
-      acc.z += gv * y.z;
-      acc.w += gv * y.w;
+  const float4 *b4 = base ? reinterpret_cast<const float4 *>(base + int64_t(i) * D) : nullptr;
+  float4 *o4 = reinterpret_cast<float4 *>(out + int64_t(i) * D);
+  if (KT > 0) {
+    float gv[KMAX];
+    const floatx4 *y4[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      gv[r] = gate[t * KMAX + r];
+      y4[r] = reinterpret_cast<const floatx4 *>(rows + int64_t(slot[int64_t(i) * KMAX + r]) * D);
     }
-    reinterpret_cast<float4 *>(out + int64_t(i) * D)[c] = acc;
+    for (int c = lane; c < D4; c += 128) {
+      float4 acc = b4 ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      floatx4 y[KMAX];
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) y[r] = __builtin_nontemporal_load(y4[r] + c);
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) {
+        acc.x += gv[r] * y[r][0];
+        acc.y += gv[r] * y[r][1];
+        acc.z += gv[r] * y[r][2];
+        acc.w += gv[r] * y[r][3];
+      }
+      o4[c] = acc;
+    }
+  } else {
+    for (int c = lane; c < D4; c += 128) {
+      float4 acc = b4 ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int r = 0; r < k; ++r) {
+        const float gv = gate[t * k + r];
+        const float4 y = reinterpret_cast<const float4 *>(rows + int64_t(slot[int64_t(i) * k + r]) * D)[c];
+        acc.x += gv * y.x;
+        acc.y += gv * y.y;
+        acc.z += gv * y.z;
+        acc.w += gv * y.w;
+      }
+      o4[c] = acc;
+    }
   }
 }
 
@@ -263,9 +298,17 @@ int moe_combine(const float *base, const float *rows, const int32_t *z, const fl
                 const int32_t *slot, int N, int T, int k, int D, float *out, hipStream_t stream) {
   if (N <= 0) return MLIP_OK;
   ProfScope ps(K_COMBINE, stream);
-  const int threads = D / 4 >= 256 ? 256 : (D / 4 >= 128 ? 128 : 64);
-  combine_kernel<<<dim3(unsigned(N)), dim3(threads), 0, stream>>>(base, rows, z, gate, slot, T, k, D,
-                                                                   out);
+  const dim3 grid(unsigned(cdiv(N, 2))), block(256);
+#define MLIP_COMBINE(KV) combine_kernel<KV><<<grid, block, 0, stream>>>(base, rows, z, gate, slot, N, T, k, D, out)
+  switch (k) {
+    case 1: MLIP_COMBINE(1); break;
+    case 2: MLIP_COMBINE(2); break;
+    case 4: MLIP_COMBINE(4); break;
+    case 8: MLIP_COMBINE(8); break;
+    case 16: MLIP_COMBINE(16); break;
+    default: MLIP_COMBINE(0); break;
+  }
+#undef MLIP_COMBINE
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
