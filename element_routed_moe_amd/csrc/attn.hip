@@ -92,17 +92,28 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// e_c = sum_k b[k] w[k][c] for the lane's channels, b read from LDS as float4
+// e_c = sum_k b[k] w[k][c] for the lane's channels, b read from LDS as float4;
+// one chain of fused multiply-adds per channel in k order
 template <int CPL>
 __device__ inline void basis_map(const float4 *b, const float (&w)[K][CPL], float (&e)[CPL]) {
+  const float4 p0 = b[0];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) e[c] = 0.f;
+  for (int c = 0; c < CPL; ++c) {
+    e[c] = p0.x * w[0][c];
+    e[c] = p0.y * w[1][c] + e[c];
+    e[c] = p0.z * w[2][c] + e[c];
+    e[c] = p0.w * w[3][c] + e[c];
+  }
 #pragma unroll
-  for (int kq = 0; kq < KQ; ++kq) {
+  for (int kq = 1; kq < KQ; ++kq) {
     const float4 p = b[kq];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      e[c] += p.x * w[4 * kq][c] + p.y * w[4 * kq + 1][c] + p.z * w[4 * kq + 2][c] + p.w * w[4 * kq + 3][c];
+    for (int c = 0; c < CPL; ++c) {
+      e[c] = p.x * w[4 * kq][c] + e[c];
+      e[c] = p.y * w[4 * kq + 1][c] + e[c];
+      e[c] = p.z * w[4 * kq + 2][c] + e[c];
+      e[c] = p.w * w[4 * kq + 3][c] + e[c];
+    }
   }
 }
 

@@ -29,13 +29,21 @@ constexpr int UNROLL = 4;
 
 __device__ inline f2v ld2(const float *p) { return *reinterpret_cast<const f2v *>(p); }
 
-// sum_k b[k] w[k] for a 16-aligned LDS row b of K floats (four 16-byte reads)
+// sum_k b[k] w[k] for a 16-aligned LDS row b of K floats (four 16-byte reads),
+// as one chain of fused multiply-adds in k order (K instructions per column)
 __device__ inline f2v basis_dot(const float *b, const f2v (&w)[K]) {
-  f2v v = {0.f, 0.f};
+  const float4 t0 = reinterpret_cast<const float4 *>(b)[0];
+  f2v v = t0.x * w[0];
+  v = t0.y * w[1] + v;
+  v = t0.z * w[2] + v;
+  v = t0.w * w[3] + v;
 #pragma unroll
-  for (int q = 0; q < K / 4; ++q) {
+  for (int q = 1; q < K / 4; ++q) {
     const float4 t = reinterpret_cast<const float4 *>(b)[q];
-    v += t.x * w[4 * q] + t.y * w[4 * q + 1] + t.z * w[4 * q + 2] + t.w * w[4 * q + 3];
+    v = t.x * w[4 * q] + v;
+    v = t.y * w[4 * q + 1] + v;
+    v = t.z * w[4 * q + 2] + v;
+    v = t.w * w[4 * q + 3] + v;
   }
   return v;
 }
