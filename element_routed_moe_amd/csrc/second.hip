@@ -507,10 +507,15 @@ __global__ void __launch_bounds__(64) edge_basis_grad_kernel(
 #pragma unroll
         for (int k4 = 0; k4 < K / 4; ++k4) {
           const float4 al = b4[k4], be = b4[K / 4 + k4];
-          dw[4 * k4] += be.x * xv + al.x * yv;
-          dw[4 * k4 + 1] += be.y * xv + al.y * yv;
-          dw[4 * k4 + 2] += be.z * xv + al.z * yv;
-          dw[4 * k4 + 3] += be.w * xv + al.w * yv;
+          // two fused multiply-adds per term into the running sums
+          dw[4 * k4] = be.x * xv + dw[4 * k4];
+          dw[4 * k4] = al.x * yv + dw[4 * k4];
+          dw[4 * k4 + 1] = be.y * xv + dw[4 * k4 + 1];
+          dw[4 * k4 + 1] = al.y * yv + dw[4 * k4 + 1];
+          dw[4 * k4 + 2] = be.z * xv + dw[4 * k4 + 2];
+          dw[4 * k4 + 2] = al.z * yv + dw[4 * k4 + 2];
+          dw[4 * k4 + 3] = be.w * xv + dw[4 * k4 + 3];
+          dw[4 * k4 + 3] = al.w * yv + dw[4 * k4 + 3];
         }
       }
     }
