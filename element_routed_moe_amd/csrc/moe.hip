@@ -113,40 +113,84 @@ __global__ void __launch_bounds__(RANK_BLOCK) elem_rank_kernel(const int32_t *__
 
 // One workgroup: per-type block offsets (in place), type counts, the
 // (expert, type) offset table and the expert offsets.
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// One workgroup of 256 threads builds the dispatch tables:
+//  1. per type t, the exclusive scan of the per-block type counts over the
+//     atom blocks (in place) and the type total n_type[t]; one wavefront per
+//     type, 64 blocks per pass;
+//  2. per expert x, pre[x][t] = the tokens of types t' < t routed to x, and
+//     exp_count[x]; the routing table and n_type are read from LDS when the
+//     table fits (TKS entries), else from global memory;
+//  3. exp_off = the exclusive scan of exp_count (a block scan).
+constexpr int TKS = 4096;
 __global__ void __launch_bounds__(256) dispatch_tables_kernel(
     int n_blocks, int T, int X, int k, const int32_t *__restrict__ topk,
     int32_t *__restrict__ blk_count, int32_t *__restrict__ n_type, int32_t *__restrict__ pre,
     int32_t *__restrict__ exp_count, int32_t *__restrict__ exp_off) {
-  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+  __shared__ int s_ntype[TKS];
+  __shared__ int s_topk[TKS];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool in_lds = T <= TKS && int64_t(T) * k <= TKS;
+  for (int t = wave; t < T; t += 4) {
     int run = 0;
-    for (int b = 0; b < n_blocks; ++b) {
+    for (int b0 = 0; b0 < n_blocks; b0 += 64) {
+      const int b = b0 + lane;
       const int64_t o = int64_t(b) * T + t;
-      const int c = blk_count[o];
-      blk_count[o] = run;
-      run += c;
+      const int c = b < n_blocks ? blk_count[o] : 0;
+      const int incl = wave_incl_scan(c);
+      if (b < n_blocks) blk_count[o] = run + incl - c;
+      run += __shfl(incl, 63, 64);
     }
-    n_type[t] = run;
+    if (lane == 0) {
+      n_type[t] = run;
+      if (in_lds) s_ntype[t] = run;
+    }
   }
+  if (in_lds)
+    for (int q = tid; q < T * k; q += 256) s_topk[q] = topk[q];
+  __threadfence_block();
   __syncthreads();
-  for (int x = threadIdx.x; x < X; x += blockDim.x) {
+  const int32_t *tk = in_lds ? s_topk : topk;
+  const int32_t *nt = in_lds ? s_ntype : n_type;
+  for (int x = tid; x < X; x += 256) {
     int run = 0;
     for (int t = 0; t < T; ++t) {
       pre[int64_t(x) * T + t] = run;
       bool hit = false;
-      for (int r = 0; r < k; ++r) hit |= topk[t * k + r] == x;
-      if (hit) run += n_type[t];
+      for (int r = 0; r < k; ++r) hit |= tk[t * k + r] == x;
+      if (hit) run += nt[t];
     }
     exp_count[x] = run;
   }
+  __threadfence_block();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int x = 0; x < X; ++x) {
-      exp_off[x] = run;
-      run += exp_count[x];
-    }
-    exp_off[X] = run;
+  // exclusive scan of exp_count over the experts, 256 at a time
+  int base = 0;
+  for (int x0 = 0; x0 < X; x0 += 256) {
+    const int x = x0 + tid;
+    const int c = x < X ? exp_count[x] : 0;
+    const int incl = wave_incl_scan(c);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    if (x < X) exp_off[x] = before + incl - c;
+    const int total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
+    base += total;
   }
+  if (tid == 0) exp_off[X] = base;
 }
 
 __global__ void dispatch_scatter_kernel(const int32_t *__restrict__ z, int N, int T, int k,
