@@ -41,7 +41,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int THREADS = 256;
 constexpr int N_XCD = 8;
-constexpr int RASTER_M = 8;
+constexpr int RASTER_M = 8;          // dense GEMMs
+constexpr int EXPERT_RASTER_M = 2;   // grouped expert GEMMs
 constexpr int EXPERT_BK = 16;   // k per pipeline step of the expert GEMMs
 constexpr int EXPERT_S = 3;     // LDS stages: 3 x 16 KB, three workgroups per CU
 constexpr int DENSE_BK = 32;
@@ -413,9 +414,10 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
     part = t_local / (Mt * Nt);
     t_local -= part * (Mt * Nt);
   }
-  const int group_size = RASTER_M * Nt;
-  const int first_m = (t_local / group_size) * RASTER_M;
-  const int gm = min(Mt - first_m, RASTER_M);
+  constexpr int RM = SPLIT ? EXPERT_RASTER_M : RASTER_M;
+  const int group_size = RM * Nt;
+  const int first_m = (t_local / group_size) * RM;
+  const int gm = min(Mt - first_m, RM);
   const int rr = t_local % group_size;
   const int mt_glob = first_m + rr % gm;
   const int nt = rr / gm;
