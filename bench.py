@@ -246,7 +246,9 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
             "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
-            "traffic": _traffic(dom) if dom in EXPERT_CLASSES else None,
+            # the counters were taken on the core step of the S workload only
+            "traffic": (_traffic(dom) if dom in EXPERT_CLASSES and args.config == "S" and args.block == "core"
+                        else None),
             "avg_launch_ms": round(avg_ms, 4), "flop_per_launch": flops[dom]}
     if dom == "gemm_wgrad":
         roof["flop_per_launch_note"] = "mean over the step's weight-gradient launches"
