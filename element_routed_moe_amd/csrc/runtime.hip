@@ -29,13 +29,14 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 static bool g_prof = false;
+static uint64_t g_prof_mask = ~uint64_t(0);   // classes timed while profiling is on
 static std::vector<std::pair<hipEvent_t, hipEvent_t>> g_pool;
 static std::vector<ProfRec> g_recs;
 static double g_ms[K_NUM_CLASSES];
 static int64_t g_cnt[K_NUM_CLASSES];
 
 ProfScope::ProfScope(KClass kk, hipStream_t ss) : k(kk), s(ss) {
-  if (!g_prof) return;
+  if (!g_prof || !((g_prof_mask >> int(kk)) & 1)) return;
   std::pair<hipEvent_t, hipEvent_t> ev;
   if (g_pool.empty()) {
     if (hipEventCreate(&ev.first) != hipSuccess) return;
@@ -81,6 +82,11 @@ int mlip_version(void) { return 1; }
 
 int mlip_profile_enable(int enable) {
   g_prof = enable != 0;
+  return MLIP_OK;
+}
+
+int mlip_profile_select(uint64_t class_mask) {
+  g_prof_mask = class_mask;
   return MLIP_OK;
 }
 

@@ -105,6 +105,7 @@ _SIGS = {
     "mlip_tri_tangent_vjp": (C.c_int, [_p, _p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                        _p, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "mlip_profile_enable": (C.c_int, [C.c_int]),
+    "mlip_profile_select": (C.c_int, [C.c_uint64]),
     "mlip_profile_reset": (C.c_int, []),
     "mlip_profile_count": (C.c_int, []),
     "mlip_profile_get": (C.c_int, [C.c_int, C.POINTER(C.c_char_p), C.POINTER(C.c_int64),
@@ -660,6 +661,22 @@ def mlip_tri_tangent_vjp(graph, tri, tjvp, h, sbar, W_s, W_ang, W_T, cutoff: flo
 # ------------------------------------------------------------------ timing
 def profile_enable(on: bool = True):
     _check(_lib.mlip_profile_enable(1 if on else 0))
+
+
+def profile_select(names=None):
+    """Time only the kernel classes named (None: every class)."""
+    if names is None:
+        mask = (1 << 64) - 1
+    else:
+        idx = {}
+        for i in range(_lib.mlip_profile_count()):
+            nm = C.c_char_p()
+            _check(_lib.mlip_profile_get(i, C.byref(nm), None, None))
+            idx[nm.value.decode()] = i
+        mask = 0
+        for n in names:
+            mask |= 1 << idx[n]
+    _check(_lib.mlip_profile_select(C.c_uint64(mask)))
 
 
 def profile_reset():

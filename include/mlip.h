@@ -558,8 +558,13 @@ int mlip_embed_grad(const int32_t *z, const float *grad_h, int32_t n_atoms, int3
  * (static string), the number of launches and their summed duration in
  * milliseconds.  Classes are numbered 0 .. mlip_profile_count()-1.  Not
  * thread-safe; meant for benchmarks.
+ * mlip_profile_select(class_mask) restricts the timing to the classes whose
+ * bit (1 << idx) is set in class_mask (all classes until it is called): each
+ * timed launch costs two event records on its stream, so a benchmark can time
+ * only the kernels it needs.  Launches of other classes are not counted.
  * ------------------------------------------------------------------------ */
 int mlip_profile_enable(int enable);
+int mlip_profile_select(uint64_t class_mask);
 int mlip_profile_reset(void);
 int mlip_profile_count(void);
 int mlip_profile_get(int idx, const char **name, int64_t *launches, double *total_ms);
