@@ -72,7 +72,8 @@ def tri_row(U: np.ndarray, f: np.ndarray, S: np.ndarray, W_ang: np.ndarray) -> n
     G = np.einsum("lab,lc->abc", legendre(X, L), W_ang)   # [deg, deg, Dt]
     F = np.outer(f, f)
     np.fill_diagonal(F, 0.0)                              # distinct edges only
-    return np.einsum("ab,abc,ac,bc->c", F, G, S, S)
+    # sum_ab F_ab G_abc S_ac S_bc, the pair weights folded into G first
+    return np.einsum("abc,ac,bc->c", F[:, :, None] * G, S, S)
 
 
 def tri_row_vjp(U: np.ndarray, r: np.ndarray, f: np.ndarray, df: np.ndarray, S: np.ndarray,
@@ -96,9 +97,12 @@ def tri_row_vjp(U: np.ndarray, r: np.ndarray, f: np.ndarray, df: np.ndarray, S: 
     Gd = np.einsum("lab,lc->abc", legendre_dx(X, L), W_ang)
     off = 1.0 - np.eye(deg)
     F = np.outer(f, f) * off
-    sbar = 2.0 * np.einsum("ab,abc,c,bc->ac", F, G, tb, S)
-    fbar = 2.0 * np.einsum("b,ab,abc,c,ac,bc->a", f, off, G, tb, S, S)
-    xbar = F * np.einsum("abc,c,ac,bc->ab", Gd, tb, S, S)
+    St = S * tb                                            # tb_c S_b,c
+    sbar = 2.0 * np.einsum("abc,bc->ac", F[:, :, None] * G, St)
+    # T_ab = sum_c tb_c G_ab,c S_a,c S_b,c
+    T = np.einsum("abc,ac,bc->ab", G, St, S)
+    fbar = 2.0 * ((off * T) @ f)
+    xbar = F * np.einsum("abc,ac,bc->ab", Gd, St, S)
     ubar = 2.0 * xbar @ U
     with np.errstate(invalid="ignore", divide="ignore"):
         inv_r = np.where(r > 0, 1.0 / r, 0.0)
