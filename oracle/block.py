@@ -27,11 +27,28 @@ What the pages fix, and the readings taken where they are silent:
 """
 from __future__ import annotations
 
+import contextlib
 from typing import Dict, Optional
 
 import numpy as np
 
+# Working precision of every array this module creates.  float64 is the
+# reference; ``working_precision(np.float32)`` re-runs the same steps in
+# float32, which is how the tests check that the float32 arithmetic the pages
+# prescribe can meet the comparison tolerance at all.
 f64 = np.float64
+
+
+@contextlib.contextmanager
+def working_precision(dtype):
+    """Evaluate this module's functions with arrays of ``dtype`` inside the block."""
+    global f64
+    saved = f64
+    f64 = dtype
+    try:
+        yield
+    finally:
+        f64 = saved
 
 
 # ----------------------------------------------------------------- basis ----
@@ -168,6 +185,19 @@ def moe_forward(u: np.ndarray, z: np.ndarray, topk: np.ndarray, gate: np.ndarray
         y = silu(p) @ np.asarray(W2[x], f64)
         out[atoms] += gate[z[atoms], ranks][:, None] * y
     return out
+
+
+def moe_preactivations(u: np.ndarray, z: np.ndarray, topk: np.ndarray, W1: np.ndarray) -> np.ndarray:
+    """First-layer outputs of the chosen experts before SiLU, [N, k, H]:
+    p[i, r] = u_i @ W1_x with x = topk[z_i, r] (the hidden state of token (i, r))."""
+    z = np.asarray(z, np.int64)
+    N, k = z.size, topk.shape[1]
+    p = np.zeros((N, k, W1.shape[2]), f64)
+    for x in range(W1.shape[0]):
+        atoms, ranks = _expert_members(z, topk, x)
+        if atoms.size:
+            p[atoms, ranks] = np.asarray(u, f64)[atoms] @ np.asarray(W1[x], f64)
+    return p
 
 
 def moe_vjp(u: np.ndarray, g: np.ndarray, z: np.ndarray, topk: np.ndarray,

@@ -206,6 +206,26 @@ def test_moe_scalar_closed_form():
         assert abs(out[n, 0] - ref) < 1e-14
 
 
+def test_moe_preactivations_closed_forms():
+    """p[i, r] of the chosen experts: shared weights give u @ W1 for every rank
+    (numpy matmul); the scalar two-expert case gives u * a_x in rank order."""
+    rng = np.random.default_rng(5)
+    N, D, H, X, T, k = 40, 9, 14, 6, 4, 3
+    u = rng.standard_normal((N, D))
+    z = rng.integers(0, T, N)
+    W1 = np.repeat(rng.standard_normal((1, D, H)), X, axis=0)
+    topk, _ = B.route(rng.standard_normal((T, X)), k)
+    p = B.moe_preactivations(u, z, topk, W1)
+    assert p.shape == (N, k, H)
+    for r in range(k):
+        assert np.allclose(p[:, r], u @ W1[0], atol=1e-12)
+    us = np.array([[0.7], [-1.3]])
+    a = np.array([[[2.0]], [[-0.5]]])
+    topk, _ = B.route(np.array([[0.2, 1.0]]), 2)          # expert 1 first
+    ps = B.moe_preactivations(us, np.zeros(2, np.int64), topk, a)
+    assert np.array_equal(ps[:, :, 0], np.stack([us[:, 0] * -0.5, us[:, 0] * 2.0], axis=1))
+
+
 # ----------------------------------------------------------- gradient ----
 def _loss_fd(inp, g_up, pos=None, h=None):
     q = dict(inp)
@@ -343,3 +363,53 @@ def test_strain_gradient_dimer():
     gs = v["grad_strain"][0]
     assert abs(gs[0, 0] - gold["dEdr"] * 2.0) < 1e-12
     assert np.all(np.abs(gs.ravel()[1:]) < 1e-15)
+
+
+# ------------------------------------------- float32 against float64 ----
+def _graph32(g):
+    q = dict(g)
+    q["r"] = g["r"].astype(np.float32)
+    q["d"] = g["d"].astype(np.float32)
+    return q
+
+
+def _relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "S_slice"])
+def test_float32_meets_the_tolerance(name):
+    """The same block evaluated in float32 stays within the 2e-4 comparison bound
+    of the float64 reference (the bound is reachable by float32 arithmetic), and
+    the bound still catches plausible mistakes: dropping one expert rank, or the
+    envelope's derivative, moves the result far beyond it."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    g = G.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    gup = synth.upstream_grad(cfg, inp, "random")
+    f = B.block_forward(inp, g)
+    v = B.block_vjp(inp, g, f, gup.astype(np.float64))
+    with B.working_precision(np.float32):
+        g32 = _graph32(g)
+        f32 = B.block_forward(inp, g32)
+        v32 = B.block_vjp(inp, g32, f32, gup.astype(np.float32))
+    assert f32["h2"].dtype == np.float32 and v32["grad_h"].dtype == np.float32
+    errs = {k: _relerr(f32[k], f[k]) for k in ("s", "u", "h2", "eps")}
+    errs.update({k: _relerr(v32[k], v[k]) for k in ("grad_h", "grad_pos", "atom_virial")})
+    assert max(errs.values()) <= 2e-4, errs
+    assert max(errs.values()) >= 1e-9, errs           # it really ran in float32
+    # a dropped rank (the last expert of every atom) is far outside the bound
+    topk, gate = f["topk"], f["gate"].copy()
+    gate[:, -1] = 0.0
+    h2_wrong = B.moe_forward(f["u"], inp["z"], topk, gate, inp["W1"], inp["W2"])
+    assert _relerr(h2_wrong, f["h2"]) > 100 * 2e-4
+    # forces without the envelope's derivative term are far outside it too
+    rc = B._cutoff(inp)
+    ebar = v["abar"][g["recv"]] * f["s"][g["src"]]
+    K = inp["W_e"].shape[0]
+    de_wrong = B.envelope(g["r"], rc)[:, None] * (B.rbf_dr(g["r"], K, rc) @ inp["W_e"].astype(np.float64))
+    c_wrong = np.sum(ebar * de_wrong, axis=1)
+    gpos_wrong = B.edge_forces(c_wrong, g, cfg.n_atoms, inp["struct_ptr"])[0]
+    assert _relerr(gpos_wrong, v["grad_pos"]) > 10 * 2e-4
