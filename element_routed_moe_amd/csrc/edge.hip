@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(64) embed_aggregate_kernel(
         const float x = r - float(k) * R.mu_step;
         phi[lane][k] = fc * __expf(-R.gamma * x * x);
       }
-      jj[lane] = src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
     for (int m = 0; m < n; m += UNROLL) {
@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(64 * NW) edge_vjp_kernel(
           vq[ed][3] = g.y * g.z * inv;
           vq[ed][4] = g.x * g.z * inv;
           vq[ed][5] = g.x * g.y * inv;
-          jj[ed] = src[e0 + ed];
+          jj[ed] = int(MLIP_IDX(src[e0 + ed], n_atoms, "sender"));
         }
         }
       }
@@ -280,10 +280,13 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
 // fixed reduction tree).
 __global__ void __launch_bounds__(256) strain_sum_kernel(const float *__restrict__ atom_virial,
                                                          const int32_t *__restrict__ struct_ptr,
-                                                         double *__restrict__ grad_strain) {
+                                                         int n_atoms, double *__restrict__ grad_strain) {
   __shared__ double part[6][256];
   const int b = blockIdx.x;
-  const int lo = struct_ptr[b], hi = struct_ptr[b + 1];
+  // the atom range is clamped into [0, n_atoms): a malformed struct_ptr
+  // cannot make the sum read past the per-atom array
+  const int lo = min(max(struct_ptr[b], 0), n_atoms);
+  const int hi = min(max(struct_ptr[b + 1], lo), n_atoms);
   double acc[6] = {0, 0, 0, 0, 0, 0};
   for (int i = lo + threadIdx.x; i < hi; i += 256)
     for (int q = 0; q < 6; ++q) acc[q] += double(atom_virial[int64_t(i) * 6 + q]);
@@ -297,10 +300,10 @@ __global__ void __launch_bounds__(256) strain_sum_kernel(const float *__restrict
   if (threadIdx.x < 6) grad_strain[b * 6 + threadIdx.x] = part[threadIdx.x][0];
 }
 
-int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs,
+int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs, int n_atoms,
                       double *grad_strain, hipStream_t stream) {
   strain_sum_kernel<<<dim3(unsigned(n_structs)), dim3(256), 0, stream>>>(atom_virial, struct_ptr,
-                                                                        grad_strain);
+                                                                        n_atoms, grad_strain);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }

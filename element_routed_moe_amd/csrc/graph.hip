@@ -34,7 +34,15 @@ enum GraphFlags {
   GF_POS_OUTSIDE = 4,
   GF_TOO_MANY_IMAGES = 8,
   GF_REV_MISSING = 16,
+  GF_BAD_STRUCTS = 32,   // struct_ptr not 0 = p_0 <= p_1 <= ... <= p_B = n_atoms
+  GF_BAD_SRC = 64,       // a caller-supplied sender index outside [0, n_atoms)
 };
+
+// Every pass after the setup skips its work when the structure table was
+// rejected, so a malformed struct_ptr never turns into an index.
+__device__ inline bool structs_rejected(const int32_t *flags) {
+  return (__atomic_load_n(flags, __ATOMIC_RELAXED) & GF_BAD_STRUCTS) != 0;
+}
 
 // accepted rounding of a general cell's fractional coordinates outside [0, 1)
 constexpr double kFracTol = 1e-6;
@@ -67,7 +75,7 @@ __global__ void graph_zero(int32_t *__restrict__ flags, int32_t *__restrict__ ma
 }
 
 __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__restrict__ struct_ptr,
-                            int n_structs, float cutoff, StructParams *__restrict__ prm,
+                            int n_structs, int n_atoms, float cutoff, StructParams *__restrict__ prm,
                             int32_t *__restrict__ flags) {
   int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= n_structs) return;
@@ -75,6 +83,13 @@ __global__ void graph_setup(const float *__restrict__ cell, const int32_t *__res
   for (int q = 0; q < 9; ++q) P.C[q] = double(cell[b * 9 + q]);
   P.lo = struct_ptr[b];
   P.hi = struct_ptr[b + 1];
+  // the table must run 0 = p_0 <= p_1 <= ... <= p_B = n_atoms; each thread
+  // checks its own pair, the first and the last thread the two ends
+  if (!(P.lo >= 0 && P.lo <= P.hi && P.hi <= n_atoms) || (b == 0 && P.lo != 0) ||
+      (b == n_structs - 1 && P.hi != n_atoms)) {
+    P.lo = P.hi = 0;
+    atomicOr(flags, GF_BAD_STRUCTS);
+  }
   P.bin_base = P.lo + b;
   int f = 0;
   const double rc = double(cutoff);
@@ -175,7 +190,7 @@ __global__ void graph_bin(const float *__restrict__ pos, const int32_t *__restri
                           int32_t *__restrict__ atom_struct, int32_t *__restrict__ atom_bin,
                           int32_t *__restrict__ bin_count, int32_t *__restrict__ flags) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_atoms) return;
+  if (i >= n_atoms || structs_rejected(flags)) return;
   int b = find_struct(struct_ptr, n_structs, i);
   const StructParams &P = prm[b];
   int c[3];
@@ -204,9 +219,9 @@ __global__ void graph_bin(const float *__restrict__ pos, const int32_t *__restri
 __global__ void graph_scatter(const float *__restrict__ pos, int n_atoms,
                               const int32_t *__restrict__ atom_bin,
                               const int32_t *__restrict__ bin_start, int32_t *__restrict__ bin_fill,
-                              float4 *__restrict__ binned) {
+                              float4 *__restrict__ binned, const int32_t *__restrict__ flags) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_atoms) return;
+  if (i >= n_atoms || structs_rejected(flags)) return;
   int gb = atom_bin[i];
   int p = atomicAdd(&bin_fill[gb], 1);
   binned[bin_start[gb] + p] =
@@ -352,10 +367,16 @@ __global__ void __launch_bounds__(64) graph_count(const float *__restrict__ pos,
                                                   const int32_t *__restrict__ bin_start,
                                                   const float4 *__restrict__ binned, double rc2,
                                                   double rc, int32_t *__restrict__ deg,
-                                                  int32_t *__restrict__ maxdeg) {
+                                                  int32_t *__restrict__ maxdeg,
+                                                  const int32_t *__restrict__ flags) {
   const int64_t blk = xcd_block(n_atoms);
   if (blk < 0) return;
   const int i = int(blk);
+  if (structs_rejected(flags)) {
+    // no atom has a structure: every row is empty
+    if (threadIdx.x == 0) deg[i] = 0;
+    return;
+  }
   const StructParams &P = prm[atom_struct[i]];
   int count = 0;
   if (P.valid) {
@@ -379,6 +400,16 @@ __global__ void graph_summary(const int32_t *__restrict__ row_ptr, int n_atoms,
   out[2] = *maxdeg;
 }
 
+// The fill and reverse passes run before the single host read of the
+// build: they proceed only when all E edges fit the caller's capacity, no row
+// exceeds the LDS row buffer and the structure table was accepted, so that
+// every edge slot [0, E) is written with an index in [0, n_atoms).
+__device__ inline bool fill_allowed(const int32_t *row_ptr, int n_atoms, int64_t capacity,
+                                    const int32_t *maxdeg, const int32_t *flags) {
+  return int64_t(row_ptr[n_atoms]) <= capacity && *maxdeg <= kMaxDeg &&
+         (__atomic_load_n(flags, __ATOMIC_RELAXED) & GF_BAD_STRUCTS) == 0;
+}
+
 __device__ inline uint64_t edge_key(int j, int s0, int s1, int s2) {
   return (uint64_t(uint32_t(j)) << 24) | (uint64_t(s0 + 128) << 16) | (uint64_t(s1 + 128) << 8) |
          uint64_t(s2 + 128);
@@ -393,6 +424,8 @@ __global__ void __launch_bounds__(64) graph_fill(const float *__restrict__ pos, 
                                                  const int32_t *__restrict__ bin_start,
                                                  const float4 *__restrict__ binned, double rc2,
                                                  double rc, const int32_t *__restrict__ row_ptr,
+                                                 int64_t capacity, const int32_t *__restrict__ maxdeg,
+                                                 const int32_t *__restrict__ flags,
                                                  int32_t *__restrict__ src, char4 *__restrict__ shift,
                                                  float4 *__restrict__ geom) {
   __shared__ uint64_t keys[kMaxDeg];
@@ -400,6 +433,9 @@ __global__ void __launch_bounds__(64) graph_fill(const float *__restrict__ pos, 
   const int64_t blk = xcd_block(n_atoms);
   if (blk < 0) return;
   int i = int(blk);
+  // runs before the host has seen the edge count: writes nothing unless all
+  // E edges fit the caller's buffers and every row fits the LDS row buffer
+  if (!fill_allowed(row_ptr, n_atoms, capacity, maxdeg, flags)) return;
   const int lane = threadIdx.x;
   const StructParams &P = prm[atom_struct[i]];
   if (!P.valid) return;
@@ -433,34 +469,58 @@ __global__ void __launch_bounds__(64) graph_fill(const float *__restrict__ pos, 
   }
 }
 
-// One wave per receiver: reverse-edge index by binary search in the sender's row.
-__global__ void __launch_bounds__(256) graph_rev(int n_atoms, const int32_t *__restrict__ row_ptr,
+// One wave per receiver: reverse-edge index by binary search in the sender's
+// row.  An edge whose reverse is absent (impossible for a graph of this
+// library: the predicate is symmetric, d_rev = -d exactly) raises
+// GF_REV_MISSING, which the calling entry point returns as an error; its
+// rev entry is then the edge itself, so no later pass indexes out of range.
+// In the build (gate >= 0) the pass runs only when fill_allowed; for a
+// caller's own CSR (gate < 0, mlip_graph_reverse) every row range and
+// sender index is checked against [0, n_edges] and [0, n_atoms) first.
+__global__ void __launch_bounds__(256) graph_rev(int n_atoms, int64_t n_edges,
+                                                 const int32_t *__restrict__ row_ptr,
                                                  const int32_t *__restrict__ src,
                                                  const char4 *__restrict__ shift,
                                                  int32_t *__restrict__ rev,
-                                                 int32_t *__restrict__ flags) {
+                                                 int32_t *__restrict__ flags, int64_t gate,
+                                                 const int32_t *__restrict__ maxdeg) {
   int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= n_atoms) return;
+  if (gate >= 0 && !fill_allowed(row_ptr, n_atoms, gate, maxdeg, flags)) return;
   const int lane = threadIdx.x & 63;
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
+  if (!(r0 >= 0 && r0 <= r1 && int64_t(r1) <= n_edges)) {
+    if (lane == 0) atomicOr(flags, GF_BAD_SRC);
+    return;
+  }
   for (int e = r0 + lane; e < r1; e += 64) {
-    int j = src[e];
-    char4 s = shift[e];
-    uint64_t want = edge_key(i, -int(s.x), -int(s.y), -int(s.z));
-    int lo = row_ptr[j], hi = row_ptr[j + 1];
-    while (lo < hi) {
-      int mid = (lo + hi) >> 1;
-      char4 t = shift[mid];
-      uint64_t km = edge_key(src[mid], t.x, t.y, t.z);
-      if (km < want) lo = mid + 1;
-      else hi = mid;
-    }
+    const int j = src[e];
     bool found = false;
-    if (lo < row_ptr[j + 1]) {
-      char4 t = shift[lo];
-      found = edge_key(src[lo], t.x, t.y, t.z) == want;
+    int lo = 0;
+    if (j < 0 || j >= n_atoms) {
+      atomicOr(flags, GF_BAD_SRC);
+    } else {
+      const int j0 = row_ptr[j], j1 = row_ptr[j + 1];
+      if (!(j0 >= 0 && j0 <= j1 && int64_t(j1) <= n_edges)) {
+        atomicOr(flags, GF_BAD_SRC);
+      } else {
+        const char4 s = shift[e];
+        const uint64_t want = edge_key(i, -int(s.x), -int(s.y), -int(s.z));
+        lo = j0;
+        int hi = j1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const char4 t = shift[mid];
+          if (edge_key(src[mid], t.x, t.y, t.z) < want) lo = mid + 1;
+          else hi = mid;
+        }
+        if (lo < j1) {
+          const char4 t = shift[lo];
+          found = edge_key(src[lo], t.x, t.y, t.z) == want;
+        }
+        if (!found) atomicOr(flags, GF_REV_MISSING);
+      }
     }
-    if (!found) atomicOr(flags, GF_REV_MISSING);
     rev[e] = found ? lo : e;
   }
 }
@@ -498,6 +558,36 @@ inline unsigned nblk(int64_t n, int per) { return unsigned(cdiv(n < 1 ? 1 : n, p
 
 using namespace mlip;
 
+namespace mlip {
+namespace {
+
+// The one host read of a build (or of mlip_graph_reverse): waits for the
+// stream, then copies the 4-word summary through a small pinned buffer kept
+// per host thread for the life of the process (a pageable target takes the
+// staged copy path).  The thread polls rather than sleeps, so the caller's
+// next launches go out as soon as the stream drains.
+int read_summary(const int32_t *dev, int32_t host[4], hipStream_t stream) {
+  static thread_local int32_t *pinned = nullptr;
+  if (!pinned)
+    MLIP_HIP(hipHostMalloc(reinterpret_cast<void **>(&pinned), 4 * sizeof(int32_t), hipHostMallocPortable));
+  MLIP_HIP(hipMemcpyAsync(pinned, dev, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  hipError_t q;
+  while ((q = hipStreamQuery(stream)) == hipErrorNotReady) std::this_thread::yield();
+  MLIP_HIP(q);
+  for (int t = 0; t < 4; ++t) host[t] = pinned[t];
+  return MLIP_OK;
+}
+
+__global__ void graph_flags_zero(int32_t *__restrict__ flags, int32_t *__restrict__ maxdeg) {
+  if (threadIdx.x < 4) {
+    flags[threadIdx.x] = 0;
+    maxdeg[threadIdx.x] = 0;
+  }
+}
+
+}  // namespace
+}  // namespace mlip
+
 extern "C" {
 
 size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs) {
@@ -530,11 +620,15 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
   const double rc2 = double(cutoff) * double(cutoff);
   int32_t host[4] = {0, 0, 0, 0};
   {
+    // Every pass is queued before the single host read: the fill and reverse
+    // passes check on the device that the edges fit (fill_allowed), so one
+    // wait reports the edge count, every input error and a missing reverse edge.
     ProfScope ps(K_GRAPH, stream);
     graph_zero<<<nblk(nbins, 256), 256, 0, stream>>>(w.flags, w.maxdeg, w.bin_count, w.bin_fill,
                                                       nbins);
     MLIP_LAUNCHED();
-    graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, cutoff, w.prm, w.flags);
+    graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, n_atoms, cutoff, w.prm,
+                                                 w.flags);
     MLIP_LAUNCHED();
     if (N > 0) {
       graph_bin<<<nblk(N, 256), 256, 0, stream>>>(pos, struct_ptr, n_structs, n_atoms, w.prm,
@@ -543,33 +637,38 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
       int rc = exclusive_scan(w.bin_count, w.bin_start, nbins, true, w.scan_tmp, stream);
       if (rc) return rc;
       graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start,
-                                                       w.bin_fill, w.binned);
+                                                       w.bin_fill, w.binned, w.flags);
       MLIP_LAUNCHED();
       graph_count<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
                                                    w.bin_start, w.binned, rc2, double(cutoff), row_ptr,
-                                                   w.maxdeg);
+                                                   w.maxdeg, w.flags);
       MLIP_LAUNCHED();
     }
     int rc = exclusive_scan(row_ptr, row_ptr, N, true, w.scan_tmp, stream);
     if (rc) return rc;
+    if (N > 0 && edge_capacity > 0) {
+      graph_fill<<<unsigned(padded_grid(N)), 64, 0, stream>>>(
+          pos, n_atoms, w.prm, w.atom_struct, w.atom_bin, w.bin_start, w.binned, rc2, double(cutoff),
+          row_ptr, edge_capacity, w.maxdeg, w.flags, src, reinterpret_cast<char4 *>(shift),
+          reinterpret_cast<float4 *>(geom));
+      MLIP_LAUNCHED();
+      graph_rev<<<nblk(N, 4), 256, 0, stream>>>(n_atoms, edge_capacity, row_ptr, src,
+                                                reinterpret_cast<const char4 *>(shift), rev, w.flags,
+                                                edge_capacity, w.maxdeg);
+      MLIP_LAUNCHED();
+    }
     graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
     MLIP_LAUNCHED();
-    // the one host sync of the build: E, the error flags and the largest
-    // degree, read into a pinned buffer kept per host thread for the life of
-    // the process (a pageable target takes the staged copy path), then
-    // polled rather than slept on, so the launches that follow go out as soon
-    // as the stream drains (the calling thread yields between polls)
-    static thread_local int32_t *pinned = nullptr;
-    if (!pinned) MLIP_HIP(hipHostMalloc(reinterpret_cast<void **>(&pinned), sizeof(host), hipHostMallocPortable));
-    MLIP_HIP(hipMemcpyAsync(pinned, w.readback, sizeof(host), hipMemcpyDeviceToHost, stream));
-    hipError_t q;
-    while ((q = hipStreamQuery(stream)) == hipErrorNotReady) std::this_thread::yield();
-    MLIP_HIP(q);
-    for (int t = 0; t < 4; ++t) host[t] = pinned[t];
+    if (int rc2 = read_summary(w.readback, host, stream)) return rc2;
   }
   const int64_t E = host[0];
   const int flags = host[1];
   *n_edges = E;
+  if (flags & GF_BAD_STRUCTS) {
+    *n_edges = 0;
+    set_error("struct_ptr rejected: it must run 0 = p_0 <= p_1 <= ... <= p_B = n_atoms");
+    return MLIP_ERR_INPUT;
+  }
   if (flags & GF_BAD_CELL) {
     set_error("cell rejected: non-finite entries or zero volume (rows must be a lattice basis; "
               "a diagonal cell needs positive edges)");
@@ -592,16 +691,50 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
     set_error("edge_capacity %lld < required %lld", (long long)edge_capacity, (long long)E);
     return MLIP_ERR_CAPACITY;
   }
-  if (N > 0 && E > 0) {
+  if (flags & (GF_REV_MISSING | GF_BAD_SRC)) {
+    set_error("internal error: an edge of the built graph has no reverse edge");
+    return MLIP_ERR_INPUT;
+  }
+  return MLIP_OK;
+}
+
+int mlip_graph_reverse(const int32_t *row_ptr, const int32_t *src, const int8_t *shift,
+                       int32_t n_atoms, int64_t n_edges, int32_t *rev, void *ws, size_t ws_bytes,
+                       void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(row_ptr, "row_ptr is null");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && shift && rev), "edge arrays are null");
+  size_t need = mlip_graph_workspace_size(0, 1);
+  MLIP_CHECK_ARG(ws && ws_bytes >= need, "workspace too small: need %zu bytes, got %zu", need,
+                 ws_bytes);
+  MLIP_CHECK_ARG((reinterpret_cast<uintptr_t>(ws) & 255) == 0, "workspace must be 256-byte aligned");
+  MLIP_CHECK_ARG((reinterpret_cast<uintptr_t>(shift) & 3) == 0, "shift must be 4-byte aligned");
+  GraphWs w = carve_graph(ws, 0, 1, nullptr);
+  int32_t host[4] = {0, 0, 0, 0};
+  {
     ProfScope ps(K_GRAPH, stream);
-    graph_fill<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
-                                               w.bin_start, w.binned, rc2, double(cutoff), row_ptr, src,
-                                               reinterpret_cast<char4 *>(shift),
-                                               reinterpret_cast<float4 *>(geom));
+    graph_flags_zero<<<1, 64, 0, stream>>>(w.flags, w.maxdeg);
     MLIP_LAUNCHED();
-    graph_rev<<<nblk(N, 4), 256, 0, stream>>>(n_atoms, row_ptr, src,
-                                              reinterpret_cast<const char4 *>(shift), rev, w.flags);
+    if (n_atoms > 0 && n_edges > 0) {
+      graph_rev<<<nblk(n_atoms, 4), 256, 0, stream>>>(n_atoms, n_edges, row_ptr, src,
+                                                      reinterpret_cast<const char4 *>(shift), rev,
+                                                      w.flags, -1, w.maxdeg);
+      MLIP_LAUNCHED();
+    }
+    graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
     MLIP_LAUNCHED();
+    if (int rc = read_summary(w.readback, host, stream)) return rc;
+  }
+  if (host[1] & GF_BAD_SRC) {
+    set_error("row_ptr or src out of range: rows must satisfy 0 <= row_ptr[i] <= row_ptr[i+1] <= "
+              "n_edges and senders lie in [0, n_atoms)");
+    return MLIP_ERR_INPUT;
+  }
+  if (host[1] & GF_REV_MISSING) {
+    set_error("the graph is not symmetric: some edge (i <- j, S) has no edge (j <- i, -S)");
+    return MLIP_ERR_INPUT;
   }
   return MLIP_OK;
 }

@@ -241,7 +241,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       gv[r] = gate[t * KMAX + r];
-      y4[r] = reinterpret_cast<const floatx4 *>(rows + int64_t(slot[int64_t(i) * KMAX + r]) * D);
+      y4[r] = reinterpret_cast<const floatx4 *>(
+          rows + MLIP_IDX(slot[int64_t(i) * KMAX + r], int64_t(N) * KMAX, "dispatch slot") * D);
     }
     for (int c = lane; c < D4; c += 128) {
       float4 acc = b4 ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -262,7 +263,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
       float4 acc = b4 ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       for (int r = 0; r < k; ++r) {
         const float gv = gate[t * k + r];
-        const float4 y = reinterpret_cast<const float4 *>(rows + int64_t(slot[int64_t(i) * k + r]) * D)[c];
+        const float4 y = reinterpret_cast<const float4 *>(
+            rows + MLIP_IDX(slot[int64_t(i) * k + r], int64_t(N) * k, "dispatch slot") * D)[c];
         acc.x += gv * y.x;
         acc.y += gv * y.y;
         acc.z += gv * y.z;
@@ -295,10 +297,12 @@ __global__ void __launch_bounds__(256) readout_eps_kernel(const float *__restric
 // E_b = sum of eps over structure b, in float64 with a fixed reduction tree.
 __global__ void __launch_bounds__(256) readout_energy_kernel(const float *__restrict__ eps,
                                                              const int32_t *__restrict__ struct_ptr,
-                                                             double *__restrict__ energy) {
+                                                             int n_atoms, double *__restrict__ energy) {
   __shared__ double part[256];
   const int b = blockIdx.x;
-  const int lo = struct_ptr[b], hi = struct_ptr[b + 1];
+  // clamped into [0, n_atoms): a malformed struct_ptr cannot read past eps
+  const int lo = min(max(struct_ptr[b], 0), n_atoms);
+  const int hi = min(max(struct_ptr[b + 1], lo), n_atoms);
   double acc = 0.0;
   for (int i = lo + threadIdx.x; i < hi; i += 256) acc += double(eps[i]);
   part[threadIdx.x] = acc;
@@ -414,7 +418,7 @@ int readout(const float *h, const float *w_r, const int32_t *struct_ptr, int N, 
     readout_eps_kernel<<<dim3(unsigned(cdiv(N, 4))), dim3(256), 0, stream>>>(h, w_r, N, D, eps);
     MLIP_LAUNCHED();
   }
-  readout_energy_kernel<<<dim3(unsigned(B)), dim3(256), 0, stream>>>(eps, struct_ptr, energy);
+  readout_energy_kernel<<<dim3(unsigned(B)), dim3(256), 0, stream>>>(eps, struct_ptr, N, energy);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }

@@ -229,3 +229,113 @@ def test_input_errors(mlip):
     q["z"][5] = 17
     blk = mlip.Block(q, device="cuda").step()
     assert mlip.mlip_moe_status(blk.ws_moe)
+
+
+def test_struct_ptr_errors(mlip):
+    """A malformed structure table is rejected before it indexes anything; a
+    valid build afterwards (same workspace) is unaffected."""
+    _say("struct_ptr errors")
+    cfg = synth.CONFIGS["ragged"]
+    inp = synth.make_inputs(cfg)
+    dev = "cuda"
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    cell = torch.from_numpy(inp["cell"]).to(dev)
+    sp_ok = inp["struct_ptr"].astype(np.int32)
+    N, B = cfg.n_atoms, cfg.n_structs
+    ws = mlip._ws(mlip._lib.mlip_graph_workspace_size(N, B), dev)
+    bads = []
+    s = sp_ok.copy(); s[0] = 1; bads.append(s)                    # does not start at 0
+    s = sp_ok.copy(); s[-1] = N - 1; bads.append(s)               # does not end at N
+    s = sp_ok.copy(); s[-1] = N + 1000; bads.append(s)            # runs past the atoms
+    s = sp_ok.copy(); s[1], s[2] = s[2] + 1, s[1]; bads.append(s)  # decreasing step
+    s = sp_ok.copy(); s[2] = -5; bads.append(s)                   # negative entry
+    for bad in bads:
+        with pytest.raises(mlip.MlipError) as ei:
+            mlip.mlip_build_graph(pos, cell, torch.from_numpy(bad).to(dev), float(inp["cutoff"]), ws=ws)
+        assert ei.value.code == mlip.MLIP_ERR_INPUT
+        assert "struct_ptr" in str(ei.value)
+    g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    out = mlip.mlip_build_graph(pos, cell, torch.from_numpy(sp_ok).to(dev), float(inp["cutoff"]), ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["src"].cpu().numpy(), g["src"])
+    assert np.array_equal(out["rev"].cpu().numpy(), g["rev"])
+    # the readout clamps a table that runs past the atoms: same energies as the
+    # clamped table, no read past eps
+    h = torch.randn(N, 8, device=dev)
+    w_r = torch.randn(8, device=dev)
+    over = sp_ok.copy(); over[-1] = N + 77
+    r1 = mlip.mlip_readout(h, w_r, torch.from_numpy(over).to(dev))
+    r0 = mlip.mlip_readout(h, w_r, torch.from_numpy(sp_ok).to(dev))
+    assert torch.equal(r1["energy"], r0["energy"])
+
+
+def test_capacity_error_leaves_edges_untouched(mlip):
+    """With too small an edge capacity the build writes only row_ptr: the fill
+    and reverse passes check the capacity on the device."""
+    _say("capacity error")
+    import ctypes as C
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_inputs(cfg)
+    dev = "cuda"
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    cell = torch.from_numpy(inp["cell"]).to(dev)
+    sp = torch.from_numpy(inp["struct_ptr"]).to(dev)
+    N = cfg.n_atoms
+    cap = 100
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    src = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+    shift = torch.full((cap, 4), 9, dtype=torch.int8, device=dev)
+    rev = torch.full((cap,), -3, dtype=torch.int32, device=dev)
+    geom = torch.full((cap, 4), 2.5, dtype=torch.float32, device=dev)
+    ws = mlip._ws(mlip._lib.mlip_graph_workspace_size(N, 1), dev)
+    ne = C.c_int64(0)
+    rc = mlip._lib.mlip_build_graph(pos.data_ptr(), cell.data_ptr(), sp.data_ptr(), N, 1,
+                                    float(inp["cutoff"]), cap, row_ptr.data_ptr(), src.data_ptr(),
+                                    shift.data_ptr(), rev.data_ptr(), geom.data_ptr(), C.byref(ne),
+                                    ws.data_ptr(), ws.numel(), mlip._stream())
+    torch.cuda.synchronize()
+    assert rc == mlip.MLIP_ERR_CAPACITY
+    g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+    assert ne.value == g["src"].size
+    assert np.array_equal(row_ptr.cpu().numpy(), g["row_ptr"])
+    assert torch.all(src == -7) and torch.all(shift == 9) and torch.all(rev == -3) and torch.all(geom == 2.5)
+
+
+def test_graph_reverse(mlip):
+    """mlip_graph_reverse reproduces the build's reverse index, and reports a
+    graph that is not symmetric or holds an out-of-range sender."""
+    _say("graph reverse")
+    cfg = synth.CONFIGS["ragged"]
+    inp = synth.make_inputs(cfg)
+    dev = "cuda"
+    out = mlip.mlip_build_graph(torch.from_numpy(inp["pos"]).to(dev), torch.from_numpy(inp["cell"]).to(dev),
+                                torch.from_numpy(inp["struct_ptr"]).to(dev), float(inp["cutoff"]))
+    rev = mlip.mlip_graph_reverse(out["row_ptr"], out["src"], out["shift"])
+    torch.cuda.synchronize()
+    assert torch.equal(rev, out["rev"])
+    rp = out["row_ptr"].cpu().numpy().astype(np.int64)
+    src = out["src"].cpu().numpy()
+    sh = out["shift"].cpu().numpy()
+    # drop one edge of the longest row: its partner loses its reverse
+    i = int(np.argmax(np.diff(rp)))
+    e0 = int(rp[i])
+    keep = np.ones(src.size, bool)
+    keep[e0] = False
+    rp2 = rp.copy()
+    rp2[i + 1:] -= 1
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_graph_reverse(t(rp2.astype(np.int32)), t(src[keep]), t(sh[keep]))
+    assert ei.value.code == mlip.MLIP_ERR_INPUT and "symmetric" in str(ei.value)
+    # a sender outside [0, N)
+    src3 = src.copy()
+    src3[e0] = cfg.n_atoms + 5
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_graph_reverse(out["row_ptr"], t(src3), out["shift"])
+    assert ei.value.code == mlip.MLIP_ERR_INPUT and "range" in str(ei.value)
+    # a row range past the edges
+    rp4 = rp.copy().astype(np.int32)
+    rp4[-1] = src.size + 100
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_graph_reverse(t(rp4), out["src"], out["shift"])
+    assert ei.value.code == mlip.MLIP_ERR_INPUT
