@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(64) attn_fwd_kernel(
       for (int kq = 0; kq < KQ; ++kq)
         phi[lane][kq] = make_float4(ph[4 * kq], ph[4 * kq + 1], ph[4 * kq + 2], ph[4 * kq + 3]);
       fcs[lane] = fc;
-      jj[lane] = src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
     for (int mm = 0; mm < n; mm += UNROLL) {
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
       }
       fcs[lane] = fc;
       dfcs[lane] = dfc;
-      jj[lane] = src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
     for (int mm = 0; mm < n; mm += UNROLL) {
@@ -400,8 +400,8 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
         }
         phi[lane][kq] = make_float4(b[0], b[1], b[2], b[3]);
       }
-      const int re = rev[e];
-      jj[lane] = src[e];
+      const int re = int(MLIP_IDX(rev[e], row_ptr[n_atoms], "reverse edge"));
+      jj[lane] = int(MLIP_IDX(src[e], n_atoms, "sender"));
       rr[lane] = re;
       const float cc = edge_c[e] + edge_c[re];
       const float inv = r > 0.f ? 1.f / r : 0.f;
@@ -527,7 +527,7 @@ __device__ inline void tan_radial(const AttnTanArgs &a, const float4 *geom, cons
                                   float *fcs, float *fdot, float *rdot, int lane) {
   const float4 gm = geom[e];
   const float r = gm.w;
-  const int j = a.src[e];
+  const int j = int(MLIP_IDX(a.src[e], a.n_atoms, "sender"));
   float rd = 0.f;
   if (r > 0.f)
     rd = a.x_sign * (gm.x * (a.x_dot[3 * j] - xi0) + gm.y * (a.x_dot[3 * j + 1] - xi1) +
@@ -596,7 +596,7 @@ __global__ void __launch_bounds__(64) attn_jvp_kernel(AttnTanArgs a) {
     const int n = min(CHUNK, r1 - e0);
     if (lane < n) {
       tan_radial<K>(a, geom, R, e0 + lane, i, xi0, xi1, xi2, phi, dph, fcs, fdot, rdot, lane);
-      jj[lane] = a.src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(a.src[e0 + lane], a.n_atoms, "sender"));
     }
     __syncthreads();
     for (int me = 0; me < n; ++me) {
@@ -693,7 +693,7 @@ __global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
     const int n = min(CHUNK, r1 - e0);
     if (lane < n) {
       tan_radial<K>(a, geom, R, e0 + lane, i, xi0, xi1, xi2, phi, dph, fcs, fdot, rdot, lane);
-      jj[lane] = a.src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(a.src[e0 + lane], a.n_atoms, "sender"));
     }
     __syncthreads();
     for (int me = 0; me < n; ++me) {
@@ -783,8 +783,8 @@ __global__ void __launch_bounds__(64) attn_tvjp_send_kernel(AttnTanArgs a) {
     const int n = min(CHUNK, r1 - e0);
     if (lane < n) {
       tan_radial<K>(a, geom, R, e0 + lane, j, xj0, xj1, xj2, phi, dph, fcs, fdot, rdot, lane);
-      jj[lane] = a.src[e0 + lane];
-      rr[lane] = a.rev[e0 + lane];
+      jj[lane] = int(MLIP_IDX(a.src[e0 + lane], a.n_atoms, "sender"));
+      rr[lane] = int(MLIP_IDX(a.rev[e0 + lane], a.row_ptr[a.n_atoms], "reverse edge"));
     }
     __syncthreads();
     for (int me = 0; me < n; ++me) {

@@ -15,7 +15,7 @@ int launch_embed_aggregate(const int32_t *row_ptr, const int32_t *src, const flo
 int launch_edge_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int n_atoms,
                     const float *W_e, const float *e, const float *s, const float *abar, int De,
                     float rc, float *sbar, float *grad_pos, float *atom_virial, hipStream_t stream);
-int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs,
+int launch_strain_sum(const float *atom_virial, const int32_t *struct_ptr, int n_structs, int n_atoms,
                       double *grad_strain, hipStream_t stream);
 int moe_route_dispatch(const int32_t *z, const float *logits, int N, int T, int X, int k,
                        int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom,
@@ -170,7 +170,7 @@ int moe_vjp_core(const float *grad_out, const int32_t *z, const float *gate,
                  float *q_save = nullptr) {
   const int M = N * k;
   GemmArgs g1;  // Q = (g[tok] @ W2[x]^T) * silu'(P)
-  g1.A = grad_out; g1.lda = Dn; g1.a_rows = tok_atom;
+  g1.A = grad_out; g1.lda = Dn; g1.a_rows = tok_atom; g1.a_row_limit = N;
   g1.B = W2; g1.ldb = Dn; g1.b_group_stride = int64_t(H) * Dn;
   g1.C = Q; g1.C2 = q_save; g1.ldc = H; g1.R = P; g1.ldr = H;
   g1.group_off = exp_off; g1.n_groups = X;
@@ -195,7 +195,7 @@ int moe_jvp_core(const float *u_dot, const int32_t *z, const float *gate, const 
                  float *act_dot, float *Y_dot, float *h_out_dot, hipStream_t stream) {
   const int M = N * k;
   GemmArgs g3;  // P_dot = u_dot[tok] @ W1[x], act_dot = silu'(P) * P_dot
-  g3.A = u_dot; g3.lda = Dn; g3.a_rows = tok_atom;
+  g3.A = u_dot; g3.lda = Dn; g3.a_rows = tok_atom; g3.a_row_limit = N;
   g3.B = W1; g3.ldb = H; g3.b_group_stride = int64_t(Dn) * H;
   g3.C = P_dot; g3.C2 = act_dot; g3.ldc = H; g3.R = P; g3.ldr = H;
   g3.group_off = exp_off; g3.n_groups = X;
@@ -243,7 +243,7 @@ int moe_tvjp_core(const int32_t *z, const int32_t *topk, const float *gate, cons
   if (N > 0) {
     if (grad_out_dot) {
       GemmArgs g;  // Q_dot = g_dot[tok] @ W2^T (into D_dot, turned into D_dot in place below)
-      g.A = grad_out_dot; g.lda = Dn; g.a_rows = tok_atom;
+      g.A = grad_out_dot; g.lda = Dn; g.a_rows = tok_atom; g.a_row_limit = N;
       g.B = W2; g.ldb = Dn; g.b_group_stride = int64_t(H) * Dn;
       g.C = w.D_dot; g.ldc = H;
       g.group_off = exp_off; g.n_groups = X;
@@ -269,7 +269,7 @@ int moe_tvjp_core(const int32_t *z, const int32_t *topk, const float *gate, cons
   {
     WgradArgs q;  // d W1_x = sum_t gate_t (u_dot[i]^T D_t + u[i]^T D_dot_t)
     q.A0 = u_dot; q.B0 = w.D; q.A1 = u; q.B1 = w.D_dot; q.lda = Dn; q.ldb = H;
-    q.a_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off; q.n_groups = X;
+    q.a_rows = tok_atom; q.row_limit = N; q.scale = w.gt; q.group_off = exp_off; q.n_groups = X;
     q.P = M; q.Mo = Dn; q.No = H; q.C = d_W1;
     if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
   }
@@ -277,7 +277,7 @@ int moe_tvjp_core(const int32_t *z, const int32_t *topk, const float *gate, cons
     WgradArgs q;  // d W2_x = sum_t gate_t (act_dot_t^T g[i] + act_t^T g_dot[i])
     q.A0 = w.act_dot; q.B0 = grad_out;
     if (grad_out_dot) { q.A1 = w.act; q.B1 = grad_out_dot; }
-    q.lda = H; q.ldb = Dn; q.b_rows = tok_atom; q.scale = w.gt; q.group_off = exp_off;
+    q.lda = H; q.ldb = Dn; q.b_rows = tok_atom; q.row_limit = N; q.scale = w.gt; q.group_off = exp_off;
     q.n_groups = X; q.P = M; q.Mo = H; q.No = Dn; q.C = d_W2;
     if (int rc = launch_wgrad(q, nullptr, stream)) return rc;
   }
@@ -364,6 +364,45 @@ TriTanWs carve_tri_tan(void *base, int64_t N, int64_t E, int64_t Dn, int64_t Dt,
   return w;
 }
 
+int check_aggregate_args(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                         int32_t n_atoms, int64_t n_edges, const float *h, const float *W_e,
+                         const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge,
+                         int32_t d_node, float cutoff, const float *e, const float *s,
+                         const float *u) {
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  if (int rc = check_width(d_edge, "d_edge")) return rc;
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (h && s && u), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_e, 16) && aligned(W_d, 16) &&
+                     aligned(W_u, 16) && aligned(e, 16) && aligned(s, 16) && aligned(u, 16),
+                 "float arrays must be 16-byte aligned");
+  return MLIP_OK;
+}
+
+// s = h W_d, the edge embedding + aggregation into w.a, u = h + a W_u.
+int aggregate_core(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                   const float *h, const float *W_e, const float *W_d, const float *W_u,
+                   int32_t d_edge, int32_t d_node, float cutoff, float *e, float *s, float *u,
+                   const AggWs &w, hipStream_t stream) {
+  GemmArgs g;  // s = h @ W_d
+  g.A = h; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s; g.ldc = d_edge;
+  g.M = n_atoms; g.N = d_edge; g.K = d_node;
+  g.k_split = dense_k_split(n_atoms, d_edge, d_node); g.split_ws = w.split;
+  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  if (int rc = launch_embed_aggregate(row_ptr, src, geom, n_atoms, W_e, s, d_edge, cutoff, e, w.a,
+                                      stream))
+    return rc;
+  GemmArgs g2;  // u = h + a @ W_u
+  g2.A = w.a; g2.lda = d_edge; g2.B = W_u; g2.ldb = d_node; g2.C = u; g2.ldc = d_node;
+  g2.R = h; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_edge;
+  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+}
+
 }  // namespace
 }  // namespace mlip
 
@@ -383,35 +422,15 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
                    const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
                    float *e, float *s, float *u, void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
-                 "n_atoms/n_edges out of range");
-  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
-  if (int rc = check_width(d_edge, "d_edge")) return rc;
-  if (int rc = check_width(d_node, "d_node")) return rc;
-  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
-  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u, "null pointer argument");
-  MLIP_CHECK_ARG(n_atoms == 0 || (h && s && u), "null pointer argument");
-  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
-  MLIP_CHECK_ARG(aligned(geom, 16) && aligned(h, 16) && aligned(W_e, 16) && aligned(W_d, 16) &&
-                     aligned(W_u, 16) && aligned(e, 16) && aligned(s, 16) && aligned(u, 16),
-                 "float arrays must be 16-byte aligned");
+  if (int rc = check_aggregate_args(row_ptr, src, geom, n_atoms, n_edges, h, W_e, W_d, W_u, n_rbf,
+                                    d_edge, d_node, cutoff, e, s, u))
+    return rc;
   if (int rc = check_ws(ws, ws_bytes, mlip_aggregate_workspace_size(n_atoms, d_edge, d_node)))
     return rc;
   if (n_atoms == 0) return MLIP_OK;
   AggWs w = carve_agg(ws, n_atoms, d_edge, d_node, nullptr);
-
-  GemmArgs g;  // s = h @ W_d
-  g.A = h; g.lda = d_node; g.B = W_d; g.ldb = d_edge; g.C = s; g.ldc = d_edge;
-  g.M = n_atoms; g.N = d_edge; g.K = d_node;
-  g.k_split = dense_k_split(n_atoms, d_edge, d_node); g.split_ws = w.split;
-  if (int rc = launch_gemm(g, false, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
-  if (int rc = launch_embed_aggregate(row_ptr, src, geom, n_atoms, W_e, s, d_edge, cutoff, e, w.a,
-                                      stream))
-    return rc;
-  GemmArgs g2;  // u = h + a @ W_u
-  g2.A = w.a; g2.lda = d_edge; g2.B = W_u; g2.ldb = d_node; g2.C = u; g2.ldc = d_node;
-  g2.R = h; g2.ldr = d_node; g2.M = n_atoms; g2.N = d_node; g2.K = d_edge;
-  return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
+  return aggregate_core(row_ptr, src, geom, n_atoms, h, W_e, W_d, W_u, d_edge, d_node, cutoff, e, s,
+                        u, w, stream);
 }
 
 // ------------------------------------------------------------------- MoE ---
@@ -453,7 +472,7 @@ int mlip_moe_forward(const float *u, const int32_t *z, const float *logits, cons
     return rc;
   if (n_atoms == 0) return MLIP_OK;
   GemmArgs g;  // P = u[tok] @ W1[x], act = silu(P)
-  g.A = u; g.lda = d_node; g.a_rows = tok_atom;
+  g.A = u; g.lda = d_node; g.a_rows = tok_atom; g.a_row_limit = n_atoms;
   g.B = W1; g.ldb = d_hidden; g.b_group_stride = int64_t(d_node) * d_hidden;
   g.C = P; g.C2 = w.act; g.ldc = d_hidden;
   g.group_off = exp_off; g.n_groups = n_experts;
@@ -536,7 +555,7 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                         mlip_vjp_workspace_size(n_atoms, top_k, d_edge, d_node, d_hidden)))
     return rc;
   if (n_atoms == 0) {
-    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, 0, grad_strain, stream);
     return MLIP_OK;
   }
   MLIP_CHECK_ARG(aligned(ubar_out, 16) && aligned(q_out, 16), "float arrays must be 16-byte aligned");
@@ -557,7 +576,7 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                                w.sbar, grad_pos, vir, stream))
     return rc;
   if (grad_strain) {
-    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, n_atoms, grad_strain, stream)) return rc;
   }
   GemmArgs g4;  // grad_h = ubar + sbar @ W_d^T
   g4.A = w.sbar; g4.lda = d_edge; g4.B = W_d; g4.ldb = d_edge; g4.C = grad_h; g4.ldc = d_node;
@@ -703,7 +722,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
                         mlip_attention_vjp_workspace_size(n_atoms, n_edges, d_attn, n_heads)))
     return rc;
   if (n_atoms == 0) {
-    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, 0, grad_strain, stream);
     return MLIP_OK;
   }
   AttnVjpWs w = carve_attn_vjp(ws, n_atoms, n_edges, d_attn, n_heads, nullptr);
@@ -723,7 +742,7 @@ int mlip_attention_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t
   a.Da = d_attn; a.nh = n_heads; a.cpl = cpl; a.lph = lph; a.rc = cutoff;
   if (int rc = launch_attn_vjp(a, stream)) return rc;
   if (grad_strain) {
-    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, n_atoms, grad_strain, stream)) return rc;
   }
   GemmArgs g2;  // grad_h0 = ubar + [qbar | kbar | vbar] @ W_qkv^T
   g2.A = w.qkv_bar; g2.lda = 3 * int64_t(d_attn); g2.B = W_qkv; g2.ldb = 3 * int64_t(d_attn);
@@ -819,7 +838,7 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   if (int rc = check_ws(ws, ws_bytes, mlip_tri_vjp_workspace_size(n_atoms, n_edges, d_tri)))
     return rc;
   if (n_atoms == 0) {
-    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, grad_strain, stream);
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, 0, grad_strain, stream);
     return MLIP_OK;
   }
   TriVjpWs w = carve_tri_vjp(ws, n_atoms, n_edges, d_tri, nullptr);
@@ -837,7 +856,7 @@ int mlip_tri_vjp(const int32_t *row_ptr, const int32_t *src, const int32_t *rev,
   a.accumulate = accumulate ? 1 : 0; a.Dt = d_tri; a.cpl = cpl; a.rc = cutoff;
   if (int rc = launch_tri_vjp(a, stream)) return rc;
   if (grad_strain) {
-    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, grad_strain, stream)) return rc;
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, n_atoms, grad_strain, stream)) return rc;
   }
   GemmArgs g2;  // grad_h = grad_hT + sbar @ W_s^T
   g2.A = w.sbar; g2.lda = d_tri; g2.B = W_s; g2.ldb = d_tri; g2.C = grad_h; g2.ldc = d_node;

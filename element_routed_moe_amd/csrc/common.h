@@ -17,6 +17,30 @@ namespace mlip {
 // ---------------------------------------------------------------- errors ---
 void set_error(const char *fmt, ...);
 
+// ------------------------------------------------------ debug bounds checks -
+// Built with -DMLIP_DEBUG_BOUNDS (python -m element_routed_moe_amd.build
+// --debug-bounds, which writes libmlip_debug.so), every index the kernels read
+// from the data and then dereference (senders, reverse edges, gathered token
+// rows, dispatch slots) is checked against its range.  A violation prints the
+// index, its range and the source line, and the access goes to the nearest
+// valid index instead, so the kernel finishes; the results are then wrong and
+// the printed line names the first bad input.  Release builds compile the
+// macro to the bare index.
+#ifdef MLIP_DEBUG_BOUNDS
+__device__ inline int64_t debug_check_index(int64_t i, int64_t n, const char *what, const char *file,
+                                            int line) {
+  if (n > 0 && (i < 0 || i >= n)) {
+    printf("mlip bounds: %s index %lld outside [0, %lld) at %s:%d\n", what, (long long)i,
+           (long long)n, file, line);
+    return i < 0 ? 0 : n - 1;
+  }
+  return i;
+}
+#define MLIP_IDX(i, n, what) (::mlip::debug_check_index(int64_t(i), int64_t(n), what, __FILE__, __LINE__))
+#else
+#define MLIP_IDX(i, n, what) int64_t(i)
+#endif
+
 struct Status {
   int code = MLIP_OK;
   bool ok() const { return code == MLIP_OK; }
@@ -74,9 +98,12 @@ enum KClass {
 struct ProfScope {
   ProfScope(KClass k, hipStream_t s);
   ~ProfScope();
+  ProfScope(const ProfScope &) = delete;
+  ProfScope &operator=(const ProfScope &) = delete;
   KClass k;
   hipStream_t s;
-  int slot = -1;
+  int slot = -1;               // >= 0 while this scope holds a recorded start event
+  hipEvent_t a = nullptr, b = nullptr;
 };
 
 // --------------------------------------------------------------- workspace -
@@ -169,6 +196,7 @@ struct GemmArgs {
   const float *A = nullptr;   // rows of length K (row stride lda)
   int64_t lda = 0;
   const int32_t *a_rows = nullptr;  // optional row gather: A row of output row p
+  int64_t a_row_limit = 0;          // rows of A behind a_rows (debug bounds checks; 0: unknown)
   const float *B = nullptr;   // per group: NN -> [K][N] (ldb = N), NT -> [N][K] (ldb = K)
   int64_t ldb = 0;
   int64_t b_group_stride = 0;
@@ -205,6 +233,7 @@ struct WgradArgs {
   const float *B0 = nullptr, *B1 = nullptr;   // rows of No floats, stride ldb
   int64_t lda = 0, ldb = 0;
   const int32_t *a_rows = nullptr, *b_rows = nullptr;
+  int64_t row_limit = 0;                      // rows behind a_rows / b_rows (debug checks; 0: unknown)
   const float *scale = nullptr;               // per-row factor on the A operand
   const int32_t *group_off = nullptr;         // [G+1]; nullptr -> one group [0, P)
   int n_groups = 1, P = 0, Mo = 0, No = 0;

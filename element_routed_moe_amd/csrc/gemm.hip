@@ -115,7 +115,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     a_kc[q] = 4 * (s ^ ((r / RPB) % KQ));
     int p = row0 + r;
     p = p < rows ? p : row0;             // padding rows read a valid row; never stored
-    const int64_t arow = g.a_rows ? int64_t(g.a_rows[p]) : int64_t(p);
+    const int64_t arow = g.a_rows ? MLIP_IDX(g.a_rows[p], g.a_row_limit, "gathered row") : int64_t(p);
     a_src[q] = g.A + arow * g.lda;
   }
   const float *b_src[B_LOADS];

@@ -1,4 +1,5 @@
 // Error reporting, kernel timing and the device-wide prefix sum.
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -24,41 +25,62 @@ static const char *kClassNames[K_NUM_CLASSES] = {
     "attn_vjp_recv", "attn_vjp_send", "tri_fwd", "tri_vjp_recv", "tri_vjp_send",
     "gemm_expert_tan", "gemm_wgrad", "edge_tan", "moe_tan", "attn_tan"};
 
+// Profiling state is process-wide and guarded by g_prof_mu, so host threads
+// may call the library concurrently with profiling on; each scope keeps its
+// own event pair and files the record only when both events are recorded.
 struct ProfRec {
   int k;
   hipEvent_t a, b;
 };
-static bool g_prof = false;
-static uint64_t g_prof_mask = ~uint64_t(0);   // classes timed while profiling is on
+static std::mutex g_prof_mu;
+static std::atomic<bool> g_prof{false};
+static std::atomic<uint64_t> g_prof_mask{~uint64_t(0)};   // classes timed while profiling is on
 static std::vector<std::pair<hipEvent_t, hipEvent_t>> g_pool;
 static std::vector<ProfRec> g_recs;
 static double g_ms[K_NUM_CLASSES];
 static int64_t g_cnt[K_NUM_CLASSES];
 
 ProfScope::ProfScope(KClass kk, hipStream_t ss) : k(kk), s(ss) {
-  if (!g_prof || !((g_prof_mask >> int(kk)) & 1)) return;
+  if (!g_prof.load(std::memory_order_relaxed) ||
+      !((g_prof_mask.load(std::memory_order_relaxed) >> int(kk)) & 1))
+    return;
   std::pair<hipEvent_t, hipEvent_t> ev;
-  if (g_pool.empty()) {
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_pool.empty()) {
+      ev = g_pool.back();
+      g_pool.pop_back();
+      slot = 1;
+    }
+  }
+  if (slot < 0) {
     if (hipEventCreate(&ev.first) != hipSuccess) return;
-    if (hipEventCreate(&ev.second) != hipSuccess) return;
-  } else {
-    ev = g_pool.back();
-    g_pool.pop_back();
+    if (hipEventCreate(&ev.second) != hipSuccess) {
+      (void)hipEventDestroy(ev.first);
+      return;
+    }
   }
   if (hipEventRecord(ev.first, s) != hipSuccess) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     g_pool.push_back(ev);
+    slot = -1;
     return;
   }
-  g_recs.push_back({int(k), ev.first, ev.second});
-  slot = int(g_recs.size()) - 1;
+  a = ev.first;
+  b = ev.second;
+  slot = 1;
 }
 
 ProfScope::~ProfScope() {
   if (slot < 0) return;
-  (void)hipEventRecord(g_recs[slot].b, s);
+  const bool ok = hipEventRecord(b, s) == hipSuccess;
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  if (ok) g_recs.push_back({int(k), a, b});
+  else g_pool.push_back({a, b});
 }
 
-static int resolve_profile() {
+// callers hold g_prof_mu
+static int resolve_profile_locked() {
   for (auto &r : g_recs) {
     MLIP_HIP(hipEventSynchronize(r.b));
     float ms = 0.f;
@@ -81,17 +103,18 @@ const char *mlip_last_error(void) { return g_err; }
 int mlip_version(void) { return 1; }
 
 int mlip_profile_enable(int enable) {
-  g_prof = enable != 0;
+  g_prof.store(enable != 0);
   return MLIP_OK;
 }
 
 int mlip_profile_select(uint64_t class_mask) {
-  g_prof_mask = class_mask;
+  g_prof_mask.store(class_mask);
   return MLIP_OK;
 }
 
 int mlip_profile_reset(void) {
-  int rc = resolve_profile();
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  int rc = resolve_profile_locked();
   for (int i = 0; i < K_NUM_CLASSES; ++i) {
     g_ms[i] = 0.0;
     g_cnt[i] = 0;
@@ -103,7 +126,8 @@ int mlip_profile_count(void) { return K_NUM_CLASSES; }
 
 int mlip_profile_get(int idx, const char **name, int64_t *launches, double *total_ms) {
   MLIP_CHECK_ARG(idx >= 0 && idx < K_NUM_CLASSES, "profile index %d out of range", idx);
-  int rc = resolve_profile();
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  int rc = resolve_profile_locked();
   if (rc != MLIP_OK) return rc;
   if (name) *name = kClassNames[idx];
   if (launches) *launches = g_cnt[idx];

@@ -171,8 +171,8 @@ __global__ void __launch_bounds__(W_THREADS, 2) wgrad_kernel(WgradArgs g, int k_
       for (int q = 0; q < W_SLOTS; ++q) {
         int p = k0 + kr[q];
         p = p < p1 ? p : p0;
-        ra[q] = GA ? int64_t(Xs[set][kr[q]]) : int64_t(p);
-        rb[q] = GB ? int64_t(Xs[set][(GA ? 64 : 0) + kr[q]]) : int64_t(p);
+        ra[q] = GA ? MLIP_IDX(Xs[set][kr[q]], g.row_limit, "token row") : int64_t(p);
+        rb[q] = GB ? MLIP_IDX(Xs[set][(GA ? 64 : 0) + kr[q]], g.row_limit, "token row") : int64_t(p);
       }
 #pragma unroll
       for (int q = 0; q < W_SLOTS; ++q)
@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(64) edge_tan_kernel(EdgeTanArgs g, int n_group
       if (lane < n) {
         const int e = e0 + lane;
         const float4 gm = geom[e];
-        const int j = g.src[e];
+        const int j = int(MLIP_IDX(g.src[e], g.n_atoms, "sender"));
         const float r = gm.w;
         float rdot = 0.f;
         if (r > 0.f) {
@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(64) edge_basis_grad_kernel(
       if (lane < n) {
         const int e = e0 + lane;
         const float4 gm = geom[e];
-        const int j = src[e];
+        const int j = int(MLIP_IDX(src[e], n_atoms, "sender"));
         const float r = gm.w;
         float rdot = 0.f;
         if (r > 0.f)
@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(256) token_gate_kernel(const int32_t *__restri
   const int i = int(idx / k), r = int(idx - int64_t(i) * k);
   const int t = z[i];
   if (t < 0 || t >= T) return;
-  gt[slot[idx]] = gate[t * k + r];
+  gt[MLIP_IDX(slot[idx], int64_t(N) * k, "dispatch slot")] = gate[t * k + r];
 }
 
 // G[t, r] = sum of dg over the tokens of element t routed at rank r.  Those

@@ -141,7 +141,7 @@ __device__ inline EdgeGeo edge_geo(float4 g, const Radial &R) {
 // Accumulates A_lm,c and B_c of row i over its edges (channel layout).
 template <int CPL>
 __device__ inline void accumulate_row(const int32_t *__restrict__ src, const float4 *__restrict__ geom,
-                                      const float *__restrict__ s, int Dt, int c0, int r0, int r1,
+                                      const float *__restrict__ s, int n_atoms, int Dt, int c0, int r0, int r1,
                                       const Radial &R, float (*ysh)[NSH], float *fsq, int *jj,
                                       float (&A)[NSH][CPL], float (&Bs)[CPL]) {
   const int lane = threadIdx.x;
@@ -160,7 +160,7 @@ __device__ inline void accumulate_row(const int32_t *__restrict__ src, const flo
 #pragma unroll
       for (int lm = 0; lm < NSH; ++lm) ysh[lane][lm] = G.fc * S[lm];
       fsq[lane] = G.fc * G.fc;
-      jj[lane] = src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
     for (int mm = 0; mm < n; mm += UNROLL) {
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(64) tri_fwd_kernel(
   const int c0 = active ? lane * CPL : 0;
   const Radial R = make_radial(rc);
   float A[NSH][CPL], Bs[CPL];
-  accumulate_row<CPL>(src, geom, s, Dt, c0, row_ptr[i], row_ptr[i + 1], R, ysh, fsq, jj, A, Bs);
+  accumulate_row<CPL>(src, geom, s, n_atoms, Dt, c0, row_ptr[i], row_ptr[i + 1], R, ysh, fsq, jj, A, Bs);
   if (!active) return;
   float w[NANG][CPL];
 #pragma unroll
@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
   const Radial R = make_radial(rc);
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
   float A[NSH][CPL], Bs[CPL];
-  accumulate_row<CPL>(src, geom, s, Dt, c0, r0, r1, R, ysh, fsq, jj, A, Bs);
+  accumulate_row<CPL>(src, geom, s, n_atoms, Dt, c0, r0, r1, R, ysh, fsq, jj, A, Bs);
 
   // Abar and Bbar of this row, in place of A and B (zero on idle lanes)
   {
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
       fcs[lane] = G.fc;
       dfcs[lane] = G.dfc;
       fsq[lane] = G.fc * G.fc;
-      jj[lane] = src[e0 + lane];
+      jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
     // channel pass: sigma_e rows, and the channel sums P_lm, Q of every edge
@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(64) tri_vjp_send_kernel(
     const int n = min(CHUNK, r1 - e0);
     if (lane < n) {
       const int e = e0 + lane;
-      const int re = rev[e];
+      const int re = int(MLIP_IDX(rev[e], row_ptr[n_atoms], "reverse edge"));
       rr[lane] = re;
       const float4 ge = gvec[e], gr = gvec[re], d = geom[e];
       const float gx = ge.x - gr.x, gy = ge.y - gr.y, gz = ge.z - gr.z;   // d_rev = -d
@@ -516,6 +516,7 @@ struct TriTanRow {
   const float *x_dot;
   float x_sign;
   int Dt, c0, i;
+  int n_atoms;
 };
 
 // y, y_dot, f^2 and 2 f f_dot of the chunk's edges into LDS (lane = edge)
@@ -523,7 +524,7 @@ __device__ inline void tan_edge_terms(const TriTanRow &t, const Radial &R, int e
                                       float xi2, float (*ysh)[NSH], float (*ydt)[NSH], float *fsq,
                                       float *ffd, int *jj, int lane) {
   const EdgeGeo G = edge_geo(t.geom[e], R);
-  const int j = t.src[e];
+  const int j = int(MLIP_IDX(t.src[e], t.n_atoms, "sender"));
   const float dx = t.x_sign * (t.x_dot[3 * j] - xi0), dy = t.x_sign * (t.x_dot[3 * j + 1] - xi1),
               dz = t.x_sign * (t.x_dot[3 * j + 2] - xi2);
   const float rd = G.u.x * dx + G.u.y * dy + G.u.z * dz;
@@ -613,7 +614,7 @@ __global__ void __launch_bounds__(64) tri_jvp_kernel(TriTanArgs a) {
   const int cc = (slice * 64 + lane) * CPL;
   const bool active = cc < a.Dt;
   TriTanRow t{a.src, reinterpret_cast<const float4 *>(a.geom), a.s, a.s_dot, a.x_dot, a.x_sign, a.Dt,
-              active ? cc : 0, i};
+              active ? cc : 0, i, a.n_atoms};
   const Radial R = make_radial(a.rc);
   float A[NSH][CPL], Ad[NSH][CPL], Bs[CPL], Bd[CPL];
   tan_accumulate<CPL>(t, a.row_ptr[i], a.row_ptr[i + 1], R, ysh, ydt, fsq, ffd, jj, A, Ad, Bs, Bd);
@@ -646,7 +647,7 @@ __global__ void __launch_bounds__(64) tri_tvjp_recv_kernel(TriTanArgs a) {
   const int cc = (slice * 64 + lane) * CPL;
   const bool active = cc < a.Dt;
   TriTanRow t{a.src, reinterpret_cast<const float4 *>(a.geom), a.s, a.s_dot, a.x_dot, a.x_sign, a.Dt,
-              active ? cc : 0, i};
+              active ? cc : 0, i, a.n_atoms};
   const Radial R = make_radial(a.rc);
   const int r0 = a.row_ptr[i], r1 = a.row_ptr[i + 1];
   float A[NSH][CPL], Ad[NSH][CPL], Bs[CPL], Bd[CPL];
@@ -736,7 +737,7 @@ __global__ void __launch_bounds__(64) tri_tvjp_send_kernel(TriTanArgs a) {
   const int r0 = a.row_ptr[j], r1 = a.row_ptr[j + 1];
   for (int e0 = r0; e0 < r1; e0 += CHUNK) {
     const int n = min(CHUNK, r1 - e0);
-    if (lane < n) rr[lane] = a.rev[e0 + lane];
+    if (lane < n) rr[lane] = int(MLIP_IDX(a.rev[e0 + lane], a.row_ptr[a.n_atoms], "reverse edge"));
     __syncthreads();
     for (int me = 0; me < n; ++me) {
       float sg[CPL];

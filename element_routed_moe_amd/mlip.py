@@ -15,7 +15,9 @@ from typing import Dict, Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmlip.so")
+# MLIP_LIBRARY selects another build of the same library (e.g. libmlip_debug.so,
+# the bounds-checked build); by default the release build next to this file.
+LIB_PATH = os.environ.get("MLIP_LIBRARY") or os.path.join(_HERE, "libmlip.so")
 
 MLIP_OK = 0
 MLIP_ERR_INVALID = -1
@@ -45,6 +47,7 @@ _SIGS = {
     "mlip_graph_workspace_size": (_sz, [_i32, _i32]),
     "mlip_build_graph": (C.c_int, [_p, _p, _p, _i32, _i32, _f32, _i64, _p, _p, _p, _p, _p,
                                    C.POINTER(C.c_int64), _p, _sz, _p]),
+    "mlip_graph_reverse": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _sz, _p]),
     "mlip_aggregate_workspace_size": (_sz, [_i32, _i32, _i32]),
     "mlip_aggregate": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                  _p, _p, _p, _p, _sz, _p]),
@@ -177,6 +180,22 @@ def mlip_build_graph(pos, cell, struct_ptr, cutoff: float, edge_capacity: Option
         return dict(row_ptr=row_ptr, src=src[:E], shift=shift[:E], rev=rev[:E], geom=geom[:E],
                     n_edges=E, buffers=buffers)
     raise MlipError(MLIP_ERR_CAPACITY, "edge capacity could not be met")
+
+
+def mlip_graph_reverse(row_ptr, src, shift, rev: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reverse-edge index of a receiver-sorted CSR graph (rows ordered by
+    sender and shift, as mlip_build_graph writes them)."""
+    N = int(row_ptr.shape[0]) - 1
+    E = int(src.shape[0])
+    dev = row_ptr.device
+    if rev is None:
+        rev = torch.empty(max(E, 1), dtype=torch.int32, device=dev)[:E]
+    if ws is None:
+        ws = _ws(_lib.mlip_graph_workspace_size(0, 1), dev)
+    _check(_lib.mlip_graph_reverse(_ptr(row_ptr), _ptr(src), _ptr(shift), N, E, _ptr(rev), _ptr(ws),
+                                   ws.numel(), _stream()))
+    return rev
 
 
 def mlip_aggregate(graph, h, W_e, W_d, W_u, cutoff: float, out: Optional[Dict] = None,
@@ -743,12 +762,20 @@ class Block:
         self.graph = self.agg = self.moe = self.ro = self.vjp = None
         self.jvp = self.tan = None
 
-    def step(self):
+    def _graph(self, build_graph: bool):
+        """The radius graph of this step: rebuilt, or (build_graph=False, as a
+        model of several blocks on one graph does) the previous step's."""
+        if not build_graph and self.graph is not None:
+            return self.graph
         g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
                              edge_capacity=self.edge_capacity, ws=self.ws_graph,
                              buffers=None if self.graph is None else self.graph["buffers"])
         if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
             self.edge_capacity = g["n_edges"]
+        return g
+
+    def step(self, build_graph: bool = True):
+        g = self._graph(build_graph)
         reuse = self.agg
         if reuse is not None and reuse["e"] is not None and reuse["e"].shape[0] != g["n_edges"]:
             reuse = None
@@ -962,12 +989,10 @@ class FullBlock:
                                          h_out_dot=h_out_dot)
         return res
 
-    def step(self):
-        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
-                             edge_capacity=self.edge_capacity, ws=self.ws_graph,
-                             buffers=None if self.graph is None else self.graph["buffers"])
-        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
-            self.edge_capacity = g["n_edges"]
+    _graph = Block._graph
+
+    def step(self, build_graph: bool = True):
+        g = self._graph(build_graph)
         self.graph = g
         h_out = self.forward(g, self.h)
         self.ro = mlip_readout(h_out, self.w_r, self.struct_ptr, out=self.ro)
@@ -1008,13 +1033,16 @@ class Stack:
         self.graph = self.h0 = self.ro = self.grad_h0 = None
         self.edge_capacity = None
 
-    def step(self):
+    def step(self, build_graph: bool = True):
         L0 = self.first
-        g = mlip_build_graph(L0.pos, L0.cell, L0.struct_ptr, L0.cutoff,
-                             edge_capacity=self.edge_capacity, ws=L0.ws_graph,
-                             buffers=None if self.graph is None else self.graph["buffers"])
-        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
-            self.edge_capacity = g["n_edges"]
+        if build_graph or self.graph is None:
+            g = mlip_build_graph(L0.pos, L0.cell, L0.struct_ptr, L0.cutoff,
+                                 edge_capacity=self.edge_capacity, ws=L0.ws_graph,
+                                 buffers=None if self.graph is None else self.graph["buffers"])
+            if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
+                self.edge_capacity = g["n_edges"]
+        else:
+            g = self.graph
         self.graph = g
         self.h0 = mlip_embed_atoms(L0.z, self.emb, out=self.h0)
         h = self.h0

@@ -22,8 +22,9 @@
  *     memory is passed as (ws, ws_bytes); its size comes from the matching
  *     mlip_*_workspace_size() call and it must be 256-byte aligned.
  *   - stream is a hipStream_t passed as void* (NULL = default stream).  All
- *     work is enqueued asynchronously on it; only mlip_build_graph waits for
- *     the stream (once, to learn the number of edges).
+ *     work is enqueued asynchronously on it; only mlip_build_graph,
+ *     mlip_graph_reverse and mlip_moe_status wait for the stream (once each,
+ *     to read a count or a device-side check).
  *   - Floating point data are float32, row-major.  Weight matrices are
  *     stored "in x out": y = x @ W.
  *   - Feature widths (d_edge, d_node, d_hidden) must be multiples of 4 and
@@ -91,14 +92,21 @@ int mlip_version(void);
  * n_edges (host)       E.
  *
  * Errors: MLIP_ERR_CAPACITY when E > edge_capacity (then *n_edges = E and
- * only row_ptr has been written); MLIP_ERR_INPUT for positions outside
- * their cell or a cell with non-finite entries or det = 0 (host message
- * says which); MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges, a
- * shift exceeds +-127 or a cell is so thin that more than 8 images per axis
- * reach the cutoff.  Synchronises the stream once: the calling thread polls
- * the stream (yielding between polls) until all work queued on it, earlier
- * work included, has finished, so that it can read E; the read goes through
- * a small pinned host buffer allocated on a thread's first call and kept for
+ * only row_ptr has been written); MLIP_ERR_INPUT for a struct_ptr that does
+ * not run 0 = p_0 <= p_1 <= ... <= p_B = n_atoms (then *n_edges = 0 and
+ * nothing is indexed through it), positions outside their cell or a cell
+ * with non-finite entries or det = 0 (host message says which), and for an
+ * edge without its reverse edge (cannot happen: the predicate is exactly
+ * symmetric; reported rather than passed on, with rev[e] = e for that edge);
+ * MLIP_ERR_UNSUPPORTED when a row has more than 1024 edges or a cell is so
+ * thin that more than 8 images per axis reach the cutoff (shifts then stay
+ * within +-8, well inside int8).  All passes are queued before one
+ * synchronisation: the calling thread polls the stream (yielding between
+ * polls) until all work queued on it, earlier work included, has finished,
+ * then reads E, the error flags and the largest degree; the passes that
+ * write the edge arrays check on the device that the edges fit, so on any
+ * error return the edge arrays are untouched.  The read goes through a
+ * small pinned host buffer allocated on a thread's first call and kept for
  * the life of the process.
  * ------------------------------------------------------------------------ */
 size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs);
@@ -107,6 +115,27 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
                      int64_t edge_capacity, int32_t *row_ptr, int32_t *src,
                      int8_t *shift, int32_t *rev, float *geom, int64_t *n_edges,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Reverse-edge index of a caller's receiver-sorted CSR graph ([review] 3.1,
+ * Fig. 1(a): the periodic graph is symmetric, every edge i <- j with shift
+ * S has the edge j <- i with shift -S).  mlip_build_graph fills rev itself;
+ * this entry point serves graphs built elsewhere (or edited) before they go
+ * to the attention and three-body passes, which read rev.
+ *
+ * row_ptr [n_atoms+1], src [n_edges], shift [n_edges,4] int8 as written by
+ * mlip_build_graph: rows sorted by (sender, S0, S1, S2).
+ * rev     [n_edges]  output: index of the reverse edge.
+ * ws      mlip_graph_workspace_size(0, 1) bytes.
+ *
+ * Errors: MLIP_ERR_INPUT when a row range leaves [0, n_edges] or a sender
+ * leaves [0, n_atoms) (those edges are skipped), or when some edge has no
+ * reverse edge (its rev entry is then the edge itself, so the array stays a
+ * valid index array).  Synchronises the stream once to read the check.
+ * ------------------------------------------------------------------------ */
+int mlip_graph_reverse(const int32_t *row_ptr, const int32_t *src, const int8_t *shift,
+                       int32_t n_atoms, int64_t n_edges, int32_t *rev, void *ws, size_t ws_bytes,
+                       void *stream);
 
 /* ------------------------------------------------------------------------
  * Edge embedding + neighbour aggregation + projections ([news] pair
@@ -172,7 +201,9 @@ int mlip_moe_status(const void *ws, int32_t *bad_types, void *stream);
 /* ------------------------------------------------------------------------
  * Readout ([review] 3.1 Fig. 1(b) names a readout; the reading here is
  * linear): eps_i = h_out_i . w_r, energy_b = sum_{i in b} eps_i in float64.
- * eps [N] f32, energy [n_structs] f64.
+ * eps [N] f32, energy [n_structs] f64.  struct_ptr as for mlip_build_graph;
+ * its entries are clamped into [0, n_atoms] on the device, so a malformed
+ * table gives wrong sums but no access outside eps.
  * ------------------------------------------------------------------------ */
 int mlip_readout(const float *h_out, const float *w_r, const int32_t *struct_ptr,
                  int32_t n_atoms, int32_t n_structs, int32_t d_node, float *eps,
@@ -556,8 +587,11 @@ int mlip_embed_grad(const int32_t *z, const float *grad_h, int32_t n_atoms, int3
  * bracketed by HIP events on its stream; mlip_profile_get() waits for the
  * recorded events and returns, for the kernel class with index idx, its name
  * (static string), the number of launches and their summed duration in
- * milliseconds.  Classes are numbered 0 .. mlip_profile_count()-1.  Not
- * thread-safe; meant for benchmarks.
+ * milliseconds.  Classes are numbered 0 .. mlip_profile_count()-1.  The
+ * timing state is process-wide and guarded by a lock, so several host
+ * threads may call the library while profiling is on; their launches then
+ * add to the same per-class totals.  Event pairs are created on first use
+ * and reused for the life of the process; meant for benchmarks.
  * mlip_profile_select(class_mask) restricts the timing to the classes whose
  * bit (1 << idx) is set in class_mask (all classes until it is called): each
  * timed launch costs two event records on its stream, so a benchmark can time

@@ -32,6 +32,17 @@ def test_exports_every_declared_symbol(mlip):
     assert mlip._lib.mlip_version() == 1
 
 
+def test_debug_build_exports_the_same_symbols(mlip):
+    """The bounds-checked build (libmlip_debug.so) is the same library: it loads
+    without a GPU and exports every declared entry point."""
+    path = os.path.join(ROOT, "element_routed_moe_amd", "libmlip_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("debug build not present")
+    lib = C.CDLL(path)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
 def test_workspace_sizes_are_monotone(mlip):
     L = mlip._lib
     assert L.mlip_graph_workspace_size(4096, 32) < L.mlip_graph_workspace_size(8192, 32)
@@ -63,6 +74,21 @@ def test_build_graph_rejects_bad_args(mlip):
     rc = L.mlip_build_graph(fake, fake, fake, 10, 1, 5.0, 100, fake, fake, fake, fake, fake,
                             C.byref(ne), fake, 16, None)
     assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+
+
+def test_graph_reverse_rejects_bad_args(mlip):
+    L = mlip._lib
+    fake = C.c_void_p(256)
+    rc = L.mlip_graph_reverse(None, fake, fake, 4, 10, fake, fake, 1 << 20, None)
+    assert "row_ptr" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_graph_reverse(fake, None, fake, 4, 10, fake, fake, 1 << 20, None)
+    assert "edge arrays" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_graph_reverse(fake, fake, fake, 4, -1, fake, fake, 1 << 20, None)
+    assert "out of range" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_graph_reverse(fake, fake, fake, 4, 10, fake, fake, 8, None)
+    assert "workspace" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_graph_reverse(fake, fake, C.c_void_p(258), 4, 10, fake, fake, 1 << 20, None)
+    assert "aligned" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
 def test_aggregate_and_moe_reject_bad_args(mlip):
