@@ -1,14 +1,17 @@
 """GPU parity at the full workload sizes (S, M, L widths and the 262144-atom
 share), in the launch configuration the benchmark times.
 
-The oracle cannot run these blocks end to end, so it checks:
-  * the whole radius graph bit for bit where it is cheap (batched 128-atom
-    cells), else sampled rows bit for bit plus the invariants of the full
-    edge list (row order, reverse-edge involution, antisymmetric shifts);
-  * the routing table and dispatch tables bit for bit (cheap at any size);
-  * sampled atoms of h_out, eps, grad_h and grad_pos, each computed from the
-    atom's own neighbourhood by the oracle, within 2e-4 of the sample's
-    max-abs.
+  * S (32 cells x 128 atoms): the float64 oracle runs the whole block, so
+    every tensor is compared in full: the radius graph and the routing and
+    dispatch tables bit for bit; s, u, P (in dispatch order), h', eps, the
+    energies, dL/dh, dL/dx, the per-atom virial and the strain gradient
+    within 2e-4 of each tensor's max-abs.
+  * M and L: the structures are independent periodic cells, so the oracle
+    runs the first whole structures on their own and every row of those
+    structures is compared as at S; the graph and tables are compared in full.
+  * share (one 262144-atom cell): the whole graph against its invariants
+    plus sampled rows bit for bit, the tables in full, and sampled atoms of
+    the float outputs from each atom's own neighbourhood (oracle.local).
 """
 import sys
 
@@ -24,6 +27,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-4
+# structures of M and L that the oracle runs in full
+ORACLE_STRUCTS = {"S": None, "M": 8, "L": 8}
 
 
 def _say(msg):
@@ -42,6 +47,7 @@ def mlip():
 def rel(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
 
 
@@ -55,6 +61,19 @@ def _sample_atoms(cfg, z, n, seed=0):
     while len(picks) < n:
         picks.add(int(rng.integers(0, cfg.n_atoms)))
     return sorted(picks)[:n]
+
+
+def first_structures(inp, nb):
+    """The first nb structures as inputs of their own (structures do not interact)."""
+    sp = np.asarray(inp["struct_ptr"])
+    n = int(sp[nb])
+    q = dict(inp)
+    q["pos"] = inp["pos"][:n]
+    q["cell"] = inp["cell"][:nb]
+    q["struct_ptr"] = sp[:nb + 1].copy()
+    q["z"] = inp["z"][:n]
+    q["h"] = inp["h"][:n]
+    return q, n
 
 
 def _edge_invariants(g_gpu, N):
@@ -77,29 +96,46 @@ def _edge_invariants(g_gpu, N):
     return recv
 
 
-@pytest.mark.parametrize("name", ["S", "M", "L", "share"])
-def test_fullsize(mlip, name):
-    cfg = synth.CONFIGS[name]
-    _say(f"{name}: generating inputs ({cfg.n_atoms} atoms)")
-    inp = synth.make_inputs(cfg)
-    gup = synth.upstream_grad(cfg, inp, "energy")
-    _say(f"{name}: GPU step")
-    blk = mlip.Block(inp, device="cuda", grad_out=gup).step()
-    torch.cuda.synchronize()
-    N = cfg.n_atoms
-    E = blk.graph["n_edges"]
-    _say(f"{name}: {E} edges; checking graph invariants")
-    _edge_invariants(blk.graph, N)
+def _tables(blk, inp, cfg):
+    topk, gate = OB.route(inp["logits"], cfg.top_k)
+    exp_off, tok_atom, slot = OB.dispatch_tables(inp["z"], topk, cfg.n_experts)
+    assert np.array_equal(blk.moe["topk"].cpu().numpy(), topk)
+    assert rel(blk.moe["gate"].cpu().numpy(), gate) <= 1e-6
+    assert np.array_equal(blk.moe["exp_off"].cpu().numpy(), exp_off)
+    assert np.array_equal(blk.moe["tok_atom"].cpu().numpy(), tok_atom)
+    assert np.array_equal(blk.moe["slot"].cpu().numpy(), slot)
+    return topk, slot
 
-    # ---- graph against the oracle ----
-    if cfg.n_structs > 1:
-        _say(f"{name}: full oracle graph")
-        g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
-        assert np.array_equal(blk.graph["row_ptr"].cpu().numpy(), g["row_ptr"])
-        assert np.array_equal(blk.graph["src"].cpu().numpy(), g["src"])
-        assert np.array_equal(blk.graph["shift"].cpu().numpy()[:, :3].astype(np.int64), g["shift"])
-        assert np.array_equal(blk.graph["rev"].cpu().numpy(), g["rev"])
-        assert np.array_equal(blk.graph["geom"].cpu().numpy(), g["geom"])
+
+def _whole_rows(name, cfg, inp, gup, blk, slot):
+    """Oracle on whole structures; every row of them compared."""
+    nb = ORACLE_STRUCTS[name]
+    if nb is None:
+        q, n, nb = inp, cfg.n_atoms, cfg.n_structs
+    else:
+        q, n = first_structures(inp, nb)
+    _say(f"{name}: float64 oracle on {nb} whole structures ({n} atoms)")
+    g = OG.radius_graph(q["pos"], q["cell"], q["struct_ptr"], q["cutoff"])
+    f = OB.block_forward(q, g)
+    v = OB.block_vjp(q, g, f, gup[:n].astype(np.float64))
+    pre = OB.moe_preactivations(f["u"], q["z"], f["topk"], q["W1"])       # [n, k, H]
+    P_gpu = blk.moe["P"].cpu().numpy()[slot[:n].reshape(-1)].reshape(pre.shape)
+    cpu = lambda t: t.cpu().numpy()
+    errs = {"s": rel(cpu(blk.agg["s"])[:n], f["s"]),
+            "u": rel(cpu(blk.agg["u"])[:n], f["u"]),
+            "P": rel(P_gpu, pre),
+            "h_out": rel(cpu(blk.moe["h_out"])[:n], f["h2"]),
+            "eps": rel(cpu(blk.ro["eps"])[:n], f["eps"]),
+            "energy": rel(cpu(blk.ro["energy"])[:nb], f["E"]),
+            "grad_h": rel(cpu(blk.vjp["grad_h"])[:n], v["grad_h"]),
+            "grad_pos": rel(cpu(blk.vjp["grad_pos"])[:n], v["grad_pos"]),
+            "atom_virial": rel(cpu(blk.vjp["atom_virial"])[:n], v["atom_virial"]),
+            "grad_strain": rel(cpu(blk.vjp["grad_strain"])[:nb], OB.voigt(v["grad_strain"]))}
+    return errs
+
+
+def _sampled_rows(name, cfg, inp, gup, blk):
+    """Sampled atoms from their own neighbourhoods (the 262144-atom cell)."""
     lb = LocalBlock(inp)
     rows_atoms = _sample_atoms(cfg, inp["z"], 24, seed=1)
     rp = blk.graph["row_ptr"].cpu().numpy()
@@ -113,37 +149,55 @@ def test_fullsize(mlip, name):
         assert np.array_equal(sh[lo:hi], rw["shift"]), i
         ref_geom = np.concatenate([rw["d"].astype(np.float32), rw["r"].astype(np.float32)[:, None]], axis=1)
         assert np.array_equal(geom[lo:hi], ref_geom), i
-
-    # ---- routing and dispatch tables ----
-    _say(f"{name}: routing / dispatch tables")
-    topk, gate = OB.route(inp["logits"], cfg.top_k)
-    exp_off, tok_atom, slot = OB.dispatch_tables(inp["z"], topk, cfg.n_experts)
-    assert np.array_equal(blk.moe["topk"].cpu().numpy(), topk)
-    assert rel(blk.moe["gate"].cpu().numpy(), gate) <= 1e-6
-    assert np.array_equal(blk.moe["exp_off"].cpu().numpy(), exp_off)
-    assert np.array_equal(blk.moe["tok_atom"].cpu().numpy(), tok_atom)
-    assert np.array_equal(blk.moe["slot"].cpu().numpy(), slot)
-
-    # ---- sampled floating-point outputs ----
     fwd_atoms = _sample_atoms(cfg, inp["z"], 12, seed=2)
     _say(f"{name}: oracle forward at {len(fwd_atoms)} atoms")
     lf = lb.forward(fwd_atoms)
     errs = {"h_out": rel(blk.moe["h_out"].cpu().numpy()[fwd_atoms], lf["h2"]),
             "eps": rel(blk.ro["eps"].cpu().numpy()[fwd_atoms], lf["eps"])}
-    sp = inp["struct_ptr"]
     vjp_atoms = _sample_atoms(cfg, inp["z"], 3, seed=3)
     _say(f"{name}: oracle VJP at {len(vjp_atoms)} atoms")
     lv = lb.vjp(vjp_atoms, gup)
     errs["grad_h"] = rel(blk.vjp["grad_h"].cpu().numpy()[vjp_atoms], lv["grad_h"])
     errs["grad_pos"] = rel(blk.vjp["grad_pos"].cpu().numpy()[vjp_atoms], lv["grad_pos"])
     errs["atom_virial"] = rel(blk.vjp["atom_virial"].cpu().numpy()[vjp_atoms], lv["atom_virial"])
-    av = blk.vjp["atom_virial"].cpu().numpy().astype(np.float64)
-    gs_ref = np.stack([av[sp[b]:sp[b + 1]].sum(0) for b in range(cfg.n_structs)])
-    # per-structure energies and strain gradients are float64 sums of per-atom terms
-    eps = blk.ro["eps"].cpu().numpy().astype(np.float64)
-    e_ref = np.array([eps[sp[b]:sp[b + 1]].sum() for b in range(cfg.n_structs)])
-    errs["energy_sum"] = rel(blk.ro["energy"].cpu().numpy(), e_ref)
-    errs["strain_sum"] = rel(blk.vjp["grad_strain"].cpu().numpy(), gs_ref)
+    return errs
+
+
+@pytest.mark.parametrize("name", ["S", "M", "L", "share"])
+def test_fullsize(mlip, name):
+    cfg = synth.CONFIGS[name]
+    _say(f"{name}: generating inputs ({cfg.n_atoms} atoms)")
+    inp = synth.make_inputs(cfg)
+    gup = synth.upstream_grad(cfg, inp, "energy")
+    _say(f"{name}: GPU step")
+    blk = mlip.Block(inp, device="cuda", grad_out=gup).step()
+    torch.cuda.synchronize()
+    N = cfg.n_atoms
+    E = blk.graph["n_edges"]
+    _say(f"{name}: {E} edges; checking graph invariants")
+    _edge_invariants(blk.graph, N)
+    if cfg.n_structs > 1:
+        _say(f"{name}: full oracle graph")
+        g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
+        assert np.array_equal(blk.graph["row_ptr"].cpu().numpy(), g["row_ptr"])
+        assert np.array_equal(blk.graph["src"].cpu().numpy(), g["src"])
+        assert np.array_equal(blk.graph["shift"].cpu().numpy()[:, :3].astype(np.int64), g["shift"])
+        assert np.array_equal(blk.graph["rev"].cpu().numpy(), g["rev"])
+        assert np.array_equal(blk.graph["geom"].cpu().numpy(), g["geom"])
+    _say(f"{name}: routing / dispatch tables")
+    _, slot = _tables(blk, inp, cfg)
+    if name in ORACLE_STRUCTS:
+        errs = _whole_rows(name, cfg, inp, gup, blk, slot)
+    else:
+        errs = _sampled_rows(name, cfg, inp, gup, blk)
+        # energies and strain gradients: float64 sums of the per-atom values
+        sp = inp["struct_ptr"]
+        eps = blk.ro["eps"].cpu().numpy().astype(np.float64)
+        av = blk.vjp["atom_virial"].cpu().numpy().astype(np.float64)
+        errs["energy_sum"] = rel(blk.ro["energy"].cpu().numpy(),
+                                 [eps[sp[b]:sp[b + 1]].sum() for b in range(cfg.n_structs)])
+        errs["strain_sum"] = rel(blk.vjp["grad_strain"].cpu().numpy(),
+                                 np.stack([av[sp[b]:sp[b + 1]].sum(0) for b in range(cfg.n_structs)]))
     _say(f"{name}: errors {errs}")
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, bad
