@@ -43,6 +43,10 @@ TRAIN_METRIC = ("atoms/s per interaction-block training step (fwd, forces, energ
                 "parameter gradients) on 1 MI355X")
 MFMA_FP32_PEAK_TFLOPS = 157.3      # MI355X dense FP32 matrix peak
 HBM_PEAK_GBS = 8000.0
+# Unpacked FP32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA) x 2.4 GHz.  The
+# 157.3 TFLOP/s vector figure counts packed FP32 (two lanes per instruction), which this
+# library does not generate.
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 EXPERT_CLASSES = ("gemm_expert_up", "gemm_expert_down", "gemm_expert_vjp_down", "gemm_expert_vjp_up")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_expert_traffic_S.txt")
 
@@ -79,17 +83,39 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
+def host_cpu():
+    """The host's CPUs as this process sees them: usable cores and the model name."""
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return ncpu, model
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(cfg, inp, n_structs: int, full: bool = False):
     """The float64 NumPy oracle on the first n_structs structures of the workload."""
     import numpy as np
     from oracle import attention as OA
     from oracle import block as OB
     from oracle import graph as OG
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
+    ncpu, model = host_cpu()
     n = int(inp["struct_ptr"][n_structs])
     sub = dict(inp)
     sub["pos"] = inp["pos"][:n]
@@ -111,7 +137,11 @@ def cpu_baseline(cfg, inp, n_structs: int, full: bool = False):
             "sample": f"first {n_structs} of {cfg.n_structs} structures ({n} atoms, "
                       f"{gr['src'].size} edges) of the {cfg.name} workload, float64 NumPy oracle"
                       f"{' of the complete block' if full else ''}, graph + forward + VJP in "
-                      f"{dt:.2f} s"}
+                      f"{dt:.2f} s",
+            "host_cpus": ncpu, "cpu_model": model, "blas_threads": int(threads),
+            "threads_note": "cores = the BLAS pool that runs the oracle's matrix products; its "
+                            "scatter-adds (np.add.at), routing loop and graph loops run on one "
+                            "thread"}
 
 
 def cpu_baseline_train(cfg, inp, n_structs: int, Ebar, Fbar):
@@ -128,10 +158,60 @@ def cpu_baseline_train(cfg, inp, n_structs: int, Ebar, Fbar):
     gr = OG.radius_graph(sub["pos"], sub["cell"], sub["struct_ptr"], sub["cutoff"])
     TR.loss_grads(sub, gr, np.asarray(Ebar[:n_structs], np.float64), np.asarray(Fbar[:n], np.float64))
     dt = time.perf_counter() - t0
+    ncpu, model = host_cpu()
     return {"value": n / dt, "unit": "atoms/s", "cores": int(torch.get_num_threads()), "kind": "oracle",
+            "host_cpus": ncpu, "cpu_model": model,
             "sample": f"first {n_structs} of {cfg.n_structs} structures ({n} atoms, {gr['src'].size} "
                       f"edges) of the {cfg.name} workload, float64 PyTorch-autograd oracle of the "
                       f"training gradient (graph, energy, forces, all parameter gradients) in {dt:.2f} s"}
+
+
+def memory_kernel_fractions(cfg, E, kernel_ms):
+    """Position of the core block's memory- and vector-bound kernels against their rooflines,
+    from the per-class times of the breakdown steps (ms per step).
+
+    Algorithmic work per step (N atoms, E edges, k experts per atom):
+      combine (forward + VJP, 2 launches): reads k expert rows + u, writes h', per atom:
+        2 x (k + 2) x 4 Dn bytes;
+      embed_aggregate (1 launch): 16 basis FMAs + 1 modulating FMA per edge and channel,
+        2 x 17 x E x De FLOP; HBM: 20 B of geometry and index per edge, the s row read
+        (the gathered s rows counted once) and the a row written per atom (8 De B);
+      edge_vjp (1 launch): about 41 FMA per edge and channel (e and de/dr rebuilt from the 16
+        radial terms, the sender gradient, the edge scalar), 2 x 41 x E x De FLOP; HBM:
+        20 B per edge, abar and s read and sbar written per atom (12 De B);
+      route_dispatch (route + dispatch kernels): z read, tok_atom and slot written,
+        (4 + 8 k) N bytes (latency-bound: the fraction only shows how far from HBM it is).
+    """
+    N, k, De, Dn = cfg.n_atoms, cfg.top_k, cfg.d_edge, cfg.d_node
+    res = {}
+
+    def hbm(name, nbytes):
+        ms = kernel_ms.get(name)
+        if not ms:
+            return
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bound": "hbm", "bytes_per_step": int(nbytes), "ms_per_step": ms,
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    def valu(name, flop, nbytes):
+        ms = kernel_ms.get(name)
+        if not ms:
+            return
+        tf = flop / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bound": "alu", "flop_per_step": flop, "ms_per_step": ms,
+                     "achieved": round(tf, 2), "peak": round(VALU_FP32_PEAK_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(tf / VALU_FP32_PEAK_TFLOPS, 4),
+                     "hbm_bytes_per_step": int(nbytes), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    hbm("combine", 2 * (k + 2) * 4.0 * Dn * N)
+    hbm("route_dispatch", (4 + 8 * k) * float(N))
+    valu("embed_aggregate", 2.0 * 17 * E * De, 20.0 * E + 8.0 * De * N)
+    valu("edge_vjp", 2.0 * 41 * E * De, 20.0 * E + 12.0 * De * N)
+    res["note"] = ("alu peak = unpacked FP32 vector rate (256 CUs x 4 SIMD x 16 lanes x 2 FLOP x "
+                   "2.4 GHz); times from the breakdown steps")
+    return res
 
 
 def main():
@@ -236,6 +316,18 @@ def main():
     N = cfg.n_atoms
     value = N * args.steps / wall
 
+    # the same step on the previous step's graph, as a model of several blocks reuses one graph
+    nog_steps = 0 if train else args.steps
+    nog_ms = None
+    if nog_steps:
+        blk.step(build_graph=False)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(nog_steps):
+            blk.step(build_graph=False)
+        torch.cuda.synchronize()
+        nog_ms = (time.perf_counter() - t1) * 1e3 / nog_steps
+
     # dominant kernel: the matrix-core class with the largest summed time
     # (with --block full each class has two launches per step, one per MoE layer).
     # Algorithmic flops per launch: 2 M Dn H for every expert GEMM (M = N k
@@ -292,6 +384,20 @@ def main():
                                    "timed; the timed steps time only the matrix-core GEMM classes",
         "roofline": roof,
     }
+    if nog_ms is not None:
+        out["ms_per_step_without_graph_build"] = round(nog_ms, 4)
+    moe_tabs = [blk.moe] if not (full or stack) else ([blk.moe0, blk.moe] if full else [])
+    if moe_tabs:
+        loads = []
+        for tab in moe_tabs:
+            cnt = np.diff(tab["exp_off"].cpu().numpy().astype(np.int64))
+            act = cnt[cnt > 0]
+            loads.append({"max": int(cnt.max()), "mean_active": round(float(act.mean()), 1),
+                          "min_active": int(act.min()), "active_experts": int(act.size),
+                          "mean_all": round(float(cnt.mean()), 1)})
+        out["expert_tokens"] = loads[0] if len(loads) == 1 else {"moe0": loads[0], "moe1": loads[1]}
+    if args.block == "core" and breakdown_steps:
+        out["memory_kernels"] = memory_kernel_fractions(cfg, E, kernel_ms)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
     if full or stack:
         out["config"]["heads"] = cfg.n_heads
