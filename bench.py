@@ -226,7 +226,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-structs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--breakdown-steps", type=int, default=2,
+    ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="untimed steps after the timed ones, with every kernel launch timed, for "
                          "kernel_ms_per_step")
     args = ap.parse_args()
@@ -300,17 +300,19 @@ def main():
     wall = time.perf_counter() - t0
     mlip.profile_enable(False)
     prof = mlip.profile_read()
-    # per-class breakdown from extra, untimed steps with every launch timed
+    # per-class breakdown from extra, untimed steps with every launch timed, read step by step;
+    # each class reports the median over the steps, so one disturbed step does not move it
     breakdown_steps = max(args.breakdown_steps, 0)
-    mlip.profile_reset()
     mlip.profile_select(None)
-    if breakdown_steps:
+    per_step = []
+    for _ in range(breakdown_steps):
+        mlip.profile_reset()
         mlip.profile_enable(True)
-        for _ in range(breakdown_steps):
-            one_step()
+        one_step()
         torch.cuda.synchronize()
         mlip.profile_enable(False)
-    prof_all = mlip.profile_read()
+        per_step.append(mlip.profile_read())
+    mlip.profile_reset()
 
     ms_per_step = wall * 1e3 / args.steps
     N = cfg.n_atoms
@@ -363,8 +365,11 @@ def main():
     if dom == "gemm_wgrad":
         roof["flop_per_launch_note"] = "mean over the step's weight-gradient launches"
 
-    kernel_ms = {name: round(v["total_ms"] / breakdown_steps, 4)
-                 for name, v in prof_all.items() if v["launches"] and breakdown_steps}
+    kernel_ms = {}
+    if per_step:
+        for name in per_step[0]:
+            if per_step[0][name]["launches"]:
+                kernel_ms[name] = round(float(np.median([p[name]["total_ms"] for p in per_step])), 4)
     out = {
         "metric": TRAIN_METRIC if train else METRIC, "value": round(value, 1), "unit": "atoms/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -380,8 +385,8 @@ def main():
         "edges_per_s": round(E * args.steps / wall, 1),
         "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
         "kernel_ms_per_step": kernel_ms,
-        "kernel_ms_per_step_note": f"from {breakdown_steps} untimed steps after the timed ones, every launch "
-                                   "timed; the timed steps time only the matrix-core GEMM classes",
+        "kernel_ms_per_step_note": f"median over {breakdown_steps} untimed steps after the timed ones, every "
+                                   "launch timed; the timed steps time only the matrix-core GEMM classes",
         "roofline": roof,
     }
     if nog_ms is not None:
