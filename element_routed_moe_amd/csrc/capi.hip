@@ -4,6 +4,7 @@
 // buffers out of the caller's workspace and enqueues its kernels on the
 // caller's stream.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -403,6 +404,37 @@ int aggregate_core(const int32_t *row_ptr, const int32_t *src, const float *geom
   return launch_gemm(g2, false, EPI_RESID, K_GEMM_DENSE, stream);
 }
 
+// ------------------------------------------- library-owned scratch memory --
+// Scratch of mlip_aggregate_static: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once, with that GPU current, and
+// kept in g_scratch_addr.
+constexpr size_t kAggScratchBytes = MLIP_AGGREGATE_STATIC_MAX_BYTES;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kAggScratchBytes];
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[kMaxScratchDevices];
+
+int scratch_address(void **out) {
+  int dev = -1;
+  MLIP_HIP(hipGetDevice(&dev));
+  MLIP_CHECK_ARG(dev >= 0 && dev < kMaxScratchDevices, "device %d outside the %d supported", dev,
+                 kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    MLIP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) {
+      set_error("hipGetSymbolAddress gave a null address for the scratch array");
+      return MLIP_ERR_HIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MLIP_OK;
+}
+
 }  // namespace
 }  // namespace mlip
 
@@ -429,6 +461,30 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
     return rc;
   if (n_atoms == 0) return MLIP_OK;
   AggWs w = carve_agg(ws, n_atoms, d_edge, d_node, nullptr);
+  return aggregate_core(row_ptr, src, geom, n_atoms, h, W_e, W_d, W_u, d_edge, d_node, cutoff, e, s,
+                        u, w, stream);
+}
+
+int mlip_aggregate_static(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                          int32_t n_atoms, int64_t n_edges, const float *h, const float *W_e,
+                          const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge,
+                          int32_t d_node, float cutoff, float *e, float *s, float *u,
+                          void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (int rc = check_aggregate_args(row_ptr, src, geom, n_atoms, n_edges, h, W_e, W_d, W_u, n_rbf,
+                                    d_edge, d_node, cutoff, e, s, u))
+    return rc;
+  const size_t need = mlip_aggregate_workspace_size(n_atoms, d_edge, d_node);
+  if (need > kAggScratchBytes) {
+    set_error("mlip_aggregate_static needs %zu bytes of scratch for %d atoms x d_edge %d; the "
+              "library's static scratch holds %zu (use mlip_aggregate with a workspace)",
+              need, n_atoms, d_edge, kAggScratchBytes);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  if (n_atoms == 0) return MLIP_OK;
+  void *base = nullptr;
+  if (int rc = scratch_address(&base)) return rc;
+  AggWs w = carve_agg(base, n_atoms, d_edge, d_node, nullptr);
   return aggregate_core(row_ptr, src, geom, n_atoms, h, W_e, W_d, W_u, d_edge, d_node, cutoff, e, s,
                         u, w, stream);
 }

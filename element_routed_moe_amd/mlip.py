@@ -51,6 +51,8 @@ _SIGS = {
     "mlip_aggregate_workspace_size": (_sz, [_i32, _i32, _i32]),
     "mlip_aggregate": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                  _p, _p, _p, _p, _sz, _p]),
+    "mlip_aggregate_static": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+                                        _p, _p, _p, _p]),
     "mlip_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "mlip_moe_forward": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
@@ -216,6 +218,22 @@ def mlip_aggregate(graph, h, W_e, W_d, W_u, cutoff: float, out: Optional[Dict] =
                                _ptr(h), _ptr(W_e), _ptr(W_d), _ptr(W_u), int(W_e.shape[0]), De, Dn,
                                float(cutoff), _ptr(out["e"]), _ptr(out["s"]), _ptr(out["u"]),
                                _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+AGGREGATE_STATIC_MAX_BYTES = 32 << 20    # MLIP_AGGREGATE_STATIC_MAX_BYTES of mlip.h
+
+
+def mlip_aggregate_static(graph, h, W_e, W_d, W_u, cutoff: float, out: Dict) -> Dict[str, torch.Tensor]:
+    """mlip_aggregate on the library's own scratch (no workspace): the caller
+    passes preallocated outputs out["e"] (or None), out["s"], out["u"]."""
+    N, Dn = int(h.shape[0]), int(h.shape[1])
+    De = int(W_e.shape[1])
+    E = int(graph["n_edges"])
+    _check(_lib.mlip_aggregate_static(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N,
+                                      E, _ptr(h), _ptr(W_e), _ptr(W_d), _ptr(W_u), int(W_e.shape[0]), De,
+                                      Dn, float(cutoff), _ptr(out.get("e")), _ptr(out["s"]),
+                                      _ptr(out["u"]), _stream()))
     return out
 
 

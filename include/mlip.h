@@ -166,6 +166,32 @@ int mlip_aggregate(const int32_t *row_ptr, const int32_t *src, const float *geom
                    void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * mlip_aggregate without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * mlip_aggregate, minus (ws, ws_bytes): the scratch (the aggregated edge
+ * messages a and the split-K parts of h @ W_d) lives in a device array of
+ * the library, MLIP_AGGREGATE_STATIC_MAX_BYTES per GPU, held from the first
+ * call on that GPU until the process ends.  The call allocates nothing and
+ * never clears the array: every byte a call reads it has written itself.
+ *
+ * The array is one per GPU and shared by every call on it: calls that
+ * overlap on one GPU (different streams or host threads) race on it.  Call
+ * with the stream's device current.
+ *
+ * Errors: as mlip_aggregate, plus MLIP_ERR_UNSUPPORTED, before any device
+ * call, when the scratch the call needs (mlip_aggregate_workspace_size(
+ * n_atoms, d_edge, d_node)) exceeds MLIP_AGGREGATE_STATIC_MAX_BYTES.  The
+ * S workload (4096 atoms, d_edge 384, d_node 2560) needs 18 MiB.
+ * ------------------------------------------------------------------------ */
+#define MLIP_AGGREGATE_STATIC_MAX_BYTES ((size_t)32 << 20)
+int mlip_aggregate_static(const int32_t *row_ptr, const int32_t *src, const float *geom,
+                          int32_t n_atoms, int64_t n_edges, const float *h, const float *W_e,
+                          const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge,
+                          int32_t d_node, float cutoff, float *e, float *s, float *u,
+                          void *stream);
+
+/* ------------------------------------------------------------------------
  * Feature-update mixture of experts with static element-type routing
  * ([news], [review] 3.2: each element type activates its own top-k experts,
  * independently of the coordinates).

@@ -91,6 +91,21 @@ def test_graph_reverse_rejects_bad_args(mlip):
     assert "aligned" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
+def test_aggregate_static_rejects_oversize_on_host(mlip):
+    """The scratch limit is checked before any device call (runs without a GPU)."""
+    L = mlip._lib
+    f = C.c_void_p(256)
+    N, De, Dn = 8192, 384, 2560
+    assert L.mlip_aggregate_workspace_size(N, De, Dn) > mlip.AGGREGATE_STATIC_MAX_BYTES
+    rc = L.mlip_aggregate_static(f, f, f, N, 1000, f, f, f, f, 16, De, Dn, 6.0, f, f, f, None)
+    assert "scratch" in _err(mlip, rc, mlip.MLIP_ERR_UNSUPPORTED)
+    rc = L.mlip_aggregate_static(None, f, f, N, 1000, f, f, f, f, 16, De, Dn, 6.0, f, f, f, None)
+    _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    hdr = open(HEADER).read()
+    assert "#define MLIP_AGGREGATE_STATIC_MAX_BYTES ((size_t)32 << 20)" in hdr
+    assert mlip.AGGREGATE_STATIC_MAX_BYTES == 32 << 20
+
+
 def test_aggregate_and_moe_reject_bad_args(mlip):
     L = mlip._lib
     f = C.c_void_p(256)
