@@ -80,10 +80,16 @@ __device__ inline void stc(float *p, const float (&x)[CPL]) {
   }
 }
 
-// Sum over the lph lanes of one head (aligned power-of-two lane groups).
+// Sum over the lph lanes of one head (aligned power-of-two lane groups); LPH
+// is the lane count when it is fixed at compile time, 0 when it is not.
+template <int LPH>
 __device__ inline float head_sum(float v, int lph) {
-  for (int d = lph >> 1; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  if constexpr (LPH > 0) {
+    return group_sum<LPH>(v);
+  } else {
+    for (int d = lph >> 1; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+  }
 }
 
 __device__ inline float wave_sum(float v) {
@@ -134,7 +140,13 @@ __device__ inline Lanes lane_map(int lane, int nh, int lph) {
 }
 
 // ------------------------------------------------------------- forward ---
+// The sender rows of the next UNROLL edges are gathered into a second set of
+// registers while the current ones are used (two sets where the register
+// budget of two waves per SIMD allows it, i.e. up to 6 channels per lane).
 template <int CPL>
+constexpr bool kPrefetch = CPL <= 6;
+
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_fwd_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ Wa_e,
@@ -164,6 +176,8 @@ __global__ void __launch_bounds__(64) attn_fwd_kernel(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   float m = -INFINITY, Z = 0.f;
+  constexpr int NB = kPrefetch<CPL> ? 2 : 1;
+  float kj[NB][UNROLL][CPL], vj[NB][UNROLL][CPL];
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
   for (int e0 = r0; e0 < r1; e0 += CHUNK) {
     const int n = min(CHUNK, r1 - e0);
@@ -183,15 +197,16 @@ __global__ void __launch_bounds__(64) attn_fwd_kernel(
       jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
-    for (int mm = 0; mm < n; mm += UNROLL) {
-      float kj[UNROLL][CPL], vj[UNROLL][CPL];
+    // gather the k and v rows of edges mm .. mm + UNROLL - 1 into set b
+    auto fetch = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int me = min(mm + u, n - 1);
-        const float *row = qkv + int64_t(jj[me]) * ld + L.c0;
-        ldc<CPL>(row + Da, kj[u]);
-        ldc<CPL>(row + 2 * Da, vj[u]);
+        const float *row = qkv + int64_t(jj[min(mm + u, n - 1)]) * ld + L.c0;
+        ldc<CPL>(row + Da, kj[b][u]);
+        ldc<CPL>(row + 2 * Da, vj[b][u]);
       }
+    };
+    auto edges = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         if (mm + u < n) {
@@ -200,16 +215,30 @@ __global__ void __launch_bounds__(64) attn_fwd_kernel(
           basis_map<CPL>(phi[me], w, e);
           float part = 0.f;
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) part += q[c] * kj[u][c] * e[c];
-          const float s = head_sum(part, lph);
+          for (int c = 0; c < CPL; ++c) part += q[c] * kj[b][u][c] * e[c];
+          const float s = head_sum<LPH>(part, lph);
           const float mn = fmaxf(m, s);
           const float sc = __expf(m - mn);
           const float wt = fcs[me] * __expf(s - mn);
           Z = Z * sc + wt;
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * sc + wt * (vj[u][c] * e[c]);
+          for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * sc + wt * (vj[b][u][c] * e[c]);
           m = mn;
         }
+      }
+    };
+    if constexpr (NB == 2) {
+      fetch(0, 0);
+      for (int mm = 0; mm < n; mm += 2 * UNROLL) {
+        if (mm + UNROLL < n) fetch(1, mm + UNROLL);
+        edges(0, mm);
+        if (mm + 2 * UNROLL < n) fetch(0, mm + 2 * UNROLL);
+        edges(1, mm + UNROLL);
+      }
+    } else {
+      for (int mm = 0; mm < n; mm += UNROLL) {
+        fetch(0, mm);
+        edges(0, mm);
       }
     }
     __syncthreads();
@@ -225,7 +254,10 @@ __global__ void __launch_bounds__(64) attn_fwd_kernel(
 }
 
 // ------------------------------------------------ gradient: receiver rows --
-template <int CPL>
+// dL/dr of an edge sums over all channels: each 16-lane row sums its lanes with
+// DPP moves, the row totals go to LDS, and after the chunk lane e adds the four
+// totals of its edge and stores them (one coalesced store per chunk).
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const float4 *__restrict__ geom, int n_atoms, const float *__restrict__ Wa_e,
@@ -237,6 +269,7 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
   __shared__ float4 dph[CHUNK][KQ];   // d(f_c phi_k)/dr
   __shared__ float fcs[CHUNK], dfcs[CHUNK];
   __shared__ int jj[CHUNK];
+  __shared__ float4 rowc[CHUNK];      // per edge: the four 16-lane rows' dL/dr parts
   const int lane = threadIdx.x;
   const int64_t blk = xcd_block(n_atoms);
   if (blk < 0) return;
@@ -261,15 +294,19 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
     ob[c] *= on;
     bpart += ob[c] * oo[c];
   }
-  const float beta = head_sum(bpart, lph);
+  const float beta = head_sum<LPH>(bpart, lph);
   const float2 st = stats[int64_t(i) * nh + L.t];
   const float m = L.active ? st.x : 0.f;
   const float invZ = (L.active && st.y > 0.f) ? 1.f / st.y : 0.f;
   const bool head_lead = L.active && lane == L.t * lph;
+  const bool row_lead = (lane & 15) == 0;
+  float *rowc_f = reinterpret_cast<float *>(rowc);
 
   float qb[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) qb[c] = 0.f;
+  constexpr int NB = kPrefetch<CPL> ? 2 : 1;
+  float kj[NB][UNROLL][CPL], vj[NB][UNROLL][CPL];
   const int r0 = row_ptr[i], r1 = row_ptr[i + 1];
   for (int e0 = r0; e0 < r1; e0 += CHUNK) {
     const int n = min(CHUNK, r1 - e0);
@@ -300,30 +337,31 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
       jj[lane] = int(MLIP_IDX(src[e0 + lane], n_atoms, "sender"));
     }
     __syncthreads();
-    for (int mm = 0; mm < n; mm += UNROLL) {
-      float kj[UNROLL][CPL], vj[UNROLL][CPL];
+    auto fetch = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int me = min(mm + u, n - 1);
-        const float *row = qkv + int64_t(jj[me]) * ld + L.c0;
-        ldc<CPL>(row + Da, kj[u]);
-        ldc<CPL>(row + 2 * Da, vj[u]);
+        const float *row = qkv + int64_t(jj[min(mm + u, n - 1)]) * ld + L.c0;
+        ldc<CPL>(row + Da, kj[b][u]);
+        ldc<CPL>(row + 2 * Da, vj[b][u]);
       }
+    };
+    auto edges = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         if (mm + u < n) {
           const int me = mm + u;
+          const float *kk = kj[b][u], *vv = vj[b][u];
           float e[CPL], de[CPL];
           basis_map<CPL>(phi[me], w, e);
           basis_map<CPL>(dph[me], w, de);
           float ps = 0.f, pa = 0.f;
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
-            ps += q[c] * kj[u][c] * e[c];
-            pa += ob[c] * vj[u][c] * e[c];
+            ps += q[c] * kk[c] * e[c];
+            pa += ob[c] * vv[c] * e[c];
           }
-          const float s = head_sum(ps, lph);
-          const float ab = head_sum(pa, lph);
+          const float s = head_sum<LPH>(ps, lph);
+          const float ab = head_sum<LPH>(pa, lph);
           const float wt = __expf(s - m);
           const float alpha = fcs[me] * wt * invZ;
           const float diff = ab - beta;
@@ -331,20 +369,38 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
           float cp = head_lead ? wt * invZ * diff * dfcs[me] : 0.f;
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
-            cp += (g * q[c] * kj[u][c] + alpha * ob[c] * vj[u][c]) * de[c];
-            qb[c] += g * kj[u][c] * e[c];
+            cp += (g * q[c] * kk[c] + alpha * ob[c] * vv[c]) * de[c];
+            qb[c] += g * kk[c] * e[c];
           }
-          const float ce = wave_sum(cp);
+          const float cr = group_sum<16>(cp);
+          if (row_lead) rowc_f[4 * me + (lane >> 4)] = cr;
           const int64_t eg = int64_t(e0 + me);
-          if (lane == 0) edge_c[eg] = ce;
           if (head_lead) {
             edge_g[eg * nh + L.t] = g;
             edge_a[eg * nh + L.t] = alpha;
           }
         }
       }
+    };
+    if constexpr (NB == 2) {
+      fetch(0, 0);
+      for (int mm = 0; mm < n; mm += 2 * UNROLL) {
+        if (mm + UNROLL < n) fetch(1, mm + UNROLL);
+        edges(0, mm);
+        if (mm + 2 * UNROLL < n) fetch(0, mm + 2 * UNROLL);
+        edges(1, mm + UNROLL);
+      }
+    } else {
+      for (int mm = 0; mm < n; mm += UNROLL) {
+        fetch(0, mm);
+        edges(0, mm);
+      }
     }
     __syncthreads();
+    if (lane < n) {
+      const float4 rc4 = rowc[lane];
+      edge_c[e0 + lane] = (rc4.x + rc4.y) + (rc4.z + rc4.w);
+    }
   }
   if (L.active) {
 #pragma unroll
@@ -354,7 +410,7 @@ __global__ void __launch_bounds__(64) attn_vjp_recv_kernel(
 }
 
 // -------------------------------------------------- gradient: sender rows --
-template <int CPL>
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ src,
     const int32_t *__restrict__ rev, const float4 *__restrict__ geom, int n_atoms,
@@ -382,6 +438,8 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
   // lane-private partial force and virial over the edges this lane set up
   float fx = 0.f, fy = 0.f, fz = 0.f;
   float vir[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int NB = kPrefetch<CPL> ? 2 : 1;
+  float qi[NB][UNROLL][CPL], oi[NB][UNROLL][CPL], gg[NB][UNROLL], aa[NB][UNROLL];
   const int r0 = row_ptr[j], r1 = row_ptr[j + 1];
   for (int e0 = r0; e0 < r1; e0 += CHUNK) {
     const int n = min(CHUNK, r1 - e0);
@@ -417,18 +475,21 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
       vir[5] += p * gm.x * gm.y;
     }
     __syncthreads();
-    for (int mm = 0; mm < n; mm += UNROLL) {
-      float qi[UNROLL][CPL], oi[UNROLL][CPL], gg[UNROLL], aa[UNROLL];
+    // the q and obar rows of the senders and the reverse edges' weights of
+    // edges mm .. mm + UNROLL - 1, into set b
+    auto fetch = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int me = min(mm + u, n - 1);
         const int64_t ii = jj[me];
-        ldc<CPL>(qkv + ii * ld + L.c0, qi[u]);
-        ldc<CPL>(obar + ii * Da + L.c0, oi[u]);
+        ldc<CPL>(qkv + ii * ld + L.c0, qi[b][u]);
+        ldc<CPL>(obar + ii * Da + L.c0, oi[b][u]);
         const int64_t re = rr[me];
-        gg[u] = edge_g[re * nh + L.t];
-        aa[u] = edge_a[re * nh + L.t];
+        gg[b][u] = edge_g[re * nh + L.t];
+        aa[b][u] = edge_a[re * nh + L.t];
       }
+    };
+    auto edges = [&](int b, int mm) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         if (mm + u < n) {
@@ -436,10 +497,24 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
           basis_map<CPL>(phi[mm + u], w, e);
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
-            kb[c] += gg[u] * qi[u][c] * e[c];
-            vb[c] += aa[u] * oi[u][c] * e[c];
+            kb[c] += gg[b][u] * qi[b][u][c] * e[c];
+            vb[c] += aa[b][u] * oi[b][u][c] * e[c];
           }
         }
+      }
+    };
+    if constexpr (NB == 2) {
+      fetch(0, 0);
+      for (int mm = 0; mm < n; mm += 2 * UNROLL) {
+        if (mm + UNROLL < n) fetch(1, mm + UNROLL);
+        edges(0, mm);
+        if (mm + 2 * UNROLL < n) fetch(0, mm + 2 * UNROLL);
+        edges(1, mm + UNROLL);
+      }
+    } else {
+      for (int mm = 0; mm < n; mm += UNROLL) {
+        fetch(0, mm);
+        edges(0, mm);
       }
     }
     __syncthreads();
@@ -466,21 +541,21 @@ __global__ void __launch_bounds__(64) attn_vjp_send_kernel(
   }
 }
 
-template <int CPL>
+template <int CPL, int LPH>
 int launch_all(int which, const AttnArgs &a, hipStream_t stream) {
   const dim3 grid(unsigned(padded_grid(a.n_atoms))), block(64);
   const float4 *g4 = reinterpret_cast<const float4 *>(a.geom);
   if (which == 0) {
-    attn_fwd_kernel<CPL><<<grid, block, 0, stream>>>(a.row_ptr, a.src, g4, a.n_atoms, a.Wa_e, a.qkv,
+    attn_fwd_kernel<CPL, LPH><<<grid, block, 0, stream>>>(a.row_ptr, a.src, g4, a.n_atoms, a.Wa_e, a.qkv,
                                                      a.Da, a.nh, a.lph, a.rc, a.o,
                                                      reinterpret_cast<float2 *>(a.stats));
   } else if (which == 1) {
-    attn_vjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(
+    attn_vjp_recv_kernel<CPL, LPH><<<grid, block, 0, stream>>>(
         a.row_ptr, a.src, g4, a.n_atoms, a.Wa_e, a.qkv, a.o,
         reinterpret_cast<const float2 *>(a.stats), a.obar, a.Da, a.nh, a.lph, a.rc, a.qkv_bar,
         a.edge_g, a.edge_a, a.edge_c);
   } else {
-    attn_vjp_send_kernel<CPL><<<grid, block, 0, stream>>>(
+    attn_vjp_send_kernel<CPL, LPH><<<grid, block, 0, stream>>>(
         a.row_ptr, a.src, a.rev, g4, a.n_atoms, a.Wa_e, a.qkv, a.obar, a.edge_g, a.edge_a,
         a.edge_c, a.Da, a.nh, a.lph, a.rc, a.accumulate, a.qkv_bar, a.grad_pos, a.atom_virial);
   }
@@ -488,14 +563,18 @@ int launch_all(int which, const AttnArgs &a, hipStream_t stream) {
   return MLIP_OK;
 }
 
+// Layouts whose head width is fixed at compile time (head sums unrolled into
+// DPP moves): 8 heads of 48 channels (6 per lane, 8 lanes per head) and 4
+// heads of 128 (8 per lane, 16 lanes per head), the widths of the S and M/L
+// models.  Every other layout sums heads in a loop over lph.
 int dispatch(int which, const AttnArgs &a, hipStream_t stream) {
   switch (a.cpl) {
-    case 1: return launch_all<1>(which, a, stream);
-    case 2: return launch_all<2>(which, a, stream);
-    case 3: return launch_all<3>(which, a, stream);
-    case 4: return launch_all<4>(which, a, stream);
-    case 6: return launch_all<6>(which, a, stream);
-    case 8: return launch_all<8>(which, a, stream);
+    case 1: return launch_all<1, 0>(which, a, stream);
+    case 2: return launch_all<2, 0>(which, a, stream);
+    case 3: return launch_all<3, 0>(which, a, stream);
+    case 4: return launch_all<4, 0>(which, a, stream);
+    case 6: return a.lph == 8 ? launch_all<6, 8>(which, a, stream) : launch_all<6, 0>(which, a, stream);
+    case 8: return a.lph == 16 ? launch_all<8, 16>(which, a, stream) : launch_all<8, 0>(which, a, stream);
     default: break;
   }
   set_error("no attention lane layout for %d channels per lane", a.cpl);
@@ -557,7 +636,7 @@ __device__ inline void tan_radial(const AttnTanArgs &a, const float4 *geom, cons
   rdot[lane] = rd;
 }
 
-template <int CPL>
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_jvp_kernel(AttnTanArgs a) {
   __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
   __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
@@ -617,8 +696,8 @@ __global__ void __launch_bounds__(64) attn_jvp_kernel(AttnTanArgs a) {
         ps += q[c] * kj[c] * e[c];
         psd += qd[c] * kj[c] * e[c] + q[c] * kd[c] * e[c] + q[c] * kj[c] * de[c];
       }
-      const float s = head_sum(ps, lph);
-      const float sd = head_sum(psd, lph);
+      const float s = head_sum<LPH>(ps, lph);
+      const float sd = head_sum<LPH>(psd, lph);
       const float wt = __expf(s - m);
       const float al = fcs[me] * wt * invZ;
       const float fw = fdot[me] * wt * invZ;
@@ -639,7 +718,7 @@ __global__ void __launch_bounds__(64) attn_jvp_kernel(AttnTanArgs a) {
   }
 }
 
-template <int CPL>
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
   __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
   __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
@@ -680,8 +759,8 @@ __global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
       qbd[c] = 0.f;
     }
   }
-  const float beta = head_sum(bp, lph);
-  const float betad = head_sum(bpd, lph);
+  const float beta = head_sum<LPH>(bp, lph);
+  const float betad = head_sum<LPH>(bpd, lph);
   const float2 st = reinterpret_cast<const float2 *>(a.stats)[int64_t(i) * nh + L.t];
   const float m = L.active ? st.x : 0.f;
   const float invZ = (L.active && st.y > 0.f) ? 1.f / st.y : 0.f;
@@ -716,10 +795,10 @@ __global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
         pa += ob[c] * vj[c] * e[c];
         pad += obd[c] * vj[c] * e[c] + ob[c] * vd[c] * e[c] + ob[c] * vj[c] * de[c];
       }
-      const float s = head_sum(ps, lph);
-      const float sd = head_sum(psd, lph);
-      const float ab = head_sum(pa, lph);
-      const float abd = head_sum(pad, lph);
+      const float s = head_sum<LPH>(ps, lph);
+      const float sd = head_sum<LPH>(psd, lph);
+      const float ab = head_sum<LPH>(pa, lph);
+      const float abd = head_sum<LPH>(pad, lph);
       const float wt = __expf(s - m);
       const float al = fcs[me] * wt * invZ;
       const float ald = al * sd + fdot[me] * wt * invZ - al * T;
@@ -755,7 +834,7 @@ __global__ void __launch_bounds__(64) attn_tvjp_recv_kernel(AttnTanArgs a) {
   }
 }
 
-template <int CPL>
+template <int CPL, int LPH>
 __global__ void __launch_bounds__(64) attn_tvjp_send_kernel(AttnTanArgs a) {
   __shared__ float4 phi[CHUNK][KQ], dph[CHUNK][KQ];
   __shared__ float fcs[CHUNK], fdot[CHUNK], rdot[CHUNK];
@@ -819,24 +898,24 @@ __global__ void __launch_bounds__(64) attn_tvjp_send_kernel(AttnTanArgs a) {
   }
 }
 
-template <int CPL>
+template <int CPL, int LPH>
 int launch_tan(int which, const AttnTanArgs &a, hipStream_t stream) {
   const dim3 grid(unsigned(padded_grid(a.n_atoms))), block(64);
-  if (which == 0) attn_jvp_kernel<CPL><<<grid, block, 0, stream>>>(a);
-  else if (which == 1) attn_tvjp_recv_kernel<CPL><<<grid, block, 0, stream>>>(a);
-  else attn_tvjp_send_kernel<CPL><<<grid, block, 0, stream>>>(a);
+  if (which == 0) attn_jvp_kernel<CPL, LPH><<<grid, block, 0, stream>>>(a);
+  else if (which == 1) attn_tvjp_recv_kernel<CPL, LPH><<<grid, block, 0, stream>>>(a);
+  else attn_tvjp_send_kernel<CPL, LPH><<<grid, block, 0, stream>>>(a);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
 
 int dispatch_tan(int which, const AttnTanArgs &a, hipStream_t stream) {
   switch (a.cpl) {
-    case 1: return launch_tan<1>(which, a, stream);
-    case 2: return launch_tan<2>(which, a, stream);
-    case 3: return launch_tan<3>(which, a, stream);
-    case 4: return launch_tan<4>(which, a, stream);
-    case 6: return launch_tan<6>(which, a, stream);
-    case 8: return launch_tan<8>(which, a, stream);
+    case 1: return launch_tan<1, 0>(which, a, stream);
+    case 2: return launch_tan<2, 0>(which, a, stream);
+    case 3: return launch_tan<3, 0>(which, a, stream);
+    case 4: return launch_tan<4, 0>(which, a, stream);
+    case 6: return a.lph == 8 ? launch_tan<6, 8>(which, a, stream) : launch_tan<6, 0>(which, a, stream);
+    case 8: return a.lph == 16 ? launch_tan<8, 16>(which, a, stream) : launch_tan<8, 0>(which, a, stream);
     default: break;
   }
   set_error("no attention lane layout for %d channels per lane", a.cpl);

@@ -92,6 +92,7 @@ enum KClass {
   K_EDGE_TAN,              // edge passes of the tangents (and the W_e gradient)
   K_MOE_TAN,               // token-wise MoE tangents, gate and readout gradients
   K_ATTN_TAN,              // attention tangents (training gradient)
+  K_GEMM_EXPERT_PAIR,      // Y = silu(P) W2 with Q = (g W2^T) silu'(P), one launch
   K_NUM_CLASSES
 };
 
@@ -159,6 +160,31 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ------------------------------------------- cross-lane sums (DPP moves) --
+// Moves inside 16-lane rows, with no LDS round trip: lane i ^ 1 and i ^ 2 of
+// each quad, lane 7 - i of each 8-lane half row, lane 15 - i of each row.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G a power of two).  Each step adds the
+// partial of a lane in the other half of the current subgroup, whose own
+// partial covers that half; a + b == b + a, so all lanes of a group end with
+// the same bits.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_mov<DPP_XOR1>(v);
+  if constexpr (G >= 4) v += dpp_mov<DPP_XOR2>(v);
+  if constexpr (G >= 8) v += dpp_mov<DPP_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dpp_mov<DPP_MIRROR>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // ------------------------------------------------------- radial basis -----
 // Constants of the pair-distance basis: K Gaussians exp(-gamma (r - k mu_step)^2),
 // k = 0..K-1, mu_step = r_c/(K-1), gamma = (K-1)^2 / (2 r_c^2), and the cosine
@@ -217,6 +243,10 @@ struct GemmArgs {
 
 int launch_gemm(const GemmArgs &a, bool b_transposed, Epilogue epi, KClass cls,
                 hipStream_t stream);
+// Two independent expert GEMMs over the same group_off in one launch (one
+// tail instead of two); timed as class cls.
+int launch_expert_pair(const GemmArgs &a, bool bt_a, Epilogue epi_a, const GemmArgs &b, bool bt_b,
+                       Epilogue epi_b, KClass cls, hipStream_t stream);
 // K parts a dense M x N x K GEMM is split into (1: none), and the floats of
 // split_ws it then needs.
 int dense_k_split(int64_t M, int64_t N, int64_t K);
