@@ -47,7 +47,8 @@ HBM_PEAK_GBS = 8000.0
 # 157.3 TFLOP/s vector figure counts packed FP32 (two lanes per instruction), which this
 # library does not generate.
 VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-EXPERT_CLASSES = ("gemm_expert_up", "gemm_expert_down", "gemm_expert_vjp_down", "gemm_expert_vjp_up")
+EXPERT_CLASSES = ("gemm_expert_up", "gemm_expert_down", "gemm_expert_vjp_down", "gemm_expert_vjp_up",
+                  "gemm_expert_pair")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_expert_traffic_S.txt")
 
 
@@ -338,6 +339,8 @@ def main():
     k = cfg.top_k
     Mtok = N * k
     flops = {c: 2.0 * Mtok * cfg.d_node * cfg.d_hidden for c in EXPERT_CLASSES + ("gemm_expert_tan",)}
+    # the forward's Y = silu(P) W2 and the gradient's Q = (g W2^T) silu'(P) in one launch
+    flops["gemm_expert_pair"] = 2 * 2.0 * Mtok * cfg.d_node * cfg.d_hidden
     Dn, H, Da = cfg.d_node, cfg.d_hidden, cfg.d_attn
     moe_wgrad = 2 * (2 * 2.0 * Mtok * Dn * H)                    # d W1, d W2: two terms each
     if full or stack:

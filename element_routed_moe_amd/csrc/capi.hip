@@ -103,6 +103,36 @@ VjpWs carve_vjp(void *base, int64_t N, int64_t k, int64_t De, int64_t Dn, int64_
   if (bytes) *bytes = c.bytes();
   return w;
 }
+struct AggVjpWs {
+  float *split, *virial, *abar, *sbar;
+};
+AggVjpWs carve_agg_vjp(void *base, int64_t N, int64_t De, int64_t Dn, size_t *bytes) {
+  Carver c(base);
+  AggVjpWs w;
+  w.split = c.take<float>(size_t(dense_split_floats(N, De, Dn)));   // abar = ubar W_u^T split over K
+  w.virial = c.take<float>(size_t(N * 6));
+  w.abar = c.take<float>(size_t(N * De));
+  w.sbar = c.take<float>(size_t(N * De));
+  if (bytes) *bytes = c.bytes();
+  return w;
+}
+
+// mlip_moe_forward_vjp: the forward's buffers, then Q [N k, H] (Utok reuses Y)
+struct MoeFwdVjpWs {
+  MoeWs f;
+  float *Q;
+};
+MoeFwdVjpWs carve_moe_fwd_vjp(void *base, int64_t N, int64_t T, int64_t X, int64_t k, int64_t Dn,
+                              int64_t H, size_t *bytes) {
+  size_t fb = 0;
+  MoeFwdVjpWs w;
+  w.f = carve_moe(base, N, T, X, k, Dn, H, &fb);
+  Carver c(base ? static_cast<char *>(base) + fb : nullptr);
+  w.Q = c.take<float>(size_t(N * k * H));
+  if (bytes) *bytes = fb + c.bytes();
+  return w;
+}
+
 
 struct MoeVjpWs {
   float *Q, *Utok;
@@ -647,6 +677,134 @@ size_t mlip_moe_vjp_workspace_size(int32_t n_atoms, int32_t top_k, int32_t d_nod
   carve_moe_vjp(nullptr, std::max(n_atoms, 0), std::max(top_k, 1), std::max(d_node, 0),
                 std::max(d_hidden, 0), &b);
   return b;
+}
+
+size_t mlip_moe_forward_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                                           int32_t top_k, int32_t d_node, int32_t d_hidden) {
+  size_t b = 0;
+  carve_moe_fwd_vjp(nullptr, std::max(n_atoms, 0), std::max(n_types, 1), std::max(n_experts, 1),
+                    std::max(top_k, 1), std::max(d_node, 0), std::max(d_hidden, 0), &b);
+  return b;
+}
+
+int mlip_moe_forward_vjp(const float *u, const int32_t *z, const float *logits, const float *W1,
+                         const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                         int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
+                         int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom, int32_t *slot,
+                         float *P, float *h_out, float *grad_u, float *q_out, void *ws, size_t ws_bytes,
+                         void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
+  MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
+  MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
+                 "need 1 <= top_k <= n_experts");
+  MLIP_CHECK_ARG(n_experts <= kMaxExperts, "n_experts must be <= %d", kMaxExperts);
+  MLIP_CHECK_ARG(int64_t(n_atoms) * top_k < (int64_t(1) << 31), "n_atoms * top_k too large");
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  if (int rc = check_width(d_hidden, "d_hidden")) return rc;
+  MLIP_CHECK_ARG(logits && W1 && W2 && topk && gate && exp_off, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (u && z && tok_atom && slot && P && h_out && grad_out && grad_u),
+                 "null pointer argument");
+  MLIP_CHECK_ARG(aligned(u, 16) && aligned(W1, 16) && aligned(W2, 16) && aligned(P, 16) &&
+                     aligned(h_out, 16) && aligned(grad_out, 16) && aligned(grad_u, 16) &&
+                     aligned(q_out, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_moe_forward_vjp_workspace_size(n_atoms, n_types, n_experts,
+                                                                          top_k, d_node, d_hidden)))
+    return rc;
+  MoeFwdVjpWs w = carve_moe_fwd_vjp(ws, n_atoms, n_types, n_experts, top_k, d_node, d_hidden, nullptr);
+  const int M = n_atoms * top_k;
+  if (int rc = moe_route_dispatch(z, logits, n_atoms, n_types, n_experts, top_k, topk, gate, exp_off,
+                                  tok_atom, slot, w.f.local_rank, w.f.blk_count, w.f.n_type, w.f.pre,
+                                  w.f.exp_count, w.f.flags, stream))
+    return rc;
+  if (n_atoms == 0) return MLIP_OK;
+  GemmArgs g;  // P = u[tok] @ W1[x], act = silu(P)
+  g.A = u; g.lda = d_node; g.a_rows = tok_atom; g.a_row_limit = n_atoms;
+  g.B = W1; g.ldb = d_hidden; g.b_group_stride = int64_t(d_node) * d_hidden;
+  g.C = P; g.C2 = w.f.act; g.ldc = d_hidden;
+  g.group_off = exp_off; g.n_groups = n_experts;
+  g.M = M; g.N = d_hidden; g.K = d_node;
+  if (int rc = launch_gemm(g, false, EPI_SILU, K_GEMM_EXPERT_UP, stream)) return rc;
+  // Y = act @ W2[x] (forward) and Q = (grad_out[tok] @ W2[x]^T) * silu'(P) (gradient) need only
+  // P and grad_out: one launch
+  GemmArgs g2;
+  g2.A = w.f.act; g2.lda = d_hidden;
+  g2.B = W2; g2.ldb = d_node; g2.b_group_stride = int64_t(d_hidden) * d_node;
+  g2.C = w.f.Y; g2.ldc = d_node;
+  g2.group_off = exp_off; g2.n_groups = n_experts;
+  g2.M = M; g2.N = d_node; g2.K = d_hidden;
+  GemmArgs g3;
+  g3.A = grad_out; g3.lda = d_node; g3.a_rows = tok_atom; g3.a_row_limit = n_atoms;
+  g3.B = W2; g3.ldb = d_node; g3.b_group_stride = int64_t(d_hidden) * d_node;
+  g3.C = w.Q; g3.C2 = q_out; g3.ldc = d_hidden; g3.R = P; g3.ldr = d_hidden;
+  g3.group_off = exp_off; g3.n_groups = n_experts;
+  g3.M = M; g3.N = d_hidden; g3.K = d_node;
+  if (int rc = launch_expert_pair(g2, false, EPI_STORE, g3, true, q_out ? EPI_DSILU_Q : EPI_DSILU,
+                                  K_GEMM_EXPERT_PAIR, stream))
+    return rc;
+  if (int rc = moe_combine(u, w.f.Y, z, gate, slot, n_atoms, n_types, top_k, d_node, h_out, stream))
+    return rc;
+  GemmArgs g4;  // U_tok = Q @ W1[x]^T, into Y (the forward's combine has read it)
+  g4.A = w.Q; g4.lda = d_hidden;
+  g4.B = W1; g4.ldb = d_hidden; g4.b_group_stride = int64_t(d_node) * d_hidden;
+  g4.C = w.f.Y; g4.ldc = d_node;
+  g4.group_off = exp_off; g4.n_groups = n_experts;
+  g4.M = M; g4.N = d_node; g4.K = d_hidden;
+  if (int rc = launch_gemm(g4, true, EPI_STORE, K_GEMM_EXPERT_VJP_UP, stream)) return rc;
+  return moe_combine(grad_out, w.f.Y, z, gate, slot, n_atoms, n_types, top_k, d_node, grad_u, stream);
+}
+
+size_t mlip_aggregate_vjp_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node) {
+  size_t b = 0;
+  carve_agg_vjp(nullptr, std::max(n_atoms, 0), std::max(d_edge, 0), std::max(d_node, 0), &b);
+  return b;
+}
+
+int mlip_aggregate_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                       int64_t n_edges, const float *e, const float *s, const float *W_e, const float *W_d,
+                       const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
+                       const float *grad_u, float *grad_h, float *grad_pos, const int32_t *struct_ptr,
+                       int32_t n_structs, float *atom_virial, double *grad_strain, void *ws,
+                       size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
+                 "n_atoms/n_edges out of range");
+  MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);
+  if (int rc = check_width(d_edge, "d_edge")) return rc;
+  if (int rc = check_width(d_node, "d_node")) return rc;
+  MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
+  MLIP_CHECK_ARG(row_ptr && W_e && W_d && W_u, "null pointer argument");
+  MLIP_CHECK_ARG(n_atoms == 0 || (s && grad_u && grad_h && grad_pos), "null pointer argument");
+  MLIP_CHECK_ARG(n_edges == 0 || (src && geom), "null edge pointer");
+  MLIP_CHECK_ARG(!grad_strain || (struct_ptr && n_structs >= 1),
+                 "grad_strain needs struct_ptr and n_structs >= 1");
+  MLIP_CHECK_ARG(aligned(e, 16) && aligned(s, 16) && aligned(grad_u, 16) && aligned(grad_h, 16) &&
+                     aligned(geom, 16),
+                 "float arrays must be 16-byte aligned");
+  if (int rc = check_ws(ws, ws_bytes, mlip_aggregate_vjp_workspace_size(n_atoms, d_edge, d_node)))
+    return rc;
+  if (n_atoms == 0) {
+    if (grad_strain) return launch_strain_sum(nullptr, struct_ptr, n_structs, 0, grad_strain, stream);
+    return MLIP_OK;
+  }
+  AggVjpWs w = carve_agg_vjp(ws, n_atoms, d_edge, d_node, nullptr);
+  float *vir = atom_virial ? atom_virial : w.virial;
+  GemmArgs g3;  // abar = ubar @ W_u^T
+  g3.A = grad_u; g3.lda = d_node; g3.B = W_u; g3.ldb = d_node; g3.C = w.abar; g3.ldc = d_edge;
+  g3.M = n_atoms; g3.N = d_edge; g3.K = d_node;
+  g3.k_split = dense_k_split(n_atoms, d_edge, d_node); g3.split_ws = w.split;
+  if (int rc = launch_gemm(g3, true, EPI_STORE, K_GEMM_DENSE, stream)) return rc;
+  if (int rc = launch_edge_vjp(row_ptr, src, geom, n_atoms, W_e, e, s, w.abar, d_edge, cutoff, w.sbar,
+                               grad_pos, vir, stream))
+    return rc;
+  if (grad_strain) {
+    if (int rc = launch_strain_sum(vir, struct_ptr, n_structs, n_atoms, grad_strain, stream)) return rc;
+  }
+  GemmArgs g4;  // grad_h = ubar + sbar @ W_d^T
+  g4.A = w.sbar; g4.lda = d_edge; g4.B = W_d; g4.ldb = d_edge; g4.C = grad_h; g4.ldc = d_node;
+  g4.R = grad_u; g4.ldr = d_node; g4.M = n_atoms; g4.N = d_node; g4.K = d_edge;
+  return launch_gemm(g4, true, EPI_RESID, K_GEMM_DENSE, stream);
 }
 
 int mlip_moe_vjp(const int32_t *z, const float *gate, const int32_t *exp_off,

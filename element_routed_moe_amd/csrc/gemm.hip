@@ -466,6 +466,106 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   gemm_tile<BM, BN, BK, WM, WN, BT, EPI, S, AST, BST>(g, As, Bs, Bg, row0, rows, n0);
 }
 
+// Two independent grouped expert GEMMs over the same expert row ranges (one
+// group_off, hence the same m-tiles) in one launch.  Each XCD is dealt the
+// full tiles of the first, then those of the second, then the short tiles of
+// each, so the second GEMM's tiles fill the slots the first one's last round
+// leaves idle and the launch has one tail instead of two.
+template <bool BT1, int EPI1, bool BT2, int EPI2>
+__global__ void __launch_bounds__(THREADS, 2) gemm_pair_kernel(GemmArgs g1, GemmArgs g2) {
+  constexpr int BM = 128, BN = 128, BK = EXPERT_BK, S = EXPERT_S;
+  constexpr int AST = BM * BK;
+  constexpr int BST = BN * BK;
+  constexpr int REM_MAX = BM / 2;
+  __shared__ __attribute__((aligned(16))) float A0[AST], A1[AST], A2[S >= 3 ? AST : 4], A3[S >= 4 ? AST : 4];
+  __shared__ __attribute__((aligned(16))) float B0[BST], B1[BST], B2[S >= 3 ? BST : 4], B3[S >= 4 ? BST : 4];
+  float *const As[4] = {A0, A1, A2, A3};
+  float *const Bs[4] = {B0, B1, B2, B3};
+  __shared__ int s_tiles[MAX_GROUPS + 1];
+  __shared__ int s_red[10];
+
+  const int tid = threadIdx.x;
+  const int G = g1.n_groups;
+  const int Nt1 = (g1.N + BN - 1) / BN, Nt2 = (g2.N + BN - 1) / BN;
+  const int L = blockIdx.x;
+  const int jx = L / N_XCD, xcd = L - jx * N_XCD;
+
+  constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;
+  int cf[PER], ch[PER], sf = 0, sh = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int gi = tid * PER + q;
+    const int c = gi < G ? g1.group_off[gi + 1] - g1.group_off[gi] : 0;
+    const int rem = c % BM;
+    cf[q] = c / BM + (rem > REM_MAX ? 1 : 0);
+    ch[q] = (rem > 0 && rem <= REM_MAX) ? 1 : 0;
+    sf += cf[q];
+    sh += ch[q];
+  }
+  int run_f = block_scan_excl(sf, s_red);
+  int run_h = block_scan_excl(sh, s_red + 4);
+  if (tid == THREADS - 1) {
+    s_red[8] = run_f + sf;
+    s_red[9] = run_h + sh;
+  }
+  __syncthreads();
+  const int Mf = s_red[8], Mh = s_red[9];
+  const int per_f1 = (Mf * Nt1 + N_XCD - 1) / N_XCD, per_f2 = (Mf * Nt2 + N_XCD - 1) / N_XCD;
+  const int per_h1 = (Mh * Nt1 + N_XCD - 1) / N_XCD, per_h2 = (Mh * Nt2 + N_XCD - 1) / N_XCD;
+  int second, t_local, Mt, Nt;
+  bool short_tile;
+  if (jx < per_f1) {
+    second = 0; short_tile = false; t_local = xcd * per_f1 + jx;
+  } else if (jx < per_f1 + per_f2) {
+    second = 1; short_tile = false; t_local = xcd * per_f2 + (jx - per_f1);
+  } else if (jx < per_f1 + per_f2 + per_h1) {
+    second = 0; short_tile = true; t_local = xcd * per_h1 + (jx - per_f1 - per_f2);
+  } else {
+    second = 1; short_tile = true; t_local = xcd * per_h2 + (jx - per_f1 - per_f2 - per_h1);
+    if (jx - per_f1 - per_f2 - per_h1 >= per_h2) return;
+  }
+  Mt = short_tile ? Mh : Mf;
+  Nt = second ? Nt2 : Nt1;
+  if (t_local >= Mt * Nt) return;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int gi = tid * PER + q;
+    if (gi <= G) s_tiles[gi] = short_tile ? run_h : run_f;
+    run_f += cf[q];
+    run_h += ch[q];
+  }
+  __syncthreads();
+  constexpr int RM = EXPERT_RASTER_M;
+  const int group_size = RM * Nt;
+  const int first_m = (t_local / group_size) * RM;
+  const int gm = min(Mt - first_m, RM);
+  const int rr = t_local % group_size;
+  const int mt_glob = first_m + rr % gm;
+  const int nt = rr / gm;
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tiles[mid] <= mt_glob) lo = mid;
+    else hi = mid;
+  }
+  const int grp = lo;
+  const int gbeg = g1.group_off[grp];
+  const int rows = g1.group_off[grp + 1];
+  const int row0 = short_tile ? gbeg + ((rows - gbeg) / BM) * BM : gbeg + (mt_glob - s_tiles[grp]) * BM;
+  const int n0 = nt * BN;
+  if (second) {
+    const float *Bg = g2.B + int64_t(grp) * g2.b_group_stride;
+    if (!short_tile) gemm_tile<BM, BN, BK, 2, 2, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+    else if (rows - row0 <= 32) gemm_tile<32, BN, BK, 1, 4, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+    else gemm_tile<64, BN, BK, 2, 2, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+  } else {
+    const float *Bg = g1.B + int64_t(grp) * g1.b_group_stride;
+    if (!short_tile) gemm_tile<BM, BN, BK, 2, 2, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+    else if (rows - row0 <= 32) gemm_tile<32, BN, BK, 1, 4, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+    else gemm_tile<64, BN, BK, 2, 2, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+  }
+}
+
 // C = (R +) the sum of the k_split parts in split_ws, in part order.
 template <bool RESID>
 __global__ void __launch_bounds__(256) split_epilogue_kernel(const float4 *__restrict__ part, int ks, int64_t mn4,
@@ -546,6 +646,24 @@ int launch_dense(const GemmArgs &a, hipStream_t s) {
   return MLIP_OK;
 }
 
+template <bool BT1, int EPI1, bool BT2, int EPI2>
+int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
+  // upper bounds of the per-XCD tile counts the kernel derives on the device
+  const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * 63) / 128;
+  const int64_t nt1 = cdiv(a.N, 128), nt2 = cdiv(b.N, 128);
+  const int64_t per = cdiv(mf * nt1, N_XCD) + cdiv(mf * nt2, N_XCD) + cdiv(int64_t(a.n_groups) * nt1, N_XCD) +
+                      cdiv(int64_t(a.n_groups) * nt2, N_XCD);
+  const int64_t grid = per * N_XCD;
+  if (grid <= 0) return MLIP_OK;
+  if (grid > int64_t(0x7fffffff)) {
+    set_error("GEMM pair too large for one launch");
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  gemm_pair_kernel<BT1, EPI1, BT2, EPI2><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a, b);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 }  // namespace
 
 // A dense output with few tiles leaves CUs idle (or a partly filled last
@@ -577,6 +695,33 @@ int64_t dense_split_floats(int64_t M, int64_t N, int64_t K) {
   return ks > 1 ? int64_t(ks) * M * N : 0;
 }
 int64_t dense_split_floats_max(int64_t M, int64_t N) { return dense_split_floats(M, N, int64_t(1) << 30); }
+
+int launch_expert_pair(const GemmArgs &a, bool bt_a, Epilogue epi_a, const GemmArgs &b, bool bt_b,
+                       Epilogue epi_b, KClass cls, hipStream_t stream) {
+  if (a.M <= 0) return MLIP_OK;
+  if (!a.group_off || a.group_off != b.group_off || a.n_groups != b.n_groups || a.M != b.M) {
+    set_error("a GEMM pair must share its expert row ranges");
+    return MLIP_ERR_INVALID;
+  }
+  for (const GemmArgs *g : {&a, &b}) {
+    if ((g->K & 3) || (g->N & 3) || (g->lda & 3) || (g->ldb & 3) || g->N <= 0) {
+      set_error("GEMM dims must be multiples of 4 (K=%d N=%d)", g->K, g->N);
+      return MLIP_ERR_UNSUPPORTED;
+    }
+  }
+  if (a.n_groups > MAX_GROUPS) {
+    set_error("at most %d expert groups", MAX_GROUPS);
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  ProfScope ps(cls, stream);
+  // Y = silu(P) W2 (forward) with Q = (g W2^T) silu'(P) (gradient), with or without saving g W2^T
+  if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU)
+    return launch_pair_t<false, EPI_STORE, true, EPI_DSILU>(a, b, stream);
+  if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU_Q)
+    return launch_pair_t<false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream);
+  set_error("unsupported GEMM pair");
+  return MLIP_ERR_INVALID;
+}
 
 int launch_gemm(const GemmArgs &a, bool bt, Epilogue epi, KClass cls, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0) return MLIP_OK;

@@ -578,34 +578,32 @@ int read_summary(const int32_t *dev, int32_t host[4], hipStream_t stream) {
   return MLIP_OK;
 }
 
-__global__ void graph_flags_zero(int32_t *__restrict__ flags, int32_t *__restrict__ maxdeg) {
-  if (threadIdx.x < 4) {
-    flags[threadIdx.x] = 0;
-    maxdeg[threadIdx.x] = 0;
-  }
+// After the summary is written: when the fill pass did not run (the edges
+// exceed the capacity, a row exceeds the LDS row buffer or the structure
+// table was rejected), row_ptr becomes an empty graph, so that a caller who
+// has not yet read the summary runs every later pass on no edges instead of
+// on edge slots that were never written.
+__global__ void graph_empty_on_error(int32_t *__restrict__ row_ptr, int n_atoms, int64_t capacity,
+                                     const int32_t *__restrict__ summary) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i > n_atoms) return;
+  const bool failed = int64_t(summary[0]) > capacity || summary[2] > kMaxDeg || (summary[1] & GF_BAD_STRUCTS);
+  if (failed) row_ptr[i] = 0;
 }
 
-}  // namespace
-}  // namespace mlip
-
-extern "C" {
-
-size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs) {
-  size_t bytes = 0;
-  carve_graph(nullptr, n_atoms < 0 ? 0 : n_atoms, n_structs < 1 ? 1 : n_structs, &bytes);
-  return bytes;
-}
-
-int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,
-                     int32_t n_atoms, int32_t n_structs, float cutoff, int64_t edge_capacity,
-                     int32_t *row_ptr, int32_t *src, int8_t *shift, int32_t *rev, float *geom,
-                     int64_t *n_edges, void *ws, size_t ws_bytes, void *stream_) {
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
+// Queues every pass of the build on the stream.  The summary (E, flags,
+// largest degree, 0) goes to summary_out when given, else to the workspace's
+// read-back slot; nothing waits for the device.
+int enqueue_build(const float *pos, const float *cell, const int32_t *struct_ptr, int32_t n_atoms,
+                  int32_t n_structs, float cutoff, int64_t edge_capacity, int32_t *row_ptr, int32_t *src,
+                  int8_t *shift, int32_t *rev, float *geom, int32_t *summary_out, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
   MLIP_CHECK_ARG(n_atoms >= 0 && n_structs >= 1, "n_atoms must be >= 0 and n_structs >= 1");
-  MLIP_CHECK_ARG(cell && struct_ptr && row_ptr && n_edges, "null pointer argument");
+  MLIP_CHECK_ARG(cell && struct_ptr && row_ptr, "null pointer argument");
   MLIP_CHECK_ARG(n_atoms == 0 || pos, "pos is null");
   MLIP_CHECK_ARG(cutoff > 0.f && cutoff < 1e30f, "cutoff must be positive and finite");
-  MLIP_CHECK_ARG(edge_capacity >= 0, "edge_capacity must be >= 0");
+  MLIP_CHECK_ARG(edge_capacity >= 0 && edge_capacity < (int64_t(1) << 31),
+                 "edge_capacity must be in [0, 2^31)");
   MLIP_CHECK_ARG(edge_capacity == 0 || (src && shift && rev && geom), "edge buffers are null");
   size_t need = mlip_graph_workspace_size(n_atoms, n_structs);
   MLIP_CHECK_ARG(ws && ws_bytes >= need, "workspace too small: need %zu bytes, got %zu", need,
@@ -616,51 +614,50 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
                  "geom must be 16-byte and shift 4-byte aligned");
 
   GraphWs w = carve_graph(ws, n_atoms, n_structs, nullptr);
+  int32_t *summary = summary_out ? summary_out : w.readback;
   const int64_t N = n_atoms, B = n_structs, nbins = N + B;
   const double rc2 = double(cutoff) * double(cutoff);
-  int32_t host[4] = {0, 0, 0, 0};
-  {
-    // Every pass is queued before the single host read: the fill and reverse
-    // passes check on the device that the edges fit (fill_allowed), so one
-    // wait reports the edge count, every input error and a missing reverse edge.
-    ProfScope ps(K_GRAPH, stream);
-    graph_zero<<<nblk(nbins, 256), 256, 0, stream>>>(w.flags, w.maxdeg, w.bin_count, w.bin_fill,
-                                                      nbins);
+  graph_zero<<<nblk(nbins, 256), 256, 0, stream>>>(w.flags, w.maxdeg, w.bin_count, w.bin_fill, nbins);
+  MLIP_LAUNCHED();
+  graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, n_atoms, cutoff, w.prm,
+                                               w.flags);
+  MLIP_LAUNCHED();
+  if (N > 0) {
+    graph_bin<<<nblk(N, 256), 256, 0, stream>>>(pos, struct_ptr, n_structs, n_atoms, w.prm,
+                                                 w.atom_struct, w.atom_bin, w.bin_count, w.flags);
     MLIP_LAUNCHED();
-    graph_setup<<<nblk(B, 64), 64, 0, stream>>>(cell, struct_ptr, n_structs, n_atoms, cutoff, w.prm,
-                                                 w.flags);
-    MLIP_LAUNCHED();
-    if (N > 0) {
-      graph_bin<<<nblk(N, 256), 256, 0, stream>>>(pos, struct_ptr, n_structs, n_atoms, w.prm,
-                                                   w.atom_struct, w.atom_bin, w.bin_count, w.flags);
-      MLIP_LAUNCHED();
-      int rc = exclusive_scan(w.bin_count, w.bin_start, nbins, true, w.scan_tmp, stream);
-      if (rc) return rc;
-      graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start,
-                                                       w.bin_fill, w.binned, w.flags);
-      MLIP_LAUNCHED();
-      graph_count<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct, w.atom_bin,
-                                                   w.bin_start, w.binned, rc2, double(cutoff), row_ptr,
-                                                   w.maxdeg, w.flags);
-      MLIP_LAUNCHED();
-    }
-    int rc = exclusive_scan(row_ptr, row_ptr, N, true, w.scan_tmp, stream);
+    int rc = exclusive_scan(w.bin_count, w.bin_start, nbins, true, w.scan_tmp, stream);
     if (rc) return rc;
-    if (N > 0 && edge_capacity > 0) {
-      graph_fill<<<unsigned(padded_grid(N)), 64, 0, stream>>>(
-          pos, n_atoms, w.prm, w.atom_struct, w.atom_bin, w.bin_start, w.binned, rc2, double(cutoff),
-          row_ptr, edge_capacity, w.maxdeg, w.flags, src, reinterpret_cast<char4 *>(shift),
-          reinterpret_cast<float4 *>(geom));
-      MLIP_LAUNCHED();
-      graph_rev<<<nblk(N, 4), 256, 0, stream>>>(n_atoms, edge_capacity, row_ptr, src,
-                                                reinterpret_cast<const char4 *>(shift), rev, w.flags,
-                                                edge_capacity, w.maxdeg);
-      MLIP_LAUNCHED();
-    }
-    graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, w.readback);
+    graph_scatter<<<nblk(N, 256), 256, 0, stream>>>(pos, n_atoms, w.atom_bin, w.bin_start, w.bin_fill,
+                                                     w.binned, w.flags);
     MLIP_LAUNCHED();
-    if (int rc2 = read_summary(w.readback, host, stream)) return rc2;
+    graph_count<<<unsigned(padded_grid(N)), 64, 0, stream>>>(pos, n_atoms, w.prm, w.atom_struct,
+                                                             w.atom_bin, w.bin_start, w.binned, rc2,
+                                                             double(cutoff), row_ptr, w.maxdeg, w.flags);
+    MLIP_LAUNCHED();
   }
+  int rc = exclusive_scan(row_ptr, row_ptr, N, true, w.scan_tmp, stream);
+  if (rc) return rc;
+  if (N > 0 && edge_capacity > 0) {
+    graph_fill<<<unsigned(padded_grid(N)), 64, 0, stream>>>(
+        pos, n_atoms, w.prm, w.atom_struct, w.atom_bin, w.bin_start, w.binned, rc2, double(cutoff),
+        row_ptr, edge_capacity, w.maxdeg, w.flags, src, reinterpret_cast<char4 *>(shift),
+        reinterpret_cast<float4 *>(geom));
+    MLIP_LAUNCHED();
+    graph_rev<<<nblk(N, 4), 256, 0, stream>>>(n_atoms, edge_capacity, row_ptr, src,
+                                              reinterpret_cast<const char4 *>(shift), rev, w.flags,
+                                              edge_capacity, w.maxdeg);
+    MLIP_LAUNCHED();
+  }
+  graph_summary<<<1, 1, 0, stream>>>(row_ptr, n_atoms, w.flags, w.maxdeg, summary);
+  MLIP_LAUNCHED();
+  graph_empty_on_error<<<nblk(N + 1, 256), 256, 0, stream>>>(row_ptr, n_atoms, edge_capacity, summary);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
+// The host's reading of a build summary (E, flags, largest degree).
+int check_summary(const int32_t *host, int64_t edge_capacity, int64_t *n_edges) {
   const int64_t E = host[0];
   const int flags = host[1];
   *n_edges = E;
@@ -696,6 +693,60 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
     return MLIP_ERR_INPUT;
   }
   return MLIP_OK;
+}
+
+__global__ void graph_flags_zero(int32_t *__restrict__ flags, int32_t *__restrict__ maxdeg) {
+  if (threadIdx.x < 4) {
+    flags[threadIdx.x] = 0;
+    maxdeg[threadIdx.x] = 0;
+  }
+}
+
+}  // namespace
+}  // namespace mlip
+
+extern "C" {
+
+size_t mlip_graph_workspace_size(int32_t n_atoms, int32_t n_structs) {
+  size_t bytes = 0;
+  carve_graph(nullptr, n_atoms < 0 ? 0 : n_atoms, n_structs < 1 ? 1 : n_structs, &bytes);
+  return bytes;
+}
+
+int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_ptr,
+                     int32_t n_atoms, int32_t n_structs, float cutoff, int64_t edge_capacity,
+                     int32_t *row_ptr, int32_t *src, int8_t *shift, int32_t *rev, float *geom,
+                     int64_t *n_edges, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(n_edges, "n_edges is null");
+  int32_t host[4] = {0, 0, 0, 0};
+  {
+    ProfScope ps(K_GRAPH, stream);
+    if (int rc = enqueue_build(pos, cell, struct_ptr, n_atoms, n_structs, cutoff, edge_capacity, row_ptr,
+                               src, shift, rev, geom, nullptr, ws, ws_bytes, stream))
+      return rc;
+    // the one host read of the build: E, the error flags and the largest degree
+    GraphWs w = carve_graph(ws, n_atoms, n_structs, nullptr);
+    if (int rc = read_summary(w.readback, host, stream)) return rc;
+  }
+  return check_summary(host, edge_capacity, n_edges);
+}
+
+int mlip_build_graph_async(const float *pos, const float *cell, const int32_t *struct_ptr,
+                           int32_t n_atoms, int32_t n_structs, float cutoff, int64_t edge_capacity,
+                           int32_t *row_ptr, int32_t *src, int8_t *shift, int32_t *rev, float *geom,
+                           int32_t *summary, void *ws, size_t ws_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(summary, "summary is null");
+  MLIP_CHECK_ARG((reinterpret_cast<uintptr_t>(summary) & 15) == 0, "summary must be 16-byte aligned");
+  ProfScope ps(K_GRAPH, stream);
+  return enqueue_build(pos, cell, struct_ptr, n_atoms, n_structs, cutoff, edge_capacity, row_ptr, src,
+                       shift, rev, geom, summary, ws, ws_bytes, stream);
+}
+
+int mlip_graph_check(const int32_t *summary_host, int64_t edge_capacity, int64_t *n_edges) {
+  MLIP_CHECK_ARG(summary_host && n_edges, "null pointer argument");
+  return check_summary(summary_host, edge_capacity, n_edges);
 }
 
 int mlip_graph_reverse(const int32_t *row_ptr, const int32_t *src, const int8_t *shift,

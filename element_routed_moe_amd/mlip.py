@@ -48,6 +48,9 @@ _SIGS = {
     "mlip_build_graph": (C.c_int, [_p, _p, _p, _i32, _i32, _f32, _i64, _p, _p, _p, _p, _p,
                                    C.POINTER(C.c_int64), _p, _sz, _p]),
     "mlip_graph_reverse": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _sz, _p]),
+    "mlip_build_graph_async": (C.c_int, [_p, _p, _p, _i32, _i32, _f32, _i64, _p, _p, _p, _p, _p, _p, _p,
+                                         _sz, _p]),
+    "mlip_graph_check": (C.c_int, [_p, _i64, C.POINTER(C.c_int64)]),
     "mlip_aggregate_workspace_size": (_sz, [_i32, _i32, _i32]),
     "mlip_aggregate": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                  _p, _p, _p, _p, _sz, _p]),
@@ -57,6 +60,12 @@ _SIGS = {
     "mlip_moe_forward": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "mlip_moe_status": (C.c_int, [_p, C.POINTER(C.c_int32), _p]),
+    "mlip_moe_forward_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "mlip_moe_forward_vjp": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p,
+                                       _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mlip_aggregate_vjp_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "mlip_aggregate_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+                                     _p, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]),
     "mlip_readout": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "mlip_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "mlip_block_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -184,6 +193,83 @@ def mlip_build_graph(pos, cell, struct_ptr, cutoff: float, edge_capacity: Option
     raise MlipError(MLIP_ERR_CAPACITY, "edge capacity could not be met")
 
 
+def mlip_build_graph_async(pos, cell, struct_ptr, cutoff: float, buffers: Dict, summary: torch.Tensor,
+                           ws: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """The graph build queued with no wait, into ``buffers`` (the "buffers" of an
+    earlier mlip_build_graph result, whose length is the edge capacity).  The
+    summary (E, flags, largest degree) goes to the device tensor ``summary``
+    [4]; read it with mlip_graph_check once copied to the host.  The result's
+    n_edges is the capacity (an upper bound every later call may use)."""
+    N, B = int(pos.shape[0]), int(cell.shape[0])
+    row_ptr, src, shift, rev, geom = (buffers[k] for k in ("row_ptr", "src", "shift", "rev", "geom"))
+    cap = int(src.shape[0])
+    _check(_lib.mlip_build_graph_async(_ptr(pos), _ptr(cell), _ptr(struct_ptr), N, B, float(cutoff), cap,
+                                       _ptr(row_ptr), _ptr(src), _ptr(shift), _ptr(rev), _ptr(geom),
+                                       _ptr(summary), _ptr(ws), ws.numel(), _stream()))
+    return dict(row_ptr=row_ptr, src=src, shift=shift, rev=rev, geom=geom, n_edges=cap, buffers=buffers)
+
+
+def mlip_graph_check(summary_host: torch.Tensor, edge_capacity: int) -> int:
+    """Status of an asynchronous build from its summary on the host: returns E,
+    raises MlipError for what mlip_build_graph would have returned as an error."""
+    ne = C.c_int64(0)
+    _check(_lib.mlip_graph_check(_ptr(summary_host), int(edge_capacity), C.byref(ne)))
+    return int(ne.value)
+
+
+class GraphState:
+    """The radius graph of a step loop.  The first build waits for the edge
+    count and sizes the buffers; later builds are queued without a wait
+    (mlip_build_graph_async) into those buffers, and their summary is read by
+    ``check()`` after the rest of the step has been queued, waiting only for
+    the build itself.  When the edges outgrow the buffers, ``check()`` says so
+    and the next build is again a waiting one, with room to spare."""
+
+    def __init__(self, pos, cell, struct_ptr, cutoff: float, device):
+        self.pos, self.cell, self.struct_ptr, self.cutoff = pos, cell, struct_ptr, float(cutoff)
+        N, B = int(pos.shape[0]), int(cell.shape[0])
+        self.ws = _ws(_lib.mlip_graph_workspace_size(N, B), device)
+        self.summary_dev = torch.zeros(4, dtype=torch.int32, device=device)
+        self.summary_host = torch.zeros(4, dtype=torch.int32).pin_memory()
+        self.event = torch.cuda.Event()
+        self.graph = None
+        self.pending = False
+        self.min_capacity = None
+
+    def build(self):
+        if self.graph is None:
+            self.graph = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
+                                          edge_capacity=self.min_capacity, ws=self.ws)
+            return self.graph
+        self.graph = mlip_build_graph_async(self.pos, self.cell, self.struct_ptr, self.cutoff,
+                                            self.graph["buffers"], self.summary_dev, self.ws)
+        self.summary_host.copy_(self.summary_dev, non_blocking=True)
+        self.event.record()
+        self.pending = True
+        return self.graph
+
+    def check(self) -> bool:
+        """False when the last build's edges did not fit: the step must be run again."""
+        if not self.pending:
+            return True
+        self.pending = False
+        self.event.synchronize()
+        buf = self.graph["buffers"]
+        cap = int(buf["src"].shape[0])
+        try:
+            E = mlip_graph_check(self.summary_host, cap)
+        except MlipError as err:
+            if err.code != MLIP_ERR_CAPACITY:
+                raise
+            need = int(self.summary_host[0])
+            self.min_capacity = need + need // 4 + 64
+            self.graph = None
+            return False
+        self.graph.update(src=buf["src"][:E], shift=buf["shift"][:E], rev=buf["rev"][:E],
+                          geom=buf["geom"][:E], n_edges=E)
+        return True
+
+
 def mlip_graph_reverse(row_ptr, src, shift, rev: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reverse-edge index of a receiver-sorted CSR graph (rows ordered by
@@ -259,6 +345,63 @@ def mlip_moe_forward(u, z, logits, W1, W2, top_k: int, out: Optional[Dict] = Non
                                  _ptr(out["topk"]), _ptr(out["gate"]), _ptr(out["exp_off"]),
                                  _ptr(out["tok_atom"]), _ptr(out["slot"]), _ptr(out["P"]),
                                  _ptr(out["h_out"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_moe_forward_vjp(u, z, logits, W1, W2, top_k: int, grad_out, out: Optional[Dict] = None,
+                         ws: Optional[torch.Tensor] = None, keep: bool = False) -> Dict[str, torch.Tensor]:
+    """MoE forward and its input gradient for a known upstream grad_out: the
+    tables, P and h_out of mlip_moe_forward plus grad_u (and, with ``keep``,
+    Q = grad_out[tok] @ W2^T per token for the training gradient)."""
+    N, Dn = int(u.shape[0]), int(u.shape[1])
+    T, X = int(logits.shape[0]), int(logits.shape[1])
+    H = int(W1.shape[2])
+    k = int(top_k)
+    dev = u.device
+    if out is None:
+        out = dict(topk=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   exp_off=torch.empty(X + 1, dtype=torch.int32, device=dev),
+                   tok_atom=torch.empty(N * k, dtype=torch.int32, device=dev),
+                   slot=torch.empty((N, k), dtype=torch.int32, device=dev),
+                   P=torch.empty((N * k, H), dtype=torch.float32, device=dev),
+                   h_out=torch.empty((N, Dn), dtype=torch.float32, device=dev),
+                   grad_u=torch.empty((N, Dn), dtype=torch.float32, device=dev))
+    if keep and out.get("Q") is None:
+        out["Q"] = torch.empty((N * k, H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(_lib.mlip_moe_forward_vjp_workspace_size(N, T, X, k, Dn, H), dev)
+    out["ws"] = ws
+    _check(_lib.mlip_moe_forward_vjp(_ptr(u), _ptr(z), _ptr(logits), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
+                                     _ptr(grad_out), _ptr(out["topk"]), _ptr(out["gate"]), _ptr(out["exp_off"]),
+                                     _ptr(out["tok_atom"]), _ptr(out["slot"]), _ptr(out["P"]),
+                                     _ptr(out["h_out"]), _ptr(out["grad_u"]),
+                                     _ptr(out.get("Q") if keep else None), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlip_aggregate_vjp(graph, agg, W_e, W_d, W_u, cutoff: float, grad_u, struct_ptr=None,
+                       out: Optional[Dict] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Input gradient of the aggregation step from grad_u = dL/du: grad_h, grad_pos,
+    atom_virial and (with struct_ptr) grad_strain."""
+    N, Dn = int(grad_u.shape[0]), int(grad_u.shape[1])
+    De = int(W_e.shape[1])
+    E = int(graph["n_edges"])
+    dev = grad_u.device
+    B = int(struct_ptr.shape[0]) - 1 if struct_ptr is not None else 0
+    if out is None:
+        out = dict(grad_h=torch.empty((N, Dn), dtype=torch.float32, device=dev),
+                   grad_pos=torch.empty((N, 3), dtype=torch.float32, device=dev),
+                   atom_virial=torch.empty((N, 6), dtype=torch.float32, device=dev))
+        if struct_ptr is not None:
+            out["grad_strain"] = torch.empty((B, 6), dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = _ws(_lib.mlip_aggregate_vjp_workspace_size(N, De, Dn), dev)
+    _check(_lib.mlip_aggregate_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
+                                   _ptr(agg["e"]), _ptr(agg["s"]), _ptr(W_e), _ptr(W_d), _ptr(W_u),
+                                   int(W_e.shape[0]), De, Dn, float(cutoff), _ptr(grad_u), _ptr(out["grad_h"]),
+                                   _ptr(out["grad_pos"]), _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
+                                   _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))
     return out
 
 
@@ -770,11 +913,10 @@ class Block:
         De, H = self.W_e.shape[1], self.W1.shape[2]
         T, X = self.logits.shape
         B = self.cell.shape[0]
-        self.ws_graph = _ws(_lib.mlip_graph_workspace_size(N, B), device)
+        self.graph_state = None      # made on the first build
         self.ws_agg = _ws(_lib.mlip_aggregate_workspace_size(N, De, Dn), device)
-        self.ws_moe = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
-        self.ws_vjp = _ws(_lib.mlip_vjp_workspace_size(N, self.top_k, De, Dn, H), device)
-        self.edge_capacity = None
+        self.ws_moe = _ws(_lib.mlip_moe_forward_vjp_workspace_size(N, T, X, self.top_k, Dn, H), device)
+        self.ws_vjp = _ws(_lib.mlip_aggregate_vjp_workspace_size(N, De, Dn), device)
         self.store_e = bool(store_edge_features)
         self.train = bool(train)
         self.graph = self.agg = self.moe = self.ro = self.vjp = None
@@ -785,12 +927,18 @@ class Block:
         model of several blocks on one graph does) the previous step's."""
         if not build_graph and self.graph is not None:
             return self.graph
-        g = mlip_build_graph(self.pos, self.cell, self.struct_ptr, self.cutoff,
-                             edge_capacity=self.edge_capacity, ws=self.ws_graph,
-                             buffers=None if self.graph is None else self.graph["buffers"])
-        if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
-            self.edge_capacity = g["n_edges"]
-        return g
+        if self.graph_state is None:
+            self.graph_state = GraphState(self.pos, self.cell, self.struct_ptr, self.cutoff, self.pos.device)
+        return self.graph_state.build()
+
+    def _graph_done(self, build_graph: bool) -> bool:
+        """After the step is queued: False when its graph build overflowed (the
+        step is then run again on a rebuilt graph)."""
+        if self.graph_state is None:
+            return True
+        ok = self.graph_state.check()
+        self.graph = self.graph_state.graph if ok else None
+        return ok
 
     def step(self, build_graph: bool = True):
         g = self._graph(build_graph)
@@ -800,13 +948,20 @@ class Block:
         self.graph = g
         self.agg = mlip_aggregate(g, self.h, self.W_e, self.W_d, self.W_u, self.cutoff,
                                   out=reuse, ws=self.ws_agg, store_e=self.store_e)
-        self.moe = mlip_moe_forward(self.agg["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
-                                    out=self.moe, ws=self.ws_moe)
+        # the upstream gradient is known before the forward: the MoE forward and
+        # its gradient run in one call (the forward's second expert GEMM and the
+        # gradient's first share a launch), then the aggregation's gradient
+        self.moe = mlip_moe_forward_vjp(self.agg["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
+                                        self.grad_out, out=self.moe, ws=self.ws_moe, keep=self.train)
         self.ro = mlip_readout(self.moe["h_out"], self.w_r, self.struct_ptr, out=self.ro)
-        self.vjp = mlip_block_vjp(g, self.agg, self.moe, self.z, self.W_e, self.W_d, self.W_u,
-                                  self.W1, self.W2, self.cutoff, self.top_k, self.grad_out,
-                                  struct_ptr=self.struct_ptr, out=self.vjp, ws=self.ws_vjp,
-                                  keep=self.train)
+        self.vjp = mlip_aggregate_vjp(g, self.agg, self.W_e, self.W_d, self.W_u, self.cutoff,
+                                      self.moe["grad_u"], struct_ptr=self.struct_ptr, out=self.vjp,
+                                      ws=self.ws_vjp)
+        if self.train:
+            self.vjp["ubar"], self.vjp["Q"] = self.moe["grad_u"], self.moe["Q"]
+        if not self._graph_done(build_graph):
+            self.agg = None
+            return self.step(True)
         return self
 
     def train_grad(self, grad_energy, grad_forces) -> Dict[str, torch.Tensor]:
@@ -886,12 +1041,11 @@ class FullBlock:
         H = self.W1.shape[2]
         T, X = self.logits.shape
         B = self.cell.shape[0]
-        self.ws_graph = _ws(_lib.mlip_graph_workspace_size(N, B), device)
+        self.graph_state = None      # made on the first build
         self.ws_moe0 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_moe1 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_mvjp = _ws(_lib.mlip_moe_vjp_workspace_size(N, self.top_k, Dn, H), device)
         self.ws_avjp = self.ws_tvjp = None
-        self.edge_capacity = None
         self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
         self.ubar = self.avjp = self.grad_hT = self.grad_h = None
         self.g_up = self.Q0 = self.Q1 = self.tri_sbar = None
@@ -1008,6 +1162,7 @@ class FullBlock:
         return res
 
     _graph = Block._graph
+    _graph_done = Block._graph_done
 
     def step(self, build_graph: bool = True):
         g = self._graph(build_graph)
@@ -1015,6 +1170,8 @@ class FullBlock:
         h_out = self.forward(g, self.h)
         self.ro = mlip_readout(h_out, self.w_r, self.struct_ptr, out=self.ro)
         self.backward(g, self.grad_out)
+        if not self._graph_done(build_graph):
+            return self.step(True)
         return self
 
 
@@ -1039,8 +1196,7 @@ class Stack:
                        for p in blocks]
         first = self.layers[0]
         for L in self.layers[1:]:        # one set of workspaces for all layers
-            L.ws_graph, L.ws_moe0, L.ws_moe1, L.ws_mvjp = (first.ws_graph, first.ws_moe0,
-                                                           first.ws_moe1, first.ws_mvjp)
+            L.ws_moe0, L.ws_moe1, L.ws_mvjp = first.ws_moe0, first.ws_moe1, first.ws_mvjp
         self.emb = dev(shared["emb"], f32)
         self.first = first
         N = int(first.z.shape[0])
@@ -1049,18 +1205,11 @@ class Stack:
                            atom_virial=torch.empty((N, 6), dtype=f32, device=device),
                            grad_strain=torch.empty((B, 6), dtype=torch.float64, device=device))
         self.graph = self.h0 = self.ro = self.grad_h0 = None
-        self.edge_capacity = None
+        self.graph_state = GraphState(first.pos, first.cell, first.struct_ptr, first.cutoff, device)
 
     def step(self, build_graph: bool = True):
         L0 = self.first
-        if build_graph or self.graph is None:
-            g = mlip_build_graph(L0.pos, L0.cell, L0.struct_ptr, L0.cutoff,
-                                 edge_capacity=self.edge_capacity, ws=L0.ws_graph,
-                                 buffers=None if self.graph is None else self.graph["buffers"])
-            if self.edge_capacity is None or g["n_edges"] > self.edge_capacity:
-                self.edge_capacity = g["n_edges"]
-        else:
-            g = self.graph
+        g = self.graph_state.build() if (build_graph or self.graph is None) else self.graph
         self.graph = g
         self.h0 = mlip_embed_atoms(L0.z, self.emb, out=self.h0)
         h = self.h0
@@ -1074,6 +1223,10 @@ class Stack:
                 L.ws_avjp, L.ws_tvjp = ws_a, ws_t      # share the per-edge workspaces
             grad = L.backward(g, grad, forces=self.forces, accumulate=n > 0)
         self.grad_h0 = grad
+        ok = self.graph_state.check()
+        self.graph = self.graph_state.graph if ok else None
+        if not ok:
+            return self.step(True)
         return self
 
     def train_grad(self, grad_energy, grad_forces):

@@ -24,7 +24,8 @@
  *   - stream is a hipStream_t passed as void* (NULL = default stream).  All
  *     work is enqueued asynchronously on it; only mlip_build_graph,
  *     mlip_graph_reverse and mlip_moe_status wait for the stream (once each,
- *     to read a count or a device-side check).
+ *     to read a count or a device-side check); mlip_build_graph_async is the
+ *     graph build without that wait.
  *   - Floating point data are float32, row-major.  Weight matrices are
  *     stored "in x out": y = x @ W.
  *   - Feature widths (d_edge, d_node, d_hidden) must be multiples of 4 and
@@ -91,8 +92,9 @@ int mlip_version(void);
  * geom    [E,4] f32    (d.x, d.y, d.z, |d|) rounded to float32.
  * n_edges (host)       E.
  *
- * Errors: MLIP_ERR_CAPACITY when E > edge_capacity (then *n_edges = E and
- * only row_ptr has been written); MLIP_ERR_INPUT for a struct_ptr that does
+ * Errors: MLIP_ERR_CAPACITY when E > edge_capacity (then *n_edges = E, the
+ * edge arrays are untouched and row_ptr describes an empty graph, all
+ * zeros); MLIP_ERR_INPUT for a struct_ptr that does
  * not run 0 = p_0 <= p_1 <= ... <= p_B = n_atoms (then *n_edges = 0 and
  * nothing is indexed through it), positions outside their cell or a cell
  * with non-finite entries or det = 0 (host message says which), and for an
@@ -115,6 +117,25 @@ int mlip_build_graph(const float *pos, const float *cell, const int32_t *struct_
                      int64_t edge_capacity, int32_t *row_ptr, int32_t *src,
                      int8_t *shift, int32_t *rev, float *geom, int64_t *n_edges,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* The same build without any wait, for step loops that must not stall the
+ * host (and can be captured in a HIP graph): every pass is queued on the
+ * stream and the summary (E, error flags, largest degree, 0) is written to
+ * the caller's device array summary [4] (16-byte aligned).  When the edges
+ * do not fit edge_capacity, a row exceeds 1024 edges or struct_ptr is
+ * rejected, the edge arrays are untouched and row_ptr becomes an empty graph
+ * (all zeros), so later calls on this graph touch no unwritten edge slot;
+ * their results are then meaningless until the caller, having copied the
+ * summary to the host, passes it to mlip_graph_check, which returns what
+ * mlip_build_graph would have returned (and E).  Later calls may take
+ * n_edges = edge_capacity: every pass over the edges is bounded by row_ptr. */
+int mlip_build_graph_async(const float *pos, const float *cell, const int32_t *struct_ptr,
+                           int32_t n_atoms, int32_t n_structs, float cutoff,
+                           int64_t edge_capacity, int32_t *row_ptr, int32_t *src,
+                           int8_t *shift, int32_t *rev, float *geom, int32_t *summary,
+                           void *ws, size_t ws_bytes, void *stream);
+/* Reads a build summary copied to the host (summary_host [4]); *n_edges = E. */
+int mlip_graph_check(const int32_t *summary_host, int64_t edge_capacity, int64_t *n_edges);
 
 /* ------------------------------------------------------------------------
  * Reverse-edge index of a caller's receiver-sorted CSR graph ([review] 3.1,
@@ -225,6 +246,31 @@ int mlip_moe_forward(const float *u, const int32_t *z, const float *logits,
 int mlip_moe_status(const void *ws, int32_t *bad_types, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The MoE forward and its input gradient in one call, for an upstream
+ * gradient known before the forward runs: forces of the energy ([news]
+ * conservative training, [review] 3.3) have grad_out = dE/dh_out = w_r for
+ * every atom when the readout follows, and any fixed upstream works.
+ * Outputs and tables as mlip_moe_forward, plus grad_u = dL/du as
+ * mlip_moe_vjp returns it (and, if q_out is not NULL, grad_out[tok] @ W2^T
+ * per token, as mlip_moe_vjp's q_out).
+ *
+ * The forward's second expert GEMM (silu(P) @ W2) and the gradient's first
+ * ((grad_out[tok] @ W2^T) * silu'(P)) need only P and grad_out, so they run
+ * as one launch whose second GEMM fills the slots the first leaves idle at
+ * its end.  Results equal mlip_moe_forward followed by mlip_moe_vjp bit for
+ * bit.  Workspace: mlip_moe_forward_vjp_workspace_size(); mlip_moe_status()
+ * reads its type check.
+ * ------------------------------------------------------------------------ */
+size_t mlip_moe_forward_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                                           int32_t top_k, int32_t d_node, int32_t d_hidden);
+int mlip_moe_forward_vjp(const float *u, const int32_t *z, const float *logits, const float *W1,
+                         const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
+                         int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
+                         int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom, int32_t *slot,
+                         float *P, float *h_out, float *grad_u, float *q_out, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* ------------------------------------------------------------------------
  * Readout ([review] 3.1 Fig. 1(b) names a readout; the reading here is
  * linear): eps_i = h_out_i . w_r, energy_b = sum_{i in b} eps_i in float64.
  * eps [N] f32, energy [n_structs] f64.  struct_ptr as for mlip_build_graph;
@@ -275,6 +321,24 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
                    const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
                    double *grad_strain, float *ubar_out, float *q_out, void *ws,
                    size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The input gradient of mlip_aggregate alone (a13, a14), from grad_u = dL/du:
+ *   abar = grad_u @ W_u^T,  sbar_j = sum_{e: src = j} e_e * abar_recv(e),
+ *   grad_h = grad_u + sbar @ W_d^T,  and dL/dr_e -> grad_pos, atom_virial,
+ *   grad_strain exactly as mlip_block_vjp computes them.
+ * mlip_block_vjp = mlip_moe_vjp followed by this call; after
+ * mlip_moe_forward_vjp it completes the block's gradient.  e may be NULL (the
+ * edge features are then rebuilt from the geometry).  atom_virial and
+ * grad_strain as in mlip_block_vjp.
+ * ------------------------------------------------------------------------ */
+size_t mlip_aggregate_vjp_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node);
+int mlip_aggregate_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
+                       int64_t n_edges, const float *e, const float *s, const float *W_e, const float *W_d,
+                       const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
+                       const float *grad_u, float *grad_h, float *grad_pos, const int32_t *struct_ptr,
+                       int32_t n_structs, float *atom_virial, double *grad_strain, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Training gradient of the block: parameter gradients of a loss on energies

@@ -193,7 +193,8 @@ def test_profile_api_without_gpu(mlip):
     assert "gemm_expert_up" in names and "edge_vjp" in names and "attn_fwd" in names
     assert "tri_fwd" in names and "tri_vjp_send" in names
     assert "gemm_wgrad" in names and "edge_tan" in names and "moe_tan" in names
-    assert len(names) == 22
+    assert "gemm_expert_pair" in names
+    assert len(names) == 23
 
 
 def test_training_entry_points_reject_bad_args(mlip):

@@ -297,8 +297,72 @@ def test_capacity_error_leaves_edges_untouched(mlip):
     assert rc == mlip.MLIP_ERR_CAPACITY
     g = OG.radius_graph(inp["pos"], inp["cell"], inp["struct_ptr"], inp["cutoff"])
     assert ne.value == g["src"].size
-    assert np.array_equal(row_ptr.cpu().numpy(), g["row_ptr"])
+    assert torch.all(row_ptr == 0)                 # an empty graph until the build succeeds
     assert torch.all(src == -7) and torch.all(shift == 9) and torch.all(rev == -3) and torch.all(geom == 2.5)
+
+
+def test_async_graph_build(mlip):
+    """mlip_build_graph_async gives the synchronous build's graph; on overflow the
+    summary reports the count, the edges stay untouched and row_ptr is an empty
+    graph, on which the aggregation runs as on a graph without edges."""
+    _say("async graph build")
+    cfg = synth.CONFIGS["ragged"]
+    inp = synth.make_inputs(cfg)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    pos, cell, sp = t(inp["pos"]), t(inp["cell"]), t(inp["struct_ptr"])
+    ref = mlip.mlip_build_graph(pos, cell, sp, float(inp["cutoff"]))
+    E = ref["n_edges"]
+    ws = mlip._ws(mlip._lib.mlip_graph_workspace_size(cfg.n_atoms, cfg.n_structs), "cuda")
+    summary = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def buffers(cap):
+        return dict(row_ptr=torch.full((cfg.n_atoms + 1,), -1, dtype=torch.int32, device="cuda"),
+                    src=torch.full((cap,), -7, dtype=torch.int32, device="cuda"),
+                    shift=torch.zeros((cap, 4), dtype=torch.int8, device="cuda"),
+                    rev=torch.zeros(cap, dtype=torch.int32, device="cuda"),
+                    geom=torch.zeros((cap, 4), dtype=torch.float32, device="cuda"))
+    g = mlip.mlip_build_graph_async(pos, cell, sp, float(inp["cutoff"]), buffers(E + 100), summary, ws)
+    torch.cuda.synchronize()
+    assert mlip.mlip_graph_check(summary.cpu(), E + 100) == E
+    for k in ("row_ptr", "src", "shift", "rev", "geom"):
+        assert torch.equal(g[k][:E] if k != "row_ptr" else g[k], ref[k]), k
+    small = buffers(E // 2)
+    g2 = mlip.mlip_build_graph_async(pos, cell, sp, float(inp["cutoff"]), small, summary, ws)
+    torch.cuda.synchronize()
+    with pytest.raises(mlip.MlipError) as ei:
+        mlip.mlip_graph_check(summary.cpu(), E // 2)
+    assert ei.value.code == mlip.MLIP_ERR_CAPACITY and int(summary[0]) == E
+    assert torch.all(g2["row_ptr"] == 0) and torch.all(g2["src"] == -7)
+    h = t(inp["h"])
+    agg = mlip.mlip_aggregate(g2, h, t(inp["W_e"]), t(inp["W_d"]), t(inp["W_u"]), float(inp["cutoff"]))
+    torch.cuda.synchronize()
+    assert torch.equal(agg["u"], h)                # no edges: no messages, u = h + 0 @ W_u
+
+
+def test_block_steps_reuse_and_regrow_the_graph(mlip):
+    """Step loops: the first step's build waits, later ones are queued without a
+    wait; a later graph that outgrows its buffers is detected and the step is
+    run again on a rebuilt graph.  Every step gives the first step's results."""
+    cfg, inp, g, f, v, gup, _ = oracle_full("ragged", "random")
+    _say("block step loop")
+    blk = mlip.Block(inp, device="cuda", grad_out=gup).step()
+    torch.cuda.synchronize()
+    first = {k: blk.vjp[k].clone() for k in ("grad_h", "grad_pos")}
+    first["h_out"] = blk.moe["h_out"].clone()
+    assert blk.graph["n_edges"] == g["src"].size
+    for it in range(3):
+        if it == 1:   # shrink the kept buffers below the edge count: the queued build overflows
+            st = blk.graph_state
+            cap = st.graph["n_edges"] // 2
+            st.graph["buffers"] = {k: (v[:cap] if k != "row_ptr" else v) for k, v in st.graph["buffers"].items()}
+        blk.step()
+        torch.cuda.synchronize()
+        assert blk.graph["n_edges"] == g["src"].size
+        assert np.array_equal(blk.graph["src"].cpu().numpy(), g["src"])
+        assert torch.equal(blk.moe["h_out"], first["h_out"])
+        for k in ("grad_h", "grad_pos"):
+            assert torch.equal(blk.vjp[k], first[k]), (it, k)
+    assert rel(blk.vjp["grad_pos"], v["grad_pos"]) <= TOL
 
 
 def test_graph_reverse(mlip):
@@ -339,3 +403,27 @@ def test_graph_reverse(mlip):
     with pytest.raises(mlip.MlipError) as ei:
         mlip.mlip_graph_reverse(t(rp4), out["src"], out["shift"])
     assert ei.value.code == mlip.MLIP_ERR_INPUT
+
+
+@pytest.mark.parametrize("name", ["ragged", "S_slice", "sparse"])
+def test_fused_moe_forward_vjp_matches_separate_calls(mlip, name):
+    """mlip_moe_forward_vjp (the forward's second expert GEMM and the gradient's
+    first in one launch) + mlip_aggregate_vjp, as Block.step runs them, give
+    bit for bit what mlip_moe_forward + mlip_block_vjp (and mlip_moe_vjp) give."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    gup = synth.upstream_grad(cfg, inp, "random")
+    _say(f"fused MoE forward+VJP {name}")
+    blk = mlip.Block(inp, device="cuda", grad_out=gup, train=True).step()
+    g, agg = blk.graph, blk.agg
+    moe = mlip.mlip_moe_forward(agg["u"], blk.z, blk.logits, blk.W1, blk.W2, blk.top_k)
+    vjp = mlip.mlip_block_vjp(g, agg, moe, blk.z, blk.W_e, blk.W_d, blk.W_u, blk.W1, blk.W2, blk.cutoff,
+                              blk.top_k, blk.grad_out, struct_ptr=blk.struct_ptr, keep=True)
+    ubar = mlip.mlip_moe_vjp(moe, blk.z, blk.W1, blk.W2, blk.grad_out)
+    torch.cuda.synchronize()
+    for k in ("topk", "gate", "exp_off", "tok_atom", "slot", "P", "h_out"):
+        assert torch.equal(blk.moe[k], moe[k]), k
+    assert torch.equal(blk.moe["grad_u"], ubar)
+    assert torch.equal(blk.moe["grad_u"], vjp["ubar"]) and torch.equal(blk.moe["Q"], vjp["Q"])
+    for k in ("grad_h", "grad_pos", "atom_virial", "grad_strain"):
+        assert torch.equal(blk.vjp[k], vjp[k]), k
