@@ -223,32 +223,29 @@ __global__ void __launch_bounds__(64) tri_fwd_kernel(
   stc<CPL>(tau + int64_t(i) * Dt + c0, t);
 }
 
-// Sums 16 per-lane values over the wavefront in 17 shuffles: at each step a
-// lane keeps half of its values and adds the partner's copy of them.
-// Afterwards lane l holds the total of value l >> 2.
+// Sums 16 per-lane values over the wavefront.  Inside each 16-lane row, four
+// halving steps (DPP moves) leave lane l with value l & 15 summed over its row:
+// at each step a lane keeps one half of its values and adds the partner's copy
+// of that half, the partner keeping the other half (partners: lane 15 - i,
+// 7 - i, i ^ 2, i ^ 1 within the row).  Two shuffles then add the four rows.
+// Afterwards lane l holds the total of value l & 15.
 __device__ inline float reduce16(const float (&v)[NSH]) {
   const int lane = threadIdx.x & 63;
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
   float a8[8], a4[4], a2[2];
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    a8[q] = (b5 ? v[q + 8] : v[q]) + __shfl_xor(b5 ? v[q] : v[q + 8], 32, 64);
+    a8[q] = (b3 ? v[q + 8] : v[q]) + dpp_mov<DPP_MIRROR>(b3 ? v[q] : v[q + 8]);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    a4[q] = (b4 ? a8[q + 4] : a8[q]) + __shfl_xor(b4 ? a8[q] : a8[q + 4], 16, 64);
+    a4[q] = (b2 ? a8[q + 4] : a8[q]) + dpp_mov<DPP_HALF_MIRROR>(b2 ? a8[q] : a8[q + 4]);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    a2[q] = (b3 ? a4[q + 2] : a4[q]) + __shfl_xor(b3 ? a4[q] : a4[q + 2], 8, 64);
-  float a1 = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4, 64);
-  a1 += __shfl_xor(a1, 2, 64);
-  a1 += __shfl_xor(a1, 1, 64);
+    a2[q] = (b1 ? a4[q + 2] : a4[q]) + dpp_mov<DPP_XOR2>(b1 ? a4[q] : a4[q + 2]);
+  float a1 = (b0 ? a2[1] : a2[0]) + dpp_mov<DPP_XOR1>(b0 ? a2[0] : a2[1]);
+  a1 += __shfl_xor(a1, 16, 64);
+  a1 += __shfl_xor(a1, 32, 64);
   return a1;
-}
-
-__device__ inline float wave_total(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
 }
 
 // ------------------------------------------------ gradient: receiver rows --
@@ -259,7 +256,6 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
     const float *__restrict__ W_ang, const float *__restrict__ taubar, int Dt, float rc,
     float *__restrict__ sigma, float4 *__restrict__ gvec) {
   __shared__ float ysh[CHUNK][NSH];     // f_e S_lm(dhat_e)
-  __shared__ float shv[CHUNK][NSH];     // S_lm(dhat_e)
   __shared__ float pq[CHUNK][NSH + 1];  // sum_c Abar_lm,c s_j,c and sum_c Bbar_c s_j,c^2
   __shared__ float4 geo[CHUNK];         // (dhat, 1/r)
   __shared__ float fcs[CHUNK], dfcs[CHUNK], fsq[CHUNK];
@@ -299,10 +295,7 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
       float S[NSH];
       harmonics(G.u.x, G.u.y, G.u.z, S);
 #pragma unroll
-      for (int lm = 0; lm < NSH; ++lm) {
-        ysh[lane][lm] = G.fc * S[lm];
-        shv[lane][lm] = S[lm];
-      }
+      for (int lm = 0; lm < NSH; ++lm) ysh[lane][lm] = G.fc * S[lm];
       geo[lane] = make_float4(G.u.x, G.u.y, G.u.z, G.inv_r);
       fcs[lane] = G.fc;
       dfcs[lane] = G.dfc;
@@ -338,9 +331,11 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
           }
           if (active) stc<CPL>(sigma + int64_t(e0 + me) * Dt + c0, out);
           const float ptot = reduce16(P);
-          const float qtot = wave_total(Q);
-          if ((lane & 3) == 0) pq[me][lane >> 2] = ptot;
-          if (lane == 0) pq[me][NSH] = qtot;
+          float qtot = group_sum<16>(Q);
+          qtot += __shfl_xor(qtot, 16, 64);
+          qtot += __shfl_xor(qtot, 32, 64);
+          // lanes 0..15 hold P_lm (lm = lane), lane 16 stores Q
+          if (lane <= NSH) pq[me][lane] = lane < NSH ? ptot : qtot;
         }
       }
     }
@@ -348,15 +343,17 @@ __global__ void __launch_bounds__(64) tri_vjp_recv_kernel(
     // edge pass: dL/dS_lm = f P_lm, dL/df = sum_lm S_lm P_lm + 2 f Q, then the edge vector
     if (lane < n) {
       const float fc = fcs[lane];
+      const float4 g = geo[lane];
+      float S[NSH];
+      harmonics(g.x, g.y, g.z, S);
       float fbar = 2.f * fc * pq[lane][NSH];
       float sbar_lm[NSH];
 #pragma unroll
       for (int lm = 0; lm < NSH; ++lm) {
         const float p = pq[lane][lm];
-        fbar += shv[lane][lm] * p;
+        fbar += S[lm] * p;
         sbar_lm[lm] = fc * p;
       }
-      const float4 g = geo[lane];
       const float3 gu = harmonics_grad(g.x, g.y, g.z, sbar_lm);
       const float rad = gu.x * g.x + gu.y * g.y + gu.z * g.z;
       const float a = fbar * dfcs[lane];

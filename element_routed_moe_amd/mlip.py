@@ -1045,6 +1045,8 @@ class FullBlock:
         self.ws_moe0 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_moe1 = _ws(_lib.mlip_moe_workspace_size(N, T, X, self.top_k, Dn, H), device)
         self.ws_mvjp = _ws(_lib.mlip_moe_vjp_workspace_size(N, self.top_k, Dn, H), device)
+        self.ws_moe1f = None         # MoE1 forward + gradient in one call (made on first use)
+        self.ubar_ready = False
         self.ws_avjp = self.ws_tvjp = None
         self.graph = self.tri = self.moe0 = self.att = self.moe = self.ro = None
         self.ubar = self.avjp = self.grad_hT = self.grad_h = None
@@ -1057,8 +1059,11 @@ class FullBlock:
             if self.has_tri:
                 self.tri_sbar = torch.empty((N, int(self.W_s.shape[1])), dtype=f32, device=device)
 
-    def forward(self, g, h):
-        """One block on graph g for input features h; returns h' (MoE1 output)."""
+    def forward(self, g, h, grad_out=None):
+        """One block on graph g for input features h; returns h' (MoE1 output).
+        With grad_out (dL/dh', known before the forward under a linear
+        readout) MoE1's input gradient is formed in the same call, and
+        ``backward`` with that grad_out starts from it."""
         self.h_in = h
         if self.has_tri:
             self.tri = mlip_tri(g, h, self.W_s, self.W_ang, self.W_T, self.cutoff, out=self.tri)
@@ -1067,16 +1072,34 @@ class FullBlock:
                                      out=self.moe0, ws=self.ws_moe0)
         self.att = mlip_attention(g, self.moe0["h_out"], self.W_qkv, self.Wa_e, self.W_o,
                                   self.n_heads, self.cutoff, out=self.att)
-        self.moe = mlip_moe_forward(self.att["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
-                                    out=self.moe, ws=self.ws_moe1)
+        if grad_out is None:
+            self.moe = mlip_moe_forward(self.att["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
+                                        out=self.moe, ws=self.ws_moe1)
+            self.ubar_ready = False
+            return self.moe["h_out"]
+        if self.ws_moe1f is None:
+            N, Dn = int(self.z.shape[0]), int(self.W1.shape[1])
+            T, X = int(self.logits.shape[0]), int(self.logits.shape[1])
+            self.ws_moe1f = _ws(_lib.mlip_moe_forward_vjp_workspace_size(
+                N, T, X, self.top_k, Dn, int(self.W1.shape[2])), grad_out.device)
+        out = self.moe if self.moe is not None and "grad_u" in self.moe else None
+        self.moe = mlip_moe_forward_vjp(self.att["u"], self.z, self.logits, self.W1, self.W2, self.top_k,
+                                        grad_out, out=out, ws=self.ws_moe1f, keep=self.train)
+        self.g_up = grad_out
+        self.ubar = self.moe["grad_u"]
+        if self.train:
+            self.Q1 = self.moe["Q"]
+        self.ubar_ready = True
         return self.moe["h_out"]
 
     def backward(self, g, grad_out, forces: Optional[Dict] = None, accumulate: bool = False):
         """Input gradient for grad_out = dL/dh'; forces (grad_pos, atom_virial,
         grad_strain) are written, or added to the given buffers when accumulate."""
-        self.g_up = grad_out
-        self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, grad_out, out=self.ubar,
-                                 ws=self.ws_mvjp, q_out=self.Q1)
+        if not (self.ubar_ready and grad_out is self.g_up):
+            self.g_up = grad_out
+            self.ubar = mlip_moe_vjp(self.moe, self.z, self.W1, self.W2, grad_out, out=self.ubar,
+                                     ws=self.ws_mvjp, q_out=self.Q1)
+        self.ubar_ready = False
         out = None
         if forces is not None:
             gh0 = self.avjp["grad_h0"] if self.avjp is not None else torch.empty_like(grad_out)
@@ -1167,7 +1190,7 @@ class FullBlock:
     def step(self, build_graph: bool = True):
         g = self._graph(build_graph)
         self.graph = g
-        h_out = self.forward(g, self.h)
+        h_out = self.forward(g, self.h, grad_out=self.grad_out)
         self.ro = mlip_readout(h_out, self.w_r, self.struct_ptr, out=self.ro)
         self.backward(g, self.grad_out)
         if not self._graph_done(build_graph):
