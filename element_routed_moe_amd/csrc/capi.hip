@@ -687,13 +687,23 @@ size_t mlip_moe_forward_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int
   return b;
 }
 
+size_t mlip_struct_size(int32_t which) {
+  switch (which) {
+    case 0: return sizeof(mlip_graph);
+    case 1: return sizeof(mlip_moe_state);
+    default: return 0;
+  }
+}
+
 int mlip_moe_forward_vjp(const float *u, const int32_t *z, const float *logits, const float *W1,
                          const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
                          int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
-                         int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom, int32_t *slot,
-                         float *P, float *h_out, float *grad_u, float *q_out, void *ws, size_t ws_bytes,
-                         void *stream_) {
+                         const mlip_moe_state *state, float *h_out, float *grad_u, float *q_out,
+                         void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(state, "null MoE state");
+  int32_t *topk = state->topk, *exp_off = state->exp_off, *tok_atom = state->tok_atom, *slot = state->slot;
+  float *gate = state->gate, *P = state->P;
   MLIP_CHECK_ARG(n_atoms >= 0, "n_atoms must be >= 0");
   MLIP_CHECK_ARG(n_types >= 1 && n_types <= kMaxTypes, "n_types must be in [1, %d]", kMaxTypes);
   MLIP_CHECK_ARG(n_experts >= 1 && top_k >= 1 && top_k <= n_experts,
@@ -761,13 +771,17 @@ size_t mlip_aggregate_vjp_workspace_size(int32_t n_atoms, int32_t d_edge, int32_
   return b;
 }
 
-int mlip_aggregate_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
-                       int64_t n_edges, const float *e, const float *s, const float *W_e, const float *W_d,
-                       const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
-                       const float *grad_u, float *grad_h, float *grad_pos, const int32_t *struct_ptr,
-                       int32_t n_structs, float *atom_virial, double *grad_strain, void *ws,
-                       size_t ws_bytes, void *stream_) {
+int mlip_aggregate_vjp(const mlip_graph *graph, const float *e, const float *s, const float *W_e,
+                       const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node,
+                       float cutoff, const float *grad_u, float *grad_h, float *grad_pos,
+                       const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
+                       double *grad_strain, void *ws, size_t ws_bytes, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  MLIP_CHECK_ARG(graph, "null graph");
+  const int32_t *row_ptr = graph->row_ptr, *src = graph->src;
+  const float *geom = graph->geom;
+  const int32_t n_atoms = graph->n_atoms;
+  const int64_t n_edges = graph->n_edges;
   MLIP_CHECK_ARG(n_atoms >= 0 && n_edges >= 0 && n_edges < (int64_t(1) << 31),
                  "n_atoms/n_edges out of range");
   MLIP_CHECK_ARG(n_rbf == MLIP_N_RBF, "n_rbf must be %d", MLIP_N_RBF);

@@ -625,13 +625,15 @@ template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
   return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG, true, EXPERT_S>(a, s);
 }
-// Dense projections: 64 x 64 tiles when the output is narrow (enough
-// workgroups for 256 CUs), else 64 x 128.
+// Dense projections: a narrow output (N <= 512, K long: the projections to
+// the edge, attention and Tri widths) takes 128 x 64 tiles with the expert
+// GEMMs' 16-deep, 3-stage ring and its K loop split (two 32 x 32 blocks per
+// wave); a wide one takes 64 x 128 tiles with a 32-deep, 2-stage ring.
 template <bool BT, int EPI, int TAG>
 int launch_dense(const GemmArgs &a, hipStream_t s) {
   static_assert(EPI == EPI_STORE || EPI == EPI_RESID, "dense epilogues");
   const bool split = a.split_ws && a.k_split > 1;
-  int rc = a.N <= 512 ? launch_t<64, 64, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s)
+  int rc = a.N <= 512 ? launch_t<128, 64, EXPERT_BK, 2, 2, BT, EPI, TAG, false, EXPERT_S>(a, s)
                       : launch_t<64, 128, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
   if (rc || !split) return rc;
   if ((a.ldc & 3) || (EPI == EPI_RESID && (a.ldr & 3))) {
@@ -671,13 +673,13 @@ int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
 // one tile into ks shorter ones; the count is the one (up to 4, parts of at
 // least 256) that minimises rounds(ks) / ks, the K loops' duration in units of
 // the unsplit loop, plus a tenth for the summing pass, where rounds(ks) is
-// the number of rounds of resident workgroups (four 64 x 64 or three 64 x 128
+// the number of rounds of resident workgroups (three 128 x 64 or 64 x 128
 // tiles per CU) the tiles take.  Outputs of two rounds or more are not split.
 int dense_k_split(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 512) return 1;
-  const int64_t bn = N <= 512 ? 64 : 128;
-  const int64_t tiles = cdiv(M, 64) * cdiv(N, bn);
-  const int64_t slots = 256 * (N <= 512 ? 4 : 3);
+  const bool narrow = N <= 512;
+  const int64_t tiles = cdiv(M, narrow ? 128 : 64) * cdiv(N, narrow ? 64 : 128);
+  const int64_t slots = 256 * 3;
   if (tiles >= 2 * slots) return 1;
   int best = 1;
   double best_cost = double(cdiv(tiles, slots));

@@ -61,10 +61,11 @@ _SIGS = {
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "mlip_moe_status": (C.c_int, [_p, C.POINTER(C.c_int32), _p]),
     "mlip_moe_forward_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "mlip_struct_size": (_sz, [_i32]),
     "mlip_moe_forward_vjp": (C.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p,
-                                       _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+                                       _p, _p, _p, _p, _p, _sz, _p]),
     "mlip_aggregate_vjp_workspace_size": (_sz, [_i32, _i32, _i32]),
-    "mlip_aggregate_vjp": (C.c_int, [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
+    "mlip_aggregate_vjp": (C.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _f32,
                                      _p, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]),
     "mlip_readout": (C.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "mlip_vjp_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -131,6 +132,33 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.argtypes = _args
 
 EXPORTED = tuple(_SIGS)
+
+
+class _Graph(C.Structure):
+    """mlip_graph of include/mlip.h: device pointers of a receiver-sorted CSR graph."""
+    _fields_ = [("row_ptr", C.c_void_p), ("src", C.c_void_p), ("shift", C.c_void_p), ("rev", C.c_void_p),
+                ("geom", C.c_void_p), ("n_atoms", C.c_int32), ("n_edges", C.c_int64)]
+
+
+class _MoeState(C.Structure):
+    """mlip_moe_state of include/mlip.h: a MoE layer's routing tables and hidden pre-activations."""
+    _fields_ = [("topk", C.c_void_p), ("gate", C.c_void_p), ("exp_off", C.c_void_p),
+                ("tok_atom", C.c_void_p), ("slot", C.c_void_p), ("P", C.c_void_p)]
+
+
+if _lib.mlip_struct_size(0) != C.sizeof(_Graph) or _lib.mlip_struct_size(1) != C.sizeof(_MoeState):
+    raise ImportError("libmlip's mlip_graph / mlip_moe_state layout differs from this binding's")
+
+
+def _graph_struct(graph) -> _Graph:
+    return _Graph(_ptr(graph["row_ptr"]), _ptr(graph.get("src")), _ptr(graph.get("shift")),
+                  _ptr(graph.get("rev")), _ptr(graph.get("geom")), int(graph["row_ptr"].shape[0]) - 1,
+                  int(graph["n_edges"]))
+
+
+def _moe_struct(moe) -> _MoeState:
+    return _MoeState(_ptr(moe["topk"]), _ptr(moe["gate"]), _ptr(moe["exp_off"]), _ptr(moe["tok_atom"]),
+                     _ptr(moe["slot"]), _ptr(moe["P"]))
 
 
 def _check(rc: int):
@@ -372,10 +400,9 @@ def mlip_moe_forward_vjp(u, z, logits, W1, W2, top_k: int, grad_out, out: Option
     if ws is None:
         ws = _ws(_lib.mlip_moe_forward_vjp_workspace_size(N, T, X, k, Dn, H), dev)
     out["ws"] = ws
+    st = _moe_struct(out)
     _check(_lib.mlip_moe_forward_vjp(_ptr(u), _ptr(z), _ptr(logits), _ptr(W1), _ptr(W2), N, T, X, k, Dn, H,
-                                     _ptr(grad_out), _ptr(out["topk"]), _ptr(out["gate"]), _ptr(out["exp_off"]),
-                                     _ptr(out["tok_atom"]), _ptr(out["slot"]), _ptr(out["P"]),
-                                     _ptr(out["h_out"]), _ptr(out["grad_u"]),
+                                     _ptr(grad_out), C.byref(st), _ptr(out["h_out"]), _ptr(out["grad_u"]),
                                      _ptr(out.get("Q") if keep else None), _ptr(ws), ws.numel(), _stream()))
     return out
 
@@ -397,8 +424,10 @@ def mlip_aggregate_vjp(graph, agg, W_e, W_d, W_u, cutoff: float, grad_u, struct_
             out["grad_strain"] = torch.empty((B, 6), dtype=torch.float64, device=dev)
     if ws is None:
         ws = _ws(_lib.mlip_aggregate_vjp_workspace_size(N, De, Dn), dev)
-    _check(_lib.mlip_aggregate_vjp(_ptr(graph["row_ptr"]), _ptr(graph["src"]), _ptr(graph["geom"]), N, E,
-                                   _ptr(agg["e"]), _ptr(agg["s"]), _ptr(W_e), _ptr(W_d), _ptr(W_u),
+    g = _graph_struct(graph)
+    if g.n_atoms != N or g.n_edges != E:
+        raise ValueError("the graph and grad_u disagree on the atom count")
+    _check(_lib.mlip_aggregate_vjp(C.byref(g), _ptr(agg["e"]), _ptr(agg["s"]), _ptr(W_e), _ptr(W_d), _ptr(W_u),
                                    int(W_e.shape[0]), De, Dn, float(cutoff), _ptr(grad_u), _ptr(out["grad_h"]),
                                    _ptr(out["grad_pos"]), _ptr(struct_ptr), B, _ptr(out.get("atom_virial")),
                                    _ptr(out.get("grad_strain")), _ptr(ws), ws.numel(), _stream()))

@@ -246,11 +246,43 @@ int mlip_moe_forward(const float *u, const int32_t *z, const float *logits,
 int mlip_moe_status(const void *ws, int32_t *bad_types, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Structured arguments of the step's hot-path calls (mlip_moe_forward_vjp,
+ * mlip_aggregate_vjp): a radius graph and a MoE layer's kept state, as
+ * mlip_build_graph(_async) and the MoE forward write them, bundled so that a
+ * call takes one pointer each instead of five or six arrays.  The structs
+ * hold device pointers and counts only; the caller owns every buffer they
+ * point to and the struct itself (read during the call, not kept).
+ * mlip_struct_size(0) / (1) return sizeof(mlip_graph) / sizeof(mlip_moe_state)
+ * so that a binding can check its own layout.
+ * ------------------------------------------------------------------------ */
+typedef struct mlip_graph {
+  const int32_t *row_ptr; /* [n_atoms+1] receiver-sorted CSR row offsets */
+  const int32_t *src;     /* [n_edges] sender of each edge */
+  const int8_t *shift;    /* [n_edges][4] periodic image (sx, sy, sz, 0); unused by the calls below */
+  const int32_t *rev;     /* [n_edges] reverse edge; unused by the calls below */
+  const float *geom;      /* [n_edges] float4 (dx, dy, dz, r), 16-byte aligned */
+  int32_t n_atoms;
+  int64_t n_edges;
+} mlip_graph;
+
+typedef struct mlip_moe_state {
+  int32_t *topk;     /* [n_types, top_k] experts of each element type */
+  float *gate;       /* [n_types, top_k] their gates */
+  int32_t *exp_off;  /* [n_experts+1] token offsets of the experts (dispatch order) */
+  int32_t *tok_atom; /* [n_atoms*top_k] atom of each token */
+  int32_t *slot;     /* [n_atoms, top_k] token of each (atom, rank) */
+  float *P;          /* [n_atoms*top_k, d_hidden] hidden pre-activations, dispatch order */
+} mlip_moe_state;
+
+size_t mlip_struct_size(int32_t which);
+
+/* ------------------------------------------------------------------------
  * The MoE forward and its input gradient in one call, for an upstream
  * gradient known before the forward runs: forces of the energy ([news]
  * conservative training, [review] 3.3) have grad_out = dE/dh_out = w_r for
  * every atom when the readout follows, and any fixed upstream works.
- * Outputs and tables as mlip_moe_forward, plus grad_u = dL/du as
+ * Outputs and tables as mlip_moe_forward (the tables and P into the buffers
+ * *state points to), plus grad_u = dL/du as
  * mlip_moe_vjp returns it (and, if q_out is not NULL, grad_out[tok] @ W2^T
  * per token, as mlip_moe_vjp's q_out).
  *
@@ -266,9 +298,8 @@ size_t mlip_moe_forward_vjp_workspace_size(int32_t n_atoms, int32_t n_types, int
 int mlip_moe_forward_vjp(const float *u, const int32_t *z, const float *logits, const float *W1,
                          const float *W2, int32_t n_atoms, int32_t n_types, int32_t n_experts,
                          int32_t top_k, int32_t d_node, int32_t d_hidden, const float *grad_out,
-                         int32_t *topk, float *gate, int32_t *exp_off, int32_t *tok_atom, int32_t *slot,
-                         float *P, float *h_out, float *grad_u, float *q_out, void *ws, size_t ws_bytes,
-                         void *stream);
+                         const mlip_moe_state *state, float *h_out, float *grad_u, float *q_out,
+                         void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Readout ([review] 3.1 Fig. 1(b) names a readout; the reading here is
@@ -328,17 +359,17 @@ int mlip_block_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom
  *   grad_h = grad_u + sbar @ W_d^T,  and dL/dr_e -> grad_pos, atom_virial,
  *   grad_strain exactly as mlip_block_vjp computes them.
  * mlip_block_vjp = mlip_moe_vjp followed by this call; after
- * mlip_moe_forward_vjp it completes the block's gradient.  e may be NULL (the
+ * mlip_moe_forward_vjp it completes the block's gradient.  The graph is read
+ * from *graph (row_ptr, src, geom, n_atoms, n_edges).  e may be NULL (the
  * edge features are then rebuilt from the geometry).  atom_virial and
  * grad_strain as in mlip_block_vjp.
  * ------------------------------------------------------------------------ */
 size_t mlip_aggregate_vjp_workspace_size(int32_t n_atoms, int32_t d_edge, int32_t d_node);
-int mlip_aggregate_vjp(const int32_t *row_ptr, const int32_t *src, const float *geom, int32_t n_atoms,
-                       int64_t n_edges, const float *e, const float *s, const float *W_e, const float *W_d,
-                       const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node, float cutoff,
-                       const float *grad_u, float *grad_h, float *grad_pos, const int32_t *struct_ptr,
-                       int32_t n_structs, float *atom_virial, double *grad_strain, void *ws,
-                       size_t ws_bytes, void *stream);
+int mlip_aggregate_vjp(const mlip_graph *graph, const float *e, const float *s, const float *W_e,
+                       const float *W_d, const float *W_u, int32_t n_rbf, int32_t d_edge, int32_t d_node,
+                       float cutoff, const float *grad_u, float *grad_h, float *grad_pos,
+                       const int32_t *struct_ptr, int32_t n_structs, float *atom_virial,
+                       double *grad_strain, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Training gradient of the block: parameter gradients of a loss on energies

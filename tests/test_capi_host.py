@@ -129,6 +129,35 @@ def test_aggregate_and_moe_reject_bad_args(mlip):
     assert "grad_strain" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
 
 
+def test_struct_arguments(mlip):
+    """mlip_graph / mlip_moe_state: the binding's ctypes layout matches the
+    library's, the fields sit where the header declares them, and a NULL
+    struct or a bad field is rejected on the host."""
+    L = mlip._lib
+    assert L.mlip_struct_size(0) == C.sizeof(mlip._Graph) == 6 * 8 + 8
+    assert L.mlip_struct_size(1) == C.sizeof(mlip._MoeState) == 6 * 8
+    assert L.mlip_struct_size(2) == 0
+    assert mlip._Graph.n_edges.offset == 48 and mlip._Graph.n_atoms.offset == 40
+    hdr = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    g_fields = re.search(r"typedef struct mlip_graph \{(.*?)\} mlip_graph;", hdr, re.S).group(1)
+    assert re.findall(r"(\w+);", g_fields) == [n for n, _ in mlip._Graph._fields_]
+    m_fields = re.search(r"typedef struct mlip_moe_state \{(.*?)\} mlip_moe_state;", hdr, re.S).group(1)
+    assert re.findall(r"(\w+);", m_fields) == [n for n, _ in mlip._MoeState._fields_]
+    f = C.c_void_p(256)
+    rc = L.mlip_aggregate_vjp(None, f, f, f, f, f, 16, 32, 64, 5.0, f, f, f, None, 0, None, None, f, 1 << 30, None)
+    assert "graph" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    g = mlip._Graph(256, 256, None, None, 256, 10, -1)
+    rc = L.mlip_aggregate_vjp(C.byref(g), f, f, f, f, f, 16, 32, 64, 5.0, f, f, f, None, 0, None, None, f,
+                              1 << 30, None)
+    assert "out of range" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    rc = L.mlip_moe_forward_vjp(f, f, f, f, f, 10, 4, 8, 2, 64, 128, f, None, f, f, None, f, 1 << 30, None)
+    assert "MoE state" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+    st = mlip._MoeState(256, 256, 256, 256, 256, 256)
+    rc = L.mlip_moe_forward_vjp(f, f, f, f, f, 10, 4, 3, 4, 64, 128, f, C.byref(st), f, f, None, f, 1 << 30,
+                                None)
+    assert "top_k" in _err(mlip, rc, mlip.MLIP_ERR_INVALID)
+
+
 def test_attention_and_moe_vjp_reject_bad_args(mlip):
     L = mlip._lib
     f = C.c_void_p(256)
