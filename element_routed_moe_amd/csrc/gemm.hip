@@ -45,9 +45,8 @@ constexpr int RASTER_M = 8;          // dense GEMMs
 constexpr int EXPERT_RASTER_M = 2;   // grouped expert GEMMs
 constexpr int EXPERT_BK = 16;   // k per pipeline step of the expert GEMMs
 constexpr int EXPERT_S = 3;     // LDS stages: 3 x 16 KB, three workgroups per CU
-constexpr int DENSE_BK = 32;
-constexpr int DENSE_S = 2;
 constexpr int MAX_GROUPS = 1024;
+constexpr int PAIR_BN = 128;   // column width of the paired expert GEMMs' tiles
 
 // Exclusive scan over the 256 threads of the block (one value each).
 __device__ inline int block_scan_excl(int v, int *red) {
@@ -473,7 +472,7 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
 // leaves idle and the launch has one tail instead of two.
 template <bool BT1, int EPI1, bool BT2, int EPI2>
 __global__ void __launch_bounds__(THREADS, 2) gemm_pair_kernel(GemmArgs g1, GemmArgs g2) {
-  constexpr int BM = 128, BN = 128, BK = EXPERT_BK, S = EXPERT_S;
+  constexpr int BM = 128, BN = PAIR_BN, BK = EXPERT_BK, S = EXPERT_S;
   constexpr int AST = BM * BK;
   constexpr int BST = BN * BK;
   constexpr int REM_MAX = BM / 2;
@@ -625,16 +624,13 @@ template <bool BT, int EPI, int TAG>
 int launch_expert(const GemmArgs &a, hipStream_t s) {
   return launch_t<128, 128, EXPERT_BK, 2, 2, BT, EPI, TAG, true, EXPERT_S>(a, s);
 }
-// Dense projections: a narrow output (N <= 512, K long: the projections to
-// the edge, attention and Tri widths) takes 128 x 64 tiles with the expert
-// GEMMs' 16-deep, 3-stage ring and its K loop split (two 32 x 32 blocks per
-// wave); a wide one takes 64 x 128 tiles with a 32-deep, 2-stage ring.
+// Dense projections: 128 x 64 tiles (two 32 x 32 blocks per wave) with the
+// expert GEMMs' 16-deep, 3-stage ring; narrow outputs split their K loop.
 template <bool BT, int EPI, int TAG>
 int launch_dense(const GemmArgs &a, hipStream_t s) {
   static_assert(EPI == EPI_STORE || EPI == EPI_RESID, "dense epilogues");
   const bool split = a.split_ws && a.k_split > 1;
-  int rc = a.N <= 512 ? launch_t<128, 64, EXPERT_BK, 2, 2, BT, EPI, TAG, false, EXPERT_S>(a, s)
-                      : launch_t<64, 128, DENSE_BK, 2, 2, BT, EPI, TAG, false, DENSE_S>(a, s);
+  int rc = launch_t<128, 64, EXPERT_BK, 2, 2, BT, EPI, TAG, false, EXPERT_S>(a, s);
   if (rc || !split) return rc;
   if ((a.ldc & 3) || (EPI == EPI_RESID && (a.ldr & 3))) {
     set_error("split-K GEMM needs ldc and ldr multiples of 4");
@@ -652,7 +648,7 @@ template <bool BT1, int EPI1, bool BT2, int EPI2>
 int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
   // upper bounds of the per-XCD tile counts the kernel derives on the device
   const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * 63) / 128;
-  const int64_t nt1 = cdiv(a.N, 128), nt2 = cdiv(b.N, 128);
+  const int64_t nt1 = cdiv(a.N, PAIR_BN), nt2 = cdiv(b.N, PAIR_BN);
   const int64_t per = cdiv(mf * nt1, N_XCD) + cdiv(mf * nt2, N_XCD) + cdiv(int64_t(a.n_groups) * nt1, N_XCD) +
                       cdiv(int64_t(a.n_groups) * nt2, N_XCD);
   const int64_t grid = per * N_XCD;
@@ -673,12 +669,11 @@ int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
 // one tile into ks shorter ones; the count is the one (up to 4, parts of at
 // least 256) that minimises rounds(ks) / ks, the K loops' duration in units of
 // the unsplit loop, plus a tenth for the summing pass, where rounds(ks) is
-// the number of rounds of resident workgroups (three 128 x 64 or 64 x 128
-// tiles per CU) the tiles take.  Outputs of two rounds or more are not split.
+// the number of rounds of resident workgroups (three 128 x 64 tiles per CU)
+// the tiles take.  Outputs of two rounds or more are not split.
 int dense_k_split(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 512) return 1;
-  const bool narrow = N <= 512;
-  const int64_t tiles = cdiv(M, narrow ? 128 : 64) * cdiv(N, narrow ? 64 : 128);
+  const int64_t tiles = cdiv(M, 128) * cdiv(N, 64);
   const int64_t slots = 256 * 3;
   if (tiles >= 2 * slots) return 1;
   int best = 1;
