@@ -46,7 +46,6 @@ constexpr int EXPERT_RASTER_M = 2;   // grouped expert GEMMs
 constexpr int EXPERT_BK = 16;   // k per pipeline step of the expert GEMMs
 constexpr int EXPERT_S = 3;     // LDS stages: 3 x 16 KB, three workgroups per CU
 constexpr int MAX_GROUPS = 1024;
-constexpr int PAIR_BN = 128;   // column width of the paired expert GEMMs' tiles
 
 // Exclusive scan over the 256 threads of the block (one value each).
 __device__ inline int block_scan_excl(int v, int *red) {
@@ -470,9 +469,9 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
 // full tiles of the first, then those of the second, then the short tiles of
 // each, so the second GEMM's tiles fill the slots the first one's last round
 // leaves idle and the launch has one tail instead of two.
-template <bool BT1, int EPI1, bool BT2, int EPI2>
+template <int BN, bool BT1, int EPI1, bool BT2, int EPI2>
 __global__ void __launch_bounds__(THREADS, 2) gemm_pair_kernel(GemmArgs g1, GemmArgs g2) {
-  constexpr int BM = 128, BN = PAIR_BN, BK = EXPERT_BK, S = EXPERT_S;
+  constexpr int BM = 128, BK = EXPERT_BK, S = EXPERT_S;
   constexpr int AST = BM * BK;
   constexpr int BST = BN * BK;
   constexpr int REM_MAX = BM / 2;
@@ -644,11 +643,11 @@ int launch_dense(const GemmArgs &a, hipStream_t s) {
   return MLIP_OK;
 }
 
-template <bool BT1, int EPI1, bool BT2, int EPI2>
+template <int BN, bool BT1, int EPI1, bool BT2, int EPI2>
 int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
   // upper bounds of the per-XCD tile counts the kernel derives on the device
   const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * 63) / 128;
-  const int64_t nt1 = cdiv(a.N, PAIR_BN), nt2 = cdiv(b.N, PAIR_BN);
+  const int64_t nt1 = cdiv(a.N, BN), nt2 = cdiv(b.N, BN);
   const int64_t per = cdiv(mf * nt1, N_XCD) + cdiv(mf * nt2, N_XCD) + cdiv(int64_t(a.n_groups) * nt1, N_XCD) +
                       cdiv(int64_t(a.n_groups) * nt2, N_XCD);
   const int64_t grid = per * N_XCD;
@@ -657,7 +656,7 @@ int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
     set_error("GEMM pair too large for one launch");
     return MLIP_ERR_UNSUPPORTED;
   }
-  gemm_pair_kernel<BT1, EPI1, BT2, EPI2><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a, b);
+  gemm_pair_kernel<BN, BT1, EPI1, BT2, EPI2><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a, b);
   MLIP_LAUNCHED();
   return MLIP_OK;
 }
@@ -711,11 +710,16 @@ int launch_expert_pair(const GemmArgs &a, bool bt_a, Epilogue epi_a, const GemmA
     return MLIP_ERR_UNSUPPORTED;
   }
   ProfScope ps(cls, stream);
-  // Y = silu(P) W2 (forward) with Q = (g W2^T) silu'(P) (gradient), with or without saving g W2^T
+  // Y = silu(P) W2 (forward) with Q = (g W2^T) silu'(P) (gradient), with or without saving g W2^T.
+  // Widths that are multiples of 256 take 128 x 256 tiles, two workgroups per CU (the S, M and
+  // share widths: at S the pair's 2560 full tiles are then exactly 5 rounds); others 128 x 128.
+  const bool wide = a.N % 256 == 0 && b.N % 256 == 0;
   if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU)
-    return launch_pair_t<false, EPI_STORE, true, EPI_DSILU>(a, b, stream);
+    return wide ? launch_pair_t<256, false, EPI_STORE, true, EPI_DSILU>(a, b, stream)
+                : launch_pair_t<128, false, EPI_STORE, true, EPI_DSILU>(a, b, stream);
   if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU_Q)
-    return launch_pair_t<false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream);
+    return wide ? launch_pair_t<256, false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream)
+                : launch_pair_t<128, false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream);
   set_error("unsupported GEMM pair");
   return MLIP_ERR_INVALID;
 }
