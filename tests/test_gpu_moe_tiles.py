@@ -14,6 +14,11 @@ Widths such as Dn = 148 and H = 260 leave a K tail (K mod 16 = 4) and a ragged
 last 128-wide column tile.  h_out and dL/du are compared with the float64
 oracle (moe_forward, moe_vjp) to 2e-4 of max-abs; the dispatch tables must
 match exactly.
+
+The fused call (forward and input gradient in one paired expert launch) runs
+the same counts, once at widths that are multiples of 256 (its 128 x 256
+tiles) and once at the ragged widths; it must equal the separate calls bit
+for bit and the oracle to 2e-4.
 """
 import sys
 
@@ -92,5 +97,41 @@ def test_moe_tile_boundaries(mlip, name, counts, Dn, H):
     errs["moe_part"] = _rel(moe["h_out"] - up(u), h_ref - u64)
     errs["moe_vjp_part"] = _rel(ubar - up(g), ubar_ref - g.astype(np.float64))
     _say(f"{name}: errors {errs}")
+    bad = {k: e for k, e in errs.items() if not e <= 2e-4}
+    assert not bad, bad
+
+
+FUSED_CASES = [
+    # widths that are multiples of 256 take the 128 x 256 tiles of the paired launch (with 32 x 256 and
+    # 64 x 256 short tiles); the others its 128 x 128 tiles
+    ("boundaries_wide", CASES[0][1], 256, 512),
+    ("short_only_wide", CASES[1][1], 512, 256),
+    ("boundaries", CASES[0][1], 148, 260),
+]
+
+
+@pytest.mark.parametrize("name,counts,Dn,H", FUSED_CASES)
+def test_fused_moe_tile_boundaries(mlip, name, counts, Dn, H):
+    """mlip_moe_forward_vjp (the paired launch) at the same tile boundaries: the
+    oracle to 2e-4, and the separate forward + VJP calls bit for bit."""
+    z, logits, u, W1, W2, g = _inputs(counts, Dn, H, seed=len(counts) * 1000 + Dn + 7)
+    X = len(counts)
+    _say(f"fused {name}: {z.size} atoms, {X} experts, Dn {Dn}, H {H}")
+    dev = "cuda"
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    fused = mlip.mlip_moe_forward_vjp(up(u), up(z), up(logits), up(W1), up(W2), 1, up(g), keep=True)
+    moe = mlip.mlip_moe_forward(up(u), up(z), up(logits), up(W1), up(W2), 1)
+    q = torch.empty_like(fused["Q"])
+    ubar = mlip.mlip_moe_vjp(moe, up(z), up(W1), up(W2), up(g), q_out=q)
+    torch.cuda.synchronize()
+    for k in ("topk", "gate", "exp_off", "tok_atom", "slot", "P", "h_out"):
+        assert torch.equal(fused[k], moe[k]), (name, k)
+    assert torch.equal(fused["grad_u"], ubar), name
+    assert torch.equal(fused["Q"], q), name
+    topk, gate = OB.route(logits, 1)
+    u64 = u.astype(np.float64)
+    errs = dict(h_out=_rel(fused["h_out"], OB.moe_forward(u64, z, topk, gate, W1, W2)),
+                ubar=_rel(fused["grad_u"], OB.moe_vjp(u64, g.astype(np.float64), z, topk, gate, W1, W2)))
+    _say(f"fused {name}: errors {errs}")
     bad = {k: e for k, e in errs.items() if not e <= 2e-4}
     assert not bad, bad
