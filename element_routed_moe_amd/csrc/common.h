@@ -156,8 +156,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Unlike __syncthreads() it does not wait for outstanding global loads, so
 // the LDS copies of later stages stay in flight; each wave waits for its own
 // copies of a stage (wait_vmcnt) before the barrier that publishes it.
+// The wait is the builtin rather than asm text so that the compiler's own
+// wait placement knows the LDS and scalar-load counter is clear after it.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // ------------------------------------------- cross-lane sums (DPP moves) --

@@ -92,7 +92,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS copy targets stay scalar
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- per-lane DMA sources (k offset 0); LDS chunk c = (q*4 + wave)*64 + lane ----
@@ -176,40 +176,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
 
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  // per-lane LDS fragment offsets (floats): A row r, logical chunk 2j + half
-  int a_off[FM], a_x[FM];
-#pragma unroll
-  for (int bi = 0; bi < FM; ++bi) {
-    const int r = wm * WTM + bi * 32 + l32;
-    a_off[bi] = r * BK;
-    a_x[bi] = half ^ ((r / RPB) % KQ);
-  }
-  int b_off[FN], b_x[FN];
-#pragma unroll
-  for (int bj = 0; bj < FN; ++bj) {
-    const int n = wn * WTN + bj * 32 + l32;
-    if (BT) {
-      b_off[bj] = n * BK;
-      b_x[bj] = half ^ ((n / RPB) % KQ);
-    } else {
-      b_off[bj] = (4 * half) * BN + (n ^ (32 * half));
-      b_x[bj] = 0;
-    }
-  }
+  // Per-lane LDS fragment offsets (floats): A row r, logical chunk 2j + half.
+  // Every 32-row block starts at a multiple of 32 rows = 8 swizzle periods of
+  // RPB rows, so the chunk swizzle depends on the lane alone and the blocks
+  // of a wave differ by constant offsets.
+  const int xs = half ^ ((l32 / RPB) % KQ);
+  const int a_off = (wm * WTM + l32) * BK;
+  const int b_off = BT ? (wn * WTN + l32) * BK : (4 * half) * BN + ((wn * WTN + l32) ^ (32 * half));
   struct Frag {
     floatx4 a[FM], b[FN];
   };
   auto read_frag = [&](const float *Ab, const float *Bb, int j, Frag &f) {   // k group 8j .. 8j+7
+    const int kx = 4 * ((2 * j) ^ xs);
 #pragma unroll
     for (int bi = 0; bi < FM; ++bi)
-      f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[a_off[bi] + 4 * ((2 * j) ^ a_x[bi])]);
+      f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[a_off + bi * 32 * BK + kx]);
 #pragma unroll
     for (int bj = 0; bj < FN; ++bj) {
       if (BT) {
-        f.b[bj] = *reinterpret_cast<const floatx4 *>(&Bb[b_off[bj] + 4 * ((2 * j) ^ b_x[bj])]);
+        f.b[bj] = *reinterpret_cast<const floatx4 *>(&Bb[b_off + bj * 32 * BK + kx]);
       } else {
+        // column n = wn*WTN + 32*bj + l32 sits at n ^ (32*half) (WTN is a multiple of 64)
+        const int col = b_off + 64 * (bj >> 1) + ((bj & 1) ? (half ? -32 : 32) : 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f.b[bj][q] = Bb[b_off[bj] + (8 * j + q) * BN];
+        for (int q = 0; q < 4; ++q) f.b[bj][q] = Bb[col + (8 * j + q) * BN];
       }
     }
   };
@@ -218,7 +208,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     read_frag(Ab, Bb, 0, f[0]);
 #pragma unroll
     for (int j = 0; j < BK / 8; ++j) {
-      if (j + 1 < BK / 8) read_frag(Ab, Bb, j + 1, f[(j + 1) & 1]);
+      if (j + 1 < BK / 8) {
+        // the next k group's reads go out before this group's MFMAs, so their
+        // latency is covered by the wave's own matrix work
+        read_frag(Ab, Bb, j + 1, f[(j + 1) & 1]);
+      }
       const Frag &c = f[j & 1];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -233,34 +227,46 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   // kt + S - 1 (clamped to the last step: past the end the copy is a dummy
   // into a stage no later step reads), so exactly (S - 2) * NL copies are
   // younger than step kt's at its top, on every path through the loop.
-  auto step = [&](auto sc, int kt) {
+  // The K tail can only be the last step, which the main loop never runs, so
+  // the loop carries no tail code (nor the registers of its LDS addresses).
+  auto step = [&](auto sc, auto tail, int kt) {
     constexpr int s = decltype(sc)::value;
     wait_vmcnt<(S - 2) * NL>();
-    if (k_tail && kt == nk - 1) zero_tail(As[s], Bs[s], kt);
+    if constexpr (decltype(tail)::value) {
+      if (k_tail && kt == nk - 1) zero_tail(As[s], Bs[s], kt);
+    }
     lds_barrier();
     issue(As[(s + S - 1) % S], Bs[(s + S - 1) % S], min(kt + S - 1, nk - 1));
     compute(As[s], Bs[s]);
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2 % S>;
+  using C3 = std::integral_constant<int, 3 % S>;
+  using NoTail = std::false_type;
+  using Tail = std::true_type;
 
   if (nk > 0) {   // K = 0: the product is zero
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) issue(As[s], Bs[s], min(s, nk - 1));
-    // whole groups of S steps (the loop's back edge only follows step S - 1),
-    // then the remaining nk % S steps, which continue at stage 0
+    // whole groups of S steps that stop short of the last step (the loop's
+    // back edge only follows step S - 1), then the remaining 1 .. S steps,
+    // which continue at stage 0
     int kt = 0;
-    for (; kt + S <= nk; kt += S) {
-      step(std::integral_constant<int, 0>{}, kt);
-      step(std::integral_constant<int, 1>{}, kt + 1);
-      if constexpr (S >= 3) step(std::integral_constant<int, 2 % S>{}, kt + 2);
-      if constexpr (S >= 4) step(std::integral_constant<int, 3 % S>{}, kt + 3);
+    for (; kt + S < nk; kt += S) {
+      step(C0{}, NoTail{}, kt);
+      step(C1{}, NoTail{}, kt + 1);
+      if constexpr (S >= 3) step(C2{}, NoTail{}, kt + 2);
+      if constexpr (S >= 4) step(C3{}, NoTail{}, kt + 3);
     }
-    if (kt < nk) {
-      step(std::integral_constant<int, 0>{}, kt);
+    step(C0{}, Tail{}, kt);
+    if (kt + 1 < nk) {
+      step(C1{}, Tail{}, kt + 1);
       if constexpr (S >= 3) {
-        if (kt + 1 < nk) {
-          step(std::integral_constant<int, 1>{}, kt + 1);
+        if (kt + 2 < nk) {
+          step(C2{}, Tail{}, kt + 2);
           if constexpr (S >= 4) {
-            if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+            if (kt + 3 < nk) step(C3{}, Tail{}, kt + 3);
           }
         }
       }
@@ -341,7 +347,9 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float B0[BST], B1[BST], B2[S >= 3 ? BST : 4], B3[S >= 4 ? BST : 4];
   float *const As[4] = {A0, A1, A2, A3};
   float *const Bs[4] = {B0, B1, B2, B3};
-  __shared__ int s_tiles[MAX_GROUPS + 1];
+  // the expert tile map (dense GEMMs have none: their 128 x 64 tiles then
+  // fit four workgroups per CU)
+  __shared__ int s_tiles[SPLIT ? MAX_GROUPS + 1 : 1];
   __shared__ int s_red[10];   // two scans' wave sums, then the two totals
 
   const int tid = threadIdx.x;
@@ -354,41 +362,34 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   int Mt, t_local, part = 0;
   bool short_tile = false;
   const int ks = (!SPLIT && g.split_ws && g.k_split > 1) ? g.k_split : 1;
-  if (g.group_off) {
+  if (SPLIT && g.group_off) {
     constexpr int PER = (MAX_GROUPS + THREADS) / THREADS;   // covers entries 0..MAX_GROUPS
     int cf[PER], ch[PER], sf = 0, sh = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int gi = tid * PER + q;
       const int c = gi < G ? g.group_off[gi + 1] - g.group_off[gi] : 0;
-      if (SPLIT) {
-        const int rem = c % BM;
-        cf[q] = c / BM + (rem > REM_MAX ? 1 : 0);
-        ch[q] = (rem > 0 && rem <= REM_MAX) ? 1 : 0;
-      } else {
-        cf[q] = (c + BM - 1) / BM;
-        ch[q] = 0;
-      }
+      const int rem = c % BM;
+      cf[q] = c / BM + (rem > REM_MAX ? 1 : 0);
+      ch[q] = (rem > 0 && rem <= REM_MAX) ? 1 : 0;
       sf += cf[q];
       sh += ch[q];
     }
     int run_f = block_scan_excl(sf, s_red);
-    int run_h = SPLIT ? block_scan_excl(sh, s_red + 4) : 0;
-    int Mf = 0, Mh = 0;
+    int run_h = block_scan_excl(sh, s_red + 4);
     if (tid == THREADS - 1) {
       s_red[8] = run_f + sf;
       s_red[9] = run_h + sh;
     }
     __syncthreads();
-    Mf = s_red[8];
-    Mh = SPLIT ? s_red[9] : 0;
+    const int Mf = s_red[8], Mh = s_red[9];
     const int per_f = (Mf * Nt + N_XCD - 1) / N_XCD;
     const int per_h = (Mh * Nt + N_XCD - 1) / N_XCD;
     if (jx < per_f) {
       t_local = xcd * per_f + jx;
       Mt = Mf;
     } else {
-      if (!SPLIT || jx - per_f >= per_h) return;
+      if (jx - per_f >= per_h) return;
       t_local = xcd * per_h + (jx - per_f);
       Mt = Mh;
       short_tile = true;
@@ -421,7 +422,7 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_kernel(GemmArgs g) {
   const int nt = rr / gm;
 
   int grp = 0, row0, rows;
-  if (g.group_off) {
+  if (SPLIT && g.group_off) {
     int lo = 0, hi = G;  // last group with s_tiles[grp] <= mt_glob
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -594,18 +595,20 @@ __global__ void __launch_bounds__(256) split_epilogue_kernel(const float4 *__res
 template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int TAG, bool SPLIT, int S>
 int launch_t(const GemmArgs &a, hipStream_t stream) {
   // Upper bounds of the per-XCD tile counts the kernel derives on the device:
-  // full tiles <= (M + G*(BM/2 - 1)) / BM and short tiles <= G with SPLIT,
-  // ceil(M/BM) + G tiles without it; surplus workgroups return at once.
+  // full tiles <= (M + G*(BM/2 - 1)) / BM and short tiles <= G for grouped
+  // (expert) GEMMs; surplus workgroups return at once.
   const int64_t nt = cdiv(a.N, BN);
   int64_t per;
+  if (!SPLIT && a.group_off) {
+    set_error("grouped GEMMs take the expert tiles");
+    return MLIP_ERR_UNSUPPORTED;
+  }
   if (!a.group_off) {
     const int64_t ks = (!SPLIT && a.split_ws && a.k_split > 1) ? a.k_split : 1;
     per = cdiv(cdiv(a.M, BM) * nt * ks, N_XCD);
-  } else if (SPLIT) {
+  } else {
     const int64_t mf = (int64_t(a.M) + int64_t(a.n_groups) * (BM / 2 - 1)) / BM;
     per = cdiv(mf * nt, N_XCD) + cdiv(int64_t(a.n_groups) * nt, N_XCD);
-  } else {
-    per = cdiv((cdiv(a.M, BM) + a.n_groups) * nt, N_XCD);
   }
   const int64_t grid = per * N_XCD;
   if (grid <= 0) return MLIP_OK;
@@ -668,12 +671,12 @@ int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
 // one tile into ks shorter ones; the count is the one (up to 4, parts of at
 // least 256) that minimises rounds(ks) / ks, the K loops' duration in units of
 // the unsplit loop, plus a tenth for the summing pass, where rounds(ks) is
-// the number of rounds of resident workgroups (three 128 x 64 tiles per CU)
+// the number of rounds of resident workgroups (four 128 x 64 tiles per CU)
 // the tiles take.  Outputs of two rounds or more are not split.
 int dense_k_split(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 512) return 1;
   const int64_t tiles = cdiv(M, 128) * cdiv(N, 64);
-  const int64_t slots = 256 * 3;
+  const int64_t slots = 256 * 4;
   if (tiles >= 2 * slots) return 1;
   int best = 1;
   double best_cost = double(cdiv(tiles, slots));
