@@ -70,23 +70,31 @@ __device__ inline int block_scan_excl(int v, int *red) {
 // reads are free of bank conflicts):
 //   A, NT-B: [row][BK], chunk kq of row r stored at kq ^ ((r / (64/BK)) % (BK/4))
 //   NN-B:    [k][BN],   4-column chunk c of row k stored at c ^ (8 * ((k/4) & 1))
-template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int S, int AST, int BST>
+//
+// XR = 32 adds one more block row (rows BM .. BM + 31, "tall" tiles): it is
+// split over the four wavefronts by columns, each wave taking the 32-column
+// blocks 2*wm and 2*wm + 1 of its own columns, so it reuses the B fragments
+// the wave has already read and costs one more A fragment per k group.
+template <int BM, int BN, int BK, int WM, int WN, bool BT, int EPI, int S, int AST, int BST, int XR = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, float *const *Bs,
                                           const float *Bg, int row0, int rows, int n0) {
   static_assert(WM * WN == 4, "four wavefronts");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(XR == 0 || (XR == 32 && WM == 2 && FN % WM == 0), "extra block row layout");
+  constexpr int XFN = FN / WM;                      // extra-row blocks per wave
+  constexpr int BMA = BM + XR;                      // rows staged in LDS
   constexpr int KQ = BK / 4;                        // 16-byte chunks per row of a k-slice
   constexpr int RPB = 64 / BK;                      // rows per 64-bank line
   // copy instructions per step: one 1 KB chunk-row (64 lanes x 16 bytes) each
-  constexpr int NIA = BM * KQ / 64;
+  constexpr int NIA = BMA * KQ / 64;
   constexpr int A_LOADS = (NIA + 3) / 4;            // per wave; spare slots copy into a sink
   constexpr int B_LOADS = BN * KQ / THREADS;
   constexpr int NL = A_LOADS + B_LOADS;             // the same on every wave
-  static_assert(NIA * 64 == BM * KQ && B_LOADS >= 1 && BN * KQ % THREADS == 0, "load split");
-  static_assert(BM * BK <= AST && BN * BK <= BST, "LDS stage size");
-  static_assert(NIA % 4 == 0 || (NIA + 1) * 256 <= AST, "room for the A sink");
+  static_assert(NIA * 64 == BMA * KQ && B_LOADS >= 1 && BN * KQ % THREADS == 0, "load split");
+  static_assert(BMA * BK <= AST && BN * BK <= BST, "LDS stage size");
+  static_assert(NIA % 4 == 0 || XR > 0 || (NIA + 1) * 256 <= AST, "room for the A sink");
   static_assert(S >= 2 && S <= 4, "stages");
   static_assert(BT || BN % 64 == 0, "NN-B swizzle needs 64-column multiples");
 
@@ -96,10 +104,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- per-lane DMA sources (k offset 0); LDS chunk c = (q*4 + wave)*64 + lane ----
-  // When BM rows do not make a multiple of four chunk-rows (BM = 32), the
-  // waves without a chunk-row of their own re-copy chunk-row 0 into the unused
-  // LDS just past the tile, so that every wave issues the same number of
-  // copies and one vmcnt value fits them all.
+  // When the staged rows do not make a multiple of four chunk-rows, the waves
+  // without a chunk-row of their own in the last slot still issue a copy, so
+  // that every wave issues the same number and one vmcnt value fits them all:
+  // for BM = 32 a copy of chunk-row 0 into the unused LDS just past the tile;
+  // for tall tiles a second copy of one of the slot's real chunk-rows onto
+  // itself (the same bytes, so the two copies agree whichever lands last).
   const float *a_src[A_LOADS];
   int a_kc[A_LOADS];     // k offset (floats) of this lane's chunk within a step
   int a_dof[A_LOADS];    // LDS offset (floats) of the slot's chunk-row
@@ -107,8 +117,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   for (int q = 0; q < A_LOADS; ++q) {
     const int ci = q * 4 + wave;
     const bool real = ci < NIA;
-    a_dof[q] = (real ? ci : NIA) * 256;
-    const int c = (real ? ci : 0) * 64 + lane;
+    const int cs = real ? ci : (XR > 0 ? ci - (4 * A_LOADS - NIA) : 0);   // chunk-row copied
+    a_dof[q] = (real || XR > 0 ? cs : NIA) * 256;
+    const int c = cs * 64 + lane;
     const int r = c / KQ, s = c % KQ;
     a_kc[q] = 4 * (s ^ ((r / RPB) % KQ));
     int p = row0 + r;
@@ -173,6 +184,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     for (int bj = 0; bj < FN; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+  floatx16 acc_x[XR > 0 ? XFN : 1];   // the extra block row (tall tiles)
+#pragma unroll
+  for (int e = 0; e < (XR > 0 ? XFN : 1); ++e)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_x[e][r] = 0.f;
 
   const int l32 = lane & 31;
   const int half = lane >> 5;
@@ -184,13 +200,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
   const int a_off = (wm * WTM + l32) * BK;
   const int b_off = BT ? (wn * WTN + l32) * BK : (4 * half) * BN + ((wn * WTN + l32) ^ (32 * half));
   struct Frag {
-    floatx4 a[FM], b[FN];
+    floatx4 a[FM], b[FN], ax;
   };
   auto read_frag = [&](const float *Ab, const float *Bb, int j, Frag &f) {   // k group 8j .. 8j+7
     const int kx = 4 * ((2 * j) ^ xs);
 #pragma unroll
     for (int bi = 0; bi < FM; ++bi)
       f.a[bi] = *reinterpret_cast<const floatx4 *>(&Ab[a_off + bi * 32 * BK + kx]);
+    if constexpr (XR > 0) f.ax = *reinterpret_cast<const floatx4 *>(&Ab[(BM + l32) * BK + kx]);
 #pragma unroll
     for (int bj = 0; bj < FN; ++bj) {
       if (BT) {
@@ -215,12 +232,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
       }
       const Frag &c = f[j & 1];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int bi = 0; bi < FM; ++bi)
 #pragma unroll
           for (int bj = 0; bj < FN; ++bj)
             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.a[bi][q], c.b[bj][q], acc[bi][bj], 0, 0, 0);
+        if constexpr (XR > 0) {
+#pragma unroll
+          for (int e = 0; e < XFN; ++e) {
+            const float bx = wm ? c.b[XFN + e][q] : c.b[e][q];   // block 2*wm + e (WM = 2)
+            acc_x[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(c.ax[q], bx, acc_x[e], 0, 0, 0);
+          }
+        }
+      }
     }
   };
   // Step kt reads stage kt % S.  Every step issues the copy of step
@@ -276,56 +301,59 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
 
   // ---- epilogue: D[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 ----
   const int kh = half * 4;
-  // Residual / pre-activation values are fetched for the whole wave tile
-  // first (clamped, always-valid addresses), then combined and stored.
-#pragma unroll
-  for (int bi = 0; bi < FM; ++bi) {
-#pragma unroll
-    for (int bj = 0; bj < FN; ++bj) {
-      const int col = n0 + wn * WTN + bj * 32 + l32;
-      const bool col_ok = col < g.N;
-      const int colc = col_ok ? col : n0;
-      float rv[16];
-      if (EPI == EPI_RESID || EPI == EPI_DSILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = row0 + wm * WTM + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
-          const int pc = p < rows ? p : row0;
-          rv[r] = g.R[int64_t(pc) * g.ldr + colc];
-        }
-      }
+  // One 32 x 32 block whose first row is prow.  Residual / pre-activation
+  // values are fetched for the whole block first (clamped, always-valid
+  // addresses), then combined and stored.
+  auto store_block = [&](const floatx16 &v, int prow, int col) {
+    const bool col_ok = col < g.N;
+    const int colc = col_ok ? col : n0;
+    float rv[16];
+    if (EPI == EPI_RESID || EPI == EPI_DSILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int p = row0 + wm * WTM + bi * 32 + 8 * (r >> 2) + kh + (r & 3);
-        const float v = acc[bi][bj][r];
-        float out, out2 = 0.f;
-        if (EPI == EPI_STORE) {
-          out = v;
-        } else if (EPI == EPI_RESID) {
-          out = rv[r] + v;
-        } else if (EPI == EPI_SILU) {
-          out = v;
-          out2 = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
-        } else {
-          // silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the saved pre-activation
-          const float x = rv[r];
-          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-x));
-          const float d1 = sg * (1.f + x * (1.f - sg));
-          if (EPI == EPI_TAN) {
-            out = v;
-            out2 = v * d1;
-          } else {
-            out = v * d1;
-            out2 = v;
-          }
-        }
-        if (col_ok && p < rows) {
-          const int64_t o = int64_t(p) * g.ldc + col;
-          g.C[o] = out;
-          if (EPI == EPI_SILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) g.C2[o] = out2;
-        }
+        const int p = prow + 8 * (r >> 2) + kh + (r & 3);
+        const int pc = p < rows ? p : row0;
+        rv[r] = g.R[int64_t(pc) * g.ldr + colc];
       }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = prow + 8 * (r >> 2) + kh + (r & 3);
+      float out, out2 = 0.f;
+      if (EPI == EPI_STORE) {
+        out = v[r];
+      } else if (EPI == EPI_RESID) {
+        out = rv[r] + v[r];
+      } else if (EPI == EPI_SILU) {
+        out = v[r];
+        out2 = v[r] * __builtin_amdgcn_rcpf(1.f + __expf(-v[r]));
+      } else {
+        // silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the saved pre-activation
+        const float x = rv[r];
+        const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-x));
+        const float d1 = sg * (1.f + x * (1.f - sg));
+        if (EPI == EPI_TAN) {
+          out = v[r];
+          out2 = v[r] * d1;
+        } else {
+          out = v[r] * d1;
+          out2 = v[r];
+        }
+      }
+      if (col_ok && p < rows) {
+        const int64_t o = int64_t(p) * g.ldc + col;
+        g.C[o] = out;
+        if (EPI == EPI_SILU || EPI == EPI_DSILU_Q || EPI == EPI_TAN) g.C2[o] = out2;
+      }
+    }
+  };
+#pragma unroll
+  for (int bi = 0; bi < FM; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) store_block(acc[bi][bj], row0 + wm * WTM + bi * 32, n0 + wn * WTN + bj * 32 + l32);
+  if constexpr (XR > 0) {
+#pragma unroll
+    for (int e = 0; e < XFN; ++e) store_block(acc_x[e], row0 + BM, n0 + wn * WTN + (wm * XFN + e) * 32 + l32);
   }
 }
 
@@ -565,6 +593,148 @@ __global__ void __launch_bounds__(THREADS, 2) gemm_pair_kernel(GemmArgs g1, Gemm
   }
 }
 
+// Tile classes of one expert of c rows for the tall paired launch: f full
+// 128-row tiles, then t tall tiles (128 rows plus up to 32 more), or h short
+// tiles (32 or 64 rows) when the remainder cannot join a full tile.  A
+// remainder of at most 32 rows joins the last full tile, one of 33 to 64
+// rows is split over the last two (the first takes the larger half), and
+// one of more than 64 rows gets a padded full tile.
+__device__ inline void tall_classes(int c, int &f, int &t, int &h) {
+  const int m = c / 128, rem = c % 128;
+  f = m;
+  t = 0;
+  h = 0;
+  if (rem == 0) return;
+  if (rem > 64) {
+    f = m + 1;
+  } else if (rem <= 32 && m >= 1) {
+    f = m - 1;
+    t = 1;
+  } else if (rem > 32 && m >= 2) {
+    f = m - 2;
+    t = 2;
+  } else {
+    h = 1;
+  }
+}
+
+// Two independent grouped expert GEMMs over the same expert row ranges on
+// 128 x 256 tiles, with each expert's short remainder folded into tall
+// tiles, which read the weight columns their full rows read anyway.  Each
+// XCD is dealt, in turn, its share of the full tiles of the first GEMM and
+// of the second, then of the tall tiles of each, then of the short tiles of
+// each (experts of fewer than 129 rows, or of 161 to 192).  The expert of a
+// tile is found by the thread whose groups hold it (no tile map in LDS, so
+// two workgroups fit per CU with 160-row A stages).
+template <bool BT1, int EPI1, bool BT2, int EPI2>
+__global__ void __launch_bounds__(THREADS, 2) gemm_pair_tall_kernel(GemmArgs g1, GemmArgs g2) {
+  constexpr int BM = 128, BN = 256, BK = EXPERT_BK, S = EXPERT_S, XR = 32;
+  constexpr int AST = (BM + XR) * BK;
+  constexpr int BST = BN * BK;
+  __shared__ __attribute__((aligned(16))) float A0[AST], A1[AST], A2[S >= 3 ? AST : 4], A3[S >= 4 ? AST : 4];
+  __shared__ __attribute__((aligned(16))) float B0[BST], B1[BST], B2[S >= 3 ? BST : 4], B3[S >= 4 ? BST : 4];
+  float *const As[4] = {A0, A1, A2, A3};
+  float *const Bs[4] = {B0, B1, B2, B3};
+  __shared__ int s_red[16];   // three scans' wave sums, then the three totals
+  __shared__ int s_hit[2];    // the tile's expert and its index among the expert's tiles of its class
+
+  const int tid = threadIdx.x;
+  const int G = g1.n_groups;
+  const int Nt1 = (g1.N + BN - 1) / BN, Nt2 = (g2.N + BN - 1) / BN;
+  const int L = blockIdx.x;
+  const int jx = L / N_XCD, xcd = L - jx * N_XCD;
+
+  constexpr int PER = MAX_GROUPS / THREADS;   // groups tid*PER .. tid*PER + PER - 1
+  int cn[3][PER], sum[3] = {0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int gi = tid * PER + q;
+    const int c = gi < G ? g1.group_off[gi + 1] - g1.group_off[gi] : 0;
+    tall_classes(c, cn[0][q], cn[1][q], cn[2][q]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) sum[k] += cn[k][q];
+  }
+  int run[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) run[k] = block_scan_excl(sum[k], s_red + 4 * k);
+  if (tid == THREADS - 1) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) s_red[12 + k] = run[k] + sum[k];
+  }
+  __syncthreads();
+  const int Mc[3] = {s_red[12], s_red[13], s_red[14]};   // full, tall and short m-tiles
+  // the six classes in dealing order: (tile class, which GEMM)
+  int cls = -1, second = 0, t_local = 0, Nt = Nt1, base = 0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const int kc = k >> 1, kg = k & 1;
+    const int nt_k = kg ? Nt2 : Nt1;
+    const int per = (Mc[kc] * nt_k + N_XCD - 1) / N_XCD;
+    if (cls < 0 && jx < base + per) {
+      cls = kc;
+      second = kg;
+      Nt = nt_k;
+      t_local = xcd * per + (jx - base);
+    }
+    base += per;
+  }
+  if (cls < 0 || t_local >= (cls == 0 ? Mc[0] : cls == 1 ? Mc[1] : Mc[2]) * Nt) return;
+  constexpr int RM = EXPERT_RASTER_M;
+  const int Mt = cls == 0 ? Mc[0] : cls == 1 ? Mc[1] : Mc[2];
+  const int group_size = RM * Nt;
+  const int first_m = (t_local / group_size) * RM;
+  const int gm = min(Mt - first_m, RM);
+  const int rr = t_local % group_size;
+  const int mt_glob = first_m + rr % gm;
+  const int nt = rr / gm;
+  // the one group whose class range holds mt_glob
+  {
+    int pre = cls == 0 ? run[0] : cls == 1 ? run[1] : run[2];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int cq = cls == 0 ? cn[0][q] : cls == 1 ? cn[1][q] : cn[2][q];
+      if (mt_glob >= pre && mt_glob < pre + cq) {
+        s_hit[0] = tid * PER + q;
+        s_hit[1] = mt_glob - pre;
+      }
+      pre += cq;
+    }
+  }
+  __syncthreads();
+  const int grp = s_hit[0], sub = s_hit[1];
+  const int gbeg = g1.group_off[grp], gend = g1.group_off[grp + 1];
+  int f, t, h;
+  tall_classes(gend - gbeg, f, t, h);
+  const int rem = (gend - gbeg) % BM;
+  int row0, rows = gend;
+  if (cls == 0) {
+    row0 = gbeg + sub * BM;
+  } else if (cls == 1) {
+    row0 = gbeg + f * BM;
+    if (t == 2) {
+      const int r1 = (rem + 1) / 2;
+      if (sub == 0) rows = row0 + BM + r1;
+      else row0 += BM + r1;
+    }
+  } else {
+    row0 = gbeg + f * BM;
+  }
+  const int n0 = nt * BN;
+  if (second) {
+    const float *Bg = g2.B + int64_t(grp) * g2.b_group_stride;
+    if (cls == 0) gemm_tile<BM, BN, BK, 2, 2, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+    else if (cls == 1) gemm_tile<BM, BN, BK, 2, 2, BT2, EPI2, S, AST, BST, XR>(g2, As, Bs, Bg, row0, rows, n0);
+    else if (rows - row0 <= 32) gemm_tile<32, BN, BK, 1, 4, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+    else gemm_tile<64, BN, BK, 2, 2, BT2, EPI2, S, AST, BST>(g2, As, Bs, Bg, row0, rows, n0);
+  } else {
+    const float *Bg = g1.B + int64_t(grp) * g1.b_group_stride;
+    if (cls == 0) gemm_tile<BM, BN, BK, 2, 2, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+    else if (cls == 1) gemm_tile<BM, BN, BK, 2, 2, BT1, EPI1, S, AST, BST, XR>(g1, As, Bs, Bg, row0, rows, n0);
+    else if (rows - row0 <= 32) gemm_tile<32, BN, BK, 1, 4, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+    else gemm_tile<64, BN, BK, 2, 2, BT1, EPI1, S, AST, BST>(g1, As, Bs, Bg, row0, rows, n0);
+  }
+}
+
 // C = (R +) the sum of the k_split parts in split_ws, in part order.
 template <bool RESID>
 __global__ void __launch_bounds__(256) split_epilogue_kernel(const float4 *__restrict__ part, int ks, int64_t mn4,
@@ -664,6 +834,26 @@ int launch_pair_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
   return MLIP_OK;
 }
 
+template <bool BT1, int EPI1, bool BT2, int EPI2>
+int launch_pair_tall_t(const GemmArgs &a, const GemmArgs &b, hipStream_t stream) {
+  // upper bounds of the per-XCD tile counts the kernel derives on the device:
+  // full tiles <= (M + G*63) / 128, tall tiles <= 2G, short tiles <= G
+  const int64_t G = a.n_groups;
+  const int64_t mc[3] = {(int64_t(a.M) + G * 63) / 128, 2 * G, G};
+  const int64_t nt1 = cdiv(a.N, 256), nt2 = cdiv(b.N, 256);
+  int64_t per = 0;
+  for (int k = 0; k < 3; ++k) per += cdiv(mc[k] * nt1, N_XCD) + cdiv(mc[k] * nt2, N_XCD);
+  const int64_t grid = per * N_XCD;
+  if (grid <= 0) return MLIP_OK;
+  if (grid > int64_t(0x7fffffff)) {
+    set_error("GEMM pair too large for one launch");
+    return MLIP_ERR_UNSUPPORTED;
+  }
+  gemm_pair_tall_kernel<BT1, EPI1, BT2, EPI2><<<dim3(unsigned(grid)), dim3(THREADS), 0, stream>>>(a, b);
+  MLIP_LAUNCHED();
+  return MLIP_OK;
+}
+
 }  // namespace
 
 // A dense output with few tiles leaves CUs idle (or a partly filled last
@@ -718,10 +908,10 @@ int launch_expert_pair(const GemmArgs &a, bool bt_a, Epilogue epi_a, const GemmA
   // share widths: at S the pair's 2560 full tiles are then exactly 5 rounds); others 128 x 128.
   const bool wide = a.N % 256 == 0 && b.N % 256 == 0;
   if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU)
-    return wide ? launch_pair_t<256, false, EPI_STORE, true, EPI_DSILU>(a, b, stream)
+    return wide ? launch_pair_tall_t<false, EPI_STORE, true, EPI_DSILU>(a, b, stream)
                 : launch_pair_t<128, false, EPI_STORE, true, EPI_DSILU>(a, b, stream);
   if (!bt_a && epi_a == EPI_STORE && bt_b && epi_b == EPI_DSILU_Q)
-    return wide ? launch_pair_t<256, false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream)
+    return wide ? launch_pair_tall_t<false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream)
                 : launch_pair_t<128, false, EPI_STORE, true, EPI_DSILU_Q>(a, b, stream);
   set_error("unsupported GEMM pair");
   return MLIP_ERR_INVALID;
