@@ -16,9 +16,12 @@ oracle (moe_forward, moe_vjp) to 2e-4 of max-abs; the dispatch tables must
 match exactly.
 
 The fused call (forward and input gradient in one paired expert launch) runs
-the same counts, once at widths that are multiples of 256 (its 128 x 256
-tiles) and once at the ragged widths; it must equal the separate calls bit
-for bit and the oracle to 2e-4.
+the same counts, once at widths that are multiples of 256 and once at the
+ragged widths; it must equal the separate calls bit for bit and the oracle to
+2e-4.  At the wide widths the launch takes 128 x 256 tiles and folds short
+remainders into tall tiles: 129, 160 and 257 rows give one tall tile, 300 two
+(a remainder of 44 split 22 + 22), 161 and every count up to 64 short tiles,
+and 96, 255 a padded full tile.
 """
 import sys
 
@@ -102,8 +105,8 @@ def test_moe_tile_boundaries(mlip, name, counts, Dn, H):
 
 
 FUSED_CASES = [
-    # widths that are multiples of 256 take the 128 x 256 tiles of the paired launch (with 32 x 256 and
-    # 64 x 256 short tiles); the others its 128 x 128 tiles
+    # widths that are multiples of 256 take the paired launch's 128 x 256 tiles (tall 160 x 256 tiles for
+    # the remainders, 32 x 256 and 64 x 256 short tiles for the smallest experts); the others its 128 x 128 tiles
     ("boundaries_wide", CASES[0][1], 256, 512),
     ("short_only_wide", CASES[1][1], 512, 256),
     ("boundaries", CASES[0][1], 148, 260),
