@@ -623,7 +623,7 @@ __device__ inline void tall_classes(int c, int &f, int &t, int &h) {
 // tiles, which read the weight columns their full rows read anyway.  Each
 // XCD is dealt, in turn, its share of the full tiles of the first GEMM and
 // of the second, then of the tall tiles of each, then of the short tiles of
-// each (experts of fewer than 129 rows, or of 161 to 192).  The expert of a
+// each (experts of at most 64 rows, or of 161 to 192).  The expert of a
 // tile is found by the thread whose groups hold it (no tile map in LDS, so
 // two workgroups fit per CU with 160-row A stages).
 template <bool BT1, int EPI1, bool BT2, int EPI2>
