@@ -24,9 +24,15 @@
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
 // given a contiguous range of tile indices; within it tiles run in groups of
-// 8 m-tiles x all n-tiles, m fastest.  The tiles resident on an XCD at one
-// time then share a few A row-blocks and a few expert weight tiles in its L2.
-// Expert row ranges are turned into tile ranges once per workgroup in LDS.
+// 8 m-tiles (2 for the expert GEMMs) x all n-tiles, m fastest.  The tiles
+// resident on an XCD at one time then share a few A row-blocks and a few
+// expert weight tiles in its L2.  Expert row ranges are turned into tile
+// ranges once per workgroup.
+//
+// Expert remainders: an expert's rows past its last whole 128-row block get
+// a 32- or 64-row short tile, or, in the paired launch on 128 x 256 tiles,
+// join the expert's last full tiles as "tall" 160-row tiles (short tiles
+// would stream the expert's weights a second time, cold, at the end).
 #include <algorithm>
 #include <type_traits>
 
