@@ -104,12 +104,22 @@ def test_moe_tile_boundaries(mlip, name, counts, Dn, H):
     assert not bad, bad
 
 
+def _many_experts():
+    """1023 experts (the most the library takes), every eighth with a tile-boundary count and the last one
+    busy: the expert lookup then spans every thread of the workgroup."""
+    marks = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 161, 192, 255, 256, 257, 300]
+    counts = [marks[(e // 8) % len(marks)] if e % 8 == 7 else 0 for e in range(1023)]
+    counts[-1] = 300
+    return counts
+
+
 FUSED_CASES = [
     # widths that are multiples of 256 take the paired launch's 128 x 256 tiles (tall 160 x 256 tiles for
     # the remainders, 32 x 256 and 64 x 256 short tiles for the smallest experts); the others its 128 x 128 tiles
     ("boundaries_wide", CASES[0][1], 256, 512),
     ("short_only_wide", CASES[1][1], 512, 256),
     ("boundaries", CASES[0][1], 148, 260),
+    ("many_experts_wide", _many_experts(), 256, 256),
 ]
 
 
