@@ -5,7 +5,10 @@ MLIP_LIBRARY (the parent has the release build loaded):
   * on valid inputs the checks stay silent and the block, the complete block
     and its training gradient still match the float64 oracle;
   * a sender index past the atoms, handed to the aggregation, is reported by
-    the check (and clamped by it, so the kernel reads nothing out of range).
+    the check (and clamped by it, so the kernel reads nothing out of range);
+  * the fused MoE call at widths that are multiples of 256 (the paired launch
+    on 128 x 256 tiles with tall and short tiles), with expert sizes on every
+    tile-class boundary, stays silent and matches the oracle.
 """
 import json
 import os
@@ -68,6 +71,37 @@ print("RESULT finite=%d" % int(torch.isfinite(out["u"]).all().item()), flush=Tru
 '''
 
 
+WIDE = r'''
+import json, sys
+import numpy as np, torch
+sys.path.insert(0, ROOT)
+from element_routed_moe_amd import mlip
+from oracle import block as OB
+assert mlip.LIB_PATH.endswith("libmlip_debug.so")
+counts = [0, 1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 160, 161, 192, 255, 256, 257, 300, 0, 5]
+X, Dn, H = len(counts), 256, 512
+rng = np.random.default_rng(5)
+z = np.concatenate([np.full(c, t, np.int32) for t, c in enumerate(counts)])
+z = z[rng.permutation(z.size)]
+logits = (rng.standard_normal((X, X)) + 10.0 * np.eye(X)).astype(np.float32)   # type t -> expert t
+u = rng.standard_normal((z.size, Dn)).astype(np.float32)
+W1 = (rng.standard_normal((X, Dn, H)) / np.sqrt(Dn)).astype(np.float32)
+W2 = (rng.standard_normal((X, H, Dn)) / np.sqrt(H)).astype(np.float32)
+g = rng.standard_normal((z.size, Dn)).astype(np.float32)
+up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+out = mlip.mlip_moe_forward_vjp(up(u), up(z), up(logits), up(W1), up(W2), 1, up(g))
+torch.cuda.synchronize()
+topk, gate = OB.route(logits, 1)
+def rel(a, b):
+    a = a.detach().cpu().numpy().astype(np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+u64 = u.astype(np.float64)
+errs = dict(h_out=rel(out["h_out"], OB.moe_forward(u64, z, topk, gate, W1, W2)),
+            ubar=rel(out["grad_u"], OB.moe_vjp(u64, g.astype(np.float64), z, topk, gate, W1, W2)))
+print("RESULT " + json.dumps(errs), flush=True)
+'''
+
+
 def _run(code):
     env = dict(os.environ, MLIP_LIBRARY=DEBUG_LIB)
     r = subprocess.run([sys.executable, "-c", f"ROOT = {ROOT!r}\n" + code], env=env, capture_output=True,
@@ -101,3 +135,12 @@ def test_debug_build_reports_a_bad_sender(debug_lib):
     assert r.returncode == 0
     assert "mlip bounds: sender index" in r.stdout + r.stderr
     assert "RESULT finite=1" in r.stdout
+
+
+def test_debug_build_silent_on_the_tall_paired_launch(debug_lib):
+    r = _run(WIDE)
+    assert r.returncode == 0
+    assert "mlip bounds" not in r.stdout + r.stderr
+    line = [x for x in r.stdout.splitlines() if x.startswith("RESULT ")][-1]
+    errs = json.loads(line[len("RESULT "):])
+    assert max(errs.values()) <= 2e-4, errs
