@@ -161,11 +161,14 @@ def test_general_cell_graph_and_rotation(mlip, name, hand):
     assert np.max(np.abs(e1 - e0)) <= TOL * max(np.max(np.abs(e0)), 1e-30)
 
 
-def test_deterministic(mlip):
-    cfg = synth.CONFIGS["ragged"]
+@pytest.mark.parametrize("name", ["ragged", "S_slice"])
+def test_deterministic(mlip, name):
+    """Two runs give the same bits (S_slice takes the full-width kernels: the tall paired expert GEMM,
+    the split-K projections)."""
+    cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg)
     gup = synth.upstream_grad(cfg, inp, "random")
-    _say("determinism ragged")
+    _say(f"determinism {name}")
     a = run_gpu(mlip, inp, gup)
     outs_a = [t.cpu().clone() for t in (a.agg["e"], a.agg["u"], a.moe["h_out"], a.vjp["grad_h"],
                                         a.vjp["grad_pos"], a.ro["energy"])]
