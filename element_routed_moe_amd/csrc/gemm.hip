@@ -231,11 +231,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, float *const *As, f
     read_frag(Ab, Bb, 0, f[0]);
 #pragma unroll
     for (int j = 0; j < BK / 8; ++j) {
-      if (j + 1 < BK / 8) {
-        // the next k group's reads go out before this group's MFMAs, so their
-        // latency is covered by the wave's own matrix work
-        read_frag(Ab, Bb, j + 1, f[(j + 1) & 1]);
-      }
+      // Two fragment buffers let the next k group's reads precede this
+      // group's MFMAs; the compiler schedules them (pinning the order with
+      // scheduling barriers measured slower).
+      if (j + 1 < BK / 8) read_frag(Ab, Bb, j + 1, f[(j + 1) & 1]);
       const Frag &c = f[j & 1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
